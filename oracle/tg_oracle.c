@@ -1,0 +1,314 @@
+/*
+ * tg_oracle.c -- CPU oracle for the tiled dense GEMM  C = epilogue(A . B).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * reference that the GPU path is checked against.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or constant with the HIP library.
+ *
+ * What it computes (the plain definition, in double precision):
+ *
+ *   C[i][j] = round_dt( act( sum_{k=0}^{K-1} A[i][k] * B[k][j]  + bias[j] ) )
+ *
+ * - The matrix product is the operation every tile of the method adds up:
+ *   per tile, an A tile and a B tile are loaded and multiplied into an
+ *   output tile, marching over K ("TileIR", the matmul inner loop; the
+ *   TileLang article, section 4, the FP16 GEMM kernel).  Tiling only changes
+ *   the order of the sum, so the oracle is the untiled sum.
+ * - The sum over k runs in ascending k, in double.  Products of two f16
+ *   (11-bit significand) or bf16 (8-bit) values are exact in double.
+ * - bias[j] is added per output column, then the activation is applied
+ *   ("TileIR", epilogue fusion: an elementwise op applied to the MMA result).
+ *   act is identity or the tanh form of GELU:
+ *       gelu(x) = 0.5 x (1 + tanh( sqrt(2/pi) (x + 0.044715 x^3) )).
+ * - round_dt is IEEE round-to-nearest, ties-to-even, taken once, directly
+ *   from double to f16 or bf16 (the TileLang example copies its f32
+ *   fragment to an f16 output; the rounding mode is not stated there and
+ *   the IEEE default is taken).
+ * - The horizontally fused QKV projection ("TileIR", horizontal fusion:
+ *   Q, K and V projections share their input) is three independent GEMMs.
+ *
+ * Every output element depends only on its own row of A and column of B,
+ * so rows are split across OpenMP threads; the value of each element does
+ * not depend on the thread count.
+ *
+ * Codecs: f16/bf16 <-> double are written here from the IEEE 754 binary16
+ * and the bfloat16 (truncated binary32) bit layouts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { TGO_F16 = 1, TGO_BF16 = 2 };
+enum { TGO_ACT_NONE = 0, TGO_ACT_GELU_TANH = 1 };
+
+/* ---------------------------------------------------------------- codecs */
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double tgo_f16_to_double(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24); /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25); /* 1.f * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* bfloat16: the top 16 bits of a binary32. */
+double tgo_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, 4);
+    return (double)x;
+}
+
+/*
+ * Round a double to a binary format with `p` significand bits (including the
+ * implicit one), minimum normal exponent emin, maximum finite exponent emax,
+ * ties to even.  Returns the sign-less bit pattern with `fbits` fraction
+ * bits and `ebits` exponent bits; overflow gives infinity.
+ */
+static uint16_t tgo_round_bits(double x, int p, int emin, int emax, int ebits)
+{
+    int fbits = p - 1;
+    uint16_t sign = 0;
+    if (signbit(x)) {
+        sign = (uint16_t)(1u << (fbits + ebits));
+        x = -x;
+    }
+    uint16_t inf = (uint16_t)(((1u << ebits) - 1) << fbits);
+    if (isnan(x))
+        return (uint16_t)(inf | (1u << (fbits - 1))); /* canonical quiet NaN, sign dropped */
+    if (isinf(x))
+        return sign | inf;
+    if (x == 0.0)
+        return sign;
+
+    int e;
+    frexp(x, &e); /* x = m * 2^e, m in [0.5, 1) -> unbiased exponent e-1 */
+    int exp = e - 1;
+    if (exp < emin)
+        exp = emin; /* subnormal range: fixed quantum 2^(emin-fbits) */
+    /* quantum (ulp) at this exponent */
+    double scaled = ldexp(x, fbits - exp); /* x / ulp; exact (power-of-two scale) */
+    double fl = floor(scaled);
+    double rem = scaled - fl; /* exact: scaled has at most 53 bits */
+    uint64_t q = (uint64_t)fl;
+    if (rem > 0.5 || (rem == 0.5 && (q & 1)))
+        q += 1;
+    /* q is now the significand in units of 2^(exp-fbits); it may have
+     * carried into the next binade (q == 2^p). */
+    if (q >= (1ull << p)) {
+        q >>= 1;
+        exp += 1;
+    }
+    if (exp > emax)
+        return sign | inf;
+    if (q < (1ull << fbits)) /* subnormal (exp == emin) */
+        return sign | (uint16_t)q;
+    uint16_t bexp = (uint16_t)(exp - emin + 1);
+    return sign | (uint16_t)(bexp << fbits) | (uint16_t)(q & ((1u << fbits) - 1));
+}
+
+uint16_t tgo_double_to_f16(double x) { return tgo_round_bits(x, 11, -14, 15, 5); }
+uint16_t tgo_double_to_bf16(double x) { return tgo_round_bits(x, 8, -126, 127, 8); }
+
+static double decode(int dt, uint16_t v)
+{
+    return dt == TGO_F16 ? tgo_f16_to_double(v) : tgo_bf16_to_double(v);
+}
+
+static uint16_t encode(int dt, double x)
+{
+    return dt == TGO_F16 ? tgo_double_to_f16(x) : tgo_double_to_bf16(x);
+}
+
+/* ------------------------------------------------------------ activation */
+
+double tgo_gelu_tanh(double x)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+}
+
+static double activate(int act, double v)
+{
+    return act == TGO_ACT_GELU_TANH ? tgo_gelu_tanh(v) : v;
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* One output element: the definition, k ascending. */
+static double element(int dt, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+                      int64_t ldb, const uint16_t *bias, int act, int64_t i, int64_t j)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        s += decode(dt, A[i * lda + k]) * decode(dt, B[k * ldb + j]);
+    if (bias)
+        s += decode(dt, bias[j]);
+    return activate(act, s);
+}
+
+/*
+ * Full GEMM over output rows [row0, row1).  A is [M,K] row-major with row
+ * pitch lda, B is [K,N] with pitch ldb, bias is [N] or NULL.  Outputs (either
+ * may be NULL): out_f64[i*ldc + j] the unrounded double result, out_bits the
+ * round-to-nearest-even bits in the same dtype.  threads <= 0 means the
+ * OpenMP default.  Returns 0, or -1 on a bad argument.
+ *
+ * For speed only, B is first decoded into a column-major double copy; each
+ * element is still the k-ascending sum of exact products.
+ */
+int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+             const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, double *out_f64,
+             uint16_t *out_bits, int64_t ldc, int64_t row0, int64_t row1, int threads)
+{
+    if ((dt != TGO_F16 && dt != TGO_BF16) || (act != TGO_ACT_NONE && act != TGO_ACT_GELU_TANH))
+        return -1;
+    if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1 || ldc < N)
+        return -1;
+    if (row0 == row1 || N == 0)
+        return 0;
+    double *bt = (double *)malloc(sizeof(double) * (size_t)(N * (K > 0 ? K : 1)));
+    double *bs = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!bt || !bs) {
+        free(bt);
+        free(bs);
+        return -1;
+    }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j)
+            bt[j * K + k] = decode(dt, B[k * ldb + j]);
+    for (int64_t j = 0; j < N; ++j)
+        bs[j] = bias ? decode(dt, bias[j]) : 0.0;
+
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#pragma omp parallel
+#endif
+    {
+        double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = row0; i < row1; ++i) {
+            for (int64_t k = 0; k < K; ++k)
+                arow[k] = decode(dt, A[i * lda + k]);
+            for (int64_t j = 0; j < N; ++j) {
+                const double *bcol = bt + j * K;
+                double s = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    s += arow[k] * bcol[k];
+                if (bias)
+                    s += bs[j];
+                double v = activate(act, s);
+                if (out_f64)
+                    out_f64[i * ldc + j] = v;
+                if (out_bits)
+                    out_bits[i * ldc + j] = encode(dt, v);
+            }
+        }
+        free(arow);
+    }
+    free(bt);
+    free(bs);
+    return 0;
+}
+
+/*
+ * Sampled outputs: the n elements (ii[s], jj[s]) of the same GEMM, for
+ * checking large problems one element at a time.
+ */
+int tgo_gemm_sample(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                    const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, int64_t n,
+                    const int64_t *ii, const int64_t *jj, double *out_f64, uint16_t *out_bits,
+                    int threads)
+{
+    if ((dt != TGO_F16 && dt != TGO_BF16) || (act != TGO_ACT_NONE && act != TGO_ACT_GELU_TANH))
+        return -1;
+    for (int64_t s = 0; s < n; ++s)
+        if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N)
+            return -1;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t s = 0; s < n; ++s) {
+        double v = element(dt, K, A, lda, B, ldb, bias, act, ii[s], jj[s]);
+        if (out_f64)
+            out_f64[s] = v;
+        if (out_bits)
+            out_bits[s] = encode(dt, v);
+    }
+    return 0;
+}
+
+/*
+ * QKV: out_t = X . W_t for t = 0,1,2 -- three independent GEMMs sharing X.
+ * W[t] is [K,N] with pitch ldw; the outputs share pitch ldo.
+ */
+int tgo_gemm_qkv(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                 const uint16_t *Wq, const uint16_t *Wk, const uint16_t *Wv, int64_t ldw,
+                 double *q_f64, double *k_f64, double *v_f64, uint16_t *q_bits, uint16_t *k_bits,
+                 uint16_t *v_bits, int64_t ldo, int64_t row0, int64_t row1, int threads)
+{
+    const uint16_t *W[3] = {Wq, Wk, Wv};
+    double *of[3] = {q_f64, k_f64, v_f64};
+    uint16_t *ob[3] = {q_bits, k_bits, v_bits};
+    for (int t = 0; t < 3; ++t) {
+        int rc = tgo_gemm(dt, M, N, K, X, ldx, W[t], ldw, NULL, TGO_ACT_NONE, of[t], ob[t], ldo,
+                          row0, row1, threads);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+int tgo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Array forms of the codecs (used by the tests to sweep all bit patterns). */
+int tgo_decode_array(int dt, int64_t n, const uint16_t *in, double *out)
+{
+    if (dt != TGO_F16 && dt != TGO_BF16)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = decode(dt, in[i]);
+    return 0;
+}
+
+int tgo_encode_array(int dt, int64_t n, const double *in, uint16_t *out)
+{
+    if (dt != TGO_F16 && dt != TGO_BF16)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = encode(dt, in[i]);
+    return 0;
+}
+
+int tgo_gelu_array(int64_t n, const double *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = tgo_gelu_tanh(in[i]);
+    return 0;
+}
