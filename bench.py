@@ -1,0 +1,277 @@
+"""Benchmark of the tiled dense GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Headline workload: f16 GEMM M=N=K=4096 with the fused epilogue
+C = GELU_tanh(A.B + bias) (A, B = U[-1,1]/8, bias = U[-0.5,0.5], FP32
+accumulation and epilogue, f16 output), one tg_gemm_bias_act launch per step,
+inputs resident in HBM.  The timing protocol follows the pages (1000 warm-up
+and 3000 timed launches, mean time per launch), bracketed by HIP events on
+the launch stream.
+
+Prints ONE JSON line with the metric, the roofline of the kernel (achieved
+algorithmic TFLOP/s over the MI355X dense f16 MFMA peak), the CPU oracle
+timed on a bounded sample of the same workload on the host cores, and the
+secondary workloads (QKV, 8192^3 bf16, the M=16 bandwidth-bound product with
+its GB/s against the HBM peak, and the small square shapes).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16/bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "GEMM TFLOP/s + % of MFMA peak (4096³ fp16); GB/s % HBM peak at M=16"
+KERNEL_SOURCES = ["tiled_dense_gemm_09_amd/csrc/gemm_tiled.hip",
+                  "tiled_dense_gemm_09_amd/csrc/gemm_skinny.hip",
+                  "tiled_dense_gemm_09_amd/csrc/tg_device.h",
+                  "tiled_dense_gemm_09_amd/csrc/tg_api.cpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps, warmup):
+    """Mean ms per launch over `steps` launches after `warmup` untimed ones."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def dev(bits, dt):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dt == 1 else torch.bfloat16).cuda()
+
+
+def traffic_record(workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if still valid."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except ValueError:
+        return None
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(p, target_s):
+    """The oracle, as it stands, on a bounded row sample of the workload."""
+    import oracle
+    threads = oracle.max_threads()
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
+    dt = time.perf_counter() - t0
+    rows = int(min(p["M"], max(rows, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
+    secs = time.perf_counter() - t0
+    flops = 2.0 * rows * p["N"] * p["K"]
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of the %dx%dx%d workload (%.1f s, double precision)"
+                      % (rows - 1, p["M"], p["N"], p["K"], secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--only", choices=["main", "qkv", "square8192", "skinny", "small", "copy"],
+                    help="run one workload only (for profiling); no JSON line")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_dense_gemm_09_amd import inputs, tg
+    assert torch.cuda.is_available(), "no GPU visible"
+
+    if args.only == "copy":
+        # plain copy of a known size, for scaling the HBM byte counters
+        n = 256 << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        return
+
+    # ---------------------------------------------------------------- main
+    p = inputs.config_problem("f16_4096_gelu")
+    M, N, K = p["M"], p["N"], p["K"]
+    A, B, bias = dev(p["A"], 1), dev(p["B"], 1), dev(p["bias"], 1)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def step():
+        tg.gemm(A, B, out=C, bias=bias, act="gelu_tanh")
+
+    if args.only in (None, "main"):
+        log("main: f16 %dx%dx%d bias+gelu, warmup %d, steps %d" % (M, N, K, args.warmup,
+                                                                    args.steps))
+        ms = time_launches(step, args.steps, args.warmup)
+        kernel = tg.last_kernel()
+        tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log("  %s: %.4f ms/launch, %.1f TFLOP/s" % (kernel, ms, tflops))
+        if args.only == "main":
+            return
+
+    extra = {}
+    if not args.no_extra or args.only:
+        extra = run_secondary(args, torch, inputs, tg)
+        if args.only:
+            return
+
+    # quick parity of the timed output on sampled elements
+    import oracle
+    cb = C.view(torch.int16).cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng(0)
+    ii, jj = rng.integers(0, M, 512), rng.integers(0, N, 512)
+    f64, _ = oracle.gemm_sample(1, p["A"], p["B"], ii, jj, p["bias"], oracle.ACT_GELU_TANH)
+    got = cb[ii, jj].view(np.float16).astype(np.float64)
+    err = np.abs(got - f64)
+    parity = {"sampled": int(ii.size), "max_abs_err": float(err.max()),
+              "pass": bool(np.all(err <= 1e-2 + 5e-3 * np.abs(f64)))}
+
+    log("cpu baseline: oracle on a row sample (~%.0f s)" % args.cpu_seconds)
+    cpu = cpu_baseline(p, args.cpu_seconds)
+
+    traffic = traffic_record("f16_4096_gelu")
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "f16 GEMM M=N=K=4096, C = GELU_tanh(A.B + bias), FP32 accumulate",
+                   "M": M, "N": N, "K": K, "kernel": kernel},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "secondary": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_secondary(args, torch, inputs, tg):
+    out = {}
+    steps = max(10, min(args.steps, 300))
+    warm = max(3, min(args.warmup, 50))
+
+    if args.only in (None, "qkv"):
+        q = inputs.config_problem("bf16_qkv")
+        X = dev(q["X"], 2)
+        Ws = [dev(w, 2) for w in q["W"]]
+        outs = [torch.empty((q["M"], q["N"]), dtype=torch.bfloat16, device="cuda")
+                for _ in range(3)]
+        log("qkv: bf16 X[%d,%d] x 3 W[%d,%d]" % (q["M"], q["K"], q["K"], q["N"]))
+        ms = time_launches(lambda: tg.gemm_qkv(X, *Ws, outs=outs), steps, warm)
+        tf = 3 * 2.0 * q["M"] * q["N"] * q["K"] / (ms * 1e-3) / 1e12
+        out["bf16_qkv_8192x4096x4096x3"] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                                            "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                                            "kernel": tg.last_kernel()}
+        log("  ", out["bf16_qkv_8192x4096x4096x3"])
+        del X, Ws, outs
+
+    if args.only in (None, "square8192"):
+        p = inputs.config_problem("bf16_8192")
+        A, B = dev(p["A"], 2), dev(p["B"], 2)
+        C = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+        log("square: bf16 8192^3")
+        ms = time_launches(lambda: tg.gemm(A, B, out=C), steps, warm)
+        tf = 2.0 * p["M"] * p["N"] * p["K"] / (ms * 1e-3) / 1e12
+        out["bf16_8192x8192x8192"] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                                      "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                                      "kernel": tg.last_kernel()}
+        log("  ", out["bf16_8192x8192x8192"])
+        del A, B, C
+
+    if args.only in (None, "skinny"):
+        p = inputs.config_problem("bf16_skinny")
+        X = dev(p["A"], 2)
+        # four distinct copies of W (4 x 128 MiB > the 256 MB last-level cache),
+        # used in rotation so every launch streams W from HBM
+        Ws = [dev(p["B"], 2)]
+        for _ in range(3):
+            Ws.append(Ws[0].clone())
+        Y = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+        it = [0]
+
+        def sk():
+            tg.gemm(X, Ws[it[0] & 3], out=Y)
+            it[0] += 1
+
+        log("skinny: bf16 M=16 N=K=8192, W rotated over 4 buffers")
+        ms = time_launches(sk, steps, warm)
+        nbytes = 2 * (p["N"] * p["K"] + p["M"] * p["K"] + p["M"] * p["N"])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        ms_hot = time_launches(lambda: tg.gemm(X, Ws[0], out=Y), steps, warm)
+        out["bf16_skinny_16x8192x8192"] = {
+            "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes,
+            "cache_resident_ms": round(ms_hot, 5),
+            "cache_resident_GB/s": round(nbytes / (ms_hot * 1e-3) / 1e9, 1),
+            "kernel": tg.last_kernel()}
+        log("  ", out["bf16_skinny_16x8192x8192"])
+        del X, Ws, Y
+
+    if args.only in (None, "small"):
+        for name in ("f16_256", "f16_1024"):
+            p = inputs.config_problem(name)
+            A, B = dev(p["A"], 1), dev(p["B"], 1)
+            C = torch.empty((p["M"], p["N"]), dtype=torch.float16, device="cuda")
+            ms = time_launches(lambda: tg.gemm(A, B, out=C), steps, warm)
+            tf = 2.0 * p["M"] * p["N"] * p["K"] / (ms * 1e-3) / 1e12
+            out["f16_%dx%dx%d" % (p["M"], p["N"], p["K"])] = {
+                "ms": round(ms, 5), "TFLOP/s": round(tf, 2),
+                "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4), "kernel": tg.last_kernel()}
+            log("  ", name, out["f16_%dx%dx%d" % (p["M"], p["N"], p["K"])])
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * tg.h -- C ABI of the tiled dense GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ *     C = epilogue(A . B),  f16 or bf16 inputs, FP32 accumulation.
+ *
+ * The operation is the tiled matrix product that the pages lower to a tile
+ * loop: an A tile and a B tile are loaded, multiplied into an FP32 register
+ * accumulator, and the loop marches over K ("TileIR", the matmul inner loop;
+ * "Beyond Hand-Written CUDA: Inside TileLang's Multi-Backend Tile Compiler
+ * Architecture", section 4, the FP16 GEMM kernel with A(M,K), B(K,N),
+ * C(M,N) and a float32 fragment).  The epilogue (bias + activation) is
+ * applied while the accumulator is still in registers ("TileIR", epilogue
+ * fusion), and the QKV entry point is the horizontal fusion of three
+ * projections that share one input ("TileIR", horizontal fusion).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Layout: all matrices are row-major.  A is [M,K] with row pitch lda, B is
+ *    [K,N] with pitch ldb, C is [M,N] with pitch ldc.  Pitches are counted in
+ *    elements and must be >= the row length.  bias is a dense [N] vector.
+ *  - dtype: one element type for A, B, C and bias (TG_DTYPE_F16 or
+ *    TG_DTYPE_BF16).  Products accumulate in FP32; the epilogue runs in
+ *    FP32; the result is rounded once, to nearest even, to the dtype.
+ *  - Memory: every pointer is a device pointer owned by the caller.  The
+ *    library keeps no pointer after the call returns.  C must not overlap A,
+ *    B or bias.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Work is enqueued asynchronously; the call does not
+ *    synchronise.  Arguments are validated on the host before anything is
+ *    enqueued: on an invalid argument nothing is launched and an error code
+ *    is returned.
+ *  - Shapes: M, N, K >= 0 and < 2^31.  M == 0 or N == 0 is a no-op that
+ *    returns TG_SUCCESS.  K == 0 gives C = act(bias) (act(0) without bias).
+ *    Bounds are logical: element (i, k) of A is read only if i < M and k < K,
+ *    whatever lies in the padding between K and lda.
+ *  - Fast path: 16-byte aligned pointers and pitches that are multiples of
+ *    8 elements take the MFMA kernels.  Anything else runs a slower,
+ *    correct fallback kernel; the choice is never silent: tg_last_kernel()
+ *    names the kernel and tile configuration the last call on this host
+ *    thread launched (and TG_LOG=1 in the environment prints it).
+ *  - Thread safety: entry points may be called from several host threads.
+ *    The split-K path of tg_gemm/tg_gemm_bias_act for small M keeps a
+ *    per-device workspace that is allocated on first use and grown when a
+ *    larger one is needed (the only allocation the library makes); calls
+ *    that use it are ordered by their streams, and two such calls on
+ *    different streams of one device must not overlap.
+ */
+#ifndef TG_H
+#define TG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_BF16 = 2 } tg_dtype;
+
+/* act(x): identity, or the tanh form of GELU
+ *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+ * evaluated in FP32 with tanh(u) = 1 - 2 / (1 + exp(2u)). */
+typedef enum { TG_ACT_NONE = 0, TG_ACT_GELU_TANH = 1 } tg_act;
+
+typedef enum {
+    TG_SUCCESS = 0,
+    TG_ERROR_INVALID_VALUE = 1, /* NULL pointer, bad size, pitch, dtype or act, overlap */
+    TG_ERROR_NOT_SUPPORTED = 2, /* no device / not gfx950 */
+    TG_ERROR_LAUNCH_FAILED = 3, /* the HIP runtime reported an error at launch */
+    TG_ERROR_OUT_OF_MEMORY = 4  /* workspace allocation failed */
+} tg_status;
+
+/* C = A . B.
+ * "TileLang" section 4 (the FP16 GEMM kernel); "TileIR" (the matmul loop). */
+tg_status tg_gemm(tg_dtype dt, int64_t M, int64_t N, int64_t K,
+                  const void *A, int64_t lda,
+                  const void *B, int64_t ldb,
+                  void *C, int64_t ldc,
+                  void *stream);
+
+/* C = act(A . B + bias), bias[n] added per output column (NULL = no bias),
+ * then act, both in FP32 on the register accumulator.
+ * "TileIR", epilogue fusion. */
+tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda,
+                           const void *B, int64_t ldb,
+                           const void *bias, tg_act act,
+                           void *C, int64_t ldc,
+                           void *stream);
+
+/* Horizontally fused projection, one launch:
+ *     Q = X . Wq,  Kout = X . Wk,  V = X . Wv.
+ * X is [M,K] (pitch ldx); Wq, Wk, Wv are each [K,N] (shared pitch ldw);
+ * Q, Kout, V are each [M,N] (shared pitch ldo).  Each output is bit-identical
+ * to tg_gemm on the same operands.  "TileIR", horizontal fusion (Q, K and V
+ * projections share their input). */
+tg_status tg_gemm_qkv(tg_dtype dt, int64_t M, int64_t N, int64_t K,
+                      const void *X, int64_t ldx,
+                      const void *Wq, const void *Wk, const void *Wv, int64_t ldw,
+                      void *Q, void *Kout, void *V, int64_t ldo,
+                      void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *tg_status_string(tg_status s);
+
+/* Kernel and tile configuration chosen by the last entry-point call on the
+ * calling host thread, e.g. "tiled_256x256x64_w2x2"; "none" before any call
+ * or after a no-op.  Thread-local, static storage. */
+const char *tg_last_kernel(void);
+
+/* ---- host-side introspection (no GPU needed; for tests and tools) ---- */
+
+/* The tile scheduler's map of a linear workgroup id to (matrix, tile_m,
+ * tile_n) for a grid of tiles_m x tiles_n tiles per matrix and n_mat
+ * matrices, as the kernels compute it.  Returns 0, or -1 if block_id is out
+ * of range.  The map is a bijection onto the tile grid. */
+int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t group_m,
+                     int64_t block_id, int64_t *mat, int64_t *tile_m, int64_t *tile_n);
+
+/* Byte offset of element (row, col) in the kernels' LDS tile of `cols`
+ * 16-bit elements per row (row pitch padded by 8 elements). */
+int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col);
+
+/* Logical bounds predicate used for every global load and store: 1 if
+ * (row, col) lies inside a rows x cols matrix, else 0 (never judged by the
+ * linear offset). */
+int tg_in_bounds(int64_t rows, int64_t cols, int64_t row, int64_t col);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H */

@@ -1,0 +1,311 @@
+"""GPU parity: every entry point of libtg.so against the CPU oracle.
+
+Bar: |gpu - oracle| <= 1e-2 + 5e-3 |oracle| per element on random inputs
+(oracle = unrounded double), and bit-exact equality with the oracle's
+round-to-nearest-even bits on inputs with entries in {-2..2}, where every
+FP32 partial sum is exact in any order.
+
+Sizes: the small workloads are compared element by element in full; the
+full-size workloads (the shapes and launch configurations the benchmark
+times) are compared on sampled outputs that the oracle computes one by one.
+Ragged shapes use padded pitches whose padding holds NaN, so any read past
+the logical bounds would show up, and outputs carry NaN canaries around the
+written region.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import util
+from tiled_dense_gemm_09_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = inputs.F16, inputs.BF16
+NAN_BITS = {F16: 0x7E00, BF16: 0x7FC0}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tg():
+    import torch
+    assert torch.cuda.is_available()
+    from tiled_dense_gemm_09_amd import tg as _tg
+    return _tg
+
+
+def dev_problem(p):
+    dt = p["dt"]
+    A = util.to_dev(p["A"], dt)
+    B = util.to_dev(p["B"], dt)
+    bias = util.to_dev(p["bias"], dt) if p.get("bias") is not None else None
+    return A, B, bias
+
+
+def run(tg, p):
+    import torch
+    A, B, bias = dev_problem(p)
+    act = "gelu_tanh" if p["act"] == inputs.ACT_GELU_TANH else "none"
+    C = tg.gemm(A, B, bias=bias, act=act)
+    torch.cuda.synchronize()
+    return util.to_bits(C), tg.last_kernel()
+
+
+# ------------------------------------------------------------ small configs
+
+@pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
+def test_small_config_random_full(tg, name):
+    p = inputs.config_problem(name)
+    say("case", name, "random", p["M"], p["N"], p["K"])
+    bits, kern = run(tg, p)
+    f64, _ = oracle.gemm(p["dt"], p["A"], p["B"])
+    err = util.check_tol(p["dt"], bits, f64, name)
+    say("  kernel", kern, "max abs err", err)
+
+
+@pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
+def test_small_config_integer_exact(tg, name):
+    p = inputs.config_problem(name, integer=True)
+    say("case", name, "integer", p["M"], p["N"], p["K"])
+    bits, _ = run(tg, p)
+    _, ref = oracle.gemm(p["dt"], p["A"], p["B"])
+    util.check_exact(bits, ref, name)
+
+
+def test_tileLang_tiling_config_runs(tg, monkeypatch):
+    # 1024^3 with a 128 x 128 tile (the pages' starting tiling) must agree too
+    monkeypatch.setenv("TG_FORCE_CONFIG", "tiled_128x128x64_w2x2")
+    p = inputs.config_problem("f16_1024", integer=True)
+    bits, kern = run(tg, p)
+    assert kern == "tiled_128x128x64_w2x2"
+    _, ref = oracle.gemm(p["dt"], p["A"], p["B"])
+    util.check_exact(bits, ref, "1024 forced 128x128")
+
+
+# --------------------------------------------------------------- epilogue
+
+def test_bias_gelu_medium_full(tg):
+    p = inputs.problem(F16, 512, 768, 640, seed=31, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.2, b_scale=0.2)
+    say("case bias+gelu 512x768x640")
+    bits, _ = run(tg, p)
+    f64, _ = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits, f64, "bias+gelu")
+
+
+def test_gelu_config_full_size_sampled(tg):
+    p = inputs.config_problem("f16_4096_gelu")
+    say("case f16_4096_gelu", p["M"], p["N"], p["K"])
+    bits, kern = run(tg, p)
+    say("  kernel", kern)
+    ii, jj = util.sample_indices(p["M"], p["N"], 3000, seed=3)
+    f64, _ = oracle.gemm_sample(F16, p["A"], p["B"], ii, jj, p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits[ii, jj], f64, "f16_4096_gelu")
+    assert np.all(np.isfinite(util.decode(F16, bits)))
+
+
+def test_gelu_config_integer_bias_exact_sampled(tg):
+    p = inputs.config_problem("f16_4096_gelu", integer=True)
+    assert p["act"] == inputs.ACT_NONE and p["bias"] is not None
+    bits, _ = run(tg, p)
+    ii, jj = util.sample_indices(p["M"], p["N"], 3000, seed=4)
+    _, ref = oracle.gemm_sample(F16, p["A"], p["B"], ii, jj, p["bias"])
+    util.check_exact(bits[ii, jj], ref, "f16_4096 integer+bias")
+    # full rows, all columns, for a few rows
+    f, rb = oracle.gemm(F16, p["A"], p["B"], p["bias"], rows=(4000, 4004))
+    util.check_exact(bits[4000:4004], rb, "f16_4096 integer rows")
+
+
+# -------------------------------------------------------------------- QKV
+
+def run_qkv(tg, q):
+    import torch
+    X = util.to_dev(q["X"], q["dt"])
+    Ws = [util.to_dev(w, q["dt"]) for w in q["W"]]
+    outs = tg.gemm_qkv(X, *Ws)
+    torch.cuda.synchronize()
+    return X, Ws, [util.to_bits(o) for o in outs]
+
+
+def test_qkv_medium_full_and_equal_to_three_gemms(tg):
+    import torch
+    q = inputs.qkv_problem(BF16, 384, 512, 320, seed=41)
+    say("case qkv 384x512x320")
+    X, Ws, outs = run_qkv(tg, q)
+    refs = oracle.gemm_qkv(BF16, q["X"], *q["W"])
+    for t in range(3):
+        util.check_tol(BF16, outs[t], refs[t][0], "qkv[%d]" % t)
+        single = util.to_bits(tg.gemm(X, Ws[t]))
+        torch.cuda.synchronize()
+        util.check_exact(outs[t], single, "qkv[%d] vs tg_gemm" % t)
+
+
+def test_qkv_config_sampled(tg):
+    q = inputs.config_problem("bf16_qkv")
+    say("case bf16_qkv", q["M"], q["N"], q["K"])
+    _, _, outs = run_qkv(tg, q)
+    ii, jj = util.sample_indices(q["M"], q["N"], 2000, seed=5)
+    for t in range(3):
+        f64, _ = oracle.gemm_sample(BF16, q["X"], q["W"][t], ii, jj)
+        util.check_tol(BF16, outs[t][ii, jj], f64, "qkv config [%d]" % t)
+
+
+def test_qkv_config_integer_exact_sampled(tg):
+    q = inputs.config_problem("bf16_qkv", integer=True)
+    _, _, outs = run_qkv(tg, q)
+    ii, jj = util.sample_indices(q["M"], q["N"], 2000, seed=6)
+    for t in range(3):
+        _, ref = oracle.gemm_sample(BF16, q["X"], q["W"][t], ii, jj)
+        util.check_exact(outs[t][ii, jj], ref, "qkv integer [%d]" % t)
+
+
+# ------------------------------------------------------------------ skinny
+
+def test_skinny_config_full(tg):
+    p = inputs.config_problem("bf16_skinny")
+    say("case bf16_skinny", p["M"], p["N"], p["K"])
+    bits, kern = run(tg, p)
+    say("  kernel", kern)
+    assert kern.startswith("skinny")
+    f64, _ = oracle.gemm(BF16, p["A"], p["B"])
+    util.check_tol(BF16, bits, f64, "skinny")
+
+
+def test_skinny_config_integer_exact_and_deterministic(tg):
+    p = inputs.config_problem("bf16_skinny", integer=True)
+    bits, _ = run(tg, p)
+    bits2, _ = run(tg, p)
+    _, ref = oracle.gemm(BF16, p["A"], p["B"])
+    util.check_exact(bits, ref, "skinny integer")
+    util.check_exact(bits2, bits, "skinny repeat")
+
+
+def test_skinny_matches_tiled_on_integers(tg, monkeypatch):
+    p = inputs.problem(BF16, 16, 2048, 4096, seed=51, kind="int")
+    a, ka = run(tg, p)
+    monkeypatch.setenv("TG_FORCE_CONFIG", "tiled_64x64x64_w2x2")
+    b, kb = run(tg, p)
+    assert ka.startswith("skinny") and kb.startswith("tiled")
+    util.check_exact(a, b, "skinny vs tiled")
+
+
+# ----------------------------------------------------------- 8192^3 square
+
+def test_square_8192_sampled(tg):
+    p = inputs.config_problem("bf16_8192")
+    say("case bf16_8192", p["M"], p["N"], p["K"])
+    bits, kern = run(tg, p)
+    say("  kernel", kern)
+    ii, jj = util.sample_indices(p["M"], p["N"], 2000, seed=7)
+    f64, _ = oracle.gemm_sample(BF16, p["A"], p["B"], ii, jj)
+    util.check_tol(BF16, bits[ii, jj], f64, "bf16_8192")
+
+
+def test_square_8192_integer_exact_sampled(tg):
+    p = inputs.config_problem("bf16_8192", integer=True)
+    bits, _ = run(tg, p)
+    ii, jj = util.sample_indices(p["M"], p["N"], 2000, seed=8)
+    _, ref = oracle.gemm_sample(BF16, p["A"], p["B"], ii, jj)
+    util.check_exact(bits[ii, jj], ref, "bf16_8192 integer")
+
+
+# ------------------------------------------------------- ragged and edges
+
+def padded(bits, ld, dt):
+    """Copy a [R, C] bit matrix into a [R, ld] buffer whose padding is NaN."""
+    R, C = bits.shape
+    buf = np.full((R, ld), NAN_BITS[dt], np.uint16)
+    buf[:, :C] = bits
+    return buf
+
+
+def round8(x):
+    return max(8, (x + 7) // 8 * 8)
+
+
+RAGGED = [
+    (F16, 1, 1, 1), (F16, 4, 4, 4), (BF16, 129, 257, 31), (F16, 17, 300, 100),
+    (BF16, 300, 17, 1000), (F16, 255, 511, 129), (BF16, 64, 64, 64), (F16, 520, 264, 72),
+    (BF16, 16, 1000, 777), (F16, 5, 513, 4100), (BF16, 1, 4096, 300), (F16, 33, 2000, 520),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K", RAGGED)
+@pytest.mark.parametrize("integer", [False, True])
+def test_ragged_shapes_with_poisoned_padding(tg, dt, M, N, K, integer):
+    import torch
+    say("case ragged", dt, M, N, K, "integer" if integer else "random")
+    p = inputs.problem(dt, M, N, K, seed=M * 7 + N * 3 + K, kind="int" if integer else "uniform",
+                       bias=not integer, act=inputs.ACT_NONE if integer else inputs.ACT_GELU_TANH)
+    lda, ldb, ldc = round8(K + 3), round8(N + 5), round8(N + 9)
+    Abuf = util.to_dev(padded(p["A"], lda, dt), dt)
+    Bbuf = util.to_dev(padded(p["B"], ldb, dt), dt)
+    # output buffer with two extra canary rows below M
+    Cbuf = util.to_dev(np.full((M + 2, ldc), NAN_BITS[dt], np.uint16), dt)
+    bias = util.to_dev(p["bias"], dt) if p["bias"] is not None else None
+    A, B, C = Abuf[:, :K], Bbuf[:, :N], Cbuf[:M, :N]
+    tg.gemm(A, B, out=C, bias=bias, act="none" if integer else "gelu_tanh")
+    torch.cuda.synchronize()
+    say("  kernel", tg.last_kernel())
+    full = util.to_bits(Cbuf)
+    f64, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"], p["act"])
+    if integer:
+        util.check_exact(full[:M, :N], ref, "ragged exact")
+    else:
+        util.check_tol(dt, full[:M, :N], f64, "ragged")
+    assert np.all(full[:M, N:] == NAN_BITS[dt]), "wrote into the pitch padding"
+    assert np.all(full[M:, :] == NAN_BITS[dt]), "wrote below the last row"
+
+
+def test_unaligned_operands_take_the_reported_fallback(tg):
+    import torch
+    dt = F16
+    p = inputs.problem(dt, 70, 90, 50, seed=61, bias=True, act=inputs.ACT_GELU_TANH)
+    Abuf = util.to_dev(padded(p["A"], 51, dt), dt)  # pitch 51: not a multiple of 8
+    A = Abuf[:, :50]
+    B = util.to_dev(p["B"], dt)
+    bias = util.to_dev(p["bias"], dt)
+    C = tg.gemm(A, B, bias=bias, act="gelu_tanh")
+    torch.cuda.synchronize()
+    assert tg.last_kernel().startswith("generic_fma (unaligned")
+    f64, _ = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(dt, util.to_bits(C), f64, "generic")
+
+
+def test_k_zero_gives_activated_bias(tg):
+    import torch
+    dt = BF16
+    bias_bits = inputs.draw(np.random.default_rng(3), (40,), "bias", dt)
+    bias = util.to_dev(bias_bits, dt)
+    A = torch.empty((24, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((0, 40), dtype=torch.bfloat16, device="cuda")
+    C = tg.gemm(A, B, bias=bias, act="gelu_tanh")
+    torch.cuda.synchronize()
+    f64, _ = oracle.gemm(dt, np.zeros((24, 0), np.uint16), np.zeros((0, 40), np.uint16),
+                         bias_bits, oracle.ACT_GELU_TANH)
+    util.check_tol(dt, util.to_bits(C), f64, "K=0")
+
+
+def test_dispatch_choices(tg):
+    import torch
+    a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
+    tg.gemm(a, a)
+    assert tg.last_kernel() == "tiled_256x256x64_w2x2"
+    x = torch.zeros((16, 8192), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    tg.gemm(x, w)
+    assert tg.last_kernel().startswith("skinny")
+    torch.cuda.synchronize()
+
+
+def test_invalid_arguments_raise(tg):
+    import torch
+    a = torch.zeros((8, 8), dtype=torch.float16, device="cuda")
+    with pytest.raises(tg.TgError):
+        tg.gemm(a, a, out=a)  # output overlaps the inputs

@@ -1,0 +1,296 @@
+// gemm_tiled.hip -- the tiled MFMA GEMM for gfx950.
+//
+// One workgroup computes one BM x BN tile of C (or of one of the three QKV
+// outputs).  The structure is the tile loop of the pages: clear an FP32
+// accumulator, march over K in BK-deep steps, at each step stage an A tile
+// and a B tile and run a tile multiply-accumulate, then apply the epilogue
+// while the accumulator is still in registers and store the tile ("TileIR",
+// the matmul inner loop and epilogue fusion; "Beyond Hand-Written CUDA",
+// section 4, the pipelined FP16 GEMM with shared-memory tiles and a float32
+// fragment).
+//
+// gfx950 mapping:
+//  - Global -> registers: 128-bit loads.  A rows are K-contiguous and are
+//    loaded as 16-byte chunks.  B[K,N] is N-contiguous, but the MFMA wants 8
+//    consecutive k of one column per lane, so every thread loads an 8 x 8
+//    block of B (8 k-rows of 8 columns) and transposes it in registers;
+//    A and B then sit in LDS with the same K-contiguous row layout.
+//  - Two LDS stages: the loads for step k+1 are in flight while step k runs
+//    its MFMAs; one barrier per step ("Beyond Hand-Written CUDA", section 5:
+//    LDS footprint = stages x (A tile + B tile); 2 x (256 + 256) x 72 x 2 B =
+//    144 KiB of the 160 KiB per CU for the largest tile).
+//  - LDS rows are padded by 8 elements (16 bytes), which makes the 128-bit
+//    fragment reads conflict-free (see lds_offset_bytes).
+//  - v_mfma_f32_16x16x32_{f16,bf16} with B as the first operand and A as
+//    the second, so the accumulator holds C transposed: each lane owns 4
+//    consecutive columns of one row, stored as one 64-bit write.
+//  - Workgroup -> tile through schedule_tile (XCD-aware, grouped).
+//  - Every load and store is guarded by logical bounds; interior tiles take
+//    the 128-bit path, edge chunks fall back to element accesses.
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace tg {
+
+namespace {
+
+template <bool EDGE>
+__device__ __forceinline__ u32x4 load_row_chunk(const unsigned short *base, int64_t ld, int rows,
+                                                int cols, int r, int c)
+{
+    // 8 consecutive elements (r, c..c+7) of a rows x cols row-major matrix;
+    // out-of-bounds elements read as zero.  EDGE = false: the caller has
+    // established that the whole chunk is in bounds.
+    if (!EDGE || (r < rows && c + 8 <= cols))
+        return *reinterpret_cast<const u32x4 *>(base + (int64_t)r * ld + c);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) {
+        const unsigned short *p = base + (int64_t)r * ld;
+        unsigned short e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            e[i] = (c + i < cols) ? p[c + i] : (unsigned short)0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = (unsigned int)e[2 * i] | ((unsigned int)e[2 * i + 1] << 16);
+    }
+    return v;
+}
+
+} // namespace
+
+template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE>
+__device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
+                                          const unsigned short *Bm, unsigned short *Cm,
+                                          unsigned short *smem)
+{
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN; // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32; // 32x32 MFMA blocks per wave
+    constexpr int PA = lds_pitch(BK);         // LDS row pitch in elements
+    constexpr int KC = BK / 8;                // 16-byte chunks per K-row
+    constexpr int CA = BM * KC / NT;          // A chunks per thread per step
+    constexpr int NBLK = KC * (BN / 8);       // 8x8 B blocks per step
+    constexpr int CB = (NBLK + NT - 1) / NT;  // B blocks per thread per step
+    constexpr int A_ELEMS = BM * PA, B_ELEMS = BN * PA;
+    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile");
+    static_assert(BK % 16 == 0 && BK >= 64, "BK: whole MFMA steps, 8 k-blocks per row");
+    static_assert((BM * KC) % NT == 0 && NT % KC == 0, "A chunk mapping");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_m = wave / WN, wave_n = wave % WN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    // A staging: chunk (row, kc) with kc fixed per thread.
+    const int a_kc = tid % KC;
+    const int a_row0 = tid / KC;
+    // B staging: block b -> (kb = b % KC, nb = b / KC); lanes of one wave
+    // cover all kb for 8 column blocks, which keeps both the global rows
+    // (128-byte segments) and the transposed LDS writes conflict-free.
+    u32x4 ra[CA];
+    u32x4 rb[CB][8];
+
+    auto load_tile = [&](int kt) {
+        const int kbase = kt * BK;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            ra[i] = load_row_chunk<EDGE>(p.A, p.lda, M, K, m0 + a_row0 + i * (NT / KC),
+                                   kbase + a_kc * 8);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int b = tid + j * NT;
+            if (NBLK % NT == 0 || b < NBLK) {
+                const int kb = b % KC, nb = b / KC;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rb[j][i] = load_row_chunk<EDGE>(Bm, p.ldb, K, N, kbase + kb * 8 + i, n0 + nb * 8);
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+        unsigned short *As = smem + buf * (A_ELEMS + B_ELEMS);
+        unsigned short *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            *reinterpret_cast<u32x4 *>(As + (a_row0 + i * (NT / KC)) * PA + a_kc * 8) = ra[i];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int b = tid + j * NT;
+            if (NBLK % NT == 0 || b < NBLK) {
+                const int kb = b % KC, nb = b / KC;
+                // rb[j][i] = row k_i, columns c = 0..7 (two per dword).  Column c
+                // over k_0..k_7 is dword e = (k_{2e}, k_{2e+1}) of that column.
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    u32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned int x = rb[j][2 * e][c >> 1];
+                        const unsigned int y = rb[j][2 * e + 1][c >> 1];
+                        o[e] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u))
+                                       : ((x & 0xFFFFu) | (y << 16));
+                    }
+                    *reinterpret_cast<u32x4 *>(Bs + (nb * 8 + c) * PA + kb * 8) = o;
+                }
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    const int lrow = lane & 31;       // operand row / column of this lane
+    const int lk = (lane >> 5) * 8;   // its 8 k-values within a 16-deep step
+
+    auto compute = [&](int buf) {
+        const unsigned short *As = smem + buf * (A_ELEMS + B_ELEMS);
+        const unsigned short *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(
+                    As + (wave_m * TM + i * 32 + lrow) * PA + kk * 16 + lk);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const u32x4 *>(
+                    Bs + (wave_n * TN + j * 32 + lrow) * PA + kk * 16 + lk);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = mfma32x32x16<DT>(bf[j], af[i], acc[i][j]);
+        }
+    };
+
+    const int KT = (K + BK - 1) / BK;
+    if (KT > 0) {
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT)
+                load_tile(kt + 1);
+            compute(cur);
+            if (kt + 1 < KT)
+                store_tile(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue on the register accumulator.  With B as the first MFMA operand
+    // the 32x32 accumulator block is C transposed: lane l holds row
+    // m = l % 32 and, in registers 4g..4g+3, the 4 consecutive columns
+    // n = 8g + 4 (l / 32) + {0,1,2,3}.
+    const unsigned short *bias = p.bias;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wave_m * TM + i * 32 + lrow;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wave_n * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = acc[i][j][4 * g + r];
+                    if (bias != nullptr && (!EDGE || n + r < N))
+                        x += from_bits<DT>(bias[n + r]);
+                    v[r] = activate<ACT>(x);
+                }
+                if (!EDGE || m < M) {
+                    unsigned short *cp = Cm + (int64_t)m * p.ldc + n;
+                    if (!EDGE || n + 4 <= N) {
+                        u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                        *reinterpret_cast<u32x2 *>(cp) = o;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N)
+                                cp[r] = to_bits<DT>(v[r]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_tiled_kernel(GemmArgs p, int tiles_m,
+                                                                   int tiles_n, int group_m)
+{
+    constexpr int PA = lds_pitch(BK);
+    __shared__ __attribute__((aligned(16))) unsigned short smem[2 * (BM + BN) * PA];
+
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    // Interior tiles (no bound can be crossed) run without any predicate.
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && p.K % BK == 0;
+    if (interior)
+        tile_body<DT, BM, BN, BK, WM, WN, ACT, false>(p, m0, n0, Bm, Cm, smem);
+    else
+        tile_body<DT, BM, BN, BK, WM, WN, ACT, true>(p, m0, n0, Bm, Cm, smem);
+}
+
+// ------------------------------------------------------------------ configs
+
+static const TileConfig kConfigs[] = {
+    {256, 256, 64, 2, 2, "tiled_256x256x64_w2x2"},
+    {256, 128, 64, 2, 2, "tiled_256x128x64_w2x2"},
+    {128, 128, 64, 2, 2, "tiled_128x128x64_w2x2"},
+    {64, 64, 64, 2, 2, "tiled_64x64x64_w2x2"},
+};
+
+int num_tile_configs() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
+const TileConfig &tile_config(int i) { return kConfigs[i]; }
+
+template <int DT, int BM, int BN, int BK, int WM, int WN>
+static hipError_t launch_cfg(int act, const GemmArgs &a, int group_m, hipStream_t s)
+{
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = (a.N + BN - 1) / BN;
+    const int blocks = tiles_m * tiles_n * a.n_mat;
+    dim3 grid(blocks), block(64 * WM * WN);
+    if (act == ACT_GELU)
+        hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_GELU>), grid, block, 0, s,
+                           a, tiles_m, tiles_n, group_m);
+    else
+        hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_NONE>), grid, block, 0, s,
+                           a, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_dt(int cfg, int act, const GemmArgs &a, int group_m, hipStream_t s)
+{
+    switch (cfg) {
+    case 0: return launch_cfg<DT, 256, 256, 64, 2, 2>(act, a, group_m, s);
+    case 1: return launch_cfg<DT, 256, 128, 64, 2, 2>(act, a, group_m, s);
+    case 2: return launch_cfg<DT, 128, 128, 64, 2, 2>(act, a, group_m, s);
+    case 3: return launch_cfg<DT, 64, 64, 64, 2, 2>(act, a, group_m, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                        hipStream_t stream)
+{
+    return dt == DT_F16 ? launch_dt<DT_F16>(cfg, act, a, group_m, stream)
+                        : launch_dt<DT_BF16>(cfg, act, a, group_m, stream);
+}
+
+} // namespace tg

@@ -1,0 +1,303 @@
+// tg_api.cpp -- the C ABI (include/tg.h): argument validation, kernel and tile
+// selection, launch on the caller's stream, diagnostics.
+//
+// Validation is synchronous and complete before anything is enqueued; an
+// invalid call launches nothing ("TIRx", section 5.4: unsupported cases are
+// rejected or take a registered fallback with a diagnostic; "Beyond
+// Hand-Written CUDA", section 5: a silent fallback to a slow path is the
+// failure mode to avoid -- here the chosen kernel is always reported).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/tg.h"
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace {
+
+thread_local char g_last_kernel[96] = "none";
+
+void set_last(const char *name, const char *detail = nullptr)
+{
+    if (detail)
+        snprintf(g_last_kernel, sizeof g_last_kernel, "%s%s", name, detail);
+    else
+        snprintf(g_last_kernel, sizeof g_last_kernel, "%s", name);
+    static const bool log = [] {
+        const char *e = getenv("TG_LOG");
+        return e && e[0] == '1';
+    }();
+    if (log)
+        fprintf(stderr, "[tg] kernel: %s\n", g_last_kernel);
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte span [lo, hi) of a rows x cols matrix with pitch ld (16-bit elements).
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld)
+{
+    Span s;
+    s.lo = (uintptr_t)p;
+    s.hi = rows > 0 && cols > 0 ? s.lo + (uintptr_t)(((rows - 1) * ld + cols) * 2) : s.lo;
+    return s;
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+// ---- per-device workspace of the split-K small-M path -------------------
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+Workspace g_ws[64];
+
+// Returns nullptr on failure.  Layout: [counters: 4096 ints][floats...]
+constexpr size_t kCounterBytes = 4096 * sizeof(int);
+
+void *get_workspace(size_t float_count, hipStream_t stream, tg_status *st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *st = TG_ERROR_NOT_SUPPORTED;
+        return nullptr;
+    }
+    const size_t need = kCounterBytes + float_count * sizeof(float);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // the old buffer may still be in use by queued work
+            if (hipDeviceSynchronize() != hipSuccess || hipFree(w.ptr) != hipSuccess) {
+                *st = TG_ERROR_LAUNCH_FAILED;
+                return nullptr;
+            }
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t bytes = need < ((size_t)16 << 20) ? ((size_t)16 << 20) : need;
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            *st = TG_ERROR_OUT_OF_MEMORY;
+            return nullptr;
+        }
+        if (hipMemsetAsync(p, 0, kCounterBytes, stream) != hipSuccess) {
+            (void)hipFree(p);
+            *st = TG_ERROR_LAUNCH_FAILED;
+            return nullptr;
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    return w.ptr;
+}
+
+int env_int(const char *name, int dflt)
+{
+    const char *e = getenv(name);
+    return e && *e ? atoi(e) : dflt;
+}
+
+// Tile configuration for a problem: the largest tile that still gives about
+// one full wave of workgroups (256 CUs); otherwise the smallest tile.
+int choose_config(int64_t M, int64_t N, int n_mat)
+{
+    const char *force = getenv("TG_FORCE_CONFIG");
+    if (force && *force) {
+        for (int i = 0; i < tg::num_tile_configs(); ++i)
+            if (strcmp(force, tg::tile_config(i).name) == 0)
+                return i;
+    }
+    const int n = tg::num_tile_configs();
+    for (int i = 0; i < n; ++i) {
+        const tg::TileConfig &c = tg::tile_config(i);
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * n_mat;
+        if (tiles >= 240)
+            return i;
+    }
+    return n - 1;
+}
+
+tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+              const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
+              int64_t ldc, int n_mat, void *stream)
+{
+    if (dt != TG_DTYPE_F16 && dt != TG_DTYPE_BF16)
+        return TG_ERROR_INVALID_VALUE;
+    if (act != TG_ACT_NONE && act != TG_ACT_GELU_TANH)
+        return TG_ERROR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return TG_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        set_last("none");
+        return TG_SUCCESS;
+    }
+    if (lda < K || ldb < N || ldc < N)
+        return TG_ERROR_INVALID_VALUE;
+    if (K > 0 && A == nullptr)
+        return TG_ERROR_INVALID_VALUE;
+    for (int t = 0; t < n_mat; ++t) {
+        if (C[t] == nullptr || (K > 0 && B[t] == nullptr))
+            return TG_ERROR_INVALID_VALUE;
+    }
+    // Outputs must not overlap any input or each other.
+    for (int t = 0; t < n_mat; ++t) {
+        const Span c = span_of(C[t], M, N, ldc);
+        if (K > 0 && overlaps(c, span_of(A, M, K, lda)))
+            return TG_ERROR_INVALID_VALUE;
+        for (int u = 0; u < n_mat; ++u) {
+            if (K > 0 && overlaps(c, span_of(B[u], K, N, ldb)))
+                return TG_ERROR_INVALID_VALUE;
+            if (u != t && overlaps(c, span_of(C[u], M, N, ldc)))
+                return TG_ERROR_INVALID_VALUE;
+        }
+        if (bias && overlaps(c, span_of(bias, 1, N, N)))
+            return TG_ERROR_INVALID_VALUE;
+    }
+    if (((uintptr_t)bias & 1u) != 0)
+        return TG_ERROR_INVALID_VALUE;
+
+    tg::GemmArgs a;
+    a.A = static_cast<const unsigned short *>(A);
+    a.lda = lda;
+    for (int t = 0; t < 3; ++t) {
+        a.B[t] = static_cast<const unsigned short *>(B[t < n_mat ? t : 0]);
+        a.C[t] = static_cast<unsigned short *>(C[t < n_mat ? t : 0]);
+    }
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.bias = static_cast<const unsigned short *>(bias);
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.n_mat = n_mat;
+
+    bool fast = (lda % 8 == 0) && (ldb % 8 == 0) && (ldc % 8 == 0) && (K == 0 || aligned16(A));
+    for (int t = 0; t < n_mat; ++t)
+        fast = fast && aligned16(C[t]) && (K == 0 || aligned16(B[t]));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int kdt = dt == TG_DTYPE_F16 ? tg::DT_F16 : tg::DT_BF16;
+    const int kact = act == TG_ACT_GELU_TANH ? tg::ACT_GELU : tg::ACT_NONE;
+    const char *force = getenv("TG_FORCE_CONFIG");
+    const bool force_generic = force && strcmp(force, "generic") == 0;
+    const bool force_tiled = force && strncmp(force, "tiled", 5) == 0;
+
+    hipError_t err;
+    if (!fast || force_generic) {
+        err = tg::launch_generic(kdt, kact, a, s);
+        set_last(fast ? "generic_fma (forced)" : "generic_fma (unaligned operands)");
+    } else if (n_mat == 1 && M <= 16 && K >= 256 && N >= 256 && !force_tiled) {
+        const tg::SkinnyPlan pl = tg::plan_skinny(a.M, a.N, a.K);
+        float *ws = nullptr;
+        int *counters = nullptr;
+        if (pl.splits > 1) {
+            if (pl.n_tiles > (int)(kCounterBytes / sizeof(int)))
+                return TG_ERROR_NOT_SUPPORTED;
+            tg_status st = TG_SUCCESS;
+            void *base = get_workspace(tg::skinny_ws_floats(pl, a.M, a.N), s, &st);
+            if (!base)
+                return st;
+            counters = static_cast<int *>(base);
+            ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
+        }
+        err = tg::launch_skinny(kdt, kact, a, pl, ws, counters, s);
+        char detail[48];
+        snprintf(detail, sizeof detail, "_bn%d_split%dx%d", pl.bn, pl.splits, pl.k_chunk);
+        set_last("skinny", detail);
+    } else {
+        const int cfg = choose_config(M, N, n_mat);
+        const tg::TileConfig &c = tg::tile_config(cfg);
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * n_mat;
+        if (tiles >= kMaxDim)
+            return TG_ERROR_NOT_SUPPORTED;
+        const int group_m = env_int("TG_GROUP_M", 8);
+        err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 8, s);
+        set_last(c.name);
+    }
+    if (err != hipSuccess)
+        return TG_ERROR_LAUNCH_FAILED;
+    return TG_SUCCESS;
+}
+
+} // namespace
+
+extern "C" {
+
+tg_status tg_gemm(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                  const void *B, int64_t ldb, void *C, int64_t ldc, void *stream)
+{
+    const void *Bs[3] = {B, nullptr, nullptr};
+    void *Cs[3] = {C, nullptr, nullptr};
+    return run(dt, M, N, K, A, lda, Bs, ldb, nullptr, TG_ACT_NONE, Cs, ldc, 1, stream);
+}
+
+tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A,
+                           int64_t lda, const void *B, int64_t ldb, const void *bias, tg_act act,
+                           void *C, int64_t ldc, void *stream)
+{
+    const void *Bs[3] = {B, nullptr, nullptr};
+    void *Cs[3] = {C, nullptr, nullptr};
+    return run(dt, M, N, K, A, lda, Bs, ldb, bias, act, Cs, ldc, 1, stream);
+}
+
+tg_status tg_gemm_qkv(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *X, int64_t ldx,
+                      const void *Wq, const void *Wk, const void *Wv, int64_t ldw, void *Q,
+                      void *Kout, void *V, int64_t ldo, void *stream)
+{
+    const void *Bs[3] = {Wq, Wk, Wv};
+    void *Cs[3] = {Q, Kout, V};
+    return run(dt, M, N, K, X, ldx, Bs, ldw, nullptr, TG_ACT_NONE, Cs, ldo, 3, stream);
+}
+
+const char *tg_status_string(tg_status s)
+{
+    switch (s) {
+    case TG_SUCCESS: return "TG_SUCCESS";
+    case TG_ERROR_INVALID_VALUE: return "TG_ERROR_INVALID_VALUE";
+    case TG_ERROR_NOT_SUPPORTED: return "TG_ERROR_NOT_SUPPORTED";
+    case TG_ERROR_LAUNCH_FAILED: return "TG_ERROR_LAUNCH_FAILED";
+    case TG_ERROR_OUT_OF_MEMORY: return "TG_ERROR_OUT_OF_MEMORY";
+    }
+    return "TG_UNKNOWN_STATUS";
+}
+
+const char *tg_last_kernel(void) { return g_last_kernel; }
+
+int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t group_m,
+                     int64_t block_id, int64_t *mat, int64_t *tile_m, int64_t *tile_n)
+{
+    if (tiles_m <= 0 || tiles_n <= 0 || n_mat <= 0 || group_m <= 0)
+        return -1;
+    const int64_t total = tiles_m * tiles_n * n_mat;
+    if (total >= kMaxDim || block_id < 0 || block_id >= total)
+        return -1;
+    const tg::TileCoord t = tg::schedule_tile((int)tiles_m, (int)tiles_n, (int)n_mat,
+                                              (int)group_m, (int)block_id);
+    *mat = t.mat;
+    *tile_m = t.tm;
+    *tile_n = t.tn;
+    return 0;
+}
+
+int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col)
+{
+    return tg::lds_offset_bytes(cols, row, col);
+}
+
+int tg_in_bounds(int64_t rows, int64_t cols, int64_t row, int64_t col)
+{
+    return tg::in_bounds(rows, cols, row, col) ? 1 : 0;
+}
+
+} // extern "C"

@@ -1,0 +1,164 @@
+// tg_device.h -- shared device/host helpers of the HIP library: vector types,
+// the tile scheduler, LDS addressing, bounds predicate, the FP32 epilogue and
+// the f16/bf16 output conversion.  Host-callable parts are __host__ __device__
+// so the CPU tests exercise the same code the kernels run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+enum { DT_F16 = 1, DT_BF16 = 2 };
+enum { ACT_NONE = 0, ACT_GELU = 1 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Number of XCDs on MI355X; the hardware hands workgroup b to XCD b % 8.
+constexpr int kNumXcd = 8;
+
+struct TileCoord {
+    int mat, tm, tn;
+};
+
+// Tile scheduler ("Beyond Hand-Written CUDA", section 2: the tile
+// scheduler stage; "TileIR": data movement is the main cost).
+//
+// 1. XCD-aware remap.  Consecutive workgroup ids land on different XCDs, each
+//    with its own L2.  Workgroup b runs on XCD b % 8 as that XCD's
+//    (b / 8)-th block; give it logical id prefix(xcd) + b / 8, so every XCD
+//    works through one contiguous run of logical tiles.
+// 2. Grouped order.  Logical ids walk group_m tile-rows at a time, column by
+//    column, over a virtual grid of tiles_m x (n_mat * tiles_n) tiles, so the
+//    tiles an XCD runs together share A row-panels and B column-panels.  For
+//    the fused QKV projection the n_mat = 3 matrices sit side by side in the
+//    virtual grid and reuse the same row-panels of X.
+// Both steps are bijections, so every tile is computed exactly once.
+__host__ __device__ inline TileCoord schedule_tile(int tiles_m, int tiles_n, int n_mat,
+                                                   int group_m, int bid)
+{
+    const int total = tiles_m * tiles_n * n_mat;
+    const int xcd = bid % kNumXcd;
+    const int slot = bid / kNumXcd;
+    const int q = total / kNumXcd, r = total % kNumXcd;
+    const int logical = xcd * q + (xcd < r ? xcd : r) + slot;
+
+    const int width = tiles_n * n_mat;
+    const int group_size = group_m * width;
+    const int g = logical / group_size;
+    const int first_m = g * group_m;
+    const int rows_left = tiles_m - first_m;
+    const int gm = rows_left < group_m ? rows_left : group_m;
+    const int in_group = logical - g * group_size;
+    TileCoord t;
+    t.tm = first_m + in_group % gm;
+    const int tv = in_group / gm;
+    t.mat = tv / tiles_n;
+    t.tn = tv - t.mat * tiles_n;
+    return t;
+}
+
+// LDS tiles store rows of `cols` 16-bit elements with the row pitch padded by
+// 8 elements (16 bytes).  With pitch (cols + 8) * 2 bytes, 16 consecutive
+// rows read at the same column start on 16 distinct 16-byte bank groups, so
+// the 128-bit fragment reads of one 16-lane phase are conflict-free.  For a
+// 128-wide tile this is pitch 136 (the padded strided layout example of
+// "TIRx", section 3.1).
+__host__ __device__ constexpr int lds_pitch(int cols) { return cols + 8; }
+__host__ __device__ inline int64_t lds_offset_bytes(int64_t cols, int64_t row, int64_t col)
+{
+    return (row * (cols + 8) + col) * 2;
+}
+
+// Logical bounds: (row, col) is inside a rows x cols matrix iff both
+// coordinates are in range, whatever the linear offset ("TIRx", section 5.2:
+// the out-of-bounds rule of the asynchronous copy).
+__host__ __device__ inline bool in_bounds(int64_t rows, int64_t cols, int64_t row, int64_t col)
+{
+    return row >= 0 && col >= 0 && row < rows && col < cols;
+}
+
+// tanh form of GELU in FP32.  tanh(u) = 1 - 2 / (1 + e^{2u}); e^{2u} is
+// computed as 2^{2u log2 e} with the hardware base-2 exponential.  For large
+// |u| the exponential saturates to 0 or +inf and tanh to -1 or +1.
+__device__ __forceinline__ float gelu_tanh_f32(float x)
+{
+    const float c = 0.7978845608028654f; // sqrt(2/pi)
+    const float u = c * (x + 0.044715f * x * x * x);
+    const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f); // 2u * log2(e)
+    const float t = 1.0f - 2.0f / (1.0f + e);
+    return 0.5f * x * (1.0f + t);
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v)
+{
+    if constexpr (ACT == ACT_GELU)
+        return gelu_tanh_f32(v);
+    else
+        return v;
+}
+
+// f32 -> 16-bit pattern, round to nearest even.
+template <int DT>
+__device__ __forceinline__ unsigned short to_bits(float v)
+{
+    if constexpr (DT == DT_F16) {
+        _Float16 h = (_Float16)v;
+        return __builtin_bit_cast(unsigned short, h);
+    } else {
+        __bf16 h = (__bf16)v;
+        return __builtin_bit_cast(unsigned short, h);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float from_bits(unsigned short b)
+{
+    if constexpr (DT == DT_F16)
+        return (float)__builtin_bit_cast(_Float16, b);
+    else
+        return __builtin_bit_cast(float, (unsigned int)b << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ unsigned int pack2(float lo, float hi)
+{
+    return (unsigned int)to_bits<DT>(lo) | ((unsigned int)to_bits<DT>(hi) << 16);
+}
+
+// One 16x16x32 MFMA step: acc += src0 (16 rows x 32 k) * src1 (32 k x 16 cols).
+// Lane l holds 8 k-values of row (l % 16) of src0 and of column (l % 16) of
+// src1; both operands use the same k order, so any k permutation is harmless.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One 32x32x16 MFMA step: acc += src0 (32 rows x 16 k) * src1 (16 k x 32 cols).
+// Lane l holds 8 k-values of row (l % 32) of src0 and of column (l % 32) of
+// src1 (the same k order on both sides).  Accumulator register r of lane l is
+// element (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+} // namespace tg

@@ -1,0 +1,55 @@
+// tg_launch.h -- host-side launch interface between the C ABI (tg_api.cpp)
+// and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+// Operands of one (possibly horizontally fused) GEMM launch.  n_mat is 1 for
+// a plain GEMM and 3 for the QKV projection; B[t] and C[t] are the t-th
+// weight and output.  All pitches are in elements.
+struct GemmArgs {
+    const unsigned short *A;
+    int64_t lda;
+    const unsigned short *B[3];
+    int64_t ldb;
+    unsigned short *C[3];
+    int64_t ldc;
+    const unsigned short *bias; // [N] or nullptr
+    int M, N, K;
+    int n_mat;
+};
+
+// Tile configurations of the MFMA kernel: BM x BN output tile, BK deep,
+// WM x WN waves of 64 lanes.
+struct TileConfig {
+    int bm, bn, bk, wm, wn;
+    const char *name;
+};
+
+int num_tile_configs();
+const TileConfig &tile_config(int i);
+
+// Launchers; each returns the hipError_t of the launch.
+hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                        hipStream_t stream);
+hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
+
+// Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
+// workspace of ws_floats floats and `counters` an int array of n_tiles
+// entries that must be zero before the first call; the kernel leaves them
+// zero.
+struct SkinnyPlan {
+    int bn;       // columns per workgroup
+    int splits;   // K splits
+    int k_chunk;  // K per split (multiple of the slab depth)
+    int n_tiles;  // ceil(N / bn)
+};
+SkinnyPlan plan_skinny(int M, int N, int K);
+size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N);
+hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &pl, float *ws,
+                         int *counters, hipStream_t stream);
+
+} // namespace tg

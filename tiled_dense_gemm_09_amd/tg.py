@@ -1,0 +1,181 @@
+"""ctypes binding of libtg.so (include/tg.h).  Argument marshalling only.
+
+Every function here hands raw device pointers, sizes and the current HIP
+stream to the C ABI; the computation happens entirely in the HIP kernels.
+There is no fallback: if the library is missing the import fails loudly.
+
+    from tiled_dense_gemm_09_amd import tg
+    c = tg.gemm(a, b)                       # a [M,K], b [K,N] -> c [M,N]
+    c = tg.gemm(a, b, bias=bias, act="gelu_tanh")
+    q, k, v = tg.gemm_qkv(x, wq, wk, wv)
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtg.so")
+
+F16 = 1
+BF16 = 2
+ACT = {"none": 0, "gelu_tanh": 1}
+
+SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_qkv", "tg_status_string", "tg_last_kernel",
+           "tg_schedule_tile", "tg_lds_offset", "tg_in_bounds"]
+
+
+class TgError(RuntimeError):
+    def __init__(self, status, name):
+        super().__init__("%s (status %d)" % (name, status))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtg.so is not built (%s); run `python -m tiled_dense_gemm_09_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.tg_gemm.argtypes = [I, L, L, L, P, L, P, L, P, L, P]
+    lib.tg_gemm.restype = I
+    lib.tg_gemm_bias_act.argtypes = [I, L, L, L, P, L, P, L, P, I, P, L, P]
+    lib.tg_gemm_bias_act.restype = I
+    lib.tg_gemm_qkv.argtypes = [I, L, L, L, P, L, P, P, P, L, P, P, P, L, P]
+    lib.tg_gemm_qkv.restype = I
+    lib.tg_status_string.argtypes = [I]
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_last_kernel.argtypes = []
+    lib.tg_last_kernel.restype = ctypes.c_char_p
+    lib.tg_schedule_tile.argtypes = [L, L, L, L, L, ctypes.POINTER(L), ctypes.POINTER(L),
+                                     ctypes.POINTER(L)]
+    lib.tg_schedule_tile.restype = I
+    lib.tg_lds_offset.argtypes = [L, L, L]
+    lib.tg_lds_offset.restype = L
+    lib.tg_in_bounds.argtypes = [L, L, L, L]
+    lib.tg_in_bounds.restype = I
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != 0:
+        raise TgError(status, lib.tg_status_string(status).decode())
+
+
+def last_kernel():
+    return lib.tg_last_kernel().decode()
+
+
+# ---------------------------------------------------------------- raw calls
+
+def gemm_ptr(dt, M, N, K, A, lda, B, ldb, C, ldc, stream=0, bias=0, act=0):
+    """tg_gemm / tg_gemm_bias_act on raw device pointers (ints)."""
+    if bias or act:
+        _check(lib.tg_gemm_bias_act(dt, M, N, K, A, lda, B, ldb, bias or None, act, C, ldc,
+                                    stream or None))
+    else:
+        _check(lib.tg_gemm(dt, M, N, K, A, lda, B, ldb, C, ldc, stream or None))
+
+
+def gemm_qkv_ptr(dt, M, N, K, X, ldx, Wq, Wk, Wv, ldw, Q, Ko, V, ldo, stream=0):
+    _check(lib.tg_gemm_qkv(dt, M, N, K, X, ldx, Wq, Wk, Wv, ldw, Q, Ko, V, ldo, stream or None))
+
+
+def schedule_tile(tiles_m, tiles_n, n_mat, group_m, block_id):
+    mat, tm, tn = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.tg_schedule_tile(tiles_m, tiles_n, n_mat, group_m, block_id, ctypes.byref(mat),
+                              ctypes.byref(tm), ctypes.byref(tn))
+    if rc:
+        raise ValueError("block id out of range")
+    return mat.value, tm.value, tn.value
+
+
+def lds_offset(cols, row, col):
+    return lib.tg_lds_offset(cols, row, col)
+
+
+def in_bounds(rows, cols, row, col):
+    return bool(lib.tg_in_bounds(rows, cols, row, col))
+
+
+# ------------------------------------------------------------ torch wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("tg supports float16 and bfloat16, got %s" % t.dtype)
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major (unit column stride)" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    return max(t.stride(0), t.shape[1])
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def gemm(a, b, out=None, bias=None, act="none", stream=None):
+    """out = act(a @ b + bias); a [M,K], b [K,N], bias [N]; f16 or bf16."""
+    torch = _torch()
+    dt = _dt(a)
+    if b.dtype != a.dtype or (bias is not None and bias.dtype != a.dtype):
+        raise TypeError("a, b and bias must share one dtype")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if out.dtype != a.dtype or tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M,N] of the input dtype")
+    lda, ldb, ldc = _rowmajor(a, "a"), _rowmajor(b, "b"), _rowmajor(out, "out")
+    bptr = 0
+    if bias is not None:
+        if bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a dense [N] vector")
+        bptr = bias.data_ptr()
+    gemm_ptr(dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+             _stream(stream), bptr, ACT[act])
+    return out
+
+
+def gemm_qkv(x, wq, wk, wv, outs=None, stream=None):
+    """(x @ wq, x @ wk, x @ wv) in one launch; the three W share shape and pitch."""
+    torch = _torch()
+    dt = _dt(x)
+    M, K = x.shape
+    K2, N = wq.shape
+    if K2 != K or tuple(wk.shape) != (K, N) or tuple(wv.shape) != (K, N):
+        raise ValueError("weights must all be [K,N]")
+    if any(w.dtype != x.dtype for w in (wq, wk, wv)):
+        raise TypeError("x and the weights must share one dtype")
+    ldw = _rowmajor(wq, "wq")
+    if _rowmajor(wk, "wk") != ldw or _rowmajor(wv, "wv") != ldw:
+        raise ValueError("the three weights must share one row pitch")
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=x.dtype, device=x.device) for _ in range(3)]
+    ldo = _rowmajor(outs[0], "q")
+    if any(_rowmajor(o, "out") != ldo or tuple(o.shape) != (M, N) for o in outs):
+        raise ValueError("the three outputs must be [M,N] with one row pitch")
+    gemm_qkv_ptr(dt, M, N, K, x.data_ptr(), _rowmajor(x, "x"), wq.data_ptr(), wk.data_ptr(),
+                 wv.data_ptr(), ldw, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                 ldo, _stream(stream))
+    return outs
