@@ -193,6 +193,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     const bool force_generic = force && strcmp(force, "generic") == 0;
     const bool force_tiled = force && strncmp(force, "tiled", 5) == 0;
 
+    // An error left behind by an earlier, unrelated runtime call must not be
+    // reported as this launch's failure.
+    (void)hipGetLastError();
     hipError_t err;
     if (!fast || force_generic) {
         err = tg::launch_generic(kdt, kact, a, s);
@@ -225,8 +228,14 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 8, s);
         set_last(c.name);
     }
-    if (err != hipSuccess)
+    if (err != hipSuccess) {
+        char detail[64];
+        snprintf(detail, sizeof detail, " (launch failed: %s)", hipGetErrorName(err));
+        char name[96];
+        snprintf(name, sizeof name, "%s", g_last_kernel);
+        set_last(name, detail);
         return TG_ERROR_LAUNCH_FAILED;
+    }
     return TG_SUCCESS;
 }
 

@@ -30,6 +30,13 @@ class TgError(RuntimeError):
 
 
 def _load():
+    # PyTorch ships its own HIP runtime.  Load it first so that libtg.so binds
+    # to the same runtime instance (same soname) instead of a second copy
+    # from /opt/rocm, which would not see the device torch has opened.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError("libtg.so is not built (%s); run `python -m tiled_dense_gemm_09_amd.build`"
                           % LIB_PATH)
@@ -60,7 +67,8 @@ lib = _load()
 
 def _check(status):
     if status != 0:
-        raise TgError(status, lib.tg_status_string(status).decode())
+        raise TgError(status, "%s [%s]" % (lib.tg_status_string(status).decode(),
+                                           lib.tg_last_kernel().decode()))
 
 
 def last_kernel():
