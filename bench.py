@@ -88,18 +88,24 @@ def cpu_baseline(p, target_s):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
     threads = oracle.max_threads()
-    rows = 8
-    t0 = time.perf_counter()
-    oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
-    dt = time.perf_counter() - t0
-    rows = int(min(p["M"], max(rows, rows * target_s / max(dt, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
-    secs = time.perf_counter() - t0
+    # grow the sample until one call takes >= 1 s, then size it for target_s
+    rows, secs = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
+        secs = time.perf_counter() - t0
+        if secs >= 1.0 or rows >= p["M"]:
+            break
+        rows = min(p["M"], rows * 4)
+    if secs < target_s and rows < p["M"]:
+        rows = int(min(p["M"], rows * target_s / secs))
+        t0 = time.perf_counter()
+        oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
+        secs = time.perf_counter() - t0
     flops = 2.0 * rows * p["N"] * p["K"]
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of the %dx%dx%d workload (%.1f s, double precision)"
-                      % (rows - 1, p["M"], p["N"], p["K"], secs)}
+            "sample": "rows 0..%d of the %dx%dx%d workload, all %d columns (%.1f s, double "
+                      "precision)" % (rows - 1, p["M"], p["N"], p["K"], p["N"], secs)}
 
 
 def main():
