@@ -296,7 +296,7 @@ def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
     tg.gemm(a, a)
-    assert tg.last_kernel() == "tiled_256x256x64_w2x2"
+    assert tg.last_kernel().startswith(("tiled_256x256", "async_256x256"))
     x = torch.zeros((16, 8192), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
     tg.gemm(x, w)

@@ -1,0 +1,309 @@
+// gemm_async.hip -- the tiled MFMA GEMM with asynchronous global->LDS copies
+// for interior problems (M, N multiples of 256, K a multiple of 128).
+//
+// Same method as gemm_tiled (tile loop with an FP32 register accumulator and
+// a register-resident epilogue; "TileIR", the matmul inner loop;
+// "Beyond Hand-Written CUDA", section 4), mapped differently onto gfx950:
+//
+//  - Both operand tiles go from HBM straight into LDS with 16-byte
+//    direct-to-LDS loads: no staging registers, no VALU work.  Lane l of a
+//    wave-wide copy writes the 16 bytes at LDS base + 16 l, so each copy
+//    instruction fills 1 KiB of LDS; which global chunk a lane fetches is
+//    chosen so that the LDS image comes out swizzled.
+//  - Four LDS stages of BK = 32 ("Beyond Hand-Written CUDA", section 5:
+//    footprint = stages x (A tile + B tile) = 4 x 32 KiB = 128 KiB of the
+//    160 KiB per CU).  The copies of step k+3 are issued while step k
+//    computes, so every load has three K-steps of MFMA work to land.
+//  - A is stored K-contiguous ([256 rows][32 k], 64-byte rows) and read with
+//    128-bit LDS reads.  B stays as it is in memory, N-contiguous
+//    ([32 k][256 n], 512-byte rows); its MFMA fragments (8 consecutive k of
+//    one column per lane) come from the LDS transposing read, which hands
+//    lane i of a 16-lane group element q = R[4q + i/4][i%4] of the 16 x 4
+//    block R the group addressed.  With lane j addressing row (j/4), columns
+//    4 (j%4)..4 (j%4)+3, lane i receives column i at 4 consecutive k; two
+//    such reads give the 8 k of a 32x32x16 MFMA operand.
+//  - XOR swizzles (16-byte granules) make both the 128-bit A reads and the
+//    transposing B reads bank-conflict-free for 32 and for 64 LDS banks:
+//        A: granule c of row r at c ^ (((r >> 1) ^ (r >> 3)) & 3)
+//        B: granule c of row r at c ^ {0, 6, 10, 12}[r & 3]
+//    (power-of-two extents throughout; "TIRx", section 7 on XOR layouts).
+#include <type_traits>
+
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace tg {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int AS_BM = 256, AS_BN = 256, AS_BK = 32, AS_STAGES = 4, AS_NT = 256;
+constexpr int AS_A_BYTES = AS_BM * AS_BK * 2;  // 16 KiB
+constexpr int AS_B_BYTES = AS_BK * AS_BN * 2;  // 16 KiB
+constexpr int AS_STAGE_BYTES = AS_A_BYTES + AS_B_BYTES;
+constexpr int AS_COPIES = AS_STAGE_BYTES / 1024 / (AS_NT / 64); // 1 KiB copies per wave per step
+
+__host__ __device__ constexpr int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__host__ __device__ constexpr int swz_b(int r)
+{
+    return (r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 10 : 12;
+}
+
+// Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
+// workgroup release fence, which waits for every outstanding direct-to-LDS
+// copy (they count as LDS writes) and would drain all stages each step.  Here
+// each wave waits for exactly the copies it needs with wait_vmcnt first; the
+// empty asm statements keep the compiler from moving LDS accesses across the
+// barrier.
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+} // namespace
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int tiles_m, int tiles_n,
+                                                              int group_m)
+{
+    // one array per stage: with the K loop unrolled by the stage count every
+    // copy and every read names its stage statically, so the compiler can
+    // tell the stages apart and only waits for the copies of the stage it reads
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[AS_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[AS_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[AS_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[AS_STAGE_BYTES];
+    auto stage = [&](auto sidx) -> unsigned char * {
+        constexpr int S = decltype(sidx)::value;
+        if constexpr (S == 0)
+            return st0;
+        else if constexpr (S == 1)
+            return st1;
+        else if constexpr (S == 2)
+            return st2;
+        else
+            return st3;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave >> 1, wave_n = wave & 1; // 2 x 2 waves of 128 x 128
+
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int m0 = tc.tm * AS_BM, n0 = tc.tn * AS_BN;
+    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    const int KT = p.K / AS_BK;
+
+    // ---- copy plan: wave w issues copies q = 4w .. 4w+3 of A and of B.
+    // A copy q fills rows 16q..16q+15; lane -> (row 16q + lane/4, granule lane%4).
+    // B copy q fills rows 2q, 2q+1;    lane -> (row 2q + lane/32, granule lane%32).
+    const unsigned short *ga[4];
+    const unsigned short *gb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i;
+        const int ra = 16 * q + (lane >> 2);
+        const int ca = (lane & 3) ^ swz_a(ra);
+        ga[i] = p.A + (int64_t)(m0 + ra) * p.lda + ca * 8;
+        const int rb = 2 * q + (lane >> 5);
+        const int cb = (lane & 31) ^ swz_b(rb);
+        gb[i] = Bm + (int64_t)rb * p.ldb + n0 + cb * 8;
+    }
+    const int64_t b_step = (int64_t)AS_BK * p.ldb;
+
+    auto issue = [&](int kt, unsigned char *st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = wave * 4 + i;
+            __builtin_amdgcn_global_load_lds((const void *)(ga[i] + kt * AS_BK),
+                                             (lds_void *)(st + q * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = wave * 4 + i;
+            __builtin_amdgcn_global_load_lds((const void *)(gb[i] + kt * b_step),
+                                             (lds_void *)(st + AS_A_BYTES + q * 1024), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    // ---- fragment addressing (byte offsets within a stage)
+    // A fragment i: row wave_m*128 + i*32 + lane%32, k granule 2kk + lane/32.
+    int a_off[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wave_m * 128 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            a_off[i][kk] = r * 64 + (((2 * kk + (lane >> 5)) ^ swz_a(r)) * 16);
+    }
+    // B fragment j, half h: 16-lane group g = lane/16, jj = lane%16:
+    // row 16kk + 8(g/2) + 4h + jj/4, column wave_n*128 + 32j + 16(g%2) + 4(jj%4).
+    int b_off[4][2][2];
+    {
+        const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 16 * kk + 8 * (g >> 1) + 4 * h + (jj >> 2);
+                    const int col = wave_n * 128 + 32 * j + 16 * (g & 1) + 4 * (jj & 3);
+                    const int gran = (col >> 3) ^ swz_b(r);
+                    b_off[j][kk][h] = AS_A_BYTES + r * 512 + gran * 16 + (col & 7) * 2;
+                }
+    }
+
+    auto compute = [&](const unsigned char *st) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(st + a_off[i][kk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(st + b_off[j][kk][0]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(st + b_off[j][kk][1]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                bf[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma32x32x16<DT>(bf[j], af[i], acc[i][j]);
+        }
+    };
+
+    // ---- pipeline: copies for steps 0..2 in flight; step k waits for its own
+    // copies (the copies of the next two steps may stay outstanding), passes
+    // the barrier, issues step k+3 into the stage step k-1 used, computes.
+    // K is a multiple of 4 steps here, so the loop body is the 4 stages.
+    auto step = [&](int kt, auto sidx) {
+        constexpr int S = decltype(sidx)::value;
+        const int ahead = KT - 1 - kt; // steps issued after this one, at most 2
+        if (ahead >= 2)
+            wait_vmcnt<2 * AS_COPIES>();
+        else if (ahead == 1)
+            wait_vmcnt<AS_COPIES>();
+        else
+            wait_vmcnt<0>();
+        stage_barrier();
+        if (kt + 3 < KT)
+            issue(kt + 3, stage(std::integral_constant<int, (S + 3) % 4>{}));
+        compute(stage(sidx));
+    };
+    issue(0, st0);
+    issue(1, st1);
+    issue(2, st2);
+    for (int kt = 0; kt < KT; kt += 4) {
+        step(kt, std::integral_constant<int, 0>{});
+        step(kt + 1, std::integral_constant<int, 1>{});
+        step(kt + 2, std::integral_constant<int, 2>{});
+        step(kt + 3, std::integral_constant<int, 3>{});
+    }
+
+    // ---- epilogue (as in gemm_tiled): lane l of a 32x32 block holds row
+    // m = l % 32 and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.
+    auto epilogue = [&](auto has_bias) {
+        constexpr bool HB = decltype(has_bias)::value;
+        // bias[n..n+3] for every (j, g) column group of this lane, loaded up
+        // front so the 16 loads overlap instead of waiting one by one
+        u32x2 braw[4][4];
+        if constexpr (HB) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    braw[j][g] = *reinterpret_cast<const u32x2 *>(
+                        p.bias + n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wave_m * 128 + i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x = acc[i][j][4 * g + r];
+                        if constexpr (HB)
+                            x += from_bits<DT>((unsigned short)(braw[j][g][r >> 1] >> (16 * (r & 1))));
+                        v[r] = activate<ACT>(x);
+                    }
+                    u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                    *reinterpret_cast<u32x2 *>(Cm + (int64_t)m * p.ldc + n) = o;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    if (p.bias != nullptr)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
+bool async_eligible(const GemmArgs &a)
+{
+    return a.M % AS_BM == 0 && a.N % AS_BN == 0 && a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 &&
+           ((uintptr_t)a.bias & 7u) == 0;
+}
+
+hipError_t launch_async(int dt, int act, const GemmArgs &a, int group_m, hipStream_t s)
+{
+    const int tiles_m = a.M / AS_BM, tiles_n = a.N / AS_BN;
+    dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
+#define TG_AS(DT_, ACT_)                                                                         \
+    hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_>), grid, block, 0, s, a, tiles_m, tiles_n,     \
+                       group_m)
+    if (dt == DT_F16) {
+        if (act == ACT_GELU)
+            TG_AS(DT_F16, ACT_GELU);
+        else
+            TG_AS(DT_F16, ACT_NONE);
+    } else {
+        if (act == ACT_GELU)
+            TG_AS(DT_BF16, ACT_GELU);
+        else
+            TG_AS(DT_BF16, ACT_NONE);
+    }
+#undef TG_AS
+    return hipGetLastError();
+}
+
+} // namespace tg

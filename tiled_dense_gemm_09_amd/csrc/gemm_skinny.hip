@@ -29,6 +29,7 @@ constexpr int SK_BN = 256;  // columns per workgroup
 constexpr int SK_BK = 64;   // slab depth
 constexpr int SK_NT = 256;  // threads
 constexpr int SK_PA = lds_pitch(SK_BK);
+constexpr int SK_DEPTH = 4; // slabs of loads in flight per thread
 
 __device__ __forceinline__ u32x4 ld_chunk(const unsigned short *base, int64_t ld, int rows,
                                           int cols, int r, int c)
@@ -56,7 +57,11 @@ struct Slot {
 
 } // namespace
 
-template <int DT, int ACT, int DEPTH>
+// EDGE = false: N is a multiple of 256 and every split's K-range a multiple
+// of DEPTH slabs, so the kernel runs branch-free on buffer loads (rows of X
+// at or beyond M read as zero through the buffer range check on the
+// per-lane offset).  EDGE = true: every chunk is bounds-checked.
+template <int DT, int ACT, int DEPTH, bool EDGE>
 __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k_chunk,
                                                                int splits, float *ws,
                                                                int *counters)
@@ -81,15 +86,36 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
     // X fragment: row (lane % 16), 8 k starting at (lane / 16) * 8
     const int xr = lane & 15, xk = (lane >> 4) * 8;
 
+    // fast path: W through a resource based at (kbeg, n0), X through one
+    // whose range ends after row M-1 (so rows >= M load zeros)
+    const int vw = (kb * 8 * (int)p.ldb + nb * 8) * 2;
+    const int vx = (xr * (int)p.lda + kbeg + xk) * 2;
+
     auto load = [&](Slot &s, int slab) {
         const int k0 = kbeg + slab * SK_BK;
+        if constexpr (!EDGE) {
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(W + (int64_t)k0 * p.ldb + n0), (short)0, 0x7FFFFFFF, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)p.A, (short)0, M * (int)p.lda * 2, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            s.w[i] = ld_chunk(W, p.ldb, kend, N, k0 + kb * 8 + i, n0 + nb * 8);
+            for (int i = 0; i < 8; ++i)
+                s.w[i] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, i * (int)p.ldb * 2, 0));
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int k = k0 + h * 32 + xk;
-            s.x[h] = ld_chunk(p.A, p.lda, M, kend, xr, k);
+            for (int h = 0; h < 2; ++h)
+                s.x[h] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rx, vx + (slab * SK_BK + h * 32) * 2, 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                s.w[i] = ld_chunk(W, p.ldb, kend, N, k0 + kb * 8 + i, n0 + nb * 8);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = k0 + h * 32 + xk;
+                s.x[h] = ld_chunk(p.A, p.lda, M, kend, xr, k);
+            }
         }
     };
 
@@ -113,7 +139,7 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
     for (int j = 0; j < 4; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Slot &s, int buf) {
+    auto compute = [&](const u32x4 (&x)[2], int buf) {
         const unsigned short *Ws = smem + buf * (SK_BN * SK_PA);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -121,30 +147,33 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
             for (int j = 0; j < 4; ++j) {
                 const int n = wave * 64 + j * 16 + (lane & 15);
                 const u32x4 wf = *reinterpret_cast<const u32x4 *>(Ws + n * SK_PA + h * 32 + xk);
-                acc[j] = mfma16x16x32<DT>(wf, s.x[h], acc[j]);
+                acc[j] = mfma16x16x32<DT>(wf, x[h], acc[j]);
             }
         }
     };
 
+    // DEPTH slabs of loads stay in flight: slot d holds slab s0 + d; it is
+    // written to LDS, reloaded with slab s0 + d + DEPTH, and the MFMAs of
+    // slab s0 + d run after the barrier.
     Slot slot[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-        if (d < slabs)
+        if (EDGE ? d < slabs : true)
             load(slot[d], d);
 
     for (int s0 = 0; s0 < slabs; s0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int s = s0 + d;
-            if (s < slabs) {
-                const int buf = s & 1;
-                store(slot[d], buf);
-                const Slot cur_x = slot[d]; // keep X fragments of slab s
-                if (s + DEPTH < slabs)
-                    load(slot[d], s + DEPTH);
-                __syncthreads();
-                compute(cur_x, buf);
-            }
+            if (EDGE && s >= slabs)
+                break;
+            const int buf = s & 1;
+            store(slot[d], buf);
+            u32x4 x[2] = {slot[d].x[0], slot[d].x[1]};
+            if (s + DEPTH < slabs)
+                load(slot[d], s + DEPTH);
+            __syncthreads();
+            compute(x, buf);
         }
     }
 
@@ -186,18 +215,22 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
         float *dst = ws + ((int64_t)split * 16 + m) * ws_ld + n0 + nl;
         *reinterpret_cast<f32x4 *>(dst) = acc[j];
     }
-    __threadfence();
+    // Release this thread's partials at device scope (the XCDs' L2 caches are
+    // not coherent with each other), then count the split in.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0) {
-        const int old = atomicAdd(&counters[tile_n], 1);
+        const int old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == splits - 1);
     }
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
+    // Last workgroup of this column tile: acquire the other splits' partials,
+    // then a fixed-order reduction + epilogue.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    // Last workgroup of this column tile: fixed-order reduction + epilogue.
     // Thread -> row rm = tid / 16, 16 columns starting at (tid % 16) * 16.
     const int rm = tid >> 4;
     const int cn = (tid & 15) * 16;
@@ -240,7 +273,7 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
         }
     }
     if (tid == 0)
-        counters[tile_n] = 0;
+        __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 SkinnyPlan plan_skinny(int M, int N, int K)
@@ -257,7 +290,8 @@ SkinnyPlan plan_skinny(int M, int N, int K)
         splits = max_splits;
     if (splits < 1)
         splits = 1;
-    const int slabs_per = (kslabs + splits - 1) / splits;
+    int slabs_per = (kslabs + splits - 1) / splits;
+    slabs_per = (slabs_per + SK_DEPTH - 1) / SK_DEPTH * SK_DEPTH; // whole pipeline rounds
     pl.k_chunk = slabs_per * SK_BK;
     pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
     if (pl.splits < 1)
@@ -275,23 +309,34 @@ size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N)
 hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &pl, float *ws,
                          int *counters, hipStream_t s)
 {
-    constexpr int D = 4;
+    constexpr int D = SK_DEPTH;
     dim3 grid(pl.n_tiles * pl.splits), block(SK_NT);
+    const bool fast = a.N % SK_BN == 0 && a.K % (D * SK_BK) == 0 && pl.k_chunk % (D * SK_BK) == 0 &&
+                      (int64_t)a.ldb * SK_BK * 2 < (1ll << 30) && (int64_t)a.lda * 16 * 2 < (1ll << 30);
+#define TG_SK(DT_, ACT_, EDGE_)                                                                  \
+    hipLaunchKernelGGL((gemm_skinny_kernel<DT_, ACT_, (EDGE_ ? 2 : D), EDGE_>), grid, block, 0, s, \
+                       a, pl.k_chunk, \
+                       pl.splits, ws, counters)
+#define TG_SK_E(DT_, ACT_)                                                                       \
+    do {                                                                                         \
+        if (fast)                                                                                \
+            TG_SK(DT_, ACT_, false);                                                             \
+        else                                                                                     \
+            TG_SK(DT_, ACT_, true);                                                              \
+    } while (0)
     if (dt == DT_F16) {
         if (act == ACT_GELU)
-            hipLaunchKernelGGL((gemm_skinny_kernel<DT_F16, ACT_GELU, D>), grid, block, 0, s, a,
-                               pl.k_chunk, pl.splits, ws, counters);
+            TG_SK_E(DT_F16, ACT_GELU);
         else
-            hipLaunchKernelGGL((gemm_skinny_kernel<DT_F16, ACT_NONE, D>), grid, block, 0, s, a,
-                               pl.k_chunk, pl.splits, ws, counters);
+            TG_SK_E(DT_F16, ACT_NONE);
     } else {
         if (act == ACT_GELU)
-            hipLaunchKernelGGL((gemm_skinny_kernel<DT_BF16, ACT_GELU, D>), grid, block, 0, s, a,
-                               pl.k_chunk, pl.splits, ws, counters);
+            TG_SK_E(DT_BF16, ACT_GELU);
         else
-            hipLaunchKernelGGL((gemm_skinny_kernel<DT_BF16, ACT_NONE, D>), grid, block, 0, s, a,
-                               pl.k_chunk, pl.splits, ws, counters);
+            TG_SK_E(DT_BF16, ACT_NONE);
     }
+#undef TG_SK_E
+#undef TG_SK
     return hipGetLastError();
 }
 

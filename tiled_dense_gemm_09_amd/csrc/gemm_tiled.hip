@@ -27,6 +27,8 @@
 //  - Workgroup -> tile through schedule_tile (XCD-aware, grouped).
 //  - Every load and store is guarded by logical bounds; interior tiles take
 //    the 128-bit path, edge chunks fall back to element accesses.
+#include <type_traits>
+
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -59,6 +61,13 @@ __device__ __forceinline__ u32x4 load_row_chunk(const unsigned short *base, int6
 
 } // namespace
 
+// Operand staging registers of one K-step: CA chunks of A and CB 8x8 blocks of B.
+template <int CA, int CB>
+struct Stage {
+    u32x4 a[CA];
+    u32x4 b[CB][8];
+};
+
 template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
                                           const unsigned short *Bm, unsigned short *Cm,
@@ -89,47 +98,81 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
     // B staging: block b -> (kb = b % KC, nb = b / KC); lanes of one wave
     // cover all kb for 8 column blocks, which keeps both the global rows
     // (128-byte segments) and the transposed LDS writes conflict-free.
-    u32x4 ra[CA];
-    u32x4 rb[CB][8];
+    using St = Stage<CA, CB>;
 
-    auto load_tile = [&](int kt) {
+    // Interior tiles load through buffer resources: one per-thread VGPR
+    // offset per operand, the per-chunk offsets in scalar registers, and the
+    // resource base advanced by one K-step at a time (so offsets stay far
+    // below 2^32).  Edge tiles use predicated element-wise loads.
+    const int va = (a_row0 * (int)p.lda + a_kc * 8) * 2;
+    int vb[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int b = tid + j * NT;
+        vb[j] = ((b % KC) * 8 * (int)p.ldb + (b / KC) * 8) * 2;
+    }
+
+    auto load = [&](St &r, int kt) {
         const int kbase = kt * BK;
+        if constexpr (!EDGE) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.A + (int64_t)m0 * p.lda + kbase), (short)0, 0x7FFFFFFF, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(Bm + (int64_t)kbase * p.ldb + n0), (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < CA; ++i)
-            ra[i] = load_row_chunk<EDGE>(p.A, p.lda, M, K, m0 + a_row0 + i * (NT / KC),
-                                   kbase + a_kc * 8);
+            for (int i = 0; i < CA; ++i)
+                r.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       ra, va, i * (NT / KC) * (int)p.lda * 2, 0));
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const int b = tid + j * NT;
-            if (NBLK % NT == 0 || b < NBLK) {
-                const int kb = b % KC, nb = b / KC;
+            for (int j = 0; j < CB; ++j) {
+                const int b = tid + j * NT;
+                if (NBLK % NT == 0 || b < NBLK) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    rb[j][i] = load_row_chunk<EDGE>(Bm, p.ldb, K, N, kbase + kb * 8 + i, n0 + nb * 8);
+                    for (int i = 0; i < 8; ++i)
+                        r.b[j][i] = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vb[j],
+                                                                         i * (int)p.ldb * 2, 0));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CA; ++i)
+                r.a[i] = load_row_chunk<true>(p.A, p.lda, M, K, m0 + a_row0 + i * (NT / KC),
+                                              kbase + a_kc * 8);
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int b = tid + j * NT;
+                if (NBLK % NT == 0 || b < NBLK) {
+                    const int kb = b % KC, nb = b / KC;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        r.b[j][i] = load_row_chunk<true>(Bm, p.ldb, K, N, kbase + kb * 8 + i,
+                                                         n0 + nb * 8);
+                }
             }
         }
     };
 
-    auto store_tile = [&](int buf) {
+    auto store = [&](const St &r, int buf) {
         unsigned short *As = smem + buf * (A_ELEMS + B_ELEMS);
         unsigned short *Bs = As + A_ELEMS;
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            *reinterpret_cast<u32x4 *>(As + (a_row0 + i * (NT / KC)) * PA + a_kc * 8) = ra[i];
+            *reinterpret_cast<u32x4 *>(As + (a_row0 + i * (NT / KC)) * PA + a_kc * 8) = r.a[i];
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
             const int b = tid + j * NT;
             if (NBLK % NT == 0 || b < NBLK) {
                 const int kb = b % KC, nb = b / KC;
-                // rb[j][i] = row k_i, columns c = 0..7 (two per dword).  Column c
+                // r.b[j][i] = row k_i, columns c = 0..7 (two per dword).  Column c
                 // over k_0..k_7 is dword e = (k_{2e}, k_{2e+1}) of that column.
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     u32x4 o;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const unsigned int x = rb[j][2 * e][c >> 1];
-                        const unsigned int y = rb[j][2 * e + 1][c >> 1];
+                        const unsigned int x = r.b[j][2 * e][c >> 1];
+                        const unsigned int y = r.b[j][2 * e + 1][c >> 1];
                         o[e] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u))
                                        : ((x & 0xFFFFu) | (y << 16));
                     }
@@ -148,43 +191,59 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.f;
 
-    const int lrow = lane & 31;       // operand row / column of this lane
-    const int lk = (lane >> 5) * 8;   // its 8 k-values within a 16-deep step
+    const int lrow = lane & 31;     // operand row / column of this lane
+    const int lk = (lane >> 5) * 8; // its 8 k-values within a 16-deep step
 
+    // One K-step from LDS stage `buf`.  The fragments of the next 16-deep
+    // sub-step are read before the MFMAs of the current one are issued, and a
+    // scheduling barrier after each sub-step keeps the compiler from hoisting
+    // further reads (which would cost registers the staging buffers need).
     auto compute = [&](int buf) {
         const unsigned short *As = smem + buf * (A_ELEMS + B_ELEMS);
         const unsigned short *Bs = As + A_ELEMS;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            u32x4 af[FM], bf[FN];
+        u32x4 af[2][FM], bf[2][FN];
+        auto read = [&](int kk, int slot) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const u32x4 *>(
+                af[slot][i] = *reinterpret_cast<const u32x4 *>(
                     As + (wave_m * TM + i * 32 + lrow) * PA + kk * 16 + lk);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const u32x4 *>(
+                bf[slot][j] = *reinterpret_cast<const u32x4 *>(
                     Bs + (wave_n * TN + j * 32 + lrow) * PA + kk * 16 + lk);
+        };
+        read(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < BK / 16)
+                read(kk + 1, cur ^ 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma32x32x16<DT>(bf[j], af[i], acc[i][j]);
+                    acc[i][j] = mfma32x32x16<DT>(bf[cur][j], af[cur][i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // Two LDS stages, one register stage: the loads of tile k+1 are issued
+    // before the MFMAs of tile k and written to the other LDS stage after
+    // them; one barrier per K-step.
     const int KT = (K + BK - 1) / BK;
     if (KT > 0) {
-        load_tile(0);
-        store_tile(0);
+        St r0;
+        load(r0, 0);
+        store(r0, 0);
         __syncthreads();
         for (int kt = 0; kt < KT; ++kt) {
             const int cur = kt & 1;
             if (kt + 1 < KT)
-                load_tile(kt + 1);
+                load(r0, kt + 1);
             compute(cur);
+            __builtin_amdgcn_sched_barrier(0);
             if (kt + 1 < KT)
-                store_tile(cur ^ 1);
+                store(r0, cur ^ 1);
             __syncthreads();
         }
     }
@@ -193,41 +252,56 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
     // the 32x32 accumulator block is C transposed: lane l holds row
     // m = l % 32 and, in registers 4g..4g+3, the 4 consecutive columns
     // n = 8g + 4 (l / 32) + {0,1,2,3}.
-    const unsigned short *bias = p.bias;
+    auto epilogue = [&](auto has_bias) {
+        constexpr bool HB = decltype(has_bias)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wave_m * TM + i * 32 + lrow;
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wave_m * TM + i * 32 + lrow;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wave_n * TN + j * 32 + g * 8 + (lane >> 5) * 4;
-                float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wave_n * TN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x = acc[i][j][4 * g + r];
-                    if (bias != nullptr && (!EDGE || n + r < N))
-                        x += from_bits<DT>(bias[n + r]);
-                    v[r] = activate<ACT>(x);
-                }
-                if (!EDGE || m < M) {
-                    unsigned short *cp = Cm + (int64_t)m * p.ldc + n;
-                    if (!EDGE || n + 4 <= N) {
-                        u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                        *reinterpret_cast<u32x2 *>(cp) = o;
-                    } else {
+                    for (int r = 0; r < 4; ++r) {
+                        float x = acc[i][j][4 * g + r];
+                        if constexpr (HB) {
+                            if (!EDGE || n + r < N)
+                                x += from_bits<DT>(p.bias[n + r]);
+                        }
+                        v[r] = activate<ACT>(x);
+                    }
+                    if (!EDGE || m < M) {
+                        unsigned short *cp = Cm + (int64_t)m * p.ldc + n;
+                        if (!EDGE || n + 4 <= N) {
+                            u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                            *reinterpret_cast<u32x2 *>(cp) = o;
+                        } else {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < N)
-                                cp[r] = to_bits<DT>(v[r]);
+                            for (int r = 0; r < 4; ++r)
+                                if (n + r < N)
+                                    cp[r] = to_bits<DT>(v[r]);
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
+    };
+    if (p.bias != nullptr)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
-template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT>
+// EDGE = false: every tile of the grid is interior (M, N, K are multiples of
+// the tile and the pitches fit 32-bit buffer offsets), so no predicate is
+// evaluated anywhere.  EDGE = true: every load and store is bounds-checked.
+// The host picks one or the other per launch; keeping them in separate
+// kernels keeps the register allocation of the fast path unaffected by the
+// predicated one.
+template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_tiled_kernel(GemmArgs p, int tiles_m,
                                                                    int tiles_n, int group_m)
 {
@@ -238,12 +312,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_tiled_kernel(GemmArgs p,
     const int m0 = tc.tm * BM, n0 = tc.tn * BN;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    // Interior tiles (no bound can be crossed) run without any predicate.
-    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && p.K % BK == 0;
-    if (interior)
-        tile_body<DT, BM, BN, BK, WM, WN, ACT, false>(p, m0, n0, Bm, Cm, smem);
-    else
-        tile_body<DT, BM, BN, BK, WM, WN, ACT, true>(p, m0, n0, Bm, Cm, smem);
+    tile_body<DT, BM, BN, BK, WM, WN, ACT, EDGE>(p, m0, n0, Bm, Cm, smem);
 }
 
 // ------------------------------------------------------------------ configs
@@ -265,12 +334,23 @@ static hipError_t launch_cfg(int act, const GemmArgs &a, int group_m, hipStream_
     const int tiles_n = (a.N + BN - 1) / BN;
     const int blocks = tiles_m * tiles_n * a.n_mat;
     dim3 grid(blocks), block(64 * WM * WN);
-    if (act == ACT_GELU)
-        hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_GELU>), grid, block, 0, s,
-                           a, tiles_m, tiles_n, group_m);
-    else
-        hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_NONE>), grid, block, 0, s,
-                           a, tiles_m, tiles_n, group_m);
+    const bool interior = a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0 &&
+                          a.lda < (1 << 22) && a.ldb < (1 << 22);
+#define TG_LAUNCH(ACT_, EDGE_)                                                                   \
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_, EDGE_>), grid, block, 0, \
+                       s, a, tiles_m, tiles_n, group_m)
+    if (act == ACT_GELU) {
+        if (interior)
+            TG_LAUNCH(ACT_GELU, false);
+        else
+            TG_LAUNCH(ACT_GELU, true);
+    } else {
+        if (interior)
+            TG_LAUNCH(ACT_NONE, false);
+        else
+            TG_LAUNCH(ACT_NONE, true);
+    }
+#undef TG_LAUNCH
     return hipGetLastError();
 }
 

@@ -218,6 +218,11 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         char detail[48];
         snprintf(detail, sizeof detail, "_bn%d_split%dx%d", pl.bn, pl.splits, pl.k_chunk);
         set_last("skinny", detail);
+    } else if (tg::async_eligible(a) && !force_tiled &&
+               (M / 256) * (N / 256) * n_mat >= 128) {
+        const int group_m = env_int("TG_GROUP_M", 8);
+        err = tg::launch_async(kdt, kact, a, group_m > 0 ? group_m : 8, s);
+        set_last("async_256x256x32_s4");
     } else {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);

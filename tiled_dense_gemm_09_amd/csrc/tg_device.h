@@ -84,14 +84,16 @@ __host__ __device__ inline bool in_bounds(int64_t rows, int64_t cols, int64_t ro
 }
 
 // tanh form of GELU in FP32.  tanh(u) = 1 - 2 / (1 + e^{2u}); e^{2u} is
-// computed as 2^{2u log2 e} with the hardware base-2 exponential.  For large
-// |u| the exponential saturates to 0 or +inf and tanh to -1 or +1.
+// computed as 2^{2u log2 e} with the hardware base-2 exponential and the
+// division with the hardware reciprocal (about 1 ulp each; the result is
+// rounded to f16/bf16 afterwards).  For large |u| the exponential saturates
+// to 0 or +inf and tanh to -1 or +1.
 __device__ __forceinline__ float gelu_tanh_f32(float x)
 {
     const float c = 0.7978845608028654f; // sqrt(2/pi)
     const float u = c * (x + 0.044715f * x * x * x);
     const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f); // 2u * log2(e)
-    const float t = 1.0f - 2.0f / (1.0f + e);
+    const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
     return 0.5f * x * (1.0f + t);
 }
 

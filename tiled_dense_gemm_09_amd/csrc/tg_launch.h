@@ -37,6 +37,11 @@ hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m
                         hipStream_t stream);
 hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
 
+// Asynchronous-copy MFMA kernel (256 x 256 x 32 tiles, 4 stages) for problems
+// with M, N multiples of 256 and K a multiple of 128.
+bool async_eligible(const GemmArgs &a);
+hipError_t launch_async(int dt, int act, const GemmArgs &a, int group_m, hipStream_t stream);
+
 // Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
 // entries that must be zero before the first call; the kernel leaves them
