@@ -129,18 +129,23 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     }
     const int64_t b_step = (int64_t)AS_BK * p.ldb;
 
+    // The copies are issued with inline assembly so that the compiler's own
+    // wait insertion (which cannot tell the stages apart and would drain every
+    // copy before each LDS read) stays out of the pipeline; the waits below
+    // (wait_vmcnt) cover them explicitly.  m0 holds the wave's LDS base.
     auto issue = [&](int kt, unsigned char *st) {
+        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = wave * 4 + i;
-            __builtin_amdgcn_global_load_lds((const void *)(ga[i] + kt * AS_BK),
-                                             (lds_void *)(st + q * 1024), 16, 0, 0);
+            const unsigned dst = lds + (wave * 4 + i) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[i] + kt * AS_BK), "{m0}"(dst)
+                         : "memory");
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = wave * 4 + i;
-            __builtin_amdgcn_global_load_lds((const void *)(gb[i] + kt * b_step),
-                                             (lds_void *)(st + AS_A_BYTES + q * 1024), 16, 0, 0);
+            const unsigned dst = lds + AS_A_BYTES + (wave * 4 + i) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[i] + kt * b_step), "{m0}"(dst)
+                         : "memory");
         }
     };
 
@@ -181,52 +186,82 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
                 }
     }
 
-    auto compute = [&](const unsigned char *st) {
+    struct Frag {
+        u32x4 a[4], b[4];
+    };
+    auto read = [&](Frag &f, const unsigned char *st, int kk) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            u32x4 af[4], bf[4];
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *reinterpret_cast<const u32x4 *>(st + a_off[i][kk]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const u32x4 *>(st + a_off[i][kk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(st + b_off[j][kk][0]));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(st + b_off[j][kk][1]));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                bf[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma32x32x16<DT>(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+            const s16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][0]));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][1]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+            f.b[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
         }
     };
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
+    };
 
-    // ---- pipeline: copies for steps 0..2 in flight; step k waits for its own
-    // copies (the copies of the next two steps may stay outstanding), passes
-    // the barrier, issues step k+3 into the stage step k-1 used, computes.
-    // K is a multiple of 4 steps here, so the loop body is the 4 stages.
+    // ---- pipeline.  Copies run three K-steps ahead of use at most; each
+    // step k (32 deep = two 16-deep halves h0, h1):
+    //     read h1 of stage k            (h0 of stage k is already in registers)
+    //     MFMAs of h0
+    //     wait for this wave's copies of step k+1, barrier
+    //     issue the copies of step k+3 into the stage step k-1 used
+    //     read h0 of stage k+1
+    //     MFMAs of h1
+    // so every LDS read overlaps MFMAs, and the barrier both publishes stage
+    // k+1 and retires stage k-1.  K is a multiple of 4 steps, so the loop
+    // body is the 4 stages with their arrays named statically.
+    // Scheduling pattern for a read batch overlapped with an MFMA batch:
+    // alternate one MFMA and one LDS read (12 reads, 16 MFMAs).
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    Frag f0, f1;
     auto step = [&](int kt, auto sidx) {
         constexpr int S = decltype(sidx)::value;
-        const int ahead = KT - 1 - kt; // steps issued after this one, at most 2
-        if (ahead >= 2)
-            wait_vmcnt<2 * AS_COPIES>();
-        else if (ahead == 1)
+        unsigned char *cur = stage(sidx);
+        unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
+        read(f1, cur, 1);
+        mma(f0);
+        interleave();
+        if (kt + 2 < KT)
             wait_vmcnt<AS_COPIES>();
         else
             wait_vmcnt<0>();
         stage_barrier();
         if (kt + 3 < KT)
             issue(kt + 3, stage(std::integral_constant<int, (S + 3) % 4>{}));
-        compute(stage(sidx));
+        // K is a multiple of 4 steps: only the last stage of the unrolled
+        // body can be the last step (keeping the read unconditional for the
+        // other three lets the scheduler interleave it with the MFMAs)
+        if (S != 3 || kt + 1 < KT)
+            read(f0, nxt, 0);
+        mma(f1);
+        interleave();
     };
     issue(0, st0);
     issue(1, st1);
     issue(2, st2);
+    wait_vmcnt<2 * AS_COPIES>();
+    stage_barrier();
+    read(f0, st0, 0);
     for (int kt = 0; kt < KT; kt += 4) {
         step(kt, std::integral_constant<int, 0>{});
         step(kt + 1, std::integral_constant<int, 1>{});

@@ -220,8 +220,8 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         set_last("skinny", detail);
     } else if (tg::async_eligible(a) && !force_tiled &&
                (M / 256) * (N / 256) * n_mat >= 128) {
-        const int group_m = env_int("TG_GROUP_M", 8);
-        err = tg::launch_async(kdt, kact, a, group_m > 0 ? group_m : 8, s);
+        const int group_m = env_int("TG_GROUP_M", 4);
+        err = tg::launch_async(kdt, kact, a, group_m > 0 ? group_m : 4, s);
         set_last("async_256x256x32_s4");
     } else {
         const int cfg = choose_config(M, N, n_mat);
@@ -229,8 +229,8 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * n_mat;
         if (tiles >= kMaxDim)
             return TG_ERROR_NOT_SUPPORTED;
-        const int group_m = env_int("TG_GROUP_M", 8);
-        err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 8, s);
+        const int group_m = env_int("TG_GROUP_M", 4);
+        err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
         set_last(c.name);
     }
     if (err != hipSuccess) {
