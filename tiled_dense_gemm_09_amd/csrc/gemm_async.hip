@@ -132,21 +132,26 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     // The copies are issued with inline assembly so that the compiler's own
     // wait insertion (which cannot tell the stages apart and would drain every
     // copy before each LDS read) stays out of the pipeline; the waits below
-    // (wait_vmcnt) cover them explicitly.  m0 holds the wave's LDS base.
-    auto issue = [&](int kt, unsigned char *st) {
+    // (wait_vmcnt) cover them explicitly.  m0 holds the copy's LDS address.
+    // Copy c (0..7) of step kt: c < 4 is A copy 4 wave + c, else B copy
+    // 4 wave + c - 4.
+    auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const unsigned dst = lds + (wave * 4 + i) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[i] + kt * AS_BK), "{m0}"(dst)
+        if (c < 4) {
+            const unsigned dst = lds + (wave * 4 + c) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[c] + kt * AS_BK), "{m0}"(dst)
+                         : "memory");
+        } else {
+            const unsigned dst = lds + AS_A_BYTES + (wave * 4 + c - 4) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - 4] + kt * b_step),
+                         "{m0}"(dst)
                          : "memory");
         }
+    };
+    auto issue = [&](int kt, unsigned char *st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const unsigned dst = lds + AS_A_BYTES + (wave * 4 + i) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[i] + kt * b_step), "{m0}"(dst)
-                         : "memory");
-        }
+        for (int c = 0; c < 8; ++c)
+            copy(kt, st, c);
     };
 
     f32x16 acc[4][4];
@@ -189,40 +194,36 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     struct Frag {
         u32x4 a[4], b[4];
     };
+    // fragment piece q of half kk: q < 4 is A fragment q, then the two
+    // transposing reads (q - 4 even: low half, odd: high half) of B fragment
+    // (q - 4) / 2
+    auto read_piece = [&](Frag &f, const unsigned char *st, int kk, int q) {
+        if (q < 4) {
+            f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q][kk]);
+        } else {
+            const int j = (q - 4) >> 1, h = (q - 4) & 1;
+            const s16x4 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][h]));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            f.b[j][2 * h] = w[0];
+            f.b[j][2 * h + 1] = w[1];
+        }
+    };
     auto read = [&](Frag &f, const unsigned char *st, int kk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f.a[i] = *reinterpret_cast<const u32x4 *>(st + a_off[i][kk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const s16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][0]));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][1]));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-            const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-            f.b[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-        }
+        for (int q = 0; q < 12; ++q)
+            read_piece(f, st, kk, q);
+    };
+    auto mma_one = [&](const Frag &f, int q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
     };
     auto mma = [&](const Frag &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
+        for (int q = 0; q < 16; ++q)
+            mma_one(f, q);
     };
 
-    // ---- pipeline.  Copies run three K-steps ahead of use at most; each
-    // step k (32 deep = two 16-deep halves h0, h1):
-    //     read h1 of stage k            (h0 of stage k is already in registers)
-    //     MFMAs of h0
-    //     wait for this wave's copies of step k+1, barrier
-    //     issue the copies of step k+3 into the stage step k-1 used
-    //     read h0 of stage k+1
-    //     MFMAs of h1
-    // so every LDS read overlaps MFMAs, and the barrier both publishes stage
-    // k+1 and retires stage k-1.  K is a multiple of 4 steps, so the loop
-    // body is the 4 stages with their arrays named statically.
     // Scheduling pattern for a read batch overlapped with an MFMA batch:
     // alternate one MFMA and one LDS read (12 reads, 16 MFMAs).
     auto interleave = [&]() {
@@ -233,6 +234,17 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
+
+    // ---- pipeline.  Each step k (32 deep = two 16-deep halves h0, h1):
+    //     read h1 of stage k            (h0 of stage k is already in registers)
+    //     MFMAs of h0
+    //     wait for this wave's copies of step k+1, barrier
+    //     MFMAs of h1, interleaved with the reads of h0 of stage k+1 and the
+    //     copies of step k+4 into stage k
+    // Stage k is free after the barrier (both of its halves were read before
+    // it), so every copy has three steps of MFMA work to land, and every LDS
+    // read overlaps MFMAs.  K is a multiple of 4 steps, so the loop body is
+    // the 4 stages with their arrays named statically.
     Frag f0, f1;
     auto step = [&](int kt, auto sidx) {
         constexpr int S = decltype(sidx)::value;
@@ -241,25 +253,27 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
         read(f1, cur, 1);
         mma(f0);
         interleave();
-        if (kt + 2 < KT)
-            wait_vmcnt<AS_COPIES>();
-        else
-            wait_vmcnt<0>();
+        // The copies of steps k+2 and k+3 may stay in flight.  The loop body
+        // is branch-free: past the last step the copies repeat the last tile
+        // (into stages nobody reads any more), so this count always holds.
+        wait_vmcnt<2 * AS_COPIES>();
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's reads of stage k are done
         stage_barrier();
-        if (kt + 3 < KT)
-            issue(kt + 3, stage(std::integral_constant<int, (S + 3) % 4>{}));
-        // K is a multiple of 4 steps: only the last stage of the unrolled
-        // body can be the last step (keeping the read unconditional for the
-        // other three lets the scheduler interleave it with the MFMAs)
-        if (S != 3 || kt + 1 < KT)
-            read(f0, nxt, 0);
-        mma(f1);
-        interleave();
+        const int kc = min(kt + 4, KT - 1);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            mma_one(f1, q);
+            if (q < 12)
+                read_piece(f0, nxt, 0, q); // past the last step: harmless reread
+            if (q < 8)
+                copy(kc, cur, q);
+        }
     };
     issue(0, st0);
     issue(1, st1);
     issue(2, st2);
-    wait_vmcnt<2 * AS_COPIES>();
+    issue(3, st3);
+    wait_vmcnt<3 * AS_COPIES>();
     stage_barrier();
     read(f0, st0, 0);
     for (int kt = 0; kt < KT; kt += 4) {
@@ -268,6 +282,8 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
         step(kt + 2, std::integral_constant<int, 2>{});
         step(kt + 3, std::integral_constant<int, 3>{});
     }
+    // no copy may still be writing this workgroup's LDS when it exits
+    wait_vmcnt<0>();
 
     // ---- epilogue (as in gemm_tiled): lane l of a 32x32 block holds row
     // m = l % 32 and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.
