@@ -276,10 +276,296 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
         __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant for the common case (N a multiple of 256, K a multiple of
+// 256): W and X go from memory straight into LDS with 16-byte direct-to-LDS
+// copies, three 64-deep slabs ahead of use, through four LDS stages; no
+// staging registers and no VALU transposition.  The W fragments (8
+// consecutive k of one column per lane) come from the LDS transposing read,
+// exactly as for B in the asynchronous square kernel.
+//
+// LDS stage (36 KiB): W slab [64 k][256 n] (512-byte rows, 16-byte granule c
+// of row r stored at c ^ ({0,6,10,12}[r & 3] ^ 2 ((r >> 3) & 1)), which makes
+// the transposing reads of two 16-lane groups at once conflict-free), then X
+// slab [16 rows][64 k] (granule c of row r at c ^ (r & 7)), then 2 KiB that
+// waves 2 and 3 fill with a second copy of X so every wave issues the same
+// number of copies per slab.
+namespace {
+
+constexpr int SA_BN = 256, SA_BK = 64, SA_NT = 256, SA_STAGES = 4;
+constexpr int SA_W_BYTES = SA_BK * SA_BN * 2;        // 32 KiB
+constexpr int SA_X_BYTES = 16 * SA_BK * 2;           // 2 KiB
+constexpr int SA_STAGE_BYTES = SA_W_BYTES + 2 * SA_X_BYTES;
+constexpr int SA_COPIES = 9;                         // 1 KiB copies per wave per slab
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__host__ __device__ constexpr int swz_w(int r)
+{
+    return ((r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 10 : 12) ^ (2 * ((r >> 3) & 1));
+}
+
+template <int N>
+__device__ __forceinline__ void sa_wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void sa_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+} // namespace
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p, int k_chunk,
+                                                                     int splits, float *ws,
+                                                                     int *counters)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[SA_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[SA_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[SA_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[SA_STAGE_BYTES];
+    __shared__ int s_last;
+    auto stage = [&](auto sidx) -> unsigned char * {
+        constexpr int S = decltype(sidx)::value;
+        if constexpr (S == 0)
+            return st0;
+        else if constexpr (S == 1)
+            return st1;
+        else if constexpr (S == 2)
+            return st2;
+        else
+            return st3;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile_n = blockIdx.x / splits;
+    const int split = blockIdx.x - tile_n * splits;
+    const int n0 = tile_n * SA_BN;
+    const int M = p.M, N = p.N;
+    const int kbeg = split * k_chunk;
+    const int slabs = (min(p.K, kbeg + k_chunk) - kbeg) / SA_BK; // a multiple of 4
+    const unsigned short *W = p.B[0];
+
+    // copies: W copy c (0..7) of this wave fills rows 2q, 2q+1 (q = 8 wave + c... /4)
+    // -> lane: row 2q + lane/32, granule (lane%32) ^ swz_w(row).
+    const unsigned short *gw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int q = wave * 8 + c;
+        const int r = 2 * q + (lane >> 5);
+        gw[c] = W + (int64_t)(kbeg + r) * p.ldb + n0 + ((lane & 31) ^ swz_w(r)) * 8;
+    }
+    // X copy: rows 8 (wave & 1) + lane/8 (clamped to M-1: rows >= M only feed
+    // output rows that are never stored), granule (lane%8) ^ (row & 7).
+    const int xr = 8 * (wave & 1) + (lane >> 3);
+    const unsigned short *gx =
+        p.A + (int64_t)min(xr, M - 1) * p.lda + kbeg + (((lane & 7) ^ (xr & 7)) * 8);
+    const int64_t w_step = (int64_t)SA_BK * p.ldb;
+
+    auto copy = [&](int s, unsigned char *st, int c) {
+        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
+        if (c < 8) {
+            const unsigned dst = lds + (wave * 8 + c) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gw[c] + s * w_step), "{m0}"(dst)
+                         : "memory");
+        } else {
+            const unsigned dst = lds + SA_W_BYTES + wave * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gx + s * SA_BK), "{m0}"(dst)
+                         : "memory");
+        }
+    };
+
+    // fragments: wave w owns columns 64 w .. 64 w + 63 (4 blocks of 16).
+    // W fragment of block j, 32-deep half kk, read half h: 16-lane group g,
+    // jj = lane % 16: row 32 kk + 8 g + 4 h + jj/4, column 64 w + 16 j + 4 (jj%4).
+    int w_off[4][2][2];
+    {
+        const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 32 * kk + 8 * g + 4 * h + (jj >> 2);
+                    const int col = wave * 64 + 16 * j + 4 * (jj & 3);
+                    w_off[j][kk][h] = r * 512 + (((col >> 3) ^ swz_w(r)) * 16) + (col & 7) * 2;
+                }
+    }
+    // X fragment of half kk: row lane % 16, granule 4 kk + lane / 16.
+    int x_off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int r = lane & 15;
+        x_off[kk] = SA_W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
+    }
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const unsigned char *st) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 xf = *reinterpret_cast<const u32x4 *>(st + x_off[kk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x2 lo = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                               (lds_s16x4 *)(st + w_off[j][kk][0])));
+                const u32x2 hi = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                               (lds_s16x4 *)(st + w_off[j][kk][1])));
+                acc[j] = mfma16x16x32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, xf, acc[j]);
+            }
+        }
+    };
+
+    // slab s: wait for its copies (those of s+1, s+2 may stay in flight),
+    // barrier, copy slab s+3 into the stage slab s-1 used (clamped past the
+    // end: repeats the last slab into a stage nobody reads), compute.
+    auto step = [&](int s, auto sidx) {
+        constexpr int S = decltype(sidx)::value;
+        sa_wait_vmcnt<2 * SA_COPIES>();
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        sa_barrier();
+        const int sc = min(s + 3, slabs - 1);
+        unsigned char *dst = stage(std::integral_constant<int, (S + 3) % 4>{});
+#pragma unroll
+        for (int c = 0; c < SA_COPIES; ++c)
+            copy(sc, dst, c);
+        compute(stage(sidx));
+    };
+#pragma unroll
+    for (int c = 0; c < SA_COPIES; ++c)
+        copy(0, st0, c);
+#pragma unroll
+    for (int c = 0; c < SA_COPIES; ++c)
+        copy(min(1, slabs - 1), st1, c);
+#pragma unroll
+    for (int c = 0; c < SA_COPIES; ++c)
+        copy(min(2, slabs - 1), st2, c);
+    for (int s = 0; s < slabs; s += 4) {
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
+        step(s + 2, std::integral_constant<int, 2>{});
+        step(s + 3, std::integral_constant<int, 3>{});
+    }
+    sa_wait_vmcnt<0>();
+
+    // Lane l holds Y[m = l % 16][n = 64 w + 16 j + 4 (l / 16) + r] in acc[j][r].
+    const int m = lane & 15;
+    if (splits == 1) {
+        if (m < M) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wave * 64 + 16 * j + 4 * (lane >> 4);
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = acc[j][r];
+                    if (p.bias != nullptr)
+                        x += from_bits<DT>(p.bias[n + r]);
+                    v[r] = activate<ACT>(x);
+                }
+                u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
+            }
+        }
+        return;
+    }
+
+    // Split-K: partials go to ws[split][m][n] with device-coherent stores
+    // (they bypass the XCD-local L2 state), the stores are waited for, then
+    // one atomic per workgroup counts the split in.  The workgroup that sees
+    // the count reach splits-1 reads all partials with device-coherent loads,
+    // sums them in split order 0..splits-1, applies the epilogue, stores Y
+    // and resets the counter.
+    const int64_t ws_ld = (int64_t)N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wave * 64 + 16 * j + 4 * (lane >> 4);
+        float *dst = ws + ((int64_t)split * 16 + m) * ws_ld + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(dst + r, acc[j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sa_wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == splits - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+
+    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15
+    const int rm = tid >> 4;
+    const int cn = n0 + (tid & 15) * 16;
+    float sum[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        sum[i] = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+        const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            sum[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (rm < M) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x = sum[i];
+            if (p.bias != nullptr)
+                x += from_bits<DT>(p.bias[cn + i]);
+            v[i] = activate<ACT>(x);
+        }
+        unsigned short *cp = p.C[0] + (int64_t)rm * p.ldc + cn;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            u32x4 o = {pack2<DT>(v[8 * q + 0], v[8 * q + 1]), pack2<DT>(v[8 * q + 2], v[8 * q + 3]),
+                       pack2<DT>(v[8 * q + 4], v[8 * q + 5]), pack2<DT>(v[8 * q + 6], v[8 * q + 7])};
+            *reinterpret_cast<u32x4 *>(cp + 8 * q) = o;
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 SkinnyPlan plan_skinny(int M, int N, int K)
 {
     (void)M;
     SkinnyPlan pl;
+    if (N % SA_BN == 0 && K % (SA_STAGES * SA_BK) == 0) {
+        // streaming kernel: about one workgroup per CU
+        pl.streaming = 1;
+        pl.bn = SA_BN;
+        pl.n_tiles = N / SA_BN;
+        const int quanta = K / (SA_STAGES * SA_BK);
+        int splits = (256 + pl.n_tiles / 2) / pl.n_tiles;
+        splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
+        const int per = (quanta + splits - 1) / splits;
+        pl.k_chunk = per * SA_STAGES * SA_BK;
+        pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
+        return pl;
+    }
+    pl.streaming = 0;
     pl.bn = SK_BN;
     pl.n_tiles = (N + SK_BN - 1) / SK_BN;
     const int kslabs = (K + SK_BK - 1) / SK_BK;
@@ -302,8 +588,10 @@ SkinnyPlan plan_skinny(int M, int N, int K)
 size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N)
 {
     (void)M;
-    (void)N;
-    return pl.splits > 1 ? (size_t)pl.splits * 16 * (size_t)pl.n_tiles * SK_BN : 0;
+    if (pl.splits <= 1)
+        return 0;
+    return pl.streaming ? (size_t)pl.splits * 16 * (size_t)N
+                        : (size_t)pl.splits * 16 * (size_t)pl.n_tiles * SK_BN;
 }
 
 hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &pl, float *ws,
@@ -311,6 +599,24 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
 {
     constexpr int D = SK_DEPTH;
     dim3 grid(pl.n_tiles * pl.splits), block(SK_NT);
+    if (pl.streaming) {
+#define TG_SA(DT_, ACT_)                                                                         \
+    hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_>), grid, dim3(SA_NT), 0, s, a,          \
+                       pl.k_chunk, pl.splits, ws, counters)
+        if (dt == DT_F16) {
+            if (act == ACT_GELU)
+                TG_SA(DT_F16, ACT_GELU);
+            else
+                TG_SA(DT_F16, ACT_NONE);
+        } else {
+            if (act == ACT_GELU)
+                TG_SA(DT_BF16, ACT_GELU);
+            else
+                TG_SA(DT_BF16, ACT_NONE);
+        }
+#undef TG_SA
+        return hipGetLastError();
+    }
     const bool fast = a.N % SK_BN == 0 && a.K % (D * SK_BK) == 0 && pl.k_chunk % (D * SK_BK) == 0 &&
                       (int64_t)a.ldb * SK_BK * 2 < (1ll << 30) && (int64_t)a.lda * 16 * 2 < (1ll << 30);
 #define TG_SK(DT_, ACT_, EDGE_)                                                                  \
