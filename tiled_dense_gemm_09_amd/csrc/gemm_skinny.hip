@@ -18,6 +18,8 @@
 // last sums the partials in split order 0, 1, ..., S-1 (so the result does
 // not depend on arrival order), applies bias + activation, rounds, stores Y,
 // and resets the counter to zero for the next call.
+#include <cstdlib>
+
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -488,20 +490,21 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         return;
     }
 
-    // Split-K: partials go to ws[split][m][n] with device-coherent stores
-    // (they bypass the XCD-local L2 state), the stores are waited for, then
-    // one atomic per workgroup counts the split in.  The workgroup that sees
-    // the count reach splits-1 reads all partials with device-coherent loads,
-    // sums them in split order 0..splits-1, applies the epilogue, stores Y
-    // and resets the counter.
+    // Split-K: partials go to ws[split][m][n] with device-coherent 16-byte
+    // stores (sc1: written through to the device coherence point, since the
+    // XCDs' L2 caches are not coherent with each other), the stores are
+    // waited for, and one atomic per workgroup counts the split in.  The
+    // workgroup that sees the count reach splits-1 reads the partials with
+    // device-coherent loads (sc1), sums them in split order 0..splits-1
+    // (independent of arrival order), applies the epilogue, stores Y and
+    // resets the counter.  Both sides use device-scope coherent accesses, so
+    // no cache-wide writeback or invalidate is needed.
     const int64_t ws_ld = (int64_t)N;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + wave * 64 + 16 * j + 4 * (lane >> 4);
         float *dst = ws + ((int64_t)split * 16 + m) * ws_ld + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            __hip_atomic_store(dst + r, acc[j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(acc[j]) : "memory");
     }
     sa_wait_vmcnt<0>();
     __syncthreads();
@@ -514,18 +517,47 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     if (!s_last)
         return;
 
-    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15
+    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15; four
+    // splits per round: 16 loads in flight, then added in split order
+    // (indices past the last split repeat it and are not added)
     const int rm = tid >> 4;
     const int cn = n0 + (tid & 15) * 16;
     float sum[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         sum[i] = 0.f;
-    for (int sp = 0; sp < splits; ++sp) {
-        const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
+    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+        f32x4 v[4][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            sum[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int u = 0; u < 4; ++u) {
+            const int sp = min(sp0 + u, splits - 1);
+            const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                             : "=v"(v[u][q])
+                             : "v"(src + 4 * q)
+                             : "memory");
+        }
+        // the loads above are invisible to the compiler's wait tracking: wait
+        // here and pass the values through so nothing reads them earlier
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
+                       "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
+                       "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[2][2]), "+v"(v[2][3]),
+                       "+v"(v[3][0]), "+v"(v[3][1]), "+v"(v[3][2]), "+v"(v[3][3])
+                     :
+                     : "memory");
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (sp0 + u < splits) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sum[4 * q + r] += v[u][q][r];
+            }
+        }
     }
     if (rm < M) {
         float v[16];
@@ -548,10 +580,198 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Column-tile variant (N a multiple of 32 with at least 128 tiles, K a
+// multiple of 256): no cross-workgroup communication at all.  Workgroup t
+// owns 32 columns of W over the whole of K; its 4 waves each stream one
+// quarter of K through a private LDS ring with direct-to-LDS copies (five
+// 64-deep slabs ahead of use, no barriers in the loop since every wave only
+// reads what it copied itself), multiply on v_mfma_f32_16x16x32, and the
+// four partial sums are added in LDS in wave order (deterministic).  Tiles
+// are placed XCD-contiguously so neighbouring 64-byte column pieces, which
+// share 128-byte cache lines, are fetched by one L2.
+//
+// Ring slot (6 KiB): W [64 k][32 n] (64-byte rows, 16-byte granule c of row
+// r at c ^ 2 (((r >> 1) ^ (r >> 3)) & 1), conflict-free for the transposing
+// reads), then X [16 rows][64 k] (granule c of row r at c ^ (r & 7)).
+namespace {
+
+constexpr int SC_BN = 32, SC_BK = 64, SC_NT = 256, SC_SLOTS = 6;
+constexpr int SC_W_BYTES = SC_BK * SC_BN * 2; // 4 KiB
+constexpr int SC_X_BYTES = 16 * SC_BK * 2;    // 2 KiB
+constexpr int SC_SLOT_BYTES = SC_W_BYTES + SC_X_BYTES;
+constexpr int SC_COPIES = SC_SLOT_BYTES / 1024; // 6 per slab
+constexpr int SC_AHEAD = SC_SLOTS - 1;          // slabs in flight beyond the current one
+
+__host__ __device__ constexpr int swz_c(int r) { return 2 * (((r >> 1) ^ (r >> 3)) & 1); }
+
+} // namespace
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, int n_tiles)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[4 * SC_SLOTS * SC_SLOT_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const TileCoord tc = schedule_tile(1, n_tiles, 1, 1, blockIdx.x);
+    const int n0 = tc.tn * SC_BN;
+    const int M = p.M;
+    const int kq = p.K / 4;           // this wave's quarter of K
+    const int kbase = wave * kq;
+    const int slabs = kq / SC_BK;     // >= 1
+    const unsigned short *W = p.B[0];
+    unsigned char *my = ring + wave * SC_SLOTS * SC_SLOT_BYTES;
+    const unsigned my_lds = (unsigned)(uintptr_t)(lds_void *)my;
+
+    // copy c < 4: W rows 16c + lane/4 of the slab, granule (lane%4) ^ swz_c(row);
+    // copy 4, 5: X rows 8 (c-4) + lane/8 (clamped to M-1), granule (lane%8) ^ (row&7)
+    const int wr = lane >> 2;
+    const unsigned short *gw = W + (int64_t)(kbase + wr) * p.ldb + n0;
+    int wg[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        wg[c] = ((lane & 3) ^ swz_c(16 * c + wr)) * 8;
+    const unsigned short *gx[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int r = 8 * c + (lane >> 3);
+        gx[c] = p.A + (int64_t)min(r, M - 1) * p.lda + kbase + (((lane & 7) ^ (r & 7)) * 8);
+    }
+    const int64_t ldb16 = (int64_t)16 * p.ldb;
+
+    auto issue = [&](int s) {
+        const unsigned slot = my_lds + (s % SC_SLOTS) * SC_SLOT_BYTES;
+        const unsigned short *w0 = gw + (int64_t)s * SC_BK * p.ldb;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(w0 + c * ldb16 + wg[c]),
+                         "{m0}"(slot + c * 1024)
+                         : "memory");
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gx[c] + s * SC_BK),
+                         "{m0}"(slot + SC_W_BYTES + c * 1024)
+                         : "memory");
+        }
+    };
+
+    // fragment offsets within a slot
+    int w_off[2][2][2]; // [nb][kk][h]
+    {
+        const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 32 * kk + 8 * g + 4 * h + (jj >> 2);
+                    const int col = 16 * nb + 4 * (jj & 3);
+                    w_off[nb][kk][h] = r * 64 + (((col >> 3) ^ swz_c(r)) * 16) + (col & 7) * 2;
+                }
+    }
+    int x_off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int r = lane & 15;
+        x_off[kk] = SC_W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
+    }
+
+    f32x4 acc[2];
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: SC_AHEAD slabs in flight (clamped repeats past the end land
+    // in slots that are never read)
+#pragma unroll
+    for (int a = 0; a < SC_AHEAD; ++a)
+        issue(min(a, slabs - 1));
+    for (int s = 0; s < slabs; ++s) {
+        // the copies of slabs s+1 .. s+SC_AHEAD-1 may stay in flight
+        __builtin_amdgcn_s_waitcnt(((SC_AHEAD - 1) * SC_COPIES & 15) |
+                                   (((SC_AHEAD - 1) * SC_COPIES >> 4) << 14) | 0x0F70);
+        asm volatile("" ::: "memory");
+        const unsigned char *st = my + (s % SC_SLOTS) * SC_SLOT_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 xf = *reinterpret_cast<const u32x4 *>(st + x_off[kk]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const u32x2 lo = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                               (lds_s16x4 *)(st + w_off[nb][kk][0])));
+                const u32x2 hi = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                               (lds_s16x4 *)(st + w_off[nb][kk][1])));
+                acc[nb] = mfma16x16x32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, xf, acc[nb]);
+            }
+        }
+        // this slab's reads are done before its slot is refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        issue(min(s + SC_AHEAD, slabs - 1));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): no copy still writing LDS
+    __syncthreads();
+
+    // sum the four K-quarters in wave order; lane l holds
+    // Y[m = l % 16][n = 16 nb + 4 (l / 16) + r] in acc[nb][r]
+    f32x4 *part = reinterpret_cast<f32x4 *>(ring);
+    if (wave != 0) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            part[((wave - 1) * 2 + nb) * 64 + lane] = acc[nb];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int m = lane & 15;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            f32x4 v = acc[nb];
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                const f32x4 q = part[(w * 2 + nb) * 64 + lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] += q[r];
+            }
+            const int n = n0 + 16 * nb + 4 * (lane >> 4);
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = v[r];
+                if (p.bias != nullptr)
+                    x += from_bits<DT>(p.bias[n + r]);
+                o[r] = activate<ACT>(x);
+            }
+            if (m < M) {
+                u32x2 ov = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+                *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = ov;
+            }
+        }
+    }
+}
+
 SkinnyPlan plan_skinny(int M, int N, int K)
 {
     (void)M;
     SkinnyPlan pl;
+    // The column-tile kernel needs no cross-workgroup reduction and is the
+    // fastest when W is cache-resident, but its 64-byte row pieces stream
+    // from HBM less efficiently than the split-K kernel's 512-byte pieces;
+    // TG_SKINNY_COLS=1 selects it.
+    const char *cols = getenv("TG_SKINNY_COLS");
+    if (N % SC_BN == 0 && N / SC_BN >= 128 && K % (4 * SC_BK) == 0 && cols && cols[0] == '1') {
+        pl.streaming = 2;
+        pl.bn = SC_BN;
+        pl.n_tiles = N / SC_BN;
+        pl.splits = 1;
+        pl.k_chunk = K;
+        return pl;
+    }
     if (N % SA_BN == 0 && K % (SA_STAGES * SA_BK) == 0) {
         // streaming kernel: about one workgroup per CU
         pl.streaming = 1;
@@ -559,6 +779,9 @@ SkinnyPlan plan_skinny(int M, int N, int K)
         pl.n_tiles = N / SA_BN;
         const int quanta = K / (SA_STAGES * SA_BK);
         int splits = (256 + pl.n_tiles / 2) / pl.n_tiles;
+        const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
+        if (force && atoi(force) > 0)
+            splits = atoi(force);
         splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
         const int per = (quanta + splits - 1) / splits;
         pl.k_chunk = per * SA_STAGES * SA_BK;
@@ -599,6 +822,23 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
 {
     constexpr int D = SK_DEPTH;
     dim3 grid(pl.n_tiles * pl.splits), block(SK_NT);
+    if (pl.streaming == 2) {
+#define TG_SC(DT_, ACT_)                                                                         \
+    hipLaunchKernelGGL((gemm_skinny_cols_kernel<DT_, ACT_>), grid, dim3(SC_NT), 0, s, a, pl.n_tiles)
+        if (dt == DT_F16) {
+            if (act == ACT_GELU)
+                TG_SC(DT_F16, ACT_GELU);
+            else
+                TG_SC(DT_F16, ACT_NONE);
+        } else {
+            if (act == ACT_GELU)
+                TG_SC(DT_BF16, ACT_GELU);
+            else
+                TG_SC(DT_BF16, ACT_NONE);
+        }
+#undef TG_SC
+        return hipGetLastError();
+    }
     if (pl.streaming) {
 #define TG_SA(DT_, ACT_)                                                                         \
     hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_>), grid, dim3(SA_NT), 0, s, a,          \

@@ -216,8 +216,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         }
         err = tg::launch_skinny(kdt, kact, a, pl, ws, counters, s);
         char detail[48];
-        snprintf(detail, sizeof detail, "%s_bn%d_split%dx%d", pl.streaming ? "_stream" : "",
-                 pl.bn, pl.splits, pl.k_chunk);
+        snprintf(detail, sizeof detail, "%s_bn%d_split%dx%d",
+                 pl.streaming == 2 ? "_cols" : (pl.streaming ? "_stream" : ""), pl.bn, pl.splits,
+                 pl.k_chunk);
         set_last("skinny", detail);
     } else if (tg::async_eligible(a) && !force_tiled &&
                (M / 256) * (N / 256) * n_mat >= 128) {

@@ -47,7 +47,7 @@ hipError_t launch_async(int dt, int act, const GemmArgs &a, int group_m, hipStre
 // entries that must be zero before the first call; the kernel leaves them
 // zero.
 struct SkinnyPlan {
-    int streaming; // 1: direct-to-LDS streaming kernel, 0: register-staged kernel
+    int streaming; // 2: column-tile kernel, 1: split-K streaming kernel, 0: register-staged kernel
     int bn;       // columns per workgroup
     int splits;   // K splits
     int k_chunk;  // K per split (multiple of the slab depth)
