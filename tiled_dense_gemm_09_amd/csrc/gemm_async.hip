@@ -245,14 +245,27 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     // it), so every copy has three steps of MFMA work to land, and every LDS
     // read overlaps MFMAs.  K is a multiple of 4 steps, so the loop body is
     // the 4 stages with their arrays named statically.
+    // The 8 copies of a step are spread over two half-steps: copies 0-3 of
+    // step k+4 go out with the MFMAs of h1 of step k, copies 4-7 with the
+    // MFMAs of h0 of step k+1 (stage k stays free until step k+4 reads it),
+    // one copy between MFMAs.  Per step this is still 8 copies, so the wait
+    // count below is unchanged.
     Frag f0, f1;
     auto step = [&](int kt, auto sidx) {
         constexpr int S = decltype(sidx)::value;
         unsigned char *cur = stage(sidx);
         unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
-        read(f1, cur, 1);
-        mma(f0);
-        interleave();
+        unsigned char *prv = stage(std::integral_constant<int, (S + 3) % 4>{});
+        const int kp = min(kt + 3, KT - 1); // second half of the copies of step k+3 (into stage k-1)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            mma_one(f0, q);
+            if (q < 12)
+                read_piece(f1, cur, 1, q);
+            if (q >= 4 && q < 8)
+                copy(kp, prv, q);
+            __builtin_amdgcn_sched_barrier(0); // keep the MFMA / read / copy order
+        }
         // The copies of steps k+2 and k+3 may stay in flight.  The loop body
         // is branch-free: past the last step the copies repeat the last tile
         // (into stages nobody reads any more), so this count always holds.
@@ -265,15 +278,20 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
             mma_one(f1, q);
             if (q < 12)
                 read_piece(f0, nxt, 0, q); // past the last step: harmless reread
-            if (q < 8)
+            if (q < 4)
                 copy(kc, cur, q);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     issue(0, st0);
     issue(1, st1);
     issue(2, st2);
-    issue(3, st3);
-    wait_vmcnt<3 * AS_COPIES>();
+    // step 3: copies 0-3 now, 4-7 in the first half of step 0
+    copy(3, st3, 0);
+    copy(3, st3, 1);
+    copy(3, st3, 2);
+    copy(3, st3, 3);
+    wait_vmcnt<2 * AS_COPIES + 4>();
     stage_barrier();
     read(f0, st0, 0);
     for (int kt = 0; kt < KT; kt += 4) {
@@ -318,8 +336,8 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
                     }
                     u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
                     *reinterpret_cast<u32x2 *>(Cm + (int64_t)m * p.ldc + n) = o;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };

@@ -83,18 +83,20 @@ __host__ __device__ inline bool in_bounds(int64_t rows, int64_t cols, int64_t ro
     return row >= 0 && col >= 0 && row < rows && col < cols;
 }
 
-// tanh form of GELU in FP32.  tanh(u) = 1 - 2 / (1 + e^{2u}); e^{2u} is
-// computed as 2^{2u log2 e} with the hardware base-2 exponential and the
-// division with the hardware reciprocal (about 1 ulp each; the result is
-// rounded to f16/bf16 afterwards).  For large |u| the exponential saturates
-// to 0 or +inf and tanh to -1 or +1.
+// tanh form of GELU in FP32, evaluated through the identity
+//     0.5 x (1 + tanh(u)) = x / (1 + e^{-2u}),   u = sqrt(2/pi) (x + 0.044715 x^3),
+// so one exponential and one reciprocal per value: e^{-2u} = 2^{x (k1 + k2 x^2)}
+// with k1 = -2 sqrt(2/pi) log2(e) and k2 = 0.044715 k1, both on the hardware
+// base-2 exponential and reciprocal (about 1 ulp each; the result is rounded
+// to f16/bf16 afterwards).  For large |x| the exponential saturates to 0 or
+// +inf and the result to x or -0.
 __device__ __forceinline__ float gelu_tanh_f32(float x)
 {
-    const float c = 0.7978845608028654f; // sqrt(2/pi)
-    const float u = c * (x + 0.044715f * x * x * x);
-    const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f); // 2u * log2(e)
-    const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
-    return 0.5f * x * (1.0f + t);
+    const float k1 = -2.302208198144325f;   // -2 sqrt(2/pi) / ln 2
+    const float k2 = -0.1029432395800235f;  // 0.044715 k1
+    const float t = __builtin_fmaf(x * x, k2, k1);
+    const float e = __builtin_amdgcn_exp2f(x * t);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 template <int ACT>
@@ -128,10 +130,20 @@ __device__ __forceinline__ float from_bits(unsigned short b)
         return __builtin_bit_cast(float, (unsigned int)b << 16);
 }
 
+// Two f32 values -> two 16-bit values packed low/high, round to nearest even
+// (one v_cvt_pk_{f16,bf16}_f32 on gfx950).
 template <int DT>
 __device__ __forceinline__ unsigned int pack2(float lo, float hi)
 {
-    return (unsigned int)to_bits<DT>(lo) | ((unsigned int)to_bits<DT>(hi) << 16);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    if constexpr (DT == DT_F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, h2));
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, b2));
+    }
 }
 
 // One 16x16x32 MFMA step: acc += src0 (16 rows x 32 k) * src1 (32 k x 16 cols).
