@@ -30,9 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16/bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "GEMM TFLOP/s + % of MFMA peak (4096³ fp16); GB/s % HBM peak at M=16"
-KERNEL_SOURCES = ["tiled_dense_gemm_09_amd/csrc/gemm_tiled.hip",
-                  "tiled_dense_gemm_09_amd/csrc/gemm_skinny.hip",
+KERNEL_SOURCES = ["tiled_dense_gemm_09_amd/csrc/gemm_async.hip",
                   "tiled_dense_gemm_09_amd/csrc/tg_device.h",
+                  "tiled_dense_gemm_09_amd/csrc/tg_launch.h",
                   "tiled_dense_gemm_09_amd/csrc/tg_api.cpp"]
 
 
@@ -195,7 +195,8 @@ def main():
                    "M": M, "N": N, "K": K, "kernel": kernel},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": (traffic["fetch"] + traffic["write"]) if traffic else None,
+                     "traffic_split": traffic},
         "cpu_baseline": cpu,
         "parity": parity,
         "secondary": extra,
