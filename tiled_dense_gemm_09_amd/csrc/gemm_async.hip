@@ -47,10 +47,8 @@ constexpr int AS_STAGE_BYTES = AS_A_BYTES + AS_B_BYTES;
 constexpr int AS_COPIES = AS_STAGE_BYTES / 1024 / (AS_NT / 64); // 1 KiB copies per wave per step
 
 __host__ __device__ constexpr int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__host__ __device__ constexpr int swz_b(int r)
-{
-    return (r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 10 : 12;
-}
+// {0, 6, 10, 12}[r & 3] as a nibble table (a shift, not a branch chain)
+__host__ __device__ constexpr int swz_b(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
 
 // Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
 // workgroup release fence, which waits for every outstanding direct-to-LDS
@@ -154,14 +152,36 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
             copy(kt, st, c);
     };
 
+    // The accumulators start at bias[n] (or 0): the bias is added once per
+    // output, before the sum over k instead of after it, and its loads and
+    // conversions overlap the first copies instead of lengthening the
+    // epilogue.  Lane l of 32x32 block (i, j) holds columns
+    // n = 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3 (any row).
     f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    if (p.bias != nullptr) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.f;
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 braw = *reinterpret_cast<const u32x2 *>(
+                    p.bias + n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float b = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i][j][4 * g + e] = b;
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.f;
+    }
 
     // ---- fragment addressing (byte offsets within a stage)
     // A fragment i: row wave_m*128 + i*32 + lane%32, k granule 2kk + lane/32.
@@ -217,22 +237,6 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     auto mma_one = [&](const Frag &f, int q) {
         const int i = q >> 2, j = q & 3;
         acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
-    };
-    auto mma = [&](const Frag &f) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            mma_one(f, q);
-    };
-
-    // Scheduling pattern for a read batch overlapped with an MFMA batch:
-    // alternate one MFMA and one LDS read (12 reads, 16 MFMAs).
-    auto interleave = [&]() {
-#pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
 
     // ---- pipeline.  Each step k (32 deep = two 16-deep halves h0, h1):
@@ -300,51 +304,51 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
         step(kt + 2, std::integral_constant<int, 2>{});
         step(kt + 3, std::integral_constant<int, 3>{});
     }
-    // no copy may still be writing this workgroup's LDS when it exits
+    // Every copy has landed (this wave's, then everybody's after the
+    // barrier) and every wave has finished reading the stages, so the LDS is
+    // free for the epilogue.
     wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
 
-    // ---- epilogue (as in gemm_tiled): lane l of a 32x32 block holds row
-    // m = l % 32 and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.
-    auto epilogue = [&](auto has_bias) {
-        constexpr bool HB = decltype(has_bias)::value;
-        // bias[n..n+3] for every (j, g) column group of this lane, loaded up
-        // front so the 16 loads overlap instead of waiting one by one
-        u32x2 braw[4][4];
-        if constexpr (HB) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    braw[j][g] = *reinterpret_cast<const u32x2 *>(
-                        p.bias + n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4);
-        }
+    // ---- epilogue.  Lane l of a 32x32 accumulator block holds row m = l % 32
+    // and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
+    // activation and rounding happen there; the rounded 128 x 128 tile of
+    // the wave is then restaged through LDS (the wave's own 32 KiB stage,
+    // 256-byte rows, 16-byte granule c of row r at c ^ (r % 16)) so that each
+    // global store writes four whole 256-byte row segments instead of 32
+    // scattered 16-byte pieces.
+    unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wave_m * 128 + i * 32 + (lane & 31);
+            const int r = i * 32 + (lane & 31);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
                     float v[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = acc[i][j][4 * g + r];
-                        if constexpr (HB)
-                            x += from_bits<DT>((unsigned short)(braw[j][g][r >> 1] >> (16 * (r & 1))));
-                        v[r] = activate<ACT>(x);
-                    }
-                    u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                    *reinterpret_cast<u32x2 *>(Cm + (int64_t)m * p.ldc + n) = o;
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = activate<ACT>(acc[i][j][4 * g + e]);
+                    const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                    const int c = (4 * j + g) ^ (r & 15);
+                    *reinterpret_cast<u32x2 *>(ep + r * 256 + c * 16 + (lane >> 5) * 8) = o;
                 }
             }
         }
-    };
-    if (p.bias != nullptr)
-        epilogue(std::true_type{});
-    else
-        epilogue(std::false_type{});
+        // each lane reads back granule lane % 16 of rows 4t + lane / 16 (its
+        // own wave's writes, so no barrier) and stores it
+        unsigned short *crow = Cm + (int64_t)(m0 + wave_m * 128) * p.ldc + n0 + wave_n * 128 +
+                               (lane & 15) * 8;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int r = 4 * t + (lane >> 4);
+            const u32x4 v =
+                *reinterpret_cast<const u32x4 *>(ep + r * 256 + (((lane & 15) ^ (r & 15)) * 16));
+            *reinterpret_cast<u32x4 *>(crow + (int64_t)r * p.ldc) = v;
+        }
+    }
 }
 
 bool async_eligible(const GemmArgs &a)
