@@ -113,7 +113,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["main", "qkv", "square8192", "skinny", "small", "copy"],
+    ap.add_argument("--only", choices=["main", "plain", "qkv", "square8192", "skinny", "small",
+                                       "vendor", "copy"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -209,6 +210,19 @@ def run_secondary(args, torch, inputs, tg):
     steps = max(10, min(args.steps, 300))
     warm = max(3, min(args.warmup, 50))
 
+    if args.only in (None, "plain"):
+        # the headline product without its epilogue, so the epilogue's cost shows
+        p = inputs.config_problem("f16_4096_gelu")
+        A, B = dev(p["A"], 1), dev(p["B"], 1)
+        C = torch.empty((p["M"], p["N"]), dtype=torch.float16, device="cuda")
+        ms = time_launches(lambda: tg.gemm(A, B, out=C), steps, warm)
+        tf = 2.0 * p["M"] * p["N"] * p["K"] / (ms * 1e-3) / 1e12
+        out["f16_4096x4096x4096_no_epilogue"] = {
+            "ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+            "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4), "kernel": tg.last_kernel()}
+        log("  ", out["f16_4096x4096x4096_no_epilogue"])
+        del A, B, C
+
     if args.only in (None, "qkv"):
         q = inputs.config_problem("bf16_qkv")
         X = dev(q["X"], 2)
@@ -265,6 +279,22 @@ def run_secondary(args, torch, inputs, tg):
             "kernel": tg.last_kernel()}
         log("  ", out["bf16_skinny_16x8192x8192"])
         del X, Ws, Y
+
+    if args.only in (None, "vendor"):
+        # context only: the ROCm BLAS library GEMM (torch.matmul) on the same
+        # operands, no epilogue; nothing of the measured path runs through it
+        ctx = {}
+        for name, dtc in (("f16_4096_gelu", 1), ("bf16_8192", 2)):
+            p = inputs.config_problem(name)
+            A, B = dev(p["A"], dtc), dev(p["B"], dtc)
+            C = torch.empty((p["M"], p["N"]), dtype=A.dtype, device="cuda")
+            ms = time_launches(lambda: torch.matmul(A, B, out=C), steps, warm)
+            tf = 2.0 * p["M"] * p["N"] * p["K"] / (ms * 1e-3) / 1e12
+            ctx["%s_%dx%dx%d" % ("f16" if dtc == 1 else "bf16", p["M"], p["N"], p["K"])] = {
+                "ms": round(ms, 5), "TFLOP/s": round(tf, 1)}
+            del A, B, C
+        out["context_rocm_blas_torch_matmul"] = ctx
+        log("  ", ctx)
 
     if args.only in (None, "small"):
         for name in ("f16_256", "f16_1024"):
