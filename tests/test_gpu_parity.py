@@ -64,8 +64,8 @@ def test_small_config_random_full(tg, name):
     p = inputs.config_problem(name)
     say("case", name, "random", p["M"], p["N"], p["K"])
     bits, kern = run(tg, p)
-    f64, _ = oracle.gemm(p["dt"], p["A"], p["B"])
-    err = util.check_tol(p["dt"], bits, f64, name)
+    f64, rbits = oracle.gemm(p["dt"], p["A"], p["B"])
+    err = util.check_tol(p["dt"], bits, f64, name, ref_bits=rbits)
     say("  kernel", kern, "max abs err", err)
 
 
@@ -95,8 +95,8 @@ def test_bias_gelu_medium_full(tg):
                        a_scale=0.2, b_scale=0.2)
     say("case bias+gelu 512x768x640")
     bits, _ = run(tg, p)
-    f64, _ = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
-    util.check_tol(F16, bits, f64, "bias+gelu")
+    f64, rbits = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits, f64, "bias+gelu", ref_bits=rbits)
 
 
 def test_gelu_config_full_size_sampled(tg):
@@ -105,8 +105,8 @@ def test_gelu_config_full_size_sampled(tg):
     bits, kern = run(tg, p)
     say("  kernel", kern)
     ii, jj = util.sample_indices(p["M"], p["N"], 3000, seed=3)
-    f64, _ = oracle.gemm_sample(F16, p["A"], p["B"], ii, jj, p["bias"], oracle.ACT_GELU_TANH)
-    util.check_tol(F16, bits[ii, jj], f64, "f16_4096_gelu")
+    f64, rbits = oracle.gemm_sample(F16, p["A"], p["B"], ii, jj, p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits[ii, jj], f64, "f16_4096_gelu", ref_bits=rbits)
     assert np.all(np.isfinite(util.decode(F16, bits)))
 
 
@@ -140,7 +140,7 @@ def test_qkv_medium_full_and_equal_to_three_gemms(tg):
     X, Ws, outs = run_qkv(tg, q)
     refs = oracle.gemm_qkv(BF16, q["X"], *q["W"])
     for t in range(3):
-        util.check_tol(BF16, outs[t], refs[t][0], "qkv[%d]" % t)
+        util.check_tol(BF16, outs[t], refs[t][0], "qkv[%d]" % t, ref_bits=refs[t][1])
         single = util.to_bits(tg.gemm(X, Ws[t]))
         torch.cuda.synchronize()
         util.check_exact(outs[t], single, "qkv[%d] vs tg_gemm" % t)
@@ -152,8 +152,8 @@ def test_qkv_config_sampled(tg):
     _, _, outs = run_qkv(tg, q)
     ii, jj = util.sample_indices(q["M"], q["N"], 2000, seed=5)
     for t in range(3):
-        f64, _ = oracle.gemm_sample(BF16, q["X"], q["W"][t], ii, jj)
-        util.check_tol(BF16, outs[t][ii, jj], f64, "qkv config [%d]" % t)
+        f64, rbits = oracle.gemm_sample(BF16, q["X"], q["W"][t], ii, jj)
+        util.check_tol(BF16, outs[t][ii, jj], f64, "qkv config [%d]" % t, ref_bits=rbits)
 
 
 def test_qkv_config_integer_exact_sampled(tg):
@@ -173,8 +173,8 @@ def test_skinny_config_full(tg):
     bits, kern = run(tg, p)
     say("  kernel", kern)
     assert kern.startswith("skinny")
-    f64, _ = oracle.gemm(BF16, p["A"], p["B"])
-    util.check_tol(BF16, bits, f64, "skinny")
+    f64, rbits = oracle.gemm(BF16, p["A"], p["B"])
+    util.check_tol(BF16, bits, f64, "skinny", ref_bits=rbits)
 
 
 def test_skinny_config_integer_exact_and_deterministic(tg):
@@ -203,8 +203,8 @@ def test_square_8192_sampled(tg):
     bits, kern = run(tg, p)
     say("  kernel", kern)
     ii, jj = util.sample_indices(p["M"], p["N"], 2000, seed=7)
-    f64, _ = oracle.gemm_sample(BF16, p["A"], p["B"], ii, jj)
-    util.check_tol(BF16, bits[ii, jj], f64, "bf16_8192")
+    f64, rbits = oracle.gemm_sample(BF16, p["A"], p["B"], ii, jj)
+    util.check_tol(BF16, bits[ii, jj], f64, "bf16_8192", ref_bits=rbits)
 
 
 def test_square_8192_integer_exact_sampled(tg):
@@ -258,7 +258,7 @@ def test_ragged_shapes_with_poisoned_padding(tg, dt, M, N, K, integer):
     if integer:
         util.check_exact(full[:M, :N], ref, "ragged exact")
     else:
-        util.check_tol(dt, full[:M, :N], f64, "ragged")
+        util.check_tol(dt, full[:M, :N], f64, "ragged", ref_bits=ref)
     assert np.all(full[:M, N:] == NAN_BITS[dt]), "wrote into the pitch padding"
     assert np.all(full[M:, :] == NAN_BITS[dt]), "wrote below the last row"
 
@@ -274,8 +274,8 @@ def test_unaligned_operands_take_the_reported_fallback(tg):
     C = tg.gemm(A, B, bias=bias, act="gelu_tanh")
     torch.cuda.synchronize()
     assert tg.last_kernel().startswith("generic_fma (unaligned")
-    f64, _ = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
-    util.check_tol(dt, util.to_bits(C), f64, "generic")
+    f64, rbits = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(dt, util.to_bits(C), f64, "generic", ref_bits=rbits)
 
 
 def test_k_zero_gives_activated_bias(tg):
@@ -287,9 +287,9 @@ def test_k_zero_gives_activated_bias(tg):
     B = torch.empty((0, 40), dtype=torch.bfloat16, device="cuda")
     C = tg.gemm(A, B, bias=bias, act="gelu_tanh")
     torch.cuda.synchronize()
-    f64, _ = oracle.gemm(dt, np.zeros((24, 0), np.uint16), np.zeros((0, 40), np.uint16),
+    f64, rbits = oracle.gemm(dt, np.zeros((24, 0), np.uint16), np.zeros((0, 40), np.uint16),
                          bias_bits, oracle.ACT_GELU_TANH)
-    util.check_tol(dt, util.to_bits(C), f64, "K=0")
+    util.check_tol(dt, util.to_bits(C), f64, "K=0", ref_bits=rbits)
 
 
 def test_dispatch_choices(tg):

@@ -29,8 +29,33 @@ def decode(dt, bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_tol(dt, gpu_bits, ref_f64, what=""):
-    """|gpu - oracle| <= 1e-2 + 5e-3 |oracle| for every element."""
+def ulp_distance(gpu_bits, ref_bits):
+    """Distance in units in the last place between two arrays of 16-bit
+    sign-magnitude patterns (f16 or bf16): the patterns are mapped to ordered
+    integers, so +0 and -0 coincide and neighbours differ by one."""
+    def ordered(b):
+        b = np.asarray(b, np.uint16).astype(np.int64)
+        mag = b & 0x7FFF
+        return np.where(b & 0x8000, -mag, mag)
+    return np.abs(ordered(gpu_bits) - ordered(ref_bits))
+
+
+# FP32 accumulation in another order than the oracle's double sum (and the
+# FP32 epilogue) moves an output to a neighbouring representable value when a
+# rounding boundary lies between the two results; where the sum nearly
+# cancels, the output is small and its steps are fine, so the distance in
+# steps can be large while the error stays far inside the tolerance.  What
+# the rounding itself must satisfy is that nearly every element rounds to the
+# oracle's bits: a truncating or otherwise wrong rounding would match about
+# half of them.
+MIN_EXACT_FRACTION = 0.98
+
+
+def check_tol(dt, gpu_bits, ref_f64, what="", ref_bits=None):
+    """|gpu - oracle| <= 1e-2 + 5e-3 |oracle| for every element; given the
+    oracle's rounded bits, also at least MIN_EXACT_FRACTION of the elements
+    equal to them.  Prints max absolute / relative error and the histogram of
+    distances in ulps."""
     g = decode(dt, gpu_bits)
     err = np.abs(g - ref_f64)
     bound = 1e-2 + 5e-3 * np.abs(ref_f64)
@@ -40,7 +65,22 @@ def check_tol(dt, gpu_bits, ref_f64, what=""):
         raise AssertionError("%s: %d of %d elements out of tolerance; first %s; gpu %s oracle %s"
                              % (what, int(bad.sum()), bad.size, idx.tolist(),
                                 g[tuple(idx.T)].tolist(), ref_f64[tuple(idx.T)].tolist()))
-    return float(err.max()) if err.size else 0.0
+    if err.size == 0:
+        return 0.0
+    rel = err / np.maximum(np.abs(ref_f64), 1e-30)
+    line = "%s: max abs err %.3g, max rel err %.3g" % (what, float(err.max()),
+                                                        float(rel[np.abs(ref_f64) > 0].max())
+                                                        if np.any(ref_f64 != 0) else 0.0)
+    if ref_bits is not None:
+        d = ulp_distance(gpu_bits, ref_bits).ravel()
+        hist = np.bincount(np.minimum(d, 3), minlength=4)
+        line += ", ulp histogram {0: %d, 1: %d, 2: %d, >=3: %d}" % tuple(int(v) for v in hist)
+        exact = float(hist[0]) / d.size
+        if d.size >= 100 and exact < MIN_EXACT_FRACTION:
+            raise AssertionError("%s: only %.4f of the elements round to the oracle's bits"
+                                 % (what, exact))
+    print(line, flush=True)
+    return float(err.max())
 
 
 def check_exact(gpu_bits, ref_bits, what=""):
