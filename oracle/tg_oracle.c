@@ -136,10 +136,17 @@ static uint16_t encode(int dt, double x)
 
 /* ------------------------------------------------------------ activation */
 
+/* The tanh-form GELU.  With u = sqrt(2/pi) (x + 0.044715 x^3), the identity
+ * 1 + tanh(u) = 2 / (1 + exp(-2u)) turns 0.5 x (1 + tanh(u)) into
+ * x / (1 + exp(-2u)), the same function.  That form is the one evaluated:
+ * in double, 1 + tanh(u) cancels to exactly 0 once u < -19 (x < -6.4),
+ * while the function's value there (-2.5e-15 at x = -7) is still far
+ * above the smallest bf16 magnitudes. */
 double tgo_gelu_tanh(double x)
 {
     const double c = sqrt(2.0 / M_PI);
-    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+    const double u = c * (x + 0.044715 * x * x * x);
+    return x / (1.0 + exp(-2.0 * u));
 }
 
 static double activate(int act, double v)

@@ -318,6 +318,36 @@ def test_gelu_asymptotes():
     assert g[2] == 30.0 and g[3] == 0.0
 
 
+def _gelu_tanh_decimal(x):
+    """0.5 x (1 + tanh(u)) at 200 significant digits, tanh from exp:
+    tanh(u) = (e^(2u) - 1) / (e^(2u) + 1).  With that many digits the
+    cancellation in 1 + tanh(u) for very negative u costs nothing."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 200
+        D = decimal.Decimal
+        X = D(x)
+        # pi to 60 digits (only its first ~20 matter for a double result)
+        pi = D("3.14159265358979323846264338327950288419716939937510582097494")
+        c = (D(2) / pi).sqrt()
+        u = c * (X + D("0.044715") * X ** 3)
+        e2u = (2 * u).exp()
+        tanh = (e2u - 1) / (e2u + 1)
+        return float(D("0.5") * X * (1 + tanh))
+
+
+def test_gelu_against_high_precision_including_the_far_negative_tail():
+    # points where the double tanh form would cancel (x < -6.4) and ordinary ones
+    xs = [-9.5, -9.0, -8.0, -7.0, -6.5, -6.0, -5.0, -3.0, -1.25, -0.5, 0.5, 1.0, 2.5, 5.0, 8.0]
+    g = oracle.gelu_tanh(np.array(xs))
+    for x, v in zip(xs, g):
+        ref = _gelu_tanh_decimal(x)
+        assert ref != 0.0
+        # rounding u = c (x + 0.044715 x^3) in double costs ~|u| ulps of exp(-2u)
+        u = math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)
+        assert abs(v - ref) <= 2.0 ** -52 * (8 + 6 * abs(u)) * abs(ref), (x, v, ref)
+
+
 def test_gelu_at_an_exactly_solvable_point():
     # With c = sqrt(2/pi): if c (x + 0.044715 x^3) = ln 3 then tanh = 4/5 and
     # gelu(x) = 0.5 x (1 + 4/5) = 0.9 x.  Solve for x by bisection.
