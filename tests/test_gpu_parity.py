@@ -292,6 +292,50 @@ def test_k_zero_gives_activated_bias(tg):
     util.check_tol(dt, util.to_bits(C), f64, "K=0", ref_bits=rbits)
 
 
+# ------------------------------------------------- async tile configurations
+
+ASYNC_CONFIGS = ["async_256x256x32_s4", "async_128x128x32_s4", "async_64x128x32_s4"]
+
+
+@pytest.mark.parametrize("cfg", ASYNC_CONFIGS)
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_async_config_integer_bias_exact(tg, monkeypatch, cfg, dt):
+    # 512 x 768 x 384: several tiles in both directions for every tile size,
+    # a K loop of 12 steps (three trips round the four stages), integer bias
+    monkeypatch.setenv("TG_FORCE_CONFIG", cfg)
+    p = inputs.problem(dt, 512, 768, 384, seed=61 + dt, kind="int", bias=True,
+                       bias_kind="int")
+    say("case", cfg, "dt", dt, "integer + bias 512x768x384")
+    bits, kern = run(tg, p)
+    assert kern == cfg
+    _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
+    util.check_exact(bits, ref, cfg)
+
+
+@pytest.mark.parametrize("cfg", ASYNC_CONFIGS)
+def test_async_config_bias_gelu_random(tg, monkeypatch, cfg):
+    monkeypatch.setenv("TG_FORCE_CONFIG", cfg)
+    p = inputs.problem(F16, 256, 512, 640, seed=71, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.2, b_scale=0.2)
+    say("case", cfg, "bias+gelu 256x512x640")
+    bits, kern = run(tg, p)
+    assert kern == cfg
+    f64, rbits = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits, f64, cfg, ref_bits=rbits)
+
+
+def test_async_small_tile_qkv(tg, monkeypatch):
+    # N = 384 is a multiple of 128 but not of 256: the 128 x 128 tiles serve it
+    q = inputs.qkv_problem(BF16, 256, 384, 256, seed=81, kind="int")
+    say("case qkv 256x384x256 small tiles")
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_128x128x32_s4")
+    _, _, outs = run_qkv(tg, q)
+    assert tg.last_kernel() == "async_128x128x32_s4"
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "qkv small tiles [%d]" % t)
+
+
 def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
@@ -301,6 +345,13 @@ def test_dispatch_choices(tg):
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
     tg.gemm(x, w)
     assert tg.last_kernel().startswith("skinny")
+    # under-filled grids take the smaller asynchronous tiles
+    b = torch.zeros((1024, 1024), dtype=torch.float16, device="cuda")
+    tg.gemm(b, b)
+    assert tg.last_kernel() == "async_64x128x32_s4"
+    c = torch.zeros((2048, 2048), dtype=torch.float16, device="cuda")
+    tg.gemm(c, c)
+    assert tg.last_kernel() == "async_128x128x32_s4"
     torch.cuda.synchronize()
 
 

@@ -40,11 +40,22 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int AS_BM = 256, AS_BN = 256, AS_BK = 32, AS_STAGES = 4, AS_NT = 256;
-constexpr int AS_A_BYTES = AS_BM * AS_BK * 2;  // 16 KiB
-constexpr int AS_B_BYTES = AS_BK * AS_BN * 2;  // 16 KiB
-constexpr int AS_STAGE_BYTES = AS_A_BYTES + AS_B_BYTES;
-constexpr int AS_COPIES = AS_STAGE_BYTES / 1024 / (AS_NT / 64); // 1 KiB copies per wave per step
+constexpr int AS_BK = 32, AS_STAGES = 4, AS_NT = 256;
+
+// Tile geometry for TI x TJ 32x32 accumulator blocks per wave and 2 x 2
+// waves: the workgroup tile is (64 TI) x (64 TJ).
+template <int TI, int TJ>
+struct AsGeom {
+    static constexpr int BM = 64 * TI, BN = 64 * TJ;
+    static constexpr int A_BYTES = BM * AS_BK * 2;      // [BM][32] K-contiguous
+    static constexpr int B_BYTES = AS_BK * BN * 2;      // [32][BN] N-contiguous
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int COPIES = TI + TJ;              // 1 KiB copies per wave per step
+    static constexpr int C1 = COPIES / 2;               // copies issued in the second half-step
+    static constexpr int B_ROWS_PER_COPY = 512 / BN;    // 1 KiB of [32][BN]
+    static constexpr int B_GRANULES = BN / 8;           // 16-byte granules per B row
+    static_assert(BN >= 128, "the B swizzle needs at least 16 granules per row");
+};
 
 __host__ __device__ constexpr int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 // {0, 6, 10, 12}[r & 3] as a nibble table (a shift, not a branch chain)
@@ -76,17 +87,20 @@ __device__ __forceinline__ void wait_vmcnt()
 
 } // namespace
 
-template <int DT, int ACT>
-__global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int tiles_m, int tiles_n,
-                                                              int group_m)
+template <int DT, int ACT, int TI, int TJ>
+__global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kernel(GemmArgs p,
+                                                                                 int tiles_m,
+                                                                                 int tiles_n,
+                                                                                 int group_m)
 {
+    using G = AsGeom<TI, TJ>;
     // one array per stage: with the K loop unrolled by the stage count every
     // copy and every read names its stage statically, so the compiler can
     // tell the stages apart and only waits for the copies of the stage it reads
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[AS_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[AS_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[AS_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[AS_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[G::STAGE_BYTES];
     auto stage = [&](auto sidx) -> unsigned char * {
         constexpr int S = decltype(sidx)::value;
         if constexpr (S == 0)
@@ -102,27 +116,33 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_m = wave >> 1, wave_n = wave & 1; // 2 x 2 waves of 128 x 128
+    const int wave_m = wave >> 1, wave_n = wave & 1; // 2 x 2 waves of (32 TI) x (32 TJ)
 
     const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
-    const int m0 = tc.tm * AS_BM, n0 = tc.tn * AS_BN;
+    const int m0 = tc.tm * G::BM, n0 = tc.tn * G::BN;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
     const int KT = p.K / AS_BK;
 
-    // ---- copy plan: wave w issues copies q = 4w .. 4w+3 of A and of B.
+    // ---- copy plan: wave w issues copies q = TI w .. TI w + TI - 1 of A and
+    // q = TJ w .. TJ w + TJ - 1 of B.
     // A copy q fills rows 16q..16q+15; lane -> (row 16q + lane/4, granule lane%4).
-    // B copy q fills rows 2q, 2q+1;    lane -> (row 2q + lane/32, granule lane%32).
-    const unsigned short *ga[4];
-    const unsigned short *gb[4];
+    // B copy q fills rows RPC q .. RPC q + RPC - 1 (RPC = 512 / BN rows of
+    // BN / 8 granules); lane -> (row RPC q + lane / (BN/8), granule lane % (BN/8)).
+    const unsigned short *ga[TI];
+    const unsigned short *gb[TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = wave * 4 + i;
+    for (int i = 0; i < TI; ++i) {
+        const int q = wave * TI + i;
         const int ra = 16 * q + (lane >> 2);
         const int ca = (lane & 3) ^ swz_a(ra);
         ga[i] = p.A + (int64_t)(m0 + ra) * p.lda + ca * 8;
-        const int rb = 2 * q + (lane >> 5);
-        const int cb = (lane & 31) ^ swz_b(rb);
+    }
+#pragma unroll
+    for (int i = 0; i < TJ; ++i) {
+        const int q = wave * TJ + i;
+        const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
+        const int cb = (lane % G::B_GRANULES) ^ swz_b(rb);
         gb[i] = Bm + (int64_t)rb * p.ldb + n0 + cb * 8;
     }
     const int64_t b_step = (int64_t)AS_BK * p.ldb;
@@ -131,24 +151,24 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     // wait insertion (which cannot tell the stages apart and would drain every
     // copy before each LDS read) stays out of the pipeline; the waits below
     // (wait_vmcnt) cover them explicitly.  m0 holds the copy's LDS address.
-    // Copy c (0..7) of step kt: c < 4 is A copy 4 wave + c, else B copy
-    // 4 wave + c - 4.
+    // Copy c (0 .. COPIES-1) of step kt: c < TI is A copy TI wave + c, else
+    // B copy TJ wave + c - TI.
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
-        if (c < 4) {
-            const unsigned dst = lds + (wave * 4 + c) * 1024;
+        if (c < TI) {
+            const unsigned dst = lds + (wave * TI + c) * 1024;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[c] + kt * AS_BK), "{m0}"(dst)
                          : "memory");
         } else {
-            const unsigned dst = lds + AS_A_BYTES + (wave * 4 + c - 4) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - 4] + kt * b_step),
+            const unsigned dst = lds + G::A_BYTES + (wave * TJ + c - TI) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - TI] + kt * b_step),
                          "{m0}"(dst)
                          : "memory");
         }
     };
     auto issue = [&](int kt, unsigned char *st) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+        for (int c = 0; c < G::COPIES; ++c)
             copy(kt, st, c);
     };
 
@@ -157,71 +177,72 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     // conversions overlap the first copies instead of lengthening the
     // epilogue.  Lane l of 32x32 block (i, j) holds columns
     // n = 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3 (any row).
-    f32x16 acc[4][4];
+    f32x16 acc[TI][TJ];
     if (p.bias != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const u32x2 braw = *reinterpret_cast<const u32x2 *>(
-                    p.bias + n0 + wave_n * 128 + j * 32 + g * 8 + (lane >> 5) * 4);
+                    p.bias + n0 + wave_n * 32 * TJ + j * 32 + g * 8 + (lane >> 5) * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float b = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < TI; ++i)
                         acc[i][j][4 * g + e] = b;
                 }
             }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < TJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.f;
     }
 
     // ---- fragment addressing (byte offsets within a stage)
-    // A fragment i: row wave_m*128 + i*32 + lane%32, k granule 2kk + lane/32.
-    int a_off[4][2];
+    // A fragment i: row wave_m*32TI + i*32 + lane%32, k granule 2kk + lane/32.
+    int a_off[TI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wave_m * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < TI; ++i) {
+        const int r = wave_m * 32 * TI + i * 32 + (lane & 31);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
             a_off[i][kk] = r * 64 + (((2 * kk + (lane >> 5)) ^ swz_a(r)) * 16);
     }
     // B fragment j, half h: 16-lane group g = lane/16, jj = lane%16:
-    // row 16kk + 8(g/2) + 4h + jj/4, column wave_n*128 + 32j + 16(g%2) + 4(jj%4).
-    int b_off[4][2][2];
+    // row 16kk + 8(g/2) + 4h + jj/4, column wave_n*32TJ + 32j + 16(g%2) + 4(jj%4).
+    int b_off[TJ][2][2];
     {
         const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = 16 * kk + 8 * (g >> 1) + 4 * h + (jj >> 2);
-                    const int col = wave_n * 128 + 32 * j + 16 * (g & 1) + 4 * (jj & 3);
+                    const int col = wave_n * 32 * TJ + 32 * j + 16 * (g & 1) + 4 * (jj & 3);
                     const int gran = (col >> 3) ^ swz_b(r);
-                    b_off[j][kk][h] = AS_A_BYTES + r * 512 + gran * 16 + (col & 7) * 2;
+                    b_off[j][kk][h] = G::A_BYTES + r * (2 * G::BN) + gran * 16 + (col & 7) * 2;
                 }
     }
 
     struct Frag {
-        u32x4 a[4], b[4];
+        u32x4 a[TI], b[TJ];
     };
-    // fragment piece q of half kk: q < 4 is A fragment q, then the two
-    // transposing reads (q - 4 even: low half, odd: high half) of B fragment
-    // (q - 4) / 2
+    // fragment piece q of half kk: q < TI is A fragment q, then the two
+    // transposing reads (q - TI even: low half, odd: high half) of B fragment
+    // (q - TI) / 2
+    constexpr int NREAD = TI + 2 * TJ, NMMA = TI * TJ;
     auto read_piece = [&](Frag &f, const unsigned char *st, int kk, int q) {
-        if (q < 4) {
+        if (q < TI) {
             f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q][kk]);
         } else {
-            const int j = (q - 4) >> 1, h = (q - 4) & 1;
+            const int j = (q - TI) >> 1, h = (q - TI) & 1;
             const s16x4 v =
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][kk][h]));
             const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -231,58 +252,60 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     };
     auto read = [&](Frag &f, const unsigned char *st, int kk) {
 #pragma unroll
-        for (int q = 0; q < 12; ++q)
+        for (int q = 0; q < NREAD; ++q)
             read_piece(f, st, kk, q);
     };
     auto mma_one = [&](const Frag &f, int q) {
-        const int i = q >> 2, j = q & 3;
+        const int i = q / TJ, j = q % TJ;
         acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
     };
 
     // ---- pipeline.  Each step k (32 deep = two 16-deep halves h0, h1):
-    //     read h1 of stage k            (h0 of stage k is already in registers)
-    //     MFMAs of h0
+    //     MFMAs of h0, interleaved with the reads of h1 of stage k and the
+    //     copies C1 .. COPIES-1 of step k+3 (into stage k-1, free since the
+    //     barrier of step k-1)
     //     wait for this wave's copies of step k+1, barrier
     //     MFMAs of h1, interleaved with the reads of h0 of stage k+1 and the
-    //     copies of step k+4 into stage k
-    // Stage k is free after the barrier (both of its halves were read before
-    // it), so every copy has three steps of MFMA work to land, and every LDS
-    // read overlaps MFMAs.  K is a multiple of 4 steps, so the loop body is
-    // the 4 stages with their arrays named statically.
-    // The 8 copies of a step are spread over two half-steps: copies 0-3 of
-    // step k+4 go out with the MFMAs of h1 of step k, copies 4-7 with the
-    // MFMAs of h0 of step k+1 (stage k stays free until step k+4 reads it),
-    // one copy between MFMAs.  Per step this is still 8 copies, so the wait
-    // count below is unchanged.
+    //     copies 0 .. C1-1 of step k+4 (into stage k, free after the barrier:
+    //     both of its halves were read before it)
+    // Every copy has three steps of MFMA work to land, and every LDS read
+    // overlaps MFMAs.  K is a multiple of 4 steps, so the loop body is the 4
+    // stages with their arrays named statically.  The MFMA / read / copy
+    // order of each half is pinned, one of each per slot.
+    constexpr int SLOTS = (NMMA > NREAD ? NMMA : NREAD) > TI + G::COPIES - G::C1
+                              ? (NMMA > NREAD ? NMMA : NREAD)
+                              : TI + G::COPIES - G::C1;
     Frag f0, f1;
     auto step = [&](int kt, auto sidx) {
         constexpr int S = decltype(sidx)::value;
         unsigned char *cur = stage(sidx);
         unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
         unsigned char *prv = stage(std::integral_constant<int, (S + 3) % 4>{});
-        const int kp = min(kt + 3, KT - 1); // second half of the copies of step k+3 (into stage k-1)
+        const int kp = min(kt + 3, KT - 1); // second part of the copies of step k+3
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            mma_one(f0, q);
-            if (q < 12)
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < NMMA)
+                mma_one(f0, q);
+            if (q < NREAD)
                 read_piece(f1, cur, 1, q);
-            if (q >= 4 && q < 8)
-                copy(kp, prv, q);
+            if (q >= TI && q < TI + G::COPIES - G::C1)
+                copy(kp, prv, G::C1 + q - TI);
             __builtin_amdgcn_sched_barrier(0); // keep the MFMA / read / copy order
         }
         // The copies of steps k+2 and k+3 may stay in flight.  The loop body
         // is branch-free: past the last step the copies repeat the last tile
         // (into stages nobody reads any more), so this count always holds.
-        wait_vmcnt<2 * AS_COPIES>();
+        wait_vmcnt<2 * G::COPIES>();
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's reads of stage k are done
         stage_barrier();
         const int kc = min(kt + 4, KT - 1);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            mma_one(f1, q);
-            if (q < 12)
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < NMMA)
+                mma_one(f1, q);
+            if (q < NREAD)
                 read_piece(f0, nxt, 0, q); // past the last step: harmless reread
-            if (q < 4)
+            if (q < G::C1)
                 copy(kc, cur, q);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -290,12 +313,11 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
     issue(0, st0);
     issue(1, st1);
     issue(2, st2);
-    // step 3: copies 0-3 now, 4-7 in the first half of step 0
-    copy(3, st3, 0);
-    copy(3, st3, 1);
-    copy(3, st3, 2);
-    copy(3, st3, 3);
-    wait_vmcnt<2 * AS_COPIES + 4>();
+    // step 3: copies 0 .. C1-1 now, the rest in the first half of step 0
+#pragma unroll
+    for (int c = 0; c < G::C1; ++c)
+        copy(3, st3, c);
+    wait_vmcnt<2 * G::COPIES + G::C1>();
     stage_barrier();
     read(f0, st0, 0);
     for (int kt = 0; kt < KT; kt += 4) {
@@ -313,68 +335,96 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async_kernel(GemmArgs p, int ti
 
     // ---- epilogue.  Lane l of a 32x32 accumulator block holds row m = l % 32
     // and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
-    // activation and rounding happen there; the rounded 128 x 128 tile of
-    // the wave is then restaged through LDS (the wave's own 32 KiB stage,
-    // 256-byte rows, 16-byte granule c of row r at c ^ (r % 16)) so that each
-    // global store writes four whole 256-byte row segments instead of 32
-    // scattered 16-byte pieces.
+    // activation and rounding happen there; the rounded (32 TI) x (32 TJ)
+    // tile of the wave is then restaged through LDS (inside the wave's own
+    // stage: rows of 4 TJ 16-byte granules, granule c of row r at
+    // c ^ (r % 4TJ)) so that each global store writes whole 64 TJ-byte row
+    // segments instead of 16-byte pieces of 32 rows.
+    constexpr int EG = 4 * TJ;              // granules per row of the wave tile
+    static_assert(2048 * TI * TJ <= G::STAGE_BYTES, "wave tile must fit its stage");
     unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = i * 32 + (lane & 31);
+    for (int i = 0; i < TI; ++i) {
+        const int r = i * 32 + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TJ; ++j) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4];
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = activate<ACT>(acc[i][j][4 * g + e]);
-                    const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                    const int c = (4 * j + g) ^ (r & 15);
-                    *reinterpret_cast<u32x2 *>(ep + r * 256 + c * 16 + (lane >> 5) * 8) = o;
-                }
+                for (int e = 0; e < 4; ++e)
+                    v[e] = activate<ACT>(acc[i][j][4 * g + e]);
+                const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                const int c = (4 * j + g) ^ (r & (EG - 1));
+                *reinterpret_cast<u32x2 *>(ep + r * (16 * EG) + c * 16 + (lane >> 5) * 8) = o;
             }
         }
-        // each lane reads back granule lane % 16 of rows 4t + lane / 16 (its
-        // own wave's writes, so no barrier) and stores it
-        unsigned short *crow = Cm + (int64_t)(m0 + wave_m * 128) * p.ldc + n0 + wave_n * 128 +
-                               (lane & 15) * 8;
+    }
+    // each lane reads back granule lane % EG of rows (64 / EG) t + lane / EG
+    // (its own wave's writes, so no barrier) and stores it
+    unsigned short *crow = Cm + (int64_t)(m0 + wave_m * 32 * TI) * p.ldc + n0 + wave_n * 32 * TJ +
+                           (lane % EG) * 8;
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-            const int r = 4 * t + (lane >> 4);
-            const u32x4 v =
-                *reinterpret_cast<const u32x4 *>(ep + r * 256 + (((lane & 15) ^ (r & 15)) * 16));
-            *reinterpret_cast<u32x4 *>(crow + (int64_t)r * p.ldc) = v;
-        }
+    for (int t = 0; t < 2 * TI * TJ; ++t) {
+        const int r = (64 / EG) * t + lane / EG;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * EG) +
+                                                         (((lane % EG) ^ (r & (EG - 1))) * 16));
+        *reinterpret_cast<u32x4 *>(crow + (int64_t)r * p.ldc) = v;
     }
 }
 
-bool async_eligible(const GemmArgs &a)
+namespace {
+struct AsyncConfig {
+    int ti, tj;
+    const char *name;
+};
+const AsyncConfig kAsyncConfigs[] = {
+    {4, 4, "async_256x256x32_s4"},
+    {2, 2, "async_128x128x32_s4"},
+    {1, 2, "async_64x128x32_s4"},
+};
+} // namespace
+
+int num_async_configs() { return (int)(sizeof kAsyncConfigs / sizeof kAsyncConfigs[0]); }
+const char *async_config_name(int cfg) { return kAsyncConfigs[cfg].name; }
+int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
+int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
+
+bool async_eligible(const GemmArgs &a, int cfg)
 {
-    return a.M % AS_BM == 0 && a.N % AS_BN == 0 && a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 &&
-           ((uintptr_t)a.bias & 7u) == 0;
+    return a.M % async_tile_m(cfg) == 0 && a.N % async_tile_n(cfg) == 0 &&
+           a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0;
 }
 
-hipError_t launch_async(int dt, int act, const GemmArgs &a, int group_m, hipStream_t s)
+hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                        hipStream_t s)
 {
-    const int tiles_m = a.M / AS_BM, tiles_n = a.N / AS_BN;
+    const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
     dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
-#define TG_AS(DT_, ACT_)                                                                         \
-    hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_>), grid, block, 0, s, a, tiles_m, tiles_n,     \
-                       group_m)
+#define TG_AS(DT_, ACT_, TI_, TJ_)                                                               \
+    hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_>), grid, block, 0, s, a, tiles_m,   \
+                       tiles_n, group_m)
+#define TG_AS_CFG(DT_, ACT_)                                                                     \
+    do {                                                                                         \
+        if (cfg == 0)                                                                            \
+            TG_AS(DT_, ACT_, 4, 4);                                                              \
+        else if (cfg == 1)                                                                       \
+            TG_AS(DT_, ACT_, 2, 2);                                                              \
+        else                                                                                     \
+            TG_AS(DT_, ACT_, 1, 2);                                                              \
+    } while (0)
     if (dt == DT_F16) {
         if (act == ACT_GELU)
-            TG_AS(DT_F16, ACT_GELU);
+            TG_AS_CFG(DT_F16, ACT_GELU);
         else
-            TG_AS(DT_F16, ACT_NONE);
+            TG_AS_CFG(DT_F16, ACT_NONE);
     } else {
         if (act == ACT_GELU)
-            TG_AS(DT_BF16, ACT_GELU);
+            TG_AS_CFG(DT_BF16, ACT_GELU);
         else
-            TG_AS(DT_BF16, ACT_NONE);
+            TG_AS_CFG(DT_BF16, ACT_NONE);
     }
+#undef TG_AS_CFG
 #undef TG_AS
     return hipGetLastError();
 }

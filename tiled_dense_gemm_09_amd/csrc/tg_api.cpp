@@ -128,6 +128,31 @@ int choose_config(int64_t M, int64_t N, int n_mat)
     return n - 1;
 }
 
+// Asynchronous-copy configuration for a problem, or -1: a forced name, else
+// the largest tile that still gives about one full wave of workgroups, else
+// the smallest eligible tile (most workgroups).
+int choose_async(const tg::GemmArgs &a, const char *force)
+{
+    const int n = tg::num_async_configs();
+    if (force && strncmp(force, "async", 5) == 0) {
+        for (int i = 0; i < n; ++i)
+            if (strcmp(force, tg::async_config_name(i)) == 0)
+                return tg::async_eligible(a, i) ? i : -1;
+        return -1;
+    }
+    int best = -1;
+    for (int i = 0; i < n; ++i) {
+        if (!tg::async_eligible(a, i))
+            continue;
+        const int64_t tiles =
+            (int64_t)(a.M / tg::async_tile_m(i)) * (a.N / tg::async_tile_n(i)) * a.n_mat;
+        if (tiles >= 240)
+            return i;
+        best = i;
+    }
+    return best;
+}
+
 tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
               int64_t ldc, int n_mat, void *stream)
@@ -220,11 +245,11 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                  pl.streaming == 2 ? "_cols" : (pl.streaming ? "_stream" : ""), pl.bn, pl.splits,
                  pl.k_chunk);
         set_last("skinny", detail);
-    } else if (tg::async_eligible(a) && !force_tiled &&
-               (M / 256) * (N / 256) * n_mat >= 128) {
+    } else if (!force_tiled && choose_async(a, force) >= 0) {
+        const int cfg = choose_async(a, force);
         const int group_m = env_int("TG_GROUP_M", 4);
-        err = tg::launch_async(kdt, kact, a, group_m > 0 ? group_m : 4, s);
-        set_last("async_256x256x32_s4");
+        err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
+        set_last(tg::async_config_name(cfg));
     } else {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);

@@ -37,10 +37,17 @@ hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m
                         hipStream_t stream);
 hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
 
-// Asynchronous-copy MFMA kernel (256 x 256 x 32 tiles, 4 stages) for problems
-// with M, N multiples of 256 and K a multiple of 128.
-bool async_eligible(const GemmArgs &a);
-hipError_t launch_async(int dt, int act, const GemmArgs &a, int group_m, hipStream_t stream);
+// Asynchronous-copy MFMA kernel: configurations 0, 1, 2 have 256 x 256,
+// 128 x 128 and 64 x 128 tiles (all 32 deep, 4 stages); a problem is
+// eligible for a configuration when its tile divides M and N and K is a
+// multiple of 128.
+int num_async_configs();
+const char *async_config_name(int cfg);
+int async_tile_m(int cfg);
+int async_tile_n(int cfg);
+bool async_eligible(const GemmArgs &a, int cfg);
+hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                        hipStream_t stream);
 
 // Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
