@@ -52,6 +52,10 @@ def _load():
         lib.tgo_gemm.argtypes = [_I, _L, _L, _L, _P, _L, _P, _L, _P, _I, _P, _P, _L, _L, _L, _I]
         lib.tgo_gemm_sample.argtypes = [_I, _L, _L, _L, _P, _L, _P, _L, _P, _I, _L, _P, _P, _P,
                                         _P, _I]
+        lib.tgo_gemm_ex.argtypes = [_I, _L, _L, _L, _P, _L, _P, _L, _I, _P, _I, _P, _L, _P, _P,
+                                    _L, _L, _L, _I]
+        lib.tgo_gemm_ex_sample.argtypes = [_I, _L, _L, _L, _P, _L, _P, _L, _I, _P, _I, _P, _L,
+                                           _L, _P, _P, _P, _P, _I]
         lib.tgo_gemm_qkv.argtypes = [_I, _L, _L, _L, _P, _L, _P, _P, _P, _L, _P, _P, _P, _P, _P,
                                      _P, _L, _L, _L, _I]
         lib.tgo_decode_array.argtypes = [_I, _L, _P, _P]
@@ -140,6 +144,56 @@ def gemm_sample(dt, A, B, ii, jj, bias=None, act=ACT_NONE, threads=0):
     bits = np.empty(ii.shape, np.uint16)
     rc = _load().tgo_gemm_sample(dt, M, N, K, _ptr(A), K, _ptr(B), N, _ptr(bias), act, ii.size,
                                  _ptr(ii), _ptr(jj), _ptr(f64), _ptr(bits), threads)
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+    return f64, bits
+
+
+def _ex_operands(A, B, trans_b, bias, R):
+    A, B = _bits(A), _bits(B)
+    M, K = A.shape
+    if trans_b:
+        N, K2 = B.shape
+    else:
+        K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if bias is not None:
+        bias = _bits(bias)
+        if bias.shape != (N,):
+            raise ValueError("bias must be [N]")
+    if R is not None:
+        R = _bits(R)
+        if R.shape != (M, N):
+            raise ValueError("residual must be [M,N]")
+    return A, B, bias, R, M, N, K
+
+
+def gemm_ex(dt, A, B, trans_b=False, bias=None, act=ACT_NONE, R=None, rows=None, threads=0):
+    """C = round(act(A.opB + bias) + R) on rows [r0, r1); opB = B ([K,N]) or
+    the transpose of B stored [N,K] when trans_b.  Returns (f64, bits)."""
+    A, B, bias, R, M, N, K = _ex_operands(A, B, trans_b, bias, R)
+    r0, r1 = (0, M) if rows is None else rows
+    f64 = np.zeros((M, N), np.float64)
+    bits = np.zeros((M, N), np.uint16)
+    rc = _load().tgo_gemm_ex(dt, M, N, K, _ptr(A), K, _ptr(B), K if trans_b else N,
+                             int(bool(trans_b)), _ptr(bias), act, _ptr(R), N, _ptr(f64),
+                             _ptr(bits), N, r0, r1, threads)
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+    return f64[r0:r1], bits[r0:r1]
+
+
+def gemm_ex_sample(dt, A, B, ii, jj, trans_b=False, bias=None, act=ACT_NONE, R=None, threads=0):
+    """The elements (ii[s], jj[s]) of gemm_ex; returns (f64, bits)."""
+    A, B, bias, R, M, N, K = _ex_operands(A, B, trans_b, bias, R)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    f64 = np.empty(ii.shape, np.float64)
+    bits = np.empty(ii.shape, np.uint16)
+    rc = _load().tgo_gemm_ex_sample(dt, M, N, K, _ptr(A), K, _ptr(B), K if trans_b else N,
+                                    int(bool(trans_b)), _ptr(bias), act, _ptr(R), N, ii.size,
+                                    _ptr(ii), _ptr(jj), _ptr(f64), _ptr(bits), threads)
     if rc:
         raise ValueError("oracle rejected the arguments")
     return f64, bits

@@ -27,6 +27,15 @@
  *   the IEEE default is taken).
  * - The horizontally fused QKV projection ("TileIR", horizontal fusion:
  *   Q, K and V projections share their input) is three independent GEMMs.
+ * - The extended form (tgo_gemm_ex) adds two things:
+ *     C[i][j] = round_dt( act( sum_k A[i][k] * opB[k][j] + bias[j] ) + R[i][j] )
+ *   R is a residual added after the activation, before the one rounding
+ *   ("TileIR", vertical fusion: the next elementwise operation, such as a
+ *   residual add, chained onto the product instead of run as a second
+ *   pass).  opB[k][j] is B[k][j] (B stored [K,N]) or B[j][k] (B stored
+ *   [N,K], one output feature per row): the same logical operand with its
+ *   two axes permuted, the placement unchanged ("TIRx", section 5.1,
+ *   permute).
  *
  * Every output element depends only on its own row of A and column of B,
  * so rows are split across OpenMP threads; the value of each element does
@@ -156,35 +165,50 @@ static double activate(int act, double v)
 
 /* ------------------------------------------------------------------ GEMM */
 
+/* opB[k][j] as stored: B[k][j] in a [K,N] matrix, B[j][k] in an [N,K] one. */
+static uint16_t op_b(const uint16_t *B, int64_t ldb, int trans_b, int64_t k, int64_t j)
+{
+    return trans_b ? B[j * ldb + k] : B[k * ldb + j];
+}
+
 /* One output element: the definition, k ascending. */
 static double element(int dt, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
-                      int64_t ldb, const uint16_t *bias, int act, int64_t i, int64_t j)
+                      int64_t ldb, int trans_b, const uint16_t *bias, int act,
+                      const uint16_t *R, int64_t ldr, int64_t i, int64_t j)
 {
     double s = 0.0;
     for (int64_t k = 0; k < K; ++k)
-        s += decode(dt, A[i * lda + k]) * decode(dt, B[k * ldb + j]);
+        s += decode(dt, A[i * lda + k]) * decode(dt, op_b(B, ldb, trans_b, k, j));
     if (bias)
         s += decode(dt, bias[j]);
-    return activate(act, s);
+    double v = activate(act, s);
+    if (R)
+        v += decode(dt, R[i * ldr + j]);
+    return v;
 }
 
 /*
  * Full GEMM over output rows [row0, row1).  A is [M,K] row-major with row
- * pitch lda, B is [K,N] with pitch ldb, bias is [N] or NULL.  Outputs (either
- * may be NULL): out_f64[i*ldc + j] the unrounded double result, out_bits the
- * round-to-nearest-even bits in the same dtype.  threads <= 0 means the
- * OpenMP default.  Returns 0, or -1 on a bad argument.
+ * pitch lda; B is [K,N] with pitch ldb (trans_b = 0) or [N,K] with pitch ldb
+ * (trans_b = 1); bias is [N] or NULL; R is [M,N] with pitch ldr, or NULL.
+ * Outputs (either may be NULL): out_f64[i*ldc + j] the unrounded double
+ * result, out_bits the round-to-nearest-even bits in the same dtype.
+ * threads <= 0 means the OpenMP default.  Returns 0, or -1 on a bad
+ * argument.
  *
- * For speed only, B is first decoded into a column-major double copy; each
+ * For speed only, opB is first decoded into a column-major double copy; each
  * element is still the k-ascending sum of exact products.
  */
-int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-             const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, double *out_f64,
-             uint16_t *out_bits, int64_t ldc, int64_t row0, int64_t row1, int threads)
+int tgo_gemm_ex(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb, int trans_b, const uint16_t *bias, int act,
+                const uint16_t *R, int64_t ldr, double *out_f64, uint16_t *out_bits, int64_t ldc,
+                int64_t row0, int64_t row1, int threads)
 {
     if ((dt != TGO_F16 && dt != TGO_BF16) || (act != TGO_ACT_NONE && act != TGO_ACT_GELU_TANH))
         return -1;
     if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1 || ldc < N)
+        return -1;
+    if (trans_b != 0 && trans_b != 1)
         return -1;
     if (row0 == row1 || N == 0)
         return 0;
@@ -197,7 +221,7 @@ int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t
     }
     for (int64_t k = 0; k < K; ++k)
         for (int64_t j = 0; j < N; ++j)
-            bt[j * K + k] = decode(dt, B[k * ldb + j]);
+            bt[j * K + k] = decode(dt, op_b(B, ldb, trans_b, k, j));
     for (int64_t j = 0; j < N; ++j)
         bs[j] = bias ? decode(dt, bias[j]) : 0.0;
 
@@ -222,6 +246,8 @@ int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t
                 if (bias)
                     s += bs[j];
                 double v = activate(act, s);
+                if (R)
+                    v += decode(dt, R[i * ldr + j]);
                 if (out_f64)
                     out_f64[i * ldc + j] = v;
                 if (out_bits)
@@ -235,16 +261,28 @@ int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t
     return 0;
 }
 
+/* The plain form: B [K,N], no residual. */
+int tgo_gemm(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+             const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, double *out_f64,
+             uint16_t *out_bits, int64_t ldc, int64_t row0, int64_t row1, int threads)
+{
+    return tgo_gemm_ex(dt, M, N, K, A, lda, B, ldb, 0, bias, act, NULL, 0, out_f64, out_bits, ldc,
+                       row0, row1, threads);
+}
+
 /*
  * Sampled outputs: the n elements (ii[s], jj[s]) of the same GEMM, for
- * checking large problems one element at a time.
+ * checking large problems one element at a time (operands as in
+ * tgo_gemm_ex).
  */
-int tgo_gemm_sample(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-                    const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, int64_t n,
-                    const int64_t *ii, const int64_t *jj, double *out_f64, uint16_t *out_bits,
-                    int threads)
+int tgo_gemm_ex_sample(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb, int trans_b, const uint16_t *bias, int act,
+                       const uint16_t *R, int64_t ldr, int64_t n, const int64_t *ii,
+                       const int64_t *jj, double *out_f64, uint16_t *out_bits, int threads)
 {
     if ((dt != TGO_F16 && dt != TGO_BF16) || (act != TGO_ACT_NONE && act != TGO_ACT_GELU_TANH))
+        return -1;
+    if (trans_b != 0 && trans_b != 1)
         return -1;
     for (int64_t s = 0; s < n; ++s)
         if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N)
@@ -255,13 +293,22 @@ int tgo_gemm_sample(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, 
 #pragma omp parallel for schedule(dynamic, 16)
 #endif
     for (int64_t s = 0; s < n; ++s) {
-        double v = element(dt, K, A, lda, B, ldb, bias, act, ii[s], jj[s]);
+        double v = element(dt, K, A, lda, B, ldb, trans_b, bias, act, R, ldr, ii[s], jj[s]);
         if (out_f64)
             out_f64[s] = v;
         if (out_bits)
             out_bits[s] = encode(dt, v);
     }
     return 0;
+}
+
+int tgo_gemm_sample(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                    const uint16_t *B, int64_t ldb, const uint16_t *bias, int act, int64_t n,
+                    const int64_t *ii, const int64_t *jj, double *out_f64, uint16_t *out_bits,
+                    int threads)
+{
+    return tgo_gemm_ex_sample(dt, M, N, K, A, lda, B, ldb, 0, bias, act, NULL, 0, n, ii, jj,
+                              out_f64, out_bits, threads);
 }
 
 /*

@@ -13,8 +13,10 @@ fix it with mathematics and independent code:
   product;
 * GELU_tanh against its odd-part identity, its asymptotes and an exactly
   solvable point (tanh(ln 3) = 4/5);
-* the epilogue order (bias before activation), QKV = three GEMMs, and
-  independence of the thread count and of row subsets.
+* the epilogue order (bias before activation, residual after it), QKV =
+  three GEMMs, the transposed-operand form against brute force and against
+  the same operand stored the other way, and independence of the thread
+  count and of row subsets.
 
 A plausible slip in the oracle -- a dropped term, a wrong sign or index, a
 transposed operand, a wrong rounding direction or constant -- fails one of
@@ -372,6 +374,80 @@ def test_epilogue_adds_bias_before_activation():
     f64, _ = oracle.gemm(F16, one, one, bias, oracle.ACT_GELU_TANH)
     assert f64[0, 0] == oracle.gelu_tanh(np.array([2.0]))[0]
     assert f64[0, 0] != oracle.gelu_tanh(np.array([1.0]))[0] + 1.0
+
+
+# ------------------------------------------- extended form: opB and residual
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_transposed_operand_brute_force(dt):
+    # B stored [N,K]: output (i, j) is the sum over k of A[i][k] * B[j][k]
+    M, N, K = 3, 4, 5
+    A = rand_bits(dt, (M, K), 41)
+    Bt = rand_bits(dt, (N, K), 42)
+    av, bv = oracle.decode(dt, A), oracle.decode(dt, Bt)
+    f64, _ = oracle.gemm_ex(dt, A, Bt, trans_b=True)
+    for i in range(M):
+        for j in range(N):
+            exact = sum((Fraction(float(av[i, k])) * Fraction(float(bv[j, k])) for k in range(K)),
+                        Fraction(0))
+            bound = sum(abs(float(av[i, k]) * float(bv[j, k])) for k in range(K)) * K * 2.0 ** -52
+            assert abs(Fraction(float(f64[i, j])) - exact) <= Fraction(bound)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_transposed_storage_gives_the_same_bits(dt):
+    p = inputs.problem(dt, 37, 53, 29, seed=43, bias=True, act=inputs.ACT_GELU_TANH)
+    Bt = np.ascontiguousarray(p["B"].T)   # the same operand stored [N,K]
+    f1, b1 = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    f2, b2 = oracle.gemm_ex(dt, p["A"], Bt, trans_b=True, bias=p["bias"], act=oracle.ACT_GELU_TANH)
+    assert np.array_equal(b1, b2) and np.array_equal(f1, f2)
+    # and a non-square transposed read is not a plain one
+    with pytest.raises(ValueError):
+        oracle.gemm_ex(dt, p["A"], Bt, trans_b=False)
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_residual_integer_exact(dt):
+    rng = np.random.default_rng(44)
+    a = rng.integers(-2, 3, (9, 31))
+    b = rng.integers(-2, 3, (31, 7))
+    r = rng.integers(-40, 41, (9, 7))
+    bias = rng.integers(-3, 4, 7)
+    f64, bits = oracle.gemm_ex(dt, bits_of(dt, a), bits_of(dt, b), bias=bits_of(dt, bias),
+                               R=bits_of(dt, r))
+    ref = (a @ b + bias[None, :] + r).astype(np.float64)
+    assert np.array_equal(f64, ref)
+    assert np.array_equal(bits, bits_of(dt, ref))
+
+
+def test_residual_is_added_after_the_activation():
+    one = bits_of(F16, np.ones((1, 1)))
+    two = bits_of(F16, 2.0 * np.ones((1, 1)))
+    f64, _ = oracle.gemm_ex(F16, one, two, act=oracle.ACT_GELU_TANH, R=one)
+    g2 = oracle.gelu_tanh(np.array([2.0]))[0]
+    assert f64[0, 0] == g2 + 1.0
+    assert f64[0, 0] != oracle.gelu_tanh(np.array([3.0]))[0]
+
+
+def test_residual_only_when_k_is_zero():
+    bias = rand_bits(F16, (6,), 46)
+    R = rand_bits(F16, (4, 6), 47)
+    f64, _ = oracle.gemm_ex(F16, np.zeros((4, 0), np.uint16), np.zeros((0, 6), np.uint16),
+                            bias=bias, act=oracle.ACT_GELU_TANH, R=R)
+    g = oracle.gelu_tanh(oracle.decode(F16, bias))
+    assert np.array_equal(f64, g[None, :] + oracle.decode(F16, R))
+
+
+def test_ex_sample_matches_full():
+    p = inputs.problem(BF16, 40, 70, 33, seed=48, bias=True, act=inputs.ACT_GELU_TANH)
+    Bt = np.ascontiguousarray(p["B"].T)
+    R = rand_bits(BF16, (40, 70), 49)
+    f, b = oracle.gemm_ex(BF16, p["A"], Bt, trans_b=True, bias=p["bias"],
+                          act=oracle.ACT_GELU_TANH, R=R)
+    ii = np.array([0, 39, 17, 5, 22]); jj = np.array([0, 69, 3, 44, 60])
+    fs, bs = oracle.gemm_ex_sample(BF16, p["A"], Bt, ii, jj, trans_b=True, bias=p["bias"],
+                                   act=oracle.ACT_GELU_TANH, R=R)
+    assert np.array_equal(fs, f[ii, jj]) and np.array_equal(bs, b[ii, jj])
 
 
 def test_qkv_is_three_gemms():
