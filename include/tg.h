@@ -57,8 +57,8 @@ extern "C" {
 typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_BF16 = 2 } tg_dtype;
 
 /* act(x): identity, or the tanh form of GELU
- *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
- * evaluated in FP32 with tanh(u) = 1 - 2 / (1 + exp(2u)). */
+ *     0.5 x (1 + tanh(u)),  u = sqrt(2/pi) (x + 0.044715 x^3),
+ * evaluated in FP32 as the same function x / (1 + exp(-2u)). */
 typedef enum { TG_ACT_NONE = 0, TG_ACT_GELU_TANH = 1 } tg_act;
 
 typedef enum {
@@ -86,6 +86,37 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K,
                            const void *bias, tg_act act,
                            void *C, int64_t ldc,
                            void *stream);
+
+/* Storage of the B operand of tg_gemm_ex. */
+typedef enum {
+    TG_OP_N = 0, /* B is [K,N] row-major, pitch ldb >= N (as in every other entry point) */
+    TG_OP_T = 1  /* B is stored [N,K] row-major, pitch ldb >= K (one output feature per
+                    row, the usual weight layout); the product uses its transpose */
+} tg_op;
+
+/* C = act(A . op(B) + bias) + R, one rounding at the end.
+ *  - R: an [M,N] residual with row pitch ldr (NULL = none), added after the
+ *    activation in FP32: "TileIR", vertical fusion (the next elementwise
+ *    operation, here a residual add, chained onto the product instead of a
+ *    second pass over C).  R may be C itself (same pointer and ldr == ldc),
+ *    an in-place residual add; any other overlap of R with C is rejected.
+ *    R must be 2-byte aligned; the MFMA kernels also need it 16-byte
+ *    aligned with ldr a multiple of 8.
+ *  - op(B): B, or the transpose of a B stored [N,K] -- one logical operand
+ *    with its two axes permuted and its placement unchanged ("TIRx",
+ *    section 5.1, permute).  TG_OP_T runs the MFMA kernel when M is a
+ *    multiple of 64, N of 128 and K of 128 (with the fast-path alignment);
+ *    any other TG_OP_T problem runs the fallback kernel, which
+ *    tg_last_kernel() reports.
+ *  - bias, act and the other arguments as in tg_gemm_bias_act; with
+ *    op_b == TG_OP_N and R == NULL the result is bit-identical to it. */
+tg_status tg_gemm_ex(tg_dtype dt, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb, tg_op op_b,
+                     const void *bias, tg_act act,
+                     const void *R, int64_t ldr,
+                     void *C, int64_t ldc,
+                     void *stream);
 
 /* Horizontally fused projection, one launch:
  *     Q = X . Wq,  Kout = X . Wk,  V = X . Wv.

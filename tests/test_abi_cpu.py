@@ -66,6 +66,34 @@ def test_invalid_arguments_launch_nothing(args):
     assert st == 1
 
 
+FAKE_R = 0x7F0030000000
+
+
+@pytest.mark.parametrize("args", [
+    dict(op=2),                       # unknown operand form
+    dict(op=1, ldb=31),               # B stored [N,K]: pitch shorter than K
+    dict(op=0, ldb=63),               # B [K,N]: pitch shorter than N
+    dict(ldr=63),                     # residual pitch shorter than N
+    dict(R=FAKE_R + 1),               # misaligned residual
+    dict(R=FAKE_C + 128),             # residual overlapping C without being C
+    dict(R=FAKE_C, ldr=72),           # C itself but with another pitch
+    dict(op=1, C=FAKE_B + 64 * 16),   # C inside B's [N,K] extent
+])
+def test_invalid_extended_arguments_launch_nothing(args):
+    a = dict(dt=2, M=64, N=64, K=32, A=FAKE_A, lda=32, B=FAKE_B, ldb=32, op=1, C=FAKE_C, ldc=64,
+             bias=0, act=0, R=FAKE_R, ldr=64)
+    a.update(args)
+    st = tg.lib.tg_gemm_ex(a["dt"], a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"],
+                           a["op"], a["bias"] or None, a["act"], a["R"] or None, a["ldr"], a["C"],
+                           a["ldc"], None)
+    assert st == 1
+
+
+def test_extended_empty_problem_is_a_noop():
+    assert tg.lib.tg_gemm_ex(1, 0, 64, 64, FAKE_A, 64, FAKE_B, 64, 1, None, 0, FAKE_C, 64,
+                             FAKE_C, 64, None) == 0
+
+
 def test_qkv_outputs_must_not_overlap():
     st = tg.lib.tg_gemm_qkv(2, 64, 64, 64, FAKE_A, 64, FAKE_B, FAKE_B + 2 ** 20, FAKE_B + 2 ** 21,
                             64, FAKE_C, FAKE_C + 128, FAKE_C + 2 ** 20, 64, None)

@@ -336,6 +336,101 @@ def test_async_small_tile_qkv(tg, monkeypatch):
         util.check_exact(outs[t], ref, "qkv small tiles [%d]" % t)
 
 
+# ------------------------------- extended epilogue: residual and B stored [N,K]
+
+def run_ex(tg, p, trans_b, R=None, Rin_place=False):
+    """C = act(A.opB + bias) + R through tg_gemm_ex; returns (bits, kernel)."""
+    import torch
+    dt = p["dt"]
+    A = util.to_dev(p["A"], dt)
+    Bd = util.to_dev(np.ascontiguousarray(p["B"].T) if trans_b else p["B"], dt)
+    b = Bd.t() if trans_b else Bd
+    bias = util.to_dev(p["bias"], dt) if p.get("bias") is not None else None
+    act = "gelu_tanh" if p["act"] == inputs.ACT_GELU_TANH else "none"
+    if Rin_place:
+        C = util.to_dev(R, dt)
+        tg.gemm(A, b, out=C, bias=bias, act=act, residual=C)
+    else:
+        res = util.to_dev(R, dt) if R is not None else None
+        C = tg.gemm(A, b, bias=bias, act=act, residual=res)
+    torch.cuda.synchronize()
+    return util.to_bits(C), tg.last_kernel()
+
+
+EX_SHAPES = [
+    # (dt, M, N, K, force): every kernel family with a residual
+    (F16, 512, 768, 384, "async_256x256x32_s4"),
+    (BF16, 256, 384, 256, "async_128x128x32_s4"),
+    (F16, 192, 256, 512, "async_64x128x32_s4"),
+    (BF16, 300, 170, 200, None),          # ragged: tiled kernel (B [K,N]) / generic (B [N,K])
+    (F16, 16, 1024, 2048, None),          # small M: streaming split-K kernel (B [K,N])
+    (BF16, 5, 520, 777, None),            # small M, ragged: register-staged kernel
+    (F16, 64, 128, 96, "generic"),
+]
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES)
+def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, force, trans_b):
+    if force:
+        monkeypatch.setenv("TG_FORCE_CONFIG", force)
+    p = inputs.problem(dt, M, N, K, seed=90 + M + N, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(91 + K), (M, N), "int", dt, 8.0)
+    say("case ex integer", dt, M, N, K, force, "B[N,K]" if trans_b else "B[K,N]")
+    bits, kern = run_ex(tg, p, trans_b, R)
+    say("  kernel", kern)
+    if force and force.startswith("async"):
+        assert kern == force
+    if trans_b and not (force or "").startswith("async"):
+        assert kern.startswith("generic")
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    util.check_exact(bits, ref, "ex %s" % kern)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES[:5])
+def test_residual_and_transposed_b_gelu_random(tg, monkeypatch, dt, M, N, K, force, trans_b):
+    if force:
+        monkeypatch.setenv("TG_FORCE_CONFIG", force)
+    p = inputs.problem(dt, M, N, K, seed=95 + M, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.25, b_scale=0.25)
+    R = inputs.draw(np.random.default_rng(96 + N), (M, N), "uniform", dt)
+    say("case ex gelu", dt, M, N, K, force, "B[N,K]" if trans_b else "B[K,N]")
+    bits, kern = run_ex(tg, p, trans_b, R)
+    Bo = np.ascontiguousarray(p["B"].T) if trans_b else p["B"]
+    f64, rbits = oracle.gemm_ex(dt, p["A"], Bo, trans_b=trans_b, bias=p["bias"],
+                                act=oracle.ACT_GELU_TANH, R=R)
+    util.check_tol(dt, bits, f64, "ex gelu %s" % kern, ref_bits=rbits)
+
+
+@pytest.mark.parametrize("force", ["async_128x128x32_s4", None])
+def test_in_place_residual(tg, monkeypatch, force):
+    if force:
+        monkeypatch.setenv("TG_FORCE_CONFIG", force)
+    for (M, N, K) in ((256, 384, 256), (16, 1024, 1024)):
+        p = inputs.problem(BF16, M, N, K, seed=97, kind="int", bias=True, bias_kind="int")
+        R = inputs.draw(np.random.default_rng(98), (M, N), "int", BF16, 4.0)
+        say("case in-place residual", M, N, K, force)
+        bits, kern = run_ex(tg, p, False, R, Rin_place=True)
+        _, ref = oracle.gemm_ex(BF16, p["A"], p["B"], bias=p["bias"], R=R)
+        util.check_exact(bits, ref, "in place %s" % kern)
+
+
+def test_transposed_b_full_size_sampled(tg):
+    # the headline shape with the weight stored [N,K] and a residual
+    p = inputs.config_problem("f16_4096_gelu")
+    R = inputs.draw(np.random.default_rng(99), (p["M"], p["N"]), "uniform", F16)
+    say("case 4096 B[N,K] + residual")
+    bits, kern = run_ex(tg, p, True, R)
+    assert kern == "async_256x256x32_s4"
+    ii, jj = util.sample_indices(p["M"], p["N"], 2000, seed=12)
+    f64, rbits = oracle.gemm_ex_sample(F16, p["A"], np.ascontiguousarray(p["B"].T), ii, jj,
+                                       trans_b=True, bias=p["bias"], act=oracle.ACT_GELU_TANH,
+                                       R=R)
+    util.check_tol(F16, bits[ii, jj], f64, "4096 B[N,K] + residual", ref_bits=rbits)
+
+
 def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")

@@ -87,7 +87,7 @@ __device__ __forceinline__ void wait_vmcnt()
 
 } // namespace
 
-template <int DT, int ACT, int TI, int TJ>
+template <int DT, int ACT, int TI, int TJ, bool BT>
 __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kernel(GemmArgs p,
                                                                                  int tiles_m,
                                                                                  int tiles_n,
@@ -129,6 +129,8 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     // A copy q fills rows 16q..16q+15; lane -> (row 16q + lane/4, granule lane%4).
     // B copy q fills rows RPC q .. RPC q + RPC - 1 (RPC = 512 / BN rows of
     // BN / 8 granules); lane -> (row RPC q + lane / (BN/8), granule lane % (BN/8)).
+    // B stored [N,K] (BT) is staged exactly like A: [BN][32] K-contiguous,
+    // copy q fills n-rows 16q..16q+15 with the A swizzle.
     const unsigned short *ga[TI];
     const unsigned short *gb[TJ];
 #pragma unroll
@@ -141,11 +143,17 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 #pragma unroll
     for (int i = 0; i < TJ; ++i) {
         const int q = wave * TJ + i;
-        const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
-        const int cb = (lane % G::B_GRANULES) ^ swz_b(rb);
-        gb[i] = Bm + (int64_t)rb * p.ldb + n0 + cb * 8;
+        if constexpr (BT) {
+            const int rb = 16 * q + (lane >> 2);
+            const int cb = (lane & 3) ^ swz_a(rb);
+            gb[i] = Bm + (int64_t)(n0 + rb) * p.ldb + cb * 8;
+        } else {
+            const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
+            const int cb = (lane % G::B_GRANULES) ^ swz_b(rb);
+            gb[i] = Bm + (int64_t)rb * p.ldb + n0 + cb * 8;
+        }
     }
-    const int64_t b_step = (int64_t)AS_BK * p.ldb;
+    const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb; // per K-step
 
     // The copies are issued with inline assembly so that the compiler's own
     // wait insertion (which cannot tell the stages apart and would drain every
@@ -215,8 +223,18 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     }
     // B fragment j, half h: 16-lane group g = lane/16, jj = lane%16:
     // row 16kk + 8(g/2) + 4h + jj/4, column wave_n*32TJ + 32j + 16(g%2) + 4(jj%4).
+    // (BT: like A, n-row wave_n*32TJ + 32j + lane%32, k granule 2kk + lane/32.)
     int b_off[TJ][2][2];
-    {
+    if constexpr (BT) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int r = wave_n * 32 * TJ + j * 32 + (lane & 31);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                b_off[j][kk][0] = b_off[j][kk][1] =
+                    G::A_BYTES + r * 64 + (((2 * kk + (lane >> 5)) ^ swz_a(r)) * 16);
+        }
+    } else {
         const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
@@ -236,11 +254,13 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     };
     // fragment piece q of half kk: q < TI is A fragment q, then the two
     // transposing reads (q - TI even: low half, odd: high half) of B fragment
-    // (q - TI) / 2
-    constexpr int NREAD = TI + 2 * TJ, NMMA = TI * TJ;
+    // (q - TI) / 2 (BT: one 128-bit read of B fragment q - TI)
+    constexpr int NREAD = TI + (BT ? TJ : 2 * TJ), NMMA = TI * TJ;
     auto read_piece = [&](Frag &f, const unsigned char *st, int kk, int q) {
         if (q < TI) {
             f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q][kk]);
+        } else if constexpr (BT) {
+            f.b[q - TI] = *reinterpret_cast<const u32x4 *>(st + b_off[q - TI][kk][0]);
         } else {
             const int j = (q - TI) >> 1, h = (q - TI) & 1;
             const s16x4 v =
@@ -343,23 +363,48 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     constexpr int EG = 4 * TJ;              // granules per row of the wave tile
     static_assert(2048 * TI * TJ <= G::STAGE_BYTES, "wave tile must fit its stage");
     unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    // The residual (if any) is added after the activation, before rounding;
+    // its 4-column pieces are read in the accumulator layout, one row block
+    // of loads at a time.
+    auto to_lds = [&](auto has_res) {
+        constexpr bool HR = decltype(has_res)::value;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-        const int r = i * 32 + (lane & 31);
+        for (int i = 0; i < TI; ++i) {
+            const int r = i * 32 + (lane & 31);
+            const int m = m0 + wave_m * 32 * TI + r;
+            u32x2 rr[TJ][4];
+            if constexpr (HR) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
+                for (int j = 0; j < TJ; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+                    for (int g = 0; g < 4; ++g)
+                        rr[j][g] = *reinterpret_cast<const u32x2 *>(
+                            p.R + (int64_t)m * p.ldr + n0 + wave_n * 32 * TJ + j * 32 + g * 8 +
+                            (lane >> 5) * 4);
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = activate<ACT>(acc[i][j][4 * g + e]);
-                const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                const int c = (4 * j + g) ^ (r & (EG - 1));
-                *reinterpret_cast<u32x2 *>(ep + r * (16 * EG) + c * 16 + (lane >> 5) * 8) = o;
+            for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = activate<ACT>(acc[i][j][4 * g + e]);
+                        if constexpr (HR)
+                            v[e] += from_bits<DT>(
+                                (unsigned short)(rr[j][g][e >> 1] >> (16 * (e & 1))));
+                    }
+                    const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                    const int c = (4 * j + g) ^ (r & (EG - 1));
+                    *reinterpret_cast<u32x2 *>(ep + r * (16 * EG) + c * 16 + (lane >> 5) * 8) = o;
+                }
             }
         }
-    }
+    };
+    if (p.R != nullptr)
+        to_lds(std::true_type{});
+    else
+        to_lds(std::false_type{});
     // each lane reads back granule lane % EG of rows (64 / EG) t + lane / EG
     // (its own wave's writes, so no barrier) and stores it
     unsigned short *crow = Cm + (int64_t)(m0 + wave_m * 32 * TI) * p.ldc + n0 + wave_n * 32 * TJ +
@@ -393,7 +438,8 @@ int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
 bool async_eligible(const GemmArgs &a, int cfg)
 {
     return a.M % async_tile_m(cfg) == 0 && a.N % async_tile_n(cfg) == 0 &&
-           a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0;
+           a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
+           ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
@@ -402,8 +448,14 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
     dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
 #define TG_AS(DT_, ACT_, TI_, TJ_)                                                               \
-    hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_>), grid, block, 0, s, a, tiles_m,   \
-                       tiles_n, group_m)
+    do {                                                                                         \
+        if (a.b_trans)                                                                           \
+            hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_, true>), grid, block, 0, s, \
+                               a, tiles_m, tiles_n, group_m);                                    \
+        else                                                                                     \
+            hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_, false>), grid, block, 0,   \
+                               s, a, tiles_m, tiles_n, group_m);                                 \
+    } while (0)
 #define TG_AS_CFG(DT_, ACT_)                                                                     \
     do {                                                                                         \
         if (cfg == 0)                                                                            \

@@ -1,6 +1,7 @@
 // gemm_generic.hip -- the correct-but-slow fallback for operands the 128-bit
 // MFMA path cannot take (pointers not 16-byte aligned, pitches that are not a
-// multiple of 8 elements).  One thread per output element, FP32 FMA over k,
+// multiple of 8 elements, a B stored [N,K] outside the shapes of the
+// asynchronous-copy kernel).  One thread per output element, FP32 FMA over k,
 // then the same FP32 epilogue and round-to-nearest-even store as the fast
 // path.  It is chosen only by explicit dispatch and reported through
 // tg_last_kernel(), never silently ("TIRx", section 5.4: a fallback comes
@@ -24,12 +25,17 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmArgs p)
          m += (int64_t)gridDim.y * 16) {
         const unsigned short *a = p.A + m * p.lda;
         float acc = 0.f;
+        // element (k, n) of op(B): B[k][n], or B[n][k] when B is stored [N,K]
+        const int64_t bk = p.b_trans ? 1 : p.ldb, bn = p.b_trans ? p.ldb : 1;
         for (int k = 0; k < p.K; ++k)
-            acc = __builtin_fmaf(from_bits<DT>(a[k]), from_bits<DT>(B[(int64_t)k * p.ldb + n]),
+            acc = __builtin_fmaf(from_bits<DT>(a[k]), from_bits<DT>(B[(int64_t)k * bk + n * bn]),
                                  acc);
         if (p.bias != nullptr)
             acc += from_bits<DT>(p.bias[n]);
-        C[m * p.ldc + n] = to_bits<DT>(activate<ACT>(acc));
+        float v = activate<ACT>(acc);
+        if (p.R != nullptr)
+            add_residual<DT, 1>(p.R, p.ldr, m, (int)n, p.N, &v);
+        C[m * p.ldc + n] = to_bits<DT>(v);
     }
 }
 

@@ -194,6 +194,8 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
                 v[r] = activate<ACT>(x);
             }
             if (m < M) {
+                if (p.R != nullptr)
+                    add_residual<DT, 4>(p.R, p.ldr, m, n, N, v);
                 unsigned short *cp = p.C[0] + (int64_t)m * p.ldc + n;
                 if (n + 4 <= N) {
                     u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
@@ -261,6 +263,8 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
                 x += from_bits<DT>(p.bias[nbase + i]);
             v[i] = activate<ACT>(x);
         }
+        if (p.R != nullptr)
+            add_residual<DT, 16>(p.R, p.ldr, rm, nbase, N, v);
         if (nbase + 16 <= N) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -483,6 +487,8 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                         x += from_bits<DT>(p.bias[n + r]);
                     v[r] = activate<ACT>(x);
                 }
+                if (p.R != nullptr)
+                    add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, v);
                 u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
                 *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
             }
@@ -568,6 +574,8 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                 x += from_bits<DT>(p.bias[cn + i]);
             v[i] = activate<ACT>(x);
         }
+        if (p.R != nullptr)
+            add_residual<DT, 16>(p.R, p.ldr, rm, cn, p.N, v);
         unsigned short *cp = p.C[0] + (int64_t)rm * p.ldc + cn;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -748,6 +756,8 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
                 o[r] = activate<ACT>(x);
             }
             if (m < M) {
+                if (p.R != nullptr)
+                    add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, o);
                 u32x2 ov = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
                 *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = ov;
             }

@@ -273,6 +273,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
                         v[r] = activate<ACT>(x);
                     }
                     if (!EDGE || m < M) {
+                        if (p.R != nullptr)
+                            add_residual<DT, 4>(p.R, p.ldr, m, n, N, v);
                         unsigned short *cp = Cm + (int64_t)m * p.ldc + n;
                         if (!EDGE || n + 4 <= N) {
                             u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};

@@ -155,7 +155,8 @@ int choose_async(const tg::GemmArgs &a, const char *force)
 
 tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
-              int64_t ldc, int n_mat, void *stream)
+              int64_t ldc, int n_mat, void *stream, int b_trans = 0, const void *R = nullptr,
+              int64_t ldr = 0)
 {
     if (dt != TG_DTYPE_F16 && dt != TG_DTYPE_BF16)
         return TG_ERROR_INVALID_VALUE;
@@ -167,7 +168,11 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         set_last("none");
         return TG_SUCCESS;
     }
-    if (lda < K || ldb < N || ldc < N)
+    // B is [K,N] (pitch >= N), or stored [N,K] (pitch >= K) when b_trans
+    const int64_t b_rows = b_trans ? N : K, b_cols = b_trans ? K : N;
+    if (lda < K || ldb < b_cols || ldc < N)
+        return TG_ERROR_INVALID_VALUE;
+    if (R != nullptr && (ldr < N || ((uintptr_t)R & 1u) != 0))
         return TG_ERROR_INVALID_VALUE;
     if (K > 0 && A == nullptr)
         return TG_ERROR_INVALID_VALUE;
@@ -181,12 +186,17 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (K > 0 && overlaps(c, span_of(A, M, K, lda)))
             return TG_ERROR_INVALID_VALUE;
         for (int u = 0; u < n_mat; ++u) {
-            if (K > 0 && overlaps(c, span_of(B[u], K, N, ldb)))
+            if (K > 0 && overlaps(c, span_of(B[u], b_rows, b_cols, ldb)))
                 return TG_ERROR_INVALID_VALUE;
             if (u != t && overlaps(c, span_of(C[u], M, N, ldc)))
                 return TG_ERROR_INVALID_VALUE;
         }
         if (bias && overlaps(c, span_of(bias, 1, N, N)))
+            return TG_ERROR_INVALID_VALUE;
+        // the residual may be C itself (each element is read before it is
+        // overwritten, by the thread that overwrites it or after a wait on
+        // that read), but not any other overlap
+        if (R && !(R == C[t] && ldr == ldc) && overlaps(c, span_of(R, M, N, ldr)))
             return TG_ERROR_INVALID_VALUE;
     }
     if (((uintptr_t)bias & 1u) != 0)
@@ -202,12 +212,16 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     a.ldb = ldb;
     a.ldc = ldc;
     a.bias = static_cast<const unsigned short *>(bias);
+    a.R = static_cast<const unsigned short *>(R);
+    a.ldr = R ? ldr : 0;
+    a.b_trans = b_trans;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
     a.n_mat = n_mat;
 
-    bool fast = (lda % 8 == 0) && (ldb % 8 == 0) && (ldc % 8 == 0) && (K == 0 || aligned16(A));
+    bool fast = (lda % 8 == 0) && (ldb % 8 == 0) && (ldc % 8 == 0) && (K == 0 || aligned16(A)) &&
+                (R == nullptr || (aligned16(R) && ldr % 8 == 0));
     for (int t = 0; t < n_mat; ++t)
         fast = fast && aligned16(C[t]) && (K == 0 || aligned16(B[t]));
 
@@ -222,10 +236,13 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     // reported as this launch's failure.
     (void)hipGetLastError();
     hipError_t err;
-    if (!fast || force_generic) {
+    const bool trans_async = b_trans && fast && !force_generic && choose_async(a, force) >= 0;
+    if (!fast || force_generic || (b_trans && !trans_async)) {
         err = tg::launch_generic(kdt, kact, a, s);
-        set_last(fast ? "generic_fma (forced)" : "generic_fma (unaligned operands)");
-    } else if (n_mat == 1 && M <= 16 && K >= 256 && N >= 256 && !force_tiled) {
+        set_last(!fast            ? "generic_fma (unaligned operands)"
+                 : force_generic ? "generic_fma (forced)"
+                                 : "generic_fma (B stored [N,K] outside the async tile shapes)");
+    } else if (n_mat == 1 && M <= 16 && K >= 256 && N >= 256 && !force_tiled && !b_trans) {
         const tg::SkinnyPlan pl = tg::plan_skinny(a.M, a.N, a.K);
         float *ws = nullptr;
         int *counters = nullptr;
@@ -245,7 +262,7 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                  pl.streaming == 2 ? "_cols" : (pl.streaming ? "_stream" : ""), pl.bn, pl.splits,
                  pl.k_chunk);
         set_last("skinny", detail);
-    } else if (!force_tiled && choose_async(a, force) >= 0) {
+    } else if ((!force_tiled || b_trans) && choose_async(a, force) >= 0) {
         const int cfg = choose_async(a, force);
         const int group_m = env_int("TG_GROUP_M", 4);
         err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
@@ -290,6 +307,18 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K, const v
     const void *Bs[3] = {B, nullptr, nullptr};
     void *Cs[3] = {C, nullptr, nullptr};
     return run(dt, M, N, K, A, lda, Bs, ldb, bias, act, Cs, ldc, 1, stream);
+}
+
+tg_status tg_gemm_ex(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     const void *B, int64_t ldb, tg_op op_b, const void *bias, tg_act act,
+                     const void *R, int64_t ldr, void *C, int64_t ldc, void *stream)
+{
+    if (op_b != TG_OP_N && op_b != TG_OP_T)
+        return TG_ERROR_INVALID_VALUE;
+    const void *Bs[3] = {B, B, B};
+    void *Cs[3] = {C, C, C};
+    return run(dt, M, N, K, A, lda, Bs, ldb, bias, act, Cs, ldc, 1, stream, op_b == TG_OP_T ? 1 : 0,
+               R, ldr);
 }
 
 tg_status tg_gemm_qkv(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *X, int64_t ldx,

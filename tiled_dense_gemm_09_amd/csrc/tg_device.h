@@ -160,6 +160,33 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v[r] += R[m][n + r] for r < CNT (the residual of the extended epilogue,
+// added after the activation and before the rounding).  Columns at or past N
+// are skipped; when all CNT columns are in range and CNT is a multiple of 4
+// the row segment is read with 8-byte loads (n a multiple of 4, R 16-byte
+// aligned and ldr a multiple of 8 on every path that passes CNT >= 4).
+template <int DT, int CNT>
+__device__ __forceinline__ void add_residual(const unsigned short *R, int64_t ldr, int64_t m,
+                                             int n, int N, float *v)
+{
+    const unsigned short *rp = R + m * ldr + n;
+    if (CNT % 4 == 0 && n + CNT <= N) {
+#pragma unroll
+        for (int q = 0; q < CNT / 4; ++q) {
+            const u32x2 w = *reinterpret_cast<const u32x2 *>(rp + 4 * q);
+            v[4 * q + 0] += from_bits<DT>((unsigned short)(w[0] & 0xFFFFu));
+            v[4 * q + 1] += from_bits<DT>((unsigned short)(w[0] >> 16));
+            v[4 * q + 2] += from_bits<DT>((unsigned short)(w[1] & 0xFFFFu));
+            v[4 * q + 3] += from_bits<DT>((unsigned short)(w[1] >> 16));
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < CNT; ++r)
+            if (n + r < N)
+                v[r] += from_bits<DT>(rp[r]);
+    }
+}
+
 // One 32x32x16 MFMA step: acc += src0 (32 rows x 16 k) * src1 (16 k x 32 cols).
 // Lane l holds 8 k-values of row (l % 32) of src0 and of column (l % 32) of
 // src1 (the same k order on both sides).  Accumulator register r of lane l is

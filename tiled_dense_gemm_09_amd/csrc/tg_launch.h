@@ -9,7 +9,8 @@ namespace tg {
 
 // Operands of one (possibly horizontally fused) GEMM launch.  n_mat is 1 for
 // a plain GEMM and 3 for the QKV projection; B[t] and C[t] are the t-th
-// weight and output.  All pitches are in elements.
+// weight and output.  All pitches are in elements.  Every kernel computes
+// C = act(A . op(B) + bias) + R with one rounding at the end.
 struct GemmArgs {
     const unsigned short *A;
     int64_t lda;
@@ -18,8 +19,11 @@ struct GemmArgs {
     unsigned short *C[3];
     int64_t ldc;
     const unsigned short *bias; // [N] or nullptr
+    const unsigned short *R;    // [M,N] residual added after the activation, or nullptr
+    int64_t ldr;
     int M, N, K;
     int n_mat;
+    int b_trans; // 1: B[t] is stored [N,K] (pitch ldb) and the product uses its transpose
 };
 
 // Tile configurations of the MFMA kernel: BM x BN output tile, BK deep,

@@ -7,6 +7,7 @@ There is no fallback: if the library is missing the import fails loudly.
     from tiled_dense_gemm_09_amd import tg
     c = tg.gemm(a, b)                       # a [M,K], b [K,N] -> c [M,N]
     c = tg.gemm(a, b, bias=bias, act="gelu_tanh")
+    c = tg.gemm(a, w.t(), residual=r)       # w stored [N,K]; c = a @ w.T + r
     q, k, v = tg.gemm_qkv(x, wq, wk, wv)
 """
 import ctypes
@@ -19,8 +20,9 @@ F16 = 1
 BF16 = 2
 ACT = {"none": 0, "gelu_tanh": 1}
 
-SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_qkv", "tg_status_string", "tg_last_kernel",
-           "tg_schedule_tile", "tg_lds_offset", "tg_in_bounds"]
+SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_qkv", "tg_status_string",
+           "tg_last_kernel", "tg_schedule_tile", "tg_lds_offset", "tg_in_bounds"]
+OP_N, OP_T = 0, 1
 
 
 class TgError(RuntimeError):
@@ -46,6 +48,8 @@ def _load():
     lib.tg_gemm.restype = I
     lib.tg_gemm_bias_act.argtypes = [I, L, L, L, P, L, P, L, P, I, P, L, P]
     lib.tg_gemm_bias_act.restype = I
+    lib.tg_gemm_ex.argtypes = [I, L, L, L, P, L, P, L, I, P, I, P, L, P, L, P]
+    lib.tg_gemm_ex.restype = I
     lib.tg_gemm_qkv.argtypes = [I, L, L, L, P, L, P, P, P, L, P, P, P, L, P]
     lib.tg_gemm_qkv.restype = I
     lib.tg_status_string.argtypes = [I]
@@ -84,6 +88,12 @@ def gemm_ptr(dt, M, N, K, A, lda, B, ldb, C, ldc, stream=0, bias=0, act=0):
                                     stream or None))
     else:
         _check(lib.tg_gemm(dt, M, N, K, A, lda, B, ldb, C, ldc, stream or None))
+
+
+def gemm_ex_ptr(dt, M, N, K, A, lda, B, ldb, op_b, C, ldc, stream=0, bias=0, act=0, R=0, ldr=0):
+    """tg_gemm_ex on raw device pointers (ints)."""
+    _check(lib.tg_gemm_ex(dt, M, N, K, A, lda, B, ldb, op_b, bias or None, act, R or None, ldr,
+                          C, ldc, stream or None))
 
 
 def gemm_qkv_ptr(dt, M, N, K, X, ldx, Wq, Wk, Wv, ldw, Q, Ko, V, ldo, stream=0):
@@ -140,8 +150,22 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def gemm(a, b, out=None, bias=None, act="none", stream=None):
-    """out = act(a @ b + bias); a [M,K], b [K,N], bias [N]; f16 or bf16."""
+def _operand_b(b):
+    """(op, ldb) for b [K,N]: row-major, or the transposed view of a row-major
+    [N,K] matrix (b = w.t()), which is passed as stored with TG_OP_T."""
+    if b.dim() != 2:
+        raise ValueError("b must be 2-D")
+    if not b.is_cuda:
+        raise ValueError("b must be a device tensor")
+    K, N = b.shape
+    if b.stride(0) == 1 and K > 1 and (N == 1 or b.stride(1) >= K):
+        return OP_T, max(b.stride(1), K)
+    return OP_N, _rowmajor(b, "b")
+
+
+def gemm(a, b, out=None, bias=None, act="none", residual=None, stream=None):
+    """out = act(a @ b + bias) + residual; a [M,K], b [K,N], bias [N], residual [M,N];
+    f16 or bf16.  b may be the transposed view of a row-major [N,K] weight."""
     torch = _torch()
     dt = _dt(a)
     if b.dtype != a.dtype or (bias is not None and bias.dtype != a.dtype):
@@ -154,14 +178,24 @@ def gemm(a, b, out=None, bias=None, act="none", stream=None):
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     if out.dtype != a.dtype or tuple(out.shape) != (M, N):
         raise ValueError("out must be [M,N] of the input dtype")
-    lda, ldb, ldc = _rowmajor(a, "a"), _rowmajor(b, "b"), _rowmajor(out, "out")
+    lda, ldc = _rowmajor(a, "a"), _rowmajor(out, "out")
+    op_b, ldb = _operand_b(b)
     bptr = 0
     if bias is not None:
         if bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
             raise ValueError("bias must be a dense [N] vector")
         bptr = bias.data_ptr()
-    gemm_ptr(dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
-             _stream(stream), bptr, ACT[act])
+    if residual is None and op_b == OP_N:
+        gemm_ptr(dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                 _stream(stream), bptr, ACT[act])
+        return out
+    rptr, ldr = 0, 0
+    if residual is not None:
+        if residual.dtype != a.dtype or tuple(residual.shape) != (M, N):
+            raise ValueError("residual must be [M,N] of the input dtype")
+        rptr, ldr = residual.data_ptr(), _rowmajor(residual, "residual")
+    gemm_ex_ptr(dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, op_b, out.data_ptr(), ldc,
+                _stream(stream), bptr, ACT[act], rptr, ldr)
     return out
 
 
