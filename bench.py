@@ -113,8 +113,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["main", "plain", "qkv", "square8192", "skinny", "small",
-                                       "vendor", "copy"],
+    ap.add_argument("--only", choices=["main", "plain", "ex", "qkv", "square8192", "skinny",
+                                       "small", "vendor", "copy"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -222,6 +222,26 @@ def run_secondary(args, torch, inputs, tg):
             "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4), "kernel": tg.last_kernel()}
         log("  ", out["f16_4096x4096x4096_no_epilogue"])
         del A, B, C
+
+    if args.only in (None, "ex"):
+        # the headline product with the weight stored [N,K] and a residual
+        # added after the activation (tg_gemm_ex, one launch)
+        p = inputs.config_problem("f16_4096_gelu")
+        A, bias = dev(p["A"], 1), dev(p["bias"], 1)
+        Wt = dev(np.ascontiguousarray(p["B"].T), 1)
+        R = dev(inputs.draw(np.random.default_rng(99), (p["M"], p["N"]), "uniform", 1), 1)
+        C = torch.empty((p["M"], p["N"]), dtype=torch.float16, device="cuda")
+        for label, b, res in (("f16_4096_gelu_B_stored_NK", Wt.t(), None),
+                              ("f16_4096_gelu_B_stored_NK_residual", Wt.t(), R),
+                              ("f16_4096_gelu_residual", dev(p["B"], 1), R)):
+            ms = time_launches(lambda: tg.gemm(A, b, out=C, bias=bias, act="gelu_tanh",
+                                               residual=res), steps, warm)
+            tf = 2.0 * p["M"] * p["N"] * p["K"] / (ms * 1e-3) / 1e12
+            out[label] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                          "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                          "kernel": tg.last_kernel()}
+            log("  ", label, out[label])
+        del A, bias, Wt, R, C
 
     if args.only in (None, "qkv"):
         q = inputs.config_problem("bf16_qkv")

@@ -23,8 +23,13 @@
 //    4 (j%4)..4 (j%4)+3, lane i receives column i at 4 consecutive k; two
 //    such reads give the 8 k of a 32x32x16 MFMA operand.
 //  - XOR swizzles (16-byte granules) make both the 128-bit A reads and the
-//    transposing B reads bank-conflict-free for 32 and for 64 LDS banks:
-//        A: granule c of row r at c ^ (((r >> 1) ^ (r >> 3)) & 3)
+//    transposing B reads bank-conflict-free.  A 128-bit LDS read is served
+//    16 lanes at a time from 64 four-byte banks (256 bytes), so the 16 rows
+//    of 64 bytes that lanes 16q..16q+15 read must land on 16 different
+//    16-byte bank groups: row r sits on groups 4 (r % 4) + (c ^ s(r)), and
+//    s(r) = (r >> 2) & 3 covers the four values for each r % 4 (measured
+//    with the bank-conflict counter on gfx950, as was the B pattern):
+//        A: granule c of row r at c ^ ((r >> 2) & 3)
 //        B: granule c of row r at c ^ {0, 6, 10, 12}[r & 3]
 //    (power-of-two extents throughout; "TIRx", section 7 on XOR layouts).
 #include <type_traits>
@@ -57,7 +62,7 @@ struct AsGeom {
     static_assert(BN >= 128, "the B swizzle needs at least 16 granules per row");
 };
 
-__host__ __device__ constexpr int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__host__ __device__ constexpr int swz_a(int r) { return (r >> 2) & 3; }
 // {0, 6, 10, 12}[r & 3] as a nibble table (a shift, not a branch chain)
 __host__ __device__ constexpr int swz_b(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
 
