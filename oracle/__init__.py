@@ -56,6 +56,9 @@ def _load():
                                     _L, _L, _L, _I]
         lib.tgo_gemm_ex_sample.argtypes = [_I, _L, _L, _L, _P, _L, _P, _L, _I, _P, _I, _P, _L,
                                            _L, _P, _P, _P, _P, _I]
+        lib.tgo_gemm_mx.argtypes = [_I, _I, _L, _L, _L, _P, _L, _P, _L, _P, _L, _P, _L, _P, _I,
+                                    _I, _P, _P, _L, _L, _L, _I]
+        lib.tgo_decode_fp8_array.argtypes = [_I, _L, _P, _P]
         lib.tgo_gemm_qkv.argtypes = [_I, _L, _L, _L, _P, _L, _P, _P, _P, _L, _P, _P, _P, _P, _P,
                                      _P, _L, _L, _L, _I]
         lib.tgo_decode_array.argtypes = [_I, _L, _P, _P]
@@ -197,6 +200,44 @@ def gemm_ex_sample(dt, A, B, ii, jj, trans_b=False, bias=None, act=ACT_NONE, R=N
     if rc:
         raise ValueError("oracle rejected the arguments")
     return f64, bits
+
+
+FP8_E4M3, FP8_E5M2, E8M0 = 0, 1, 2
+
+
+def decode_fp8(fmt, x):
+    """8-bit floats (FP8_E4M3 / FP8_E5M2) or e8m0 scales (E8M0) to double."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    out = np.empty(x.shape, np.float64)
+    _load().tgo_decode_fp8_array(fmt, x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def gemm_mx(fmt_a, fmt_b, A, SA, B, SB, bias=None, act=ACT_NONE, dt=BF16, rows=None, threads=0):
+    """Block-scaled 8-bit GEMM: A [M,K] and B [N,K] bytes, SA [K/32,M] and
+    SB [K/32,N] e8m0 bytes; C = round_dt(act(sum_k a*sa * b*sb + bias)).
+    Returns (f64, bits) for rows [r0, r1)."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    SA = np.ascontiguousarray(SA, dtype=np.uint8)
+    SB = np.ascontiguousarray(SB, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K or K % 32 or SA.shape != (K // 32, M) or SB.shape != (K // 32, N):
+        raise ValueError("operand shapes do not match")
+    if bias is not None:
+        bias = _bits(bias)
+        if bias.shape != (N,):
+            raise ValueError("bias must be [N]")
+    r0, r1 = (0, M) if rows is None else rows
+    f64 = np.zeros((M, N), np.float64)
+    bits = np.zeros((M, N), np.uint16)
+    rc = _load().tgo_gemm_mx(fmt_a, fmt_b, M, N, K, _ptr(A), K, _ptr(SA), M, _ptr(B), K,
+                             _ptr(SB), N, _ptr(bias), act, dt, _ptr(f64), _ptr(bits), N, r0, r1,
+                             threads)
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+    return f64[r0:r1], bits[r0:r1]
 
 
 def gemm_qkv(dt, X, Wq, Wk, Wv, rows=None, threads=0):

@@ -36,13 +36,26 @@
  *   [N,K], one output feature per row): the same logical operand with its
  *   two axes permuted, the placement unchanged ("TIRx", section 5.1,
  *   permute).
+ * - The block-scaled low-precision form (tgo_gemm_mx) computes
+ *     C[i][j] = round_dt( act( sum_k  a(A[i][k]) 2^(SA[k/32][i] - 127)
+ *                                   * b(B[j][k]) 2^(SB[k/32][j] - 127) + bias[j] ) )
+ *   with A [M,K] and B [N,K] in an 8-bit float format (e4m3 or e5m2) and
+ *   one 8-bit power-of-two scale (e8m0) per 32 consecutive k of each row of
+ *   A and each column of B ("TIRx", section 6: the FP8 GEMM with e8m0
+ *   block-wise scaling).  The pages fix neither the block length nor the
+ *   axes; 32 along K is the block of the OCP microscaling formats and of
+ *   the gfx950 matrix cores.  Products of two 8-bit floats and two powers
+ *   of two are exact in double.
  *
  * Every output element depends only on its own row of A and column of B,
  * so rows are split across OpenMP threads; the value of each element does
  * not depend on the thread count.
  *
  * Codecs: f16/bf16 <-> double are written here from the IEEE 754 binary16
- * and the bfloat16 (truncated binary32) bit layouts.
+ * and the bfloat16 (truncated binary32) bit layouts; the 8-bit formats from
+ * the OCP 8-bit floating point layouts (e4m3: bias 7, no infinities, NaN
+ * at exponent and mantissa all ones; e5m2: bias 15, IEEE-style infinities
+ * and NaNs) and e8m0 (an exponent only, bias 127, 0xFF = NaN).
  */
 #include <math.h>
 #include <stdint.h>
@@ -132,6 +145,32 @@ static uint16_t tgo_round_bits(double x, int p, int emin, int emax, int ebits)
 
 uint16_t tgo_double_to_f16(double x) { return tgo_round_bits(x, 11, -14, 15, 5); }
 uint16_t tgo_double_to_bf16(double x) { return tgo_round_bits(x, 8, -126, 127, 8); }
+
+/* 8-bit floats (OCP).  e4m3: 1 sign, 4 exponent (bias 7), 3 fraction bits;
+ * exponent 15 with fraction 7 is NaN, there are no infinities.  e5m2: 1
+ * sign, 5 exponent (bias 15), 2 fraction bits, IEEE-style specials. */
+enum { TGO_FP8_E4M3 = 0, TGO_FP8_E5M2 = 1 };
+
+double tgo_fp8_to_double(int fmt, uint8_t x)
+{
+    const int s = (x >> 7) & 1;
+    double v;
+    if (fmt == TGO_FP8_E4M3) {
+        const int e = (x >> 3) & 15, f = x & 7;
+        if (e == 15 && f == 7)
+            return NAN;
+        v = e == 0 ? ldexp((double)f, -9) : ldexp(8.0 + f, e - 10); /* (1 + f/8) 2^(e-7) */
+    } else {
+        const int e = (x >> 2) & 31, f = x & 3;
+        if (e == 31)
+            return f ? NAN : (s ? -INFINITY : INFINITY);
+        v = e == 0 ? ldexp((double)f, -16) : ldexp(4.0 + f, e - 17); /* (1 + f/4) 2^(e-15) */
+    }
+    return s ? -v : v;
+}
+
+/* e8m0 scale: 2^(e - 127); 0xFF is NaN. */
+double tgo_e8m0_to_double(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
 
 static double decode(int dt, uint16_t v)
 {
@@ -329,6 +368,80 @@ int tgo_gemm_qkv(int dt, int64_t M, int64_t N, int64_t K, const uint16_t *X, int
         if (rc)
             return rc;
     }
+    return 0;
+}
+
+/*
+ * Block-scaled 8-bit GEMM over output rows [row0, row1).  A is [M,K] bytes
+ * (pitch lda), B is [N,K] bytes (pitch ldb), SA is [K/32][M] scale bytes
+ * (pitch ldsa: the M scales of one k-block are contiguous), SB is [K/32][N]
+ * (pitch ldsb).  bias is [N] in the output dtype dt, or NULL.  Outputs as in
+ * tgo_gemm_ex.  K must be a multiple of 32.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int tgo_gemm_mx(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                int64_t lda, const uint8_t *SA, int64_t ldsa, const uint8_t *B, int64_t ldb,
+                const uint8_t *SB, int64_t ldsb, const uint16_t *bias, int act, int dt,
+                double *out_f64, uint16_t *out_bits, int64_t ldc, int64_t row0, int64_t row1,
+                int threads)
+{
+    if ((dt != TGO_F16 && dt != TGO_BF16) || (act != TGO_ACT_NONE && act != TGO_ACT_GELU_TANH))
+        return -1;
+    if ((fmt_a != TGO_FP8_E4M3 && fmt_a != TGO_FP8_E5M2) ||
+        (fmt_b != TGO_FP8_E4M3 && fmt_b != TGO_FP8_E5M2))
+        return -1;
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || row0 < 0 || row1 > M || row0 > row1 ||
+        ldc < N)
+        return -1;
+    if (row0 == row1 || N == 0)
+        return 0;
+    /* opB with its scales applied, column-major double copy (speed only) */
+    double *bt = (double *)malloc(sizeof(double) * (size_t)(N * (K > 0 ? K : 1)));
+    if (!bt)
+        return -1;
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            bt[j * K + k] = tgo_fp8_to_double(fmt_b, B[j * ldb + k]) *
+                            tgo_e8m0_to_double(SB[(k / 32) * ldsb + j]);
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#pragma omp parallel
+#endif
+    {
+        double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = row0; i < row1; ++i) {
+            for (int64_t k = 0; k < K; ++k)
+                arow[k] = tgo_fp8_to_double(fmt_a, A[i * lda + k]) *
+                          tgo_e8m0_to_double(SA[(k / 32) * ldsa + i]);
+            for (int64_t j = 0; j < N; ++j) {
+                const double *bcol = bt + j * K;
+                double sum = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    sum += arow[k] * bcol[k];
+                if (bias)
+                    sum += decode(dt, bias[j]);
+                const double v = activate(act, sum);
+                if (out_f64)
+                    out_f64[i * ldc + j] = v;
+                if (out_bits)
+                    out_bits[i * ldc + j] = encode(dt, v);
+            }
+        }
+        free(arow);
+    }
+    free(bt);
+    return 0;
+}
+
+/* Decode n 8-bit floats (fmt) or, with fmt = 2, e8m0 scales. */
+int tgo_decode_fp8_array(int fmt, int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fmt == 2 ? tgo_e8m0_to_double(in[i]) : tgo_fp8_to_double(fmt, in[i]);
     return 0;
 }
 

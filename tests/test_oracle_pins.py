@@ -13,6 +13,9 @@ fix it with mathematics and independent code:
   product;
 * GELU_tanh against its odd-part identity, its asymptotes and an exactly
   solvable point (tanh(ln 3) = 4/5);
+* the 8-bit float and e8m0 decoders against torch's float8 types over every
+  pattern; the block-scaled GEMM against the f16 GEMM (unit scales), a closed
+  form for the scales and rational brute force;
 * the epilogue order (bias before activation, residual after it), QKV =
   three GEMMs, the transposed-operand form against brute force and against
   the same operand stored the other way, and independence of the thread
@@ -448,6 +451,93 @@ def test_ex_sample_matches_full():
     fs, bs = oracle.gemm_ex_sample(BF16, p["A"], Bt, ii, jj, trans_b=True, bias=p["bias"],
                                    act=oracle.ACT_GELU_TANH, R=R)
     assert np.array_equal(fs, f[ii, jj]) and np.array_equal(bs, b[ii, jj])
+
+
+# -------------------------------------- block-scaled 8-bit GEMM (e8m0 scales)
+
+ALL8 = np.arange(256, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("fmt,tname", [(oracle.FP8_E4M3, "float8_e4m3fn"),
+                                       (oracle.FP8_E5M2, "float8_e5m2")])
+def test_fp8_decode_matches_torch_on_every_pattern(fmt, tname):
+    torch = pytest.importorskip("torch")
+    ref = torch.from_numpy(ALL8.copy()).view(getattr(torch, tname)).to(torch.float64).numpy()
+    got = oracle.decode_fp8(fmt, ALL8)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e8m0_decode_is_a_power_of_two():
+    got = oracle.decode_fp8(oracle.E8M0, ALL8)
+    assert np.isnan(got[255])
+    for e in range(255):
+        assert got[e] == math.ldexp(1.0, e - 127)
+
+
+def _fp8_bits(fmt, rng, shape):
+    """Random finite 8-bit patterns (NaN and infinity patterns redrawn)."""
+    v = rng.integers(0, 256, shape).astype(np.uint8)
+    d = oracle.decode_fp8(fmt, v)
+    bad = ~np.isfinite(d)
+    while bad.any():
+        v[bad] = rng.integers(0, 256, int(bad.sum())).astype(np.uint8)
+        d = oracle.decode_fp8(fmt, v)
+        bad = ~np.isfinite(d)
+    return v
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 1), (0, 1)])
+def test_mx_with_unit_scales_is_the_f16_gemm(fa, fb):
+    # every e4m3 / e5m2 value is an f16 value, so with scales 2^0 the
+    # block-scaled product must be the (pinned) f16 GEMM of the decoded values
+    rng = np.random.default_rng(50 + fa + 2 * fb)
+    M, N, K = 7, 9, 96
+    A = _fp8_bits(fa, rng, (M, K))
+    Bt = _fp8_bits(fb, rng, (N, K))
+    SA = np.full((K // 32, M), 127, np.uint8)
+    SB = np.full((K // 32, N), 127, np.uint8)
+    f1, b1 = oracle.gemm_mx(fa, fb, A, SA, Bt, SB, dt=F16)
+    a16 = bits_of(F16, oracle.decode_fp8(fa, A))
+    b16 = bits_of(F16, oracle.decode_fp8(fb, Bt).T)
+    f2, b2 = oracle.gemm(F16, a16, b16)
+    assert np.array_equal(f1, f2) and np.array_equal(b1, b2)
+
+
+def test_mx_block_scales_closed_form():
+    # A = B = 1: C[i][j] = sum over k-blocks b of 32 * 2^(sa[b][i] - 127) * 2^(sb[b][j] - 127)
+    M, N, K = 3, 4, 128
+    one = 0x38  # e4m3 1.0
+    A = np.full((M, K), one, np.uint8)
+    Bt = np.full((N, K), one, np.uint8)
+    SA = np.array([[127 + b + i for i in range(M)] for b in range(K // 32)], np.uint8)
+    SB = np.array([[125 + (b * j) % 3 for j in range(N)] for b in range(K // 32)], np.uint8)
+    f64, _ = oracle.gemm_mx(0, 0, A, SA, Bt, SB)
+    for i in range(M):
+        for j in range(N):
+            ref = sum(32 * 2.0 ** (int(SA[b, i]) - 127) * 2.0 ** (int(SB[b, j]) - 127)
+                      for b in range(K // 32))
+            assert f64[i, j] == ref
+
+
+def test_mx_brute_force_rational_nonsquare():
+    rng = np.random.default_rng(52)
+    M, N, K = 2, 3, 64
+    A = _fp8_bits(0, rng, (M, K))
+    Bt = _fp8_bits(1, rng, (N, K))
+    SA = rng.integers(120, 134, (K // 32, M)).astype(np.uint8)
+    SB = rng.integers(120, 134, (K // 32, N)).astype(np.uint8)
+    f64, _ = oracle.gemm_mx(0, 1, A, SA, Bt, SB)
+    av, bv = oracle.decode_fp8(0, A), oracle.decode_fp8(1, Bt)
+    for i in range(M):
+        for j in range(N):
+            exact = sum((Fraction(float(av[i, k])) * Fraction(2) ** (int(SA[k // 32, i]) - 127) *
+                         Fraction(float(bv[j, k])) * Fraction(2) ** (int(SB[k // 32, j]) - 127)
+                         for k in range(K)), Fraction(0))
+            bound = sum(abs(float(av[i, k]) * float(bv[j, k])) * 2.0 ** (int(SA[k // 32, i]) +
+                        int(SB[k // 32, j]) - 254) for k in range(K)) * K * 2.0 ** -52
+            assert abs(Fraction(float(f64[i, j])) - exact) <= Fraction(bound)
 
 
 def test_qkv_is_three_gemms():

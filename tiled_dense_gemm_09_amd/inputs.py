@@ -75,6 +75,53 @@ def qkv_problem(dt, M, N, K, seed, kind="normal", x_scale=1.0, w_scale=None):
     return dict(dt=dt, M=M, N=N, K=K, X=X, W=Ws)
 
 
+# ------------------------------------------- block-scaled 8-bit operands
+
+FP8_E4M3, FP8_E5M2 = 0, 1
+_FP8_MAX = {FP8_E4M3: 448.0, FP8_E5M2: 57344.0}
+
+
+def to_fp8(x, fmt):
+    """float64 array -> 8-bit float bytes (OCP e4m3 / e5m2, round to nearest
+    even through torch's float8 conversion of the float32 value)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.to(torch.float8_e4m3fn if fmt == FP8_E4M3 else torch.float8_e5m2)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def mx_quantize(x, fmt):
+    """Rows of x [R, K] -> (bytes [R, K], e8m0 scales [K/32, R]).  Each row's
+    32-element k-block gets the smallest power of two 2^(e - 127) that brings
+    its largest magnitude within the format's largest finite value (the
+    microscaling recipe); the block is divided by it and rounded."""
+    R, K = x.shape
+    peak = np.abs(x).reshape(R, K // 32, 32).max(axis=2)
+    e = np.ceil(np.log2(np.maximum(peak, 1e-30) / _FP8_MAX[fmt])).astype(np.int64) + 127
+    e = np.clip(e, 1, 254)
+    q = to_fp8(x / np.repeat(np.ldexp(1.0, e - 127), 32, axis=1), fmt)
+    return q, np.ascontiguousarray(e.T.astype(np.uint8))
+
+
+def mx_problem(fmt_a, fmt_b, M, N, K, seed, kind="normal", bias=False, act=ACT_NONE, dt=BF16):
+    """A [M,K] and B [N,K] 8-bit operands with e8m0 scales SA [K/32,M] and
+    SB [K/32,N].  kind "normal": A ~ N(0,1), B ~ N(0, 1/K), quantized per
+    32-block; kind "int": entries in {-2..2} and scales 2^-2..2^2, so every
+    FP32 partial sum is exact in any order (|sum| < 2^20, step 2^-4)."""
+    rng = np.random.default_rng(seed)
+    if kind == "int":
+        A = to_fp8(rng.integers(-2, 3, (M, K)), fmt_a)
+        Bt = to_fp8(rng.integers(-2, 3, (N, K)), fmt_b)
+        SA = rng.integers(125, 130, (K // 32, M)).astype(np.uint8)
+        SB = rng.integers(125, 130, (K // 32, N)).astype(np.uint8)
+    else:
+        A, SA = mx_quantize(rng.standard_normal((M, K)), fmt_a)
+        Bt, SB = mx_quantize(rng.standard_normal((N, K)) / math.sqrt(K), fmt_b)
+    bv = draw(rng, (N,), "int" if kind == "int" else "bias", dt) if bias else None
+    return dict(fmt_a=fmt_a, fmt_b=fmt_b, M=M, N=N, K=K, A=A, SA=SA, B=Bt, SB=SB, bias=bv,
+                act=act, dt=dt)
+
+
 # The five workloads.  Config names follow their shapes.
 CONFIGS = {
     # f16 256^3, U[-1,1]; integer variant {-2..2}
