@@ -118,6 +118,41 @@ tg_status tg_gemm_ex(tg_dtype dt, int64_t M, int64_t N, int64_t K,
                      void *C, int64_t ldc,
                      void *stream);
 
+/* 8-bit float formats of tg_gemm_mx (OCP 8-bit floating point). */
+typedef enum {
+    TG_FP8_E4M3 = 0, /* 1 sign, 4 exponent (bias 7), 3 fraction bits; no infinities, max 448 */
+    TG_FP8_E5M2 = 1  /* 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style specials */
+} tg_fp8_format;
+
+/* Block-scaled 8-bit GEMM:
+ *   C[m][n] = act( sum_k a(A[m][k]) 2^(SA[k/32][m] - 127) * b(B[n][k]) 2^(SB[k/32][n] - 127)
+ *                  + bias[n] ),
+ * FP32 accumulation and epilogue, one rounding to out_dt.  "TIRx", section
+ * 6: the FP8 GEMM with e8m0 block-wise scaling.  The pages fix neither the
+ * block length nor the axes; here one e8m0 scale (an exponent byte, 2^(e-127),
+ * 0xFF = NaN) covers 32 consecutive k of one row of A or one column of B,
+ * the block of the OCP microscaling formats and of gfx950's scaled matrix
+ * cores.  Coarser schemes (1x128, 128x128) are the same with repeated scales.
+ *  - A: [M,K] bytes, row pitch lda >= K (bytes).  B: stored [N,K] (one output
+ *    column per row, K-contiguous like A), pitch ldb >= K.
+ *  - scale_a: [K/32][M] bytes, pitch ld_sa >= M: block-major, the M scales
+ *    of one k-block contiguous (so that each k-step's scales are contiguous
+ *    runs); scale_b: [K/32][N], pitch ld_sb >= N.
+ *  - bias: [N] in out_dt or NULL; C: [M,N] in out_dt, pitch ldc >= N.
+ *  - K must be a multiple of 32.  M, N multiples of 256 and K of 256 with
+ *    16-byte aligned operands and scales, byte pitches multiples of 16 and
+ *    ldc a multiple of 8 run the MFMA kernel; anything else runs a slower
+ *    fallback kernel (reported by tg_last_kernel()).
+ *  - Validation and asynchronous execution as for the other entry points; C
+ *    must not overlap any input. */
+tg_status tg_gemm_mx(tg_fp8_format fmt_a, tg_fp8_format fmt_b,
+                     int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, const void *scale_a, int64_t ld_sa,
+                     const void *B, int64_t ldb, const void *scale_b, int64_t ld_sb,
+                     const void *bias, tg_act act, tg_dtype out_dt,
+                     void *C, int64_t ldc,
+                     void *stream);
+
 /* Horizontally fused projection, one launch:
  *     Q = X . Wq,  Kout = X . Wk,  V = X . Wv.
  * X is [M,K] (pitch ldx); Wq, Wk, Wv are each [K,N] (shared pitch ldw);

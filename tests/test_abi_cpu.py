@@ -94,6 +94,33 @@ def test_extended_empty_problem_is_a_noop():
                              FAKE_C, 64, None) == 0
 
 
+FAKE_SA = 0x7F0040000000
+FAKE_SB = 0x7F0050000000
+
+
+@pytest.mark.parametrize("args", [
+    dict(fa=3),                       # unknown 8-bit format
+    dict(odt=7),                      # unknown output dtype
+    dict(K=48),                       # K not a multiple of the 32-element scale block
+    dict(lda=63),                     # A pitch (bytes) shorter than K
+    dict(ldb=63),
+    dict(ldsa=255),                   # scale pitch shorter than M
+    dict(ldsb=255),
+    dict(SA=0),                       # NULL scales
+    dict(C=FAKE_A + 128),             # output overlapping A
+    dict(C=FAKE_SB + 64),             # output overlapping the B scales
+    dict(act=4),
+])
+def test_invalid_mx_arguments_launch_nothing(args):
+    a = dict(fa=0, fb=1, M=256, N=256, K=64, A=FAKE_A, lda=64, SA=FAKE_SA, ldsa=256, B=FAKE_B,
+             ldb=64, SB=FAKE_SB, ldsb=256, bias=0, act=0, odt=2, C=FAKE_C, ldc=256)
+    a.update(args)
+    st = tg.lib.tg_gemm_mx(a["fa"], a["fb"], a["M"], a["N"], a["K"], a["A"], a["lda"],
+                           a["SA"] or None, a["ldsa"], a["B"], a["ldb"], a["SB"], a["ldsb"],
+                           a["bias"] or None, a["act"], a["odt"], a["C"], a["ldc"], None)
+    assert st == 1
+
+
 def test_qkv_outputs_must_not_overlap():
     st = tg.lib.tg_gemm_qkv(2, 64, 64, 64, FAKE_A, 64, FAKE_B, FAKE_B + 2 ** 20, FAKE_B + 2 ** 21,
                             64, FAKE_C, FAKE_C + 128, FAKE_C + 2 ** 20, 64, None)

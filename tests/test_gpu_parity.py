@@ -431,6 +431,73 @@ def test_transposed_b_full_size_sampled(tg):
     util.check_tol(F16, bits[ii, jj], f64, "4096 B[N,K] + residual", ref_bits=rbits)
 
 
+# -------------------------------------- block-scaled 8-bit GEMM (e8m0 scales)
+
+def run_mx(tg, p, out_dtype=None):
+    import torch
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bias = util.to_dev(p["bias"], p["dt"]) if p.get("bias") is not None else None
+    names = {inputs.FP8_E4M3: "e4m3", inputs.FP8_E5M2: "e5m2"}
+    C = tg.gemm_mx(dev(p["A"]), dev(p["SA"]), dev(p["B"]), dev(p["SB"]), names[p["fmt_a"]],
+                   names[p["fmt_b"]], bias=bias,
+                   act="gelu_tanh" if p["act"] == inputs.ACT_GELU_TANH else "none",
+                   out_dtype=util.torch_dtype(p["dt"]))
+    torch.cuda.synchronize()
+    return util.to_bits(C), tg.last_kernel()
+
+
+MX_FORMATS = [(0, 0), (1, 1), (0, 1), (1, 0)]
+
+
+@pytest.mark.parametrize("fa,fb", MX_FORMATS)
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (100, 72, 96)])
+def test_mx_integer_exact(tg, fa, fb, M, N, K):
+    # entries in {-2..2}, scales 2^-2..2^2: every FP32 partial sum is exact
+    p = inputs.mx_problem(fa, fb, M, N, K, seed=120 + 2 * fa + fb, kind="int", bias=True,
+                          dt=BF16 if fa == fb else F16)
+    say("case mx integer", fa, fb, M, N, K)
+    bits, kern = run_mx(tg, p)
+    say("  kernel", kern)
+    assert kern.startswith("mx_256x256" if M % 256 == 0 and N % 256 == 0 else "mx_generic")
+    _, ref = oracle.gemm_mx(fa, fb, p["A"], p["SA"], p["B"], p["SB"], p["bias"], dt=p["dt"])
+    util.check_exact(bits, ref, "mx %s" % kern)
+
+
+@pytest.mark.parametrize("fa,fb", MX_FORMATS[:3])
+def test_mx_random_bias_gelu(tg, fa, fb):
+    p = inputs.mx_problem(fa, fb, 512, 512, 1024, seed=130 + fa + fb, bias=True,
+                          act=inputs.ACT_GELU_TANH)
+    say("case mx random bias+gelu", fa, fb)
+    bits, kern = run_mx(tg, p)
+    assert kern.startswith("mx_256x256")
+    f64, rbits = oracle.gemm_mx(fa, fb, p["A"], p["SA"], p["B"], p["SB"], p["bias"],
+                                oracle.ACT_GELU_TANH, dt=BF16)
+    util.check_tol(BF16, bits, f64, "mx random", ref_bits=rbits)
+
+
+def test_mx_generic_matches_fast_path(tg, monkeypatch):
+    p = inputs.mx_problem(0, 0, 256, 256, 512, seed=140)
+    fast, k1 = run_mx(tg, p)
+    monkeypatch.setenv("TG_FORCE_CONFIG", "generic")
+    slow, k2 = run_mx(tg, p)
+    assert k1.startswith("mx_256x256") and k2.startswith("mx_generic")
+    f64, rbits = oracle.gemm_mx(0, 0, p["A"], p["SA"], p["B"], p["SB"], dt=BF16)
+    util.check_tol(BF16, fast, f64, "mx fast", ref_bits=rbits)
+    util.check_tol(BF16, slow, f64, "mx generic", ref_bits=rbits)
+
+
+def test_mx_full_size_rows(tg):
+    # 4096^3, e4m3 x e4m3 with microscaled N(0,1) data; whole rows checked
+    p = inputs.mx_problem(0, 0, 4096, 4096, 4096, seed=150, bias=True)
+    say("case mx 4096^3")
+    bits, kern = run_mx(tg, p)
+    assert kern.startswith("mx_256x256")
+    for r0 in (0, 2047, 4092):
+        f64, rbits = oracle.gemm_mx(0, 0, p["A"], p["SA"], p["B"], p["SB"], p["bias"], dt=BF16,
+                                    rows=(r0, r0 + 4))
+        util.check_tol(BF16, bits[r0:r0 + 4], f64, "mx 4096 rows %d" % r0, ref_bits=rbits)
+
+
 def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")

@@ -36,6 +36,7 @@
 
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_pipeline.h"
 
 namespace tg {
 
@@ -62,33 +63,8 @@ struct AsGeom {
     static_assert(BN >= 128, "the B swizzle needs at least 16 granules per row");
 };
 
-__host__ __device__ constexpr int swz_a(int r) { return (r >> 2) & 3; }
 // {0, 6, 10, 12}[r & 3] as a nibble table (a shift, not a branch chain)
 __host__ __device__ constexpr int swz_b(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
-
-// Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
-// workgroup release fence, which waits for every outstanding direct-to-LDS
-// copy (they count as LDS writes) and would drain all stages each step.  Here
-// each wave waits for exactly the copies it needs with wait_vmcnt first; the
-// empty asm statements keep the compiler from moving LDS accesses across the
-// barrier.
-__device__ __forceinline__ void stage_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 } // namespace
 
@@ -358,69 +334,18 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
 
-    // ---- epilogue.  Lane l of a 32x32 accumulator block holds row m = l % 32
-    // and columns n = 8g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
-    // activation and rounding happen there; the rounded (32 TI) x (32 TJ)
-    // tile of the wave is then restaged through LDS (inside the wave's own
-    // stage: rows of 4 TJ 16-byte granules, granule c of row r at
-    // c ^ (r % 4TJ)) so that each global store writes whole 64 TJ-byte row
-    // segments instead of 16-byte pieces of 32 rows.
-    constexpr int EG = 4 * TJ;              // granules per row of the wave tile
+    // ---- epilogue: activation, residual and rounding in registers, the
+    // rounded wave tile restaged through the wave's own stage for whole-row
+    // stores.
     static_assert(2048 * TI * TJ <= G::STAGE_BYTES, "wave tile must fit its stage");
     unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    // The residual (if any) is added after the activation, before rounding;
-    // its 4-column pieces are read in the accumulator layout, one row block
-    // of loads at a time.
-    auto to_lds = [&](auto has_res) {
-        constexpr bool HR = decltype(has_res)::value;
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int r = i * 32 + (lane & 31);
-            const int m = m0 + wave_m * 32 * TI + r;
-            u32x2 rr[TJ][4];
-            if constexpr (HR) {
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        rr[j][g] = *reinterpret_cast<const u32x2 *>(
-                            p.R + (int64_t)m * p.ldr + n0 + wave_n * 32 * TJ + j * 32 + g * 8 +
-                            (lane >> 5) * 4);
-            }
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[e] = activate<ACT>(acc[i][j][4 * g + e]);
-                        if constexpr (HR)
-                            v[e] += from_bits<DT>(
-                                (unsigned short)(rr[j][g][e >> 1] >> (16 * (e & 1))));
-                    }
-                    const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                    const int c = (4 * j + g) ^ (r & (EG - 1));
-                    *reinterpret_cast<u32x2 *>(ep + r * (16 * EG) + c * 16 + (lane >> 5) * 8) = o;
-                }
-            }
-        }
-    };
+    const int64_t cm = m0 + wave_m * 32 * TI, cn = n0 + wave_n * 32 * TJ;
+    unsigned short *cw = Cm + cm * p.ldc + cn;
     if (p.R != nullptr)
-        to_lds(std::true_type{});
+        restaged_epilogue<DT, ACT, TI, TJ, true>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
+                                                 p.ldr);
     else
-        to_lds(std::false_type{});
-    // each lane reads back granule lane % EG of rows (64 / EG) t + lane / EG
-    // (its own wave's writes, so no barrier) and stores it
-    unsigned short *crow = Cm + (int64_t)(m0 + wave_m * 32 * TI) * p.ldc + n0 + wave_n * 32 * TJ +
-                           (lane % EG) * 8;
-#pragma unroll
-    for (int t = 0; t < 2 * TI * TJ; ++t) {
-        const int r = (64 / EG) * t + lane / EG;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * EG) +
-                                                         (((lane % EG) ^ (r & (EG - 1))) * 16));
-        *reinterpret_cast<u32x4 *>(crow + (int64_t)r * p.ldc) = v;
-    }
+        restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0);
 }
 
 namespace {

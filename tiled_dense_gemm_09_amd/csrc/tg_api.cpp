@@ -330,6 +330,93 @@ tg_status tg_gemm_qkv(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *
     return run(dt, M, N, K, X, ldx, Bs, ldw, nullptr, TG_ACT_NONE, Cs, ldo, 3, stream);
 }
 
+tg_status tg_gemm_mx(tg_fp8_format fmt_a, tg_fp8_format fmt_b, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, const void *scale_a, int64_t ld_sa,
+                     const void *B, int64_t ldb, const void *scale_b, int64_t ld_sb,
+                     const void *bias, tg_act act, tg_dtype out_dt, void *C, int64_t ldc,
+                     void *stream)
+{
+    if ((fmt_a != TG_FP8_E4M3 && fmt_a != TG_FP8_E5M2) ||
+        (fmt_b != TG_FP8_E4M3 && fmt_b != TG_FP8_E5M2))
+        return TG_ERROR_INVALID_VALUE;
+    if (out_dt != TG_DTYPE_F16 && out_dt != TG_DTYPE_BF16)
+        return TG_ERROR_INVALID_VALUE;
+    if (act != TG_ACT_NONE && act != TG_ACT_GELU_TANH)
+        return TG_ERROR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || K % 32 != 0)
+        return TG_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        set_last("none");
+        return TG_SUCCESS;
+    }
+    const int64_t KB = K / 32;
+    if (ldc < N || (K > 0 && (lda < K || ldb < K || ld_sa < M || ld_sb < N)))
+        return TG_ERROR_INVALID_VALUE;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr || scale_a == nullptr ||
+                                   scale_b == nullptr)))
+        return TG_ERROR_INVALID_VALUE;
+    if (((uintptr_t)bias & 1u) != 0 || ((uintptr_t)C & 1u) != 0)
+        return TG_ERROR_INVALID_VALUE;
+    // C must not overlap any input (byte spans; the 8-bit operands and the
+    // scales are byte matrices, C and bias 16-bit)
+    auto bytes = [](const void *p, int64_t rows, int64_t cols, int64_t ld) {
+        Span sp;
+        sp.lo = (uintptr_t)p;
+        sp.hi = rows > 0 && cols > 0 ? sp.lo + (uintptr_t)((rows - 1) * ld + cols) : sp.lo;
+        return sp;
+    };
+    const Span c = span_of(C, M, N, ldc);
+    if (K > 0 && (overlaps(c, bytes(A, M, K, lda)) || overlaps(c, bytes(B, N, K, ldb)) ||
+                  overlaps(c, bytes(scale_a, KB, M, ld_sa)) ||
+                  overlaps(c, bytes(scale_b, KB, N, ld_sb))))
+        return TG_ERROR_INVALID_VALUE;
+    if (bias && overlaps(c, span_of(bias, 1, N, N)))
+        return TG_ERROR_INVALID_VALUE;
+
+    tg::MxArgs a;
+    a.A = static_cast<const unsigned char *>(A);
+    a.lda = lda;
+    a.SA = static_cast<const unsigned char *>(scale_a);
+    a.ldsa = ld_sa;
+    a.B = static_cast<const unsigned char *>(B);
+    a.ldb = ldb;
+    a.SB = static_cast<const unsigned char *>(scale_b);
+    a.ldsb = ld_sb;
+    a.bias = static_cast<const unsigned short *>(bias);
+    a.C = static_cast<unsigned short *>(C);
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.fmt_a = fmt_a == TG_FP8_E5M2 ? 1 : 0;
+    a.fmt_b = fmt_b == TG_FP8_E5M2 ? 1 : 0;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int kdt = out_dt == TG_DTYPE_F16 ? tg::DT_F16 : tg::DT_BF16;
+    const int kact = act == TG_ACT_GELU_TANH ? tg::ACT_GELU : tg::ACT_NONE;
+    const char *force = getenv("TG_FORCE_CONFIG");
+    const bool force_generic = force && strcmp(force, "generic") == 0;
+    (void)hipGetLastError();
+    hipError_t err;
+    if (tg::mx_fast_eligible(a) && !force_generic) {
+        const int group_m = env_int("TG_GROUP_M", 4);
+        err = tg::launch_mx(kdt, kact, a, group_m > 0 ? group_m : 4, s);
+        set_last("mx_256x256x64_s4");
+    } else {
+        err = tg::launch_mx_generic(kdt, kact, a, s);
+        set_last(force_generic ? "mx_generic (forced)" : "mx_generic (shape or alignment)");
+    }
+    if (err != hipSuccess) {
+        char detail[64];
+        snprintf(detail, sizeof detail, " (launch failed: %s)", hipGetErrorName(err));
+        char name[96];
+        snprintf(name, sizeof name, "%s", g_last_kernel);
+        set_last(name, detail);
+        return TG_ERROR_LAUNCH_FAILED;
+    }
+    return TG_SUCCESS;
+}
+
 const char *tg_status_string(tg_status s)
 {
     switch (s) {

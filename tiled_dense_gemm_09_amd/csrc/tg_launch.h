@@ -53,6 +53,31 @@ bool async_eligible(const GemmArgs &a, int cfg);
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
                         hipStream_t stream);
 
+// Block-scaled 8-bit GEMM: C = act(sum_k a(A[m][k]) 2^(SA[k/32][m]-127)
+// * b(B[n][k]) 2^(SB[k/32][n]-127) + bias[n]).  A [M,K] and B [N,K] bytes
+// (pitches in bytes), SA [K/32][M] and SB [K/32][N] e8m0 bytes, bias and C
+// in the 16-bit output dtype.  fmt: 0 = e4m3, 1 = e5m2.
+struct MxArgs {
+    const unsigned char *A;
+    int64_t lda;
+    const unsigned char *SA;
+    int64_t ldsa;
+    const unsigned char *B;
+    int64_t ldb;
+    const unsigned char *SB;
+    int64_t ldsb;
+    const unsigned short *bias; // [N] or nullptr
+    unsigned short *C;
+    int64_t ldc;
+    int M, N, K;
+    int fmt_a, fmt_b;
+};
+// 256 x 256 tiles, 64-deep steps, 4 stages: M, N multiples of 256, K of 256,
+// 16-byte aligned operands, byte pitches multiples of 16, ldc of 8.
+bool mx_fast_eligible(const MxArgs &a);
+hipError_t launch_mx(int dt, int act, const MxArgs &a, int group_m, hipStream_t stream);
+hipError_t launch_mx_generic(int dt, int act, const MxArgs &a, hipStream_t stream);
+
 // Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
 // entries that must be zero before the first call; the kernel leaves them

@@ -1,0 +1,97 @@
+// tg_pipeline.h -- pieces shared by the asynchronous-copy kernels: the
+// 64-byte-row LDS swizzle, the copy-pipeline barrier and wait, and the
+// epilogue that restages a wave's rounded output tile through LDS.
+#pragma once
+
+#include "tg_device.h"
+
+namespace tg {
+
+// Granule c (16 bytes) of row r of a 64-byte-row tile sits at c ^ swz_a(r).
+// A 128-bit LDS read is served 16 lanes at a time from 64 four-byte banks
+// (256 bytes, measured with the bank-conflict counter on gfx950); the 16
+// consecutive rows that one such group reads then land on 16 different
+// 16-byte bank groups: row r covers groups 4 (r % 4) + (c ^ swz_a(r)).
+__host__ __device__ constexpr int swz_a(int r) { return (r >> 2) & 3; }
+
+// Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
+// workgroup release fence, which waits for every outstanding direct-to-LDS
+// copy (they count as LDS writes) and would drain all stages each step.  Here
+// each wave waits for exactly the copies it needs with wait_vmcnt first; the
+// empty asm statements keep the compiler from moving LDS accesses across the
+// barrier.
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Epilogue of one wave holding TI x TJ 32x32 FP32 accumulator blocks (the
+// bias already inside).  Lane l of block (i, j) holds row 32 i + l % 32 and
+// columns 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
+// activation, the residual (HR: R[m][n] added after it) and the rounding
+// happen there; the rounded (32 TI) x (32 TJ) tile is then restaged through
+// the wave's own LDS region `ep` (rows of 4 TJ 16-byte granules, granule c
+// of row r at c ^ (r % 4TJ)) so that each global store writes whole
+// 64 TJ-byte row segments instead of 16-byte pieces of 32 rows.  C points
+// at the wave tile's first element; R likewise (row pitch ldr).
+template <int DT, int ACT, int TI, int TJ, bool HR>
+__device__ __forceinline__ void restaged_epilogue(const f32x16 (&acc)[TI][TJ], unsigned char *ep,
+                                                  int lane, unsigned short *C, int64_t ldc,
+                                                  const unsigned short *R, int64_t ldr)
+{
+    constexpr int EG = 4 * TJ; // granules per row of the wave tile
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+        const int r = i * 32 + (lane & 31);
+        u32x2 rr[TJ][4];
+        if constexpr (HR) {
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    rr[j][g] = *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + j * 32 +
+                                                                g * 8 + (lane >> 5) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = activate<ACT>(acc[i][j][4 * g + e]);
+                    if constexpr (HR)
+                        v[e] += from_bits<DT>((unsigned short)(rr[j][g][e >> 1] >> (16 * (e & 1))));
+                }
+                const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                const int c = (4 * j + g) ^ (r & (EG - 1));
+                *reinterpret_cast<u32x2 *>(ep + r * (16 * EG) + c * 16 + (lane >> 5) * 8) = o;
+            }
+        }
+    }
+    // each lane reads back granule lane % EG of rows (64 / EG) t + lane / EG
+    // (its own wave's writes, so no barrier) and stores it
+    unsigned short *crow = C + (lane % EG) * 8;
+#pragma unroll
+    for (int t = 0; t < 2 * TI * TJ; ++t) {
+        const int r = (64 / EG) * t + lane / EG;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * EG) +
+                                                         (((lane % EG) ^ (r & (EG - 1))) * 16));
+        *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
+    }
+}
+
+} // namespace tg

@@ -20,8 +20,10 @@ F16 = 1
 BF16 = 2
 ACT = {"none": 0, "gelu_tanh": 1}
 
-SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_qkv", "tg_status_string",
-           "tg_last_kernel", "tg_schedule_tile", "tg_lds_offset", "tg_in_bounds"]
+SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_gemm_qkv",
+           "tg_status_string", "tg_last_kernel", "tg_schedule_tile", "tg_lds_offset",
+           "tg_in_bounds"]
+FP8 = {"e4m3": 0, "e5m2": 1}
 OP_N, OP_T = 0, 1
 
 
@@ -50,6 +52,8 @@ def _load():
     lib.tg_gemm_bias_act.restype = I
     lib.tg_gemm_ex.argtypes = [I, L, L, L, P, L, P, L, I, P, I, P, L, P, L, P]
     lib.tg_gemm_ex.restype = I
+    lib.tg_gemm_mx.argtypes = [I, I, L, L, L, P, L, P, L, P, L, P, L, P, I, I, P, L, P]
+    lib.tg_gemm_mx.restype = I
     lib.tg_gemm_qkv.argtypes = [I, L, L, L, P, L, P, P, P, L, P, P, P, L, P]
     lib.tg_gemm_qkv.restype = I
     lib.tg_status_string.argtypes = [I]
@@ -196,6 +200,48 @@ def gemm(a, b, out=None, bias=None, act="none", residual=None, stream=None):
         rptr, ldr = residual.data_ptr(), _rowmajor(residual, "residual")
     gemm_ex_ptr(dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, op_b, out.data_ptr(), ldc,
                 _stream(stream), bptr, ACT[act], rptr, ldr)
+    return out
+
+
+def _bytes2d(t, name):
+    """(pointer, pitch) of a 2-D row-major uint8 (or float8) device tensor."""
+    if t.dim() != 2 or t.element_size() != 1:
+        raise ValueError("%s must be a 2-D tensor of bytes" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    return t.data_ptr(), max(t.stride(0), t.shape[1])
+
+
+def gemm_mx(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", bias=None, act="none", out=None,
+            out_dtype=None, stream=None):
+    """Block-scaled 8-bit GEMM: out = act(sum_k a 2^(sa-127) * b 2^(sb-127) + bias).
+
+    a [M,K] and b [N,K]: 8-bit floats as bytes (uint8 or float8 tensors);
+    sa [K/32,M] and sb [K/32,N]: e8m0 scale bytes (block-major); bias [N]
+    and out [M,N]: float16 or bfloat16 (out_dtype, default bfloat16)."""
+    torch = _torch()
+    M, K = a.shape
+    N, K2 = b.shape
+    if K2 != K:
+        raise ValueError("a is [M,K] and b is [N,K]; K differs: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    odt = _dt(out)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M,N]")
+    if bias is not None and (bias.dtype != out.dtype or bias.dim() != 1 or bias.shape[0] != N):
+        raise ValueError("bias must be a dense [N] vector of the output dtype")
+    pa, lda = _bytes2d(a, "a")
+    pb, ldb = _bytes2d(b, "b")
+    psa, ldsa = _bytes2d(sa, "sa")
+    psb, ldsb = _bytes2d(sb, "sb")
+    if tuple(sa.shape) != (K // 32, M) or tuple(sb.shape) != (K // 32, N):
+        raise ValueError("scales must be sa [K/32,M] and sb [K/32,N]")
+    _check(lib.tg_gemm_mx(FP8[fmt_a], FP8[fmt_b], M, N, K, pa, lda, psa, ldsa, pb, ldb, psb, ldsb,
+                          bias.data_ptr() if bias is not None else None, ACT[act], odt,
+                          out.data_ptr(), _rowmajor(out, "out"), _stream(stream) or None))
     return out
 
 
