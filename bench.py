@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16/bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA (twice the f16 rate)
 METRIC = "GEMM TFLOP/s + % of MFMA peak (4096³ fp16); GB/s % HBM peak at M=16"
 KERNEL_SOURCES = ["tiled_dense_gemm_09_amd/csrc/gemm_async.hip",
                   "tiled_dense_gemm_09_amd/csrc/tg_device.h",
@@ -113,7 +114,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["main", "plain", "ex", "qkv", "square8192", "skinny",
+    ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "qkv", "square8192", "skinny",
                                        "small", "vendor", "copy"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -242,6 +243,21 @@ def run_secondary(args, torch, inputs, tg):
                           "kernel": tg.last_kernel()}
             log("  ", label, out[label])
         del A, bias, Wt, R, C
+
+    if args.only in (None, "mx"):
+        # block-scaled 8-bit GEMM (e4m3 operands, e8m0 scales per 32 k, bf16 out)
+        for n in (4096, 8192):
+            p = inputs.mx_problem(inputs.FP8_E4M3, inputs.FP8_E4M3, n, n, n, seed=160 + n % 7)
+            d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+            A, SA, B, SB = d(p["A"]), d(p["SA"]), d(p["B"]), d(p["SB"])
+            C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+            ms = time_launches(lambda: tg.gemm_mx(A, SA, B, SB, out=C), steps, warm)
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            out["mx_e4m3_%dx%dx%d" % (n, n, n)] = {
+                "ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                "frac_fp8_mfma_peak": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": tg.last_kernel()}
+            log("  ", out["mx_e4m3_%dx%dx%d" % (n, n, n)])
+            del A, SA, B, SB, C
 
     if args.only in (None, "qkv"):
         q = inputs.config_problem("bf16_qkv")
