@@ -59,6 +59,8 @@ def _load():
         lib.tgo_gemm_mx.argtypes = [_I, _I, _L, _L, _L, _P, _L, _P, _L, _P, _L, _P, _L, _P, _I,
                                     _I, _P, _P, _L, _L, _L, _I]
         lib.tgo_decode_fp8_array.argtypes = [_I, _L, _P, _P]
+        lib.tgo_attention.argtypes = [_I, _L, _L, _L, _L, _P, _P, _P, ctypes.c_double, _I, _P,
+                                      _P, _P, _I]
         lib.tgo_gemm_qkv.argtypes = [_I, _L, _L, _L, _P, _L, _P, _P, _P, _L, _P, _P, _P, _P, _P,
                                      _P, _L, _L, _L, _I]
         lib.tgo_decode_array.argtypes = [_I, _L, _P, _P]
@@ -238,6 +240,25 @@ def gemm_mx(fmt_a, fmt_b, A, SA, B, SB, bias=None, act=ACT_NONE, dt=BF16, rows=N
     if rc:
         raise ValueError("oracle rejected the arguments")
     return f64[r0:r1], bits[r0:r1]
+
+
+def attention(dt, Q, K, V, causal=False, scale=None, threads=0):
+    """Softmax(scale Q K^T + mask) V for Q, K, V [B, H, S, D] bit arrays;
+    scale defaults to 1/sqrt(D).  Returns (f64, bits, lse)."""
+    Q, K, V = _bits(Q), _bits(K), _bits(V)
+    if Q.ndim != 4 or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must share one [B, H, S, D] shape")
+    B, H, S, D = Q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    f64 = np.zeros(Q.shape, np.float64)
+    bits = np.zeros(Q.shape, np.uint16)
+    lse = np.zeros((B, H, S), np.float64)
+    rc = _load().tgo_attention(dt, B, H, S, D, _ptr(Q), _ptr(K), _ptr(V), float(scale),
+                               int(bool(causal)), _ptr(f64), _ptr(bits), _ptr(lse), threads)
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+    return f64, bits, lse
 
 
 def gemm_qkv(dt, X, Wq, Wk, Wv, rows=None, threads=0):

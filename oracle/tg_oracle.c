@@ -46,6 +46,14 @@
  *   axes; 32 along K is the block of the OCP microscaling formats and of
  *   the gfx950 matrix cores.  Products of two 8-bit floats and two powers
  *   of two are exact in double.
+ * - Attention (tgo_attention) is the plain definition
+ *     O[i] = sum_j softmax_j( scale * Q[i] . K[j] + mask[i][j] ) V[j],
+ *   scale = 1/sqrt(D) by default, mask[i][j] = -inf for j > i when causal
+ *   ("TileIR", Softmax(Q K^T / sqrt(d)) V, which the fused kernel evaluates
+ *   with an online softmax; "TIRx", section 6: forward multi-head attention
+ *   with head dimension 128, causal and non-causal).  It materialises every
+ *   score row, in double: m = max_j s_j, p_j = exp(s_j - m), l = sum_j p_j,
+ *   O[i] = (sum_j p_j V[j]) / l, and the log-sum-exp m + log(l).
  *
  * Every output element depends only on its own row of A and column of B,
  * so rows are split across OpenMP threads; the value of each element does
@@ -442,6 +450,73 @@ int tgo_decode_fp8_array(int fmt, int64_t n, const uint8_t *in, double *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = fmt == 2 ? tgo_e8m0_to_double(in[i]) : tgo_fp8_to_double(fmt, in[i]);
+    return 0;
+}
+
+/*
+ * Attention over Q, K, V of shape [B][H][S][D] (contiguous, dtype dt).  For
+ * every (b, h, i): scores s_j = scale * sum_d Q[i][d] K[j][d] for j < S (j <= i
+ * when causal), then the softmax-weighted sum of the V rows.  out_f64 /
+ * out_bits receive O (same layout; either may be NULL), lse (may be NULL)
+ * the [B][H][S] log-sum-exp of the scaled scores.  Returns 0 or -1.
+ */
+int tgo_attention(int dt, int64_t B, int64_t H, int64_t S, int64_t D, const uint16_t *Q,
+                  const uint16_t *K, const uint16_t *V, double scale, int causal,
+                  double *out_f64, uint16_t *out_bits, double *lse, int threads)
+{
+    if ((dt != TGO_F16 && dt != TGO_BF16) || B < 0 || H < 0 || S < 0 || D <= 0)
+        return -1;
+    const int64_t heads = B * H;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#pragma omp parallel
+#endif
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+        for (int64_t row = 0; row < heads * S; ++row) {
+            const int64_t hd = row / S, i = row % S;
+            const uint16_t *Qh = Q + hd * S * D, *Kh = K + hd * S * D, *Vh = V + hd * S * D;
+            const int64_t nkeys = causal ? i + 1 : S;
+            for (int64_t d = 0; d < D; ++d)
+                q[d] = decode(dt, Qh[i * D + d]);
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += q[d] * decode(dt, Kh[j * D + d]);
+                sc[j] = scale * dot;
+                if (sc[j] > m)
+                    m = sc[j];
+            }
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double pj = exp(sc[j] - m);
+                l += pj;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] += pj * decode(dt, Vh[j * D + d]);
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                const double v = o[d] / l;
+                if (out_f64)
+                    out_f64[row * D + d] = v;
+                if (out_bits)
+                    out_bits[row * D + d] = encode(dt, v);
+            }
+            if (lse)
+                lse[row] = m + log(l);
+        }
+        free(sc);
+        free(q);
+        free(o);
+    }
     return 0;
 }
 

@@ -16,6 +16,9 @@ fix it with mathematics and independent code:
 * the 8-bit float and e8m0 decoders against torch's float8 types over every
   pattern; the block-scaled GEMM against the f16 GEMM (unit scales), a closed
   form for the scales and rational brute force;
+* attention against uniform weights (Q = 0), the causal first row (= V[0]),
+  pure-Python brute force, a NumPy cross-check and the invariance of the
+  softmax to a common shift of the keys;
 * the epilogue order (bias before activation, residual after it), QKV =
   three GEMMs, the transposed-operand form against brute force and against
   the same operand stored the other way, and independence of the thread
@@ -538,6 +541,81 @@ def test_mx_brute_force_rational_nonsquare():
             bound = sum(abs(float(av[i, k]) * float(bv[j, k])) * 2.0 ** (int(SA[k // 32, i]) +
                         int(SB[k // 32, j]) - 254) for k in range(K)) * K * 2.0 ** -52
             assert abs(Fraction(float(f64[i, j])) - exact) <= Fraction(bound)
+
+
+# --------------------------------------------------------------- attention
+
+def _att_decode(dt, x):
+    return oracle.decode(dt, x)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_uniform_weights_when_q_is_zero(causal):
+    p = inputs.attention_problem(BF16, 1, 2, 9, 16, seed=60)
+    Q = np.zeros_like(p["Q"])
+    f64, _, lse = oracle.attention(BF16, Q, p["K"], p["V"], causal=causal)
+    V = _att_decode(BF16, p["V"])
+    for i in range(9):
+        n = i + 1 if causal else 9
+        assert np.allclose(f64[:, :, i], V[:, :, :n].mean(axis=2), rtol=1e-14, atol=1e-15)
+        assert np.allclose(lse[:, :, i], math.log(n), rtol=1e-15)
+
+
+def test_attention_causal_first_row_is_v0():
+    p = inputs.attention_problem(F16, 2, 3, 7, 8, seed=61)
+    f64, bits, lse = oracle.attention(F16, p["Q"], p["K"], p["V"], causal=True)
+    assert np.array_equal(f64[:, :, 0], _att_decode(F16, p["V"])[:, :, 0])
+    assert np.array_equal(bits[:, :, 0], p["V"][:, :, 0])
+    q0 = _att_decode(F16, p["Q"])[:, :, 0]
+    k0 = _att_decode(F16, p["K"])[:, :, 0]
+    assert np.allclose(lse[:, :, 0], (q0 * k0).sum(-1) / math.sqrt(8), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_brute_force_python(causal):
+    # pure-Python floats and math.exp, independent of the oracle's C
+    p = inputs.attention_problem(BF16, 1, 2, 5, 3, seed=62)
+    f64, _, lse = oracle.attention(BF16, p["Q"], p["K"], p["V"], causal=causal, scale=0.7)
+    Q, K, V = (_att_decode(BF16, p[n]).tolist() for n in ("Q", "K", "V"))
+    for h in range(2):
+        for i in range(5):
+            keys = range(i + 1) if causal else range(5)
+            sc = [0.7 * sum(Q[0][h][i][d] * K[0][h][j][d] for d in range(3)) for j in keys]
+            m = max(sc)
+            w = [math.exp(x - m) for x in sc]
+            tot = sum(w)
+            for d in range(3):
+                ref = sum(w[t] * V[0][h][j][d] for t, j in enumerate(keys)) / tot
+                assert abs(f64[0, h, i, d] - ref) <= 1e-13 * max(1.0, abs(ref))
+            assert abs(lse[0, h, i] - (m + math.log(tot))) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_numpy_crosscheck(causal):
+    p = inputs.attention_problem(F16, 2, 2, 64, 16, seed=63)
+    f64, _, lse = oracle.attention(F16, p["Q"], p["K"], p["V"], causal=causal)
+    Q, K, V = (_att_decode(F16, p[n]) for n in ("Q", "K", "V"))
+    s = np.einsum("bhid,bhjd->bhij", Q, K) / 4.0
+    if causal:
+        s = np.where(np.tril(np.ones((64, 64), bool)), s, -np.inf)
+    w = np.exp(s - s.max(-1, keepdims=True))
+    ref = np.einsum("bhij,bhjd->bhid", w / w.sum(-1, keepdims=True), V)
+    assert np.allclose(f64, ref, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) +
+                       s.max(-1), rtol=1e-13)
+
+
+def test_attention_is_invariant_to_a_common_key_shift():
+    # adding one vector w to every key row adds q.w to every score of query q:
+    # the softmax weights, hence O, do not change; lse shifts by scale q.w
+    p = inputs.attention_problem(BF16, 1, 1, 12, 8, seed=64, kind="int")
+    w = np.array([1, -2, 0, 1, 2, -1, 0, 1], np.float64)
+    K2 = bits_of(BF16, _att_decode(BF16, p["K"]) + w)
+    f1, _, l1 = oracle.attention(BF16, p["Q"], p["K"], p["V"])
+    f2, _, l2 = oracle.attention(BF16, p["Q"], K2, p["V"])
+    assert np.allclose(f1, f2, rtol=1e-13, atol=1e-14)
+    qw = _att_decode(BF16, p["Q"])[0, 0] @ w
+    assert np.allclose(l2[0, 0] - l1[0, 0], qw / math.sqrt(8), rtol=1e-12, atol=1e-12)
 
 
 def test_qkv_is_three_gemms():

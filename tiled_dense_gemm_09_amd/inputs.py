@@ -122,6 +122,18 @@ def mx_problem(fmt_a, fmt_b, M, N, K, seed, kind="normal", bias=False, act=ACT_N
                 act=act, dt=dt)
 
 
+# --------------------------------------------------------------- attention
+
+def attention_problem(dt, B, H, S, D, seed, kind="normal", causal=False):
+    """Q, K, V [B, H, S, D] bit patterns: i.i.d. N(0, 1) (kind "normal"), or
+    integers in {-2..2} (kind "int")."""
+    rng = np.random.default_rng(seed)
+    Q = draw(rng, (B, H, S, D), kind, dt)
+    K = draw(rng, (B, H, S, D), kind, dt)
+    V = draw(rng, (B, H, S, D), kind, dt)
+    return dict(dt=dt, B=B, H=H, S=S, D=D, Q=Q, K=K, V=V, causal=causal)
+
+
 # The five workloads.  Config names follow their shapes.
 CONFIGS = {
     # f16 256^3, U[-1,1]; integer variant {-2..2}
