@@ -153,6 +153,24 @@ tg_status tg_gemm_mx(tg_fp8_format fmt_a, tg_fp8_format fmt_b,
                      void *C, int64_t ldc,
                      void *stream);
 
+/* Fused forward attention ("TileIR": Softmax(Q K^T / sqrt(d)) V in one
+ * kernel with an online softmax, the score matrix never materialised;
+ * "TIRx", section 6: forward multi-head attention, head dimension 128,
+ * causal and non-causal):
+ *     O[b][h][i] = sum_j softmax_j( scale * Q[b][h][i] . K[b][h][j] + mask ) V[b][h][j]
+ * with mask = -inf for j > i when causal != 0.  Q, K, V, O are contiguous
+ * [batch][heads][seq][head_dim] tensors of dtype dt; scores, softmax and
+ * accumulation in FP32, one rounding of O.  scale <= 0 means 1/sqrt(head_dim).
+ * lse, if not NULL, receives the FP32 [batch][heads][seq] natural-log
+ * log-sum-exp of each row's scaled scores.  head_dim 128 with seq a
+ * multiple of 128 and 16-byte aligned tensors runs the MFMA kernel;
+ * head_dim <= 128 otherwise runs a slower fallback (reported by
+ * tg_last_kernel()); head_dim > 128 is TG_ERROR_NOT_SUPPORTED.  O must not
+ * overlap Q, K, V or lse. */
+tg_status tg_attention_fwd(tg_dtype dt, int64_t batch, int64_t heads, int64_t seq,
+                           int64_t head_dim, const void *Q, const void *K, const void *V,
+                           void *O, float *lse, float scale, int causal, void *stream);
+
 /* Horizontally fused projection, one launch:
  *     Q = X . Wq,  Kout = X . Wk,  V = X . Wv.
  * X is [M,K] (pitch ldx); Wq, Wk, Wv are each [K,N] (shared pitch ldw);

@@ -121,6 +121,23 @@ def test_invalid_mx_arguments_launch_nothing(args):
     assert st == 1
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(dt=5), 1),                   # unknown dtype
+    (dict(D=0), 1),                    # empty head dimension
+    (dict(D=256), 2),                  # head dimension beyond the kernels
+    (dict(S=-1), 1),
+    (dict(Q=0), 1),                    # NULL input
+    (dict(O=FAKE_A + 64), 1),          # output overlapping Q
+    (dict(lse=FAKE_C + 2), 1),         # misaligned log-sum-exp
+])
+def test_invalid_attention_arguments_launch_nothing(args, status):
+    a = dict(dt=2, B=1, H=2, S=128, D=128, Q=FAKE_A, K=FAKE_B, V=FAKE_SA, O=FAKE_C, lse=0)
+    a.update(args)
+    st = tg.lib.tg_attention_fwd(a["dt"], a["B"], a["H"], a["S"], a["D"], a["Q"] or None, a["K"],
+                                 a["V"], a["O"], a["lse"] or None, 0.0, 0, None)
+    assert st == status
+
+
 def test_qkv_outputs_must_not_overlap():
     st = tg.lib.tg_gemm_qkv(2, 64, 64, 64, FAKE_A, 64, FAKE_B, FAKE_B + 2 ** 20, FAKE_B + 2 ** 21,
                             64, FAKE_C, FAKE_C + 128, FAKE_C + 2 ** 20, 64, None)

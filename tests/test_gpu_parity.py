@@ -498,6 +498,72 @@ def test_mx_full_size_rows(tg):
         util.check_tol(BF16, bits[r0:r0 + 4], f64, "mx 4096 rows %d" % r0, ref_bits=rbits)
 
 
+# -------------------------------------------------------- fused attention
+
+def run_attn(tg, p, lse=True):
+    import torch
+    q, k, v = (util.to_dev(p[n], p["dt"]) for n in ("Q", "K", "V"))
+    out, l = tg.attention(q, k, v, causal=p["causal"], lse=True)
+    torch.cuda.synchronize()
+    return util.to_bits(out), l.cpu().numpy().astype(np.float64), tg.last_kernel()
+
+
+# P is rounded to the input dtype before the P.V product (as FlashAttention
+# does); the oracle keeps P in double, so O is compared within the
+# tolerance only, not for correct rounding.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("B,H,S,D", [(1, 2, 256, 128), (2, 3, 384, 128), (1, 2, 200, 64)])
+def test_attention_random(tg, dt, causal, B, H, S, D):
+    p = inputs.attention_problem(dt, B, H, S, D, seed=170 + S + dt, causal=causal)
+    say("case attention", dt, B, H, S, D, "causal" if causal else "full")
+    bits, lse, kern = run_attn(tg, p)
+    say("  kernel", kern)
+    assert kern.startswith("attn_fwd" if D == 128 and S % 128 == 0 else "attn_generic")
+    f64, _, lse_ref = oracle.attention(dt, p["Q"], p["K"], p["V"], causal=causal)
+    util.check_tol(dt, bits, f64, "attention %s" % kern)
+    assert np.max(np.abs(lse - lse_ref)) < 2e-3
+    if causal:
+        # row 0 attends to key 0 alone: O = V[0] exactly
+        assert np.array_equal(bits[:, :, 0], p["V"][:, :, 0])
+
+
+def test_attention_uniform_integer_values(tg):
+    # Q = 0: every weight is exactly 1, O = mean of the V rows it can see
+    p = inputs.attention_problem(BF16, 1, 2, 256, 128, seed=180, kind="int", causal=True)
+    p["Q"] = np.zeros_like(p["Q"])
+    bits, lse, _ = run_attn(tg, p)
+    f64, rbits, lse_ref = oracle.attention(BF16, p["Q"], p["K"], p["V"], causal=True)
+    util.check_tol(BF16, bits, f64, "uniform attention", ref_bits=rbits)
+    assert np.allclose(lse, lse_ref, atol=1e-5)
+
+
+def test_attention_generic_matches_fast_path(tg, monkeypatch):
+    p = inputs.attention_problem(F16, 1, 2, 256, 128, seed=181, causal=True)
+    fast, l1, k1 = run_attn(tg, p)
+    monkeypatch.setenv("TG_FORCE_CONFIG", "generic")
+    slow, l2, k2 = run_attn(tg, p)
+    assert k1.startswith("attn_fwd") and k2.startswith("attn_generic")
+    f64, _, lse_ref = oracle.attention(F16, p["Q"], p["K"], p["V"], causal=True)
+    util.check_tol(F16, fast, f64, "attn fast")
+    util.check_tol(F16, slow, f64, "attn generic")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_full_size_heads(tg, causal):
+    # the benchmark shape: batch 4, 16 heads, 4096 tokens, head dim 128;
+    # heads (0, 0) and (3, 15) checked in full against the oracle
+    p = inputs.attention_problem(BF16, 4, 16, 4096, 128, seed=190, causal=causal)
+    say("case attention 4x16x4096x128", "causal" if causal else "full")
+    bits, lse, kern = run_attn(tg, p)
+    assert kern.startswith("attn_fwd")
+    for (b, h) in ((0, 0), (3, 15)):
+        sub = {n: p[n][b:b + 1, h:h + 1] for n in ("Q", "K", "V")}
+        f64, _, lse_ref = oracle.attention(BF16, sub["Q"], sub["K"], sub["V"], causal=causal)
+        util.check_tol(BF16, bits[b:b + 1, h:h + 1], f64, "attention head %d,%d" % (b, h))
+        assert np.max(np.abs(lse[b:b + 1, h:h + 1] - lse_ref)) < 2e-3
+
+
 def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")

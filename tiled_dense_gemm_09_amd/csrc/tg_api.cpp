@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <cmath>
 #include <mutex>
 
 #include "../../include/tg.h"
@@ -405,6 +406,77 @@ tg_status tg_gemm_mx(tg_fp8_format fmt_a, tg_fp8_format fmt_b, int64_t M, int64_
     } else {
         err = tg::launch_mx_generic(kdt, kact, a, s);
         set_last(force_generic ? "mx_generic (forced)" : "mx_generic (shape or alignment)");
+    }
+    if (err != hipSuccess) {
+        char detail[64];
+        snprintf(detail, sizeof detail, " (launch failed: %s)", hipGetErrorName(err));
+        char name[96];
+        snprintf(name, sizeof name, "%s", g_last_kernel);
+        set_last(name, detail);
+        return TG_ERROR_LAUNCH_FAILED;
+    }
+    return TG_SUCCESS;
+}
+
+tg_status tg_attention_fwd(tg_dtype dt, int64_t batch, int64_t heads, int64_t seq,
+                           int64_t head_dim, const void *Q, const void *K, const void *V,
+                           void *O, float *lse, float scale, int causal, void *stream)
+{
+    if (dt != TG_DTYPE_F16 && dt != TG_DTYPE_BF16)
+        return TG_ERROR_INVALID_VALUE;
+    if (batch < 0 || heads < 0 || seq < 0 || head_dim <= 0)
+        return TG_ERROR_INVALID_VALUE;
+    if (head_dim > 128)
+        return TG_ERROR_NOT_SUPPORTED;
+    const int64_t bh = batch * heads;
+    if (bh >= kMaxDim || seq >= kMaxDim || bh * seq * head_dim >= ((int64_t)1 << 40))
+        return TG_ERROR_INVALID_VALUE;
+    if (bh == 0 || seq == 0) {
+        set_last("none");
+        return TG_SUCCESS;
+    }
+    if (!Q || !K || !V || !O)
+        return TG_ERROR_INVALID_VALUE;
+    if (((uintptr_t)lse & 3u) != 0 || ((uintptr_t)Q & 1u) || ((uintptr_t)K & 1u) ||
+        ((uintptr_t)V & 1u) || ((uintptr_t)O & 1u))
+        return TG_ERROR_INVALID_VALUE;
+    const Span o = span_of(O, bh * seq, head_dim, head_dim);
+    if (overlaps(o, span_of(Q, bh * seq, head_dim, head_dim)) ||
+        overlaps(o, span_of(K, bh * seq, head_dim, head_dim)) ||
+        overlaps(o, span_of(V, bh * seq, head_dim, head_dim)))
+        return TG_ERROR_INVALID_VALUE;
+    if (lse) {
+        Span l;
+        l.lo = (uintptr_t)lse;
+        l.hi = l.lo + (uintptr_t)(bh * seq) * sizeof(float);
+        if (overlaps(o, l))
+            return TG_ERROR_INVALID_VALUE;
+    }
+    if (!(scale > 0.f))
+        scale = 1.0f / sqrtf((float)head_dim);
+
+    tg::AttnArgs a;
+    a.Q = static_cast<const unsigned short *>(Q);
+    a.K = static_cast<const unsigned short *>(K);
+    a.V = static_cast<const unsigned short *>(V);
+    a.O = static_cast<unsigned short *>(O);
+    a.lse = lse;
+    a.BH = (int)bh;
+    a.S = (int)seq;
+    a.scale_log2 = scale * 1.4426950408889634f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int kdt = dt == TG_DTYPE_F16 ? tg::DT_F16 : tg::DT_BF16;
+    const char *force = getenv("TG_FORCE_CONFIG");
+    const bool force_generic = force && strcmp(force, "generic") == 0;
+    (void)hipGetLastError();
+    hipError_t err;
+    if (!force_generic && tg::attn_fast_eligible(a, (int)head_dim) && a.S / 128 < 65536) {
+        err = tg::launch_attn(kdt, causal != 0, a, s);
+        set_last(causal ? "attn_fwd_128x64_causal" : "attn_fwd_128x64");
+    } else {
+        err = tg::launch_attn_generic(kdt, causal != 0, a, (int)head_dim, s);
+        set_last(force_generic ? "attn_generic (forced)" : "attn_generic (shape or alignment)");
     }
     if (err != hipSuccess) {
         char detail[64];

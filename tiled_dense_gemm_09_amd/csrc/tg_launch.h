@@ -78,6 +78,20 @@ bool mx_fast_eligible(const MxArgs &a);
 hipError_t launch_mx(int dt, int act, const MxArgs &a, int group_m, hipStream_t stream);
 hipError_t launch_mx_generic(int dt, int act, const MxArgs &a, hipStream_t stream);
 
+// Fused forward attention: Q, K, V, O [BH][S][D] (BH = batch * heads),
+// lse [BH][S] FP32 or nullptr; scale_log2 = softmax scale * log2(e).
+struct AttnArgs {
+    const unsigned short *Q, *K, *V;
+    unsigned short *O;
+    float *lse;
+    int BH, S;
+    float scale_log2;
+};
+// D = 128, S a multiple of 128, 16-byte aligned tensors
+bool attn_fast_eligible(const AttnArgs &a, int D);
+hipError_t launch_attn(int dt, bool causal, const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_generic(int dt, bool causal, const AttnArgs &a, int D, hipStream_t stream);
+
 // Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
 // entries that must be zero before the first call; the kernel leaves them

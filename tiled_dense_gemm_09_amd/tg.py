@@ -20,9 +20,9 @@ F16 = 1
 BF16 = 2
 ACT = {"none": 0, "gelu_tanh": 1}
 
-SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_gemm_qkv",
-           "tg_status_string", "tg_last_kernel", "tg_schedule_tile", "tg_lds_offset",
-           "tg_in_bounds"]
+SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_attention_fwd",
+           "tg_gemm_qkv", "tg_status_string", "tg_last_kernel", "tg_schedule_tile",
+           "tg_lds_offset", "tg_in_bounds"]
 FP8 = {"e4m3": 0, "e5m2": 1}
 OP_N, OP_T = 0, 1
 
@@ -54,6 +54,8 @@ def _load():
     lib.tg_gemm_ex.restype = I
     lib.tg_gemm_mx.argtypes = [I, I, L, L, L, P, L, P, L, P, L, P, L, P, I, I, P, L, P]
     lib.tg_gemm_mx.restype = I
+    lib.tg_attention_fwd.argtypes = [I, L, L, L, L, P, P, P, P, P, ctypes.c_float, I, P]
+    lib.tg_attention_fwd.restype = I
     lib.tg_gemm_qkv.argtypes = [I, L, L, L, P, L, P, P, P, L, P, P, P, L, P]
     lib.tg_gemm_qkv.restype = I
     lib.tg_status_string.argtypes = [I]
@@ -243,6 +245,28 @@ def gemm_mx(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", bias=None, act="none", out
                           bias.data_ptr() if bias is not None else None, ACT[act], odt,
                           out.data_ptr(), _rowmajor(out, "out"), _stream(stream) or None))
     return out
+
+
+def attention(q, k, v, causal=False, scale=None, out=None, lse=False, stream=None):
+    """Fused softmax(scale q k^T + mask) v for contiguous [B, H, S, D] tensors
+    (float16 / bfloat16).  Returns out, or (out, lse [B, H, S] float32)."""
+    torch = _torch()
+    dt = _dt(q)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one shape and dtype")
+    if q.dim() != 4 or not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, S, D] tensors")
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    l = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse else None
+    _check(lib.tg_attention_fwd(dt, B, H, S, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), l.data_ptr() if l is not None else None,
+                                float(scale or 0.0), int(bool(causal)),
+                                _stream(stream) or None))
+    return (out, l) if lse else out
 
 
 def gemm_qkv(x, wq, wk, wv, outs=None, stream=None):
