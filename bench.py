@@ -114,8 +114,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "qkv", "square8192", "skinny",
-                                       "small", "vendor", "copy"],
+    ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "attn", "qkv", "square8192",
+                                       "skinny", "small", "vendor", "copy"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -258,6 +258,25 @@ def run_secondary(args, torch, inputs, tg):
                 "frac_fp8_mfma_peak": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": tg.last_kernel()}
             log("  ", out["mx_e4m3_%dx%dx%d" % (n, n, n)])
             del A, SA, B, SB, C
+
+    if args.only in (None, "attn"):
+        # fused forward attention, head dim 128, 16384 tokens per launch;
+        # flop = 4 B H S^2 D (non-causal), half of it causal
+        for (b, hds, seq) in ((4, 16, 4096), (2, 16, 8192)):
+            p = inputs.attention_problem(inputs.BF16, b, hds, seq, 128, seed=200 + seq % 9)
+            q, k, v = (dev(p[n], 2) for n in ("Q", "K", "V"))
+            o = torch.empty_like(q)
+            for causal in (False, True):
+                ms = time_launches(lambda: tg.attention(q, k, v, causal=causal, out=o), steps,
+                                   warm)
+                flop = 4.0 * b * hds * seq * seq * 128 * (0.5 if causal else 1.0)
+                tf = flop / (ms * 1e-3) / 1e12
+                key = "attn_bf16_%dx%dx%dx128%s" % (b, hds, seq, "_causal" if causal else "")
+                out[key] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                            "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                            "kernel": tg.last_kernel()}
+                log("  ", key, out[key])
+            del q, k, v, o
 
     if args.only in (None, "qkv"):
         q = inputs.config_problem("bf16_qkv")

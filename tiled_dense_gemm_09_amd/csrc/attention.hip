@@ -61,9 +61,11 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int nqb = p.S / AT_BM;
-    // causal: the longest query blocks first
-    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    const int64_t head = (int64_t)blockIdx.y * p.S * AT_D;
+    // grid (heads, query blocks): workgroups are dispatched with x fastest,
+    // so every head's block of a given length goes out together; causal
+    // blocks are taken longest first so the short ones fill the tail
+    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.y : (int)blockIdx.y;
+    const int64_t head = (int64_t)blockIdx.x * p.S * AT_D;
     const unsigned short *Qh = p.Q + head, *Kh = p.K + head, *Vh = p.V + head;
     const int q0 = qb * AT_BM + wave * 32;   // this wave's first query
     const int myq = q0 + (lane & 31);        // the query this lane's scores belong to
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
         for (int r = 0; r < 16; ++r)
             acc_o[0][db][r] *= inv_l;
     if (p.lse != nullptr && lane < 32)
-        p.lse[(int64_t)blockIdx.y * p.S + myq] =
+        p.lse[(int64_t)blockIdx.x * p.S + myq] =
             (m_run + __builtin_amdgcn_logf(l_run)) * 0.6931471805599453f;
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -292,7 +294,7 @@ bool attn_fast_eligible(const AttnArgs &a, int D)
 
 hipError_t launch_attn(int dt, bool causal, const AttnArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.S / AT_BM, a.BH), block(AT_NT);
+    const dim3 grid(a.BH, a.S / AT_BM), block(AT_NT);
     if (dt == DT_F16) {
         if (causal)
             hipLaunchKernelGGL((attn_fwd_kernel<DT_F16, true>), grid, block, 0, s, a);
