@@ -32,6 +32,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA (twice the f16 rate)
 METRIC = "GEMM TFLOP/s + % of MFMA peak (4096³ fp16); GB/s % HBM peak at M=16"
 KERNEL_SOURCES = ["tiled_dense_gemm_09_amd/csrc/gemm_async.hip",
+                  "tiled_dense_gemm_09_amd/csrc/tg_pipeline.h",
                   "tiled_dense_gemm_09_amd/csrc/tg_device.h",
                   "tiled_dense_gemm_09_amd/csrc/tg_launch.h",
                   "tiled_dense_gemm_09_amd/csrc/tg_api.cpp"]
