@@ -523,19 +523,20 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     if (!s_last)
         return;
 
-    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15; four
-    // splits per round: 16 loads in flight, then added in split order
-    // (indices past the last split repeat it and are not added)
+    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15; eight
+    // splits per round (one round for the usual split counts): 32 loads in
+    // flight, then added in split order (indices past the last split repeat
+    // it and are not added)
     const int rm = tid >> 4;
     const int cn = n0 + (tid & 15) * 16;
     float sum[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         sum[i] = 0.f;
-    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
-        f32x4 v[4][4];
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+        f32x4 v[8][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const int sp = min(sp0 + u, splits - 1);
             const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
 #pragma unroll
@@ -547,15 +548,23 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         }
         // the loads above are invisible to the compiler's wait tracking: wait
         // here and pass the values through so nothing reads them earlier
-        asm volatile("s_waitcnt vmcnt(0)"
+        // (loads return in order: vmcnt(16) covers the first 16, vmcnt(0) the rest)
+        asm volatile("s_waitcnt vmcnt(16)"
                      : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
                        "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
                        "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[2][2]), "+v"(v[2][3]),
                        "+v"(v[3][0]), "+v"(v[3][1]), "+v"(v[3][2]), "+v"(v[3][3])
                      :
                      : "memory");
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[4][2]), "+v"(v[4][3]),
+                       "+v"(v[5][0]), "+v"(v[5][1]), "+v"(v[5][2]), "+v"(v[5][3]),
+                       "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[6][2]), "+v"(v[6][3]),
+                       "+v"(v[7][0]), "+v"(v[7][1]), "+v"(v[7][2]), "+v"(v[7][3])
+                     :
+                     : "memory");
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             if (sp0 + u < splits) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
