@@ -272,7 +272,9 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     // Every copy has three steps of MFMA work to land, and every LDS read
     // overlaps MFMAs.  K is a multiple of 4 steps, so the loop body is the 4
     // stages with their arrays named statically.  The MFMA / read / copy
-    // order of each half is pinned, one of each per slot.
+    // order of each half is pinned: one MFMA and two fragment reads per slot
+    // (the reads finish early in the half, leaving the last MFMAs as slack
+    // before the wait), the copies spread over the middle slots.
     constexpr int SLOTS = (NMMA > NREAD ? NMMA : NREAD) > TI + G::COPIES - G::C1
                               ? (NMMA > NREAD ? NMMA : NREAD)
                               : TI + G::COPIES - G::C1;
@@ -287,8 +289,10 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         for (int q = 0; q < SLOTS; ++q) {
             if (q < NMMA)
                 mma_one(f0, q);
-            if (q < NREAD)
-                read_piece(f1, cur, 1, q);
+            if (2 * q < NREAD)
+                read_piece(f1, cur, 1, 2 * q);
+            if (2 * q + 1 < NREAD)
+                read_piece(f1, cur, 1, 2 * q + 1);
             if (q >= TI && q < TI + G::COPIES - G::C1)
                 copy(kp, prv, G::C1 + q - TI);
             __builtin_amdgcn_sched_barrier(0); // keep the MFMA / read / copy order
@@ -304,8 +308,10 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         for (int q = 0; q < SLOTS; ++q) {
             if (q < NMMA)
                 mma_one(f1, q);
-            if (q < NREAD)
-                read_piece(f0, nxt, 0, q); // past the last step: harmless reread
+            if (2 * q < NREAD)
+                read_piece(f0, nxt, 0, 2 * q);
+            if (2 * q + 1 < NREAD)
+                read_piece(f0, nxt, 0, 2 * q + 1);
             if (q < G::C1)
                 copy(kc, cur, q);
             __builtin_amdgcn_sched_barrier(0);
