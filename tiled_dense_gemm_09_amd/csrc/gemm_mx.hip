@@ -230,7 +230,9 @@ __global__ __launch_bounds__(MX_NT, 1) void gemm_mx_kernel(MxArgs p, int tiles_m
     //     wait for this wave's copies of step k+1 and its reads of stage k,
     //     barrier (everybody's copies of k+1 landed; stage k is free)
     //     16 MFMAs of step k, interleaved with the reads of step k+1's
-    //     fragments from stage k+1 and the copies of step k+4 into stage k
+    //     fragments from stage k+1 (three per MFMA in the first half, so they
+    //     are done long before the next wait) and the copies of step k+4
+    //     into stage k
     // Copies have three steps to land; the loop is unrolled by the stage
     // count so every stage is named statically; past the last step the
     // copies repeat the last tile and the reads reread a stage (harmless).
@@ -246,9 +248,11 @@ __global__ __launch_bounds__(MX_NT, 1) void gemm_mx_kernel(MxArgs p, int tiles_m
         static_for<16>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             mma_one(fc, qc);
-            read_piece(fn, nxt, q);
-            if constexpr (q < 8)
-                read_piece(fn, nxt, 16 + q);
+            if constexpr (q < 8) {
+                read_piece(fn, nxt, 3 * q);
+                read_piece(fn, nxt, 3 * q + 1);
+                read_piece(fn, nxt, 3 * q + 2);
+            }
             if constexpr (q >= 4 && q < 4 + MX_COPIES)
                 copy(kc, cur, q - 4);
             __builtin_amdgcn_sched_barrier(0);
