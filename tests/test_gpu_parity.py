@@ -564,6 +564,45 @@ def test_attention_full_size_heads(tg, causal):
         assert np.max(np.abs(lse[b:b + 1, h:h + 1] - lse_ref)) < 2e-3
 
 
+# ------------------------------------------------------------ edge cases
+
+def test_mx_k_zero_gives_activated_bias(tg):
+    import torch
+    p = inputs.mx_problem(0, 0, 40, 24, 0, seed=210, bias=True, act=inputs.ACT_GELU_TANH)
+    bits, kern = run_mx(tg, p)
+    assert kern.startswith("mx_generic")
+    f64, rbits = oracle.gemm_mx(0, 0, p["A"], p["SA"], p["B"], p["SB"], p["bias"],
+                                oracle.ACT_GELU_TANH, dt=BF16)
+    util.check_tol(BF16, bits, f64, "mx K=0", ref_bits=rbits)
+
+
+@pytest.mark.parametrize("S,D", [(1, 128), (7, 32), (129, 128)])
+def test_attention_tiny_and_ragged(tg, S, D):
+    for causal in (False, True):
+        p = inputs.attention_problem(F16, 1, 3, S, D, seed=211 + S, causal=causal)
+        bits, lse, kern = run_attn(tg, p)
+        assert kern.startswith("attn_generic")
+        f64, _, lse_ref = oracle.attention(F16, p["Q"], p["K"], p["V"], causal=causal)
+        util.check_tol(F16, bits, f64, "attention S=%d D=%d" % (S, D))
+        assert np.max(np.abs(lse - lse_ref)) < 2e-3
+
+
+def test_transposed_b_k_zero(tg):
+    # K = 0 with B given as [N,K] (TG_OP_T): C = act(bias) + R
+    import torch
+    dt = BF16
+    bias = inputs.draw(np.random.default_rng(212), (24,), "bias", dt)
+    R = inputs.draw(np.random.default_rng(213), (8, 24), "uniform", dt)
+    bd, Rd = util.to_dev(bias, dt), util.to_dev(R, dt)
+    C = torch.empty((8, 24), dtype=torch.bfloat16, device="cuda")
+    tg.gemm_ex_ptr(dt, 8, 24, 0, 0, 0, 0, 0, tg.OP_T, C.data_ptr(), 24,
+                   bias=bd.data_ptr(), act=1, R=Rd.data_ptr(), ldr=24)
+    torch.cuda.synchronize()
+    f64, rbits = oracle.gemm_ex(dt, np.zeros((8, 0), np.uint16), np.zeros((24, 0), np.uint16),
+                                trans_b=True, bias=bias, act=oracle.ACT_GELU_TANH, R=R)
+    util.check_tol(dt, util.to_bits(C), f64, "B[N,K] K=0", ref_bits=rbits)
+
+
 def test_dispatch_choices(tg):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")

@@ -209,6 +209,9 @@ def _bytes2d(t, name):
     """(pointer, pitch) of a 2-D row-major uint8 (or float8) device tensor."""
     if t.dim() != 2 or t.element_size() != 1:
         raise ValueError("%s must be a 2-D tensor of bytes" % name)
+    if t.numel() == 0:
+        # an empty operand is never read; its strides carry no layout
+        return t.data_ptr(), t.shape[1]
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must be row-major" % name)
     if not t.is_cuda:
