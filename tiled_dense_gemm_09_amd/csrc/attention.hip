@@ -17,8 +17,14 @@
 //    (256-byte rows, granule c of row r at c ^ (r % 16)) and read with
 //    128-bit reads.
 //  - Online softmax in the log2 domain: t = s * scale * log2(e); per row a
-//    running max m and sum l; each tile rescales O and l by 2^(m_old - m_new).
-//    A row's 64 scores of a tile sit in lanes l and l ^ 32 (32 each).
+//    reference maximum m and a sum l.  A row's 64 scores of a tile sit in
+//    lanes l and l ^ 32 (32 each), combined with v_permlane32_swap.  The
+//    reference is raised (and O and l rescaled by 2^(m_old - m_new)) only
+//    when some row of the wave sees a tile maximum more than 8 above its
+//    reference; otherwise the exponentials may reach 2^8, which FP32 and the
+//    16-bit P hold with the same relative precision as values below 1.  Every
+//    exponent of a row is still taken against the one reference its O and l
+//    share, so the result is the same softmax.
 //  - O += P V on the same MFMA with V as src0 (rows = d) and P as src1.  The
 //    16 keys of each P chunk are taken in the order the S accumulator holds
 //    them (registers 8c .. 8c+7: keys 16c + 4(l/32) + {0..3} and
@@ -43,11 +49,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int AT_D = 128, AT_BM = 128, AT_BN = 64, AT_NT = 256;
+constexpr float AT_SLACK = 8.f;                  // log2 units a tile maximum may exceed the reference
 constexpr int AT_TILE = AT_BN * AT_D * 2;        // 16 KiB: one K or V tile
 constexpr int AT_STAGE = 2 * AT_TILE;            // K tile, then V tile
 
 __host__ __device__ constexpr int swz_k(int r) { return r & 15; }
 __host__ __device__ constexpr int swz_v(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
+
+// max and sum over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_max(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 } // namespace
 
@@ -184,8 +205,10 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = __builtin_fmaxf(mx, s[jb][r]);
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = __builtin_fmaxf(m_run, mx * c2);
+        mx = pair_max(mx);
+        const float tm = mx * c2;
+        const bool raise = __builtin_amdgcn_ballot_w64(tm > m_run + AT_SLACK) != 0;
+        const float m_new = raise ? __builtin_fmaxf(m_run, tm) : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float rs = 0.f;
 #pragma unroll
@@ -196,14 +219,16 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
                 s[jb][r] = e;
                 rs += e;
             }
-        rs += __shfl_xor(rs, 32);
+        rs = pair_sum(rs);
         l_run = l_run * alpha + rs;
         m_run = m_new;
+        if (raise) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc_o[0][db][r] *= alpha;
+                for (int r = 0; r < 16; ++r)
+                    acc_o[0][db][r] *= alpha;
+        }
 
         // O += P V: four 16-key chunks, four 32-column d blocks
 #pragma unroll
