@@ -258,7 +258,25 @@ def run_secondary(args, torch, inputs, tg):
                 "ms": round(ms, 5), "TFLOP/s": round(tf, 1),
                 "frac_fp8_mfma_peak": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": tg.last_kernel()}
             log("  ", out["mx_e4m3_%dx%dx%d" % (n, n, n)])
-            del A, SA, B, SB, C
+            # context only: the ROCm library's 8-bit GEMMs (torch._scaled_mm) on
+            # the same operands, with one scale per tensor (no block scaling)
+            # and with the same e8m0 scales per 32 k
+            ctx8 = out.setdefault("context_rocm_blas_fp8_scaled_mm", {})
+            a8, b8 = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn)
+            one = torch.tensor(1.0, device="cuda")
+            sa = SA.t().contiguous().view(torch.float8_e8m0fnu)
+            sb = SB.t().contiguous().view(torch.float8_e8m0fnu)
+            for key, (xa, xb) in (("e4m3_per_tensor_%d" % n, (one, one)),
+                                  ("mx_e4m3_1x32_%d" % n, (sa, sb))):
+                try:
+                    ms = time_launches(lambda: torch._scaled_mm(
+                        a8, b8.t(), scale_a=xa, scale_b=xb, out_dtype=torch.bfloat16), steps, warm)
+                    ctx8[key] = {"ms": round(ms, 5),
+                                 "TFLOP/s": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+                except Exception as e:  # not every build has both paths
+                    ctx8[key] = {"error": str(e)[:120]}
+            log("  ", ctx8)
+            del A, SA, B, SB, C, a8, b8, sa, sb
 
     if args.only in (None, "attn"):
         # fused forward attention, head dim 128, 16384 tokens per launch;
