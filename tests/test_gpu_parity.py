@@ -528,6 +528,22 @@ def test_attention_random(tg, dt, causal, B, H, S, D):
         assert np.array_equal(bits[:, :, 0], p["V"][:, :, 0])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [512, 384])
+def test_attention_rising_scores(tg, causal, S):
+    # key j scaled by 1 + j/24: row maxima keep rising along the sequence, so
+    # the running reference is raised (and O, l rescaled) on many tiles, not
+    # only the first
+    p = inputs.attention_problem(BF16, 1, 2, S, 128, seed=185 + S, causal=causal)
+    k = util.decode(BF16, p["K"]) * (1.0 + np.arange(S) / 24.0)[None, None, :, None]
+    p["K"] = inputs.to_bits(k, BF16)
+    bits, lse, kern = run_attn(tg, p)
+    assert kern.startswith("attn_fwd")
+    f64, _, lse_ref = oracle.attention(BF16, p["Q"], p["K"], p["V"], causal=causal)
+    util.check_tol(BF16, bits, f64, "attention rising scores")
+    assert np.all(np.abs(lse - lse_ref) < 1e-3 + 1e-4 * np.abs(lse_ref))
+
+
 def test_attention_uniform_integer_values(tg):
     # Q = 0: every weight is exactly 1, O = mean of the V rows it can see
     p = inputs.attention_problem(BF16, 1, 2, 256, 128, seed=180, kind="int", causal=True)
