@@ -310,6 +310,14 @@ def run_secondary(args, torch, inputs, tg):
                                             "frac_mfma_peak": round(tf / PEAK_F16_TFLOPS, 4),
                                             "kernel": tg.last_kernel()}
         log("  ", out["bf16_qkv_8192x4096x4096x3"])
+        # context only: the library GEMM called three times on the same operands
+        def three():
+            for w, o in zip(Ws, outs):
+                torch.matmul(X, w, out=o)
+        ms = time_launches(three, steps, warm)
+        out.setdefault("context_rocm_blas_torch_matmul", {})["bf16_qkv_three_matmuls"] = {
+            "ms": round(ms, 5), "TFLOP/s": round(3 * 2.0 * q["M"] * q["N"] * q["K"] /
+                                                 (ms * 1e-3) / 1e12, 1)}
         del X, Ws, outs
 
     if args.only in (None, "square8192"):
@@ -357,7 +365,7 @@ def run_secondary(args, torch, inputs, tg):
     if args.only in (None, "vendor"):
         # context only: the ROCm BLAS library GEMM (torch.matmul) on the same
         # operands, no epilogue; nothing of the measured path runs through it
-        ctx = {}
+        ctx = out.setdefault("context_rocm_blas_torch_matmul", {})
         for name, dtc in (("f16_4096_gelu", 1), ("bf16_8192", 2)):
             p = inputs.config_problem(name)
             A, B = dev(p["A"], dtc), dev(p["B"], dtc)
@@ -367,6 +375,17 @@ def run_secondary(args, torch, inputs, tg):
             ctx["%s_%dx%dx%d" % ("f16" if dtc == 1 else "bf16", p["M"], p["N"], p["K"])] = {
                 "ms": round(ms, 5), "TFLOP/s": round(tf, 1)}
             del A, B, C
+        # the same workload done the unfused way: the library GEMM with its
+        # bias epilogue (torch.addmm), then GELU_tanh as a second pass
+        p = inputs.config_problem("f16_4096_gelu")
+        A, B, bias = dev(p["A"], 1), dev(p["B"], 1), dev(p["bias"], 1)
+        C = torch.empty((p["M"], p["N"]), dtype=A.dtype, device="cuda")
+        fn = torch.nn.functional.gelu
+        ms = time_launches(lambda: fn(torch.addmm(bias, A, B, out=C), approximate="tanh"),
+                           steps, warm)
+        ctx["f16_4096_gelu_unfused_addmm_then_gelu"] = {
+            "ms": round(ms, 5), "TFLOP/s": round(2.0 * 4096 ** 3 / (ms * 1e-3) / 1e12, 1)}
+        del A, B, bias, C
         out["context_rocm_blas_torch_matmul"] = ctx
         log("  ", ctx)
 
