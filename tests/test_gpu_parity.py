@@ -195,6 +195,59 @@ def test_skinny_matches_tiled_on_integers(tg, monkeypatch):
     util.check_exact(a, b, "skinny vs tiled")
 
 
+# Both column widths of the streaming small-M kernel, forced, on shapes with
+# one split, a few splits and more than eight (a second combine round), with
+# M below 16 (rows past M are clamped on load and never stored).
+SKINNY_FORCED = [
+    # bn, dt, M, N, K, splits ("" = the planner's choice)
+    (128, BF16, 16, 2048, 4096, ""), (128, F16, 7, 1024, 4096, "1"),
+    (128, BF16, 16, 4096, 5120, "10"), (128, F16, 1, 384, 1536, ""),
+    (256, BF16, 16, 2048, 4096, ""), (256, F16, 9, 1024, 4096, "1"),
+    (256, BF16, 16, 2048, 8192, "11"),
+]
+
+
+@pytest.mark.parametrize("bn,dt,M,N,K,splits", SKINNY_FORCED)
+@pytest.mark.parametrize("integer", [False, True])
+def test_skinny_stream_widths(tg, monkeypatch, bn, dt, M, N, K, splits, integer):
+    monkeypatch.setenv("TG_SKINNY_BN", str(bn))
+    monkeypatch.setenv("TG_SKINNY_SPLITS", splits)
+    seed = 5000 + bn + M + N // 128 + K // 512 + (7 if integer else 0)
+    p = inputs.problem(dt, M, N, K, seed=seed, kind="int" if integer else "normal",
+                       b_scale=1.0 if integer else K ** -0.5)
+    say("case skinny bn", bn, "splits", splits or "auto", dt, M, N, K, "integer" if integer else "")
+    bits, kern = run(tg, p)
+    say("  kernel", kern)
+    assert kern.startswith("skinny_stream_bn%d_" % bn)
+    if splits:
+        assert ("_split%sx" % splits) in kern
+    f64, rbits = oracle.gemm(dt, p["A"], p["B"])
+    if integer:
+        util.check_exact(bits, rbits, "skinny bn%d integer" % bn)
+    else:
+        util.check_tol(dt, bits, f64, "skinny bn%d" % bn, ref_bits=rbits)
+
+
+@pytest.mark.parametrize("bn", [128, 256])
+def test_skinny_stream_epilogue(tg, monkeypatch, bn):
+    """Bias, GELU_tanh and a residual through the split-K combine."""
+    import torch
+    monkeypatch.setenv("TG_SKINNY_BN", str(bn))
+    dt, M, N, K = BF16, 13, 2048, 4096
+    p = inputs.problem(dt, M, N, K, seed=5200 + bn, kind="normal", b_scale=K ** -0.5,
+                       bias=True, act=inputs.ACT_GELU_TANH)
+    R = inputs.draw(np.random.default_rng(5300 + bn), (M, N), "uniform", dt)
+    A, B, bias = dev_problem(p)
+    Rd = util.to_dev(R, dt)
+    C = tg.gemm(A, B, bias=bias, act="gelu_tanh", residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("case skinny epilogue bn", bn, "kernel", kern)
+    assert kern.startswith("skinny_stream_bn%d_" % bn) and "_split1x" not in kern
+    f64, rbits = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], act=oracle.ACT_GELU_TANH, R=R)
+    util.check_tol(dt, util.to_bits(C), f64, "skinny epilogue bn%d" % bn, ref_bits=rbits)
+
+
 # ----------------------------------------------------------- 8192^3 square
 
 def test_square_8192_sampled(tg):

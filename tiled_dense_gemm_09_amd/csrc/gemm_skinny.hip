@@ -283,35 +283,65 @@ __global__ __launch_bounds__(SK_NT, 2) void gemm_skinny_kernel(GemmArgs p, int k
 }
 
 // ---------------------------------------------------------------------------
-// Streaming variant for the common case (N a multiple of 256, K a multiple of
-// 256): W and X go from memory straight into LDS with 16-byte direct-to-LDS
-// copies, three 64-deep slabs ahead of use, through four LDS stages; no
-// staging registers and no VALU transposition.  The W fragments (8
+// Streaming variant for the common case: W and X go from memory straight
+// into LDS with 16-byte direct-to-LDS copies, STAGES-1 64-deep slabs ahead of
+// use; no staging registers and no VALU transposition.  The W fragments (8
 // consecutive k of one column per lane) come from the LDS transposing read,
 // exactly as for B in the asynchronous square kernel.
 //
-// LDS stage (36 KiB): W slab [64 k][256 n] (512-byte rows, 16-byte granule c
-// of row r stored at c ^ ({0,6,10,12}[r & 3] ^ 2 ((r >> 3) & 1)), which makes
-// the transposing reads of two 16-lane groups at once conflict-free), then X
-// slab [16 rows][64 k] (granule c of row r at c ^ (r & 7)), then 2 KiB that
-// waves 2 and 3 fill with a second copy of X so every wave issues the same
-// number of copies per slab.
+// Two column widths.  BN = 256 (N a multiple of 256, K of 256): four stages
+// of 36 KiB.  BN = 128 (N a multiple of 128, K of 512): eight stages of
+// 20 KiB, so more bytes are in flight (seven 16 KiB slabs against three 32
+// KiB ones) and a column tile needs half as many K splits for the same
+// number of workgroups; the workgroup that combines a column tile's split
+// partials then reads a quarter of the data, and that read, issued by one
+// CU after every split has finished, is the part of the launch that no other
+// work overlaps.
+//
+// LDS stage: W slab [64 k][BN n] (rows of 2 BN bytes, 16-byte granule c of
+// row r stored at c ^ swz_w(r), which makes the transposing reads of two
+// 16-lane groups at once conflict-free), then X slab [16 rows][64 k]
+// (granule c of row r at c ^ (r & 7)), then 2 KiB that waves 2 and 3 fill
+// with a second copy of X so every wave issues the same number of copies per
+// slab.
 namespace {
 
-constexpr int SA_BN = 256, SA_BK = 64, SA_NT = 256, SA_STAGES = 4;
-constexpr int SA_W_BYTES = SA_BK * SA_BN * 2;        // 32 KiB
-constexpr int SA_X_BYTES = 16 * SA_BK * 2;           // 2 KiB
-constexpr int SA_STAGE_BYTES = SA_W_BYTES + 2 * SA_X_BYTES;
-constexpr int SA_COPIES = 9;                         // 1 KiB copies per wave per slab
+constexpr int SA_BK = 64, SA_NT = 256;
+constexpr int SA_X_BYTES = 16 * SA_BK * 2; // 2 KiB
+
+template <int BN>
+struct SaCfg {
+    static_assert(BN == 128 || BN == 256, "streaming column widths");
+    static constexpr int STAGES = BN == 256 ? 4 : 8;
+    static constexpr int W_BYTES = SA_BK * BN * 2;
+    static constexpr int STAGE_BYTES = W_BYTES + 2 * SA_X_BYTES;
+    static constexpr int W_COPIES = W_BYTES / 1024 / 4;  // 1 KiB W copies per wave per slab
+    static constexpr int COPIES = W_COPIES + 1;          // plus one X copy
+    static constexpr int ROWS_PER_COPY = 1024 / (2 * BN);
+    static constexpr int GRANULES = BN / 8;              // 16-byte granules per W row
+    static constexpr int WAVE_COLS = BN / 4;             // columns per wave
+    static constexpr int NJ = WAVE_COLS / 16;            // 16-column MFMA blocks per wave
+    static constexpr int CPT = BN / 16;                  // combine: columns per thread
+};
+
+// Granule swizzle of W row r.  BN = 256 (512-byte rows, two bank sweeps per
+// row): {0,6,10,12}[r & 3] ^ 2 ((r >> 3) & 1).  BN = 128 (256-byte rows, one
+// sweep of the 64 four-byte banks): a 16-lane transposing read touches rows
+// r0..r0+3 of one granule pair and a second group rows r0+8..r0+11, so the
+// pair index is moved by r & 3 and by bit 3 of r: eight distinct pairs, all
+// 64 banks.
+template <int BN>
+__host__ __device__ constexpr int swz_w(int r)
+{
+    if constexpr (BN == 256)
+        return ((r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 10 : 12) ^ (2 * ((r >> 3) & 1));
+    else
+        return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__host__ __device__ constexpr int swz_w(int r)
-{
-    return ((r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 10 : 12) ^ (2 * ((r >> 3) & 1));
-}
 
 template <int N>
 __device__ __forceinline__ void sa_wait_vmcnt()
@@ -329,49 +359,48 @@ __device__ __forceinline__ void sa_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Calls f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 } // namespace
 
-template <int DT, int ACT>
+template <int DT, int ACT, int BN>
 __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p, int k_chunk,
                                                                      int splits, float *ws,
                                                                      int *counters)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[SA_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[SA_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[SA_STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[SA_STAGE_BYTES];
-    __shared__ int s_last;
-    auto stage = [&](auto sidx) -> unsigned char * {
-        constexpr int S = decltype(sidx)::value;
-        if constexpr (S == 0)
-            return st0;
-        else if constexpr (S == 1)
-            return st1;
-        else if constexpr (S == 2)
-            return st2;
-        else
-            return st3;
-    };
+    using C = SaCfg<BN>;
+    constexpr int STAGES = C::STAGES, NJ = C::NJ, CPT = C::CPT;
+    __shared__ __attribute__((aligned(1024))) unsigned char st[STAGES][C::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile_n = blockIdx.x / splits;
     const int split = blockIdx.x - tile_n * splits;
-    const int n0 = tile_n * SA_BN;
+    const int n0 = tile_n * BN;
     const int M = p.M, N = p.N;
     const int kbeg = split * k_chunk;
-    const int slabs = (min(p.K, kbeg + k_chunk) - kbeg) / SA_BK; // a multiple of 4
+    const int slabs = (min(p.K, kbeg + k_chunk) - kbeg) / SA_BK; // a multiple of STAGES
     const unsigned short *W = p.B[0];
 
-    // copies: W copy c (0..7) of this wave fills rows 2q, 2q+1 (q = 8 wave + c... /4)
-    // -> lane: row 2q + lane/32, granule (lane%32) ^ swz_w(row).
-    const unsigned short *gw[8];
+    // W copy c of this wave is copy q = wave W_COPIES + c of the slab: rows
+    // ROWS_PER_COPY q .. +ROWS_PER_COPY-1; lane -> row ROWS_PER_COPY q +
+    // lane / GRANULES, LDS granule lane % GRANULES, which holds W granule
+    // (lane % GRANULES) ^ swz_w(row).
+    const unsigned short *gw[C::W_COPIES];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int q = wave * 8 + c;
-        const int r = 2 * q + (lane >> 5);
-        gw[c] = W + (int64_t)(kbeg + r) * p.ldb + n0 + ((lane & 31) ^ swz_w(r)) * 8;
+    for (int c = 0; c < C::W_COPIES; ++c) {
+        const int q = wave * C::W_COPIES + c;
+        const int r = C::ROWS_PER_COPY * q + lane / C::GRANULES;
+        gw[c] = W + (int64_t)(kbeg + r) * p.ldb + n0 + ((lane % C::GRANULES) ^ swz_w<BN>(r)) * 8;
     }
     // X copy: rows 8 (wave & 1) + lane/8 (clamped to M-1: rows >= M only feed
     // output rows that are never stored), granule (lane%8) ^ (row & 7).
@@ -380,34 +409,36 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         p.A + (int64_t)min(xr, M - 1) * p.lda + kbeg + (((lane & 7) ^ (xr & 7)) * 8);
     const int64_t w_step = (int64_t)SA_BK * p.ldb;
 
-    auto copy = [&](int s, unsigned char *st, int c) {
-        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
-        if (c < 8) {
-            const unsigned dst = lds + (wave * 8 + c) * 1024;
+    auto copy = [&](int s, unsigned char *stage, int c) {
+        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)stage;
+        if (c < C::W_COPIES) {
+            const unsigned dst = lds + (wave * C::W_COPIES + c) * 1024;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gw[c] + s * w_step), "{m0}"(dst)
                          : "memory");
         } else {
-            const unsigned dst = lds + SA_W_BYTES + wave * 1024;
+            const unsigned dst = lds + C::W_BYTES + wave * 1024;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gx + s * SA_BK), "{m0}"(dst)
                          : "memory");
         }
     };
 
-    // fragments: wave w owns columns 64 w .. 64 w + 63 (4 blocks of 16).
-    // W fragment of block j, 32-deep half kk, read half h: 16-lane group g,
-    // jj = lane % 16: row 32 kk + 8 g + 4 h + jj/4, column 64 w + 16 j + 4 (jj%4).
-    int w_off[4][2][2];
+    // fragments: wave w owns columns WAVE_COLS w .. +WAVE_COLS-1 (NJ blocks
+    // of 16).  W fragment of block j, 32-deep half kk, read half h: 16-lane
+    // group g, jj = lane % 16: row 32 kk + 8 g + 4 h + jj/4, column
+    // WAVE_COLS w + 16 j + 4 (jj%4).
+    int w_off[NJ][2][2];
     {
         const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = 32 * kk + 8 * g + 4 * h + (jj >> 2);
-                    const int col = wave * 64 + 16 * j + 4 * (jj & 3);
-                    w_off[j][kk][h] = r * 512 + (((col >> 3) ^ swz_w(r)) * 16) + (col & 7) * 2;
+                    const int col = wave * C::WAVE_COLS + 16 * j + 4 * (jj & 3);
+                    w_off[j][kk][h] =
+                        r * (2 * BN) + (((col >> 3) ^ swz_w<BN>(r)) * 16) + (col & 7) * 2;
                 }
     }
     // X fragment of half kk: row lane % 16, granule 4 kk + lane / 16.
@@ -415,70 +446,64 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int r = lane & 15;
-        x_off[kk] = SA_W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
+        x_off[kk] = C::W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
     }
 
-    f32x4 acc[4];
+    f32x4 acc[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const unsigned char *st) {
+    auto compute = [&](const unsigned char *stage) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const u32x4 xf = *reinterpret_cast<const u32x4 *>(st + x_off[kk]);
+            const u32x4 xf = *reinterpret_cast<const u32x4 *>(stage + x_off[kk]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const u32x2 lo = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                               (lds_s16x4 *)(st + w_off[j][kk][0])));
+                               (lds_s16x4 *)(stage + w_off[j][kk][0])));
                 const u32x2 hi = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                               (lds_s16x4 *)(st + w_off[j][kk][1])));
+                               (lds_s16x4 *)(stage + w_off[j][kk][1])));
                 acc[j] = mfma16x16x32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, xf, acc[j]);
             }
         }
     };
 
-    // slab s: wait for its copies (those of s+1, s+2 may stay in flight),
-    // barrier, copy slab s+3 into the stage slab s-1 used (clamped past the
-    // end: repeats the last slab into a stage nobody reads), compute.
+    // slab s: wait for its copies (those of the next STAGES-2 slabs may stay
+    // in flight), barrier, copy slab s+STAGES-1 into the stage slab s-1 used
+    // (clamped past the end: repeats the last slab into a stage nobody
+    // reads), compute.
     auto step = [&](int s, auto sidx) {
         constexpr int S = decltype(sidx)::value;
-        sa_wait_vmcnt<2 * SA_COPIES>();
+        sa_wait_vmcnt<(STAGES - 2) * C::COPIES>();
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         sa_barrier();
-        const int sc = min(s + 3, slabs - 1);
-        unsigned char *dst = stage(std::integral_constant<int, (S + 3) % 4>{});
+        const int sc = min(s + STAGES - 1, slabs - 1);
 #pragma unroll
-        for (int c = 0; c < SA_COPIES; ++c)
-            copy(sc, dst, c);
-        compute(stage(sidx));
+        for (int c = 0; c < C::COPIES; ++c)
+            copy(sc, st[(S + STAGES - 1) % STAGES], c);
+        compute(st[S]);
     };
+    auto prologue = [&](auto sidx) {
+        constexpr int S = decltype(sidx)::value;
 #pragma unroll
-    for (int c = 0; c < SA_COPIES; ++c)
-        copy(0, st0, c);
-#pragma unroll
-    for (int c = 0; c < SA_COPIES; ++c)
-        copy(min(1, slabs - 1), st1, c);
-#pragma unroll
-    for (int c = 0; c < SA_COPIES; ++c)
-        copy(min(2, slabs - 1), st2, c);
-    for (int s = 0; s < slabs; s += 4) {
-        step(s, std::integral_constant<int, 0>{});
-        step(s + 1, std::integral_constant<int, 1>{});
-        step(s + 2, std::integral_constant<int, 2>{});
-        step(s + 3, std::integral_constant<int, 3>{});
-    }
+        for (int c = 0; c < C::COPIES; ++c)
+            copy(min(S, slabs - 1), st[S], c);
+    };
+    static_for<0, STAGES - 1>([&](auto i) { prologue(i); });
+    for (int s = 0; s < slabs; s += STAGES)
+        static_for<0, STAGES>([&](auto i) { step(s + decltype(i)::value, i); });
     sa_wait_vmcnt<0>();
 
-    // Lane l holds Y[m = l % 16][n = 64 w + 16 j + 4 (l / 16) + r] in acc[j][r].
+    // Lane l holds Y[m = l % 16][n = WAVE_COLS w + 16 j + 4 (l / 16) + r] in acc[j][r].
     const int m = lane & 15;
     if (splits == 1) {
         if (m < M) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + wave * 64 + 16 * j + 4 * (lane >> 4);
+            for (int j = 0; j < NJ; ++j) {
+                const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -507,40 +532,44 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     // no cache-wide writeback or invalidate is needed.
     const int64_t ws_ld = (int64_t)N;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wave * 64 + 16 * j + 4 * (lane >> 4);
+    for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
         float *dst = ws + ((int64_t)split * 16 + m) * ws_ld + n;
         asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(acc[j]) : "memory");
     }
     sa_wait_vmcnt<0>();
+    // Every wave has waited for its own copies, so the stages are idle and
+    // the first word of stage 0 carries the arrival flag.
+    int *s_last = reinterpret_cast<int *>(&st[0][0]);
     __syncthreads();
     if (tid == 0) {
         const int old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == splits - 1);
+        *s_last = (old == splits - 1);
     }
     __syncthreads();
-    if (!s_last)
+    if (!*s_last)
         return;
 
-    // thread -> row rm = tid / 16, columns n0 + 16 (tid % 16) .. +15; eight
-    // splits per round (one round for the usual split counts): 32 loads in
-    // flight, then added in split order (indices past the last split repeat
-    // it and are not added)
+    // thread -> row rm = tid / 16, columns n0 + CPT (tid % 16) .. +CPT-1;
+    // eight splits per round (one round for the usual split counts): 8 CPT/4
+    // loads in flight, then added in split order (indices past the last
+    // split repeat it and are not added)
+    constexpr int Q = CPT / 4; // 16-byte loads per split
     const int rm = tid >> 4;
-    const int cn = n0 + (tid & 15) * 16;
-    float sum[16];
+    const int cn = n0 + (tid & 15) * CPT;
+    float sum[CPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < CPT; ++i)
         sum[i] = 0.f;
     for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-        f32x4 v[8][4];
+        f32x4 v[8][Q];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int sp = min(sp0 + u, splits - 1);
             const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < Q; ++q)
                 asm volatile("global_load_dwordx4 %0, %1, off sc1"
                              : "=v"(v[u][q])
                              : "v"(src + 4 * q)
@@ -548,26 +577,37 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         }
         // the loads above are invisible to the compiler's wait tracking: wait
         // here and pass the values through so nothing reads them earlier
-        // (loads return in order: vmcnt(16) covers the first 16, vmcnt(0) the rest)
-        asm volatile("s_waitcnt vmcnt(16)"
-                     : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
-                       "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
-                       "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[2][2]), "+v"(v[2][3]),
-                       "+v"(v[3][0]), "+v"(v[3][1]), "+v"(v[3][2]), "+v"(v[3][3])
-                     :
-                     : "memory");
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[4][2]), "+v"(v[4][3]),
-                       "+v"(v[5][0]), "+v"(v[5][1]), "+v"(v[5][2]), "+v"(v[5][3]),
-                       "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[6][2]), "+v"(v[6][3]),
-                       "+v"(v[7][0]), "+v"(v[7][1]), "+v"(v[7][2]), "+v"(v[7][3])
-                     :
-                     : "memory");
+        // (loads return in order)
+        if constexpr (Q == 4) {
+            asm volatile("s_waitcnt vmcnt(16)"
+                         : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
+                           "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
+                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[2][2]), "+v"(v[2][3]),
+                           "+v"(v[3][0]), "+v"(v[3][1]), "+v"(v[3][2]), "+v"(v[3][3])
+                         :
+                         : "memory");
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[4][2]), "+v"(v[4][3]),
+                           "+v"(v[5][0]), "+v"(v[5][1]), "+v"(v[5][2]), "+v"(v[5][3]),
+                           "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[6][2]), "+v"(v[6][3]),
+                           "+v"(v[7][0]), "+v"(v[7][1]), "+v"(v[7][2]), "+v"(v[7][3])
+                         :
+                         : "memory");
+        } else {
+            static_assert(Q == 2, "combine load count");
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]),
+                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]),
+                           "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[5][0]), "+v"(v[5][1]),
+                           "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[7][0]), "+v"(v[7][1])
+                         :
+                         : "memory");
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (sp0 + u < splits) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < Q; ++q)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         sum[4 * q + r] += v[u][q][r];
@@ -575,19 +615,19 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         }
     }
     if (rm < M) {
-        float v[16];
+        float v[CPT];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < CPT; ++i) {
             float x = sum[i];
             if (p.bias != nullptr)
                 x += from_bits<DT>(p.bias[cn + i]);
             v[i] = activate<ACT>(x);
         }
         if (p.R != nullptr)
-            add_residual<DT, 16>(p.R, p.ldr, rm, cn, p.N, v);
+            add_residual<DT, CPT>(p.R, p.ldr, rm, cn, p.N, v);
         unsigned short *cp = p.C[0] + (int64_t)rm * p.ldc + cn;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < CPT / 8; ++q) {
             u32x4 o = {pack2<DT>(v[8 * q + 0], v[8 * q + 1]), pack2<DT>(v[8 * q + 2], v[8 * q + 3]),
                        pack2<DT>(v[8 * q + 4], v[8 * q + 5]), pack2<DT>(v[8 * q + 6], v[8 * q + 7])};
             *reinterpret_cast<u32x4 *>(cp + 8 * q) = o;
@@ -791,19 +831,37 @@ SkinnyPlan plan_skinny(int M, int N, int K)
         pl.k_chunk = K;
         return pl;
     }
-    if (N % SA_BN == 0 && K % (SA_STAGES * SA_BK) == 0) {
-        // streaming kernel: about one workgroup per CU
+    // Streaming kernel, about one workgroup per CU.  128-column tiles when
+    // 256-column ones would need four or more K splits to fill the chip (N <=
+    // 16384): the combine then reads half as many splits of half as many
+    // columns.  Wider N keeps the 256-column tiles, whose 512-byte row pieces
+    // stream from HBM slightly faster (measured at N = 32768 and 65536).
+    const bool ok256 = N % 256 == 0 && K % (SaCfg<256>::STAGES * SA_BK) == 0;
+    const bool ok128 = N % 128 == 0 && K % (SaCfg<128>::STAGES * SA_BK) == 0;
+    const char *bn_env = getenv("TG_SKINNY_BN"); // for sweeps
+    const int want = bn_env && *bn_env ? atoi(bn_env) : 0;
+    int bn = 0;
+    if (want == 128 && ok128)
+        bn = 128;
+    else if (want == 256 && ok256)
+        bn = 256;
+    else if (ok128 && (N / 256 <= 64 || !ok256))
+        bn = 128;
+    else if (ok256)
+        bn = 256;
+    if (bn) {
+        const int stages = bn == 256 ? SaCfg<256>::STAGES : SaCfg<128>::STAGES;
         pl.streaming = 1;
-        pl.bn = SA_BN;
-        pl.n_tiles = N / SA_BN;
-        const int quanta = K / (SA_STAGES * SA_BK);
+        pl.bn = bn;
+        pl.n_tiles = N / bn;
+        const int quanta = K / (stages * SA_BK);
         int splits = (256 + pl.n_tiles / 2) / pl.n_tiles;
         const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
         if (force && atoi(force) > 0)
             splits = atoi(force);
         splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
         const int per = (quanta + splits - 1) / splits;
-        pl.k_chunk = per * SA_STAGES * SA_BK;
+        pl.k_chunk = per * stages * SA_BK;
         pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
         return pl;
     }
@@ -859,20 +917,28 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
         return hipGetLastError();
     }
     if (pl.streaming) {
-#define TG_SA(DT_, ACT_)                                                                         \
-    hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_>), grid, dim3(SA_NT), 0, s, a,          \
+#define TG_SA(DT_, ACT_, BN_)                                                                    \
+    hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_, BN_>), grid, dim3(SA_NT), 0, s, a,     \
                        pl.k_chunk, pl.splits, ws, counters)
+#define TG_SA_BN(DT_, ACT_)                                                                      \
+    do {                                                                                         \
+        if (pl.bn == 128)                                                                        \
+            TG_SA(DT_, ACT_, 128);                                                               \
+        else                                                                                     \
+            TG_SA(DT_, ACT_, 256);                                                               \
+    } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)
-                TG_SA(DT_F16, ACT_GELU);
+                TG_SA_BN(DT_F16, ACT_GELU);
             else
-                TG_SA(DT_F16, ACT_NONE);
+                TG_SA_BN(DT_F16, ACT_NONE);
         } else {
             if (act == ACT_GELU)
-                TG_SA(DT_BF16, ACT_GELU);
+                TG_SA_BN(DT_BF16, ACT_GELU);
             else
-                TG_SA(DT_BF16, ACT_NONE);
+                TG_SA_BN(DT_BF16, ACT_NONE);
         }
+#undef TG_SA_BN
 #undef TG_SA
         return hipGetLastError();
     }
