@@ -321,7 +321,6 @@ struct SaCfg {
     static constexpr int GRANULES = BN / 8;              // 16-byte granules per W row
     static constexpr int WAVE_COLS = BN / 4;             // columns per wave
     static constexpr int NJ = WAVE_COLS / 16;            // 16-column MFMA blocks per wave
-    static constexpr int CPT = BN / 16;                  // combine: columns per thread
 };
 
 // Granule swizzle of W row r.  BN = 256 (512-byte rows, two bank sweeps per
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                                                                      int *counters)
 {
     using C = SaCfg<BN>;
-    constexpr int STAGES = C::STAGES, NJ = C::NJ, CPT = C::CPT;
+    constexpr int STAGES = C::STAGES, NJ = C::NJ;
     __shared__ __attribute__((aligned(1024))) unsigned char st[STAGES][C::STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -386,7 +385,7 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     const int tile_n = blockIdx.x / splits;
     const int split = blockIdx.x - tile_n * splits;
     const int n0 = tile_n * BN;
-    const int M = p.M, N = p.N;
+    const int M = p.M;
     const int kbeg = split * k_chunk;
     const int slabs = (min(p.K, kbeg + k_chunk) - kbeg) / SA_BK; // a multiple of STAGES
     const unsigned short *W = p.B[0];
@@ -521,21 +520,26 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         return;
     }
 
-    // Split-K: partials go to ws[split][m][n] with device-coherent 16-byte
-    // stores (sc1: written through to the device coherence point, since the
-    // XCDs' L2 caches are not coherent with each other), the stores are
-    // waited for, and one atomic per workgroup counts the split in.  The
-    // workgroup that sees the count reach splits-1 reads the partials with
-    // device-coherent loads (sc1), sums them in split order 0..splits-1
+    // Split-K.  Each workgroup stores its FP32 partial in accumulator order
+    // (workgroup block [4 waves][NJ][64 lanes] of 16-byte vectors, the blocks
+    // of one column tile's splits side by side), so every store and every
+    // load below moves one contiguous KiB per wave.  The stores are
+    // device-coherent (sc1: written through to the device coherence point,
+    // since the XCDs' L2 caches are not coherent with each other) and waited
+    // for, then one atomic per workgroup counts the split in.  The workgroup
+    // that sees the count reach splits-1 reads the partials back with
+    // device-coherent loads (sc1), adds them in split order 0..splits-1
     // (independent of arrival order), applies the epilogue, stores Y and
-    // resets the counter.  Both sides use device-scope coherent accesses, so
-    // no cache-wide writeback or invalidate is needed.
-    const int64_t ws_ld = (int64_t)N;
+    // resets the counter.  Both sides use device-scope coherent
+    // accesses, so no cache-wide writeback or invalidate is needed.
+    float *ws_tile = ws + (int64_t)tile_n * splits * (16 * BN);
+    const int lane_off = (wave * NJ) * 256 + lane * 4;
+    {
+        float *dst = ws_tile + split * (16 * BN) + lane_off;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
-        float *dst = ws + ((int64_t)split * 16 + m) * ws_ld + n;
-        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(acc[j]) : "memory");
+        for (int j = 0; j < NJ; ++j)
+            asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst + j * 256), "v"(acc[j])
+                         : "memory");
     }
     sa_wait_vmcnt<0>();
     // Every wave has waited for its own copies, so the stages are idle and
@@ -551,34 +555,32 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     if (!*s_last)
         return;
 
-    // thread -> row rm = tid / 16, columns n0 + CPT (tid % 16) .. +CPT-1;
-    // eight splits per round (one round for the usual split counts): 8 CPT/4
-    // loads in flight, then added in split order (indices past the last
-    // split repeat it and are not added)
-    constexpr int Q = CPT / 4; // 16-byte loads per split
-    const int rm = tid >> 4;
-    const int cn = n0 + (tid & 15) * CPT;
-    float sum[CPT];
+    // The partials are read back in rounds of RS splits (one round for the
+    // planner's split counts: 4 at BN = 128, 8 at BN = 256), all 8 loads of a
+    // round in flight together, then added in split order (indices past the
+    // last split repeat it and are not added).  The own split is read back
+    // too, so no branch sits between a load and its wait.
+    constexpr int RS = BN == 128 ? 4 : 8;
+    f32x4 sum[NJ];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-        sum[i] = 0.f;
-    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-        f32x4 v[8][Q];
+    for (int j = 0; j < NJ; ++j)
+        sum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
+        f32x4 v[RS][NJ];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sp = min(sp0 + u, splits - 1);
-            const float *src = ws + ((int64_t)sp * 16 + rm) * ws_ld + cn;
+        for (int u = 0; u < RS; ++u) {
+            const float *src = ws_tile + min(sp0 + u, splits - 1) * (16 * BN) + lane_off;
 #pragma unroll
-            for (int q = 0; q < Q; ++q)
+            for (int j = 0; j < NJ; ++j)
                 asm volatile("global_load_dwordx4 %0, %1, off sc1"
-                             : "=v"(v[u][q])
-                             : "v"(src + 4 * q)
+                             : "=v"(v[u][j])
+                             : "v"(src + j * 256)
                              : "memory");
         }
         // the loads above are invisible to the compiler's wait tracking: wait
-        // here and pass the values through so nothing reads them earlier
-        // (loads return in order)
-        if constexpr (Q == 4) {
+        // here and pass every value through, so nothing reads (or moves) one
+        // earlier (loads return in order)
+        if constexpr (RS * NJ == 32) {
             asm volatile("s_waitcnt vmcnt(16)"
                          : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
                            "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
@@ -594,43 +596,36 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                          :
                          : "memory");
         } else {
-            static_assert(Q == 2, "combine load count");
+            static_assert(RS * NJ == 8, "combine operand count");
             asm volatile("s_waitcnt vmcnt(0)"
                          : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]),
-                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]),
-                           "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[5][0]), "+v"(v[5][1]),
-                           "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[7][0]), "+v"(v[7][1])
+                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1])
                          :
                          : "memory");
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (sp0 + u < splits) {
+        for (int u = 0; u < RS; ++u)
+            if (sp0 + u < splits)
 #pragma unroll
-                for (int q = 0; q < Q; ++q)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sum[4 * q + r] += v[u][q][r];
-            }
-        }
+                for (int j = 0; j < NJ; ++j)
+                    sum[j] += v[u][j];
     }
-    if (rm < M) {
-        float v[CPT];
+    if (m < M) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            float x = sum[i];
-            if (p.bias != nullptr)
-                x += from_bits<DT>(p.bias[cn + i]);
-            v[i] = activate<ACT>(x);
-        }
-        if (p.R != nullptr)
-            add_residual<DT, CPT>(p.R, p.ldr, rm, cn, p.N, v);
-        unsigned short *cp = p.C[0] + (int64_t)rm * p.ldc + cn;
+        for (int j = 0; j < NJ; ++j) {
+            const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
+            float v[4];
 #pragma unroll
-        for (int q = 0; q < CPT / 8; ++q) {
-            u32x4 o = {pack2<DT>(v[8 * q + 0], v[8 * q + 1]), pack2<DT>(v[8 * q + 2], v[8 * q + 3]),
-                       pack2<DT>(v[8 * q + 4], v[8 * q + 5]), pack2<DT>(v[8 * q + 6], v[8 * q + 7])};
-            *reinterpret_cast<u32x4 *>(cp + 8 * q) = o;
+            for (int r = 0; r < 4; ++r) {
+                float x = sum[j][r];
+                if (p.bias != nullptr)
+                    x += from_bits<DT>(p.bias[n + r]);
+                v[r] = activate<ACT>(x);
+            }
+            if (p.R != nullptr)
+                add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, v);
+            u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+            *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
         }
     }
     if (tid == 0)
