@@ -572,7 +572,8 @@ def test_attention_random(tg, dt, causal, B, H, S, D):
     say("case attention", dt, B, H, S, D, "causal" if causal else "full")
     bits, lse, kern = run_attn(tg, p)
     say("  kernel", kern)
-    assert kern.startswith("attn_fwd" if D == 128 and S % 128 == 0 else "attn_generic")
+    assert kern.startswith("attn_fwd_256x64" if D == 128 and S % 256 == 0 else
+                           "attn_fwd_128x64" if D == 128 and S % 128 == 0 else "attn_generic")
     f64, _, lse_ref = oracle.attention(dt, p["Q"], p["K"], p["V"], causal=causal)
     util.check_tol(dt, bits, f64, "attention %s" % kern)
     assert np.max(np.abs(lse - lse_ref)) < 2e-3
@@ -595,6 +596,22 @@ def test_attention_rising_scores(tg, causal, S):
     f64, _, lse_ref = oracle.attention(BF16, p["Q"], p["K"], p["V"], causal=causal)
     util.check_tol(BF16, bits, f64, "attention rising scores")
     assert np.all(np.abs(lse - lse_ref) < 1e-3 + 1e-4 * np.abs(lse_ref))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_block_sizes_agree_bitwise(tg, monkeypatch, causal):
+    # every wave runs the same tiles in the same order whether its workgroup
+    # holds 128 or 256 queries (tiles above a wave's causal diagonal are exact
+    # no-ops, skipped or not), so the two kernels give the same bits
+    p = inputs.attention_problem(BF16, 2, 2, 768, 128, seed=187, causal=causal)
+    a, la, ka = run_attn(tg, p)
+    monkeypatch.setenv("TG_ATTN_BM", "128")
+    b, lb, kb = run_attn(tg, p)
+    assert ka.startswith("attn_fwd_256x64") and kb.startswith("attn_fwd_128x64"), (ka, kb)
+    util.check_exact(a, b, "attention 256 vs 128 queries per workgroup")
+    assert np.array_equal(la, lb)
+    f64, _, _ = oracle.attention(BF16, p["Q"], p["K"], p["V"], causal=causal)
+    util.check_tol(BF16, a, f64, "attention block sizes")
 
 
 def test_attention_uniform_integer_values(tg):

@@ -8,8 +8,14 @@
 // dimension 128, causal and non-causal).  Q, K, V, O: [B][H][S][128], f16 or
 // bf16; FP32 scores, softmax and accumulation; optional log-sum-exp per row.
 //
-// Mapping onto gfx950 (one workgroup = 128 queries of one head, 4 waves of
-// 32 queries; K and V stream through LDS in 64-key tiles):
+// Mapping onto gfx950 (one workgroup = 32 WAVES queries of one head, WAVES
+// waves of 32 queries; K and V stream through LDS in 64-key tiles):
+//  - Workgroup size.  Every K/V tile a workgroup copies into LDS serves all
+//    of its queries, so the bytes moved per flop halve from 128 queries (4
+//    waves, two workgroups per CU) to 256 (8 waves, one workgroup per CU);
+//    both keep two waves per SIMD.  The copies' energy is what holds the
+//    clock down under this load, so the larger block is the default when S
+//    is a multiple of 256.
 //  - S = Q K^T on v_mfma_f32_32x32x16 with K as src0 (its rows are keys) and
 //    Q as src1: lane l then holds query l % 32 and keys 8g + 4(l/32) + e of
 //    each 32-key block in register 4g + e.  Q's fragments (8 of 16 d) stay
@@ -33,9 +39,12 @@
 //    c of row r at c ^ {0, 6, 10, 12}[r % 4]).  The sum over k is order-free,
 //    so P never leaves the registers.
 //  - K and V tiles arrive by direct global->LDS copies one tile ahead (two
-//    stages, 64 KiB, so two workgroups share a CU); the epilogue divides by
-//    l, rounds, and restages each wave's 32 x 128 tile through LDS for
-//    whole-row stores (tg_pipeline.h).
+//    stages, 64 KiB: two 4-wave workgroups or one 8-wave workgroup per CU,
+//    two waves per SIMD either way); the epilogue divides by l, rounds, and
+//    restages each wave's 32 x 128 tile through LDS for whole-row stores
+//    (tg_pipeline.h).
+//  - Causal: a wave skips the work of key tiles wholly above its diagonal
+//    (they would add exp2(-inf) = 0 and raise no reference).
 #include "tg_device.h"
 #include "tg_launch.h"
 #include "tg_pipeline.h"
@@ -48,7 +57,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int AT_D = 128, AT_BM = 128, AT_BN = 64, AT_NT = 256;
+constexpr int AT_D = 128, AT_BN = 64;
 constexpr float AT_SLACK = 8.f;                  // log2 units a tile maximum may exceed the reference
 constexpr int AT_TILE = AT_BN * AT_D * 2;        // 16 KiB: one K or V tile
 constexpr int AT_STAGE = 2 * AT_TILE;            // K tile, then V tile
@@ -72,25 +81,29 @@ __device__ __forceinline__ float pair_sum(float v)
 
 } // namespace
 
-template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
+template <int DT, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs p)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * AT_STAGE];
+    static_assert(WAVES == 4 || WAVES == 8, "128 or 256 queries per workgroup");
+    constexpr int BM = 32 * WAVES; // queries per workgroup
+    constexpr int CPW = 16 / WAVES; // 1 KiB copies of K (and of V) per wave per tile
+    constexpr int STAGES = 2; // tile t+1 lands while tile t is used
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * AT_STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
-    const int nqb = p.S / AT_BM;
+    const int nqb = p.S / BM;
     // grid (heads, query blocks): workgroups are dispatched with x fastest,
     // so every head's block of a given length goes out together; causal
     // blocks are taken longest first so the short ones fill the tail
     const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.y : (int)blockIdx.y;
     const int64_t head = (int64_t)blockIdx.x * p.S * AT_D;
     const unsigned short *Qh = p.Q + head, *Kh = p.K + head, *Vh = p.V + head;
-    const int q0 = qb * AT_BM + wave * 32;   // this wave's first query
+    const int q0 = qb * BM + wave * 32;      // this wave's first query
     const int myq = q0 + (lane & 31);        // the query this lane's scores belong to
-    const int ntiles = CAUSAL ? ((qb + 1) * AT_BM) / AT_BN : p.S / AT_BN;
+    const int ntiles = CAUSAL ? ((qb + 1) * BM) / AT_BN : p.S / AT_BN;
 
     // ---- Q fragments: d 16 dc + 8 h .. + 7 of query myq (src1 operand)
     u32x4 qf[8];
@@ -101,11 +114,11 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
 
     // ---- copy plan: tile copy q (0..15) of K or V fills rows 4q .. 4q+3
     // (256 bytes each); lane -> (row 4q + lane/16, granule lane%16).  Wave w
-    // issues K copies 4w .. 4w+3 and V copies 4w .. 4w+3.
-    const unsigned short *gk[4], *gv[4];
+    // issues K copies CPW w .. CPW w + CPW-1 and the same V copies.
+    const unsigned short *gk[CPW], *gv[CPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * (wave * 4 + i) + (lane >> 4);
+    for (int i = 0; i < CPW; ++i) {
+        const int r = 4 * (wave * CPW + i) + (lane >> 4);
         gk[i] = Kh + (int64_t)r * AT_D + ((lane & 15) ^ swz_k(r)) * 8;
         gv[i] = Vh + (int64_t)r * AT_D + ((lane & 15) ^ swz_v(r)) * 8;
     }
@@ -114,14 +127,14 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
         const unsigned st = lds_base + stage * AT_STAGE;
         const int64_t off = (int64_t)t * AT_BN * AT_D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < CPW; ++i)
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gk[i] + off),
-                         "{m0}"(st + (wave * 4 + i) * 1024)
+                         "{m0}"(st + (wave * CPW + i) * 1024)
                          : "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < CPW; ++i)
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gv[i] + off),
-                         "{m0}"(st + AT_TILE + (wave * 4 + i) * 1024)
+                         "{m0}"(st + AT_TILE + (wave * CPW + i) * 1024)
                          : "memory");
     };
 
@@ -160,18 +173,10 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
     float m_run = -__builtin_inff(), l_run = 0.f;
     const float c2 = p.scale_log2;
 
-    issue(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
-        const unsigned char *st = lds + stage * AT_STAGE;
-        wait_vmcnt<0>();                      // this wave's copies of tile t
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // and its reads of tile t-1
-        stage_barrier();
-        if (t + 1 < ntiles)
-            issue(t + 1, stage ^ 1);          // stage ^ 1 held tile t-1: read by everybody
-
-        // S = Q K^T for 64 keys: two 32-key blocks
-        f32x16 s[2];
+    // ---- per-tile pieces: S = Q K^T of a 64-key tile (two 32-key blocks),
+    // the causal mask, the online softmax (which turns S into P in place),
+    // and O += P V.
+    auto qk = [&](f32x16 (&s)[2], const unsigned char *st) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
                 const u32x4 kf = *reinterpret_cast<const u32x4 *>(st + k_off[jb][dc]);
                 s[jb] = mfma32x32x16<DT>(kf, qf[dc], s[jb]);
             }
-
-        // causal mask on the tiles that reach past this wave's first query
-        const int k0 = t * AT_BN;
+    };
+    // causal mask on the tiles that reach past this wave's first query
+    auto mask = [&](f32x16 (&s)[2], int k0) {
         if (CAUSAL && k0 + AT_BN - 1 > q0) {
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
                         s[jb][r] = -__builtin_inff();
                 }
         }
-
-        // online softmax (log2 domain)
+    };
+    auto softmax = [&](f32x16 (&s)[2]) {
         float mx = -__builtin_inff();
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
@@ -229,8 +234,9 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
                 for (int r = 0; r < 16; ++r)
                     acc_o[0][db][r] *= alpha;
         }
-
-        // O += P V: four 16-key chunks, four 32-column d blocks
+    };
+    // O += P V: four 16-key chunks, four 32-column d blocks
+    auto pv = [&](const f32x16 (&s)[2], const unsigned char *st) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int jb = c >> 1, cc = c & 1;
@@ -252,6 +258,33 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_fwd_kernel(AttnArgs p)
                 acc_o[0][db] = mfma32x32x16<DT>(vf, pf, acc_o[0][db]);
             }
         }
+    };
+    // tile t lands in stage t % STAGES; before a tile's copies are issued
+    // into a stage, every wave has finished the tile that stage held
+    // (STAGES - 1 tiles earlier) and passed a barrier.
+    auto stage_ptr = [&](int t) { return lds + (t % STAGES) * AT_STAGE; };
+    auto sync_and_issue = [&](int t) {
+        wait_vmcnt<0>();                      // this wave's copies of tile t
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // and its outstanding LDS reads
+        stage_barrier();
+        if (t + 1 < ntiles)
+            issue(t + 1, (t + 1) % STAGES);
+    };
+    // causal: a tile wholly above this wave's diagonal adds exp2(-inf) = 0
+    // to every row and raises no reference, so the wave skips its work (the
+    // copies and barriers stay shared by the workgroup)
+    auto active = [&](int t) { return !CAUSAL || t * AT_BN <= q0 + 31; };
+
+    issue(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+        sync_and_issue(t);
+        if (!active(t))
+            continue;
+        f32x16 s[2];
+        qk(s, stage_ptr(t));
+        mask(s, t * AT_BN);
+        softmax(s);
+        pv(s, stage_ptr(t));
     }
 
     // ---- epilogue: O / l, log-sum-exp, restaged stores
@@ -313,24 +346,39 @@ __global__ __launch_bounds__(128) void attn_fwd_generic_kernel(AttnArgs p, int D
 bool attn_fast_eligible(const AttnArgs &a, int D)
 {
     auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
-    return D == AT_D && a.S % AT_BM == 0 && a.S > 0 && al16(a.Q) && al16(a.K) && al16(a.V) &&
+    return D == AT_D && a.S % 128 == 0 && a.S > 0 && al16(a.Q) && al16(a.K) && al16(a.V) &&
            al16(a.O);
 }
 
-hipError_t launch_attn(int dt, bool causal, const AttnArgs &a, hipStream_t s)
+int attn_block_m(const AttnArgs &a, int want)
 {
-    const dim3 grid(a.BH, a.S / AT_BM), block(AT_NT);
+    if (want == 128)
+        return 128;
+    return a.S % 256 == 0 ? 256 : 128;
+}
+
+hipError_t launch_attn(int dt, bool causal, int bm, const AttnArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.BH, a.S / bm), block(bm * 2);
+#define TG_AT(DT_, C_)                                                                           \
+    do {                                                                                         \
+        if (bm == 256)                                                                           \
+            hipLaunchKernelGGL((attn_fwd_kernel<DT_, C_, 8>), grid, block, 0, s, a);             \
+        else                                                                                     \
+            hipLaunchKernelGGL((attn_fwd_kernel<DT_, C_, 4>), grid, block, 0, s, a);             \
+    } while (0)
     if (dt == DT_F16) {
         if (causal)
-            hipLaunchKernelGGL((attn_fwd_kernel<DT_F16, true>), grid, block, 0, s, a);
+            TG_AT(DT_F16, true);
         else
-            hipLaunchKernelGGL((attn_fwd_kernel<DT_F16, false>), grid, block, 0, s, a);
+            TG_AT(DT_F16, false);
     } else {
         if (causal)
-            hipLaunchKernelGGL((attn_fwd_kernel<DT_BF16, true>), grid, block, 0, s, a);
+            TG_AT(DT_BF16, true);
         else
-            hipLaunchKernelGGL((attn_fwd_kernel<DT_BF16, false>), grid, block, 0, s, a);
+            TG_AT(DT_BF16, false);
     }
+#undef TG_AT
     return hipGetLastError();
 }
 

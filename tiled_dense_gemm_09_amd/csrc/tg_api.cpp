@@ -472,8 +472,10 @@ tg_status tg_attention_fwd(tg_dtype dt, int64_t batch, int64_t heads, int64_t se
     (void)hipGetLastError();
     hipError_t err;
     if (!force_generic && tg::attn_fast_eligible(a, (int)head_dim) && a.S / 128 < 65536) {
-        err = tg::launch_attn(kdt, causal != 0, a, s);
-        set_last(causal ? "attn_fwd_128x64_causal" : "attn_fwd_128x64");
+        const int bm = tg::attn_block_m(a, env_int("TG_ATTN_BM", 0)); // override for sweeps
+        err = tg::launch_attn(kdt, causal != 0, bm, a, s);
+        set_last(bm == 256 ? (causal ? "attn_fwd_256x64_causal" : "attn_fwd_256x64")
+                           : (causal ? "attn_fwd_128x64_causal" : "attn_fwd_128x64"));
     } else {
         err = tg::launch_attn_generic(kdt, causal != 0, a, (int)head_dim, s);
         set_last(force_generic ? "attn_generic (forced)" : "attn_generic (shape or alignment)");

@@ -89,7 +89,10 @@ struct AttnArgs {
 };
 // D = 128, S a multiple of 128, 16-byte aligned tensors
 bool attn_fast_eligible(const AttnArgs &a, int D);
-hipError_t launch_attn(int dt, bool causal, const AttnArgs &a, hipStream_t stream);
+// Queries per workgroup of the fast kernel: 256 when S is a multiple of 256
+// (unless want == 128), else 128.
+int attn_block_m(const AttnArgs &a, int want);
+hipError_t launch_attn(int dt, bool causal, int bm, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_generic(int dt, bool causal, const AttnArgs &a, int D, hipStream_t stream);
 
 // Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
