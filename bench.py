@@ -50,20 +50,33 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def time_launches(fn, steps, warmup):
-    """Mean ms per launch over `steps` launches after `warmup` untimed ones."""
+def time_launches(fn, steps, warmup, batches=1):
+    """Mean ms per launch over `steps` launches after `warmup` untimed ones.
+    With batches > 1 the timed loop also carries events at `batches` evenly
+    spaced boundaries, and the median of the per-batch means is returned
+    beside the mean."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        fn()
-    stop.record()
+    bounds = sorted(set(round(i * steps / batches) for i in range(batches + 1)))
+    events = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    events[0].record()
+    done = 0
+    for b, stop in zip(events[1:], bounds[1:]):
+        while done < stop:
+            fn()
+            done += 1
+        b.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    mean = events[0].elapsed_time(events[-1]) / steps
+    if batches == 1:
+        return mean
+    per = sorted(events[i].elapsed_time(events[i + 1]) / (bounds[i + 1] - bounds[i])
+                 for i in range(len(bounds) - 1))
+    mid = len(per) // 2
+    median = per[mid] if len(per) % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return mean, median
 
 
 def dev(bits, dt):
@@ -153,7 +166,7 @@ def main():
     if args.only in (None, "main"):
         log("main: f16 %dx%dx%d bias+gelu, warmup %d, steps %d" % (M, N, K, args.warmup,
                                                                     args.steps))
-        ms = time_launches(step, args.steps, args.warmup)
+        ms, ms_median = time_launches(step, args.steps, args.warmup, batches=10)
         kernel = tg.last_kernel()
         tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log("  %s: %.4f ms/launch, %.1f TFLOP/s" % (kernel, ms, tflops))
@@ -189,6 +202,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "ms_per_step_median_of_10_batches": round(ms_median, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
