@@ -354,15 +354,284 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0);
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles on the 16x16x32 MFMA (B stored [K,N]).
+//
+// The same copy pipeline as above (four 32 KiB stages, direct-to-LDS copies
+// of step k+4 issued three steps before they are read), with the product
+// taken on v_mfma_f32_16x16x32 instead of 32x32x16.  For the same flops the
+// smaller instruction moves half as many accumulator bytes through the
+// register file (4 FP32 per lane per 16K flop against 16 per 32K flop);
+// measured alone on random f16 operands it holds a 1.9 GHz clock where the
+// larger one sags to 1.5 GHz, and this kernel is power-bound.
+//
+// Wave w (2 x 2 waves of 128 x 128) keeps 8 x 8 accumulator blocks of
+// 16 x 16: lane l of block (i, j) holds row 16 i + l % 16 and columns
+// 16 j + 4 (l / 16) + {0..3} (B's fragment is src0, A's src1).
+//  - A fragment i: row 16 i + l % 16, k granule l / 16 (one 128-bit read;
+//    the A swizzle c ^ ((r >> 2) & 3) keeps the 16 rows a read pass covers
+//    on 16 distinct 16-byte bank groups).
+//  - B fragment j: two transposing reads, 16-lane group g at k-rows
+//    8 g + 4 h + (l % 16) / 4 (h = 0, 1), columns 16 j + 4 (l % 4); lane i
+//    of the group receives column 16 j + i at those k.  Groups g and g + 1
+//    read rows 8 apart at the same columns, so the B swizzle gains a term in
+//    bit 3 of the row: granule c of row r at c ^ {0,6,10,12}[r & 3] ^
+//    2 ((r >> 3) & 1), which puts 32 lanes' 8-byte reads on 16 distinct
+//    granules (all 64 banks).
+//  - Step k (32 deep): 32 MFMAs (columns j = 0..3); wait for this wave's
+//    copies of step k+1 and barrier; 32 MFMAs (j = 4..7) with the 24
+//    fragment reads of stage k+1 and the 8 copies of step k+4 into stage k,
+//    which every wave finished reading before the barrier.  The order within
+//    a half is left to the compiler: pinning every MFMA with a scheduling
+//    barrier made it rotate the 64 accumulator blocks through spare
+//    registers (about 500 register moves per four steps).
+namespace {
+
+constexpr int A16_BM = 256, A16_BN = 256;
+constexpr int A16_A_BYTES = A16_BM * AS_BK * 2;             // [256][32] K-contiguous
+constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-contiguous
+constexpr int A16_COPIES = 8;                               // 1 KiB copies per wave per step
+constexpr int A16_READS = 8 + 16;                           // A reads + B transposing reads
+
+__host__ __device__ constexpr int swz_b16(int r) { return swz_b(r) ^ (2 * ((r >> 3) & 1)); }
+
+} // namespace
+
+template <int DT, int ACT, bool HR>
+__device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][8], unsigned char *ep,
+                                                    int lane, unsigned short *C, int64_t ldc,
+                                                    const unsigned short *R, int64_t ldr)
+{
+    // the rounded 128 x 128 wave tile goes to the wave's own 32 KiB of LDS
+    // (256-byte rows, granule c of row r at c ^ (r % 16)), then each store
+    // writes 16 bytes per lane, 4 whole 256-byte row segments per wave
+    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 16 * i + (lane & 15);
+        u32x2 rr[8];
+        if constexpr (HR) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                rr[j] = *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = activate<ACT>(acc[i][j][e]);
+                if constexpr (HR)
+                    v[e] += from_bits<DT>((unsigned short)(rr[j][e >> 1] >> (16 * (e & 1))));
+            }
+            const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+            const int c = (2 * j + (q >> 1)) ^ (r & 15);
+            *reinterpret_cast<u32x2 *>(ep + r * 256 + c * 16 + (q & 1) * 8) = o;
+        }
+    }
+    unsigned short *crow = C + (lane & 15) * 8;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int r = 4 * t + q;
+        const u32x4 v =
+            *reinterpret_cast<const u32x4 *>(ep + r * 256 + (((lane & 15) ^ (r & 15)) * 16));
+        *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
+    }
+}
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
+                                                                int tiles_n, int group_m)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[A16_STAGE];
+    auto stage = [&](auto sidx) -> unsigned char * {
+        constexpr int S = decltype(sidx)::value;
+        if constexpr (S == 0)
+            return st0;
+        else if constexpr (S == 1)
+            return st1;
+        else if constexpr (S == 2)
+            return st2;
+        else
+            return st3;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave >> 1, wave_n = wave & 1;
+
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int m0 = tc.tm * A16_BM, n0 = tc.tn * A16_BN;
+    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    const int KT = p.K / AS_BK;
+
+    // copy c < 4: A copy q = 4 w + c, rows 16 q .. 16 q + 15 (lane -> row
+    // 16 q + lane / 4, granule lane % 4); c >= 4: B copy q = 4 w + c - 4, rows
+    // 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
+    const unsigned short *ga[4], *gb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int q = wave * 4 + c;
+        const int ra = 16 * q + (lane >> 2);
+        ga[c] = p.A + (int64_t)(m0 + ra) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
+        const int rb = 2 * q + (lane >> 5);
+        gb[c] = Bm + (int64_t)rb * p.ldb + n0 + ((lane & 31) ^ swz_b16(rb)) * 8;
+    }
+    const int64_t b_step = (int64_t)AS_BK * p.ldb;
+    auto copy = [&](int kt, unsigned char *st, int c) {
+        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
+        if (c < 4) {
+            const unsigned dst = lds + (wave * 4 + c) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[c] + kt * AS_BK), "{m0}"(dst)
+                         : "memory");
+        } else {
+            const unsigned dst = lds + A16_A_BYTES + (wave * 4 + c - 4) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - 4] + kt * b_step),
+                         "{m0}"(dst)
+                         : "memory");
+        }
+    };
+    auto issue = [&](int kt, unsigned char *st) {
+#pragma unroll
+        for (int c = 0; c < A16_COPIES; ++c)
+            copy(kt, st, c);
+    };
+
+    // accumulators start at bias[n] (or 0)
+    f32x4 acc[8][8];
+    const int q16 = lane >> 4;
+    if (p.bias != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const u32x2 braw = *reinterpret_cast<const u32x2 *>(p.bias + n0 + wave_n * 128 +
+                                                                 16 * j + 4 * q16);
+            f32x4 b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                b[e] = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i][j] = b;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // fragment offsets within a stage
+    int a_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = wave_m * 128 + 16 * i + (lane & 15);
+        a_off[i] = r * 64 + ((q16 ^ swz_a(r)) * 16);
+    }
+    int b_off[8][2];
+    {
+        const int jj = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 8 * q16 + 4 * h + (jj >> 2);
+                const int col = wave_n * 128 + 16 * j + 4 * (jj & 3);
+                b_off[j][h] =
+                    A16_A_BYTES + r * (2 * A16_BN) + (((col >> 3) ^ swz_b16(r)) * 16) + (col & 7) * 2;
+            }
+    }
+
+    struct Frag {
+        u32x4 a[8], b[8];
+    };
+    // read piece q: q < 8 is A fragment q, then B fragment (q - 8) / 2, half (q - 8) % 2
+    auto read_piece = [&](Frag &f, const unsigned char *st, int q) {
+        if (q < 8) {
+            f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q]);
+        } else {
+            const int j = (q - 8) >> 1, h = (q - 8) & 1;
+            const s16x4 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][h]));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            f.b[j][2 * h] = w[0];
+            f.b[j][2 * h + 1] = w[1];
+        }
+    };
+
+    Frag f0, f1;
+    auto step = [&](int kt, auto sidx, Frag &fc, Frag &fn) {
+        constexpr int S = decltype(sidx)::value;
+        unsigned char *cur = stage(sidx);
+        unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+        }
+        // copies of steps k+2 and k+3 may stay in flight; past the last step
+        // the copies repeat the last tile into stages nobody reads, so the
+        // count always holds
+        wait_vmcnt<2 * A16_COPIES>();
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        stage_barrier();
+        const int kc = min(kt + 4, KT - 1);
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int i = q >> 2, j = 4 + (q & 3);
+            acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+            if ((q & 3) == 3)
+                copy(kc, cur, q >> 2);
+            else
+                read_piece(fn, nxt, q - ((q + 1) >> 2));
+        }
+    };
+    issue(0, st0);
+    issue(min(1, KT - 1), st1);
+    issue(min(2, KT - 1), st2);
+    issue(min(3, KT - 1), st3);
+    wait_vmcnt<3 * A16_COPIES>();
+    stage_barrier();
+#pragma unroll
+    for (int q = 0; q < A16_READS; ++q)
+        read_piece(f0, st0, q);
+    for (int kt = 0; kt < KT; kt += 4) {
+        step(kt, std::integral_constant<int, 0>{}, f0, f1);
+        step(kt + 1, std::integral_constant<int, 1>{}, f1, f0);
+        step(kt + 2, std::integral_constant<int, 2>{}, f0, f1);
+        step(kt + 3, std::integral_constant<int, 3>{}, f1, f0);
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
+
+    unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * 128;
+    unsigned short *cw = Cm + cm * p.ldc + cn;
+    if (p.R != nullptr)
+        restaged_epilogue16<DT, ACT, true>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn, p.ldr);
+    else
+        restaged_epilogue16<DT, ACT, false>(acc, ep, lane, cw, p.ldc, nullptr, 0);
+}
+
 namespace {
 struct AsyncConfig {
     int ti, tj;
+    bool mfma16; // 256 x 256 on the 16x16x32 MFMA (B stored [K,N] only)
     const char *name;
 };
+// in order of preference: the first eligible configuration with a full wave
+// of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
-    {4, 4, "async_256x256x32_s4"},
-    {2, 2, "async_128x128x32_s4"},
-    {1, 2, "async_64x128x32_s4"},
+    {4, 4, true, "async_256x256x32_s4_mfma16"},
+    {4, 4, false, "async_256x256x32_s4"},
+    {2, 2, false, "async_128x128x32_s4"},
+    {1, 2, false, "async_64x128x32_s4"},
 };
 } // namespace
 
@@ -375,7 +644,8 @@ bool async_eligible(const GemmArgs &a, int cfg)
 {
     return a.M % async_tile_m(cfg) == 0 && a.N % async_tile_n(cfg) == 0 &&
            a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
-           ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
+           ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0 &&
+           !(kAsyncConfigs[cfg].mfma16 && a.b_trans);
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
@@ -383,6 +653,24 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
 {
     const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
     dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
+    if (kAsyncConfigs[cfg].mfma16) {
+#define TG_A16(DT_, ACT_)                                                                        \
+    hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_>), grid, block, 0, s, a, tiles_m, tiles_n, \
+                       group_m)
+        if (dt == DT_F16) {
+            if (act == ACT_GELU)
+                TG_A16(DT_F16, ACT_GELU);
+            else
+                TG_A16(DT_F16, ACT_NONE);
+        } else {
+            if (act == ACT_GELU)
+                TG_A16(DT_BF16, ACT_GELU);
+            else
+                TG_A16(DT_BF16, ACT_NONE);
+        }
+#undef TG_A16
+        return hipGetLastError();
+    }
 #define TG_AS(DT_, ACT_, TI_, TJ_)                                                               \
     do {                                                                                         \
         if (a.b_trans)                                                                           \
@@ -394,9 +682,10 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     } while (0)
 #define TG_AS_CFG(DT_, ACT_)                                                                     \
     do {                                                                                         \
-        if (cfg == 0)                                                                            \
+        const AsyncConfig &c_ = kAsyncConfigs[cfg];                                              \
+        if (c_.ti == 4)                                                                          \
             TG_AS(DT_, ACT_, 4, 4);                                                              \
-        else if (cfg == 1)                                                                       \
+        else if (c_.ti == 2)                                                                     \
             TG_AS(DT_, ACT_, 2, 2);                                                              \
         else                                                                                     \
             TG_AS(DT_, ACT_, 1, 2);                                                              \
