@@ -347,8 +347,8 @@ def test_k_zero_gives_activated_bias(tg):
 
 # ------------------------------------------------- async tile configurations
 
-ASYNC_CONFIGS = ["async_256x256x32_s4_mfma16", "async_256x256x32_s4", "async_128x128x32_s4",
-                 "async_64x128x32_s4"]
+ASYNC_CONFIGS = ["async_256x256x32_s4_mfma16_w8", "async_256x256x32_s4_mfma16",
+                 "async_256x256x32_s4", "async_128x128x32_s4", "async_64x128x32_s4"]
 
 
 @pytest.mark.parametrize("cfg", ASYNC_CONFIGS)
@@ -415,6 +415,7 @@ EX_SHAPES = [
     # (dt, M, N, K, force): every kernel family with a residual
     (F16, 512, 768, 384, "async_256x256x32_s4"),
     (BF16, 768, 512, 256, "async_256x256x32_s4_mfma16"),  # B [K,N] only; [N,K] falls back
+    (F16, 512, 512, 512, "async_256x256x32_s4_mfma16_w8"),
     (BF16, 256, 384, 256, "async_128x128x32_s4"),
     (F16, 192, 256, 512, "async_64x128x32_s4"),
     (BF16, 300, 170, 200, None),          # ragged: tiled kernel (B [K,N]) / generic (B [N,K])
@@ -434,7 +435,7 @@ def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, f
     say("case ex integer", dt, M, N, K, force, "B[N,K]" if trans_b else "B[K,N]")
     bits, kern = run_ex(tg, p, trans_b, R)
     say("  kernel", kern)
-    if force and force.startswith("async") and not (trans_b and force.endswith("mfma16")):
+    if force and force.startswith("async") and not (trans_b and "mfma16" in force):
         assert kern == force
     if trans_b and not (force or "").startswith("async"):
         assert kern.startswith("generic")
@@ -444,7 +445,7 @@ def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, f
 
 
 @pytest.mark.parametrize("trans_b", [False, True])
-@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES[:6])
+@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES[:7])
 def test_residual_and_transposed_b_gelu_random(tg, monkeypatch, dt, M, N, K, force, trans_b):
     if force:
         monkeypatch.setenv("TG_FORCE_CONFIG", force)

@@ -363,10 +363,17 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 // smaller instruction moves half as many accumulator bytes through the
 // register file (4 FP32 per lane per 16K flop against 16 per 32K flop);
 // measured alone on random f16 operands it holds a 1.9 GHz clock where the
-// larger one sags to 1.5 GHz, and this kernel is power-bound.
+// larger one sags to 1.5 GHz, and this kernel is power-bound.  The tile is
+// split over WN = 2 waves along N (4 waves of 128 x 128, one per SIMD, the
+// default) or WN = 4 (8 waves of 128 x 64, two per SIMD).  One wave per SIMD
+// issues this MFMA at only about 55 % of the matrix core's rate and two
+// waves reach 85 % in a loop of MFMAs alone, but in the GEMM the 8-wave
+// split reads a third more fragments from LDS and the power limit takes the
+// difference back: it measures level with the 4-wave kernel (f16 4096^3
+// within 1 %, QKV +0.5 %, bf16 8192^3 -1 %).
 //
-// Wave w (2 x 2 waves of 128 x 128) keeps 8 x 8 accumulator blocks of
-// 16 x 16: lane l of block (i, j) holds row 16 i + l % 16 and columns
+// Wave (wm, wn) keeps 8 x NJ accumulator blocks of 16 x 16 (NJ = 16 / WN):
+// lane l of block (i, j) holds row 16 i + l % 16 and columns
 // 16 j + 4 (l / 16) + {0..3} (B's fragment is src0, A's src1).
 //  - A fragment i: row 16 i + l % 16, k granule l / 16 (one 128-bit read;
 //    the A swizzle c ^ ((r >> 2) & 3) keeps the 16 rows a read pass covers
@@ -376,47 +383,67 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 //    of the group receives column 16 j + i at those k.  Groups g and g + 1
 //    read rows 8 apart at the same columns, so the B swizzle gains a term in
 //    bit 3 of the row: granule c of row r at c ^ {0,6,10,12}[r & 3] ^
-//    2 ((r >> 3) & 1), which puts 32 lanes' 8-byte reads on 16 distinct
-//    granules (all 64 banks).
-//  - Step k (32 deep): 32 MFMAs (columns j = 0..3); wait for this wave's
-//    copies of step k+1 and barrier; 32 MFMAs (j = 4..7) with the 24
-//    fragment reads of stage k+1 and the 8 copies of step k+4 into stage k,
+//    2 ((r >> 3) & 1) (without it the bank-conflict counter doubles).
+//  - Step k (32 deep): the MFMAs of columns j < NJ / 2; wait for this wave's
+//    copies of step k+1 and barrier; the MFMAs of j >= NJ / 2 with the
+//    fragment reads of stage k+1 and the copies of step k+4 into stage k,
 //    which every wave finished reading before the barrier.  The order within
 //    a half is left to the compiler: pinning every MFMA with a scheduling
-//    barrier made it rotate the 64 accumulator blocks through spare
-//    registers (about 500 register moves per four steps).
+//    barrier made it rotate the accumulator blocks through spare registers
+//    (about 500 register moves per four steps at WN = 2).
 namespace {
 
 constexpr int A16_BM = 256, A16_BN = 256;
 constexpr int A16_A_BYTES = A16_BM * AS_BK * 2;             // [256][32] K-contiguous
 constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-contiguous
-constexpr int A16_COPIES = 8;                               // 1 KiB copies per wave per step
-constexpr int A16_READS = 8 + 16;                           // A reads + B transposing reads
 
 __host__ __device__ constexpr int swz_b16(int r) { return swz_b(r) ^ (2 * ((r >> 3) & 1)); }
 
+template <int WN>
+struct A16Geom {
+    static_assert(WN == 2 || WN == 4, "waves along N");
+    static constexpr int NW = 2 * WN;               // waves
+    static constexpr int NT = 64 * NW;              // lanes
+    static constexpr int NJ = 16 / WN;              // 16-column blocks per wave
+    static constexpr int WCOLS = 16 * NJ;           // columns per wave
+    static constexpr int CA = 16 / NW;              // A copies per wave per step (16 in all)
+    static constexpr int COPIES = 2 * CA;           // + as many B copies
+    static constexpr int READS = 8 + 2 * NJ;        // A reads + B transposing reads
+    static constexpr int G = 2 * NJ;                // epilogue granules per wave-tile row
+    static constexpr int EP_BYTES = 128 * 16 * G;   // wave tile restaged in LDS
+};
+
+// epilogue row swizzle: 16 rows of a read pass on 16 distinct bank groups
+// (256-byte rows: r % 16; 128-byte rows: rows r, r + 1 share a bank sweep)
+template <int G>
+__device__ __forceinline__ int ep_swz(int r)
+{
+    return G == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
 } // namespace
 
-template <int DT, int ACT, bool HR>
-__device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][8], unsigned char *ep,
+template <int DT, int ACT, bool HR, int NJ>
+__device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], unsigned char *ep,
                                                     int lane, unsigned short *C, int64_t ldc,
                                                     const unsigned short *R, int64_t ldr)
 {
-    // the rounded 128 x 128 wave tile goes to the wave's own 32 KiB of LDS
-    // (256-byte rows, granule c of row r at c ^ (r % 16)), then each store
-    // writes 16 bytes per lane, 4 whole 256-byte row segments per wave
+    // the rounded 128 x (16 NJ) wave tile goes to the wave's own LDS region
+    // (rows of G = 2 NJ granules, granule c of row r at c ^ ep_swz(r)), then
+    // each store writes 16 bytes per lane, whole row segments
+    constexpr int G = 2 * NJ;
     const int q = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 16 * i + (lane & 15);
-        u32x2 rr[8];
+        u32x2 rr[NJ];
         if constexpr (HR) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < NJ; ++j)
                 rr[j] = *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -425,24 +452,27 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][8], un
                     v[e] += from_bits<DT>((unsigned short)(rr[j][e >> 1] >> (16 * (e & 1))));
             }
             const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-            const int c = (2 * j + (q >> 1)) ^ (r & 15);
-            *reinterpret_cast<u32x2 *>(ep + r * 256 + c * 16 + (q & 1) * 8) = o;
+            const int c = (2 * j + (q >> 1)) ^ ep_swz<G>(r);
+            *reinterpret_cast<u32x2 *>(ep + r * (16 * G) + c * 16 + (q & 1) * 8) = o;
         }
     }
-    unsigned short *crow = C + (lane & 15) * 8;
+    // lane -> granule lane % G of rows (64 / G) t + lane / G
+    unsigned short *crow = C + (lane % G) * 8;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-        const int r = 4 * t + q;
-        const u32x4 v =
-            *reinterpret_cast<const u32x4 *>(ep + r * 256 + (((lane & 15) ^ (r & 15)) * 16));
+    for (int t = 0; t < 2 * G; ++t) {
+        const int r = (64 / G) * t + lane / G;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) +
+                                                         (((lane % G) ^ ep_swz<G>(r)) * 16));
         *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
     }
 }
 
-template <int DT, int ACT>
-__global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
-                                                                int tiles_n, int group_m)
+template <int DT, int ACT, int WN>
+__global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
+                                                                         int tiles_n, int group_m)
 {
+    using Gm = A16Geom<WN>;
+    constexpr int NJ = Gm::NJ, CA = Gm::CA;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
@@ -462,7 +492,7 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_m = wave >> 1, wave_n = wave & 1;
+    const int wave_m = wave / WN, wave_n = wave % WN;
 
     const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
     const int m0 = tc.tm * A16_BM, n0 = tc.tn * A16_BN;
@@ -470,13 +500,13 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
     const int KT = p.K / AS_BK;
 
-    // copy c < 4: A copy q = 4 w + c, rows 16 q .. 16 q + 15 (lane -> row
-    // 16 q + lane / 4, granule lane % 4); c >= 4: B copy q = 4 w + c - 4, rows
-    // 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
-    const unsigned short *ga[4], *gb[4];
+    // copy c < CA: A copy q = CA w + c, rows 16 q .. 16 q + 15 (lane -> row
+    // 16 q + lane / 4, granule lane % 4); c >= CA: B copy q = CA w + c - CA,
+    // rows 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
+    const unsigned short *ga[CA], *gb[CA];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int q = wave * 4 + c;
+    for (int c = 0; c < CA; ++c) {
+        const int q = wave * CA + c;
         const int ra = 16 * q + (lane >> 2);
         ga[c] = p.A + (int64_t)(m0 + ra) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
         const int rb = 2 * q + (lane >> 5);
@@ -485,30 +515,30 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
     const int64_t b_step = (int64_t)AS_BK * p.ldb;
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
-        if (c < 4) {
-            const unsigned dst = lds + (wave * 4 + c) * 1024;
+        if (c < CA) {
+            const unsigned dst = lds + (wave * CA + c) * 1024;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[c] + kt * AS_BK), "{m0}"(dst)
                          : "memory");
         } else {
-            const unsigned dst = lds + A16_A_BYTES + (wave * 4 + c - 4) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - 4] + kt * b_step),
+            const unsigned dst = lds + A16_A_BYTES + (wave * CA + c - CA) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - CA] + kt * b_step),
                          "{m0}"(dst)
                          : "memory");
         }
     };
     auto issue = [&](int kt, unsigned char *st) {
 #pragma unroll
-        for (int c = 0; c < A16_COPIES; ++c)
+        for (int c = 0; c < Gm::COPIES; ++c)
             copy(kt, st, c);
     };
 
     // accumulators start at bias[n] (or 0)
-    f32x4 acc[8][8];
+    f32x4 acc[8][NJ];
     const int q16 = lane >> 4;
     if (p.bias != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const u32x2 braw = *reinterpret_cast<const u32x2 *>(p.bias + n0 + wave_n * 128 +
+        for (int j = 0; j < NJ; ++j) {
+            const u32x2 braw = *reinterpret_cast<const u32x2 *>(p.bias + n0 + wave_n * Gm::WCOLS +
                                                                  16 * j + 4 * q16);
             f32x4 b;
 #pragma unroll
@@ -522,7 +552,7 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
@@ -533,22 +563,22 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
         const int r = wave_m * 128 + 16 * i + (lane & 15);
         a_off[i] = r * 64 + ((q16 ^ swz_a(r)) * 16);
     }
-    int b_off[8][2];
+    int b_off[NJ][2];
     {
         const int jj = lane & 15;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int r = 8 * q16 + 4 * h + (jj >> 2);
-                const int col = wave_n * 128 + 16 * j + 4 * (jj & 3);
-                b_off[j][h] =
-                    A16_A_BYTES + r * (2 * A16_BN) + (((col >> 3) ^ swz_b16(r)) * 16) + (col & 7) * 2;
+                const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
+                b_off[j][h] = A16_A_BYTES + r * (2 * A16_BN) + (((col >> 3) ^ swz_b16(r)) * 16) +
+                              (col & 7) * 2;
             }
     }
 
     struct Frag {
-        u32x4 a[8], b[8];
+        u32x4 a[8], b[NJ];
     };
     // read piece q: q < 8 is A fragment q, then B fragment (q - 8) / 2, half (q - 8) % 2
     auto read_piece = [&](Frag &f, const unsigned char *st, int q) {
@@ -564,41 +594,50 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
         }
     };
 
+    constexpr int MH = 8 * NJ / 2; // MFMAs per half step
+    constexpr int OPS = Gm::READS + Gm::COPIES;
     Frag f0, f1;
     auto step = [&](int kt, auto sidx, Frag &fc, Frag &fn) {
         constexpr int S = decltype(sidx)::value;
         unsigned char *cur = stage(sidx);
         unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int i = q >> 2, j = q & 3;
+        for (int q = 0; q < MH; ++q) {
+            const int i = q % 8, j = q / 8;
             acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
         }
         // copies of steps k+2 and k+3 may stay in flight; past the last step
         // the copies repeat the last tile into stages nobody reads, so the
         // count always holds
-        wait_vmcnt<2 * A16_COPIES>();
+        wait_vmcnt<2 * Gm::COPIES>();
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         stage_barrier();
         const int kc = min(kt + 4, KT - 1);
+        // second half: MFMAs, the next stage's reads and this step's copies
+        // (one copy after every READS / COPIES reads)
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int i = q >> 2, j = 4 + (q & 3);
-            acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
-            if ((q & 3) == 3)
-                copy(kc, cur, q >> 2);
-            else
-                read_piece(fn, nxt, q - ((q + 1) >> 2));
+        for (int q = 0; q < (MH > OPS ? MH : OPS); ++q) {
+            if (q < MH) {
+                const int i = q % 8, j = NJ / 2 + q / 8;
+                acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+            }
+            if (q < OPS) {
+                constexpr int PER = OPS / Gm::COPIES; // ops per copy slot
+                if (q % PER == PER - 1)
+                    copy(kc, cur, q / PER);
+                else
+                    read_piece(fn, nxt, q - q / PER);
+            }
         }
     };
     issue(0, st0);
     issue(min(1, KT - 1), st1);
     issue(min(2, KT - 1), st2);
     issue(min(3, KT - 1), st3);
-    wait_vmcnt<3 * A16_COPIES>();
+    wait_vmcnt<3 * Gm::COPIES>();
     stage_barrier();
 #pragma unroll
-    for (int q = 0; q < A16_READS; ++q)
+    for (int q = 0; q < Gm::READS; ++q)
         read_piece(f0, st0, q);
     for (int kt = 0; kt < KT; kt += 4) {
         step(kt, std::integral_constant<int, 0>{}, f0, f1);
@@ -610,28 +649,34 @@ __global__ __launch_bounds__(AS_NT, 1) void gemm_async16_kernel(GemmArgs p, int 
     __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
 
-    unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * 128;
+    // each wave restages its tile in its own EP_BYTES of the (now idle) stages
+    constexpr int PER_STAGE = A16_STAGE / Gm::EP_BYTES; // wave tiles per stage
+    const int es = wave / PER_STAGE;
+    unsigned char *ep = (es == 0 ? st0 : es == 1 ? st1 : es == 2 ? st2 : st3) +
+                        (wave % PER_STAGE) * Gm::EP_BYTES;
+    const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * Gm::WCOLS;
     unsigned short *cw = Cm + cm * p.ldc + cn;
     if (p.R != nullptr)
-        restaged_epilogue16<DT, ACT, true>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn, p.ldr);
+        restaged_epilogue16<DT, ACT, true, NJ>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
+                                               p.ldr);
     else
-        restaged_epilogue16<DT, ACT, false>(acc, ep, lane, cw, p.ldc, nullptr, 0);
+        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0);
 }
 
 namespace {
 struct AsyncConfig {
     int ti, tj;
-    bool mfma16; // 256 x 256 on the 16x16x32 MFMA (B stored [K,N] only)
+    int mfma16; // 256 x 256 on the 16x16x32 MFMA with this many waves (B stored [K,N] only); 0: 32x32x16
     const char *name;
 };
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
-    {4, 4, true, "async_256x256x32_s4_mfma16"},
-    {4, 4, false, "async_256x256x32_s4"},
-    {2, 2, false, "async_128x128x32_s4"},
-    {1, 2, false, "async_64x128x32_s4"},
+    {4, 4, 4, "async_256x256x32_s4_mfma16"},
+    {4, 4, 8, "async_256x256x32_s4_mfma16_w8"}, // forced only: never ahead of the 4-wave kernel
+    {4, 4, 0, "async_256x256x32_s4"},
+    {2, 2, 0, "async_128x128x32_s4"},
+    {1, 2, 0, "async_64x128x32_s4"},
 };
 } // namespace
 
@@ -654,9 +699,16 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
     dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
     if (kAsyncConfigs[cfg].mfma16) {
+        const int wn = kAsyncConfigs[cfg].mfma16 / 2;
 #define TG_A16(DT_, ACT_)                                                                        \
-    hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_>), grid, block, 0, s, a, tiles_m, tiles_n, \
-                       group_m)
+    do {                                                                                         \
+        if (wn == 4)                                                                             \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4>), grid,                        \
+                               dim3(A16Geom<4>::NT), 0, s, a, tiles_m, tiles_n, group_m);        \
+        else                                                                                     \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2>), grid,                        \
+                               dim3(A16Geom<2>::NT), 0, s, a, tiles_m, tiles_n, group_m);        \
+    } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)
                 TG_A16(DT_F16, ACT_GELU);
