@@ -414,7 +414,7 @@ def run_ex(tg, p, trans_b, R=None, Rin_place=False):
 EX_SHAPES = [
     # (dt, M, N, K, force): every kernel family with a residual
     (F16, 512, 768, 384, "async_256x256x32_s4"),
-    (BF16, 768, 512, 256, "async_256x256x32_s4_mfma16"),  # B [K,N] only; [N,K] falls back
+    (BF16, 768, 512, 256, "async_256x256x32_s4_mfma16"),
     (F16, 512, 512, 512, "async_256x256x32_s4_mfma16_w8"),
     (BF16, 256, 384, 256, "async_128x128x32_s4"),
     (F16, 192, 256, 512, "async_64x128x32_s4"),
@@ -435,7 +435,7 @@ def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, f
     say("case ex integer", dt, M, N, K, force, "B[N,K]" if trans_b else "B[K,N]")
     bits, kern = run_ex(tg, p, trans_b, R)
     say("  kernel", kern)
-    if force and force.startswith("async") and not (trans_b and "mfma16" in force):
+    if force and force.startswith("async"):
         assert kern == force
     if trans_b and not (force or "").startswith("async"):
         assert kern.startswith("generic")
@@ -479,7 +479,7 @@ def test_transposed_b_full_size_sampled(tg):
     R = inputs.draw(np.random.default_rng(99), (p["M"], p["N"]), "uniform", F16)
     say("case 4096 B[N,K] + residual")
     bits, kern = run_ex(tg, p, True, R)
-    assert kern == "async_256x256x32_s4"
+    assert kern == "async_256x256x32_s4_mfma16"
     ii, jj = util.sample_indices(p["M"], p["N"], 2000, seed=12)
     f64, rbits = oracle.gemm_ex_sample(F16, p["A"], np.ascontiguousarray(p["B"].T), ii, jj,
                                        trans_b=True, bias=p["bias"], act=oracle.ACT_GELU_TANH,

@@ -355,7 +355,8 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles on the 16x16x32 MFMA (B stored [K,N]).
+// 256 x 256 tiles on the 16x16x32 MFMA (B stored [K,N], or [N,K] staged
+// like A).
 //
 // The same copy pipeline as above (four 32 KiB stages, direct-to-LDS copies
 // of step k+4 issued three steps before they are read), with the product
@@ -399,7 +400,7 @@ constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-con
 
 __host__ __device__ constexpr int swz_b16(int r) { return swz_b(r) ^ (2 * ((r >> 3) & 1)); }
 
-template <int WN>
+template <int WN, bool BT>
 struct A16Geom {
     static_assert(WN == 2 || WN == 4, "waves along N");
     static constexpr int NW = 2 * WN;               // waves
@@ -408,7 +409,7 @@ struct A16Geom {
     static constexpr int WCOLS = 16 * NJ;           // columns per wave
     static constexpr int CA = 16 / NW;              // A copies per wave per step (16 in all)
     static constexpr int COPIES = 2 * CA;           // + as many B copies
-    static constexpr int READS = 8 + 2 * NJ;        // A reads + B transposing reads
+    static constexpr int READS = 8 + (BT ? NJ : 2 * NJ); // A reads + B reads (2 transposing each)
     static constexpr int G = 2 * NJ;                // epilogue granules per wave-tile row
     static constexpr int EP_BYTES = 128 * 16 * G;   // wave tile restaged in LDS
 };
@@ -467,11 +468,13 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
     }
 }
 
-template <int DT, int ACT, int WN>
-__global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
-                                                                         int tiles_n, int group_m)
+template <int DT, int ACT, int WN, bool BT>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p,
+                                                                             int tiles_m,
+                                                                             int tiles_n,
+                                                                             int group_m)
 {
-    using Gm = A16Geom<WN>;
+    using Gm = A16Geom<WN, BT>;
     constexpr int NJ = Gm::NJ, CA = Gm::CA;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
@@ -503,16 +506,22 @@ __global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmAr
     // copy c < CA: A copy q = CA w + c, rows 16 q .. 16 q + 15 (lane -> row
     // 16 q + lane / 4, granule lane % 4); c >= CA: B copy q = CA w + c - CA,
     // rows 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
+    // B stored [N,K] (BT) is staged like A: [256 n][32 k] K-contiguous, B
+    // copy q filling n-rows 16 q .. 16 q + 15 with the A swizzle.
     const unsigned short *ga[CA], *gb[CA];
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
         const int q = wave * CA + c;
         const int ra = 16 * q + (lane >> 2);
         ga[c] = p.A + (int64_t)(m0 + ra) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
-        const int rb = 2 * q + (lane >> 5);
-        gb[c] = Bm + (int64_t)rb * p.ldb + n0 + ((lane & 31) ^ swz_b16(rb)) * 8;
+        if constexpr (BT) {
+            gb[c] = Bm + (int64_t)(n0 + ra) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8;
+        } else {
+            const int rb = 2 * q + (lane >> 5);
+            gb[c] = Bm + (int64_t)rb * p.ldb + n0 + ((lane & 31) ^ swz_b16(rb)) * 8;
+        }
     }
-    const int64_t b_step = (int64_t)AS_BK * p.ldb;
+    const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
         if (c < CA) {
@@ -563,6 +572,9 @@ __global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmAr
         const int r = wave_m * 128 + 16 * i + (lane & 15);
         a_off[i] = r * 64 + ((q16 ^ swz_a(r)) * 16);
     }
+    // B fragment j: transposing reads of [32 k][256 n] (two per fragment), or
+    // for BT one 128-bit read of n-row wave_n WCOLS + 16 j + l % 16, k
+    // granule l / 16 of [256 n][32 k] (b_off[j][0])
     int b_off[NJ][2];
     {
         const int jj = lane & 15;
@@ -570,20 +582,28 @@ __global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmAr
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int r = 8 * q16 + 4 * h + (jj >> 2);
-                const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
-                b_off[j][h] = A16_A_BYTES + r * (2 * A16_BN) + (((col >> 3) ^ swz_b16(r)) * 16) +
-                              (col & 7) * 2;
+                if constexpr (BT) {
+                    const int r = wave_n * Gm::WCOLS + 16 * j + jj;
+                    b_off[j][h] = A16_A_BYTES + r * 64 + ((q16 ^ swz_a(r)) * 16);
+                } else {
+                    const int r = 8 * q16 + 4 * h + (jj >> 2);
+                    const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
+                    b_off[j][h] = A16_A_BYTES + r * (2 * A16_BN) +
+                                  (((col >> 3) ^ swz_b16(r)) * 16) + (col & 7) * 2;
+                }
             }
     }
 
     struct Frag {
         u32x4 a[8], b[NJ];
     };
-    // read piece q: q < 8 is A fragment q, then B fragment (q - 8) / 2, half (q - 8) % 2
+    // read piece q: q < 8 is A fragment q, then B fragment (q - 8) / 2, half
+    // (q - 8) % 2 (BT: B fragment q - 8)
     auto read_piece = [&](Frag &f, const unsigned char *st, int q) {
         if (q < 8) {
             f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q]);
+        } else if constexpr (BT) {
+            f.b[q - 8] = *reinterpret_cast<const u32x4 *>(st + b_off[q - 8][0]);
         } else {
             const int j = (q - 8) >> 1, h = (q - 8) & 1;
             const s16x4 v =
@@ -666,7 +686,7 @@ __global__ __launch_bounds__(A16Geom<WN>::NT, 1) void gemm_async16_kernel(GemmAr
 namespace {
 struct AsyncConfig {
     int ti, tj;
-    int mfma16; // 256 x 256 on the 16x16x32 MFMA with this many waves (B stored [K,N] only); 0: 32x32x16
+    int mfma16; // 256 x 256 on the 16x16x32 MFMA with this many waves; 0: 32x32x16
     const char *name;
 };
 // in order of preference: the first eligible configuration with a full wave
@@ -689,8 +709,7 @@ bool async_eligible(const GemmArgs &a, int cfg)
 {
     return a.M % async_tile_m(cfg) == 0 && a.N % async_tile_n(cfg) == 0 &&
            a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
-           ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0 &&
-           !(kAsyncConfigs[cfg].mfma16 && a.b_trans);
+           ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
@@ -702,12 +721,18 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
 #define TG_A16(DT_, ACT_)                                                                        \
     do {                                                                                         \
-        if (wn == 4)                                                                             \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4>), grid,                        \
-                               dim3(A16Geom<4>::NT), 0, s, a, tiles_m, tiles_n, group_m);        \
+        if (wn == 4 && a.b_trans)                                                                \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, true>), grid, dim3(512), 0, s, \
+                               a, tiles_m, tiles_n, group_m);                                    \
+        else if (wn == 4)                                                                        \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, false>), grid, dim3(512), 0,   \
+                               s, a, tiles_m, tiles_n, group_m);                                 \
+        else if (a.b_trans)                                                                      \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true>), grid, dim3(256), 0, s, \
+                               a, tiles_m, tiles_n, group_m);                                    \
         else                                                                                     \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2>), grid,                        \
-                               dim3(A16Geom<2>::NT), 0, s, a, tiles_m, tiles_n, group_m);        \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false>), grid, dim3(256), 0,   \
+                               s, a, tiles_m, tiles_n, group_m);                                 \
     } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)
