@@ -469,10 +469,8 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
 }
 
 template <int DT, int ACT, int WN, bool BT>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p,
-                                                                             int tiles_m,
-                                                                             int tiles_n,
-                                                                             int group_m)
+__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
+                                                                    int tiles_n, int group_m)
 {
     using Gm = A16Geom<WN, BT>;
     constexpr int NJ = Gm::NJ, CA = Gm::CA;
@@ -616,6 +614,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p,
 
     constexpr int MH = 8 * NJ / 2; // MFMAs per half step
     constexpr int OPS = Gm::READS + Gm::COPIES;
+    static_assert(OPS % Gm::COPIES == 0, "copies evenly spread over the second half");
     Frag f0, f1;
     auto step = [&](int kt, auto sidx, Frag &fc, Frag &fn) {
         constexpr int S = decltype(sidx)::value;
@@ -718,6 +717,9 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
     dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
     if (kAsyncConfigs[cfg].mfma16) {
+        static_assert(A16Geom<4, false>::NT == 512 && A16Geom<2, false>::NT == 256 &&
+                          A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
+                      "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
 #define TG_A16(DT_, ACT_)                                                                        \
     do {                                                                                         \
