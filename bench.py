@@ -374,7 +374,24 @@ def run_secondary(args, torch, inputs, tg):
             "cache_resident_GB/s": round(nbytes / (ms_hot * 1e-3) / 1e9, 1),
             "kernel": tg.last_kernel()}
         log("  ", out["bf16_skinny_16x8192x8192"])
-        del X, Ws, Y
+        # the same path at its upper row count (M = 32: two 16-row blocks per
+        # W fragment), same rotated W, X ~ N(0, 1)
+        X32 = dev(inputs.draw(np.random.default_rng(55), (32, p["K"]), "normal", 2), 2)
+        Y32 = torch.empty((32, p["N"]), dtype=torch.bfloat16, device="cuda")
+
+        def sk32():
+            tg.gemm(X32, Ws[it[0] & 3], out=Y32)
+            it[0] += 1
+
+        ms = time_launches(sk32, steps, warm)
+        nbytes = 2 * (p["N"] * p["K"] + 32 * p["K"] + 32 * p["N"])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["bf16_skinny_32x8192x8192"] = {
+            "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "TFLOP/s": round(2.0 * 32 * p["N"] * p["K"] / (ms * 1e-3) / 1e12, 1),
+            "algorithmic_bytes": nbytes, "kernel": tg.last_kernel()}
+        log("  ", out["bf16_skinny_32x8192x8192"])
+        del X, Ws, Y, X32, Y32
 
     if args.only in (None, "vendor"):
         # context only: the ROCm BLAS library GEMM (torch.matmul) on the same

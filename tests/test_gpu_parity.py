@@ -186,6 +186,22 @@ def test_skinny_config_integer_exact_and_deterministic(tg):
     util.check_exact(bits2, bits, "skinny repeat")
 
 
+@pytest.mark.parametrize("integer", [False, True])
+def test_skinny_32_rows_full_size(tg, integer):
+    # the benchmark's M = 32 line: bf16 32 x 8192 x 8192, every output checked
+    p = inputs.problem(BF16, 32, 8192, 8192, seed=5400 + integer, kind="int" if integer else "normal",
+                       b_scale=1.0 if integer else 8192 ** -0.5)
+    say("case skinny 32x8192x8192", "integer" if integer else "")
+    bits, kern = run(tg, p)
+    say("  kernel", kern)
+    assert kern.startswith("skinny_stream") and kern.endswith("_m32")
+    f64, rbits = oracle.gemm(BF16, p["A"], p["B"])
+    if integer:
+        util.check_exact(bits, rbits, "skinny 32 rows integer")
+    else:
+        util.check_tol(BF16, bits, f64, "skinny 32 rows", ref_bits=rbits)
+
+
 def test_skinny_matches_tiled_on_integers(tg, monkeypatch):
     p = inputs.problem(BF16, 16, 2048, 4096, seed=51, kind="int")
     a, ka = run(tg, p)
@@ -204,6 +220,10 @@ SKINNY_FORCED = [
     (128, BF16, 16, 4096, 5120, "10"), (128, F16, 1, 384, 1536, ""),
     (256, BF16, 16, 2048, 4096, ""), (256, F16, 9, 1024, 4096, "1"),
     (256, BF16, 16, 2048, 8192, "11"),
+    # 16 < M <= 32: two 16-row blocks
+    (128, BF16, 32, 2048, 4096, ""), (128, F16, 17, 1024, 4096, "1"),
+    (128, BF16, 32, 4096, 5120, "10"), (256, BF16, 24, 2048, 8192, "11"),
+    (256, F16, 32, 1024, 4096, "1"),
 ]
 
 
@@ -219,6 +239,7 @@ def test_skinny_stream_widths(tg, monkeypatch, bn, dt, M, N, K, splits, integer)
     bits, kern = run(tg, p)
     say("  kernel", kern)
     assert kern.startswith("skinny_stream_bn%d_" % bn)
+    assert kern.endswith("_m32") == (M > 16)
     if splits:
         assert ("_split%sx" % splits) in kern
     f64, rbits = oracle.gemm(dt, p["A"], p["B"])
@@ -229,14 +250,15 @@ def test_skinny_stream_widths(tg, monkeypatch, bn, dt, M, N, K, splits, integer)
 
 
 @pytest.mark.parametrize("bn", [128, 256])
-def test_skinny_stream_epilogue(tg, monkeypatch, bn):
+@pytest.mark.parametrize("M", [13, 29])
+def test_skinny_stream_epilogue(tg, monkeypatch, bn, M):
     """Bias, GELU_tanh and a residual through the split-K combine."""
     import torch
     monkeypatch.setenv("TG_SKINNY_BN", str(bn))
-    dt, M, N, K = BF16, 13, 2048, 4096
-    p = inputs.problem(dt, M, N, K, seed=5200 + bn, kind="normal", b_scale=K ** -0.5,
+    dt, N, K = BF16, 2048, 4096
+    p = inputs.problem(dt, M, N, K, seed=5200 + bn + M, kind="normal", b_scale=K ** -0.5,
                        bias=True, act=inputs.ACT_GELU_TANH)
-    R = inputs.draw(np.random.default_rng(5300 + bn), (M, N), "uniform", dt)
+    R = inputs.draw(np.random.default_rng(5300 + bn + M), (M, N), "uniform", dt)
     A, B, bias = dev_problem(p)
     Rd = util.to_dev(R, dt)
     C = tg.gemm(A, B, bias=bias, act="gelu_tanh", residual=Rd)
@@ -690,6 +712,21 @@ def test_transposed_b_k_zero(tg):
     f64, rbits = oracle.gemm_ex(dt, np.zeros((8, 0), np.uint16), np.zeros((24, 0), np.uint16),
                                 trans_b=True, bias=bias, act=oracle.ACT_GELU_TANH, R=R)
     util.check_tol(dt, util.to_bits(C), f64, "B[N,K] K=0", ref_bits=rbits)
+
+
+def test_small_m_dispatch_bounds(tg):
+    # M <= 32 streams W when the streaming kernel fits; larger M, or 16 < M
+    # <= 32 on shapes it does not fit, take the square-tile paths
+    import torch
+    w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    for M, expect in ((16, "skinny_stream"), (32, "skinny_stream"), (33, "tiled")):
+        x = torch.zeros((M, 8192), dtype=torch.bfloat16, device="cuda")
+        tg.gemm(x, w)
+        assert tg.last_kernel().startswith(expect), (M, tg.last_kernel())
+    x = torch.zeros((20, 1000), dtype=torch.bfloat16, device="cuda")
+    tg.gemm(x, torch.zeros((1000, 1000), dtype=torch.bfloat16, device="cuda"))
+    assert not tg.last_kernel().startswith("skinny"), tg.last_kernel()
+    torch.cuda.synchronize()
 
 
 def test_dispatch_choices(tg):

@@ -370,11 +370,13 @@ __device__ __forceinline__ void static_for(F &&f)
 
 } // namespace
 
-template <int DT, int ACT, int BN>
+// MB: 16-row blocks of X and Y (1: M <= 16, 2: M <= 32).
+template <int DT, int ACT, int BN, int MB>
 __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p, int k_chunk,
                                                                      int splits, float *ws,
                                                                      int *counters)
 {
+    static_assert(MB == 1 || MB == 2, "up to 32 rows");
     using C = SaCfg<BN>;
     constexpr int STAGES = C::STAGES, NJ = C::NJ;
     __shared__ __attribute__((aligned(1024))) unsigned char st[STAGES][C::STAGE_BYTES];
@@ -401,9 +403,10 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         const int r = C::ROWS_PER_COPY * q + lane / C::GRANULES;
         gw[c] = W + (int64_t)(kbeg + r) * p.ldb + n0 + ((lane % C::GRANULES) ^ swz_w<BN>(r)) * 8;
     }
-    // X copy: rows 8 (wave & 1) + lane/8 (clamped to M-1: rows >= M only feed
-    // output rows that are never stored), granule (lane%8) ^ (row & 7).
-    const int xr = 8 * (wave & 1) + (lane >> 3);
+    // X copy: rows 8 w + lane/8 for MB = 2, rows 8 (w & 1) + lane/8 for
+    // MB = 1 (waves 2 and 3 write the duplicate), clamped to M-1 (rows >= M
+    // only feed output rows that are never stored), granule (lane%8) ^ (row & 7).
+    const int xr = 8 * (MB == 2 ? wave : (wave & 1)) + (lane >> 3);
     const unsigned short *gx =
         p.A + (int64_t)min(xr, M - 1) * p.lda + kbeg + (((lane & 7) ^ (xr & 7)) * 8);
     const int64_t w_step = (int64_t)SA_BK * p.ldb;
@@ -440,23 +443,32 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                         r * (2 * BN) + (((col >> 3) ^ swz_w<BN>(r)) * 16) + (col & 7) * 2;
                 }
     }
-    // X fragment of half kk: row lane % 16, granule 4 kk + lane / 16.
-    int x_off[2];
+    // X fragment of row block mb, half kk: row 16 mb + lane % 16, granule
+    // 4 kk + lane / 16.
+    int x_off[MB][2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int r = lane & 15;
-        x_off[kk] = C::W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
-    }
-
-    f32x4 acc[NJ];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 2; ++kk) {
+            const int r = 16 * mb + (lane & 15);
+            x_off[mb][kk] = C::W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
+        }
 
+    f32x4 acc[MB][NJ];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // each W fragment serves every 16-row block of X
     auto compute = [&](const unsigned char *stage) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const u32x4 xf = *reinterpret_cast<const u32x4 *>(stage + x_off[kk]);
+            u32x4 xf[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                xf[mb] = *reinterpret_cast<const u32x4 *>(stage + x_off[mb][kk]);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const u32x2 lo = __builtin_bit_cast(
@@ -465,7 +477,10 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
                 const u32x2 hi = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                (lds_s16x4 *)(stage + w_off[j][kk][1])));
-                acc[j] = mfma16x16x32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, xf, acc[j]);
+                const u32x4 wf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][j] = mfma16x16x32<DT>(wf, xf[mb], acc[mb][j]);
             }
         }
     };
@@ -496,32 +511,39 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         static_for<0, STAGES>([&](auto i) { step(s + decltype(i)::value, i); });
     sa_wait_vmcnt<0>();
 
-    // Lane l holds Y[m = l % 16][n = WAVE_COLS w + 16 j + 4 (l / 16) + r] in acc[j][r].
-    const int m = lane & 15;
-    if (splits == 1) {
-        if (m < M) {
+    // Lane l holds Y[m = 16 mb + l % 16][n = WAVE_COLS w + 16 j + 4 (l / 16) + r]
+    // in acc[mb][j][r].
+    auto store_rows = [&](const f32x4 (&val)[MB][NJ]) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
-                float v[4];
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + (lane & 15);
+            if (m < M) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x = acc[j][r];
-                    if (p.bias != nullptr)
-                        x += from_bits<DT>(p.bias[n + r]);
-                    v[r] = activate<ACT>(x);
+                for (int j = 0; j < NJ; ++j) {
+                    const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x = val[mb][j][r];
+                        if (p.bias != nullptr)
+                            x += from_bits<DT>(p.bias[n + r]);
+                        v[r] = activate<ACT>(x);
+                    }
+                    if (p.R != nullptr)
+                        add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, v);
+                    u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+                    *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
                 }
-                if (p.R != nullptr)
-                    add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, v);
-                u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-                *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
             }
         }
+    };
+    if (splits == 1) {
+        store_rows(acc);
         return;
     }
 
     // Split-K.  Each workgroup stores its FP32 partial in accumulator order
-    // (workgroup block [4 waves][NJ][64 lanes] of 16-byte vectors, the blocks
+    // (workgroup block [4 waves][MB][NJ][64 lanes] of 16-byte vectors, the blocks
     // of one column tile's splits side by side), so every store and every
     // load below moves one contiguous KiB per wave.  The stores are
     // device-coherent (sc1: written through to the device coherence point,
@@ -532,14 +554,18 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     // (independent of arrival order), applies the epilogue, stores Y and
     // resets the counter.  Both sides use device-scope coherent
     // accesses, so no cache-wide writeback or invalidate is needed.
-    float *ws_tile = ws + (int64_t)tile_n * splits * (16 * BN);
-    const int lane_off = (wave * NJ) * 256 + lane * 4;
+    constexpr int BLOCK = 16 * MB * BN; // floats per workgroup partial
+    float *ws_tile = ws + (int64_t)tile_n * splits * BLOCK;
+    const int lane_off = (wave * MB * NJ) * 256 + lane * 4;
     {
-        float *dst = ws_tile + split * (16 * BN) + lane_off;
+        float *dst = ws_tile + split * BLOCK + lane_off;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst + j * 256), "v"(acc[j])
-                         : "memory");
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst + (mb * NJ + j) * 256),
+                             "v"(acc[mb][j])
+                             : "memory");
     }
     sa_wait_vmcnt<0>();
     // Every wave has waited for its own copies, so the stages are idle and
@@ -556,50 +582,60 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         return;
 
     // The partials are read back in rounds of RS splits (one round for the
-    // planner's split counts: 4 at BN = 128, 8 at BN = 256), all 8 loads of a
-    // round in flight together, then added in split order (indices past the
-    // last split repeat it and are not added).  The own split is read back
-    // too, so no branch sits between a load and its wait.
-    constexpr int RS = BN == 128 ? 4 : 8;
-    f32x4 sum[NJ];
+    // planner's split counts: 4 at BN = 128, 8 at BN = 256 with MB = 1), all
+    // RS MB NJ loads of a round in flight together, then added in split order
+    // (indices past the last split repeat it and are not added).  The own
+    // split is read back too, so no branch sits between a load and its wait.
+    constexpr int PV = MB * NJ;                       // vectors per lane per split
+    constexpr int RS = (BN == 128 || MB == 2) ? 4 : 8;
+    constexpr int L = RS * PV;                         // loads per round: 8, 16 or 32
+    f32x4 sum[MB][NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-        sum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            sum[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sp0 = 0; sp0 < splits; sp0 += RS) {
-        f32x4 v[RS][NJ];
+        f32x4 v[L];
 #pragma unroll
         for (int u = 0; u < RS; ++u) {
-            const float *src = ws_tile + min(sp0 + u, splits - 1) * (16 * BN) + lane_off;
+            const float *src = ws_tile + min(sp0 + u, splits - 1) * BLOCK + lane_off;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int t = 0; t < PV; ++t)
                 asm volatile("global_load_dwordx4 %0, %1, off sc1"
-                             : "=v"(v[u][j])
-                             : "v"(src + j * 256)
+                             : "=v"(v[u * PV + t])
+                             : "v"(src + t * 256)
                              : "memory");
         }
         // the loads above are invisible to the compiler's wait tracking: wait
         // here and pass every value through, so nothing reads (or moves) one
         // earlier (loads return in order)
-        if constexpr (RS * NJ == 32) {
+        if constexpr (L == 32) {
             asm volatile("s_waitcnt vmcnt(16)"
-                         : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
-                           "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
-                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[2][2]), "+v"(v[2][3]),
-                           "+v"(v[3][0]), "+v"(v[3][1]), "+v"(v[3][2]), "+v"(v[3][3])
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                           "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                           "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
                          :
                          : "memory");
             asm volatile("s_waitcnt vmcnt(0)"
-                         : "+v"(v[4][0]), "+v"(v[4][1]), "+v"(v[4][2]), "+v"(v[4][3]),
-                           "+v"(v[5][0]), "+v"(v[5][1]), "+v"(v[5][2]), "+v"(v[5][3]),
-                           "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[6][2]), "+v"(v[6][3]),
-                           "+v"(v[7][0]), "+v"(v[7][1]), "+v"(v[7][2]), "+v"(v[7][3])
+                         : "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]),
+                           "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]),
+                           "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]),
+                           "+v"(v[31])
+                         :
+                         : "memory");
+        } else if constexpr (L == 16) {
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                           "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                           "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
                          :
                          : "memory");
         } else {
-            static_assert(RS * NJ == 8, "combine operand count");
+            static_assert(L == 8, "combine operand count");
             asm volatile("s_waitcnt vmcnt(0)"
-                         : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]),
-                           "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1])
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                           "+v"(v[6]), "+v"(v[7])
                          :
                          : "memory");
         }
@@ -607,27 +643,12 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
         for (int u = 0; u < RS; ++u)
             if (sp0 + u < splits)
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    sum[j] += v[u][j];
-    }
-    if (m < M) {
+                for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int n = n0 + wave * C::WAVE_COLS + 16 * j + 4 * (lane >> 4);
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = sum[j][r];
-                if (p.bias != nullptr)
-                    x += from_bits<DT>(p.bias[n + r]);
-                v[r] = activate<ACT>(x);
-            }
-            if (p.R != nullptr)
-                add_residual<DT, 4>(p.R, p.ldr, m, n, p.N, v);
-            u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-            *reinterpret_cast<u32x2 *>(p.C[0] + (int64_t)m * p.ldc + n) = o;
-        }
+                    for (int j = 0; j < NJ; ++j)
+                        sum[mb][j] += v[u * PV + mb * NJ + j];
     }
+    store_rows(sum);
     if (tid == 0)
         __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -811,14 +832,15 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
 
 SkinnyPlan plan_skinny(int M, int N, int K)
 {
-    (void)M;
     SkinnyPlan pl;
+    pl.mb = M > 16 ? 2 : 1;
     // The column-tile kernel needs no cross-workgroup reduction and is the
     // fastest when W is cache-resident, but its 64-byte row pieces stream
     // from HBM less efficiently than the split-K kernel's 512-byte pieces;
     // TG_SKINNY_COLS=1 selects it.
     const char *cols = getenv("TG_SKINNY_COLS");
-    if (N % SC_BN == 0 && N / SC_BN >= 128 && K % (4 * SC_BK) == 0 && cols && cols[0] == '1') {
+    if (M <= 16 && N % SC_BN == 0 && N / SC_BN >= 128 && K % (4 * SC_BK) == 0 && cols &&
+        cols[0] == '1') {
         pl.streaming = 2;
         pl.bn = SC_BN;
         pl.n_tiles = N / SC_BN;
@@ -860,6 +882,14 @@ SkinnyPlan plan_skinny(int M, int N, int K)
         pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
         return pl;
     }
+    if (M > 16) {
+        pl.streaming = -1; // the register-staged kernel holds 16 rows
+        pl.bn = 0;
+        pl.n_tiles = 0;
+        pl.splits = 0;
+        pl.k_chunk = 0;
+        return pl;
+    }
     pl.streaming = 0;
     pl.bn = SK_BN;
     pl.n_tiles = (N + SK_BN - 1) / SK_BN;
@@ -885,7 +915,7 @@ size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N)
     (void)M;
     if (pl.splits <= 1)
         return 0;
-    return pl.streaming ? (size_t)pl.splits * 16 * (size_t)N
+    return pl.streaming ? (size_t)pl.splits * 16 * (size_t)pl.mb * (size_t)N
                         : (size_t)pl.splits * 16 * (size_t)pl.n_tiles * SK_BN;
 }
 
@@ -911,16 +941,20 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
 #undef TG_SC
         return hipGetLastError();
     }
-    if (pl.streaming) {
-#define TG_SA(DT_, ACT_, BN_)                                                                    \
-    hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_, BN_>), grid, dim3(SA_NT), 0, s, a,     \
-                       pl.k_chunk, pl.splits, ws, counters)
+    if (pl.streaming == 1) {
+#define TG_SA(DT_, ACT_, BN_, MB_)                                                               \
+    hipLaunchKernelGGL((gemm_skinny_async_kernel<DT_, ACT_, BN_, MB_>), grid, dim3(SA_NT), 0, s, \
+                       a, pl.k_chunk, pl.splits, ws, counters)
 #define TG_SA_BN(DT_, ACT_)                                                                      \
     do {                                                                                         \
-        if (pl.bn == 128)                                                                        \
-            TG_SA(DT_, ACT_, 128);                                                               \
+        if (pl.bn == 128 && pl.mb == 2)                                                          \
+            TG_SA(DT_, ACT_, 128, 2);                                                            \
+        else if (pl.bn == 128)                                                                   \
+            TG_SA(DT_, ACT_, 128, 1);                                                            \
+        else if (pl.mb == 2)                                                                     \
+            TG_SA(DT_, ACT_, 256, 2);                                                            \
         else                                                                                     \
-            TG_SA(DT_, ACT_, 256);                                                               \
+            TG_SA(DT_, ACT_, 256, 1);                                                            \
     } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)

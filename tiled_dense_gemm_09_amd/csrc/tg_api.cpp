@@ -243,7 +243,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         set_last(!fast            ? "generic_fma (unaligned operands)"
                  : force_generic ? "generic_fma (forced)"
                                  : "generic_fma (B stored [N,K] outside the async tile shapes)");
-    } else if (n_mat == 1 && M <= 16 && K >= 256 && N >= 256 && !force_tiled && !b_trans) {
+    } else if (n_mat == 1 && M <= 32 && K >= 256 && N >= 256 && !force_tiled && !b_trans &&
+               tg::plan_skinny(a.M, a.N, a.K).streaming >= 0) {
+        // M <= 16 always; 16 < M <= 32 when the streaming kernel fits the shape
         const tg::SkinnyPlan pl = tg::plan_skinny(a.M, a.N, a.K);
         float *ws = nullptr;
         int *counters = nullptr;
@@ -259,9 +261,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         }
         err = tg::launch_skinny(kdt, kact, a, pl, ws, counters, s);
         char detail[48];
-        snprintf(detail, sizeof detail, "%s_bn%d_split%dx%d",
+        snprintf(detail, sizeof detail, "%s_bn%d_split%dx%d%s",
                  pl.streaming == 2 ? "_cols" : (pl.streaming ? "_stream" : ""), pl.bn, pl.splits,
-                 pl.k_chunk);
+                 pl.k_chunk, pl.mb == 2 ? "_m32" : "");
         set_last("skinny", detail);
     } else if ((!force_tiled || b_trans) && choose_async(a, force) >= 0) {
         const int cfg = choose_async(a, force);

@@ -95,12 +95,14 @@ int attn_block_m(const AttnArgs &a, int want);
 hipError_t launch_attn(int dt, bool causal, int bm, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_generic(int dt, bool causal, const AttnArgs &a, int D, hipStream_t stream);
 
-// Small-M path (M <= 16): W streamed once, split over K.  `ws` is an FP32
+// Small-M path (M <= 32): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
 // entries that must be zero before the first call; the kernel leaves them
-// zero.
+// zero.  M <= 16 has every kernel below; 16 < M <= 32 only the split-K
+// streaming kernel (streaming = -1 when the shape does not fit it).
 struct SkinnyPlan {
-    int streaming; // 2: column-tile kernel, 1: split-K streaming kernel, 0: register-staged kernel
+    int streaming; // 2: column-tile kernel, 1: split-K streaming kernel, 0: register-staged kernel, -1: none
+    int mb;       // 16-row blocks (1: M <= 16, 2: M <= 32)
     int bn;       // columns per workgroup
     int splits;   // K splits
     int k_chunk;  // K per split (multiple of the slab depth)
