@@ -118,9 +118,35 @@ def cpu_baseline(p, target_s):
         oracle.gemm(p["dt"], p["A"], p["B"], p["bias"], p["act"], rows=(0, rows))
         secs = time.perf_counter() - t0
     flops = 2.0 * rows * p["N"] * p["K"]
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of the %dx%dx%d workload, all %d columns (%.1f s, double "
-                      "precision)" % (rows - 1, p["M"], p["N"], p["K"], p["N"], secs)}
+    rec = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "rows 0..%d of the %dx%dx%d workload, all %d columns (%.1f s, double "
+                     "precision)" % (rows - 1, p["M"], p["N"], p["K"], p["N"], secs),
+           "cpu_model": cpu_model()}
+    # the two small square shapes in full, one thread (their GPU rates are
+    # graph-replay launches of the same shapes)
+    from tiled_dense_gemm_09_amd import inputs
+    single = {}
+    for name in ("f16_256", "f16_1024"):
+        q = inputs.config_problem(name)
+        t0 = time.perf_counter()
+        oracle.gemm(q["dt"], q["A"], q["B"], threads=1)
+        dt_s = time.perf_counter() - t0
+        single[name] = {"s": round(dt_s, 4),
+                        "GFLOP/s": round(2.0 * q["M"] * q["N"] * q["K"] / dt_s / 1e9, 3)}
+    rec["single_thread_full"] = single
+    return rec
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (Linux)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
