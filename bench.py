@@ -155,7 +155,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "attn", "qkv", "square8192",
-                                       "skinny", "small", "vendor", "copy"],
+                                       "skinny", "small", "vendor", "copy", "sweep"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -169,6 +169,10 @@ def main():
     import torch
     from tiled_dense_gemm_09_amd import inputs, tg
     assert torch.cuda.is_available(), "no GPU visible"
+
+    if args.only == "sweep":
+        run_sweep(torch, tg)
+        return
 
     if args.only == "copy":
         # plain copy of a known size, for scaling the HBM byte counters
@@ -472,6 +476,72 @@ def run_secondary(args, torch, inputs, tg):
                         "eager_TFLOP/s": round(flop / (ms_eager * 1e-3) / 1e12, 2)}
             log("  ", name, out[key])
     return out
+
+
+def run_sweep(torch, tg):
+    """Rates across shapes beside the ROCm library (torch.matmul), one JSON
+    object per shape on stdout: square f16/bf16 GEMMs from 512^3 to 8192^3
+    (A, B = U[-1,1]/8, no epilogue; up to 2048^3 both sides replayed from
+    captured graphs of 50 launches) and bf16 products with M = 1..32
+    (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB)."""
+    def graph_ms(fn, per=50, reps=10):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per):
+                fn()
+        torch.cuda.synchronize()
+        return time_launches(lambda: g.replay(), reps, 2) / per
+
+    torch.manual_seed(0)
+    for dt in (torch.float16, torch.bfloat16):
+        for n in (512, 1024, 2048, 3072, 4096, 6144, 8192):
+            A = (torch.rand(n, n, device="cuda") * 2 - 1).to(dt) / 8
+            B = (torch.rand(n, n, device="cuda") * 2 - 1).to(dt) / 8
+            C = torch.empty(n, n, dtype=dt, device="cuda")
+            steps = max(20, min(2000, int(2e13 / (2 * n ** 3))))
+
+            def timed(fn):
+                return graph_ms(fn) if n <= 2048 else time_launches(fn, steps, steps // 10 + 2)
+            ms = timed(lambda: tg.gemm(A, B, out=C))
+            kern = tg.last_kernel()
+            ml = timed(lambda: torch.matmul(A, B, out=C))
+            print(json.dumps({"shape": "%s %d^3" % (str(dt).split(".")[-1], n),
+                              "ms": round(ms, 5), "TFLOP/s": round(2 * n ** 3 / ms / 1e9, 1),
+                              "kernel": kern,
+                              "library_TFLOP/s": round(2 * n ** 3 / ml / 1e9, 1)}), flush=True)
+            del A, B, C
+    for (N, K) in ((4096, 4096), (8192, 8192)):
+        rot = max(1, (1 << 30) // (N * K * 2))
+        Ws = [torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+              for _ in range(rot)]
+        for M in (1, 4, 8, 16, 24, 32):
+            X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            it = [0]
+
+            def ours():
+                tg.gemm(X, Ws[it[0] % rot], out=Y)
+                it[0] += 1
+
+            def lib():
+                torch.matmul(X, Ws[it[0] % rot], out=Y)
+                it[0] += 1
+            ms = time_launches(ours, 500, 50)
+            kern = tg.last_kernel()
+            ml = time_launches(lib, 500, 50)
+            nb = 2 * (K * N + M * K + M * N)
+            print(json.dumps({"shape": "bf16 M=%d N=%d K=%d" % (M, N, K), "ms": round(ms, 5),
+                              "GB/s": round(nb / ms / 1e6), "kernel": kern,
+                              "library_GB/s": round(nb / ml / 1e6)}), flush=True)
+        del Ws
+        torch.cuda.empty_cache()
 
 
 def graph_launch_ms(fn, out, ref, replays, per_graph=100):
