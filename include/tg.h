@@ -39,11 +39,14 @@
  *    names the kernel and tile configuration the last call on this host
  *    thread launched (and TG_LOG=1 in the environment prints it).
  *  - Thread safety: entry points may be called from several host threads.
- *    The split-K path of tg_gemm/tg_gemm_bias_act for small M keeps a
- *    per-device workspace that is allocated on first use and grown when a
- *    larger one is needed (the only allocation the library makes); calls
- *    that use it are ordered by their streams, and two such calls on
- *    different streams of one device must not overlap.
+ *    The split-K paths of tg_gemm, tg_gemm_bias_act, tg_gemm_ex and
+ *    tg_gemm_qkv (small M, and square tiles that would leave most compute
+ *    units idle; tg_last_kernel() then ends in "_split..." or "_splitk<n>")
+ *    keep a per-device workspace that is allocated on first use and grown
+ *    when a larger one is needed (the only allocation the library makes;
+ *    growing it synchronizes the device).  Calls that use it are ordered by
+ *    their streams; two such calls on different streams of one device must
+ *    not overlap.
  */
 #ifndef TG_H
 #define TG_H

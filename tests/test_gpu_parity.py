@@ -70,6 +70,23 @@ def test_small_config_random_full(tg, name):
 
 
 @pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
+def test_small_config_automatic_split_k(tg, monkeypatch, name):
+    # the same workloads with TG_SPLITK=0 (two splits of 64 x 128 tiles):
+    # integer inputs bit-exact, random inputs within the tolerance
+    monkeypatch.setenv("TG_SPLITK", "0")
+    for integer in (True, False):
+        p = inputs.config_problem(name, integer=integer)
+        say("case", name, "automatic split-K", "integer" if integer else "random")
+        bits, kern = run(tg, p)
+        assert kern == "async_64x128x32_s4_splitk2", kern
+        f64, rbits = oracle.gemm(p["dt"], p["A"], p["B"])
+        if integer:
+            util.check_exact(bits, rbits, name + " split-K")
+        else:
+            util.check_tol(p["dt"], bits, f64, name + " split-K", ref_bits=rbits)
+
+
+@pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
 def test_small_config_integer_exact(tg, name):
     p = inputs.config_problem(name, integer=True)
     say("case", name, "integer", p["M"], p["N"], p["K"])
@@ -412,6 +429,101 @@ def test_async_small_tile_qkv(tg, monkeypatch):
         util.check_exact(outs[t], ref, "qkv small tiles [%d]" % t)
 
 
+# ------------------------------------------- split-K for under-filled grids
+
+SPLIT_CASES = [
+    # (dt, M, N, K, config, splits): 24 and 6 tiles of 128 x 128, 6 and 2 tiles
+    # of 64 x 128; 8 splits of 128, 4 of 256, 2 of 512, 3 of 128
+    (F16, 512, 768, 1024, "async_128x128x32_s4", 8),
+    (BF16, 512, 768, 1024, "async_128x128x32_s4", 4),
+    (F16, 256, 384, 1024, "async_128x128x32_s4", 2),
+    (BF16, 192, 256, 512, "async_64x128x32_s4", 4),
+    (F16, 128, 128, 384, "async_64x128x32_s4", 3),
+]
+
+
+def forced_split(monkeypatch, cfg, splits):
+    monkeypatch.setenv("TG_FORCE_CONFIG", cfg)
+    monkeypatch.setenv("TG_SPLITK", str(splits))
+    return "%s_splitk%d" % (cfg, splits)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,cfg,splits", SPLIT_CASES)
+def test_split_k_integer_exact(tg, monkeypatch, dt, M, N, K, cfg, splits, trans_b):
+    # integer operands, bias and residual: every FP32 partial sum is exact, so
+    # the ordered sum of the splits must reproduce the oracle's bits
+    name = forced_split(monkeypatch, cfg, splits)
+    p = inputs.problem(dt, M, N, K, seed=140 + splits + M, kind="int", bias=True,
+                       bias_kind="int")
+    R = inputs.draw(np.random.default_rng(141 + N), (M, N), "int", dt, 8.0)
+    say("case split-K integer", dt, M, N, K, name, "B[N,K]" if trans_b else "B[K,N]")
+    bits, kern = run_ex(tg, p, trans_b, R)
+    assert kern == name
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    util.check_exact(bits, ref, name)
+
+
+@pytest.mark.parametrize("dt,M,N,K,cfg,splits", SPLIT_CASES[:4])
+def test_split_k_bias_gelu_random_and_repeatable(tg, monkeypatch, dt, M, N, K, cfg, splits):
+    # random operands: within the tolerance, and the same bits on every call
+    # (the splits are added in split order whatever order they finish in)
+    name = forced_split(monkeypatch, cfg, splits)
+    p = inputs.problem(dt, M, N, K, seed=150 + splits, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.2, b_scale=0.2)
+    say("case split-K gelu", dt, M, N, K, name)
+    bits, kern = run(tg, p)
+    assert kern == name
+    f64, rbits = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(dt, bits, f64, name, ref_bits=rbits)
+    for _ in range(3):
+        again, _ = run(tg, p)
+        assert np.array_equal(again, bits), "split-K result changed between calls"
+
+
+def test_split_k_qkv_and_more_than_one_wave(tg, monkeypatch):
+    # three outputs in one launch (18 tiles x 4 splits), then 256 tiles x 2
+    # splits = 512 workgroups, then the first shape again: the tile counters
+    # must come back to zero after every launch
+    name = forced_split(monkeypatch, "async_128x128x32_s4", 4)
+    q = inputs.qkv_problem(BF16, 256, 384, 512, seed=161, kind="int")
+    say("case split-K qkv 256x384x512 x3")
+    _, _, outs = run_qkv(tg, q)
+    assert tg.last_kernel() == name
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "split-K qkv [%d]" % t)
+    monkeypatch.setenv("TG_SPLITK", "2")
+    p = inputs.problem(F16, 2048, 2048, 256, seed=162, kind="int")
+    say("case split-K 2048x2048x256, 512 workgroups")
+    bits, kern = run(tg, p)
+    assert kern == "async_128x128x32_s4_splitk2"
+    _, ref = oracle.gemm(F16, p["A"], p["B"])
+    util.check_exact(bits, ref, kern)
+    monkeypatch.setenv("TG_SPLITK", "4")
+    _, _, outs = run_qkv(tg, q)
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "split-K qkv again [%d]" % t)
+
+
+def test_split_k_off_and_unsplittable_k(tg, monkeypatch):
+    # TG_SPLITK=1 keeps the forced tile unsplit; a K that no split count
+    # divides into multiples of 128 (K = 128) runs unsplit too
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_64x128x32_s4")
+    monkeypatch.setenv("TG_SPLITK", "1")
+    a = torch.zeros((256, 256), dtype=torch.float16, device="cuda")
+    tg.gemm(a, a)
+    assert tg.last_kernel() == "async_64x128x32_s4"
+    monkeypatch.setenv("TG_SPLITK", "4")
+    b = torch.zeros((256, 128), dtype=torch.float16, device="cuda")
+    tg.gemm(b, torch.zeros((128, 256), dtype=torch.float16, device="cuda"))
+    assert tg.last_kernel() == "async_64x128x32_s4"
+    torch.cuda.synchronize()
+
+
 # ------------------------------- extended epilogue: residual and B stored [N,K]
 
 def run_ex(tg, p, trans_b, R=None, Rin_place=False):
@@ -729,7 +841,7 @@ def test_small_m_dispatch_bounds(tg):
     torch.cuda.synchronize()
 
 
-def test_dispatch_choices(tg):
+def test_dispatch_choices(tg, monkeypatch):
     import torch
     a = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
     tg.gemm(a, a)
@@ -738,10 +850,20 @@ def test_dispatch_choices(tg):
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
     tg.gemm(x, w)
     assert tg.last_kernel().startswith("skinny")
-    # under-filled grids take the smaller asynchronous tiles
+    # under-filled grids take the smaller asynchronous tiles, unsplit unless
+    # TG_SPLITK asks (0: automatic, up to one wave of workgroups)
     b = torch.zeros((1024, 1024), dtype=torch.float16, device="cuda")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x128x32_s4"
+    d = torch.zeros((256, 256), dtype=torch.float16, device="cuda")
+    tg.gemm(d, d)
+    assert tg.last_kernel() == "async_64x128x32_s4"
+    monkeypatch.setenv("TG_SPLITK", "0")
+    tg.gemm(b, b)
+    assert tg.last_kernel() == "async_64x128x32_s4_splitk2"
+    tg.gemm(d, d)
+    assert tg.last_kernel() == "async_64x128x32_s4_splitk2"
+    monkeypatch.delenv("TG_SPLITK")
     c = torch.zeros((2048, 2048), dtype=torch.float16, device="cuda")
     tg.gemm(c, c)
     assert tg.last_kernel() == "async_128x128x32_s4"

@@ -68,11 +68,114 @@ __host__ __device__ constexpr int swz_b(int r) { return (0xCA60 >> (4 * (r & 3))
 
 } // namespace
 
+// Split-K partial exchange of one workgroup (see the kernel below).  The
+// partial of a tile's split is [4 waves][4 TI TJ vectors][64 lanes] of
+// 16-byte vectors, vector 4 (TJ i + j) + g holding registers 4g..4g+3 of
+// accumulator block (i, j), so each store or load instruction moves one
+// contiguous KiB per wave.  Returns true in the workgroup that completed
+// the count, with acc replaced by the ordered sum of all the splits.
+template <int TI, int TJ>
+__device__ __forceinline__ bool combine_splits(f32x16 (&acc)[TI][TJ], float *ws, int *counters,
+                                               int tile, int split, int splits, int wave, int lane)
+{
+    constexpr int PV = 4 * TI * TJ;                  // vectors per lane per split: 4, 8 or 16
+    constexpr int BLOCK = AS_NT / 64 * PV * 256;     // floats per split partial
+    constexpr int RS = 32 / PV;                      // splits read back per round
+    __shared__ int s_last;
+    float *ws_tile = ws + (int64_t)tile * splits * BLOCK;
+    const int lane_off = wave * PV * 256 + lane * 4;
+    {
+        f32x4 v[PV];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    v[(i * TJ + j) * 4 + g] = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                                    acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        store_partial<PV>(ws_tile + (int64_t)split * BLOCK + lane_off, v);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == splits - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return false;
+
+    // Rounds of RS splits, all 32 loads of a round in flight together, added
+    // in split order; indices past the last split repeat it and are not
+    // added.  The own split is read back too, so no branch sits between a
+    // load and its wait.
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
+        f32x4 v[32];
+#pragma unroll
+        for (int u = 0; u < RS; ++u) {
+            const float *src = ws_tile + (int64_t)min(sp0 + u, splits - 1) * BLOCK + lane_off;
+#pragma unroll
+            for (int t = 0; t < PV; ++t)
+                asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                             : "=v"(v[u * PV + t])
+                             : "v"(src + t * 256)
+                             : "memory");
+        }
+        // the loads are invisible to the compiler's wait tracking: wait here
+        // with every value passed through, so nothing reads one earlier
+        // (loads return in order)
+        asm volatile("s_waitcnt vmcnt(16)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                       "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                     :
+                     : "memory");
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]),
+                       "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]),
+                       "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]),
+                       "+v"(v[31])
+                     :
+                     : "memory");
+#pragma unroll
+        for (int u = 0; u < RS; ++u)
+            if (sp0 + u < splits)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[i][j][4 * g + e] += v[u * PV + (i * TJ + j) * 4 + g][e];
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// Split-K (splits > 1, grid = tiles x splits, block b = split * tiles + tile):
+// split s covers k in [s K / splits, (s + 1) K / splits), a multiple of the
+// four-step loop.  Each split's FP32 partial goes to ws with device-coherent
+// stores (the XCDs' L2 caches are not coherent with each other); one atomic
+// per workgroup counts it in, and the workgroup that completes the count
+// reads every partial back (device-coherent loads), adds them in split order
+// 0 .. splits-1 whatever the arrival order, runs the epilogue and resets the
+// tile's counter to zero.  The bias enters through split 0's accumulators.
+// ws holds splits x BM x BN floats per tile; counters one int per tile, zero
+// before the launch and zero after it.
 template <int DT, int ACT, int TI, int TJ, bool BT>
-__global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kernel(GemmArgs p,
-                                                                                 int tiles_m,
-                                                                                 int tiles_n,
-                                                                                 int group_m)
+__global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kernel(
+    GemmArgs p, int tiles_m, int tiles_n, int group_m, int splits, float *ws, int *counters)
 {
     using G = AsGeom<TI, TJ>;
     // one array per stage: with the K loop unrolled by the stage count every
@@ -99,11 +202,15 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave >> 1, wave_n = wave & 1; // 2 x 2 waves of (32 TI) x (32 TJ)
 
-    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int total = tiles_m * tiles_n * p.n_mat;
+    const int split = (int)blockIdx.x / total;
+    const int tile = (int)blockIdx.x - split * total;
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, tile);
     const int m0 = tc.tm * G::BM, n0 = tc.tn * G::BN;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    const int KT = p.K / AS_BK;
+    const int KT = p.K / (AS_BK * splits);
+    const int k0 = split * KT * AS_BK; // first k of this split
 
     // ---- copy plan: wave w issues copies q = TI w .. TI w + TI - 1 of A and
     // q = TJ w .. TJ w + TJ - 1 of B.
@@ -119,7 +226,7 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         const int q = wave * TI + i;
         const int ra = 16 * q + (lane >> 2);
         const int ca = (lane & 3) ^ swz_a(ra);
-        ga[i] = p.A + (int64_t)(m0 + ra) * p.lda + ca * 8;
+        ga[i] = p.A + (int64_t)(m0 + ra) * p.lda + k0 + ca * 8;
     }
 #pragma unroll
     for (int i = 0; i < TJ; ++i) {
@@ -127,11 +234,11 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         if constexpr (BT) {
             const int rb = 16 * q + (lane >> 2);
             const int cb = (lane & 3) ^ swz_a(rb);
-            gb[i] = Bm + (int64_t)(n0 + rb) * p.ldb + cb * 8;
+            gb[i] = Bm + (int64_t)(n0 + rb) * p.ldb + k0 + cb * 8;
         } else {
             const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
             const int cb = (lane % G::B_GRANULES) ^ swz_b(rb);
-            gb[i] = Bm + (int64_t)rb * p.ldb + n0 + cb * 8;
+            gb[i] = Bm + (int64_t)(k0 + rb) * p.ldb + n0 + cb * 8;
         }
     }
     const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb; // per K-step
@@ -167,7 +274,7 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     // epilogue.  Lane l of 32x32 block (i, j) holds columns
     // n = 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3 (any row).
     f32x16 acc[TI][TJ];
-    if (p.bias != nullptr) {
+    if (p.bias != nullptr && split == 0) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -339,6 +446,13 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
+
+    if constexpr (TI * TJ <= 4) {
+        if (splits > 1) {
+            if (!combine_splits<TI, TJ>(acc, ws, counters, tile, split, splits, wave, lane))
+                return;
+        }
+    }
 
     // ---- epilogue: activation, residual and rounding in registers, the
     // rounded wave tile restaged through the wave's own stage for whole-row
@@ -711,11 +825,38 @@ bool async_eligible(const GemmArgs &a, int cfg)
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
 
-hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
-                        hipStream_t s)
+int plan_async_splits(const GemmArgs &a, int cfg, int want)
+{
+    const AsyncConfig &c = kAsyncConfigs[cfg];
+    if (c.mfma16 || c.ti * c.tj > 4 || want == 1)
+        return 1;
+    const int64_t tiles = (int64_t)(a.M / async_tile_m(cfg)) * (a.N / async_tile_n(cfg)) * a.n_mat;
+    if (tiles > kMaxSplitTiles || (want <= 0 && tiles >= 240))
+        return 1;
+    // enough workgroups for one wave of the 256 CUs, at most 8 splits, each
+    // a multiple of the four-step loop
+    int s = want > 0 ? want : (int)(256 / tiles);
+    s = s > 8 ? 8 : s;
+    for (; s >= 2; --s)
+        if (a.K % (s * AS_STAGES * AS_BK) == 0)
+            return s;
+    return 1;
+}
+
+size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
+{
+    return (size_t)splits * ((size_t)a.M / async_tile_m(cfg)) * (a.N / async_tile_n(cfg)) *
+           a.n_mat * async_tile_m(cfg) * async_tile_n(cfg);
+}
+
+hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,
+                        float *ws, int *counters, hipStream_t s)
 {
     const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
-    dim3 grid(tiles_m * tiles_n * a.n_mat), block(AS_NT);
+    if (splits < 1 || (splits > 1 && (plan_async_splits(a, cfg, splits) != splits ||
+                                      ws == nullptr || counters == nullptr)))
+        return hipErrorInvalidValue;
+    dim3 grid(tiles_m * tiles_n * a.n_mat * splits), block(AS_NT);
     if (kAsyncConfigs[cfg].mfma16) {
         static_assert(A16Geom<4, false>::NT == 512 && A16Geom<2, false>::NT == 256 &&
                           A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
@@ -754,10 +895,10 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     do {                                                                                         \
         if (a.b_trans)                                                                           \
             hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_, true>), grid, block, 0, s, \
-                               a, tiles_m, tiles_n, group_m);                                    \
+                               a, tiles_m, tiles_n, group_m, splits, ws, counters);              \
         else                                                                                     \
             hipLaunchKernelGGL((gemm_async_kernel<DT_, ACT_, TI_, TJ_, false>), grid, block, 0,   \
-                               s, a, tiles_m, tiles_n, group_m);                                 \
+                               s, a, tiles_m, tiles_n, group_m, splits, ws, counters);           \
     } while (0)
 #define TG_AS_CFG(DT_, ACT_)                                                                     \
     do {                                                                                         \

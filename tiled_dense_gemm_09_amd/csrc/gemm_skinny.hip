@@ -558,16 +558,14 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     float *ws_tile = ws + (int64_t)tile_n * splits * BLOCK;
     const int lane_off = (wave * MB * NJ) * 256 + lane * 4;
     {
-        float *dst = ws_tile + split * BLOCK + lane_off;
+        f32x4 v[MB * NJ];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst + (mb * NJ + j) * 256),
-                             "v"(acc[mb][j])
-                             : "memory");
+                v[mb * NJ + j] = acc[mb][j];
+        store_partial<MB * NJ>(ws_tile + split * BLOCK + lane_off, v); // stores and waits
     }
-    sa_wait_vmcnt<0>();
     // Every wave has waited for its own copies, so the stages are idle and
     // the first word of stage 0 carries the arrival flag.
     int *s_last = reinterpret_cast<int *>(&st[0][0]);

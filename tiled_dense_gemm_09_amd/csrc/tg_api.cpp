@@ -268,8 +268,28 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     } else if ((!force_tiled || b_trans) && choose_async(a, force) >= 0) {
         const int cfg = choose_async(a, force);
         const int group_m = env_int("TG_GROUP_M", 4);
-        err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
-        set_last(tg::async_config_name(cfg));
+        // Split-K is opt-in (TG_SPLITK=0: automatic, n: n splits): at 256^3
+        // and 1024^3 the three device-scope round trips of the exchange
+        // (partial stores, counter, read-back) cost more than the split saves
+        const int want = env_int("TG_SPLITK", 1);
+        const int splits = tg::plan_async_splits(a, cfg, want);
+        float *ws = nullptr;
+        int *counters = nullptr;
+        if (splits > 1) {
+            static_assert(tg::kMaxSplitTiles * sizeof(int) <= kCounterBytes, "counter room");
+            tg_status st = TG_SUCCESS;
+            void *base = get_workspace(tg::async_ws_floats(a, cfg, splits), s, &st);
+            if (!base)
+                return st;
+            counters = static_cast<int *>(base);
+            ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
+        }
+        err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, splits, ws, counters,
+                               s);
+        char detail[24] = "";
+        if (splits > 1)
+            snprintf(detail, sizeof detail, "_splitk%d", splits);
+        set_last(tg::async_config_name(cfg), detail);
     } else {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);

@@ -202,4 +202,49 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c)
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Split-K partials: stores PV 16-byte vectors at dst + 1 KiB v (v = 0 ..
+// PV-1) with device-coherent stores (sc1, written through to the device
+// coherence point since the XCDs' L2 caches are not coherent with each
+// other) and waits for them, all in one asm statement.
+// The compiler treats the data registers of an asm store as free once the
+// statement ends and may write them at once, while the store can still be
+// reading them; with the wait inside the statement they stay untouched until
+// every store has completed.  Four vectors share a base address (immediate
+// offsets 0, 1, 2, 3 KiB).
+#define TG_ST4(B, V0, V1, V2, V3)                                                                   \
+    "global_store_dwordx4 %" #B ", %" #V0 ", off sc1\n\t"                                         \
+    "global_store_dwordx4 %" #B ", %" #V1 ", off offset:1024 sc1\n\t"                             \
+    "global_store_dwordx4 %" #B ", %" #V2 ", off offset:2048 sc1\n\t"                             \
+    "global_store_dwordx4 %" #B ", %" #V3 ", off offset:3072 sc1\n\t"
+template <int PV>
+__device__ __forceinline__ void store_partial(float *dst, const f32x4 (&v)[PV])
+{
+    if constexpr (PV == 16) {
+        asm volatile(TG_ST4(0, 4, 5, 6, 7) TG_ST4(1, 8, 9, 10, 11) TG_ST4(2, 12, 13, 14, 15)
+                         TG_ST4(3, 16, 17, 18, 19) "s_waitcnt vmcnt(0)" ::"v"(dst),
+                     "v"(dst + 1024), "v"(dst + 2048), "v"(dst + 3072), "v"(v[0]), "v"(v[1]),
+                     "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+                     "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]),
+                     "v"(v[15])
+                     : "memory");
+    } else if constexpr (PV == 8) {
+        asm volatile(TG_ST4(0, 2, 3, 4, 5) TG_ST4(1, 6, 7, 8, 9) "s_waitcnt vmcnt(0)" ::"v"(dst),
+                     "v"(dst + 1024), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]),
+                     "v"(v[5]), "v"(v[6]), "v"(v[7])
+                     : "memory");
+    } else if constexpr (PV == 4) {
+        asm volatile(TG_ST4(0, 1, 2, 3, 4) "s_waitcnt vmcnt(0)" ::"v"(dst), "v"(v[0]), "v"(v[1]),
+                     "v"(v[2]), "v"(v[3])
+                     : "memory");
+    } else {
+        static_assert(PV == 2, "partial vector count");
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\t"
+                     "global_store_dwordx4 %0, %2, off offset:1024 sc1\n\t"
+                     "s_waitcnt vmcnt(0)" ::"v"(dst),
+                     "v"(v[0]), "v"(v[1])
+                     : "memory");
+    }
+}
+#undef TG_ST4
+
 } // namespace tg

@@ -41,17 +41,30 @@ hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m
                         hipStream_t stream);
 hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
 
-// Asynchronous-copy MFMA kernel: configurations 0, 1, 2 have 256 x 256,
-// 128 x 128 and 64 x 128 tiles (all 32 deep, 4 stages); a problem is
-// eligible for a configuration when its tile divides M and N and K is a
-// multiple of 128.
+// Asynchronous-copy MFMA kernel: 256 x 256 tiles (16x16x32 or 32x32x16
+// MFMA), 128 x 128 and 64 x 128 tiles (32x32x16), all 32 deep, 4 stages; a
+// problem is eligible for a configuration when its tile divides M and N and
+// K is a multiple of 128.
 int num_async_configs();
 const char *async_config_name(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);
-hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m,
-                        hipStream_t stream);
+// Split-K for under-filled grids (128 x 128 and 64 x 128 tiles only, at most
+// kMaxSplitTiles tiles): the number of K splits for the configuration, 1 for
+// none.  want > 1 asks for that many (fewer when K does not divide), want
+// == 1 disables it; want <= 0 splits only grids of fewer than 240 tiles,
+// up to one wave of 256 workgroups.  The C ABI takes want from TG_SPLITK
+// (default 1).
+constexpr int kMaxSplitTiles = 4096;
+int plan_async_splits(const GemmArgs &a, int cfg, int want);
+// FP32 workspace the split kernel needs: splits x M x N x n_mat floats.
+size_t async_ws_floats(const GemmArgs &a, int cfg, int splits);
+// splits > 1 needs `ws` (async_ws_floats floats) and `counters` (one int per
+// tile, zero before the launch; the kernel leaves them zero), and must equal
+// plan_async_splits(a, cfg, splits).
+hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,
+                        float *ws, int *counters, hipStream_t stream);
 
 // Block-scaled 8-bit GEMM: C = act(sum_k a(A[m][k]) 2^(SA[k/32][m]-127)
 // * b(B[n][k]) 2^(SB[k/32][n]-127) + bias[n]).  A [M,K] and B [N,K] bytes
