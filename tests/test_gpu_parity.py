@@ -69,16 +69,18 @@ def test_small_config_random_full(tg, name):
     say("  kernel", kern, "max abs err", err)
 
 
-@pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
-def test_small_config_automatic_split_k(tg, monkeypatch, name):
-    # the same workloads with TG_SPLITK=0 (two splits of 64 x 128 tiles):
-    # integer inputs bit-exact, random inputs within the tolerance
+@pytest.mark.parametrize("name,expect", [("f16_256", "async_64x64x32_s4_splitk2"),
+                                         ("f16_1024", "async_64x64x32_s4")])
+def test_small_config_automatic_split_k(tg, monkeypatch, name, expect):
+    # the same workloads with TG_SPLITK=0: 256^3 (16 tiles of 64 x 64) splits
+    # K in two, 1024^3 (256 tiles) fills the chip unsplit; integer inputs
+    # bit-exact, random inputs within the tolerance
     monkeypatch.setenv("TG_SPLITK", "0")
     for integer in (True, False):
         p = inputs.config_problem(name, integer=integer)
         say("case", name, "automatic split-K", "integer" if integer else "random")
         bits, kern = run(tg, p)
-        assert kern == "async_64x128x32_s4_splitk2", kern
+        assert kern == expect, kern
         f64, rbits = oracle.gemm(p["dt"], p["A"], p["B"])
         if integer:
             util.check_exact(bits, rbits, name + " split-K")
@@ -387,7 +389,8 @@ def test_k_zero_gives_activated_bias(tg):
 # ------------------------------------------------- async tile configurations
 
 ASYNC_CONFIGS = ["async_256x256x32_s4_mfma16_w8", "async_256x256x32_s4_mfma16",
-                 "async_256x256x32_s4", "async_128x128x32_s4", "async_64x128x32_s4"]
+                 "async_256x256x32_s4", "async_128x128x32_s4", "async_64x128x32_s4",
+                 "async_64x64x32_s4"]
 
 
 @pytest.mark.parametrize("cfg", ASYNC_CONFIGS)
@@ -439,6 +442,7 @@ SPLIT_CASES = [
     (F16, 256, 384, 1024, "async_128x128x32_s4", 2),
     (BF16, 192, 256, 512, "async_64x128x32_s4", 4),
     (F16, 128, 128, 384, "async_64x128x32_s4", 3),
+    (BF16, 192, 320, 1024, "async_64x64x32_s4", 8),
 ]
 
 
@@ -552,6 +556,7 @@ EX_SHAPES = [
     (F16, 512, 512, 512, "async_256x256x32_s4_mfma16_w8"),
     (BF16, 256, 384, 256, "async_128x128x32_s4"),
     (F16, 192, 256, 512, "async_64x128x32_s4"),
+    (BF16, 192, 320, 384, "async_64x64x32_s4"),   # N a multiple of 64, not of 128
     (BF16, 300, 170, 200, None),          # ragged: tiled kernel (B [K,N]) / generic (B [N,K])
     (F16, 16, 1024, 2048, None),          # small M: streaming split-K kernel (B [K,N])
     (BF16, 5, 520, 777, None),            # small M, ragged: register-staged kernel
@@ -579,7 +584,7 @@ def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, f
 
 
 @pytest.mark.parametrize("trans_b", [False, True])
-@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES[:7])
+@pytest.mark.parametrize("dt,M,N,K,force", EX_SHAPES[:8])
 def test_residual_and_transposed_b_gelu_random(tg, monkeypatch, dt, M, N, K, force, trans_b):
     if force:
         monkeypatch.setenv("TG_FORCE_CONFIG", force)
@@ -850,23 +855,27 @@ def test_dispatch_choices(tg, monkeypatch):
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
     tg.gemm(x, w)
     assert tg.last_kernel().startswith("skinny")
-    # under-filled grids take the smaller asynchronous tiles, unsplit unless
-    # TG_SPLITK asks (0: automatic, up to one wave of workgroups)
-    b = torch.zeros((1024, 1024), dtype=torch.float16, device="cuda")
-    tg.gemm(b, b)
-    assert tg.last_kernel() == "async_64x128x32_s4"
-    d = torch.zeros((256, 256), dtype=torch.float16, device="cuda")
-    tg.gemm(d, d)
-    assert tg.last_kernel() == "async_64x128x32_s4"
-    monkeypatch.setenv("TG_SPLITK", "0")
-    tg.gemm(b, b)
-    assert tg.last_kernel() == "async_64x128x32_s4_splitk2"
-    tg.gemm(d, d)
-    assert tg.last_kernel() == "async_64x128x32_s4_splitk2"
-    monkeypatch.delenv("TG_SPLITK")
     c = torch.zeros((2048, 2048), dtype=torch.float16, device="cuda")
     tg.gemm(c, c)
     assert tg.last_kernel() == "async_128x128x32_s4"
+    # under-filled grids take the smaller asynchronous tiles (the largest
+    # with a full wave, else the smallest), unsplit unless TG_SPLITK asks
+    # (0: automatic, up to one wave of workgroups)
+    b = torch.zeros((1024, 1024), dtype=torch.float16, device="cuda")
+    tg.gemm(b, b)
+    assert tg.last_kernel() == "async_64x64x32_s4"
+    d = torch.zeros((256, 256), dtype=torch.float16, device="cuda")
+    tg.gemm(d, d)
+    assert tg.last_kernel() == "async_64x64x32_s4"
+    e = torch.zeros((1024, 2048), dtype=torch.float16, device="cuda")
+    tg.gemm(e, c)
+    assert tg.last_kernel() == "async_64x128x32_s4"
+    monkeypatch.setenv("TG_SPLITK", "0")
+    tg.gemm(b, b)
+    assert tg.last_kernel() == "async_64x64x32_s4"
+    tg.gemm(d, d)
+    assert tg.last_kernel() == "async_64x64x32_s4_splitk2"
+    monkeypatch.delenv("TG_SPLITK")
     torch.cuda.synchronize()
 
 

@@ -31,6 +31,7 @@
 //    with the bank-conflict counter on gfx950, as was the B pattern):
 //        A: granule c of row r at c ^ ((r >> 2) & 3)
 //        B: granule c of row r at c ^ {0, 6, 10, 12}[r & 3]
+//           (64-column tiles: c ^ 4 ((r >> 1) & 1))
 //    (power-of-two extents throughout; "TIRx", section 7 on XOR layouts).
 #include <type_traits>
 
@@ -60,11 +61,20 @@ struct AsGeom {
     static constexpr int C1 = COPIES / 2;               // copies issued in the second half-step
     static constexpr int B_ROWS_PER_COPY = 512 / BN;    // 1 KiB of [32][BN]
     static constexpr int B_GRANULES = BN / 8;           // 16-byte granules per B row
-    static_assert(BN >= 128, "the B swizzle needs at least 16 granules per row");
+    static_assert(BN >= 64, "B rows of at least 8 granules");
 };
 
-// {0, 6, 10, 12}[r & 3] as a nibble table (a shift, not a branch chain)
-__host__ __device__ constexpr int swz_b(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
+// B swizzle for rows of 16 or more granules: {0, 6, 10, 12}[r & 3] as a
+// nibble table (a shift, not a branch chain).  For 8-granule (128-byte) rows
+// the rows r and r + 2 share banks; flipping granule bit 2 on rows with bit
+// 1 set moves the four 64-byte row pieces one transposing read pass covers
+// (rows 4q .. 4q+3, 64 bytes each) onto four disjoint quarters of the
+// 256-byte bank window.
+template <int BN>
+__host__ __device__ constexpr int swz_b(int r)
+{
+    return BN >= 128 ? (0xCA60 >> (4 * (r & 3))) & 15 : 4 * ((r >> 1) & 1);
+}
 
 } // namespace
 
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
             gb[i] = Bm + (int64_t)(n0 + rb) * p.ldb + k0 + cb * 8;
         } else {
             const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
-            const int cb = (lane % G::B_GRANULES) ^ swz_b(rb);
+            const int cb = (lane % G::B_GRANULES) ^ swz_b<G::BN>(rb);
             gb[i] = Bm + (int64_t)(k0 + rb) * p.ldb + n0 + cb * 8;
         }
     }
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
                 for (int h = 0; h < 2; ++h) {
                     const int r = 16 * kk + 8 * (g >> 1) + 4 * h + (jj >> 2);
                     const int col = wave_n * 32 * TJ + 32 * j + 16 * (g & 1) + 4 * (jj & 3);
-                    const int gran = (col >> 3) ^ swz_b(r);
+                    const int gran = (col >> 3) ^ swz_b<G::BN>(r);
                     b_off[j][kk][h] = G::A_BYTES + r * (2 * G::BN) + gran * 16 + (col & 7) * 2;
                 }
     }
@@ -512,7 +522,7 @@ constexpr int A16_BM = 256, A16_BN = 256;
 constexpr int A16_A_BYTES = A16_BM * AS_BK * 2;             // [256][32] K-contiguous
 constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-contiguous
 
-__host__ __device__ constexpr int swz_b16(int r) { return swz_b(r) ^ (2 * ((r >> 3) & 1)); }
+__host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * ((r >> 3) & 1)); }
 
 template <int WN, bool BT>
 struct A16Geom {
@@ -810,6 +820,7 @@ const AsyncConfig kAsyncConfigs[] = {
     {4, 4, 0, "async_256x256x32_s4"},
     {2, 2, 0, "async_128x128x32_s4"},
     {1, 2, 0, "async_64x128x32_s4"},
+    {1, 1, 0, "async_64x64x32_s4"},
 };
 } // namespace
 
@@ -907,8 +918,10 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
             TG_AS(DT_, ACT_, 4, 4);                                                              \
         else if (c_.ti == 2)                                                                     \
             TG_AS(DT_, ACT_, 2, 2);                                                              \
-        else                                                                                     \
+        else if (c_.tj == 2)                                                                     \
             TG_AS(DT_, ACT_, 1, 2);                                                              \
+        else                                                                                     \
+            TG_AS(DT_, ACT_, 1, 1);                                                              \
     } while (0)
     if (dt == DT_F16) {
         if (act == ACT_GELU)

@@ -42,7 +42,8 @@ hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m
 hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
 
 // Asynchronous-copy MFMA kernel: 256 x 256 tiles (16x16x32 or 32x32x16
-// MFMA), 128 x 128 and 64 x 128 tiles (32x32x16), all 32 deep, 4 stages; a
+// MFMA), 128 x 128, 64 x 128 and 64 x 64 tiles (32x32x16), all 32 deep, 4
+// stages; a
 // problem is eligible for a configuration when its tile divides M and N and
 // K is a multiple of 128.
 int num_async_configs();
