@@ -207,6 +207,15 @@ int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t gr
  * 16-bit elements per row (row pitch padded by 8 elements). */
 int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col);
 
+/* Granule swizzle of the asynchronous kernels' LDS tiles: 16-byte granule c
+ * of tile row `row` is stored at granule c ^ tg_lds_swizzle(layout, row).
+ * layout 0: A (and B stored [N,K]), 64-byte rows of 32 k; 1: B stored
+ * [K,N], rows of 128 or more columns (256 bytes or more); 2: B stored
+ * [K,N], 64-column (128-byte) rows; 3: B stored [K,N] in the 256 x 256
+ * kernel on the 16x16x32 MFMA (512-byte rows).  Returns -1 for an unknown
+ * layout or a negative row. */
+int tg_lds_swizzle(int layout, int64_t row);
+
 /* Logical bounds predicate used for every global load and store: 1 if
  * (row, col) lies inside a rows x cols matrix, else 0 (never judged by the
  * linear offset). */

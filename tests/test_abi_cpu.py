@@ -230,6 +230,108 @@ def test_unpadded_layout_would_conflict():
     assert _banks_16b(addrs, 32) == 8
 
 
+# ---- XOR-swizzled LDS tiles of the asynchronous kernels.  Bank model of
+# gfx950: 64 four-byte banks (256 bytes per pass); a 128-bit read is served
+# 16 lanes per pass, a 64-bit (transposing) read 32 lanes per pass.  Each
+# pass below is the set of addresses the kernels' lanes read together; a
+# conflict-free pass touches every bank at most once.
+
+NBANKS = 64
+
+
+def _swz(layout, r):
+    v = tg.lib.tg_lds_swizzle(layout, r)
+    assert v >= 0
+    return v
+
+
+def _max_bank_load(pieces):
+    """pieces: (byte address, length) per lane; the most lanes on one bank."""
+    hits = {}
+    for lane, (a, n) in enumerate(pieces):
+        for w in range(n // 4):
+            hits.setdefault((a // 4 + w) % NBANKS, set()).add(lane)
+    return max(len(v) for v in hits.values())
+
+
+def _a_pass(base_row, gran, swizzle=True):
+    # 16 lanes read granule `gran` of rows base .. base+15 (64-byte rows)
+    return [((base_row + i) * 64 + 16 * (gran ^ (_swz(0, base_row + i) if swizzle else 0)), 16)
+            for i in range(16)]
+
+
+def _b_pass(layout, row_bytes, rows, cols, swizzle=True):
+    # lanes read 8 bytes (4 columns) at (row, col); granule col / 8, byte
+    # (col % 8) * 2 within it
+    out = []
+    for r, c in zip(rows, cols):
+        g = (c >> 3) ^ (_swz(layout, r) if swizzle else 0)
+        out.append((r * row_bytes + 16 * g + (c & 7) * 2, 8))
+    return out
+
+
+def _b32_lanes(kk, h, col0):
+    # 32x32x16 kernel, lanes 0..31 of a transposing B read: 16-lane group
+    # g = lane / 16, jj = lane % 16 -> row 16 kk + 4 h + jj / 4, column
+    # col0 + 16 g + 4 (jj % 4)
+    rows, cols = [], []
+    for lane in range(32):
+        g, jj = lane >> 4, lane & 15
+        rows.append(16 * kk + 4 * h + (jj >> 2))
+        cols.append(col0 + 16 * g + 4 * (jj & 3))
+    return rows, cols
+
+
+def _b16_lanes(q0, h, col0):
+    # 16x16x32 kernel, lanes of 16-lane groups q0 and q0 + 1 -> row 8 q + 4 h
+    # + jj / 4, column col0 + 4 (jj % 4)
+    rows, cols = [], []
+    for q in (q0, q0 + 1):
+        for jj in range(16):
+            rows.append(8 * q + 4 * h + (jj >> 2))
+            cols.append(col0 + 4 * (jj & 3))
+    return rows, cols
+
+
+@pytest.mark.parametrize("layout,granules", [(0, 4), (1, 16), (1, 32), (2, 8), (3, 32)])
+def test_swizzles_permute_each_row(layout, granules):
+    for r in range(64):
+        s = _swz(layout, r)
+        assert sorted(c ^ s for c in range(granules)) == list(range(granules))
+    assert tg.lib.tg_lds_swizzle(7, 0) == -1 and tg.lib.tg_lds_swizzle(0, -1) == -1
+
+
+def test_a_fragment_reads_are_bank_conflict_free():
+    for base in range(0, 256, 16):
+        for gran in range(4):
+            assert _max_bank_load(_a_pass(base, gran)) == 1
+    assert _max_bank_load(_a_pass(0, 0, swizzle=False)) == 4  # control
+
+
+@pytest.mark.parametrize("bn", [64, 128, 256])
+def test_b_transposing_reads_32x32_kernel_are_bank_conflict_free(bn):
+    layout = 2 if bn == 64 else 1
+    tj = bn // 64
+    for kk in range(2):
+        for h in range(2):
+            for wave_n in range(2):
+                for j in range(tj):
+                    rows, cols = _b32_lanes(kk, h, wave_n * 32 * tj + 32 * j)
+                    assert _max_bank_load(_b_pass(layout, 2 * bn, rows, cols)) == 1
+    rows, cols = _b32_lanes(0, 0, 0)
+    assert _max_bank_load(_b_pass(layout, 2 * bn, rows, cols, swizzle=False)) > 1  # control
+
+
+def test_b_transposing_reads_16x16_kernel_are_bank_conflict_free():
+    for q0 in (0, 2):
+        for h in range(2):
+            for col0 in range(0, 256, 16):
+                rows, cols = _b16_lanes(q0, h, col0)
+                assert _max_bank_load(_b_pass(3, 512, rows, cols)) == 1
+    rows, cols = _b16_lanes(0, 0, 0)
+    assert _max_bank_load(_b_pass(1, 512, rows, cols)) == 2  # without the row-bit-3 term
+
+
 def test_bounds_rule_matches_printed_example():
     g = json.load(open(os.path.join(GOLDEN, "oob_16x16.json")))
     rows, cols = g["shape"]

@@ -64,18 +64,6 @@ struct AsGeom {
     static_assert(BN >= 64, "B rows of at least 8 granules");
 };
 
-// B swizzle for rows of 16 or more granules: {0, 6, 10, 12}[r & 3] as a
-// nibble table (a shift, not a branch chain).  For 8-granule (128-byte) rows
-// the rows r and r + 2 share banks; flipping granule bit 2 on rows with bit
-// 1 set moves the four 64-byte row pieces one transposing read pass covers
-// (rows 4q .. 4q+3, 64 bytes each) onto four disjoint quarters of the
-// 256-byte bank window.
-template <int BN>
-__host__ __device__ constexpr int swz_b(int r)
-{
-    return BN >= 128 ? (0xCA60 >> (4 * (r & 3))) & 15 : 4 * ((r >> 1) & 1);
-}
-
 } // namespace
 
 // Split-K partial exchange of one workgroup (see the kernel below).  The
@@ -521,8 +509,6 @@ namespace {
 constexpr int A16_BM = 256, A16_BN = 256;
 constexpr int A16_A_BYTES = A16_BM * AS_BK * 2;             // [256][32] K-contiguous
 constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-contiguous
-
-__host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * ((r >> 3) & 1)); }
 
 template <int WN, bool BT>
 struct A16Geom {

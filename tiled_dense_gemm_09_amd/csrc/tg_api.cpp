@@ -18,6 +18,7 @@
 #include "../../include/tg.h"
 #include "tg_device.h"
 #include "tg_launch.h"
+#include "tg_pipeline.h"
 
 namespace {
 
@@ -546,6 +547,25 @@ int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t gr
 int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col)
 {
     return tg::lds_offset_bytes(cols, row, col);
+}
+
+int tg_lds_swizzle(int layout, int64_t row)
+{
+    if (row < 0)
+        return -1;
+    const int r = (int)(row & 0x7fffffff);
+    switch (layout) {
+    case 0:
+        return tg::swz_a(r);
+    case 1:
+        return tg::swz_b<128>(r);
+    case 2:
+        return tg::swz_b<64>(r);
+    case 3:
+        return tg::swz_b16(r);
+    default:
+        return -1;
+    }
 }
 
 int tg_in_bounds(int64_t rows, int64_t cols, int64_t row, int64_t col)

@@ -14,6 +14,24 @@ namespace tg {
 // 16-byte bank groups: row r covers groups 4 (r % 4) + (c ^ swz_a(r)).
 __host__ __device__ constexpr int swz_a(int r) { return (r >> 2) & 3; }
 
+// B swizzle for rows of 16 or more granules: {0, 6, 10, 12}[r & 3] as a
+// nibble table (a shift, not a branch chain).  For 8-granule (128-byte) rows
+// the rows r and r + 2 share banks; flipping granule bit 2 on rows with bit
+// 1 set moves the four 64-byte row pieces one transposing read pass covers
+// (rows 4q .. 4q+3, 64 bytes each) onto four disjoint quarters of the
+// 256-byte bank window.
+template <int BN>
+__host__ __device__ constexpr int swz_b(int r)
+{
+    return BN >= 128 ? (0xCA60 >> (4 * (r & 3))) & 15 : 4 * ((r >> 1) & 1);
+}
+
+// B swizzle of the 16x16x32 kernel (512-byte rows): one transposing read
+// pass covers rows 4q .. 4q+3 and 4q+8 .. 4q+11 (two 16-lane groups), 32
+// bytes each; the row-bit-3 term puts the second group's rows on the other
+// eight granule pairs, so the pass hits all 64 banks once.
+__host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * ((r >> 3) & 1)); }
+
 // Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
 // workgroup release fence, which waits for every outstanding direct-to-LDS
 // copy (they count as LDS writes) and would drain all stages each step.  Here

@@ -22,7 +22,7 @@ ACT = {"none": 0, "gelu_tanh": 1}
 
 SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_attention_fwd",
            "tg_gemm_qkv", "tg_status_string", "tg_last_kernel", "tg_schedule_tile",
-           "tg_lds_offset", "tg_in_bounds"]
+           "tg_lds_offset", "tg_lds_swizzle", "tg_in_bounds"]
 FP8 = {"e4m3": 0, "e5m2": 1}
 OP_N, OP_T = 0, 1
 
@@ -67,6 +67,8 @@ def _load():
     lib.tg_schedule_tile.restype = I
     lib.tg_lds_offset.argtypes = [L, L, L]
     lib.tg_lds_offset.restype = L
+    lib.tg_lds_swizzle.argtypes = [I, L]
+    lib.tg_lds_swizzle.restype = I
     lib.tg_in_bounds.argtypes = [L, L, L, L]
     lib.tg_in_bounds.restype = I
     return lib
