@@ -44,9 +44,11 @@
  *    units idle; tg_last_kernel() then ends in "_split..." or "_splitk<n>")
  *    keep a per-device workspace that is allocated on first use and grown
  *    when a larger one is needed (the only allocation the library makes;
- *    growing it synchronizes the device).  Calls that use it are ordered by
- *    their streams; two such calls on different streams of one device must
- *    not overlap.
+ *    growing it synchronizes the device and frees the old buffer, so a HIP
+ *    graph that captured such a call must not be replayed after a call
+ *    that grew the workspace).  Calls that use it are ordered by their
+ *    streams; two such calls on different streams of one device must not
+ *    overlap.
  */
 #ifndef TG_H
 #define TG_H
