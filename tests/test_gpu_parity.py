@@ -512,6 +512,49 @@ def test_split_k_qkv_and_more_than_one_wave(tg, monkeypatch):
         util.check_exact(outs[t], ref, "split-K qkv again [%d]" % t)
 
 
+def test_split_paths_replay_in_graphs(tg, monkeypatch):
+    # both split-K paths keep per-tile counters that each launch leaves at
+    # zero, so a captured call replays correctly with no reset; eager calls
+    # between the replays share the same counters and workspace
+    import torch
+    cases = [
+        (F16, 256, 320, 1024, {"TG_FORCE_CONFIG": "async_64x64x32_s4", "TG_SPLITK": "4"},
+         "async_64x64x32_s4_splitk4"),
+        (BF16, 16, 4096, 4096, {}, "skinny_stream"),
+    ]
+    for dt, M, N, K, env, kern in cases:
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        p = inputs.problem(dt, M, N, K, seed=200 + M, kind="int", bias=True, bias_kind="int")
+        A, B, bias = dev_problem(p)
+        C = torch.empty((M, N), dtype=torch.float16 if dt == F16 else torch.bfloat16,
+                        device="cuda")
+        tg.gemm(A, B, out=C, bias=bias)  # allocates the workspace outside the capture
+        torch.cuda.synchronize()
+        assert tg.last_kernel().startswith(kern), tg.last_kernel()
+        _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
+        util.check_exact(util.to_bits(C), ref, kern + " eager")
+        say("case graph replay", kern, M, N, K)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g):
+                tg.gemm(A, B, out=C, bias=bias)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(4):
+            C.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            util.check_exact(util.to_bits(C), ref, "%s replay %d" % (kern, i))
+            tg.gemm(A, B, out=C, bias=bias)
+            torch.cuda.synchronize()
+            util.check_exact(util.to_bits(C), ref, "%s eager after replay %d" % (kern, i))
+        for k in env:
+            monkeypatch.delenv(k)
+
+
 def test_split_k_off_and_unsplittable_k(tg, monkeypatch):
     # TG_SPLITK=1 keeps the forced tile unsplit; a K that no split count
     # divides into multiples of 128 (K = 128) runs unsplit too
