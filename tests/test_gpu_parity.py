@@ -301,6 +301,62 @@ def test_square_8192_sampled(tg):
     util.check_tol(BF16, bits[ii, jj], f64, "bf16_8192", ref_bits=rbits)
 
 
+def test_output_past_2_to_the_31_elements(tg):
+    # 98304 x 32768 outputs (3.2e9 elements, 6 GiB): element offsets pass
+    # 2^31 (and byte offsets 2^32), so any 32-bit index arithmetic in the
+    # 256 x 256 kernel would wrap; integer inputs and bias, sampled outputs
+    # on both sides of offset 2^31, bit-exact
+    import torch
+    M, N, K = 98304, 32768, 256
+    p = inputs.problem(F16, M, N, K, seed=210, kind="int", bias=True, bias_kind="int")
+    say("case large output", M, N, K)
+    A, B, bias = dev_problem(p)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    tg.gemm(A, B, out=C, bias=bias)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("async_256x256")
+    ii, jj = util.sample_indices(M, N, 1000, seed=211)
+    extra = [(65535, N - 1), (65536, 0), (65536, 1), (M - 1, N - 1), (M - 1, 0), (80000, 12345)]
+    ii = np.concatenate([ii, [e[0] for e in extra]]).astype(np.int64)
+    jj = np.concatenate([jj, [e[1] for e in extra]]).astype(np.int64)
+    got = util.to_bits(C[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
+    del C
+    _, ref = oracle.gemm_sample(F16, p["A"], p["B"], ii, jj, p["bias"])
+    util.check_exact(got, ref, "large output")
+
+
+def test_small_m_weight_past_2_to_the_31_elements(tg):
+    # W of 8192 x 393216 bf16 (3.2e9 elements, 6 GiB) streamed by the small-M
+    # kernel: row offsets k * ldb pass 2^31.  W is drawn on the device from a
+    # seeded generator (integers in {-2..2}); the oracle gets the same values
+    # of 64 sampled columns, including the last ones, and checks every row
+    import torch
+    M, N, K = 16, 393216, 8192
+    say("case small M, large W", M, N, K)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(220)
+    W = torch.randint(-2, 3, (K, N), generator=gen, dtype=torch.int8, device="cuda")
+    W = W.to(torch.bfloat16)
+    x = inputs.problem(BF16, M, 64, K, seed=221, kind="int")["A"]
+    X = util.to_dev(x, BF16)
+    Y = tg.gemm(X, W)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("skinny_stream")
+    rng = np.random.default_rng(222)
+    jj = np.unique(np.concatenate([rng.integers(0, N, 56), [0, 1, N - 256, N - 129, N - 8,
+                                                            N - 2, N - 1, 270000]]))
+    jt = torch.from_numpy(jj).cuda()
+    wsub = util.to_bits(W[:, jt].contiguous())
+    got = util.to_bits(Y[:, jt].contiguous())
+    del W
+    _, ref = oracle.gemm(BF16, x, wsub)
+    util.check_exact(got, ref, "small M, large W")
+
+
 def test_square_8192_integer_exact_sampled(tg):
     p = inputs.config_problem("bf16_8192", integer=True)
     bits, _ = run(tg, p)
