@@ -413,7 +413,7 @@ def test_ragged_shapes_with_poisoned_padding(tg, dt, M, N, K, integer):
     assert np.all(full[M:, :] == NAN_BITS[dt]), "wrote below the last row"
 
 
-def test_unaligned_operands_take_the_reported_fallback(tg):
+def test_unaligned_operands_take_the_reported_element_wise_kernel(tg):
     import torch
     dt = F16
     p = inputs.problem(dt, 70, 90, 50, seed=61, bias=True, act=inputs.ACT_GELU_TANH)
@@ -423,9 +423,59 @@ def test_unaligned_operands_take_the_reported_fallback(tg):
     bias = util.to_dev(p["bias"], dt)
     C = tg.gemm(A, B, bias=bias, act="gelu_tanh")
     torch.cuda.synchronize()
-    assert tg.last_kernel().startswith("generic_fma (unaligned")
+    assert tg.last_kernel().endswith("_unaligned"), tg.last_kernel()
     f64, rbits = oracle.gemm(dt, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
-    util.check_tol(dt, util.to_bits(C), f64, "generic", ref_bits=rbits)
+    util.check_tol(dt, util.to_bits(C), f64, "unaligned", ref_bits=rbits)
+    # B stored [N,K] with an odd pitch stays on the reported scalar fallback
+    Bt = util.to_dev(padded(np.ascontiguousarray(p["B"].T), 51, dt), dt)[:, :50]
+    C2 = tg.gemm(A, Bt.t(), bias=bias, act="gelu_tanh")
+    torch.cuda.synchronize()
+    assert tg.last_kernel().startswith("generic_fma (unaligned"), tg.last_kernel()
+    util.check_tol(dt, util.to_bits(C2), f64, "generic", ref_bits=rbits)
+
+
+UNALIGNED_CASES = [
+    # (dt, M, N, K, pitch pads of A, B, C, output offset in elements): odd
+    # and even pitches off the 8-element grid, an output starting one
+    # element into its buffer, every tile size of the chooser, a residual
+    # with its own (odd) pitch
+    (F16, 255, 257, 129, (1, 3, 5), 0),
+    (BF16, 1000, 1000, 1000, (0, 0, 0), 1),
+    (F16, 513, 1025, 777, (2, 6, 1), 0),
+    (BF16, 4095, 4095, 263, (0, 0, 0), 1),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,pads,off", UNALIGNED_CASES)
+def test_unaligned_pitches_integer_exact(tg, dt, M, N, K, pads, off):
+    # operands and output carved out of padded buffers whose pitches are not
+    # multiples of 8 elements, or an output that starts off the 16-byte
+    # grid; integer inputs, bias and residual: bit-exact.  Padding holds NaN
+    # so a read past the logical bounds shows.
+    import torch
+    p = inputs.problem(dt, M, N, K, seed=230 + M, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(231 + N), (M, N), "int", dt, 8.0)
+    lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
+    A = util.to_dev(padded(p["A"], lda, dt), dt)[:, :K]
+    B = util.to_dev(padded(p["B"], ldb, dt), dt)[:, :N]
+    bias = util.to_dev(p["bias"], dt)
+    Cbuf = util.to_dev(np.full(M * ldc + 1, NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[off:off + M * ldc].view(M, ldc)[:, :N]
+    Rd = util.to_dev(R, dt)
+    say("case unaligned", dt, M, N, K, "pitches", lda, ldb, ldc, "C offset", off)
+    tg.gemm(A, B, out=C, bias=bias, residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.endswith("_unaligned"), kern
+    _, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], R=R)
+    util.check_exact(util.to_bits(C), ref, "unaligned " + kern)
+    # nothing written outside the logical output
+    full = util.to_bits(Cbuf)
+    inside = np.zeros(full.shape, bool)
+    for i in range(M):
+        inside[off + i * ldc: off + i * ldc + N] = True
+    assert np.all(full[~inside] == NAN_BITS[dt]), "write outside the output"
 
 
 def test_k_zero_gives_activated_bias(tg):

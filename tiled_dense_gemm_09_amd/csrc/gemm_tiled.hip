@@ -36,14 +36,15 @@ namespace tg {
 
 namespace {
 
-template <bool EDGE>
+template <bool EDGE, bool UNAL = false>
 __device__ __forceinline__ u32x4 load_row_chunk(const unsigned short *base, int64_t ld, int rows,
                                                 int cols, int r, int c)
 {
     // 8 consecutive elements (r, c..c+7) of a rows x cols row-major matrix;
     // out-of-bounds elements read as zero.  EDGE = false: the caller has
-    // established that the whole chunk is in bounds.
-    if (!EDGE || (r < rows && c + 8 <= cols))
+    // established that the whole chunk is in bounds.  UNAL: the chunk need
+    // not be 16-byte aligned, so every element is loaded on its own.
+    if (!UNAL && (!EDGE || (r < rows && c + 8 <= cols)))
         return *reinterpret_cast<const u32x4 *>(base + (int64_t)r * ld + c);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < rows && c < cols) {
@@ -68,7 +69,7 @@ struct Stage {
     u32x4 b[CB][8];
 };
 
-template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE>
+template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE, bool UNAL>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
                                           const unsigned short *Bm, unsigned short *Cm,
                                           unsigned short *smem)
@@ -137,8 +138,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
         } else {
 #pragma unroll
             for (int i = 0; i < CA; ++i)
-                r.a[i] = load_row_chunk<true>(p.A, p.lda, M, K, m0 + a_row0 + i * (NT / KC),
-                                              kbase + a_kc * 8);
+                r.a[i] = load_row_chunk<true, UNAL>(p.A, p.lda, M, K,
+                                                    m0 + a_row0 + i * (NT / KC), kbase + a_kc * 8);
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int b = tid + j * NT;
@@ -146,8 +147,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
                     const int kb = b % KC, nb = b / KC;
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        r.b[j][i] = load_row_chunk<true>(Bm, p.ldb, K, N, kbase + kb * 8 + i,
-                                                         n0 + nb * 8);
+                        r.b[j][i] = load_row_chunk<true, UNAL>(Bm, p.ldb, K, N,
+                                                               kbase + kb * 8 + i, n0 + nb * 8);
                 }
             }
         }
@@ -274,9 +275,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
                     }
                     if (!EDGE || m < M) {
                         if (p.R != nullptr)
-                            add_residual<DT, 4>(p.R, p.ldr, m, n, N, v);
+                            add_residual<DT, 4, !UNAL>(p.R, p.ldr, m, n, N, v);
                         unsigned short *cp = Cm + (int64_t)m * p.ldc + n;
-                        if (!EDGE || n + 4 <= N) {
+                        if (!UNAL && (!EDGE || n + 4 <= N)) {
                             u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
                             *reinterpret_cast<u32x2 *>(cp) = o;
                         } else {
@@ -300,10 +301,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, int m0, int n0,
 // EDGE = false: every tile of the grid is interior (M, N, K are multiples of
 // the tile and the pitches fit 32-bit buffer offsets), so no predicate is
 // evaluated anywhere.  EDGE = true: every load and store is bounds-checked.
-// The host picks one or the other per launch; keeping them in separate
-// kernels keeps the register allocation of the fast path unaffected by the
-// predicated one.
-template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE>
+// UNAL (with EDGE): operands, pitches or the output are not 16-byte aligned
+// (only 2-byte), so every global load and store moves one element; the MFMA
+// loop and the LDS layout are unchanged.  The host picks the variant per
+// launch; keeping them in separate kernels keeps the register allocation of
+// the fast path unaffected by the predicated ones.
+template <int DT, int BM, int BN, int BK, int WM, int WN, int ACT, bool EDGE, bool UNAL>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_tiled_kernel(GemmArgs p, int tiles_m,
                                                                    int tiles_n, int group_m)
 {
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_tiled_kernel(GemmArgs p,
     const int m0 = tc.tm * BM, n0 = tc.tn * BN;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    tile_body<DT, BM, BN, BK, WM, WN, ACT, EDGE>(p, m0, n0, Bm, Cm, smem);
+    tile_body<DT, BM, BN, BK, WM, WN, ACT, EDGE, UNAL>(p, m0, n0, Bm, Cm, smem);
 }
 
 // ------------------------------------------------------------------ configs
@@ -329,6 +332,16 @@ static const TileConfig kConfigs[] = {
 int num_tile_configs() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
 const TileConfig &tile_config(int i) { return kConfigs[i]; }
 
+bool tiled_unaligned(const GemmArgs &a)
+{
+    auto mis = [](const void *q) { return ((uintptr_t)q & 15u) != 0; };
+    bool u = a.lda % 8 != 0 || a.ldb % 8 != 0 || a.ldc % 8 != 0 || mis(a.A) ||
+             (a.R != nullptr && (a.ldr % 8 != 0 || mis(a.R)));
+    for (int t = 0; t < a.n_mat; ++t)
+        u = u || mis(a.B[t]) || mis(a.C[t]);
+    return u;
+}
+
 template <int DT, int BM, int BN, int BK, int WM, int WN>
 static hipError_t launch_cfg(int act, const GemmArgs &a, int group_m, hipStream_t s)
 {
@@ -336,21 +349,26 @@ static hipError_t launch_cfg(int act, const GemmArgs &a, int group_m, hipStream_
     const int tiles_n = (a.N + BN - 1) / BN;
     const int blocks = tiles_m * tiles_n * a.n_mat;
     dim3 grid(blocks), block(64 * WM * WN);
-    const bool interior = a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0 &&
+    const bool unal = tiled_unaligned(a);
+    const bool interior = !unal && a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0 &&
                           a.lda < (1 << 22) && a.ldb < (1 << 22);
-#define TG_LAUNCH(ACT_, EDGE_)                                                                   \
-    hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_, EDGE_>), grid, block, 0, \
-                       s, a, tiles_m, tiles_n, group_m)
+#define TG_LAUNCH(ACT_, EDGE_, UNAL_)                                                            \
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, BM, BN, BK, WM, WN, ACT_, EDGE_, UNAL_>), grid,    \
+                       block, 0, s, a, tiles_m, tiles_n, group_m)
     if (act == ACT_GELU) {
-        if (interior)
-            TG_LAUNCH(ACT_GELU, false);
+        if (unal)
+            TG_LAUNCH(ACT_GELU, true, true);
+        else if (interior)
+            TG_LAUNCH(ACT_GELU, false, false);
         else
-            TG_LAUNCH(ACT_GELU, true);
+            TG_LAUNCH(ACT_GELU, true, false);
     } else {
-        if (interior)
-            TG_LAUNCH(ACT_NONE, false);
+        if (unal)
+            TG_LAUNCH(ACT_NONE, true, true);
+        else if (interior)
+            TG_LAUNCH(ACT_NONE, false, false);
         else
-            TG_LAUNCH(ACT_NONE, true);
+            TG_LAUNCH(ACT_NONE, true, false);
     }
 #undef TG_LAUNCH
     return hipGetLastError();

@@ -239,7 +239,22 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     (void)hipGetLastError();
     hipError_t err;
     const bool trans_async = b_trans && fast && !force_generic && choose_async(a, force) >= 0;
-    if (!fast || force_generic || (b_trans && !trans_async)) {
+    // Pitches or pointers off the 16-byte grid but every pointer 2-byte
+    // aligned: the tiled MFMA kernel with element-wise loads and stores.
+    bool even = ((uintptr_t)A & 1u) == 0;
+    for (int t = 0; t < n_mat; ++t)
+        even = even && ((uintptr_t)C[t] & 1u) == 0 && ((uintptr_t)B[t] & 1u) == 0;
+    const bool unal_tiled = !fast && even && !b_trans && K > 0 && !force_generic;
+    if (unal_tiled) {
+        const int cfg = choose_config(M, N, n_mat);
+        const tg::TileConfig &c = tg::tile_config(cfg);
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * n_mat;
+        if (tiles >= kMaxDim)
+            return TG_ERROR_NOT_SUPPORTED;
+        const int group_m = env_int("TG_GROUP_M", 4);
+        err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
+        set_last(c.name, "_unaligned");
+    } else if (!fast || force_generic || (b_trans && !trans_async)) {
         err = tg::launch_generic(kdt, kact, a, s);
         set_last(!fast            ? "generic_fma (unaligned operands)"
                  : force_generic ? "generic_fma (forced)"

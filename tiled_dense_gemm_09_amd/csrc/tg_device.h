@@ -165,12 +165,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
 // are skipped; when all CNT columns are in range and CNT is a multiple of 4
 // the row segment is read with 8-byte loads (n a multiple of 4, R 16-byte
 // aligned and ldr a multiple of 8 on every path that passes CNT >= 4).
-template <int DT, int CNT>
+// VEC = false: element-wise loads only (R or its pitch not 8-byte aligned)
+template <int DT, int CNT, bool VEC = true>
 __device__ __forceinline__ void add_residual(const unsigned short *R, int64_t ldr, int64_t m,
                                              int n, int N, float *v)
 {
     const unsigned short *rp = R + m * ldr + n;
-    if (CNT % 4 == 0 && n + CNT <= N) {
+    if (VEC && CNT % 4 == 0 && n + CNT <= N) {
 #pragma unroll
         for (int q = 0; q < CNT / 4; ++q) {
             const u32x2 w = *reinterpret_cast<const u32x2 *>(rp + 4 * q);

@@ -39,6 +39,10 @@ const TileConfig &tile_config(int i);
 // Launchers; each returns the hipError_t of the launch.
 hipError_t launch_tiled(int cfg, int dt, int act, const GemmArgs &a, int group_m,
                         hipStream_t stream);
+// True when the tiled kernel must load and store element by element: a
+// pointer not 16-byte aligned or a pitch not a multiple of 8 elements.  It
+// still needs 2-byte aligned pointers and B stored [K,N].
+bool tiled_unaligned(const GemmArgs &a);
 hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream);
 
 // Asynchronous-copy MFMA kernel: 256 x 256 tiles (16x16x32 or 32x32x16
