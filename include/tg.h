@@ -34,8 +34,10 @@
  *    Bounds are logical: element (i, k) of A is read only if i < M and k < K,
  *    whatever lies in the padding between K and lda.
  *  - Fast path: 16-byte aligned pointers and pitches that are multiples of
- *    8 elements take the MFMA kernels.  Anything else runs a slower,
- *    correct fallback kernel; the choice is never silent: tg_last_kernel()
+ *    8 elements take the MFMA kernels.  Other 2-byte aligned operands (B
+ *    stored [K,N]) take an MFMA kernel that loads and stores element by
+ *    element; anything else runs a slower, correct scalar fallback.  The
+ *    choice is never silent: tg_last_kernel()
  *    names the kernel and tile configuration the last call on this host
  *    thread launched (and TG_LOG=1 in the environment prints it).
  *  - Thread safety: entry points may be called from several host threads.
