@@ -677,6 +677,77 @@ def test_split_k_off_and_unsplittable_k(tg, monkeypatch):
     torch.cuda.synchronize()
 
 
+# ---------------- partial last row tile on the 256 x 256 (16x16x32) kernels
+
+RAGGED_M_CASES = [
+    # (dt, M, N, K, config): the last row tile holds 1, 131, 184 and 255 rows
+    # (at most M/8 padding rows), both wave rows partly or wholly outside
+    (F16, 2049, 512, 256, "async_256x256x32_s4_mfma16"),
+    (BF16, 1923, 768, 384, "async_256x256x32_s4_mfma16"),
+    (F16, 3000, 512, 512, "async_256x256x32_s4_mfma16"),
+    (BF16, 2303, 256, 256, "async_256x256x32_s4_mfma16_w8"),
+]
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,cfg", RAGGED_M_CASES)
+def test_partial_row_tile_integer_exact(tg, monkeypatch, dt, M, N, K, cfg, trans_b):
+    # integer operands, bias and residual: bit-exact; the output sits in a
+    # buffer with 8 extra rows of NaN that must stay untouched
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", cfg)
+    p = inputs.problem(dt, M, N, K, seed=240 + M, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(241 + N), (M, N), "int", dt, 8.0)
+    A = util.to_dev(p["A"], dt)
+    Bd = util.to_dev(np.ascontiguousarray(p["B"].T) if trans_b else p["B"], dt)
+    b = Bd.t() if trans_b else Bd
+    bias = util.to_dev(p["bias"], dt)
+    Cbuf = util.to_dev(np.full((M + 8, N), NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[:M]
+    say("case partial row tile", dt, M, N, K, cfg, "B[N,K]" if trans_b else "B[K,N]")
+    tg.gemm(A, b, out=C, bias=bias, residual=util.to_dev(R, dt))
+    torch.cuda.synchronize()
+    assert tg.last_kernel() == cfg, tg.last_kernel()
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    full = util.to_bits(Cbuf)
+    util.check_exact(full[:M], ref, "partial row tile")
+    assert np.all(full[M:] == NAN_BITS[dt]), "rows past M were written"
+
+
+def test_partial_row_tile_gelu_random_and_qkv(tg, monkeypatch):
+    # M = 1200: 5 row tiles, 80 padding rows (at most M / 8 are allowed)
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_256x256x32_s4_mfma16")
+    p = inputs.problem(BF16, 1200, 512, 640, seed=250, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.2, b_scale=0.2)
+    say("case partial row tile gelu 1200x512x640")
+    bits, kern = run(tg, p)
+    assert kern == "async_256x256x32_s4_mfma16"
+    f64, rbits = oracle.gemm(BF16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(BF16, bits, f64, "partial row tile gelu", ref_bits=rbits)
+    q = inputs.qkv_problem(BF16, 1200, 256, 256, seed=251, kind="int")
+    say("case partial row tile qkv 1200x256x256 x3")
+    _, _, outs = run_qkv(tg, q)
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16"
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "partial row tile qkv [%d]" % t)
+
+
+def test_projection_with_ragged_token_count(tg):
+    # X[3000, 4096] . W[4096, 11008]: a token count off the tile grid with
+    # model dimensions on it takes the 256 x 256 kernel by itself
+    import torch
+    p = inputs.problem(BF16, 3000, 11008, 4096, seed=252, kind="normal", b_scale=1 / 64)
+    say("case projection 3000x11008x4096")
+    bits, kern = run(tg, p)
+    assert kern == "async_256x256x32_s4_mfma16", kern
+    ii, jj = util.sample_indices(3000, 11008, 1500, seed=253)
+    f64, rbits = oracle.gemm_sample(BF16, p["A"], p["B"], ii, jj)
+    util.check_tol(BF16, bits[ii, jj], f64, "projection", ref_bits=rbits)
+
+
 # ------------------------------- extended epilogue: residual and B stored [N,K]
 
 def run_ex(tg, p, trans_b, R=None, Rin_place=False):

@@ -537,8 +537,11 @@ __device__ __forceinline__ int ep_swz(int r)
 template <int DT, int ACT, bool HR, int NJ>
 __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], unsigned char *ep,
                                                     int lane, unsigned short *C, int64_t ldc,
-                                                    const unsigned short *R, int64_t ldr)
+                                                    const unsigned short *R, int64_t ldr,
+                                                    int rows)
 {
+    // rows: output rows of this wave tile inside the matrix (>= 128: all);
+    // rows past it are neither read from R nor stored
     // the rounded 128 x (16 NJ) wave tile goes to the wave's own LDS region
     // (rows of G = 2 NJ granules, granule c of row r at c ^ ep_swz(r)), then
     // each store writes 16 bytes per lane, whole row segments
@@ -551,7 +554,8 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
         if constexpr (HR) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                rr[j] = *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q);
+                rr[j] = r < rows ? *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q)
+                                 : u32x2{0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -574,7 +578,8 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
         const int r = (64 / G) * t + lane / G;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) +
                                                          (((lane % G) ^ ep_swz<G>(r)) * 16));
-        *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
+        if (r < rows)
+            *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
     }
 }
 
@@ -621,7 +626,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     for (int c = 0; c < CA; ++c) {
         const int q = wave * CA + c;
         const int ra = 16 * q + (lane >> 2);
-        ga[c] = p.A + (int64_t)(m0 + ra) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
+        // rows past M (a last row tile that M does not fill) read row M-1:
+        // every copy stays inside A, and those rows only reach outputs that
+        // are never stored
+        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
         if constexpr (BT) {
             gb[c] = Bm + (int64_t)(n0 + ra) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8;
         } else {
@@ -785,11 +793,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
                         (wave % PER_STAGE) * Gm::EP_BYTES;
     const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * Gm::WCOLS;
     unsigned short *cw = Cm + cm * p.ldc + cn;
+    const int rows = (int)min((int64_t)128, (int64_t)p.M - cm);
     if (p.R != nullptr)
         restaged_epilogue16<DT, ACT, true, NJ>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
-                                               p.ldr);
+                                               p.ldr, rows);
     else
-        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0);
+        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows);
 }
 
 namespace {
@@ -815,9 +824,19 @@ const char *async_config_name(int cfg) { return kAsyncConfigs[cfg].name; }
 int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
 int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
 
+int async_tiles_m(const GemmArgs &a, int cfg)
+{
+    return (a.M + async_tile_m(cfg) - 1) / async_tile_m(cfg);
+}
+
 bool async_eligible(const GemmArgs &a, int cfg)
 {
-    return a.M % async_tile_m(cfg) == 0 && a.N % async_tile_n(cfg) == 0 &&
+    // The 256 x 256 kernels on the 16x16x32 MFMA take an M that is not a
+    // multiple of 256 when the last row tile wastes at most M / 8 rows.
+    const int pad = async_tiles_m(a, cfg) * async_tile_m(cfg) - a.M;
+    const bool m_ok = a.M % async_tile_m(cfg) == 0 ||
+                      (kAsyncConfigs[cfg].mfma16 && a.M > 256 && 8 * pad <= a.M);
+    return m_ok && a.N % async_tile_n(cfg) == 0 &&
            a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
@@ -827,7 +846,7 @@ int plan_async_splits(const GemmArgs &a, int cfg, int want)
     const AsyncConfig &c = kAsyncConfigs[cfg];
     if (c.mfma16 || c.ti * c.tj > 4 || want == 1)
         return 1;
-    const int64_t tiles = (int64_t)(a.M / async_tile_m(cfg)) * (a.N / async_tile_n(cfg)) * a.n_mat;
+    const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * (a.N / async_tile_n(cfg)) * a.n_mat;
     if (tiles > kMaxSplitTiles || (want <= 0 && tiles >= 240))
         return 1;
     // enough workgroups for one wave of the 256 CUs, at most 8 splits, each
@@ -849,7 +868,7 @@ size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,
                         float *ws, int *counters, hipStream_t s)
 {
-    const int tiles_m = a.M / async_tile_m(cfg), tiles_n = a.N / async_tile_n(cfg);
+    const int tiles_m = async_tiles_m(a, cfg), tiles_n = a.N / async_tile_n(cfg);
     if (splits < 1 || (splits > 1 && (plan_async_splits(a, cfg, splits) != splits ||
                                       ws == nullptr || counters == nullptr)))
         return hipErrorInvalidValue;

@@ -49,12 +49,16 @@ hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream
 // MFMA), 128 x 128, 64 x 128 and 64 x 64 tiles (32x32x16), all 32 deep, 4
 // stages; a
 // problem is eligible for a configuration when its tile divides M and N and
-// K is a multiple of 128.
+// K is a multiple of 128 (the 16x16x32 kernels also take a partial last row
+// tile).
 int num_async_configs();
 const char *async_config_name(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);
+// Row tiles of a problem: M / tile, or its ceiling where the configuration
+// takes a partial last row tile (the 256 x 256 kernels on the 16x16x32 MFMA).
+int async_tiles_m(const GemmArgs &a, int cfg);
 // Split-K for under-filled grids (128 x 128 and 64 x 128 tiles only, at most
 // kMaxSplitTiles tiles): the number of K splits for the configuration, 1 for
 // none.  want > 1 asks for that many (fewer when K does not divide), want
