@@ -1090,6 +1090,12 @@ def test_dispatch_choices(tg, monkeypatch):
     e = torch.zeros((1024, 2048), dtype=torch.float16, device="cuda")
     tg.gemm(e, c)
     assert tg.last_kernel() == "async_64x128x32_s4"
+    # a partial row tile with fewer than 240 tiles: the 4-wave 256 x 256
+    # kernel, never the forced-only 8-wave variant
+    f = torch.zeros((2049, 4096), dtype=torch.float16, device="cuda")
+    g = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
+    tg.gemm(f, g)
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
     monkeypatch.setenv("TG_SPLITK", "0")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x64x32_s4"

@@ -805,22 +805,24 @@ namespace {
 struct AsyncConfig {
     int ti, tj;
     int mfma16; // 256 x 256 on the 16x16x32 MFMA with this many waves; 0: 32x32x16
+    bool forced_only; // taken only when TG_FORCE_CONFIG names it
     const char *name;
 };
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
-    {4, 4, 4, "async_256x256x32_s4_mfma16"},
-    {4, 4, 8, "async_256x256x32_s4_mfma16_w8"}, // forced only: never ahead of the 4-wave kernel
-    {4, 4, 0, "async_256x256x32_s4"},
-    {2, 2, 0, "async_128x128x32_s4"},
-    {1, 2, 0, "async_64x128x32_s4"},
-    {1, 1, 0, "async_64x64x32_s4"},
+    {4, 4, 4, false, "async_256x256x32_s4_mfma16"},
+    {4, 4, 8, true, "async_256x256x32_s4_mfma16_w8"}, // never ahead of the 4-wave kernel
+    {4, 4, 0, false, "async_256x256x32_s4"},
+    {2, 2, 0, false, "async_128x128x32_s4"},
+    {1, 2, 0, false, "async_64x128x32_s4"},
+    {1, 1, 0, false, "async_64x64x32_s4"},
 };
 } // namespace
 
 int num_async_configs() { return (int)(sizeof kAsyncConfigs / sizeof kAsyncConfigs[0]); }
 const char *async_config_name(int cfg) { return kAsyncConfigs[cfg].name; }
+bool async_forced_only(int cfg) { return kAsyncConfigs[cfg].forced_only; }
 int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
 int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
 

@@ -144,7 +144,7 @@ int choose_async(const tg::GemmArgs &a, const char *force)
     }
     int best = -1;
     for (int i = 0; i < n; ++i) {
-        if (!tg::async_eligible(a, i))
+        if (tg::async_forced_only(i) || !tg::async_eligible(a, i))
             continue;
         const int64_t tiles =
             (int64_t)tg::async_tiles_m(a, i) * (a.N / tg::async_tile_n(i)) * a.n_mat;

@@ -53,6 +53,8 @@ hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream
 // tile).
 int num_async_configs();
 const char *async_config_name(int cfg);
+// taken only when TG_FORCE_CONFIG names it
+bool async_forced_only(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);
