@@ -549,6 +549,7 @@ SPLIT_CASES = [
     (BF16, 192, 256, 512, "async_64x128x32_s4", 4),
     (F16, 128, 128, 384, "async_64x128x32_s4", 3),
     (BF16, 192, 320, 1024, "async_64x64x32_s4", 8),
+    (F16, 1000, 384, 1024, "async_128x128x32_s4", 4),   # partial last row tile
 ]
 
 
@@ -680,12 +681,18 @@ def test_split_k_off_and_unsplittable_k(tg, monkeypatch):
 # ---------------- partial last row tile on the 256 x 256 (16x16x32) kernels
 
 RAGGED_M_CASES = [
-    # (dt, M, N, K, config): the last row tile holds 1, 131, 184 and 255 rows
-    # (at most M/8 padding rows), both wave rows partly or wholly outside
+    # (dt, M, N, K, config): on the 16x16x32 kernels the last row tile holds
+    # 1, 131, 184 and 255 rows (at most M/8 padding rows), both wave rows
+    # partly or wholly outside
     (F16, 2049, 512, 256, "async_256x256x32_s4_mfma16"),
     (BF16, 1923, 768, 384, "async_256x256x32_s4_mfma16"),
     (F16, 3000, 512, 512, "async_256x256x32_s4_mfma16"),
     (BF16, 2303, 256, 256, "async_256x256x32_s4_mfma16_w8"),
+    # the 32x32x16 kernel: last row tiles of 152, 104, 24 and 30 rows
+    (BF16, 2200, 256, 256, "async_256x256x32_s4"),
+    (F16, 1000, 384, 256, "async_128x128x32_s4"),
+    (BF16, 600, 256, 384, "async_64x128x32_s4"),
+    (F16, 350, 320, 256, "async_64x64x32_s4"),
 ]
 
 
@@ -1090,12 +1097,12 @@ def test_dispatch_choices(tg, monkeypatch):
     e = torch.zeros((1024, 2048), dtype=torch.float16, device="cuda")
     tg.gemm(e, c)
     assert tg.last_kernel() == "async_64x128x32_s4"
-    # a partial row tile with fewer than 240 tiles: the 4-wave 256 x 256
-    # kernel, never the forced-only 8-wave variant
+    # partial last row tiles: an asynchronous kernel (128 x 128 tiles fill a
+    # wave at 2049 rows), never the forced-only 8-wave variant
     f = torch.zeros((2049, 4096), dtype=torch.float16, device="cuda")
     g = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
     tg.gemm(f, g)
-    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
+    assert tg.last_kernel() == "async_128x128x32_s4", tg.last_kernel()
     monkeypatch.setenv("TG_SPLITK", "0")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x64x32_s4"

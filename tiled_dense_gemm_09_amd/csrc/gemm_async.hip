@@ -224,7 +224,9 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         const int q = wave * TI + i;
         const int ra = 16 * q + (lane >> 2);
         const int ca = (lane & 3) ^ swz_a(ra);
-        ga[i] = p.A + (int64_t)(m0 + ra) * p.lda + k0 + ca * 8;
+        // rows past M (partial last row tile) read row M-1; their outputs
+        // are never stored
+        ga[i] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + k0 + ca * 8;
     }
 #pragma unroll
     for (int i = 0; i < TJ; ++i) {
@@ -459,11 +461,12 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     unsigned char *ep = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
     const int64_t cm = m0 + wave_m * 32 * TI, cn = n0 + wave_n * 32 * TJ;
     unsigned short *cw = Cm + cm * p.ldc + cn;
+    const int rows = (int)min((int64_t)(32 * TI), (int64_t)p.M - cm);
     if (p.R != nullptr)
         restaged_epilogue<DT, ACT, TI, TJ, true>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
-                                                 p.ldr);
+                                                 p.ldr, rows);
     else
-        restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0);
+        restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -833,11 +836,10 @@ int async_tiles_m(const GemmArgs &a, int cfg)
 
 bool async_eligible(const GemmArgs &a, int cfg)
 {
-    // The 256 x 256 kernels on the 16x16x32 MFMA take an M that is not a
-    // multiple of 256 when the last row tile wastes at most M / 8 rows.
+    // An M that is not a multiple of the tile is taken when the partial
+    // last row tile wastes at most M / 8 rows.
     const int pad = async_tiles_m(a, cfg) * async_tile_m(cfg) - a.M;
-    const bool m_ok = a.M % async_tile_m(cfg) == 0 ||
-                      (kAsyncConfigs[cfg].mfma16 && a.M > 256 && 8 * pad <= a.M);
+    const bool m_ok = a.M % async_tile_m(cfg) == 0 || (a.M > async_tile_m(cfg) && 8 * pad <= a.M);
     return m_ok && a.N % async_tile_n(cfg) == 0 &&
            a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
@@ -863,8 +865,8 @@ int plan_async_splits(const GemmArgs &a, int cfg, int want)
 
 size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 {
-    return (size_t)splits * ((size_t)a.M / async_tile_m(cfg)) * (a.N / async_tile_n(cfg)) *
-           a.n_mat * async_tile_m(cfg) * async_tile_n(cfg);
+    return (size_t)splits * (size_t)async_tiles_m(a, cfg) * (a.N / async_tile_n(cfg)) * a.n_mat *
+           async_tile_m(cfg) * async_tile_n(cfg);
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,

@@ -48,9 +48,9 @@ hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream
 // Asynchronous-copy MFMA kernel: 256 x 256 tiles (16x16x32 or 32x32x16
 // MFMA), 128 x 128, 64 x 128 and 64 x 64 tiles (32x32x16), all 32 deep, 4
 // stages; a
-// problem is eligible for a configuration when its tile divides M and N and
-// K is a multiple of 128 (the 16x16x32 kernels also take a partial last row
-// tile).
+// problem is eligible for a configuration when its tile width divides N, K
+// is a multiple of 128, and M is a multiple of the tile height or leaves a
+// partial last row tile of at most M / 8 padding rows.
 int num_async_configs();
 const char *async_config_name(int cfg);
 // taken only when TG_FORCE_CONFIG names it
@@ -58,8 +58,8 @@ bool async_forced_only(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);
-// Row tiles of a problem: M / tile, or its ceiling where the configuration
-// takes a partial last row tile (the 256 x 256 kernels on the 16x16x32 MFMA).
+// Row tiles of a problem: the ceiling of M / tile (a partial last row tile
+// counts as a tile).
 int async_tiles_m(const GemmArgs &a, int cfg);
 // Split-K for under-filled grids (128 x 128 and 64 x 128 tiles only, at most
 // kMaxSplitTiles tiles): the number of K splits for the configuration, 1 for
