@@ -722,6 +722,64 @@ def test_partial_row_tile_integer_exact(tg, monkeypatch, dt, M, N, K, cfg, trans
     assert np.all(full[M:] == NAN_BITS[dt]), "rows past M were written"
 
 
+RAGGED_N_CASES = [
+    # (dt, M, N, K, config): N a multiple of 8 leaving a partial last column
+    # tile of at most N/8 padding columns; the last case is ragged in M too
+    (F16, 512, 2000, 256, "async_256x256x32_s4_mfma16"),
+    (BF16, 256, 2200, 384, "async_256x256x32_s4"),
+    (F16, 256, 1000, 256, "async_128x128x32_s4"),
+    (BF16, 192, 600, 512, "async_64x128x32_s4"),
+    (F16, 128, 360, 256, "async_64x64x32_s4"),
+    (BF16, 1000, 1000, 256, "async_128x128x32_s4"),
+]
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,cfg", RAGGED_N_CASES)
+def test_partial_column_tile_integer_exact(tg, monkeypatch, dt, M, N, K, cfg, trans_b):
+    # integer operands, bias and residual: bit-exact; the output's rows carry
+    # 8 extra columns of NaN that must stay untouched
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", cfg)
+    p = inputs.problem(dt, M, N, K, seed=260 + N, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(261 + M), (M, N), "int", dt, 8.0)
+    A = util.to_dev(p["A"], dt)
+    Bd = util.to_dev(np.ascontiguousarray(p["B"].T) if trans_b else p["B"], dt)
+    b = Bd.t() if trans_b else Bd
+    bias = util.to_dev(p["bias"], dt)
+    Cbuf = util.to_dev(np.full((M, N + 8), NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[:, :N]
+    say("case partial column tile", dt, M, N, K, cfg, "B[N,K]" if trans_b else "B[K,N]")
+    tg.gemm(A, b, out=C, bias=bias, residual=util.to_dev(R, dt))
+    torch.cuda.synchronize()
+    assert tg.last_kernel() == cfg, tg.last_kernel()
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    full = util.to_bits(Cbuf)
+    util.check_exact(full[:, :N], ref, "partial column tile")
+    assert np.all(full[:, N:] == NAN_BITS[dt]), "columns past N were written"
+
+
+def test_partial_column_tile_split_k_and_qkv(tg, monkeypatch):
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_128x128x32_s4")
+    monkeypatch.setenv("TG_SPLITK", "2")
+    p = inputs.problem(BF16, 256, 1000, 1024, seed=270, kind="int", bias=True, bias_kind="int")
+    say("case partial column tile split-K 256x1000x1024")
+    bits, kern = run(tg, p)
+    assert kern == "async_128x128x32_s4_splitk2", kern
+    _, ref = oracle.gemm(BF16, p["A"], p["B"], p["bias"])
+    util.check_exact(bits, ref, "partial column tile split-K")
+    monkeypatch.delenv("TG_SPLITK")
+    q = inputs.qkv_problem(BF16, 512, 1000, 256, seed=271, kind="int")
+    say("case partial column tile qkv 512x1000x256 x3")
+    _, _, outs = run_qkv(tg, q)
+    assert tg.last_kernel() == "async_128x128x32_s4"
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "partial column tile qkv [%d]" % t)
+
+
 def test_partial_row_tile_gelu_random_and_qkv(tg, monkeypatch):
     # M = 1200: 5 row tiles, 80 padding rows (at most M / 8 are allowed)
     import torch

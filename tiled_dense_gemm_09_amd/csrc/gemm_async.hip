@@ -234,11 +234,13 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         if constexpr (BT) {
             const int rb = 16 * q + (lane >> 2);
             const int cb = (lane & 3) ^ swz_a(rb);
-            gb[i] = Bm + (int64_t)(n0 + rb) * p.ldb + k0 + cb * 8;
+            gb[i] = Bm + (int64_t)min(n0 + rb, p.N - 1) * p.ldb + k0 + cb * 8;
         } else {
             const int rb = G::B_ROWS_PER_COPY * q + lane / G::B_GRANULES;
             const int cb = (lane % G::B_GRANULES) ^ swz_b<G::BN>(rb);
-            gb[i] = Bm + (int64_t)(k0 + rb) * p.ldb + n0 + cb * 8;
+            // columns past N (partial last column tile) read the last 8;
+            // their outputs are never stored
+            gb[i] = Bm + (int64_t)(k0 + rb) * p.ldb + min(n0 + cb * 8, p.N - 8);
         }
     }
     const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb; // per K-step
@@ -279,8 +281,9 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const u32x2 braw = *reinterpret_cast<const u32x2 *>(
-                    p.bias + n0 + wave_n * 32 * TJ + j * 32 + g * 8 + (lane >> 5) * 4);
+                const int bc = n0 + wave_n * 32 * TJ + j * 32 + g * 8 + (lane >> 5) * 4;
+                const u32x2 braw = bc < p.N ? *reinterpret_cast<const u32x2 *>(p.bias + bc)
+                                            : u32x2{0u, 0u};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float b = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
@@ -462,11 +465,13 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
     const int64_t cm = m0 + wave_m * 32 * TI, cn = n0 + wave_n * 32 * TJ;
     unsigned short *cw = Cm + cm * p.ldc + cn;
     const int rows = (int)min((int64_t)(32 * TI), (int64_t)p.M - cm);
+    const int cols = (int)min((int64_t)(32 * TJ), (int64_t)p.N - cn);
     if (p.R != nullptr)
         restaged_epilogue<DT, ACT, TI, TJ, true>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
-                                                 p.ldr, rows);
+                                                 p.ldr, rows, cols);
     else
-        restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows);
+        restaged_epilogue<DT, ACT, TI, TJ, false>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows,
+                                                  cols);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,10 +546,11 @@ template <int DT, int ACT, bool HR, int NJ>
 __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], unsigned char *ep,
                                                     int lane, unsigned short *C, int64_t ldc,
                                                     const unsigned short *R, int64_t ldr,
-                                                    int rows)
+                                                    int rows, int cols)
 {
-    // rows: output rows of this wave tile inside the matrix (>= 128: all);
-    // rows past it are neither read from R nor stored
+    // rows, cols: output rows and columns of this wave tile inside the
+    // matrix (a multiple of 8 columns); the rest are neither read from R nor
+    // stored
     // the rounded 128 x (16 NJ) wave tile goes to the wave's own LDS region
     // (rows of G = 2 NJ granules, granule c of row r at c ^ ep_swz(r)), then
     // each store writes 16 bytes per lane, whole row segments
@@ -557,8 +563,9 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
         if constexpr (HR) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                rr[j] = r < rows ? *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q)
-                                 : u32x2{0u, 0u};
+                rr[j] = r < rows && 16 * j + 4 * q < cols
+                            ? *reinterpret_cast<const u32x2 *>(R + (int64_t)r * ldr + 16 * j + 4 * q)
+                            : u32x2{0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -581,7 +588,7 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
         const int r = (64 / G) * t + lane / G;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) +
                                                          (((lane % G) ^ ep_swz<G>(r)) * 16));
-        if (r < rows)
+        if (r < rows && (lane % G) * 8 < cols)
             *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
     }
 }
@@ -634,10 +641,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
         // are never stored
         ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
         if constexpr (BT) {
-            gb[c] = Bm + (int64_t)(n0 + ra) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8;
+            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8;
         } else {
             const int rb = 2 * q + (lane >> 5);
-            gb[c] = Bm + (int64_t)rb * p.ldb + n0 + ((lane & 31) ^ swz_b16(rb)) * 8;
+            gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8);
         }
     }
     const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
@@ -666,8 +673,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     if (p.bias != nullptr) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const u32x2 braw = *reinterpret_cast<const u32x2 *>(p.bias + n0 + wave_n * Gm::WCOLS +
-                                                                 16 * j + 4 * q16);
+            const int bc = n0 + wave_n * Gm::WCOLS + 16 * j + 4 * q16;
+            const u32x2 braw = bc < p.N ? *reinterpret_cast<const u32x2 *>(p.bias + bc)
+                                        : u32x2{0u, 0u};
             f32x4 b;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -797,11 +805,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * Gm::WCOLS;
     unsigned short *cw = Cm + cm * p.ldc + cn;
     const int rows = (int)min((int64_t)128, (int64_t)p.M - cm);
+    const int cols = (int)min((int64_t)Gm::WCOLS, (int64_t)p.N - cn);
     if (p.R != nullptr)
         restaged_epilogue16<DT, ACT, true, NJ>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
-                                               p.ldr, rows);
+                                               p.ldr, rows, cols);
     else
-        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows);
+        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows, cols);
 }
 
 namespace {
@@ -834,13 +843,22 @@ int async_tiles_m(const GemmArgs &a, int cfg)
     return (a.M + async_tile_m(cfg) - 1) / async_tile_m(cfg);
 }
 
+int async_tiles_n(const GemmArgs &a, int cfg)
+{
+    return (a.N + async_tile_n(cfg) - 1) / async_tile_n(cfg);
+}
+
 bool async_eligible(const GemmArgs &a, int cfg)
 {
-    // An M that is not a multiple of the tile is taken when the partial
-    // last row tile wastes at most M / 8 rows.
+    // An M (or an N that is a multiple of 8) that is not a multiple of the
+    // tile is taken when the partial last row (column) tile wastes at most
+    // M / 8 rows (N / 8 columns).
     const int pad = async_tiles_m(a, cfg) * async_tile_m(cfg) - a.M;
     const bool m_ok = a.M % async_tile_m(cfg) == 0 || (a.M > async_tile_m(cfg) && 8 * pad <= a.M);
-    return m_ok && a.N % async_tile_n(cfg) == 0 &&
+    const int padn = async_tiles_n(a, cfg) * async_tile_n(cfg) - a.N;
+    const bool n_ok = a.N % async_tile_n(cfg) == 0 ||
+                      (a.N % 8 == 0 && a.N > async_tile_n(cfg) && 8 * padn <= a.N);
+    return m_ok && n_ok &&
            a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
@@ -850,7 +868,7 @@ int plan_async_splits(const GemmArgs &a, int cfg, int want)
     const AsyncConfig &c = kAsyncConfigs[cfg];
     if (c.mfma16 || c.ti * c.tj > 4 || want == 1)
         return 1;
-    const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * (a.N / async_tile_n(cfg)) * a.n_mat;
+    const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
     if (tiles > kMaxSplitTiles || (want <= 0 && tiles >= 240))
         return 1;
     // enough workgroups for one wave of the 256 CUs, at most 8 splits, each
@@ -865,14 +883,14 @@ int plan_async_splits(const GemmArgs &a, int cfg, int want)
 
 size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 {
-    return (size_t)splits * (size_t)async_tiles_m(a, cfg) * (a.N / async_tile_n(cfg)) * a.n_mat *
+    return (size_t)splits * (size_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat *
            async_tile_m(cfg) * async_tile_n(cfg);
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,
                         float *ws, int *counters, hipStream_t s)
 {
-    const int tiles_m = async_tiles_m(a, cfg), tiles_n = a.N / async_tile_n(cfg);
+    const int tiles_m = async_tiles_m(a, cfg), tiles_n = async_tiles_n(a, cfg);
     if (splits < 1 || (splits > 1 && (plan_async_splits(a, cfg, splits) != splits ||
                                       ws == nullptr || counters == nullptr)))
         return hipErrorInvalidValue;

@@ -147,7 +147,7 @@ int choose_async(const tg::GemmArgs &a, const char *force)
         if (tg::async_forced_only(i) || !tg::async_eligible(a, i))
             continue;
         const int64_t tiles =
-            (int64_t)tg::async_tiles_m(a, i) * (a.N / tg::async_tile_n(i)) * a.n_mat;
+            (int64_t)tg::async_tiles_m(a, i) * tg::async_tiles_n(a, i) * a.n_mat;
         if (tiles >= 240)
             return i;
         best = i;

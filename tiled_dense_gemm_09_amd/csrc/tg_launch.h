@@ -48,9 +48,9 @@ hipError_t launch_generic(int dt, int act, const GemmArgs &a, hipStream_t stream
 // Asynchronous-copy MFMA kernel: 256 x 256 tiles (16x16x32 or 32x32x16
 // MFMA), 128 x 128, 64 x 128 and 64 x 64 tiles (32x32x16), all 32 deep, 4
 // stages; a
-// problem is eligible for a configuration when its tile width divides N, K
-// is a multiple of 128, and M is a multiple of the tile height or leaves a
-// partial last row tile of at most M / 8 padding rows.
+// problem is eligible for a configuration when K is a multiple of 128, M is
+// a multiple of the tile height or leaves a partial last row tile of at
+// most M / 8 padding rows, and N likewise (N a multiple of 8).
 int num_async_configs();
 const char *async_config_name(int cfg);
 // taken only when TG_FORCE_CONFIG names it
@@ -58,9 +58,10 @@ bool async_forced_only(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);
-// Row tiles of a problem: the ceiling of M / tile (a partial last row tile
-// counts as a tile).
+// Row and column tiles of a problem: the ceilings of M / tile height and
+// N / tile width (a partial last tile counts as a tile).
 int async_tiles_m(const GemmArgs &a, int cfg);
+int async_tiles_n(const GemmArgs &a, int cfg);
 // Split-K for under-filled grids (128 x 128 and 64 x 128 tiles only, at most
 // kMaxSplitTiles tiles): the number of K splits for the configuration, 1 for
 // none.  want > 1 asks for that many (fewer when K does not divide), want

@@ -65,13 +65,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // of row r at c ^ (r % 4TJ)) so that each global store writes whole
 // 64 TJ-byte row segments instead of 16-byte pieces of 32 rows.  C points
 // at the wave tile's first element; R likewise (row pitch ldr).
-// Rows at or past `rows` (the matrix's last row, for a partial last row
-// tile) are neither read from R nor stored.
+// Rows at or past `rows` and columns at or past `cols` (a multiple of 8;
+// partial last row or column tiles) are neither read from R nor stored.
 template <int DT, int ACT, int TI, int TJ, bool HR>
 __device__ __forceinline__ void restaged_epilogue(const f32x16 (&acc)[TI][TJ], unsigned char *ep,
                                                   int lane, unsigned short *C, int64_t ldc,
                                                   const unsigned short *R, int64_t ldr,
-                                                  int rows = 1 << 30)
+                                                  int rows = 1 << 30, int cols = 1 << 30)
 {
     constexpr int EG = 4 * TJ; // granules per row of the wave tile
 #pragma unroll
@@ -83,9 +83,10 @@ __device__ __forceinline__ void restaged_epilogue(const f32x16 (&acc)[TI][TJ], u
             for (int j = 0; j < TJ; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    rr[j][g] = r < rows ? *reinterpret_cast<const u32x2 *>(
-                                              R + (int64_t)r * ldr + j * 32 + g * 8 + (lane >> 5) * 4)
-                                        : u32x2{0u, 0u};
+                    rr[j][g] = r < rows && j * 32 + g * 8 + (lane >> 5) * 4 < cols
+                                   ? *reinterpret_cast<const u32x2 *>(
+                                         R + (int64_t)r * ldr + j * 32 + g * 8 + (lane >> 5) * 4)
+                                   : u32x2{0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
@@ -112,7 +113,7 @@ __device__ __forceinline__ void restaged_epilogue(const f32x16 (&acc)[TI][TJ], u
         const int r = (64 / EG) * t + lane / EG;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * EG) +
                                                          (((lane % EG) ^ (r & (EG - 1))) * 16));
-        if (r < rows)
+        if (r < rows && (lane % EG) * 8 < cols)
             *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
     }
 }
