@@ -482,8 +482,11 @@ def run_sweep(torch, tg):
     """Rates across shapes beside the ROCm library (torch.matmul), one JSON
     object per shape on stdout: square f16/bf16 GEMMs from 512^3 to 8192^3
     (A, B = U[-1,1]/8, no epilogue; up to 2048^3 both sides replayed from
-    captured graphs of 50 launches) and bf16 products with M = 1..32
-    (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB)."""
+    captured graphs of 50 launches), bf16 products with M = 1..32
+    (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB), and bf16
+    shapes off the tile grid (X ~ N(0,1), W ~ N(0, 1/K)): token counts that
+    leave a partial last tile, pitches off the 8-element grid, and square
+    sizes whose K is not a multiple of 128."""
     def graph_ms(fn, per=50, reps=10):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -541,6 +544,21 @@ def run_sweep(torch, tg):
                               "GB/s": round(nb / ms / 1e6), "kernel": kern,
                               "library_GB/s": round(nb / ml / 1e6)}), flush=True)
         del Ws
+    for (M, N, K) in ((2049, 4096, 4096), (3000, 11008, 4096), (5000, 4096, 4096),
+                      (4096, 4000, 4096), (4095, 4095, 4095), (4000, 4000, 4000),
+                      (8000, 8000, 8000)):
+        X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        f = 2.0 * M * N * K
+        steps = max(20, min(500, int(2e13 / f)))
+        ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, steps // 10 + 2)
+        kern = tg.last_kernel()
+        ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, steps // 10 + 2)
+        print(json.dumps({"shape": "bf16 %dx%dx%d" % (M, N, K), "ms": round(ms, 5),
+                          "TFLOP/s": round(f / ms / 1e9, 1), "kernel": kern,
+                          "library_TFLOP/s": round(f / ml / 1e9, 1)}), flush=True)
+        del X, W, Y
         torch.cuda.empty_cache()
 
 
