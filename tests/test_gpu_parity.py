@@ -780,6 +780,50 @@ def test_partial_column_tile_split_k_and_qkv(tg, monkeypatch):
         util.check_exact(outs[t], ref, "partial column tile qkv [%d]" % t)
 
 
+KPAD_CASES = [
+    # (dt, M, N, K): K off the 128 grid on problems of >= 2^30 multiply-adds;
+    # the padded problems take 64 x 64, 128 x 128 and 64 x 128 tiles
+    (F16, 1000, 1200, 1000),
+    (BF16, 2000, 2000, 2000),
+    (F16, 1536, 2048, 520),
+]
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K", KPAD_CASES)
+def test_k_padded_to_the_loop_integer_exact(tg, dt, M, N, K, trans_b):
+    # A and B sit in buffers whose pitch padding holds NaN: the padded copies
+    # must read only k < K.  Integer operands, bias and residual: bit-exact.
+    import torch
+    p = inputs.problem(dt, M, N, K, seed=280 + K, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(281 + M), (M, N), "int", dt, 8.0)
+    A = util.to_dev(padded(p["A"], K + 8, dt), dt)[:, :K]
+    if trans_b:
+        b = util.to_dev(padded(np.ascontiguousarray(p["B"].T), K + 8, dt), dt)[:, :K].t()
+    else:
+        b = util.to_dev(padded(p["B"], N + 8, dt), dt)[:, :N]
+    bias = util.to_dev(p["bias"], dt)
+    say("case K padded", dt, M, N, K, "B[N,K]" if trans_b else "B[K,N]")
+    C = tg.gemm(A, b, bias=bias, residual=util.to_dev(R, dt))
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.endswith("_kpad"), kern
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    util.check_exact(util.to_bits(C), ref, "K padded " + kern)
+
+
+def test_k_padded_gelu_random(tg):
+    p = inputs.problem(BF16, 2000, 2000, 2000, seed=290, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.1, b_scale=0.1)
+    say("case K padded gelu 2000^3")
+    bits, kern = run(tg, p)
+    assert kern.endswith("_kpad"), kern
+    f64, rbits = oracle.gemm(BF16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(BF16, bits, f64, "K padded gelu", ref_bits=rbits)
+
+
 def test_partial_row_tile_gelu_random_and_qkv(tg, monkeypatch):
     # M = 1200: 5 row tiles, 80 padding rows (at most M / 8 are allowed)
     import torch

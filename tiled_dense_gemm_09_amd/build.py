@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtg.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gemm_tiled.hip", "gemm_async.hip", "gemm_mx.hip", "attention.hip", "gemm_skinny.hip",
-           "gemm_generic.hip", "tg_api.cpp"]
+           "gemm_generic.hip", "gemm_kpad.hip", "tg_api.cpp"]
 ARCH = os.environ.get("TG_ARCH", "gfx950")
 
 FLAGS = [

@@ -155,6 +155,26 @@ int choose_async(const tg::GemmArgs &a, const char *force)
     return best;
 }
 
+// A problem worth padding K to the asynchronous kernels' loop: one matrix,
+// K not a multiple of 128, at least 2^30 multiply-adds, no forced
+// configuration, and the padded problem eligible for a configuration with a
+// full wave of tiles.
+bool kpad_eligible(const tg::GemmArgs &a, const char *force)
+{
+    if ((force && *force) || a.n_mat != 1 || a.K % 128 == 0 || a.K < 128 ||
+        (double)a.M * a.N * a.K < (double)(1 << 30))
+        return false;
+    tg::GemmArgs a2 = a;
+    a2.K = (a.K + 127) / 128 * 128;
+    a2.lda = a2.K;
+    a2.ldb = a.b_trans ? a2.K : (a.N + 7) / 8 * 8;
+    const int cfg = choose_async(a2, nullptr);
+    if (cfg < 0)
+        return false;
+    const int64_t tiles = (int64_t)tg::async_tiles_m(a2, cfg) * tg::async_tiles_n(a2, cfg);
+    return tiles >= 240;
+}
+
 tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
               int64_t ldc, int n_mat, void *stream, int b_trans = 0, const void *R = nullptr,
@@ -245,6 +265,7 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     for (int t = 0; t < n_mat; ++t)
         even = even && ((uintptr_t)C[t] & 1u) == 0 && ((uintptr_t)B[t] & 1u) == 0;
     const bool unal_tiled = !fast && even && !b_trans && K > 0 && !force_generic;
+    const bool kpad = fast && !force_generic && M > 32 && kpad_eligible(a, force);
     if (unal_tiled) {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);
@@ -254,7 +275,7 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         const int group_m = env_int("TG_GROUP_M", 4);
         err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
         set_last(c.name, "_unaligned");
-    } else if (!fast || force_generic || (b_trans && !trans_async)) {
+    } else if (!fast || force_generic || (b_trans && !trans_async && !kpad)) {
         err = tg::launch_generic(kdt, kact, a, s);
         set_last(!fast            ? "generic_fma (unaligned operands)"
                  : force_generic ? "generic_fma (forced)"
@@ -306,6 +327,38 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (splits > 1)
             snprintf(detail, sizeof detail, "_splitk%d", splits);
         set_last(tg::async_config_name(cfg), detail);
+    } else if (kpad) {
+        // K off the 128 grid on a large problem: A and B copied with K
+        // rounded up to 128 and zeros in the added entries, then the
+        // asynchronous kernel (partial last tiles for M and N) writes C.
+        tg::GemmArgs a2 = a;
+        const int K2 = (a.K + 127) / 128 * 128;
+        const int N8 = (a.N + 7) / 8 * 8;
+        const int64_t a_elems = (int64_t)a.M * K2;
+        const int64_t b_elems = b_trans ? (int64_t)a.N * K2 : (int64_t)K2 * N8;
+        tg_status st = TG_SUCCESS;
+        void *base = get_workspace((size_t)((a_elems + b_elems) / 2 + 64), s, &st);
+        if (!base)
+            return st;
+        unsigned short *Ap = reinterpret_cast<unsigned short *>(static_cast<char *>(base) +
+                                                                kCounterBytes);
+        unsigned short *Bp = Ap + (a_elems + 127) / 128 * 128;
+        err = tg::launch_pad_copy(a.A, a.lda, a.M, a.K, Ap, a.M, K2, s);
+        if (err == hipSuccess)
+            err = b_trans ? tg::launch_pad_copy(a.B[0], a.ldb, a.N, a.K, Bp, a.N, K2, s)
+                          : tg::launch_pad_copy(a.B[0], a.ldb, a.K, a.N, Bp, K2, N8, s);
+        a2.A = Ap;
+        a2.lda = K2;
+        a2.B[0] = a2.B[1] = a2.B[2] = Bp;
+        a2.ldb = b_trans ? K2 : N8;
+        a2.K = K2;
+        const int cfg = choose_async(a2, nullptr);
+        if (err == hipSuccess) {
+            const int group_m = env_int("TG_GROUP_M", 4);
+            err = tg::launch_async(cfg, kdt, kact, a2, group_m > 0 ? group_m : 4, 1, nullptr,
+                                   nullptr, s);
+        }
+        set_last(tg::async_config_name(cfg), "_kpad");
     } else {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);

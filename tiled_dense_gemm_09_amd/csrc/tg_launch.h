@@ -120,6 +120,12 @@ int attn_block_m(const AttnArgs &a, int want);
 hipError_t launch_attn(int dt, bool causal, int bm, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_generic(int dt, bool causal, const AttnArgs &a, int D, hipStream_t stream);
 
+// Zero-padded copy: dst[r][c] = src[r][c] inside src_rows x src_cols, else
+// 0, for a dst_rows x dst_cols destination of pitch dst_cols (a multiple of
+// 8, 16-byte aligned).  Used to round K up to the asynchronous kernels' loop.
+hipError_t launch_pad_copy(const unsigned short *src, int64_t lds, int src_rows, int src_cols,
+                           unsigned short *dst, int dst_rows, int dst_cols, hipStream_t stream);
+
 // Small-M path (M <= 32): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
 // entries that must be zero before the first call; the kernel leaves them
