@@ -44,7 +44,8 @@
  *    The split-K paths of tg_gemm, tg_gemm_bias_act, tg_gemm_ex and
  *    tg_gemm_qkv (small M, and square tiles that would leave most compute
  *    units idle; tg_last_kernel() then ends in "_split..." or "_splitk<n>")
- *    keep a per-device workspace that is allocated on first use and grown
+ *    and the K-padding path (K not a multiple of 128 on large problems;
+ *    "_kpad") keep a per-device workspace that is allocated on first use and grown
  *    when a larger one is needed (the only allocation the library makes;
  *    growing it synchronizes the device and frees the old buffer, so a HIP
  *    graph that captured such a call must not be replayed after a call
