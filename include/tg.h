@@ -40,18 +40,25 @@
  *    choice is never silent: tg_last_kernel()
  *    names the kernel and tile configuration the last call on this host
  *    thread launched (and TG_LOG=1 in the environment prints it).
- *  - Thread safety: entry points may be called from several host threads.
- *    The split-K paths of tg_gemm, tg_gemm_bias_act, tg_gemm_ex and
- *    tg_gemm_qkv (small M, and square tiles that would leave most compute
- *    units idle; tg_last_kernel() then ends in "_split..." or "_splitk<n>")
- *    and the K-padding path (K not a multiple of 128 on large problems;
- *    "_kpad") keep a per-device workspace that is allocated on first use and grown
- *    when a larger one is needed (the only allocation the library makes;
- *    growing it synchronizes the device and frees the old buffer, so a HIP
- *    graph that captured such a call must not be replayed after a call
- *    that grew the workspace).  Calls that use it are ordered by their
- *    streams; two such calls on different streams of one device must not
- *    overlap.
+ *  - Workspace: the split-K paths of tg_gemm, tg_gemm_bias_act, tg_gemm_ex
+ *    and tg_gemm_qkv (small M, and square tiles that would leave most
+ *    compute units idle; tg_last_kernel() then ends in "_split..." or
+ *    "_splitk<n>") and the K-padding path (K not a multiple of 128 on large
+ *    problems; "_kpad") use a per-device workspace that is allocated on
+ *    first use and grown when a larger one is needed (the only allocation
+ *    the library makes; tg_workspace_bytes() reports its size).  Growing it
+ *    synchronizes the device, frees the old buffer and clears the new one's
+ *    counters on the caller's stream, so:
+ *      - a call that would grow it while its stream is being captured into
+ *        a HIP graph launches nothing: the split-K paths return
+ *        TG_ERROR_NOT_SUPPORTED (tg_last_kernel() says why), the K-padding
+ *        path runs a kernel that needs no workspace instead (reported);
+ *      - a graph that captured a call using the workspace must not be
+ *        replayed after a later call grew it.
+ *    Calls that use it are ordered by their streams; two such calls on
+ *    different streams of one device must not overlap.
+ *  - Thread safety: entry points may be called from several host threads
+ *    (the workspace rule above still applies to calls that use it).
  */
 #ifndef TG_H
 #define TG_H
@@ -72,7 +79,7 @@ typedef enum { TG_ACT_NONE = 0, TG_ACT_GELU_TANH = 1 } tg_act;
 typedef enum {
     TG_SUCCESS = 0,
     TG_ERROR_INVALID_VALUE = 1, /* NULL pointer, bad size, pitch, dtype or act, overlap */
-    TG_ERROR_NOT_SUPPORTED = 2, /* no device / not gfx950 */
+    TG_ERROR_NOT_SUPPORTED = 2, /* no device / not gfx950 / workspace growth during capture */
     TG_ERROR_LAUNCH_FAILED = 3, /* the HIP runtime reported an error at launch */
     TG_ERROR_OUT_OF_MEMORY = 4  /* workspace allocation failed */
 } tg_status;
@@ -191,13 +198,27 @@ tg_status tg_gemm_qkv(tg_dtype dt, int64_t M, int64_t N, int64_t K,
                       void *Q, void *Kout, void *V, int64_t ldo,
                       void *stream);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage; an unknown value
+ * gives "TG_UNKNOWN_STATUS").  The statuses are the diagnostic half of the
+ * dispatch contract: an unsupported case is rejected with a reason or runs
+ * a registered fallback, never silently ("TIRx", section 5.4). */
 const char *tg_status_string(tg_status s);
 
 /* Kernel and tile configuration chosen by the last entry-point call on the
- * calling host thread, e.g. "tiled_256x256x64_w2x2"; "none" before any call
- * or after a no-op.  Thread-local, static storage. */
+ * calling host thread, e.g. "tiled_256x256x64_w2x2", with the reason
+ * appended when the call fell back to a slower kernel or launched nothing;
+ * "none" before any call or after a no-op.  Thread-local, static storage,
+ * valid until the thread's next call.  It exists because a silent fallback
+ * to a slow path is the failure mode that a user cannot see ("Beyond
+ * Hand-Written CUDA: Inside TileLang's Multi-Backend Tile Compiler
+ * Architecture", section 5). */
 const char *tg_last_kernel(void);
+
+/* Bytes of the library-managed workspace on the current device (0 before its
+ * first use).  A caller that captures HIP graphs can make one eager call of
+ * each shape first, so that the captured calls find the workspace large
+ * enough. */
+int64_t tg_workspace_bytes(void);
 
 /* ---- host-side introspection (no GPU needed; for tests and tools) ---- */
 

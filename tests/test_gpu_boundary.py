@@ -1,0 +1,164 @@
+"""GPU checks of the C ABI's boundary rules that need a device: calls that
+would have to grow the library's workspace while their stream is captured
+into a graph, and argument views the binding must refuse before anything is
+launched."""
+import numpy as np
+import pytest
+
+import oracle
+import util
+from tiled_dense_gemm_09_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = inputs.F16, inputs.BF16
+NOT_SUPPORTED = 2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tg():
+    import torch
+    assert torch.cuda.is_available()
+    from tiled_dense_gemm_09_amd import tg as _tg
+    return _tg
+
+
+def capture(fn):
+    """Capture fn() (plus a small marker kernel, so the graph is never empty)
+    on a side stream; returns the graph, the marker tensor and whatever fn
+    raised."""
+    import torch
+    mark = torch.zeros(16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    raised = None
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            mark.add_(1.0)
+            try:
+                fn()
+            except Exception as e:  # noqa: BLE001 -- inspected by the caller
+                raised = e
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g, mark, raised
+
+
+def test_cold_k_padding_call_under_capture_takes_a_kernel_without_workspace(tg):
+    # K off the 128 grid on a large problem normally copies A and B into the
+    # workspace with K padded.  When the workspace would have to grow during
+    # a capture, the call runs the tiled kernel (no workspace) instead; the
+    # graph then replays correctly, with eager work between the replays.
+    import torch
+    w0 = tg.workspace_bytes()
+    n = 1024
+    while 16384 + 4 * n * (n + 128) + 256 <= w0:
+        n *= 2
+    if n > 8192:
+        pytest.skip("workspace already %d bytes" % w0)
+    M, N, K = n, n, n + 8  # K rounds up to n + 128: 120 padded k, at most K / 8
+    p = inputs.problem(F16, M, N, K, seed=700, kind="int", bias=True, bias_kind="int")
+    A, B = util.to_dev(p["A"], F16), util.to_dev(p["B"], F16)
+    bias = util.to_dev(p["bias"], F16)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    say("case cold K padding under capture", M, N, K, "workspace", w0)
+    g, mark, raised = capture(lambda: tg.gemm(A, B, out=C, bias=bias))
+    assert raised is None, raised
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("tiled_") and "stream capture" in kern, kern
+    assert tg.workspace_bytes() == w0
+    rows = [0, 1, M // 2, M - 1]
+    refs = [oracle.gemm(F16, p["A"], p["B"], p["bias"], rows=(r, r + 1))[1] for r in rows]
+    for i in range(3):
+        C.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "replay %d row %d" % (i, r))
+        tg.gemm(A, B, out=C, bias=bias)  # eager: now grows the workspace, K padded
+        torch.cuda.synchronize()
+        assert tg.last_kernel().endswith("_kpad"), tg.last_kernel()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "eager %d row %d" % (i, r))
+    assert float(mark[0]) == 3.0
+    assert tg.workspace_bytes() > w0
+
+
+def test_cold_split_k_call_under_capture_launches_nothing(tg, monkeypatch):
+    # a split-K call whose workspace would have to grow inside a capture
+    # returns TG_ERROR_NOT_SUPPORTED, says why, and captures no launch: the
+    # replayed graph leaves the output untouched.  The same call made eagerly
+    # afterwards grows the workspace and is exact.
+    import torch
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_128x128x32_s4")
+    monkeypatch.setenv("TG_SPLITK", "8")
+    w0 = tg.workspace_bytes()
+    n = 1024
+    while 16384 + 8 * n * n * 4 <= w0:
+        n *= 2
+    if n > 8192:
+        pytest.skip("workspace already %d bytes" % w0)
+    M, N, K = n, n, 1024
+    p = inputs.problem(BF16, M, N, K, seed=701, kind="int")
+    A, B = util.to_dev(p["A"], BF16), util.to_dev(p["B"], BF16)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    say("case cold split-K under capture", M, N, K, "workspace", w0)
+    g, mark, raised = capture(lambda: tg.gemm(A, B, out=C))
+    assert isinstance(raised, tg.TgError) and raised.status == NOT_SUPPORTED, raised
+    assert "stream capture" in tg.last_kernel(), tg.last_kernel()
+    assert tg.workspace_bytes() == w0
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(mark[0]) == 1.0
+    assert bool(torch.isnan(C).all()), "the failed call launched something"
+    tg.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    assert tg.last_kernel() == "async_128x128x32_s4_splitk8", tg.last_kernel()
+    assert tg.workspace_bytes() > w0
+    got = util.to_bits(C)
+    for r in (0, M // 3, M - 1):
+        _, ref = oracle.gemm(BF16, p["A"], p["B"], rows=(r, r + 1))
+        util.check_exact(got[r:r + 1], ref, "eager split-K row %d" % r)
+
+
+def test_overlapping_views_and_host_bias_are_refused(tg):
+    # a broadcast row (stride 0) or rows that overlap would make the library
+    # read or write a full pitch per row past the allocation; a host bias is
+    # not a device pointer.  All are refused in the binding, before any call.
+    import torch
+    K, N = 256, 256
+    row = torch.zeros((1, K), dtype=torch.float16, device="cuda")
+    b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="overlapping rows"):
+        tg.gemm(row.expand(64, K), b)
+    flat = torch.zeros(64 * K, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="overlapping rows"):
+        tg.gemm(flat.as_strided((64, K), (K // 2, 1)), b)
+    out = torch.zeros((1, N), dtype=torch.float16, device="cuda").expand(64, N)
+    a = torch.zeros((64, K), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="overlapping rows"):
+        tg.gemm(a, b, out=out)
+    with pytest.raises(ValueError, match="device"):
+        tg.gemm(a, b, bias=torch.zeros(N, dtype=torch.float16))
+    with pytest.raises(ValueError, match="device"):
+        tg.gemm(a, b, residual=torch.zeros((64, N), dtype=torch.float16))
+    x = torch.zeros((64, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((1, N), dtype=torch.bfloat16, device="cuda").expand(K, N)
+    with pytest.raises(ValueError, match="overlapping rows"):
+        tg.gemm_qkv(x, w, w, w)
+    a8 = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    s8 = torch.full((8, 256), 127, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="device"):
+        tg.gemm_mx(a8, s8, a8, s8, bias=torch.zeros(256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="overlapping rows"):
+        tg.gemm_mx(torch.zeros((1, 256), dtype=torch.uint8, device="cuda").expand(256, 256), s8,
+                   a8, s8)
+    torch.cuda.synchronize()

@@ -1,0 +1,312 @@
+"""GPU parity on special values: NaN, infinities and overflow, on every kernel
+family of the library, against the CPU oracle.
+
+The readings these tests hold the kernels to (the pages are silent on them):
+NaN propagates through the sum, the bias, the activation and the rounding;
+an infinity times zero is NaN and opposite infinities sum to NaN; a value
+beyond the output format's range rounds to an infinity (f16: |v| >= 65520,
+the midpoint above 65504 rounding to even; bf16: |v| >= 2^128 - 2^119).
+Operands are integer-valued apart from the planted specials, so every FP32
+partial sum is exact in any order and the comparison is exact by class:
+where the oracle gives NaN the GPU must give a NaN (its sign and payload are
+not fixed), everywhere else the bits must be equal.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import util
+from tiled_dense_gemm_09_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = inputs.F16, inputs.BF16
+POS_INF = {F16: 0x7C00, BF16: 0x7F80}
+NEG_INF = {F16: 0xFC00, BF16: 0xFF80}
+QNAN = {F16: 0x7E00, BF16: 0x7FC0}
+NAN_PITCH = {F16: 0x7E00, BF16: 0x7FC0}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tg():
+    import torch
+    assert torch.cuda.is_available()
+    from tiled_dense_gemm_09_amd import tg as _tg
+    return _tg
+
+
+def is_nan(dt, bits):
+    b = np.asarray(bits, np.uint16)
+    if dt == F16:
+        return ((b & 0x7C00) == 0x7C00) & ((b & 0x03FF) != 0)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+
+
+def check_classes(dt, gpu, ref, what):
+    """NaN exactly where the oracle has NaN; equal bits everywhere else."""
+    gpu = np.asarray(gpu, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    gn, rn = is_nan(dt, gpu), is_nan(dt, ref)
+    bad = (gn != rn) | (~rn & (gpu != ref))
+    if bad.any():
+        idx = np.argwhere(bad)[:6]
+        raise AssertionError("%s: %d of %d elements differ; first %s: gpu %s oracle %s"
+                             % (what, int(bad.sum()), bad.size, idx.tolist(),
+                                [hex(int(v)) for v in gpu[tuple(idx.T)]],
+                                [hex(int(v)) for v in ref[tuple(idx.T)]]))
+    n_nan, n_inf = int(rn.sum()), int(np.isin(ref, [POS_INF[dt], NEG_INF[dt]]).sum())
+    say("  %s: %d NaN, %d infinities, the rest bit-exact" % (what, n_nan, n_inf))
+    return n_nan, n_inf
+
+
+# Every kernel family: (id, environment, dtype, M, N, K, B stored [N,K],
+# expected kernel-name prefix)
+FAMILIES = [
+    ("async16_f16", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"}, F16, 512, 512, 256,
+     False, "async_256x256x32_s4_mfma16"),
+    ("async16_bf16_bt", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"}, BF16, 512, 512, 256,
+     True, "async_256x256x32_s4_mfma16"),
+    ("async16_w8", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16_w8"}, F16, 512, 512, 256,
+     False, "async_256x256x32_s4_mfma16_w8"),
+    ("async32_256", {"TG_FORCE_CONFIG": "async_256x256x32_s4"}, BF16, 512, 512, 256, False,
+     "async_256x256x32_s4"),
+    ("async32_128", {"TG_FORCE_CONFIG": "async_128x128x32_s4"}, F16, 256, 256, 256, False,
+     "async_128x128x32_s4"),
+    ("async32_64x128_bt", {"TG_FORCE_CONFIG": "async_64x128x32_s4"}, BF16, 256, 256, 256, True,
+     "async_64x128x32_s4"),
+    ("async32_64", {"TG_FORCE_CONFIG": "async_64x64x32_s4"}, F16, 128, 128, 256, False,
+     "async_64x64x32_s4"),
+    ("async32_splitk", {"TG_FORCE_CONFIG": "async_128x128x32_s4", "TG_SPLITK": "2"}, BF16, 256,
+     256, 256, False, "async_128x128x32_s4_splitk2"),
+    ("tiled_256", {"TG_FORCE_CONFIG": "tiled_256x256x64_w2x2"}, F16, 512, 512, 256, False,
+     "tiled_256x256x64_w2x2"),
+    ("tiled_128_edges", {"TG_FORCE_CONFIG": "tiled_128x128x64_w2x2"}, BF16, 200, 136, 104, False,
+     "tiled_128x128x64_w2x2"),
+    ("tiled_64", {"TG_FORCE_CONFIG": "tiled_64x64x64_w2x2"}, F16, 128, 192, 256, False,
+     "tiled_64x64x64_w2x2"),
+    ("generic", {"TG_FORCE_CONFIG": "generic"}, BF16, 64, 96, 80, False, "generic_fma"),
+    ("generic_bt", {"TG_FORCE_CONFIG": "generic"}, F16, 64, 96, 80, True, "generic_fma"),
+    ("skinny_stream", {}, BF16, 16, 2048, 1024, False, "skinny_stream"),
+    ("skinny_stream_m32", {}, F16, 32, 2048, 1024, False, "skinny_stream"),
+    ("skinny_registers", {}, F16, 16, 1000, 1024, False, "skinny_bn"),
+    ("skinny_cols", {"TG_SKINNY_COLS": "1"}, BF16, 16, 4096, 1024, False, "skinny_cols"),
+]
+
+
+def set_env(monkeypatch, env):
+    for k in ("TG_FORCE_CONFIG", "TG_SPLITK", "TG_SKINNY_COLS"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+
+
+def launch(tg, dt, A, B, bias, act, trans_b, unaligned=False):
+    """Run the GEMM on the bit matrices (B given [K,N]); returns the output bits
+    and the kernel name.  trans_b passes B stored [N,K]; unaligned carves the
+    operands out of buffers with a pitch off the 8-element grid (NaN padding)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    if unaligned:
+        Ad = util.to_dev(np.pad(A, ((0, 0), (0, 3)), constant_values=NAN_PITCH[dt]), dt)[:, :K]
+        Bd = util.to_dev(np.pad(B, ((0, 0), (0, 5)), constant_values=NAN_PITCH[dt]), dt)[:, :N]
+    else:
+        Ad = util.to_dev(A, dt)
+        Bd = util.to_dev(np.ascontiguousarray(B.T), dt).t() if trans_b else util.to_dev(B, dt)
+    bd = util.to_dev(bias, dt) if bias is not None else None
+    C = tg.gemm(Ad, Bd, bias=bd, act=act)
+    torch.cuda.synchronize()
+    return util.to_bits(C), tg.last_kernel()
+
+
+def plant_specials(dt, A, B, bias):
+    """NaN and infinities at fixed places of A, B and bias (copies)."""
+    A, B = A.copy(), B.copy()
+    M, K = A.shape
+    N = B.shape[1]
+    A[3 % M, 5 % K] = QNAN[dt]
+    A[7 % M, 9 % K] = POS_INF[dt]
+    A[(M - 2) % M, (K - 3) % K] = NEG_INF[dt]
+    B[11 % K, 13 % N] = QNAN[dt]
+    B[17 % K, 19 % N] = POS_INF[dt]
+    B[(K - 1) % K, (N - 7) % N] = NEG_INF[dt]
+    # an infinity in B on the k of A's +infinity: that product term is
+    # infinite itself (and may meet an infinite term of the other sign)
+    B[9 % K, 40 % N] = NEG_INF[dt]
+    if bias is not None:
+        bias = bias.copy()
+        bias[21 % N] = QNAN[dt]
+        bias[22 % N] = POS_INF[dt]
+        bias[23 % N] = NEG_INF[dt]
+    return A, B, bias
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_nan_and_infinities_propagate(tg, monkeypatch, fam):
+    name, env, dt, M, N, K, trans_b, prefix = fam
+    set_env(monkeypatch, env)
+    p = inputs.problem(dt, M, N, K, seed=500 + M + N, kind="int", bias=True, bias_kind="int")
+    A, B, bias = plant_specials(dt, p["A"], p["B"], p["bias"])
+    say("case specials", name, M, N, K)
+    bits, kern = launch(tg, dt, A, B, bias, "none", trans_b)
+    say("  kernel", kern)
+    assert kern.startswith(prefix), kern
+    _, ref = oracle.gemm(dt, A, B, bias)
+    n_nan, n_inf = check_classes(dt, bits, ref, "specials " + kern)
+    assert n_nan > 0 and n_inf > 0
+
+
+def overflow_operands(dt, M, N, K):
+    """Integer-valued operands whose exact sums sit on both sides of the
+    output format's overflow threshold.
+    f16: A[i][0..2] = s_i, B rows 0..2 = 32768, 32736, t_j, so the sums are
+    s_i (65504 + t_j) with t_j in {0, 8, 15, 16, 17, 32}: 65504 is the
+    largest finite f16, up to 65519 rounds down to it, 65520 is the midpoint
+    that rounds to even (up, to infinity).
+    bf16: A[i][0..9] = s_i, B[k][j] = 2^(127-k) for k <= L_j (2^118 for k = 9
+    in the last column type), so the sums are s_i (2^128 - 2^(127-L_j)):
+    L = 6 and 7 are finite (7 gives the largest bf16), L = 8 is the rounding
+    midpoint (up, to infinity), and the 2^118 term lands just below the
+    midpoint (down).  s_i = 2 overflows FP32 itself."""
+    s = np.array([1, -1, 0, 2, -2, 1, -1, 1])[np.arange(M) % 8].astype(np.float64)
+    A = np.zeros((M, K))
+    B = np.zeros((K, N))
+    if dt == F16:
+        A[:, :3] = s[:, None]
+        B[0, :] = 32768.0
+        B[1, :] = 32736.0
+        B[2, :] = np.array([0, 8, 15, 16, 17, 32], np.float64)[np.arange(N) % 6]
+    else:
+        A[:, :10] = s[:, None]
+        kind = np.arange(N) % 4
+        L = np.array([6, 7, 8, 7])[kind]
+        for k in range(9):
+            B[k, :] = np.where(k <= L, 2.0 ** (127 - k), 0.0)
+        B[9, :] = np.where(kind == 3, 2.0 ** 118, 0.0)
+    return inputs.to_bits(A, dt), inputs.to_bits(B, dt)
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_overflow_rounds_to_infinity(tg, monkeypatch, fam):
+    name, env, dt, M, N, K, trans_b, prefix = fam
+    set_env(monkeypatch, env)
+    A, B = overflow_operands(dt, M, N, K)
+    say("case overflow", name, M, N, K)
+    bits, kern = launch(tg, dt, A, B, None, "none", trans_b)
+    assert kern.startswith(prefix), kern
+    _, ref = oracle.gemm(dt, A, B)
+    _, n_inf = check_classes(dt, bits, ref, "overflow " + kern)
+    assert n_inf > 0
+    # the largest finite value is reached too
+    top = 0x7BFF if dt == F16 else 0x7F7F
+    assert np.any(ref == top) and np.any(bits == top)
+
+
+GELU_BIAS = {
+    F16: [0.0, 1.0, -1.0, 5.5, -5.5, 10.0, -10.0, 100.0, -100.0, 1000.0, -1000.0, 60000.0,
+          -60000.0, 65504.0, -65504.0, np.inf, -np.inf, np.nan],
+    BF16: [0.0, 1.0, -1.0, 10.0, -10.0, 1e4, -1e4, 1e10, -1e10, 1e30, -1e30, 3e38, -3e38,
+           np.inf, -np.inf, np.nan],
+}
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_gelu_saturates_like_the_oracle(tg, monkeypatch, fam):
+    # A = 0, so every output is gelu(bias[n]): the exponential and the
+    # reciprocal of the FP32 GELU saturate for large |x| (to x, or to -0) and
+    # infinities and NaN pass through as the oracle's double evaluation has it
+    name, env, dt, M, N, K, trans_b, prefix = fam
+    set_env(monkeypatch, env)
+    rng = np.random.default_rng(77)
+    A = np.zeros((M, K), np.uint16)
+    B = inputs.draw(rng, (K, N), "int", dt)
+    vals = np.array(GELU_BIAS[dt])
+    bias = inputs.to_bits(vals[np.arange(N) % len(vals)], dt)
+    say("case gelu saturation", name)
+    bits, kern = launch(tg, dt, A, B, bias, "gelu_tanh", trans_b)
+    assert kern.startswith(prefix), kern
+    f64, ref = oracle.gemm(dt, A, B, bias, oracle.ACT_GELU_TANH)
+    gn, rn = is_nan(dt, bits), is_nan(dt, ref)
+    assert np.array_equal(gn, rn), "NaN positions differ"
+    inf_bits = [POS_INF[dt], NEG_INF[dt]]
+    assert np.array_equal(np.isin(bits, inf_bits), np.isin(ref, inf_bits)), "infinities differ"
+    assert np.array_equal(bits[np.isin(ref, inf_bits)], ref[np.isin(ref, inf_bits)])
+    fin = ~rn & ~np.isin(ref, inf_bits)
+    util.check_tol(dt, bits[fin], f64[fin], "gelu saturation " + kern)
+    # large magnitudes are exact: gelu(x) = x for x >> 0 and -0 for x << 0
+    big = fin & (np.abs(f64) >= 100.0) | (fin & (ref == 0x8000))
+    assert np.array_equal(bits[big], ref[big])
+
+
+def test_unaligned_kernel_specials_and_overflow(tg, monkeypatch):
+    # the tiled kernel with element-wise loads and stores (pitches off the
+    # 8-element grid, NaN in the padding)
+    set_env(monkeypatch, {})
+    for dt in (F16, BF16):
+        p = inputs.problem(dt, 130, 140, 150, seed=600 + dt, kind="int", bias=True,
+                           bias_kind="int")
+        A, B, bias = plant_specials(dt, p["A"], p["B"], p["bias"])
+        bits, kern = launch(tg, dt, A, B, bias, "none", False, unaligned=True)
+        assert kern.endswith("_unaligned"), kern
+        _, ref = oracle.gemm(dt, A, B, bias)
+        check_classes(dt, bits, ref, "unaligned specials")
+        A, B = overflow_operands(dt, 130, 140, 150)
+        bits, kern = launch(tg, dt, A, B, None, "none", False, unaligned=True)
+        _, ref = oracle.gemm(dt, A, B)
+        check_classes(dt, bits, ref, "unaligned overflow")
+
+
+def test_qkv_specials(tg, monkeypatch):
+    set_env(monkeypatch, {})
+    import torch
+    q = inputs.qkv_problem(BF16, 512, 512, 256, seed=610, kind="int")
+    W = [w.copy() for w in q["W"]]
+    X, _, _ = plant_specials(BF16, q["X"], W[0], None)
+    for t in range(3):
+        _, W[t], _ = plant_specials(BF16, q["X"], W[t], None)
+        W[t][100 + t, 200 + t] = QNAN[BF16]
+    outs = tg.gemm_qkv(util.to_dev(X, BF16), *[util.to_dev(w, BF16) for w in W])
+    torch.cuda.synchronize()
+    assert tg.last_kernel().startswith("async_"), tg.last_kernel()
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, X, W[t])
+        check_classes(BF16, util.to_bits(outs[t]), ref, "qkv specials [%d]" % t)
+
+
+# ------------------------------------------------ block-scaled 8-bit GEMM
+
+E5M2_INF, E5M2_NINF, E5M2_NAN, E4M3_NAN, E8M0_NAN = 0x7C, 0xFC, 0x7F, 0x7F, 0xFF
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_mx_specials(tg, monkeypatch, generic):
+    # e5m2 infinities and NaN, e4m3 NaN and a NaN scale (e8m0 0xFF) on
+    # integer-valued data: classes exact against the oracle
+    set_env(monkeypatch, {"TG_FORCE_CONFIG": "generic"} if generic else {})
+    import torch
+    for fa, fb in ((1, 0), (0, 1)):
+        p = inputs.mx_problem(fa, fb, 512, 512, 512, seed=620 + fa, kind="int", bias=True)
+        A, B, SA, SB = p["A"].copy(), p["B"].copy(), p["SA"].copy(), p["SB"].copy()
+        if fa == 1:
+            A[3, 5], A[7, 9], A[200, 300] = E5M2_NAN, E5M2_INF, E5M2_NINF
+            B[11, 13] = E4M3_NAN
+        else:
+            A[3, 5] = E4M3_NAN
+            B[11, 13], B[17, 19], B[40, 9] = E5M2_NAN, E5M2_INF, E5M2_NINF
+        SA[2, 50] = E8M0_NAN   # k-block 2 of row 50
+        SB[5, 77] = E8M0_NAN   # k-block 5 of column 77
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        names = {0: "e4m3", 1: "e5m2"}
+        C = tg.gemm_mx(dev(A), dev(SA), dev(B), dev(SB), names[fa], names[fb],
+                       bias=util.to_dev(p["bias"], BF16), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        kern = tg.last_kernel()
+        say("case mx specials", fa, fb, kern)
+        assert kern.startswith("mx_generic" if generic else "mx_256x256"), kern
+        _, ref = oracle.gemm_mx(fa, fb, A, SA, B, SB, p["bias"], dt=BF16)
+        n_nan, _ = check_classes(BF16, util.to_bits(C), ref, "mx specials " + kern)
+        assert n_nan >= 512 + 512

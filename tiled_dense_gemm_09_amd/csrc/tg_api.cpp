@@ -55,7 +55,7 @@ Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld)
 }
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
 
-// ---- per-device workspace of the split-K small-M path -------------------
+// ---- per-device workspace of the split-K and K-padding paths -------------
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -63,9 +63,26 @@ struct Workspace {
 std::mutex g_ws_mutex;
 Workspace g_ws[64];
 
-// Returns nullptr on failure.  Layout: [counters: 4096 ints][floats...]
+// Layout of every workspace: [counters: 4096 ints][floats...]
 constexpr size_t kCounterBytes = 4096 * sizeof(int);
 
+// True when `stream` is being captured into a graph (or when the runtime
+// cannot tell, which is treated the same way).
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// The library-managed workspace of at least float_count floats, or nullptr
+// with *st set.  Growing it frees the old buffer after a device
+// synchronisation and clears the new counters on `stream`; none of that may
+// happen inside a stream capture, so a call that would grow it while
+// `stream` is capturing gets TG_ERROR_NOT_SUPPORTED (and launches nothing).
 void *get_workspace(size_t float_count, hipStream_t stream, tg_status *st)
 {
     int dev = 0;
@@ -77,6 +94,10 @@ void *get_workspace(size_t float_count, hipStream_t stream, tg_status *st)
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[dev];
     if (w.bytes < need) {
+        if (stream_capturing(stream)) {
+            *st = TG_ERROR_NOT_SUPPORTED;
+            return nullptr;
+        }
         if (w.ptr) {
             // the old buffer may still be in use by queued work
             if (hipDeviceSynchronize() != hipSuccess || hipFree(w.ptr) != hipSuccess) {
@@ -156,16 +177,18 @@ int choose_async(const tg::GemmArgs &a, const char *force)
 }
 
 // A problem worth padding K to the asynchronous kernels' loop: one matrix,
-// K not a multiple of 128, at least 2^30 multiply-adds, no forced
-// configuration, and the padded problem eligible for a configuration with a
-// full wave of tiles.
+// K not a multiple of 128, at least 2^30 multiply-adds, at most K / 8 added
+// k (the padded multiply-adds are wasted work on top of the copies), no
+// forced configuration, and the padded problem eligible for a configuration
+// with a full wave of tiles.
 bool kpad_eligible(const tg::GemmArgs &a, const char *force)
 {
+    const int K2 = (a.K + 127) / 128 * 128;
     if ((force && *force) || a.n_mat != 1 || a.K % 128 == 0 || a.K < 128 ||
-        (double)a.M * a.N * a.K < (double)(1 << 30))
+        (double)a.M * a.N * a.K < (double)(1 << 30) || 8 * (K2 - a.K) > a.K)
         return false;
     tg::GemmArgs a2 = a;
-    a2.K = (a.K + 127) / 128 * 128;
+    a2.K = K2;
     a2.lda = a2.K;
     a2.ldb = a.b_trans ? a2.K : (a.N + 7) / 8 * 8;
     const int cfg = choose_async(a2, nullptr);
@@ -265,7 +288,23 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     for (int t = 0; t < n_mat; ++t)
         even = even && ((uintptr_t)C[t] & 1u) == 0 && ((uintptr_t)B[t] & 1u) == 0;
     const bool unal_tiled = !fast && even && !b_trans && K > 0 && !force_generic;
-    const bool kpad = fast && !force_generic && M > 32 && kpad_eligible(a, force);
+    // K padding needs the workspace; when it cannot be had (a capture that
+    // would grow it, no memory) the kernels that need none run instead
+    bool kpad = fast && !force_generic && M > 32 && kpad_eligible(a, force);
+    const int kpad_k2 = (a.K + 127) / 128 * 128, kpad_n8 = (a.N + 7) / 8 * 8;
+    const int64_t kpad_a_elems = (int64_t)a.M * kpad_k2;
+    const int64_t kpad_b_elems = b_trans ? (int64_t)a.N * kpad_k2 : (int64_t)kpad_k2 * kpad_n8;
+    void *kpad_base = nullptr;
+    const char *kpad_note = nullptr;
+    if (kpad) {
+        tg_status st = TG_SUCCESS;
+        kpad_base = get_workspace((size_t)((kpad_a_elems + kpad_b_elems) / 2 + 64), s, &st);
+        if (!kpad_base) {
+            kpad = false;
+            kpad_note = st == TG_ERROR_NOT_SUPPORTED ? " (no K padding: stream capture)"
+                                                     : " (no K padding: no workspace)";
+        }
+    }
     if (unal_tiled) {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);
@@ -279,7 +318,8 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         err = tg::launch_generic(kdt, kact, a, s);
         set_last(!fast            ? "generic_fma (unaligned operands)"
                  : force_generic ? "generic_fma (forced)"
-                                 : "generic_fma (B stored [N,K] outside the async tile shapes)");
+                                 : "generic_fma (B stored [N,K] outside the async tile shapes)",
+                 kpad_note);
     } else if (n_mat == 1 && M <= 32 && K >= 256 && N >= 256 && !force_tiled && !b_trans &&
                tg::plan_skinny(a.M, a.N, a.K).streaming >= 0) {
         // M <= 16 always; 16 < M <= 32 when the streaming kernel fits the shape
@@ -291,8 +331,13 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                 return TG_ERROR_NOT_SUPPORTED;
             tg_status st = TG_SUCCESS;
             void *base = get_workspace(tg::skinny_ws_floats(pl, a.M, a.N), s, &st);
-            if (!base)
+            if (!base) {
+                set_last("skinny", st == TG_ERROR_NOT_SUPPORTED
+                                       ? " (not launched: its workspace would grow during "
+                                         "stream capture)"
+                                       : " (not launched: no workspace)");
                 return st;
+            }
             counters = static_cast<int *>(base);
             ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
         }
@@ -316,8 +361,14 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             static_assert(tg::kMaxSplitTiles * sizeof(int) <= kCounterBytes, "counter room");
             tg_status st = TG_SUCCESS;
             void *base = get_workspace(tg::async_ws_floats(a, cfg, splits), s, &st);
-            if (!base)
+            if (!base) {
+                set_last(tg::async_config_name(cfg),
+                         st == TG_ERROR_NOT_SUPPORTED
+                             ? " (split-K not launched: its workspace would grow during stream "
+                               "capture)"
+                             : " (split-K not launched: no workspace)");
                 return st;
+            }
             counters = static_cast<int *>(base);
             ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
         }
@@ -332,17 +383,10 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         // rounded up to 128 and zeros in the added entries, then the
         // asynchronous kernel (partial last tiles for M and N) writes C.
         tg::GemmArgs a2 = a;
-        const int K2 = (a.K + 127) / 128 * 128;
-        const int N8 = (a.N + 7) / 8 * 8;
-        const int64_t a_elems = (int64_t)a.M * K2;
-        const int64_t b_elems = b_trans ? (int64_t)a.N * K2 : (int64_t)K2 * N8;
-        tg_status st = TG_SUCCESS;
-        void *base = get_workspace((size_t)((a_elems + b_elems) / 2 + 64), s, &st);
-        if (!base)
-            return st;
-        unsigned short *Ap = reinterpret_cast<unsigned short *>(static_cast<char *>(base) +
+        const int K2 = kpad_k2, N8 = kpad_n8;
+        unsigned short *Ap = reinterpret_cast<unsigned short *>(static_cast<char *>(kpad_base) +
                                                                 kCounterBytes);
-        unsigned short *Bp = Ap + (a_elems + 127) / 128 * 128;
+        unsigned short *Bp = Ap + (kpad_a_elems + 127) / 128 * 128;
         err = tg::launch_pad_copy(a.A, a.lda, a.M, a.K, Ap, a.M, K2, s);
         if (err == hipSuccess)
             err = b_trans ? tg::launch_pad_copy(a.B[0], a.ldb, a.N, a.K, Bp, a.N, K2, s)
@@ -367,7 +411,7 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             return TG_ERROR_NOT_SUPPORTED;
         const int group_m = env_int("TG_GROUP_M", 4);
         err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
-        set_last(c.name);
+        set_last(c.name, kpad_note);
     }
     if (err != hipSuccess) {
         char detail[64];
@@ -595,6 +639,17 @@ const char *tg_status_string(tg_status s)
 }
 
 const char *tg_last_kernel(void) { return g_last_kernel; }
+
+int64_t tg_workspace_bytes(void)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    return (int64_t)g_ws[dev].bytes;
+}
 
 int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t group_m,
                      int64_t block_id, int64_t *mat, int64_t *tile_m, int64_t *tile_n)

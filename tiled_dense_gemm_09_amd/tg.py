@@ -21,7 +21,8 @@ BF16 = 2
 ACT = {"none": 0, "gelu_tanh": 1}
 
 SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_attention_fwd",
-           "tg_gemm_qkv", "tg_status_string", "tg_last_kernel", "tg_schedule_tile",
+           "tg_gemm_qkv", "tg_status_string", "tg_last_kernel", "tg_workspace_bytes",
+           "tg_schedule_tile",
            "tg_lds_offset", "tg_lds_swizzle", "tg_in_bounds"]
 FP8 = {"e4m3": 0, "e5m2": 1}
 OP_N, OP_T = 0, 1
@@ -62,6 +63,8 @@ def _load():
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_last_kernel.argtypes = []
     lib.tg_last_kernel.restype = ctypes.c_char_p
+    lib.tg_workspace_bytes.argtypes = []
+    lib.tg_workspace_bytes.restype = L
     lib.tg_schedule_tile.argtypes = [L, L, L, L, L, ctypes.POINTER(L), ctypes.POINTER(L),
                                      ctypes.POINTER(L)]
     lib.tg_schedule_tile.restype = I
@@ -85,6 +88,11 @@ def _check(status):
 
 def last_kernel():
     return lib.tg_last_kernel().decode()
+
+
+def workspace_bytes():
+    """Size of the library-managed workspace on the current device."""
+    return int(lib.tg_workspace_bytes())
 
 
 # ---------------------------------------------------------------- raw calls
@@ -142,13 +150,30 @@ def _dt(t):
 
 
 def _rowmajor(t, name):
+    """Row pitch (elements) of a row-major 2-D device tensor.  Views whose rows
+    overlap (a broadcast row, stride(0) < shape[1]) are rejected: the library
+    would read or write a full pitch per row past the allocation."""
     if t.dim() != 2:
         raise ValueError("%s must be 2-D" % name)
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must be row-major (unit column stride)" % name)
+    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) < t.shape[1]:
+        raise ValueError("%s has overlapping rows (row stride %d < %d columns)"
+                         % (name, t.stride(0), t.shape[1]))
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
     return max(t.stride(0), t.shape[1])
+
+
+def _same_device(ref, *named):
+    """Every (tensor, name) given (None skipped) is a device tensor on ref's device."""
+    for t, name in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if t.device != ref.device:
+            raise ValueError("%s is on %s, the operands on %s" % (name, t.device, ref.device))
 
 
 def _stream(stream):
@@ -188,6 +213,7 @@ def gemm(a, b, out=None, bias=None, act="none", residual=None, stream=None):
         raise ValueError("out must be [M,N] of the input dtype")
     lda, ldc = _rowmajor(a, "a"), _rowmajor(out, "out")
     op_b, ldb = _operand_b(b)
+    _same_device(a, (b, "b"), (out, "out"), (bias, "bias"), (residual, "residual"))
     bptr = 0
     if bias is not None:
         if bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
@@ -216,6 +242,9 @@ def _bytes2d(t, name):
         return t.data_ptr(), t.shape[1]
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must be row-major" % name)
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError("%s has overlapping rows (row stride %d < %d columns)"
+                         % (name, t.stride(0), t.shape[1]))
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
     return t.data_ptr(), max(t.stride(0), t.shape[1])
@@ -238,8 +267,10 @@ def gemm_mx(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", bias=None, act="none", out
     odt = _dt(out)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [M,N]")
-    if bias is not None and (bias.dtype != out.dtype or bias.dim() != 1 or bias.shape[0] != N):
+    if bias is not None and (bias.dtype != out.dtype or bias.dim() != 1 or bias.shape[0] != N
+                             or (N > 1 and bias.stride(0) != 1)):
         raise ValueError("bias must be a dense [N] vector of the output dtype")
+    _same_device(a, (sa, "sa"), (b, "b"), (sb, "sb"), (out, "out"), (bias, "bias"))
     pa, lda = _bytes2d(a, "a")
     pb, ldb = _bytes2d(b, "b")
     psa, ldsa = _bytes2d(sa, "sa")
@@ -266,6 +297,7 @@ def attention(q, k, v, causal=False, scale=None, out=None, lse=False, stream=Non
         out = torch.empty_like(q)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    _same_device(q, (q, "q"), (k, "k"), (v, "v"), (out, "out"))
     l = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse else None
     _check(lib.tg_attention_fwd(dt, B, H, S, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 out.data_ptr(), l.data_ptr() if l is not None else None,
@@ -289,6 +321,7 @@ def gemm_qkv(x, wq, wk, wv, outs=None, stream=None):
         raise ValueError("the three weights must share one row pitch")
     if outs is None:
         outs = [torch.empty((M, N), dtype=x.dtype, device=x.device) for _ in range(3)]
+    _same_device(x, (wq, "wq"), (wk, "wk"), (wv, "wv"), *[(o, "out") for o in outs])
     ldo = _rowmajor(outs[0], "q")
     if any(_rowmajor(o, "out") != ldo or tuple(o.shape) != (M, N) for o in outs):
         raise ValueError("the three outputs must be [M,N] with one row pitch")
