@@ -102,6 +102,30 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K,
                            void *C, int64_t ldc,
                            void *stream);
 
+/* tg_gemm_bias_act for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, same kernels and bit-identical results; it
+ * never allocates, frees or clears memory through the runtime:
+ *  - the split-K paths (small M; TG_SPLITK) keep their partials and
+ *    counters in a fixed scratch array of the library, 16 MiB + 16 KiB per
+ *    device, held until the process ends (set up by the first call on each
+ *    device, which also launches one small kernel that zeroes the
+ *    counters; every split kernel leaves them at zero again);
+ *  - a problem whose partials need more than 16 MiB (4 Mi floats) returns
+ *    TG_ERROR_NOT_SUPPORTED and launches nothing (tg_last_kernel() gives
+ *    the size it needed);
+ *  - K off the 128 grid is never padded into a workspace (the kernels that
+ *    need none run instead).
+ * Every call on a device shares that device's scratch and finds it as the
+ * last call left it: two calls that overlap on one device (different
+ * streams, or host threads without ordering) race on it. */
+tg_status tg_gemm_bias_act_noalloc(tg_dtype dt, int64_t M, int64_t N, int64_t K,
+                                   const void *A, int64_t lda,
+                                   const void *B, int64_t ldb,
+                                   const void *bias, tg_act act,
+                                   void *C, int64_t ldc,
+                                   void *stream);
+
 /* Storage of the B operand of tg_gemm_ex. */
 typedef enum {
     TG_OP_N = 0, /* B is [K,N] row-major, pitch ldb >= N (as in every other entry point) */

@@ -125,6 +125,56 @@ void *get_workspace(size_t float_count, hipStream_t stream, tg_status *st)
     return w.ptr;
 }
 
+// ---- fixed scratch of the allocation-free entry point -------------------
+// One array per device that runs the library, held until the process ends:
+// the split-K counters, then kScratchFloats FP32 partials.  Host code never
+// uses the array's name as an address; it takes the device address that
+// hipGetSymbolAddress reports for the current device, once per device.
+constexpr size_t kScratchFloats = (size_t)4 << 20; // 16 MiB of partials
+constexpr size_t kScratchBytes = kCounterBytes + kScratchFloats * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words_kernel(unsigned int *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mutex;
+void *g_scratch[64];
+
+// Device address of this device's scratch, or nullptr with *st set.  The
+// first call on a device looks the address up and clears the counters with
+// a fill kernel on `stream` (the split kernels leave them at zero after
+// every launch).
+void *get_scratch(hipStream_t stream, tg_status *st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *st = TG_ERROR_NOT_SUPPORTED;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            *st = TG_ERROR_NOT_SUPPORTED;
+            return nullptr;
+        }
+        constexpr int words = (int)(kCounterBytes / sizeof(unsigned int));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                           static_cast<unsigned int *>(ptr), words);
+        if (hipGetLastError() != hipSuccess) {
+            *st = TG_ERROR_LAUNCH_FAILED;
+            return nullptr;
+        }
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
 int env_int(const char *name, int dflt)
 {
     const char *e = getenv(name);
@@ -198,10 +248,12 @@ bool kpad_eligible(const tg::GemmArgs &a, const char *force)
     return tiles >= 240;
 }
 
+// noalloc: the split paths take the fixed scratch (never the growable
+// workspace) and K is never padded, so the call allocates nothing.
 tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
               int64_t ldc, int n_mat, void *stream, int b_trans = 0, const void *R = nullptr,
-              int64_t ldr = 0)
+              int64_t ldr = 0, bool noalloc = false)
 {
     if (dt != TG_DTYPE_F16 && dt != TG_DTYPE_BF16)
         return TG_ERROR_INVALID_VALUE;
@@ -288,9 +340,35 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     for (int t = 0; t < n_mat; ++t)
         even = even && ((uintptr_t)C[t] & 1u) == 0 && ((uintptr_t)B[t] & 1u) == 0;
     const bool unal_tiled = !fast && even && !b_trans && K > 0 && !force_generic;
+    // Workspace of the split-K paths: the growable one, or the fixed scratch
+    // for the allocation-free entry point.  On failure *st is set and
+    // ws_note says why for tg_last_kernel().
+    char ws_note[128] = "";
+    auto split_workspace = [&](size_t float_count, tg_status *st) -> void * {
+        if (noalloc) {
+            if (float_count > kScratchFloats) {
+                *st = TG_ERROR_NOT_SUPPORTED;
+                snprintf(ws_note, sizeof ws_note,
+                         " (not launched: needs %zu bytes of scratch, the fixed scratch holds %zu)",
+                         kCounterBytes + float_count * sizeof(float), kScratchBytes);
+                return nullptr;
+            }
+            void *p = get_scratch(s, st);
+            if (!p)
+                snprintf(ws_note, sizeof ws_note, " (not launched: no scratch on this device)");
+            return p;
+        }
+        void *p = get_workspace(float_count, s, st);
+        if (!p)
+            snprintf(ws_note, sizeof ws_note, "%s",
+                     *st == TG_ERROR_NOT_SUPPORTED
+                         ? " (not launched: its workspace would grow during stream capture)"
+                         : " (not launched: no workspace)");
+        return p;
+    };
     // K padding needs the workspace; when it cannot be had (a capture that
     // would grow it, no memory) the kernels that need none run instead
-    bool kpad = fast && !force_generic && M > 32 && kpad_eligible(a, force);
+    bool kpad = !noalloc && fast && !force_generic && M > 32 && kpad_eligible(a, force);
     const int kpad_k2 = (a.K + 127) / 128 * 128, kpad_n8 = (a.N + 7) / 8 * 8;
     const int64_t kpad_a_elems = (int64_t)a.M * kpad_k2;
     const int64_t kpad_b_elems = b_trans ? (int64_t)a.N * kpad_k2 : (int64_t)kpad_k2 * kpad_n8;
@@ -330,12 +408,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             if (pl.n_tiles > (int)(kCounterBytes / sizeof(int)))
                 return TG_ERROR_NOT_SUPPORTED;
             tg_status st = TG_SUCCESS;
-            void *base = get_workspace(tg::skinny_ws_floats(pl, a.M, a.N), s, &st);
+            void *base = split_workspace(tg::skinny_ws_floats(pl, a.M, a.N), &st);
             if (!base) {
-                set_last("skinny", st == TG_ERROR_NOT_SUPPORTED
-                                       ? " (not launched: its workspace would grow during "
-                                         "stream capture)"
-                                       : " (not launched: no workspace)");
+                set_last("skinny", ws_note);
                 return st;
             }
             counters = static_cast<int *>(base);
@@ -360,13 +435,11 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (splits > 1) {
             static_assert(tg::kMaxSplitTiles * sizeof(int) <= kCounterBytes, "counter room");
             tg_status st = TG_SUCCESS;
-            void *base = get_workspace(tg::async_ws_floats(a, cfg, splits), s, &st);
+            void *base = split_workspace(tg::async_ws_floats(a, cfg, splits), &st);
             if (!base) {
-                set_last(tg::async_config_name(cfg),
-                         st == TG_ERROR_NOT_SUPPORTED
-                             ? " (split-K not launched: its workspace would grow during stream "
-                               "capture)"
-                             : " (split-K not launched: no workspace)");
+                char name[64];
+                snprintf(name, sizeof name, "%s_splitk%d", tg::async_config_name(cfg), splits);
+                set_last(name, ws_note);
                 return st;
             }
             counters = static_cast<int *>(base);
@@ -443,6 +516,15 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K, const v
     const void *Bs[3] = {B, nullptr, nullptr};
     void *Cs[3] = {C, nullptr, nullptr};
     return run(dt, M, N, K, A, lda, Bs, ldb, bias, act, Cs, ldc, 1, stream);
+}
+
+tg_status tg_gemm_bias_act_noalloc(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A,
+                                   int64_t lda, const void *B, int64_t ldb, const void *bias,
+                                   tg_act act, void *C, int64_t ldc, void *stream)
+{
+    const void *Bs[3] = {B, nullptr, nullptr};
+    void *Cs[3] = {C, nullptr, nullptr};
+    return run(dt, M, N, K, A, lda, Bs, ldb, bias, act, Cs, ldc, 1, stream, 0, nullptr, 0, true);
 }
 
 tg_status tg_gemm_ex(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,

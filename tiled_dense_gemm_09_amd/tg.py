@@ -20,7 +20,7 @@ F16 = 1
 BF16 = 2
 ACT = {"none": 0, "gelu_tanh": 1}
 
-SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_ex", "tg_gemm_mx", "tg_attention_fwd",
+SYMBOLS = ["tg_gemm", "tg_gemm_bias_act", "tg_gemm_bias_act_noalloc", "tg_gemm_ex", "tg_gemm_mx", "tg_attention_fwd",
            "tg_gemm_qkv", "tg_status_string", "tg_last_kernel", "tg_workspace_bytes",
            "tg_schedule_tile",
            "tg_lds_offset", "tg_lds_swizzle", "tg_in_bounds"]
@@ -51,6 +51,8 @@ def _load():
     lib.tg_gemm.restype = I
     lib.tg_gemm_bias_act.argtypes = [I, L, L, L, P, L, P, L, P, I, P, L, P]
     lib.tg_gemm_bias_act.restype = I
+    lib.tg_gemm_bias_act_noalloc.argtypes = [I, L, L, L, P, L, P, L, P, I, P, L, P]
+    lib.tg_gemm_bias_act_noalloc.restype = I
     lib.tg_gemm_ex.argtypes = [I, L, L, L, P, L, P, L, I, P, I, P, L, P, L, P]
     lib.tg_gemm_ex.restype = I
     lib.tg_gemm_mx.argtypes = [I, I, L, L, L, P, L, P, L, P, L, P, L, P, I, I, P, L, P]
@@ -104,6 +106,12 @@ def gemm_ptr(dt, M, N, K, A, lda, B, ldb, C, ldc, stream=0, bias=0, act=0):
                                     stream or None))
     else:
         _check(lib.tg_gemm(dt, M, N, K, A, lda, B, ldb, C, ldc, stream or None))
+
+
+def gemm_noalloc_ptr(dt, M, N, K, A, lda, B, ldb, C, ldc, stream=0, bias=0, act=0):
+    """tg_gemm_bias_act_noalloc on raw device pointers (ints)."""
+    _check(lib.tg_gemm_bias_act_noalloc(dt, M, N, K, A, lda, B, ldb, bias or None, act, C, ldc,
+                                        stream or None))
 
 
 def gemm_ex_ptr(dt, M, N, K, A, lda, B, ldb, op_b, C, ldc, stream=0, bias=0, act=0, R=0, ldr=0):
