@@ -69,19 +69,35 @@
 extern "C" {
 #endif
 
-typedef enum { TG_DTYPE_F16 = 1, TG_DTYPE_BF16 = 2 } tg_dtype;
+/* Every enum below carries two reserved enumerators that give it the range
+ * of a 32-bit int, so that any int value a C caller passes is a value of the
+ * type (and an unknown one is rejected with TG_ERROR_INVALID_VALUE) instead
+ * of a value outside the C++ type's range. */
+typedef enum {
+    TG_DTYPE_F16 = 1,
+    TG_DTYPE_BF16 = 2,
+    TG_DTYPE_RESERVED_MIN_ = -0x7fffffff - 1,
+    TG_DTYPE_RESERVED_MAX_ = 0x7fffffff
+} tg_dtype;
 
 /* act(x): identity, or the tanh form of GELU
  *     0.5 x (1 + tanh(u)),  u = sqrt(2/pi) (x + 0.044715 x^3),
  * evaluated in FP32 as the same function x / (1 + exp(-2u)). */
-typedef enum { TG_ACT_NONE = 0, TG_ACT_GELU_TANH = 1 } tg_act;
+typedef enum {
+    TG_ACT_NONE = 0,
+    TG_ACT_GELU_TANH = 1,
+    TG_ACT_RESERVED_MIN_ = -0x7fffffff - 1,
+    TG_ACT_RESERVED_MAX_ = 0x7fffffff
+} tg_act;
 
 typedef enum {
     TG_SUCCESS = 0,
     TG_ERROR_INVALID_VALUE = 1, /* NULL pointer, bad size, pitch, dtype or act, overlap */
     TG_ERROR_NOT_SUPPORTED = 2, /* no device / not gfx950 / workspace growth during capture */
     TG_ERROR_LAUNCH_FAILED = 3, /* the HIP runtime reported an error at launch */
-    TG_ERROR_OUT_OF_MEMORY = 4  /* workspace allocation failed */
+    TG_ERROR_OUT_OF_MEMORY = 4, /* workspace allocation failed */
+    TG_STATUS_RESERVED_MIN_ = -0x7fffffff - 1,
+    TG_STATUS_RESERVED_MAX_ = 0x7fffffff
 } tg_status;
 
 /* C = A . B.
@@ -129,8 +145,10 @@ tg_status tg_gemm_bias_act_noalloc(tg_dtype dt, int64_t M, int64_t N, int64_t K,
 /* Storage of the B operand of tg_gemm_ex. */
 typedef enum {
     TG_OP_N = 0, /* B is [K,N] row-major, pitch ldb >= N (as in every other entry point) */
-    TG_OP_T = 1  /* B is stored [N,K] row-major, pitch ldb >= K (one output feature per
+    TG_OP_T = 1, /* B is stored [N,K] row-major, pitch ldb >= K (one output feature per
                     row, the usual weight layout); the product uses its transpose */
+    TG_OP_RESERVED_MIN_ = -0x7fffffff - 1,
+    TG_OP_RESERVED_MAX_ = 0x7fffffff
 } tg_op;
 
 /* C = act(A . op(B) + bias) + R, one rounding at the end.
@@ -160,7 +178,9 @@ tg_status tg_gemm_ex(tg_dtype dt, int64_t M, int64_t N, int64_t K,
 /* 8-bit float formats of tg_gemm_mx (OCP 8-bit floating point). */
 typedef enum {
     TG_FP8_E4M3 = 0, /* 1 sign, 4 exponent (bias 7), 3 fraction bits; no infinities, max 448 */
-    TG_FP8_E5M2 = 1  /* 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style specials */
+    TG_FP8_E5M2 = 1, /* 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style specials */
+    TG_FP8_RESERVED_MIN_ = -0x7fffffff - 1,
+    TG_FP8_RESERVED_MAX_ = 0x7fffffff
 } tg_fp8_format;
 
 /* Block-scaled 8-bit GEMM:
@@ -249,12 +269,14 @@ int64_t tg_workspace_bytes(void);
 /* The tile scheduler's map of a linear workgroup id to (matrix, tile_m,
  * tile_n) for a grid of tiles_m x tiles_n tiles per matrix and n_mat
  * matrices, as the kernels compute it.  Returns 0, or -1 if block_id is out
- * of range.  The map is a bijection onto the tile grid. */
+ * of range or the grid has 2^31 tiles or more.  The map is a bijection onto
+ * the tile grid. */
 int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t group_m,
                      int64_t block_id, int64_t *mat, int64_t *tile_m, int64_t *tile_n);
 
 /* Byte offset of element (row, col) in the kernels' LDS tile of `cols`
- * 16-bit elements per row (row pitch padded by 8 elements). */
+ * 16-bit elements per row (row pitch padded by 8 elements); -1 when an
+ * argument is negative or >= 2^31. */
 int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col);
 
 /* Granule swizzle of the asynchronous kernels' LDS tiles: 16-byte granule c

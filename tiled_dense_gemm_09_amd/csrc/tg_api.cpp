@@ -55,6 +55,24 @@ Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld)
 }
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
 
+// A rows x cols matrix with pitch ld (elements of `bytes` bytes) at p has an
+// extent the span arithmetic can hold: non-negative sizes, ld >= cols, at
+// most 2^56 elements from its first to its last one, and no wrap past the
+// end of the address space.  Rejecting larger pitches keeps every later
+// (rows - 1) * ld in range.
+bool extent_ok(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t bytes)
+{
+    constexpr int64_t kMaxElems = (int64_t)1 << 56;
+    if (rows < 0 || cols < 0 || ld < cols || cols > kMaxElems)
+        return false;
+    if (rows > 1 && ld > (kMaxElems - cols) / (rows - 1))
+        return false;
+    if (rows == 0 || cols == 0)
+        return true;
+    const uint64_t span = (uint64_t)((rows - 1) * ld + cols) * (uint64_t)bytes;
+    return (uintptr_t)p <= UINTPTR_MAX - span;
+}
+
 // ---- per-device workspace of the split-K and K-padding paths -------------
 struct Workspace {
     void *ptr = nullptr;
@@ -271,6 +289,12 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         return TG_ERROR_INVALID_VALUE;
     if (R != nullptr && (ldr < N || ((uintptr_t)R & 1u) != 0))
         return TG_ERROR_INVALID_VALUE;
+    if ((K > 0 && !extent_ok(A, M, K, lda, 2)) || !extent_ok(bias, 1, N, N, 2) ||
+        (R != nullptr && !extent_ok(R, M, N, ldr, 2)))
+        return TG_ERROR_INVALID_VALUE;
+    for (int t = 0; t < n_mat; ++t)
+        if ((K > 0 && !extent_ok(B[t], b_rows, b_cols, ldb, 2)) || !extent_ok(C[t], M, N, ldc, 2))
+            return TG_ERROR_INVALID_VALUE;
     if (K > 0 && A == nullptr)
         return TG_ERROR_INVALID_VALUE;
     for (int t = 0; t < n_mat; ++t) {
@@ -570,6 +594,10 @@ tg_status tg_gemm_mx(tg_fp8_format fmt_a, tg_fp8_format fmt_b, int64_t M, int64_
     const int64_t KB = K / 32;
     if (ldc < N || (K > 0 && (lda < K || ldb < K || ld_sa < M || ld_sb < N)))
         return TG_ERROR_INVALID_VALUE;
+    if (!extent_ok(C, M, N, ldc, 2) || !extent_ok(bias, 1, N, N, 2) ||
+        (K > 0 && (!extent_ok(A, M, K, lda, 1) || !extent_ok(B, N, K, ldb, 1) ||
+                   !extent_ok(scale_a, KB, M, ld_sa, 1) || !extent_ok(scale_b, KB, N, ld_sb, 1))))
+        return TG_ERROR_INVALID_VALUE;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr || scale_a == nullptr ||
                                    scale_b == nullptr)))
         return TG_ERROR_INVALID_VALUE;
@@ -645,8 +673,10 @@ tg_status tg_attention_fwd(tg_dtype dt, int64_t batch, int64_t heads, int64_t se
         return TG_ERROR_INVALID_VALUE;
     if (head_dim > 128)
         return TG_ERROR_NOT_SUPPORTED;
-    const int64_t bh = batch * heads;
-    if (bh >= kMaxDim || seq >= kMaxDim || bh * seq * head_dim >= ((int64_t)1 << 40))
+    if (batch >= kMaxDim || heads >= kMaxDim || seq >= kMaxDim)
+        return TG_ERROR_INVALID_VALUE;
+    const int64_t bh = batch * heads; // < 2^62
+    if (bh >= kMaxDim || (seq > 0 && bh > (((int64_t)1 << 40) / head_dim) / seq))
         return TG_ERROR_INVALID_VALUE;
     if (bh == 0 || seq == 0) {
         set_last("none");
@@ -716,6 +746,7 @@ const char *tg_status_string(tg_status s)
     case TG_ERROR_NOT_SUPPORTED: return "TG_ERROR_NOT_SUPPORTED";
     case TG_ERROR_LAUNCH_FAILED: return "TG_ERROR_LAUNCH_FAILED";
     case TG_ERROR_OUT_OF_MEMORY: return "TG_ERROR_OUT_OF_MEMORY";
+    default: break;
     }
     return "TG_UNKNOWN_STATUS";
 }
@@ -736,10 +767,14 @@ int64_t tg_workspace_bytes(void)
 int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t group_m,
                      int64_t block_id, int64_t *mat, int64_t *tile_m, int64_t *tile_n)
 {
-    if (tiles_m <= 0 || tiles_n <= 0 || n_mat <= 0 || group_m <= 0)
+    if (tiles_m <= 0 || tiles_n <= 0 || n_mat <= 0 || group_m <= 0 || tiles_m >= kMaxDim ||
+        tiles_n >= kMaxDim || n_mat >= kMaxDim || group_m >= kMaxDim)
         return -1;
-    const int64_t total = tiles_m * tiles_n * n_mat;
-    if (total >= kMaxDim || block_id < 0 || block_id >= total)
+    const int64_t plane = tiles_m * tiles_n; // < 2^62
+    if (plane > (kMaxDim - 1) / n_mat)
+        return -1;
+    const int64_t total = plane * n_mat;
+    if (block_id < 0 || block_id >= total)
         return -1;
     const tg::TileCoord t = tg::schedule_tile((int)tiles_m, (int)tiles_n, (int)n_mat,
                                               (int)group_m, (int)block_id);
@@ -751,6 +786,8 @@ int tg_schedule_tile(int64_t tiles_m, int64_t tiles_n, int64_t n_mat, int64_t gr
 
 int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col)
 {
+    if (cols < 0 || row < 0 || col < 0 || cols >= kMaxDim || row >= kMaxDim || col >= kMaxDim)
+        return -1;
     return tg::lds_offset_bytes(cols, row, col);
 }
 
