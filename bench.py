@@ -159,7 +159,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "attn", "qkv", "square8192",
-                                       "skinny", "small", "vendor", "copy", "sweep"],
+                                       "skinny", "small", "vendor", "copy", "sweep", "streamk"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -176,6 +176,9 @@ def main():
 
     if args.only == "sweep":
         run_sweep(torch, tg)
+        return
+    if args.only == "streamk":
+        run_stream_k_sweep(torch, tg)
         return
 
     if args.only == "copy":
@@ -577,6 +580,34 @@ def run_sweep(torch, tg):
         print(json.dumps({"shape": "bf16 %dx%dx%d" % (M, N, K), "ms": round(ms, 5),
                           "TFLOP/s": round(f / ms / 1e9, 1), "kernel": kern,
                           "library_TFLOP/s": round(f / ml / 1e9, 1)}), flush=True)
+        del X, W, Y
+        torch.cuda.empty_cache()
+
+
+def run_stream_k_sweep(torch, tg):
+    """Shapes whose 256 x 256 tiles leave a partial last wave, timed with
+    stream-K on and off (TG_STREAMK) in the same process, beside the ROCm
+    library; bf16, X ~ N(0,1), W ~ N(0, 1/K), one JSON object per shape."""
+    torch.manual_seed(0)
+    shapes = [(3072, 3072, 3072), (3584, 3584, 3584), (5120, 5120, 5120), (6144, 6144, 6144),
+              (7168, 7168, 7168), (2049, 4096, 4096), (5000, 4096, 4096), (3000, 11008, 4096),
+              (4608, 4096, 4096), (4096, 4096, 4096)]
+    for (M, N, K) in shapes:
+        X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        f = 2.0 * M * N * K
+        steps = max(20, min(1000, int(4e13 / f)))
+        rec = {"shape": "bf16 %dx%dx%d" % (M, N, K)}
+        for flag in ("1", "0"):
+            os.environ["TG_STREAMK"] = flag
+            ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, steps // 5 + 2)
+            rec["on" if flag == "1" else "off"] = {"TFLOP/s": round(f / ms / 1e9, 1),
+                                                   "kernel": tg.last_kernel()}
+        os.environ.pop("TG_STREAMK")
+        ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, steps // 5 + 2)
+        rec["library_TFLOP/s"] = round(f / ml / 1e9, 1)
+        print(json.dumps(rec), flush=True)
         del X, W, Y
         torch.cuda.empty_cache()
 

@@ -49,6 +49,13 @@ hipError_t launch_async(int, int, int, const GemmArgs &, int, int, float *, int 
 {
     reached("launch_async");
 }
+SkPlan plan_stream_k(const GemmArgs &, int, int, bool) { reached("plan_stream_k"); }
+size_t stream_k_ws_floats(const SkPlan &) { reached("stream_k_ws_floats"); }
+hipError_t launch_async_sk(int, int, int, const GemmArgs &, int, const SkPlan &, float *, int *,
+                           hipStream_t)
+{
+    reached("launch_async_sk");
+}
 bool mx_fast_eligible(const MxArgs &) { reached("mx_fast_eligible"); }
 hipError_t launch_mx(int, int, const MxArgs &, int, hipStream_t) { reached("launch_mx"); }
 hipError_t launch_mx_generic(int, int, const MxArgs &, hipStream_t) { reached("launch_mx_generic"); }

@@ -900,7 +900,8 @@ def test_projection_with_ragged_token_count(tg):
     p = inputs.problem(BF16, 3000, 11008, 4096, seed=252, kind="normal", b_scale=1 / 64)
     say("case projection 3000x11008x4096")
     bits, kern = run(tg, p)
-    assert kern == "async_256x256x32_s4_mfma16", kern
+    # 12 x 43 = 516 tiles: two whole waves plus 4 tiles, so stream-K
+    assert kern == "async_256x256x32_s4_mfma16_streamk", kern
     f64, rbits = oracle.gemm(BF16, p["A"], p["B"])
     util.check_tol(BF16, bits, f64, "projection", ref_bits=rbits)
 
@@ -1246,12 +1247,20 @@ def test_dispatch_choices(tg, monkeypatch):
     e = torch.zeros((1024, 2048), dtype=torch.float16, device="cuda")
     tg.gemm(e, c)
     assert tg.last_kernel() == "async_64x128x32_s4"
-    # partial last row tiles: an asynchronous kernel (128 x 128 tiles fill a
-    # wave at 2049 rows), never the forced-only 8-wave variant
+    # partial last row tiles: 144 tiles of 256 x 256 (more than half a wave,
+    # not a whole one) run stream-K; with stream-K off, the 128 x 128 tiles
+    # that fill a wave; never the forced-only 8-wave variant
     f = torch.zeros((2049, 4096), dtype=torch.float16, device="cuda")
     g = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
     tg.gemm(f, g)
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16_streamk", tg.last_kernel()
+    monkeypatch.setenv("TG_STREAMK", "0")
+    tg.gemm(f, g)
     assert tg.last_kernel() == "async_128x128x32_s4", tg.last_kernel()
+    monkeypatch.delenv("TG_STREAMK")
+    # whole waves (4096^3: 256 tiles) stay data-parallel
+    tg.gemm(g, g)
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
     monkeypatch.setenv("TG_SPLITK", "0")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x64x32_s4"

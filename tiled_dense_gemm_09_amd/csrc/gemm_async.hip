@@ -593,16 +593,20 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
     }
 }
 
-template <int DT, int ACT, int WN, bool BT>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
-                                                                    int tiles_n, int group_m)
+// The K loop of one 256 x 256 tile on the 16x16x32 MFMA: K-steps kt0 ..
+// kt0 + KT - 1 (KT a multiple of the four stages) of the tile at (m0, n0)
+// of the product with the weight Bm, accumulated into acc (which the caller
+// has initialised).  On return every copy has landed and every wave has
+// finished reading the stages, so the LDS is free.
+template <int DT, int WN, bool BT>
+__device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
+                                             const unsigned short *Bm, int kt0, int KT, int wave,
+                                             int lane, unsigned char *st0, unsigned char *st1,
+                                             unsigned char *st2, unsigned char *st3,
+                                             f32x4 (&acc)[8][16 / WN])
 {
     using Gm = A16Geom<WN, BT>;
     constexpr int NJ = Gm::NJ, CA = Gm::CA;
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[A16_STAGE];
     auto stage = [&](auto sidx) -> unsigned char * {
         constexpr int S = decltype(sidx)::value;
         if constexpr (S == 0)
@@ -614,23 +618,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
         else
             return st3;
     };
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_m = wave / WN, wave_n = wave % WN;
-
-    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
-    const int m0 = tc.tm * A16_BM, n0 = tc.tn * A16_BN;
-    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
-    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    const int KT = p.K / AS_BK;
+    const int wave_n = wave % WN;
+    const int wave_m = wave / WN;
 
     // copy c < CA: A copy q = CA w + c, rows 16 q .. 16 q + 15 (lane -> row
     // 16 q + lane / 4, granule lane % 4); c >= CA: B copy q = CA w + c - CA,
     // rows 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
     // B stored [N,K] (BT) is staged like A: [256 n][32 k] K-contiguous, B
     // copy q filling n-rows 16 q .. 16 q + 15 with the A swizzle.
+    const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
     const unsigned short *ga[CA], *gb[CA];
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
@@ -639,15 +635,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
         // rows past M (a last row tile that M does not fill) read row M-1:
         // every copy stays inside A, and those rows only reach outputs that
         // are never stored
-        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8;
+        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8 +
+                (int64_t)kt0 * AS_BK;
         if constexpr (BT) {
-            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8;
+            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8 +
+                    (int64_t)kt0 * AS_BK;
         } else {
             const int rb = 2 * q + (lane >> 5);
-            gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8);
+            gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) +
+                    (int64_t)kt0 * b_step;
         }
     }
-    const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
         if (c < CA) {
@@ -667,32 +665,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
             copy(kt, st, c);
     };
 
-    // accumulators start at bias[n] (or 0)
-    f32x4 acc[8][NJ];
-    const int q16 = lane >> 4;
-    if (p.bias != nullptr) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int bc = n0 + wave_n * Gm::WCOLS + 16 * j + 4 * q16;
-            const u32x2 braw = bc < p.N ? *reinterpret_cast<const u32x2 *>(p.bias + bc)
-                                        : u32x2{0u, 0u};
-            f32x4 b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                b[e] = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i][j] = b;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
     // fragment offsets within a stage
+    const int q16 = lane >> 4;
     int a_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -796,13 +770,50 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
+}
 
-    // each wave restages its tile in its own EP_BYTES of the (now idle) stages
+// Accumulators of a 16x16x32 wave tile set to bias[n] (or 0): lane l of
+// block (i, j) holds columns 16 j + 4 (l / 16) + {0..3} of the wave's
+// columns.
+template <int DT, int WN>
+__device__ __forceinline__ void a16_init_acc(const GemmArgs &p, int n0, int wave, int lane,
+                                             bool with_bias, f32x4 (&acc)[8][16 / WN])
+{
+    constexpr int NJ = 16 / WN, WCOLS = 16 * NJ;
+    const bool use = with_bias && p.bias != nullptr;
+    const int wave_n = wave % WN;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        if (use) {
+            const int bc = n0 + wave_n * WCOLS + 16 * j + 4 * (lane >> 4);
+            const u32x2 braw = bc < p.N ? *reinterpret_cast<const u32x2 *>(p.bias + bc)
+                                        : u32x2{0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                b[e] = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i][j] = b;
+    }
+}
+
+// Epilogue of a 16x16x32 wave tile: each wave restages its tile in its own
+// EP_BYTES of the (idle) stages and stores whole row segments.
+template <int DT, int ACT, int WN, bool BT>
+__device__ __forceinline__ void a16_epilogue(const GemmArgs &p, unsigned short *Cm, int m0, int n0,
+                                             int wave, int lane, unsigned char *st0,
+                                             unsigned char *st1, unsigned char *st2,
+                                             unsigned char *st3, const f32x4 (&acc)[8][16 / WN])
+{
+    using Gm = A16Geom<WN, BT>;
+    constexpr int NJ = Gm::NJ;
     constexpr int PER_STAGE = A16_STAGE / Gm::EP_BYTES; // wave tiles per stage
     const int es = wave / PER_STAGE;
     unsigned char *ep = (es == 0 ? st0 : es == 1 ? st1 : es == 2 ? st2 : st3) +
                         (wave % PER_STAGE) * Gm::EP_BYTES;
-    const int64_t cm = m0 + wave_m * 128, cn = n0 + wave_n * Gm::WCOLS;
+    const int64_t cm = m0 + (wave / WN) * 128, cn = n0 + (wave % WN) * Gm::WCOLS;
     unsigned short *cw = Cm + cm * p.ldc + cn;
     const int rows = (int)min((int64_t)128, (int64_t)p.M - cm);
     const int cols = (int)min((int64_t)Gm::WCOLS, (int64_t)p.N - cn);
@@ -811,6 +822,226 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
                                                p.ldr, rows, cols);
     else
         restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows, cols);
+}
+
+template <int DT, int ACT, int WN, bool BT>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
+                                                                    int tiles_n, int group_m)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[A16_STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int m0 = tc.tm * A16_BM, n0 = tc.tn * A16_BN;
+    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    f32x4 acc[8][16 / WN];
+    a16_init_acc<DT, WN>(p, n0, wave, lane, true, acc);
+    a16_mainloop<DT, WN, BT>(p, m0, n0, Bm, 0, p.K / AS_BK, wave, lane, st0, st1, st2, st3, acc);
+    a16_epilogue<DT, ACT, WN, BT>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K over the 256 x 256 16x16x32 tiles ("TIRx", section 4.3: work
+// partitioning decided at run time rather than by a static one-tile-per-
+// workgroup dispatch; "Beyond Hand-Written CUDA", section 2: the tile
+// scheduler stage).  A grid whose tile count is not a multiple of the
+// workgroups that run at once leaves a last, partly filled wave; here the
+// launch is persistent (plan.grid workgroups, one per compute unit) and
+//  - tiles 0 .. dp_tiles - 1 (whole waves) run data-parallel, each
+//    workgroup taking dp_tiles / grid consecutive ones;
+//  - the last sk_tiles tiles are cut into 128-deep K quads, units (tile,
+//    quad) in tile-major order, and workgroup w takes the contiguous units
+//    [w per, (w + 1) per): whole tiles it covers are finished directly, a
+//    tile it covers only in part gets its FP32 partial stored
+//    (device-coherent) in the workgroup's slot (2 w for its first piece,
+//    2 w + 1 for its last), counted in with one atomic, and the workgroup
+//    that completes the count adds every piece of the tile in K order (the
+//    piece starting at k = 0 carries the bias), runs the epilogue and
+//    resets the counter; a workgroup that finds the other piece of a
+//    two-piece tile already counted adds it to its own in registers
+//    instead of storing.  No workgroup ever waits for another.
+// Slot layout: [4 waves][64 vectors][64 lanes] of 16 bytes (vector 8 j + i
+// holds accumulator block (i, j)), 256 KiB per slot.
+namespace {
+constexpr int SK_SLOT_FLOATS = 256 * 256;
+} // namespace
+
+template <int DT, int ACT, int WN, bool BT>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p, int tiles_m,
+                                                                       int tiles_n, int group_m,
+                                                                       SkPlan sk, float *ws,
+                                                                       int *counters)
+{
+    static_assert(WN == 2, "stream-K on the 4-wave 16x16x32 kernel");
+    constexpr int NJ = 16 / WN, PV = 8 * NJ; // 64 accumulator vectors per lane
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[A16_STAGE];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // XCD-aware placement: workgroup b runs on XCD b % 8, so it takes the
+    // place v = (b % 8) (grid / 8) + b / 8 (grid a multiple of 8): each XCD
+    // works through one contiguous run of data-parallel tiles and one of
+    // split units, in grouped tile order, and its L2 keeps their panels.
+    const int per_xcd = sk.grid / kNumXcd;
+    const int w = ((int)blockIdx.x % kNumXcd) * per_xcd + (int)blockIdx.x / kNumXcd;
+    const int Q = sk.q;
+    f32x4 acc[8][NJ];
+
+    // Each pass of the loops below takes lane and wave through an empty asm
+    // statement, so the compiler cannot hoist the lane-dependent address
+    // arithmetic of the K loop and the epilogue out of the persistent loop
+    // (kept live across it, that arithmetic spills hundreds of registers).
+    auto opaque = [&](int &ln, int &wv) {
+        ln = lane;
+        wv = wave;
+        asm volatile("" : "+v"(ln), "+s"(wv));
+    };
+    auto coords = [&](int logical, int &m0, int &n0, const unsigned short *&Bm,
+                      unsigned short *&Cm) {
+        const TileCoord tc = grouped_tile(tiles_m, tiles_n, p.n_mat, group_m, logical);
+        m0 = tc.tm * A16_BM;
+        n0 = tc.tn * A16_BN;
+        Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+        Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    };
+    // Work of this workgroup: its whole tiles of the data-parallel waves,
+    // then its units [u0, u1) of the split tiles, taken
+    // last piece first: the head of a tile (its K start) is then published
+    // early by the workgroup before, and the tail, computed last, usually
+    // finishes the tile.  One loop with one K loop and one epilogue (two
+    // inlined copies of each grow the function past what the compiler
+    // unrolls, and the accumulators end up on the stack).
+    // data-parallel tiles (dp_tiles is a whole number of waves): the XCD's
+    // run of per_xcd per_dp tiles, one contiguous slice of per_xcd tiles per
+    // round
+    const int per_dp = sk.dp_tiles / sk.grid;
+    const int n_dp = per_dp;
+    const int units = sk.sk_tiles * Q;
+    const int u0 = w * sk.per, u1 = min(units, u0 + sk.per);
+    int i_dp = 0, u = u1; // split units still to do: [u0, u)
+    while (i_dp < n_dp || u > u0) {
+        int logical, q0, q1, ts = -1;
+        bool first_piece = false;
+        if (i_dp < n_dp) {
+            logical = (w / per_xcd) * per_xcd * per_dp + i_dp * per_xcd + w % per_xcd;
+            q0 = 0;
+            q1 = Q;
+            ++i_dp;
+        } else {
+            ts = (u - 1) / Q; // stream-K tile of the last unit left
+            q1 = u - ts * Q;
+            q0 = max(0, q1 - (u - u0));
+            logical = sk.dp_tiles + ts;
+            first_piece = ts * Q + q0 == u0;
+            u -= q1 - q0;
+        }
+        int m0, n0;
+        const unsigned short *Bm;
+        unsigned short *Cm;
+        coords(logical, m0, n0, Bm, Cm);
+        int ln, wv;
+        opaque(ln, wv);
+        a16_init_acc<DT, WN>(p, n0, wv, ln, q0 == 0, acc);
+        a16_mainloop<DT, WN, BT>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv, ln, st0, st1, st2, st3,
+                                 acc);
+        bool finish = q0 == 0 && q1 == Q;
+        if (!finish) {
+            // pieces of tile ts: workgroups w_first .. w_last, piece s stored
+            // in slot 2 (w_first + s) (+ 1 for the first piece when the tile
+            // does not start that workgroup's range: it is then that
+            // workgroup's last piece)
+            const int w_first = (ts * Q) / sk.per;
+            const int w_last = ((ts + 1) * Q - 1) / sk.per;
+            const int n_pieces = w_last - w_first + 1;
+            const int lane_off = wv * PV * 256 + ln * 4;
+            auto slot_of = [&](int wp) {
+                return ws + (int64_t)(2 * wp + (wp == w_first && ts * Q != wp * sk.per ? 1 : 0)) *
+                                SK_SLOT_FLOATS +
+                       lane_off;
+            };
+            // half hh: vectors 32 hh .. 32 hh + 31 = blocks (i, j), j in 4 hh .. 4 hh + 3
+            auto add_half = [&](auto hc, const float *src) {
+                constexpr int hh = decltype(hc)::value;
+                f32x4 v[32];
+                load_partial32(src + hh * 32 * 256, v);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc[i][4 * hh + jj] += v[8 * jj + i];
+            };
+            // Every other piece of a two-piece tile already in: keep this one
+            // in registers and add the other (a + b == b + a, so the bits do
+            // not depend on which piece finishes; no piece is -0, since each
+            // starts from +0 or from the bias, so 0 + a + b on the stored
+            // path below gives the same bits).  Tiles of three pieces always
+            // take the stored path, which adds in K order.
+            if (threadIdx.x == 0)
+                s_last = n_pieces == 2 && __hip_atomic_load(&counters[ts], __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT) == 1;
+            __syncthreads();
+            const bool in_registers = s_last;
+            if (!in_registers) {
+                float *dst =
+                    ws + (int64_t)(2 * w + (first_piece ? 0 : 1)) * SK_SLOT_FLOATS + lane_off;
+                auto store_half = [&](auto hc) {
+                    constexpr int hh = decltype(hc)::value;
+                    f32x4 v[32];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            v[8 * jj + i] = acc[i][4 * hh + jj];
+                    store_partial<32>(dst + hh * 32 * 256, v);
+                };
+                static_assert(PV == 64, "two halves of 32 vectors");
+                store_half(std::integral_constant<int, 0>{});
+                store_half(std::integral_constant<int, 1>{});
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    const int old = __hip_atomic_fetch_add(&counters[ts], 1, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                    s_last = (old == n_pieces - 1);
+                }
+                __syncthreads();
+                if (s_last) {
+                    // the last piece in: every piece comes from memory
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            finish = s_last;
+            if (finish) {
+                // add the pieces in K order (the own one is already in the
+                // registers when it stayed there)
+                for (int wp = w_first; wp <= w_last; ++wp) {
+                    if (in_registers && wp == w)
+                        continue;
+                    add_half(std::integral_constant<int, 0>{}, slot_of(wp));
+                    add_half(std::integral_constant<int, 1>{}, slot_of(wp));
+                }
+            }
+            if (finish && threadIdx.x == 0)
+                __hip_atomic_store(&counters[ts], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (finish) {
+            // the epilogue restages through the stages: every wave is done
+            // with them before the next tile's copies land there
+            a16_epilogue<DT, ACT, WN, BT>(p, Cm, m0, n0, wv, ln, st0, st1, st2, st3, acc);
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            stage_barrier();
+        }
+    }
 }
 
 namespace {
@@ -885,6 +1116,82 @@ size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 {
     return (size_t)splits * (size_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat *
            async_tile_m(cfg) * async_tile_n(cfg);
+}
+
+SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
+{
+    SkPlan pl{0, 0, 0, 0, 0};
+    if (kAsyncConfigs[cfg].mfma16 != 4 || !async_eligible(a, cfg) || cus <= 0 ||
+        cus % kNumXcd != 0)
+        return pl;
+    const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
+    const int q = a.K / (AS_STAGES * AS_BK);
+    // whole waves need no split; below half a wave each tile would be cut
+    // into more than two pieces (smaller tiles do better there)
+    if (tiles % cus == 0 || 2 * tiles < cus || q < 2 || tiles >= (int64_t)1 << 24)
+        return pl;
+    const int64_t full = tiles / cus, rest = tiles % cus;
+    // After whole waves, a last wave of at least half the compute units stays
+    // data-parallel: the kernel is power-bound, and such a wave runs at a
+    // higher clock than a full one, which recovers most of what the idle
+    // units cost (measured: 5120^3, 400 tiles, 1222 TFLOP/s data-parallel
+    // against 1149 with the last 144 tiles split).
+    if (full >= 1 && 2 * rest >= cus)
+        return pl;
+    // Split tiles: all of them when there is no whole wave, else the short
+    // last wave plus one whole wave, so that no tile is cut into more than
+    // about two pieces.  The waves before run whole, in lockstep over K,
+    // which keeps their panels in L2.
+    const int64_t sk_tiles = full == 0 ? tiles : rest + cus;
+    const int64_t units = sk_tiles * q;
+    const int64_t per = (units + cus - 1) / cus;
+    // each workgroup's share of the split tiles must be long enough to pay
+    // for the partial exchange and for running out of lockstep: at least 16
+    // quads (K = 2048) unless any_size (measured: 3072^3, 144 tiles of 14
+    // quads each, is faster on 128 x 128 tiles)
+    if (per < 16 && !any_size)
+        return pl;
+    pl.dp_tiles = (int)(tiles - sk_tiles);
+    pl.sk_tiles = (int)sk_tiles;
+    pl.q = q;
+    pl.per = (int)per;
+    pl.grid = cus; // places past the last unit get data-parallel tiles only
+    return pl;
+}
+
+size_t stream_k_ws_floats(const SkPlan &sk) { return (size_t)2 * sk.grid * SK_SLOT_FLOATS; }
+
+hipError_t launch_async_sk(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                           const SkPlan &sk, float *ws, int *counters, hipStream_t s)
+{
+    if (kAsyncConfigs[cfg].mfma16 != 4 || sk.sk_tiles <= 0 || sk.grid <= 0 || sk.q <= 0 ||
+        sk.per <= 0 || ws == nullptr || counters == nullptr || sk.grid % kNumXcd != 0 ||
+        (int64_t)sk.per * sk.grid < (int64_t)sk.sk_tiles * sk.q || sk.dp_tiles % sk.grid != 0)
+        return hipErrorInvalidValue;
+    const int tiles_m = async_tiles_m(a, cfg), tiles_n = async_tiles_n(a, cfg);
+    dim3 grid(sk.grid), block(A16Geom<2, false>::NT);
+#define TG_SK(DT_, ACT_)                                                                         \
+    do {                                                                                         \
+        if (a.b_trans)                                                                           \
+            hipLaunchKernelGGL((gemm_async16_sk_kernel<DT_, ACT_, 2, true>), grid, block, 0, s,  \
+                               a, tiles_m, tiles_n, group_m, sk, ws, counters);                  \
+        else                                                                                     \
+            hipLaunchKernelGGL((gemm_async16_sk_kernel<DT_, ACT_, 2, false>), grid, block, 0, s, \
+                               a, tiles_m, tiles_n, group_m, sk, ws, counters);                  \
+    } while (0)
+    if (dt == DT_F16) {
+        if (act == ACT_GELU)
+            TG_SK(DT_F16, ACT_GELU);
+        else
+            TG_SK(DT_F16, ACT_NONE);
+    } else {
+        if (act == ACT_GELU)
+            TG_SK(DT_BF16, ACT_GELU);
+        else
+            TG_SK(DT_BF16, ACT_NONE);
+    }
+#undef TG_SK
+    return hipGetLastError();
 }
 
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,

@@ -193,6 +193,28 @@ void *get_scratch(hipStream_t stream, tg_status *st)
     return g_scratch[dev];
 }
 
+// Compute units of the current device (workgroups of the persistent
+// stream-K grid), looked up once per device; 256 if the runtime cannot say.
+int device_cus()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int env_int(const char *name, int dflt)
 {
     const char *e = getenv(name);
@@ -407,7 +429,47 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                                                      : " (no K padding: no workspace)";
         }
     }
-    if (unal_tiled) {
+    // Stream-K: the 4-wave 256 x 256 configuration when its tiles leave a
+    // partial last wave (unforced, or forced by name); TG_STREAMK=0 turns it
+    // off, TG_STREAMK=2 also takes shapes whose K share per workgroup is
+    // short.  It needs the workspace for its partial tiles; without one (a
+    // capture that would grow it, no memory) the tiles run data-parallel.
+    tg::SkPlan sk{0, 0, 0, 0, 0};
+    int sk_cfg = -1;
+    void *sk_base = nullptr;
+    const char *sk_note = nullptr;
+    const int sk_mode = env_int("TG_STREAMK", 1);
+    if (fast && !noalloc && !force_generic && !force_tiled && sk_mode != 0 &&
+        !(n_mat == 1 && M <= 32)) {
+        for (int i = 0; i < tg::num_async_configs() && sk_cfg < 0; ++i) {
+            if (tg::async_forced_only(i) ||
+                (force && *force && strcmp(force, tg::async_config_name(i)) != 0))
+                continue;
+            sk = tg::plan_stream_k(a, i, device_cus(), sk_mode == 2);
+            if (sk.sk_tiles > 0)
+                sk_cfg = i;
+        }
+        if (sk_cfg >= 0) {
+            tg_status st = TG_SUCCESS;
+            static_assert(tg::kMaxSplitTiles * sizeof(int) <= kCounterBytes, "counter room");
+            sk_base = sk.sk_tiles <= tg::kMaxSplitTiles
+                          ? get_workspace(tg::stream_k_ws_floats(sk), s, &st)
+                          : nullptr;
+            if (!sk_base) {
+                sk_note = st == TG_ERROR_NOT_SUPPORTED ? " (no stream-K: stream capture)"
+                                                       : " (no stream-K: no workspace)";
+                sk_cfg = -1;
+            }
+        }
+    }
+    if (sk_cfg >= 0) {
+        const int group_m = env_int("TG_GROUP_M", 4);
+        err = tg::launch_async_sk(sk_cfg, kdt, kact, a, group_m > 0 ? group_m : 4, sk,
+                                  reinterpret_cast<float *>(static_cast<char *>(sk_base) +
+                                                            kCounterBytes),
+                                  static_cast<int *>(sk_base), s);
+        set_last(tg::async_config_name(sk_cfg), "_streamk");
+    } else if (unal_tiled) {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * n_mat;
@@ -471,9 +533,11 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         }
         err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, splits, ws, counters,
                                s);
-        char detail[24] = "";
+        char detail[64] = "";
         if (splits > 1)
             snprintf(detail, sizeof detail, "_splitk%d", splits);
+        else if (sk_note)
+            snprintf(detail, sizeof detail, "%s", sk_note);
         set_last(tg::async_config_name(cfg), detail);
     } else if (kpad) {
         // K off the 128 grid on a large problem: A and B copied with K

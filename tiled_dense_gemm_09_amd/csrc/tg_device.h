@@ -39,15 +39,11 @@ struct TileCoord {
 //    the fused QKV projection the n_mat = 3 matrices sit side by side in the
 //    virtual grid and reuse the same row-panels of X.
 // Both steps are bijections, so every tile is computed exactly once.
-__host__ __device__ inline TileCoord schedule_tile(int tiles_m, int tiles_n, int n_mat,
-                                                   int group_m, int bid)
+// Step 2 alone: logical id -> tile in grouped order (a bijection of
+// [0, tiles_m * tiles_n * n_mat) onto the tiles).
+__host__ __device__ inline TileCoord grouped_tile(int tiles_m, int tiles_n, int n_mat, int group_m,
+                                                  int logical)
 {
-    const int total = tiles_m * tiles_n * n_mat;
-    const int xcd = bid % kNumXcd;
-    const int slot = bid / kNumXcd;
-    const int q = total / kNumXcd, r = total % kNumXcd;
-    const int logical = xcd * q + (xcd < r ? xcd : r) + slot;
-
     const int width = tiles_n * n_mat;
     const int group_size = group_m * width;
     const int g = logical / group_size;
@@ -61,6 +57,17 @@ __host__ __device__ inline TileCoord schedule_tile(int tiles_m, int tiles_n, int
     t.mat = tv / tiles_n;
     t.tn = tv - t.mat * tiles_n;
     return t;
+}
+
+// Both steps: workgroup id -> tile.
+__host__ __device__ inline TileCoord schedule_tile(int tiles_m, int tiles_n, int n_mat,
+                                                   int group_m, int bid)
+{
+    const int total = tiles_m * tiles_n * n_mat;
+    const int xcd = bid % kNumXcd;
+    const int slot = bid / kNumXcd;
+    const int q = total / kNumXcd, r = total % kNumXcd;
+    return grouped_tile(tiles_m, tiles_n, n_mat, group_m, xcd * q + (xcd < r ? xcd : r) + slot);
 }
 
 // LDS tiles store rows of `cols` 16-bit elements with the row pitch padded by
@@ -220,7 +227,20 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c)
 template <int PV>
 __device__ __forceinline__ void store_partial(float *dst, const f32x4 (&v)[PV])
 {
-    if constexpr (PV == 16) {
+    if constexpr (PV == 32) {
+        asm volatile(TG_ST4(0, 8, 9, 10, 11) TG_ST4(1, 12, 13, 14, 15) TG_ST4(2, 16, 17, 18, 19)
+                         TG_ST4(3, 20, 21, 22, 23) TG_ST4(4, 24, 25, 26, 27)
+                             TG_ST4(5, 28, 29, 30, 31) TG_ST4(6, 32, 33, 34, 35)
+                                 TG_ST4(7, 36, 37, 38, 39) "s_waitcnt vmcnt(0)" ::"v"(dst),
+                     "v"(dst + 1024), "v"(dst + 2048), "v"(dst + 3072), "v"(dst + 4096),
+                     "v"(dst + 5120), "v"(dst + 6144), "v"(dst + 7168), "v"(v[0]), "v"(v[1]),
+                     "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+                     "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]),
+                     "v"(v[15]), "v"(v[16]), "v"(v[17]), "v"(v[18]), "v"(v[19]), "v"(v[20]),
+                     "v"(v[21]), "v"(v[22]), "v"(v[23]), "v"(v[24]), "v"(v[25]), "v"(v[26]),
+                     "v"(v[27]), "v"(v[28]), "v"(v[29]), "v"(v[30]), "v"(v[31])
+                     : "memory");
+    } else if constexpr (PV == 16) {
         asm volatile(TG_ST4(0, 4, 5, 6, 7) TG_ST4(1, 8, 9, 10, 11) TG_ST4(2, 12, 13, 14, 15)
                          TG_ST4(3, 16, 17, 18, 19) "s_waitcnt vmcnt(0)" ::"v"(dst),
                      "v"(dst + 1024), "v"(dst + 2048), "v"(dst + 3072), "v"(v[0]), "v"(v[1]),
@@ -247,5 +267,33 @@ __device__ __forceinline__ void store_partial(float *dst, const f32x4 (&v)[PV])
     }
 }
 #undef TG_ST4
+
+// The counterpart of store_partial<32>: loads 32 16-byte vectors at src +
+// 1 KiB v with device-coherent loads (sc1) and waits for them, all in one asm
+// statement, so no result register is read (or copied) before its data has
+// landed.
+#define TG_LD4(B, V0, V1, V2, V3)                                                                   \
+    "global_load_dwordx4 %" #V0 ", %" #B ", off sc1\n\t"                                        \
+    "global_load_dwordx4 %" #V1 ", %" #B ", off offset:1024 sc1\n\t"                            \
+    "global_load_dwordx4 %" #V2 ", %" #B ", off offset:2048 sc1\n\t"                            \
+    "global_load_dwordx4 %" #V3 ", %" #B ", off offset:3072 sc1\n\t"
+__device__ __forceinline__ void load_partial32(const float *src, f32x4 (&v)[32])
+{
+    asm volatile(TG_LD4(32, 0, 1, 2, 3) TG_LD4(33, 4, 5, 6, 7) TG_LD4(34, 8, 9, 10, 11)
+                     TG_LD4(35, 12, 13, 14, 15) TG_LD4(36, 16, 17, 18, 19)
+                         TG_LD4(37, 20, 21, 22, 23) TG_LD4(38, 24, 25, 26, 27)
+                             TG_LD4(39, 28, 29, 30, 31) "s_waitcnt vmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]),
+                   "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]),
+                   "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]),
+                   "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]),
+                   "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]),
+                   "=&v"(v[31])
+                 : "v"(src), "v"(src + 1024), "v"(src + 2048), "v"(src + 3072), "v"(src + 4096),
+                   "v"(src + 5120), "v"(src + 6144), "v"(src + 7168)
+                 : "memory");
+}
+#undef TG_LD4
 
 } // namespace tg

@@ -78,6 +78,27 @@ size_t async_ws_floats(const GemmArgs &a, int cfg, int splits);
 hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m, int splits,
                         float *ws, int *counters, hipStream_t stream);
 
+// Stream-K over the 256 x 256 tiles of the 4-wave 16x16x32 kernel: a
+// persistent grid of `grid` workgroups; logical tiles 0 .. dp_tiles - 1
+// run whole (data-parallel), the last sk_tiles are split into 128-deep K
+// quads (q per tile), `per` consecutive (tile, quad) units per workgroup.
+// sk_tiles == 0: stream-K does not apply (the tiles fill whole waves, leave
+// a last wave of at least half the compute units after whole ones, are
+// fewer than half a wave, K is shorter than two quads or each workgroup's
+// share shorter than 16, another configuration).
+struct SkPlan {
+    int dp_tiles, sk_tiles, q, per, grid;
+};
+// cus: workgroups that run at once (one per compute unit); any_size also
+// splits shapes whose per-workgroup share of K is short (tests)
+SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size);
+// FP32 workspace: two 256 x 256 partial slots per workgroup; the counters
+// (one int per stream-K tile, zero before the launch and after it) are
+// separate.
+size_t stream_k_ws_floats(const SkPlan &sk);
+hipError_t launch_async_sk(int cfg, int dt, int act, const GemmArgs &a, int group_m,
+                           const SkPlan &sk, float *ws, int *counters, hipStream_t stream);
+
 // Block-scaled 8-bit GEMM: C = act(sum_k a(A[m][k]) 2^(SA[k/32][m]-127)
 // * b(B[n][k]) 2^(SB[k/32][n]-127) + bias[n]).  A [M,K] and B [N,K] bytes
 // (pitches in bytes), SA [K/32][M] and SB [K/32][N] e8m0 bytes, bias and C
