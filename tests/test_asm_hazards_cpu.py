@@ -43,7 +43,10 @@ def _regs(text):
 def scan(asm_text):
     """[(function, outstanding instruction, offending instruction)]"""
     found = []
+    objects = set(re.findall(r"^\s*\.type\s+(_ZN2tg\w+),\s*@object", asm_text, re.M))
     for fn in re.findall(r"^(_ZN2tg\w+):", asm_text, re.M):
+        if fn in objects:  # data symbols (e.g. a zero granule) carry no code
+            continue
         a = asm_text.index(fn + ":")
         b = asm_text.index(".Lfunc_end", a)
         in_asm = False

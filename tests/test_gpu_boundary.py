@@ -50,10 +50,11 @@ def capture(fn):
 
 
 def test_cold_k_padding_call_under_capture_takes_a_kernel_without_workspace(tg):
-    # K off the 128 grid on a large problem normally copies A and B into the
-    # workspace with K padded.  When the workspace would have to grow during
-    # a capture, the call runs the tiled kernel (no workspace) instead; the
-    # graph then replays correctly, with eager work between the replays.
+    # K off the 8-element grid on a large problem normally copies A and B
+    # into the workspace with K padded.  When the workspace would have to
+    # grow during a capture, the call runs the tiled kernel (no workspace)
+    # instead; the graph then replays correctly, with eager work between the
+    # replays.
     import torch
     w0 = tg.workspace_bytes()
     n = 1024
@@ -61,9 +62,12 @@ def test_cold_k_padding_call_under_capture_takes_a_kernel_without_workspace(tg):
         n *= 2
     if n > 8192:
         pytest.skip("workspace already %d bytes" % w0)
-    M, N, K = n, n, n + 8  # K rounds up to n + 128: 120 padded k, at most K / 8
+    M, N, K = n, n, n + 4  # K rounds up to n + 128: 124 padded k, at most K / 8
     p = inputs.problem(F16, M, N, K, seed=700, kind="int", bias=True, bias_kind="int")
-    A, B = util.to_dev(p["A"], F16), util.to_dev(p["B"], F16)
+    # A in a buffer whose pitch (n + 8) is a multiple of 8, NaN in the padding
+    abuf = np.full((M, n + 8), 0x7E00, np.uint16)
+    abuf[:, :K] = p["A"]
+    A, B = util.to_dev(abuf, F16)[:, :K], util.to_dev(p["B"], F16)
     bias = util.to_dev(p["bias"], F16)
     C = torch.empty((M, N), dtype=torch.float16, device="cuda")
     say("case cold K padding under capture", M, N, K, "workspace", w0)

@@ -815,26 +815,86 @@ def test_partial_column_tile_split_k_and_qkv(tg, monkeypatch):
         util.check_exact(outs[t], ref, "partial column tile qkv [%d]" % t)
 
 
-KPAD_CASES = [
-    # (dt, M, N, K): K off the 128 grid on problems of >= 2^30 multiply-adds;
-    # the padded problems take 64 x 64, 128 x 128 and 64 x 128 tiles
-    (F16, 1000, 1200, 1000),
-    (BF16, 2000, 2000, 2000),
-    (F16, 1536, 2048, 1928),
+KMASK_CASES = [
+    # (dt, M, N, K, forced configuration or None): K a multiple of 8 off the
+    # 128 grid on the 256 x 256 16x16x32 tiles (chosen with a full wave of
+    # them, or forced): the whole 128-deep quads on the unmasked loop, then
+    # the last quad with the k past K read as zeros; K below one quad (72)
+    # runs the masked quad alone
+    (F16, 4000, 4000, 1000, None),
+    (BF16, 4096, 3840, 2000, None),
+    (BF16, 512, 512, 200, "async_256x256x32_s4_mfma16"),
+    (F16, 512, 512, 72, "async_256x256x32_s4_mfma16"),
+    (BF16, 768, 512, 4040, "async_256x256x32_s4_mfma16"),
 ]
 
 
-def test_k_padding_is_capped_at_an_eighth(tg):
-    # K = 520 would pad to 640 (23 % more multiply-adds): the tiled kernel
-    # runs instead; K = 1000 pads to 1024 (2.4 %)
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("dt,M,N,K,force", KMASK_CASES)
+def test_k_off_the_loop_grid_integer_exact(tg, monkeypatch, dt, M, N, K, force, trans_b):
+    # A and B sit in buffers whose pitch padding holds NaN: the kernels must
+    # read only k < K.  Integer operands, bias and residual: bit-exact.
     import torch
-    for K, padded in ((520, False), (1000, True)):
-        a = torch.zeros((1536, K), dtype=torch.float16, device="cuda")
-        b = torch.zeros((K, 2048), dtype=torch.float16, device="cuda")
+    if force:
+        monkeypatch.setenv("TG_FORCE_CONFIG", force)
+    p = inputs.problem(dt, M, N, K, seed=280 + K, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(281 + M), (M, N), "int", dt, 8.0)
+    A = util.to_dev(padded(p["A"], K + 8, dt), dt)[:, :K]
+    if trans_b:
+        b = util.to_dev(padded(np.ascontiguousarray(p["B"].T), K + 8, dt), dt)[:, :K].t()
+    else:
+        b = util.to_dev(padded(p["B"], N + 8, dt), dt)[:, :N]
+    bias = util.to_dev(p["bias"], dt)
+    say("case K off the grid", dt, M, N, K, "B[N,K]" if trans_b else "B[K,N]", force or "")
+    C = tg.gemm(A, b, bias=bias, residual=util.to_dev(R, dt))
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("async_") and not kern.endswith("_kpad"), kern
+    if force:
+        assert kern == force, kern
+    _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
+                            trans_b=trans_b, bias=p["bias"], R=R)
+    util.check_exact(util.to_bits(C), ref, "K off the grid " + kern)
+
+
+def test_k_off_the_loop_grid_gelu_random(tg):
+    p = inputs.problem(BF16, 4096, 4096, 2000, seed=290, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.1, b_scale=0.1)
+    say("case K off the grid, gelu 4096 x 4096 x 2000")
+    bits, kern = run(tg, p)
+    assert kern.startswith("async_") and not kern.endswith("_kpad"), kern
+    f64, rbits = oracle.gemm(BF16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(BF16, bits, f64, "K off the grid, gelu", ref_bits=rbits)
+
+
+KPAD_CASES = [
+    # (dt, M, N, K): K off the 8-element grid (pitches padded to it) on
+    # problems of >= 2^30 multiply-adds: A and B are copied with K rounded
+    # up to 128 and zeros in the added entries
+    (F16, 1000, 1200, 1004),
+    (BF16, 2000, 2000, 1995),
+]
+
+
+def test_k_dispatch_off_the_grids(tg):
+    # 4096 x 4096 outputs (a full wave of 256 x 256 tiles): K = 520, the
+    # masked loop (120 padded k, fewer than K); K = 36: 92 padded k would be
+    # more than K, the tiled kernel; K = 1004 (off the 8-element grid, 20
+    # padded k): K padding; K = 524 (116 padded k, more than K / 8): the tiled
+    # kernel.  1536 x 2048 outputs (48 tiles, under a wave): K = 1000 is
+    # padded instead of masked
+    import torch
+    for (M, N), K, ld, expect in (((4096, 4096), 520, 520, "async_256x256x32_s4_mfma16"),
+                                  ((4096, 4096), 36, 40, "tiled_"),
+                                  ((4096, 4096), 1004, 1008, "_kpad"),
+                                  ((4096, 4096), 524, 528, "tiled_"),
+                                  ((1536, 2048), 1000, 1000, "_kpad")):
+        a = torch.zeros((M, ld), dtype=torch.float16, device="cuda")[:, :K]
+        b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
         tg.gemm(a, b)
         kern = tg.last_kernel()
-        assert kern.endswith("_kpad") == padded, (K, kern)
-        assert padded or kern.startswith("tiled_"), kern
+        assert kern == expect or kern.startswith(expect) or kern.endswith(expect), (K, kern)
     torch.cuda.synchronize()
 
 
@@ -846,9 +906,10 @@ def test_k_padded_to_the_loop_integer_exact(tg, dt, M, N, K, trans_b):
     import torch
     p = inputs.problem(dt, M, N, K, seed=280 + K, kind="int", bias=True, bias_kind="int")
     R = inputs.draw(np.random.default_rng(281 + M), (M, N), "int", dt, 8.0)
-    A = util.to_dev(padded(p["A"], K + 8, dt), dt)[:, :K]
+    ldk = round8(K + 8)
+    A = util.to_dev(padded(p["A"], ldk, dt), dt)[:, :K]
     if trans_b:
-        b = util.to_dev(padded(np.ascontiguousarray(p["B"].T), K + 8, dt), dt)[:, :K].t()
+        b = util.to_dev(padded(np.ascontiguousarray(p["B"].T), ldk, dt), dt)[:, :K].t()
     else:
         b = util.to_dev(padded(p["B"], N + 8, dt), dt)[:, :N]
     bias = util.to_dev(p["bias"], dt)
@@ -861,16 +922,6 @@ def test_k_padded_to_the_loop_integer_exact(tg, dt, M, N, K, trans_b):
     _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
                             trans_b=trans_b, bias=p["bias"], R=R)
     util.check_exact(util.to_bits(C), ref, "K padded " + kern)
-
-
-def test_k_padded_gelu_random(tg):
-    p = inputs.problem(BF16, 2000, 2000, 2000, seed=290, bias=True, act=inputs.ACT_GELU_TANH,
-                       a_scale=0.1, b_scale=0.1)
-    say("case K padded gelu 2000^3")
-    bits, kern = run(tg, p)
-    assert kern.endswith("_kpad"), kern
-    f64, rbits = oracle.gemm(BF16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
-    util.check_tol(BF16, bits, f64, "K padded gelu", ref_bits=rbits)
 
 
 def test_partial_row_tile_gelu_random_and_qkv(tg, monkeypatch):

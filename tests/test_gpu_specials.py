@@ -82,6 +82,12 @@ FAMILIES = [
      "async_64x64x32_s4"),
     ("async32_splitk", {"TG_FORCE_CONFIG": "async_128x128x32_s4", "TG_SPLITK": "2"}, BF16, 256,
      256, 256, False, "async_128x128x32_s4_splitk2"),
+    # K off the 128 grid: the masked loop (the planted -inf at k = K - 1 sits
+    # just inside the mask)
+    ("async16_kmask", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"}, F16, 512, 512, 200,
+     False, "async_256x256x32_s4_mfma16"),
+    ("async16_kmask_bt", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"}, BF16, 512, 512,
+     392, True, "async_256x256x32_s4_mfma16"),
     ("tiled_256", {"TG_FORCE_CONFIG": "tiled_256x256x64_w2x2"}, F16, 512, 512, 256, False,
      "tiled_256x256x64_w2x2"),
     ("tiled_128_edges", {"TG_FORCE_CONFIG": "tiled_128x128x64_w2x2"}, BF16, 200, 136, 104, False,

@@ -66,6 +66,14 @@ struct AsGeom {
 
 } // namespace
 
+// K not a multiple of the 128-deep loop (KM kernels): the last, partial
+// quad's copies whose 8 k (A, B stored [N,K]) or whose k row (B stored
+// [K,N]) lie at or past K read this zero granule instead,
+// so the added k terms multiply exact zeros on both sides ("TIRx", section
+// 5.2: out-of-bounds reads give zeros, judged by the logical coordinate).
+// K must be a multiple of 8, so a granule is never cut by K.
+__device__ __align__(16) unsigned int kZeroGranule[4];
+
 // Split-K partial exchange of one workgroup (see the kernel below).  The
 // partial of a tile's split is [4 waves][4 TI TJ vectors][64 lanes] of
 // 16-byte vectors, vector 4 (TJ i + j) + g holding registers 4g..4g+3 of
@@ -598,7 +606,7 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
 // of the product with the weight Bm, accumulated into acc (which the caller
 // has initialised).  On return every copy has landed and every wave has
 // finished reading the stages, so the LDS is free.
-template <int DT, int WN, bool BT>
+template <int DT, int WN, bool BT, bool KM>
 __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
                                              const unsigned short *Bm, int kt0, int KT, int wave,
                                              int lane, unsigned char *st0, unsigned char *st1,
@@ -627,36 +635,44 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
     // B stored [N,K] (BT) is staged like A: [256 n][32 k] K-contiguous, B
     // copy q filling n-rows 16 q .. 16 q + 15 with the A swizzle.
     const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
+    // KM: copy c of step kt is inside K iff kt * 32 < a_kl[c] (b_kl[c])
     const unsigned short *ga[CA], *gb[CA];
+    int a_kl[CA], b_kl[CA];
+    const unsigned short *zero = reinterpret_cast<const unsigned short *>(kZeroGranule);
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
         const int q = wave * CA + c;
         const int ra = 16 * q + (lane >> 2);
+        const int ka = ((lane & 3) ^ swz_a(ra)) * 8;
         // rows past M (a last row tile that M does not fill) read row M-1:
         // every copy stays inside A, and those rows only reach outputs that
         // are never stored
-        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ((lane & 3) ^ swz_a(ra)) * 8 +
-                (int64_t)kt0 * AS_BK;
+        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ka + (int64_t)kt0 * AS_BK;
+        a_kl[c] = p.K - kt0 * AS_BK - ka;
         if constexpr (BT) {
-            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ((lane & 3) ^ swz_a(ra)) * 8 +
-                    (int64_t)kt0 * AS_BK;
+            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ka + (int64_t)kt0 * AS_BK;
+            b_kl[c] = a_kl[c];
         } else {
             const int rb = 2 * q + (lane >> 5);
             gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) +
                     (int64_t)kt0 * b_step;
+            b_kl[c] = p.K - kt0 * AS_BK - rb;
         }
     }
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
         if (c < CA) {
             const unsigned dst = lds + (wave * CA + c) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ga[c] + kt * AS_BK), "{m0}"(dst)
-                         : "memory");
+            const unsigned short *src = ga[c] + kt * AS_BK;
+            if constexpr (KM)
+                src = kt * AS_BK < a_kl[c] ? src : zero;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         } else {
             const unsigned dst = lds + A16_A_BYTES + (wave * CA + c - CA) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gb[c - CA] + kt * b_step),
-                         "{m0}"(dst)
-                         : "memory");
+            const unsigned short *src = gb[c - CA] + kt * b_step;
+            if constexpr (KM)
+                src = kt * AS_BK < b_kl[c - CA] ? src : zero;
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         }
     };
     auto issue = [&](int kt, unsigned char *st) {
@@ -824,7 +840,7 @@ __device__ __forceinline__ void a16_epilogue(const GemmArgs &p, unsigned short *
         restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows, cols);
 }
 
-template <int DT, int ACT, int WN, bool BT>
+template <int DT, int ACT, int WN, bool BT, bool KM>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
                                                                     int tiles_n, int group_m)
 {
@@ -840,7 +856,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
     f32x4 acc[8][16 / WN];
     a16_init_acc<DT, WN>(p, n0, wave, lane, true, acc);
-    a16_mainloop<DT, WN, BT>(p, m0, n0, Bm, 0, p.K / AS_BK, wave, lane, st0, st1, st2, st3, acc);
+    // KM (K off the 128 grid): the whole quads on the unmasked loop, then
+    // the last, partial quad on its own with the k past K masked (a second
+    // pipeline fill, but the masking's registers stay out of the main loop,
+    // where they made the compiler move the accumulators in and out of the
+    // register file)
+    const int KT = (p.K / (AS_STAGES * AS_BK)) * AS_STAGES;
+    if (!KM || KT > 0)
+        a16_mainloop<DT, WN, BT, false>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2, st3, acc);
+    if constexpr (KM)
+        a16_mainloop<DT, WN, BT, true>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1, st2,
+                                       st3, acc);
     a16_epilogue<DT, ACT, WN, BT>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
@@ -949,8 +975,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p
         int ln, wv;
         opaque(ln, wv);
         a16_init_acc<DT, WN>(p, n0, wv, ln, q0 == 0, acc);
-        a16_mainloop<DT, WN, BT>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv, ln, st0, st1, st2, st3,
-                                 acc);
+        a16_mainloop<DT, WN, BT, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv, ln, st0, st1,
+                                        st2, st3, acc);
         bool finish = q0 == 0 && q1 == Q;
         if (!finish) {
             // pieces of tile ts: workgroups w_first .. w_last, piece s stored
@@ -1079,6 +1105,15 @@ int async_tiles_n(const GemmArgs &a, int cfg)
     return (a.N + async_tile_n(cfg) - 1) / async_tile_n(cfg);
 }
 
+// K a multiple of the 128-deep loop; on the 16x16x32 configurations also a
+// multiple of 8 with at most as many padded k as real ones (the masked last
+// quad multiplies zeros for the rest)
+static bool async_k_ok(int K, bool masked_ok)
+{
+    constexpr int Q = AS_STAGES * AS_BK;
+    return K > 0 && (K % Q == 0 || (masked_ok && K % 8 == 0 && (K + Q - 1) / Q * Q - K <= K));
+}
+
 bool async_eligible(const GemmArgs &a, int cfg)
 {
     // An M (or an N that is a multiple of 8) that is not a multiple of the
@@ -1090,7 +1125,7 @@ bool async_eligible(const GemmArgs &a, int cfg)
     const bool n_ok = a.N % async_tile_n(cfg) == 0 ||
                       (a.N % 8 == 0 && a.N > async_tile_n(cfg) && 8 * padn <= a.N);
     return m_ok && n_ok &&
-           a.K % (AS_STAGES * AS_BK) == 0 && a.K > 0 && ((uintptr_t)a.bias & 7u) == 0 &&
+           async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0) && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
 
@@ -1126,6 +1161,8 @@ SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
         return pl;
     const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
     const int q = a.K / (AS_STAGES * AS_BK);
+    if (a.K % (AS_STAGES * AS_BK) != 0)
+        return pl;
     // whole waves need no split; below half a wave each tile would be cut
     // into more than two pieces (smaller tiles do better there)
     if (tiles % cus == 0 || 2 * tiles < cus || q < 2 || tiles >= (int64_t)1 << 24)
@@ -1202,25 +1239,35 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                                       ws == nullptr || counters == nullptr)))
         return hipErrorInvalidValue;
     dim3 grid(tiles_m * tiles_n * a.n_mat * splits), block(AS_NT);
+    const bool km = a.K % (AS_STAGES * AS_BK) != 0;
+    if (km && splits != 1)
+        return hipErrorInvalidValue;
     if (kAsyncConfigs[cfg].mfma16) {
         static_assert(A16Geom<4, false>::NT == 512 && A16Geom<2, false>::NT == 256 &&
                           A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
-#define TG_A16(DT_, ACT_)                                                                        \
+#define TG_A16K(DT_, ACT_, KM_)                                                                  \
     do {                                                                                         \
         if (wn == 4 && a.b_trans)                                                                \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, true>), grid, dim3(512), 0, s, \
-                               a, tiles_m, tiles_n, group_m);                                    \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, true, KM_>), grid, dim3(512), \
+                               0, s, a, tiles_m, tiles_n, group_m);                              \
         else if (wn == 4)                                                                        \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, false>), grid, dim3(512), 0,   \
-                               s, a, tiles_m, tiles_n, group_m);                                 \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, false, KM_>), grid, dim3(512), \
+                               0, s, a, tiles_m, tiles_n, group_m);                              \
         else if (a.b_trans)                                                                      \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true>), grid, dim3(256), 0, s, \
-                               a, tiles_m, tiles_n, group_m);                                    \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_>), grid, dim3(256), \
+                               0, s, a, tiles_m, tiles_n, group_m);                              \
         else                                                                                     \
-            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false>), grid, dim3(256), 0,   \
-                               s, a, tiles_m, tiles_n, group_m);                                 \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_>), grid, dim3(256), \
+                               0, s, a, tiles_m, tiles_n, group_m);                              \
+    } while (0)
+#define TG_A16(DT_, ACT_)                                                                        \
+    do {                                                                                         \
+        if (km)                                                                                  \
+            TG_A16K(DT_, ACT_, true);                                                            \
+        else                                                                                     \
+            TG_A16K(DT_, ACT_, false);                                                           \
     } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)
@@ -1234,6 +1281,7 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                 TG_A16(DT_BF16, ACT_NONE);
         }
 #undef TG_A16
+#undef TG_A16K
         return hipGetLastError();
     }
 #define TG_AS(DT_, ACT_, TI_, TJ_)                                                               \

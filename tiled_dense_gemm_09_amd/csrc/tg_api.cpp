@@ -263,6 +263,10 @@ int choose_async(const tg::GemmArgs &a, const char *force)
             return i;
         best = i;
     }
+    // K off the 128 grid (masked on the 256 x 256 tiles only): without a
+    // full wave of those tiles, K padding or the tiled kernel does better
+    if (a.K % 128 != 0)
+        return -1;
     return best;
 }
 
