@@ -28,6 +28,16 @@ def test_every_declared_symbol_is_exported():
     assert set(syms) == set(tg.SYMBOLS)
 
 
+def test_synchronising_build_loads_and_exports_the_same_symbols():
+    # libtg_debugsync.so: the same sources with every pipeline wait a full
+    # wait; a GPU test compares its outputs with libtg.so's bit for bit
+    dbg = tg.load_library(tg.DEBUG_SYNC_PATH)
+    for s in declared_symbols():
+        assert hasattr(dbg, s), s
+    assert dbg.tg_status_string(1) == b"TG_ERROR_INVALID_VALUE"
+    assert dbg.tg_workspace_bytes() == 0
+
+
 def test_status_strings():
     assert tg.lib.tg_status_string(0) == b"TG_SUCCESS"
     assert tg.lib.tg_status_string(1) == b"TG_ERROR_INVALID_VALUE"

@@ -342,22 +342,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int N>
-__device__ __forceinline__ void sa_wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-__device__ __forceinline__ void sa_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
-
 // Calls f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F &&f)
@@ -491,9 +475,9 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     // reads), compute.
     auto step = [&](int s, auto sidx) {
         constexpr int S = decltype(sidx)::value;
-        sa_wait_vmcnt<(STAGES - 2) * C::COPIES>();
+        wait_vmcnt<(STAGES - 2) * C::COPIES>();
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
-        sa_barrier();
+        stage_barrier();
         const int sc = min(s + STAGES - 1, slabs - 1);
 #pragma unroll
         for (int c = 0; c < C::COPIES; ++c)
@@ -509,7 +493,7 @@ __global__ __launch_bounds__(SA_NT, 1) void gemm_skinny_async_kernel(GemmArgs p,
     static_for<0, STAGES - 1>([&](auto i) { prologue(i); });
     for (int s = 0; s < slabs; s += STAGES)
         static_for<0, STAGES>([&](auto i) { step(s + decltype(i)::value, i); });
-    sa_wait_vmcnt<0>();
+    wait_vmcnt<0>();
 
     // Lane l holds Y[m = 16 mb + l % 16][n = WAVE_COLS w + 16 j + 4 (l / 16) + r]
     // in acc[mb][j][r].
@@ -762,8 +746,7 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
         issue(min(a, slabs - 1));
     for (int s = 0; s < slabs; ++s) {
         // the copies of slabs s+1 .. s+SC_AHEAD-1 may stay in flight
-        __builtin_amdgcn_s_waitcnt(((SC_AHEAD - 1) * SC_COPIES & 15) |
-                                   (((SC_AHEAD - 1) * SC_COPIES >> 4) << 14) | 0x0F70);
+        wait_vmcnt<(SC_AHEAD - 1) * SC_COPIES>();
         asm volatile("" ::: "memory");
         const unsigned char *st = my + (s % SC_SLOTS) * SC_SLOT_BYTES;
 #pragma unroll
@@ -785,7 +768,7 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
         asm volatile("" ::: "memory");
         issue(min(s + SC_AHEAD, slabs - 1));
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): no copy still writing LDS
+    wait_vmcnt<0>(); // no copy still writing LDS
     __syncthreads();
 
     // sum the four K-quarters in wave order; lane l holds

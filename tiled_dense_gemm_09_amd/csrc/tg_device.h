@@ -22,6 +22,50 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Number of XCDs on MI355X; the hardware hands workgroup b to XCD b % 8.
 constexpr int kNumXcd = 8;
 
+// Synchronising build (compiled with -DTG_DEBUG_SYNC into
+// libtg_debugsync.so beside the library): every partial wait of a copy
+// pipeline waits for all outstanding memory operations instead, and every
+// pipeline barrier is preceded by such a wait, so no LDS stage is read
+// before every copy into it has landed, nor refilled while a wave may still
+// read it.  The arithmetic and its order are unchanged, so the outputs must
+// equal the normal build's bit for bit; a difference exposes a wait or a
+// barrier that the normal build gets wrong.
+#ifdef TG_DEBUG_SYNC
+constexpr bool kDebugSync = true;
+#else
+constexpr bool kDebugSync = false;
+#endif
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum);
+// in the synchronising build, every counter at zero.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (kDebugSync)
+        __builtin_amdgcn_s_waitcnt(0);
+    else
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for the copy pipelines.  The usual __syncthreads() adds
+// a workgroup release fence, which waits for every outstanding direct-to-LDS
+// copy (they count as LDS writes) and would drain all stages each step.  Here
+// each wave waits for exactly the copies it needs with wait_vmcnt first; the
+// empty asm statements keep the compiler from moving LDS accesses across the
+// barrier.  The synchronising build waits for everything first.
+__device__ __forceinline__ void stage_barrier()
+{
+    if constexpr (kDebugSync)
+        __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
 struct TileCoord {
     int mat, tm, tn;
 };

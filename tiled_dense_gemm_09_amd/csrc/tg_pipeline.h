@@ -32,30 +32,6 @@ __host__ __device__ constexpr int swz_b(int r)
 // eight granule pairs, so the pass hits all 64 banks once.
 __host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * ((r >> 3) & 1)); }
 
-// Workgroup barrier for the copy pipeline.  The usual __syncthreads() adds a
-// workgroup release fence, which waits for every outstanding direct-to-LDS
-// copy (they count as LDS writes) and would drain all stages each step.  Here
-// each wave waits for exactly the copies it needs with wait_vmcnt first; the
-// empty asm statements keep the compiler from moving LDS accesses across the
-// barrier.
-__device__ __forceinline__ void stage_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // Epilogue of one wave holding TI x TJ 32x32 FP32 accumulator blocks (the
 // bias already inside).  Lane l of block (i, j) holds row 32 i + l % 32 and
 // columns 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The

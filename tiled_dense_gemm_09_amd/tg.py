@@ -15,6 +15,9 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtg.so")
+# the same sources built with TG_DEBUG_SYNC (every pipeline wait is a full
+# wait); loaded only by the test that compares its outputs with libtg.so's
+DEBUG_SYNC_PATH = os.path.join(HERE, "libtg_debugsync.so")
 
 F16 = 1
 BF16 = 2
@@ -34,7 +37,9 @@ class TgError(RuntimeError):
         self.status = status
 
 
-def _load():
+def load_library(path=LIB_PATH):
+    """ctypes handle of a build of the library with every entry point's
+    argument types declared."""
     # PyTorch ships its own HIP runtime.  Load it first so that libtg.so binds
     # to the same runtime instance (same soname) instead of a second copy
     # from /opt/rocm, which would not see the device torch has opened.
@@ -42,10 +47,9 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libtg.so is not built (%s); run `python -m tiled_dense_gemm_09_amd.build`"
-                          % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run `python -m tiled_dense_gemm_09_amd.build`" % path)
+    lib = ctypes.CDLL(path)
     P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.tg_gemm.argtypes = [I, L, L, L, P, L, P, L, P, L, P]
     lib.tg_gemm.restype = I
@@ -79,7 +83,7 @@ def _load():
     return lib
 
 
-lib = _load()
+lib = load_library()
 
 
 def _check(status):
