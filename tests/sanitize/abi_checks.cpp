@@ -71,6 +71,11 @@ hipError_t launch_pad_copy(const unsigned short *, int64_t, int, int, unsigned s
 {
     reached("launch_pad_copy");
 }
+hipError_t launch_unpad_copy(const unsigned short *, int, unsigned short *, int64_t, int, int,
+                             hipStream_t)
+{
+    reached("launch_unpad_copy");
+}
 SkinnyPlan plan_skinny(int, int, int) { reached("plan_skinny"); }
 size_t skinny_ws_floats(const SkinnyPlan &, int, int) { reached("skinny_ws_floats"); }
 hipError_t launch_skinny(int, int, const GemmArgs &, const SkinnyPlan &, float *, int *, hipStream_t)

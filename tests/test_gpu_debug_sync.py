@@ -123,6 +123,7 @@ CASES = [
     ("tiled_128_edges", {"TG_FORCE_CONFIG": "tiled_128x128x64_w2x2"},
      gemm_case(200, 136, 520, "bf16"), "tiled_128x128x64_w2x2"),
     ("tiled_unaligned", {}, gemm_case(300, 264, 264, a_pad=3, b_pad=3), "tiled_"),
+    ("staged", {}, gemm_case(1100, 1003, 1024, "bf16", b_pad=1), "async_"),
     ("generic_bt", {"TG_FORCE_CONFIG": "generic"}, gemm_case(64, 96, 80, bt=True),
      "generic_fma"),
     ("skinny_bn128", {}, gemm_case(16, 2048, 2048, "bf16", bias=False, act="none"),

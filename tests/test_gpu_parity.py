@@ -477,7 +477,6 @@ UNALIGNED_CASES = [
     (F16, 255, 257, 129, (1, 3, 5), 0),
     (BF16, 1000, 1000, 1000, (0, 0, 0), 1),
     (F16, 513, 1025, 777, (2, 6, 1), 0),
-    (BF16, 4095, 4095, 263, (0, 0, 0), 1),
 ]
 
 
@@ -511,6 +510,87 @@ def test_unaligned_pitches_integer_exact(tg, dt, M, N, K, pads, off):
     for i in range(M):
         inside[off + i * ldc: off + i * ldc + N] = True
     assert np.all(full[~inside] == NAN_BITS[dt]), "write outside the output"
+
+
+STAGED_CASES = [
+    # (dt, M, N, K, pitch pads of A, B, C, output offset in elements, B
+    # stored [N,K], bias offset in elements, residual read from the output):
+    # problems of at least 2^30 multiply-adds with operands off the 16-byte
+    # grid, staged through aligned, zero-padded copies.  N off the 8 grid and
+    # an output one element into its buffer (output staged and copied back;
+    # K padded to 264 for the masked 256 x 256 loop); only A off the grid
+    # (the kernel writes C itself; K padded to 1152 for 128 x 128 tiles);
+    # B stored [N,K] with an odd pitch; a bias 2 bytes past an 8-byte
+    # boundary with the residual read from the output itself
+    (BF16, 4095, 4095, 263, (0, 0, 0), 1, False, 0, False),
+    (F16, 2000, 2056, 1030, (1, 0, 0), 0, False, 0, False),
+    (F16, 1536, 1000, 2047, (0, 0, 0), 0, True, 0, False),
+    (BF16, 1100, 1003, 1024, (0, 0, 2), 0, False, 1, True),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,pads,off,trans_b,boff,inplace", STAGED_CASES)
+def test_off_grid_operands_staged_integer_exact(tg, dt, M, N, K, pads, off, trans_b, boff,
+                                                inplace):
+    # NaN in every pitch padding and around the output: the staged copies
+    # must read only the logical operands, the copy back write only the
+    # logical output.  Integer inputs, bias and residual: bit-exact.
+    import torch
+    p = inputs.problem(dt, M, N, K, seed=240 + M, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(241 + N), (M, N), "int", dt, 8.0)
+    lda, ldc = K + pads[0], N + pads[2]
+    A = util.to_dev(padded(p["A"], lda, dt), dt)[:, :K]
+    if trans_b:
+        ldb = K + pads[1]
+        B = util.to_dev(padded(np.ascontiguousarray(p["B"].T), ldb, dt), dt)[:, :K].t()
+    else:
+        ldb = N + pads[1]
+        B = util.to_dev(padded(p["B"], ldb, dt), dt)[:, :N]
+    bbuf = util.to_dev(np.concatenate([np.full(boff, NAN_BITS[dt], np.uint16), p["bias"]]), dt)
+    bias = bbuf[boff:]
+    Cbuf = util.to_dev(np.full(M * ldc + 1, NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[off:off + M * ldc].view(M, ldc)[:, :N]
+    if inplace:
+        C.copy_(util.to_dev(R, dt))
+        Rd = C
+    else:
+        Rd = util.to_dev(R, dt)
+    say("case staged", dt, M, N, K, "pitches", lda, ldb, ldc, "C offset", off,
+        "B[N,K]" if trans_b else "", "bias offset", boff, "in place" if inplace else "")
+    tg.gemm(A, B, out=C, bias=bias, residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.endswith("_staged"), kern
+    _, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], R=R)
+    util.check_exact(util.to_bits(C), ref, "staged " + kern)
+    full = util.to_bits(Cbuf)
+    inside = np.zeros(full.shape, bool)
+    for i in range(M):
+        inside[off + i * ldc: off + i * ldc + N] = True
+    assert np.all(full[~inside] == NAN_BITS[dt]), "write outside the output"
+
+
+def test_off_grid_operands_staged_on_stream_k_integer_exact(tg, monkeypatch):
+    # A with an odd pitch on a problem whose 256 x 256 tiles leave a partial
+    # wave (9 x 16 tiles; TG_STREAMK=2 takes it although each workgroup gets
+    # fewer than 16 K quads): the staged copies feed the stream-K kernel.
+    import torch
+    monkeypatch.setenv("TG_STREAMK", "2")
+    dt, M, N, K = F16, 2049, 4096, 1023
+    p = inputs.problem(dt, M, N, K, seed=250, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(251), (M, N), "int", dt, 8.0)
+    A = util.to_dev(padded(p["A"], K, dt), dt)
+    B = util.to_dev(p["B"], dt)
+    bias, Rd = util.to_dev(p["bias"], dt), util.to_dev(R, dt)
+    say("case staged stream-K", dt, M, N, K)
+    C = tg.gemm(A, B, bias=bias, residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern == "async_256x256x32_s4_mfma16_streamk_staged", kern
+    _, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], R=R)
+    util.check_exact(util.to_bits(C), ref, "staged stream-K")
 
 
 def test_k_zero_gives_activated_bias(tg):

@@ -292,8 +292,90 @@ bool kpad_eligible(const tg::GemmArgs &a, const char *force)
     return tiles >= 240;
 }
 
+// Operands off the 16-byte grid (a pitch that is not a multiple of 8
+// elements, or a pointer that is only 2-byte aligned) on a problem of at
+// least 2^30 multiply-adds: A and B are copied into aligned, zero-padded
+// buffers (K rounded up to 8, or to 128 when no asynchronous configuration
+// takes the former), the residual and the bias too when they are off the
+// grid or N is not a multiple of 8, and the asynchronous kernel writes C
+// itself when C is on the grid with N a multiple of 8, otherwise an aligned
+// copy that is then moved into place.  The element counts are rounded up to
+// 128 (256-byte aligned pieces); the staged output has 8 spare elements for
+// the copy back, which reads whole 16-byte pieces.
+struct StagePlan {
+    int cfg = -1;                  // configuration on the staged problem; -1: not staged
+    int K2 = 0, N8 = 0;            // staged K and N
+    tg::SkPlan sk{0, 0, 0, 0, 0};  // stream-K plan on the staged problem (sk_tiles 0: none)
+    bool c = false, r = false, bias = false; // output, residual, bias staged
+    int64_t a_elems = 0, b_elems = 0, c_elems = 0, r_elems = 0, bias_elems = 0;
+    int64_t total() const { return a_elems + b_elems + c_elems + r_elems + bias_elems; }
+};
+
+// cus > 0 and sk_mode != 0: stream-K is planned on the staged problem as on
+// an aligned one (K then rounded up to 128, at most K / 8 added).
+StagePlan plan_staging(const tg::GemmArgs &a, const char *force, int cus, int sk_mode)
+{
+    StagePlan sp;
+    if ((force && *force) || a.n_mat != 1 || a.M <= 32 || a.K < 8 ||
+        (double)a.M * a.N * a.K < (double)(1 << 30))
+        return sp;
+    const int N8 = (a.N + 7) / 8 * 8;
+    const bool c_ok = aligned16(a.C[0]) && a.ldc % 8 == 0 && N8 == a.N;
+    const bool r_ok = a.R == nullptr || (aligned16(a.R) && a.ldr % 8 == 0 && c_ok);
+    const bool bias_ok = a.bias == nullptr || (((uintptr_t)a.bias & 7u) == 0 && N8 == a.N);
+    auto staged = [&](int K2) {
+        tg::GemmArgs a2 = a;
+        a2.K = K2;
+        a2.lda = K2;
+        a2.ldb = a.b_trans ? K2 : N8;
+        a2.N = N8;
+        // the staged residual and bias are aligned, the others passed the
+        // checks above
+        a2.bias = nullptr;
+        a2.R = nullptr;
+        a2.ldr = 0;
+        return a2;
+    };
+    auto take = [&](int cfg, int K2) {
+        auto round = [](int64_t e) { return (e + 127) / 128 * 128; };
+        sp.cfg = cfg;
+        sp.K2 = K2;
+        sp.N8 = N8;
+        sp.c = !c_ok;
+        sp.r = !r_ok;
+        sp.bias = !bias_ok;
+        sp.a_elems = round((int64_t)a.M * K2);
+        sp.b_elems = round((int64_t)N8 * K2);
+        sp.c_elems = sp.c ? round((int64_t)a.M * N8 + 8) : 0;
+        sp.r_elems = sp.r ? round((int64_t)a.M * N8) : 0;
+        sp.bias_elems = sp.bias ? round(N8) : 0;
+    };
+    const int K128 = (a.K + 127) / 128 * 128;
+    if (sk_mode != 0 && cus > 0 && 8 * (K128 - a.K) <= a.K) {
+        const tg::GemmArgs a2 = staged(K128);
+        for (int i = 0; i < tg::num_async_configs(); ++i) {
+            if (tg::async_forced_only(i))
+                continue;
+            const tg::SkPlan sk = tg::plan_stream_k(a2, i, cus, sk_mode == 2);
+            if (sk.sk_tiles > 0 && sk.sk_tiles <= tg::kMaxSplitTiles) {
+                take(i, K128);
+                sp.sk = sk;
+                return sp;
+            }
+        }
+    }
+    for (const int K2 : {(a.K + 7) / 8 * 8, K128}) {
+        const int cfg = choose_async(staged(K2), nullptr);
+        if (cfg >= 0) {
+            take(cfg, K2);
+            return sp;
+        }
+    }
+    return sp;
+}
+
 // noalloc: the split paths take the fixed scratch (never the growable
-// workspace) and K is never padded, so the call allocates nothing.
+// workspace) and nothing is padded or staged, so the call allocates nothing.
 tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *const B[3], int64_t ldb, const void *bias, tg_act act, void *const C[3],
               int64_t ldc, int n_mat, void *stream, int b_trans = 0, const void *R = nullptr,
@@ -433,6 +515,28 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                                                      : " (no K padding: no workspace)";
         }
     }
+    // Operands off the 16-byte grid: staged through aligned copies (above)
+    // when the problem pays for the copies and the workspace can be had,
+    // else the element-wise kernels below.
+    StagePlan stg;
+    void *stg_base = nullptr;
+    const char *stg_note = nullptr;
+    const int sk_mode = env_int("TG_STREAMK", 1);
+    size_t stg_sk_floats = 0;
+    if (!fast && even && !force_generic && !noalloc) {
+        stg = plan_staging(a, force, device_cus(), sk_mode);
+        if (stg.cfg >= 0) {
+            // stream-K partial slots (after the counters), then the staged copies
+            stg_sk_floats = stg.sk.sk_tiles > 0 ? tg::stream_k_ws_floats(stg.sk) : 0;
+            tg_status st = TG_SUCCESS;
+            stg_base = get_workspace(stg_sk_floats + (size_t)(stg.total() / 2 + 64), s, &st);
+            if (!stg_base) {
+                stg.cfg = -1;
+                stg_note = st == TG_ERROR_NOT_SUPPORTED ? " (not staged: stream capture)"
+                                                        : " (not staged: no workspace)";
+            }
+        }
+    }
     // Stream-K: the 4-wave 256 x 256 configuration when its tiles leave a
     // partial last wave (unforced, or forced by name); TG_STREAMK=0 turns it
     // off, TG_STREAMK=2 also takes shapes whose K share per workgroup is
@@ -442,7 +546,6 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     int sk_cfg = -1;
     void *sk_base = nullptr;
     const char *sk_note = nullptr;
-    const int sk_mode = env_int("TG_STREAMK", 1);
     if (fast && !noalloc && !force_generic && !force_tiled && sk_mode != 0 &&
         !(n_mat == 1 && M <= 32)) {
         for (int i = 0; i < tg::num_async_configs() && sk_cfg < 0; ++i) {
@@ -473,6 +576,54 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                                                             kCounterBytes),
                                   static_cast<int *>(sk_base), s);
         set_last(tg::async_config_name(sk_cfg), "_streamk");
+    } else if (stg.cfg >= 0) {
+        // staged copies in, the asynchronous kernel, the output copied out
+        float *sk_slots = reinterpret_cast<float *>(static_cast<char *>(stg_base) + kCounterBytes);
+        unsigned short *p = reinterpret_cast<unsigned short *>(sk_slots + stg_sk_floats);
+        unsigned short *Ap = p, *Bp = p + stg.a_elems;
+        p = Bp + stg.b_elems;
+        unsigned short *Cp = stg.c ? p : nullptr;
+        p += stg.c_elems;
+        unsigned short *Rp = stg.r ? p : nullptr;
+        p += stg.r_elems;
+        unsigned short *biasp = stg.bias ? p : nullptr;
+        const int K2 = stg.K2, N8 = stg.N8;
+        err = tg::launch_pad_copy(a.A, a.lda, a.M, a.K, Ap, a.M, K2, s);
+        if (err == hipSuccess)
+            err = b_trans ? tg::launch_pad_copy(a.B[0], a.ldb, a.N, a.K, Bp, N8, K2, s)
+                          : tg::launch_pad_copy(a.B[0], a.ldb, a.K, a.N, Bp, K2, N8, s);
+        if (err == hipSuccess && Rp)
+            err = tg::launch_pad_copy(a.R, a.ldr, a.M, a.N, Rp, a.M, N8, s);
+        if (err == hipSuccess && biasp)
+            err = tg::launch_pad_copy(a.bias, a.N, 1, a.N, biasp, 1, N8, s);
+        tg::GemmArgs a2 = a;
+        a2.A = Ap;
+        a2.lda = K2;
+        a2.B[0] = a2.B[1] = a2.B[2] = Bp;
+        a2.ldb = b_trans ? K2 : N8;
+        a2.K = K2;
+        a2.N = N8;
+        if (Cp) {
+            a2.C[0] = a2.C[1] = a2.C[2] = Cp;
+            a2.ldc = N8;
+        }
+        if (Rp) {
+            a2.R = Rp;
+            a2.ldr = N8;
+        }
+        if (biasp)
+            a2.bias = biasp;
+        if (err == hipSuccess) {
+            const int group_m = env_int("TG_GROUP_M", 4);
+            err = stg.sk.sk_tiles > 0
+                      ? tg::launch_async_sk(stg.cfg, kdt, kact, a2, group_m > 0 ? group_m : 4,
+                                            stg.sk, sk_slots, static_cast<int *>(stg_base), s)
+                      : tg::launch_async(stg.cfg, kdt, kact, a2, group_m > 0 ? group_m : 4, 1,
+                                         nullptr, nullptr, s);
+        }
+        if (err == hipSuccess && Cp)
+            err = tg::launch_unpad_copy(Cp, N8, a.C[0], a.ldc, a.M, a.N, s);
+        set_last(tg::async_config_name(stg.cfg), stg.sk.sk_tiles > 0 ? "_streamk_staged" : "_staged");
     } else if (unal_tiled) {
         const int cfg = choose_config(M, N, n_mat);
         const tg::TileConfig &c = tg::tile_config(cfg);
@@ -481,13 +632,15 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             return TG_ERROR_NOT_SUPPORTED;
         const int group_m = env_int("TG_GROUP_M", 4);
         err = tg::launch_tiled(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, s);
-        set_last(c.name, "_unaligned");
+        char detail[64];
+        snprintf(detail, sizeof detail, "_unaligned%s", stg_note ? stg_note : "");
+        set_last(c.name, detail);
     } else if (!fast || force_generic || (b_trans && !trans_async && !kpad)) {
         err = tg::launch_generic(kdt, kact, a, s);
         set_last(!fast            ? "generic_fma (unaligned operands)"
                  : force_generic ? "generic_fma (forced)"
                                  : "generic_fma (B stored [N,K] outside the async tile shapes)",
-                 kpad_note);
+                 !fast ? stg_note : kpad_note);
     } else if (n_mat == 1 && M <= 32 && K >= 256 && N >= 256 && !force_tiled && !b_trans &&
                tg::plan_skinny(a.M, a.N, a.K).streaming >= 0) {
         // M <= 16 always; 16 < M <= 32 when the streaming kernel fits the shape

@@ -146,6 +146,11 @@ hipError_t launch_attn_generic(int dt, bool causal, const AttnArgs &a, int D, hi
 // 8, 16-byte aligned).  Used to round K up to the asynchronous kernels' loop.
 hipError_t launch_pad_copy(const unsigned short *src, int64_t lds, int src_rows, int src_cols,
                            unsigned short *dst, int dst_rows, int dst_cols, hipStream_t stream);
+// The way back: dst[r][c] = src[r][c] for r < rows, c < cols, from rows of
+// src_pitch elements (a multiple of 8, 16-byte aligned, with 8 readable
+// elements past the last row) into any 2-byte aligned dst of pitch ldd.
+hipError_t launch_unpad_copy(const unsigned short *src, int src_pitch, unsigned short *dst,
+                             int64_t ldd, int rows, int cols, hipStream_t stream);
 
 // Small-M path (M <= 32): W streamed once, split over K.  `ws` is an FP32
 // workspace of ws_floats floats and `counters` an int array of n_tiles
