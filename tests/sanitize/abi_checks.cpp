@@ -38,6 +38,7 @@ hipError_t launch_generic(int, int, const GemmArgs &, hipStream_t) { reached("la
 int num_async_configs() { reached("num_async_configs"); }
 const char *async_config_name(int) { reached("async_config_name"); }
 bool async_forced_only(int) { reached("async_forced_only"); }
+bool async_mfma16(int) { reached("async_mfma16"); }
 int async_tile_m(int) { reached("async_tile_m"); }
 int async_tile_n(int) { reached("async_tile_n"); }
 bool async_eligible(const GemmArgs &, int) { reached("async_eligible"); }

@@ -641,6 +641,45 @@ def test_async_config_bias_gelu_random(tg, monkeypatch, cfg):
     util.check_tol(F16, bits, f64, cfg, ref_bits=rbits)
 
 
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_192_tiles_integer_bias_exact(tg, monkeypatch, dt):
+    # 576 x 768 x 384: 3 x 4 tiles of 192 x 192 (384-byte B rows with their
+    # own swizzle, 96 x 96 wave tiles, 192-byte epilogue rows), 12 K steps
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_192x192x32_s4_mfma16")
+    p = inputs.problem(dt, 576, 768, 384, seed=63 + dt, kind="int", bias=True,
+                       bias_kind="int")
+    say("case 192 x 192 tiles dt", dt, "integer + bias 576x768x384")
+    bits, kern = run(tg, p)
+    assert kern == "async_192x192x32_s4_mfma16", kern
+    _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
+    util.check_exact(bits, ref, kern)
+
+
+def test_192_tiles_bias_gelu_random(tg, monkeypatch):
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_192x192x32_s4_mfma16")
+    p = inputs.problem(F16, 384, 576, 640, seed=73, bias=True, act=inputs.ACT_GELU_TANH,
+                       a_scale=0.2, b_scale=0.2)
+    say("case 192 x 192 tiles bias+gelu 384x576x640")
+    bits, kern = run(tg, p)
+    assert kern == "async_192x192x32_s4_mfma16", kern
+    f64, rbits = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
+    util.check_tol(F16, bits, f64, kern, ref_bits=rbits)
+
+
+def test_192_tiles_chosen_for_3072_outputs(tg):
+    # 3072 x 3072 outputs: 144 tiles of 256 x 256 (a partial wave, too short
+    # a K share per workgroup for stream-K) but 256 of 192 x 192; every output
+    # compared with the oracle
+    import torch
+    dt = BF16
+    p = inputs.problem(dt, 3072, 3072, 512, seed=74, kind="int", bias=True, bias_kind="int")
+    say("case 192 x 192 tiles chosen, 3072x3072x512")
+    bits, kern = run(tg, p)
+    assert kern == "async_192x192x32_s4_mfma16", kern
+    _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
+    util.check_exact(bits, ref, kern)
+
+
 def test_async_small_tile_qkv(tg, monkeypatch):
     # N = 384 is a multiple of 128 but not of 256: the 128 x 128 tiles serve it
     q = inputs.qkv_problem(BF16, 256, 384, 256, seed=81, kind="int")
@@ -803,6 +842,9 @@ RAGGED_M_CASES = [
     (BF16, 1923, 768, 384, "async_256x256x32_s4_mfma16"),
     (F16, 3000, 512, 512, "async_256x256x32_s4_mfma16"),
     (BF16, 2303, 256, 256, "async_256x256x32_s4_mfma16_w8"),
+    # 192 x 192 tiles: a last row tile of 140 rows (the second wave row
+    # holds 44)
+    (F16, 1100, 384, 256, "async_192x192x32_s4_mfma16"),
     # the 32x32x16 kernel: last row tiles of 152, 104, 24 and 30 rows
     (BF16, 2200, 256, 256, "async_256x256x32_s4"),
     (F16, 1000, 384, 256, "async_128x128x32_s4"),
@@ -841,6 +883,7 @@ RAGGED_N_CASES = [
     # (dt, M, N, K, config): N a multiple of 8 leaving a partial last column
     # tile of at most N/8 padding columns; the last case is ragged in M too
     (F16, 512, 2000, 256, "async_256x256x32_s4_mfma16"),
+    (BF16, 384, 1096, 256, "async_192x192x32_s4_mfma16"),
     (BF16, 256, 2200, 384, "async_256x256x32_s4"),
     (F16, 256, 1000, 256, "async_128x128x32_s4"),
     (BF16, 192, 600, 512, "async_64x128x32_s4"),
@@ -906,6 +949,7 @@ KMASK_CASES = [
     (BF16, 512, 512, 200, "async_256x256x32_s4_mfma16"),
     (F16, 512, 512, 72, "async_256x256x32_s4_mfma16"),
     (BF16, 768, 512, 4040, "async_256x256x32_s4_mfma16"),
+    (F16, 576, 576, 200, "async_192x192x32_s4_mfma16"),
 ]
 
 
@@ -1063,6 +1107,7 @@ EX_SHAPES = [
     (F16, 512, 768, 384, "async_256x256x32_s4"),
     (BF16, 768, 512, 256, "async_256x256x32_s4_mfma16"),
     (F16, 512, 512, 512, "async_256x256x32_s4_mfma16_w8"),
+    (F16, 384, 576, 256, "async_192x192x32_s4_mfma16"),
     (BF16, 256, 384, 256, "async_128x128x32_s4"),
     (F16, 192, 256, 512, "async_64x128x32_s4"),
     (BF16, 192, 320, 384, "async_64x64x32_s4"),   # N a multiple of 64, not of 128
@@ -1379,15 +1424,16 @@ def test_dispatch_choices(tg, monkeypatch):
     tg.gemm(e, c)
     assert tg.last_kernel() == "async_64x128x32_s4"
     # partial last row tiles: 144 tiles of 256 x 256 (more than half a wave,
-    # not a whole one) run stream-K; with stream-K off, the 128 x 128 tiles
-    # that fill a wave; never the forced-only 8-wave variant
+    # not a whole one) against 242 of 192 x 192, which fill their wave
+    # better: the 192 x 192 tiles; stream-K with TG_STREAMK=2; never the
+    # forced-only 8-wave variant
     f = torch.zeros((2049, 4096), dtype=torch.float16, device="cuda")
     g = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
     tg.gemm(f, g)
-    assert tg.last_kernel() == "async_256x256x32_s4_mfma16_streamk", tg.last_kernel()
-    monkeypatch.setenv("TG_STREAMK", "0")
+    assert tg.last_kernel() == "async_192x192x32_s4_mfma16", tg.last_kernel()
+    monkeypatch.setenv("TG_STREAMK", "2")
     tg.gemm(f, g)
-    assert tg.last_kernel() == "async_128x128x32_s4", tg.last_kernel()
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16_streamk", tg.last_kernel()
     monkeypatch.delenv("TG_STREAMK")
     # whole waves (4096^3: 256 tiles) stay data-parallel
     tg.gemm(g, g)

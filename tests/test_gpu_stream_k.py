@@ -143,11 +143,12 @@ def test_stream_k_replays_from_a_graph_with_eager_calls_between(tg, monkeypatch)
         util.check_exact(util.to_bits(C), ref, "eager after replay %d" % i)
 
 
-def test_stream_k_full_size_shapes_off_the_wave(tg):
-    # by default: bf16 3584^3 (196 tiles, fewer than a wave, 22 quads per
-    # workgroup) and 6144^3 (576 tiles: two waves whole, 64 + 256 split),
-    # every output against the oracle
+def test_stream_k_full_size_shapes_off_the_wave(tg, monkeypatch):
+    # bf16 3584^3 (196 tiles, fewer than a wave, 22 quads per workgroup;
+    # split only with TG_STREAMK=2) and 6144^3 (576 tiles: two waves whole,
+    # 64 + 256 split, by default), every output against the oracle
     for n in (3584, 6144):
+        monkeypatch.setenv("TG_STREAMK", "2" if n == 3584 else "1")
         p = inputs.problem(BF16, n, n, n, seed=1400 + n, kind="normal", b_scale=n ** -0.5)
         say("case stream-K %d^3" % n)
         bits, kern = run(tg, BF16, p["A"], p["B"], False)
@@ -157,12 +158,16 @@ def test_stream_k_full_size_shapes_off_the_wave(tg):
 
 
 def test_stream_k_default_threshold(tg):
-    # 144 tiles with 14 quads per workgroup (3072^3) stay on the 128 x 128
-    # tiles; 3000 x 11008 x 4096 (two waves + 4 tiles) and 2049 x 4096 x
-    # 4096 (144 tiles, 18 quads each) take stream-K
+    # by default only grids of a whole wave or more split their short last
+    # wave: 3000 x 11008 x 4096 (two waves + 4 tiles) takes stream-K; short
+    # of a wave the grid stays whole: 3072^3 and 2049 x 4096 x 4096 (144
+    # tiles of 256, 256 and 242 of 192) on 192 x 192 tiles, 3584^3 (196 of
+    # 256, 361 of 192) on a partly filled wave of 256 x 256 tiles
     import torch
-    for (M, N, K), expect in (((3072, 3072, 3072), "async_128x128x32_s4"),
-                              ((3000, 11008, 4096), SK), ((2049, 4096, 4096), SK)):
+    for (M, N, K), expect in (((3072, 3072, 3072), "async_192x192x32_s4_mfma16"),
+                              ((3000, 11008, 4096), SK),
+                              ((2049, 4096, 4096), "async_192x192x32_s4_mfma16"),
+                              ((3584, 3584, 3584), "async_256x256x32_s4_mfma16")):
         a = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
         b = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
         tg.gemm(a, b)

@@ -522,36 +522,52 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 //    (about 500 register moves per four steps at WN = 2).
 namespace {
 
-constexpr int A16_BM = 256, A16_BN = 256;
-constexpr int A16_A_BYTES = A16_BM * AS_BK * 2;             // [256][32] K-contiguous
-constexpr int A16_STAGE = A16_A_BYTES + AS_BK * A16_BN * 2; // + [32][256] N-contiguous
+// Tiles of the 16x16x32 kernels: TM x TM outputs (256, or 192 for sizes
+// whose 256 x 256 tiles would leave most of a wave idle), K steps of 32.
+// A stage holds A [TM][32] K-contiguous, then B [32][TM] N-contiguous (or,
+// stored [N,K], [TM][32] like A).
+template <int TM>
+struct A16Tile {
+    static_assert(TM == 256 || TM == 192, "16x16x32 tile sizes");
+    static constexpr int A_BYTES = TM * AS_BK * 2;
+    static constexpr int STAGE = 2 * A_BYTES;
+};
+constexpr int A16_BM = 256, A16_BN = 256; // the stream-K kernel's tiles
+constexpr int A16_STAGE = A16Tile<256>::STAGE;
 
-template <int WN, bool BT>
+// WN x 2 waves; each wave owns (TM / 2) x (TM / WN) outputs: MI x NJ blocks
+// of 16 x 16.
+template <int WN, bool BT, int TM = 256>
 struct A16Geom {
-    static_assert(WN == 2 || WN == 4, "waves along N");
+    static_assert(WN == 2 || (WN == 4 && TM == 256), "waves along N");
     static constexpr int NW = 2 * WN;               // waves
     static constexpr int NT = 64 * NW;              // lanes
-    static constexpr int NJ = 16 / WN;              // 16-column blocks per wave
+    static constexpr int MI = TM / 32;              // 16-row blocks per wave
+    static constexpr int NJ = TM / 16 / WN;         // 16-column blocks per wave
+    static constexpr int WROWS = 16 * MI;           // rows per wave
     static constexpr int WCOLS = 16 * NJ;           // columns per wave
-    static constexpr int CA = 16 / NW;              // A copies per wave per step (16 in all)
+    static constexpr int CA = TM / 16 / NW;         // A copies of 1 KiB per wave per step
     static constexpr int COPIES = 2 * CA;           // + as many B copies
-    static constexpr int READS = 8 + (BT ? NJ : 2 * NJ); // A reads + B reads (2 transposing each)
+    static constexpr int READS = MI + (BT ? NJ : 2 * NJ); // A reads + B reads (2 transposing each)
     static constexpr int G = 2 * NJ;                // epilogue granules per wave-tile row
-    static constexpr int EP_BYTES = 128 * 16 * G;   // wave tile restaged in LDS
+    static constexpr int EP_BYTES = WROWS * 16 * G; // wave tile restaged in LDS
 };
 
 // epilogue row swizzle: 16 rows of a read pass on 16 distinct bank groups
-// (256-byte rows: r % 16; 128-byte rows: rows r, r + 1 share a bank sweep)
+// (256-byte rows: r % 16; 128-byte rows: rows r, r + 1 share a bank sweep;
+// 192-byte rows: rows r and r + 4 start on the same bank, so (r / 4) % 4
+// moves the granule inside its aligned group of four)
 template <int G>
 __device__ __forceinline__ int ep_swz(int r)
 {
-    return G == 16 ? (r & 15) : ((r >> 1) & 7);
+    static_assert(G == 16 || G == 8 || G == 12, "epilogue row widths");
+    return G == 16 ? (r & 15) : G == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 } // namespace
 
-template <int DT, int ACT, bool HR, int NJ>
-__device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], unsigned char *ep,
+template <int DT, int ACT, bool HR, int MI, int NJ>
+__device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[MI][NJ], unsigned char *ep,
                                                     int lane, unsigned short *C, int64_t ldc,
                                                     const unsigned short *R, int64_t ldr,
                                                     int rows, int cols)
@@ -559,13 +575,14 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
     // rows, cols: output rows and columns of this wave tile inside the
     // matrix (a multiple of 8 columns); the rest are neither read from R nor
     // stored
-    // the rounded 128 x (16 NJ) wave tile goes to the wave's own LDS region
-    // (rows of G = 2 NJ granules, granule c of row r at c ^ ep_swz(r)), then
-    // each store writes 16 bytes per lane, whole row segments
+    // the rounded (16 MI) x (16 NJ) wave tile goes to the wave's own LDS
+    // region (rows of G = 2 NJ granules, granule c of row r at c ^
+    // ep_swz(r)), then each store writes 16 bytes per lane, whole row
+    // segments
     constexpr int G = 2 * NJ;
     const int q = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MI; ++i) {
         const int r = 16 * i + (lane & 15);
         u32x2 rr[NJ];
         if constexpr (HR) {
@@ -589,32 +606,44 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[8][NJ], u
             *reinterpret_cast<u32x2 *>(ep + r * (16 * G) + c * 16 + (q & 1) * 8) = o;
         }
     }
-    // lane -> granule lane % G of rows (64 / G) t + lane / G
-    unsigned short *crow = C + (lane % G) * 8;
+    if constexpr (64 % G == 0) {
+        // lane -> granule lane % G of rows (64 / G) t + lane / G
+        unsigned short *crow = C + (lane % G) * 8;
 #pragma unroll
-    for (int t = 0; t < 2 * G; ++t) {
-        const int r = (64 / G) * t + lane / G;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) +
-                                                         (((lane % G) ^ ep_swz<G>(r)) * 16));
-        if (r < rows && (lane % G) * 8 < cols)
-            *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
+        for (int t = 0; t < MI * G / 4; ++t) {
+            const int r = (64 / G) * t + lane / G;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) +
+                                                             (((lane % G) ^ ep_swz<G>(r)) * 16));
+            if (r < rows && (lane % G) * 8 < cols)
+                *reinterpret_cast<u32x4 *>(crow + (int64_t)r * ldc) = v;
+        }
+    } else {
+        // lane -> granule (64 t + lane) % G of row (64 t + lane) / G
+#pragma unroll
+        for (int t = 0; t < MI * G / 4; ++t) {
+            const int r = (64 * t + lane) / G, g = (64 * t + lane) % G;
+            const u32x4 v =
+                *reinterpret_cast<const u32x4 *>(ep + r * (16 * G) + ((g ^ ep_swz<G>(r)) * 16));
+            if (r < rows && g * 8 < cols)
+                *reinterpret_cast<u32x4 *>(C + (int64_t)r * ldc + g * 8) = v;
+        }
     }
 }
 
-// The K loop of one 256 x 256 tile on the 16x16x32 MFMA: K-steps kt0 ..
+// The K loop of one TM x TM tile on the 16x16x32 MFMA: K-steps kt0 ..
 // kt0 + KT - 1 (KT a multiple of the four stages) of the tile at (m0, n0)
 // of the product with the weight Bm, accumulated into acc (which the caller
 // has initialised).  On return every copy has landed and every wave has
 // finished reading the stages, so the LDS is free.
-template <int DT, int WN, bool BT, bool KM>
-__device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
-                                             const unsigned short *Bm, int kt0, int KT, int wave,
-                                             int lane, unsigned char *st0, unsigned char *st1,
-                                             unsigned char *st2, unsigned char *st3,
-                                             f32x4 (&acc)[8][16 / WN])
+template <int DT, int WN, bool BT, bool KM, int TM = 256>
+__device__ __forceinline__ void a16_mainloop(
+    const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int kt0, int KT, int wave,
+    int lane, unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
+    f32x4 (&acc)[A16Geom<WN, BT, TM>::MI][A16Geom<WN, BT, TM>::NJ])
 {
-    using Gm = A16Geom<WN, BT>;
-    constexpr int NJ = Gm::NJ, CA = Gm::CA;
+    using Gm = A16Geom<WN, BT, TM>;
+    constexpr int MI = Gm::MI, NJ = Gm::NJ, CA = Gm::CA;
+    constexpr int A_BYTES = A16Tile<TM>::A_BYTES;
     auto stage = [&](auto sidx) -> unsigned char * {
         constexpr int S = decltype(sidx)::value;
         if constexpr (S == 0)
@@ -631,9 +660,11 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
 
     // copy c < CA: A copy q = CA w + c, rows 16 q .. 16 q + 15 (lane -> row
     // 16 q + lane / 4, granule lane % 4); c >= CA: B copy q = CA w + c - CA,
-    // rows 2 q, 2 q + 1 (lane -> row 2 q + lane / 32, granule lane % 32).
-    // B stored [N,K] (BT) is staged like A: [256 n][32 k] K-contiguous, B
-    // copy q filling n-rows 16 q .. 16 q + 15 with the A swizzle.
+    // bytes 1024 q .. 1024 q + 1023 of [32][TM] (lane -> byte 1024 q + 16
+    // lane: row rb of 2 TM bytes, granule gb; at TM = 256 rows 2 q + lane /
+    // 32, granule lane % 32).  B stored [N,K] (BT) is staged like A:
+    // [TM n][32 k] K-contiguous, B copy q filling n-rows 16 q .. 16 q + 15
+    // with the A swizzle.
     const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
     // KM: copy c of step kt is inside K iff kt * 32 < a_kl[c] (b_kl[c])
     const unsigned short *ga[CA], *gb[CA];
@@ -653,10 +684,19 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
             gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ka + (int64_t)kt0 * AS_BK;
             b_kl[c] = a_kl[c];
         } else {
-            const int rb = 2 * q + (lane >> 5);
-            gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) +
-                    (int64_t)kt0 * b_step;
-            b_kl[c] = p.K - kt0 * AS_BK - rb;
+            if constexpr (TM == 256) {
+                const int rb = 2 * q + (lane >> 5);
+                gb[c] = Bm + (int64_t)rb * p.ldb +
+                        min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) + (int64_t)kt0 * b_step;
+                b_kl[c] = p.K - kt0 * AS_BK - rb;
+            } else {
+                const unsigned byte = 1024u * q + 16u * lane;
+                const int rb = (int)(byte / (2 * TM));
+                const int gb0 = (int)(byte % (2 * TM) / 16) ^ swz_b192(rb);
+                gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + gb0 * 8, p.N - 8) +
+                        (int64_t)kt0 * b_step;
+                b_kl[c] = p.K - kt0 * AS_BK - rb;
+            }
         }
     }
     auto copy = [&](int kt, unsigned char *st, int c) {
@@ -668,7 +708,7 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
                 src = kt * AS_BK < a_kl[c] ? src : zero;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         } else {
-            const unsigned dst = lds + A16_A_BYTES + (wave * CA + c - CA) * 1024;
+            const unsigned dst = lds + A_BYTES + (wave * CA + c - CA) * 1024;
             const unsigned short *src = gb[c - CA] + kt * b_step;
             if constexpr (KM)
                 src = kt * AS_BK < b_kl[c - CA] ? src : zero;
@@ -683,15 +723,15 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
 
     // fragment offsets within a stage
     const int q16 = lane >> 4;
-    int a_off[8];
+    int a_off[MI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wave_m * 128 + 16 * i + (lane & 15);
+    for (int i = 0; i < MI; ++i) {
+        const int r = wave_m * Gm::WROWS + 16 * i + (lane & 15);
         a_off[i] = r * 64 + ((q16 ^ swz_a(r)) * 16);
     }
-    // B fragment j: transposing reads of [32 k][256 n] (two per fragment), or
+    // B fragment j: transposing reads of [32 k][TM n] (two per fragment), or
     // for BT one 128-bit read of n-row wave_n WCOLS + 16 j + l % 16, k
-    // granule l / 16 of [256 n][32 k] (b_off[j][0])
+    // granule l / 16 of [TM n][32 k] (b_off[j][0])
     int b_off[NJ][2];
     {
         const int jj = lane & 15;
@@ -701,28 +741,28 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
             for (int h = 0; h < 2; ++h) {
                 if constexpr (BT) {
                     const int r = wave_n * Gm::WCOLS + 16 * j + jj;
-                    b_off[j][h] = A16_A_BYTES + r * 64 + ((q16 ^ swz_a(r)) * 16);
+                    b_off[j][h] = A_BYTES + r * 64 + ((q16 ^ swz_a(r)) * 16);
                 } else {
                     const int r = 8 * q16 + 4 * h + (jj >> 2);
                     const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
-                    b_off[j][h] = A16_A_BYTES + r * (2 * A16_BN) +
-                                  (((col >> 3) ^ swz_b16(r)) * 16) + (col & 7) * 2;
+                    const int sw = TM == 256 ? swz_b16(r) : swz_b192(r);
+                    b_off[j][h] = A_BYTES + r * (2 * TM) + (((col >> 3) ^ sw) * 16) + (col & 7) * 2;
                 }
             }
     }
 
     struct Frag {
-        u32x4 a[8], b[NJ];
+        u32x4 a[MI], b[NJ];
     };
-    // read piece q: q < 8 is A fragment q, then B fragment (q - 8) / 2, half
-    // (q - 8) % 2 (BT: B fragment q - 8)
+    // read piece q: q < MI is A fragment q, then B fragment (q - MI) / 2,
+    // half (q - MI) % 2 (BT: B fragment q - MI)
     auto read_piece = [&](Frag &f, const unsigned char *st, int q) {
-        if (q < 8) {
+        if (q < MI) {
             f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q]);
         } else if constexpr (BT) {
-            f.b[q - 8] = *reinterpret_cast<const u32x4 *>(st + b_off[q - 8][0]);
+            f.b[q - MI] = *reinterpret_cast<const u32x4 *>(st + b_off[q - MI][0]);
         } else {
-            const int j = (q - 8) >> 1, h = (q - 8) & 1;
+            const int j = (q - MI) >> 1, h = (q - MI) & 1;
             const s16x4 v =
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][h]));
             const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -731,7 +771,7 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
         }
     };
 
-    constexpr int MH = 8 * NJ / 2; // MFMAs per half step
+    constexpr int MH = MI * NJ / 2; // MFMAs per half step
     constexpr int OPS = Gm::READS + Gm::COPIES;
     static_assert(OPS % Gm::COPIES == 0, "copies evenly spread over the second half");
     Frag f0, f1;
@@ -741,7 +781,7 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
         unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
 #pragma unroll
         for (int q = 0; q < MH; ++q) {
-            const int i = q % 8, j = q / 8;
+            const int i = q % MI, j = q / MI;
             acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
         }
         // copies of steps k+2 and k+3 may stay in flight; past the last step
@@ -756,7 +796,7 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
 #pragma unroll
         for (int q = 0; q < (MH > OPS ? MH : OPS); ++q) {
             if (q < MH) {
-                const int i = q % 8, j = NJ / 2 + q / 8;
+                const int i = q % MI, j = NJ / 2 + q / MI;
                 acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
             }
             if (q < OPS) {
@@ -791,11 +831,13 @@ __device__ __forceinline__ void a16_mainloop(const GemmArgs &p, int m0, int n0,
 // Accumulators of a 16x16x32 wave tile set to bias[n] (or 0): lane l of
 // block (i, j) holds columns 16 j + 4 (l / 16) + {0..3} of the wave's
 // columns.
-template <int DT, int WN>
-__device__ __forceinline__ void a16_init_acc(const GemmArgs &p, int n0, int wave, int lane,
-                                             bool with_bias, f32x4 (&acc)[8][16 / WN])
+template <int DT, int WN, int TM = 256>
+__device__ __forceinline__ void a16_init_acc(
+    const GemmArgs &p, int n0, int wave, int lane, bool with_bias,
+    f32x4 (&acc)[A16Geom<WN, false, TM>::MI][A16Geom<WN, false, TM>::NJ])
 {
-    constexpr int NJ = 16 / WN, WCOLS = 16 * NJ;
+    constexpr int MI = A16Geom<WN, false, TM>::MI, NJ = A16Geom<WN, false, TM>::NJ;
+    constexpr int WCOLS = 16 * NJ;
     const bool use = with_bias && p.bias != nullptr;
     const int wave_n = wave % WN;
 #pragma unroll
@@ -810,52 +852,55 @@ __device__ __forceinline__ void a16_init_acc(const GemmArgs &p, int n0, int wave
                 b[e] = from_bits<DT>((unsigned short)(braw[e >> 1] >> (16 * (e & 1))));
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < MI; ++i)
             acc[i][j] = b;
     }
 }
 
 // Epilogue of a 16x16x32 wave tile: each wave restages its tile in its own
 // EP_BYTES of the (idle) stages and stores whole row segments.
-template <int DT, int ACT, int WN, bool BT>
-__device__ __forceinline__ void a16_epilogue(const GemmArgs &p, unsigned short *Cm, int m0, int n0,
-                                             int wave, int lane, unsigned char *st0,
-                                             unsigned char *st1, unsigned char *st2,
-                                             unsigned char *st3, const f32x4 (&acc)[8][16 / WN])
+template <int DT, int ACT, int WN, bool BT, int TM = 256>
+__device__ __forceinline__ void a16_epilogue(
+    const GemmArgs &p, unsigned short *Cm, int m0, int n0, int wave, int lane,
+    unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
+    const f32x4 (&acc)[A16Geom<WN, BT, TM>::MI][A16Geom<WN, BT, TM>::NJ])
 {
-    using Gm = A16Geom<WN, BT>;
-    constexpr int NJ = Gm::NJ;
-    constexpr int PER_STAGE = A16_STAGE / Gm::EP_BYTES; // wave tiles per stage
+    using Gm = A16Geom<WN, BT, TM>;
+    constexpr int MI = Gm::MI, NJ = Gm::NJ;
+    constexpr int PER_STAGE = A16Tile<TM>::STAGE / Gm::EP_BYTES; // wave tiles per stage
+    static_assert(PER_STAGE >= 1 && Gm::NW <= 4 * PER_STAGE, "epilogue fits the stages");
     const int es = wave / PER_STAGE;
     unsigned char *ep = (es == 0 ? st0 : es == 1 ? st1 : es == 2 ? st2 : st3) +
                         (wave % PER_STAGE) * Gm::EP_BYTES;
-    const int64_t cm = m0 + (wave / WN) * 128, cn = n0 + (wave % WN) * Gm::WCOLS;
+    const int64_t cm = m0 + (wave / WN) * Gm::WROWS, cn = n0 + (wave % WN) * Gm::WCOLS;
     unsigned short *cw = Cm + cm * p.ldc + cn;
-    const int rows = (int)min((int64_t)128, (int64_t)p.M - cm);
+    const int rows = (int)min((int64_t)Gm::WROWS, (int64_t)p.M - cm);
     const int cols = (int)min((int64_t)Gm::WCOLS, (int64_t)p.N - cn);
     if (p.R != nullptr)
-        restaged_epilogue16<DT, ACT, true, NJ>(acc, ep, lane, cw, p.ldc, p.R + cm * p.ldr + cn,
-                                               p.ldr, rows, cols);
+        restaged_epilogue16<DT, ACT, true, MI, NJ>(acc, ep, lane, cw, p.ldc,
+                                                   p.R + cm * p.ldr + cn, p.ldr, rows, cols);
     else
-        restaged_epilogue16<DT, ACT, false, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows, cols);
+        restaged_epilogue16<DT, ACT, false, MI, NJ>(acc, ep, lane, cw, p.ldc, nullptr, 0, rows,
+                                                    cols);
 }
 
-template <int DT, int ACT, int WN, bool BT, bool KM>
+template <int DT, int ACT, int WN, bool BT, bool KM, int TM = 256>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
                                                                     int tiles_n, int group_m)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[A16_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[A16_STAGE];
+    constexpr int STAGE = A16Tile<TM>::STAGE;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
-    const int m0 = tc.tm * A16_BM, n0 = tc.tn * A16_BN;
+    const int m0 = tc.tm * TM, n0 = tc.tn * TM;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    f32x4 acc[8][16 / WN];
-    a16_init_acc<DT, WN>(p, n0, wave, lane, true, acc);
+    f32x4 acc[A16Geom<WN, BT, TM>::MI][A16Geom<WN, BT, TM>::NJ];
+    a16_init_acc<DT, WN, TM>(p, n0, wave, lane, true, acc);
     // KM (K off the 128 grid): the whole quads on the unmasked loop, then
     // the last, partial quad on its own with the k past K masked (a second
     // pipeline fill, but the masking's registers stay out of the main loop,
@@ -863,11 +908,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     // register file)
     const int KT = (p.K / (AS_STAGES * AS_BK)) * AS_STAGES;
     if (!KM || KT > 0)
-        a16_mainloop<DT, WN, BT, false>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2, st3, acc);
+        a16_mainloop<DT, WN, BT, false, TM>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2, st3,
+                                            acc);
     if constexpr (KM)
-        a16_mainloop<DT, WN, BT, true>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1, st2,
-                                       st3, acc);
-    a16_epilogue<DT, ACT, WN, BT>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
+        a16_mainloop<DT, WN, BT, true, TM>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1,
+                                           st2, st3, acc);
+    a16_epilogue<DT, ACT, WN, BT, TM>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1073,7 +1119,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p
 namespace {
 struct AsyncConfig {
     int ti, tj;
-    int mfma16; // 256 x 256 on the 16x16x32 MFMA with this many waves; 0: 32x32x16
+    int mfma16; // tiles on the 16x16x32 MFMA with this many waves; 0: 32x32x16
     bool forced_only; // taken only when TG_FORCE_CONFIG names it
     const char *name;
 };
@@ -1082,6 +1128,9 @@ struct AsyncConfig {
 const AsyncConfig kAsyncConfigs[] = {
     {4, 4, 4, false, "async_256x256x32_s4_mfma16"},
     {4, 4, 8, true, "async_256x256x32_s4_mfma16_w8"}, // never ahead of the 4-wave kernel
+    // 192 x 192 tiles fill a wave where 256 x 256 ones leave much of it idle
+    // (3072^2 outputs: 256 tiles against 144)
+    {3, 3, 4, false, "async_192x192x32_s4_mfma16"},
     {4, 4, 0, false, "async_256x256x32_s4"},
     {2, 2, 0, false, "async_128x128x32_s4"},
     {1, 2, 0, false, "async_64x128x32_s4"},
@@ -1092,6 +1141,7 @@ const AsyncConfig kAsyncConfigs[] = {
 int num_async_configs() { return (int)(sizeof kAsyncConfigs / sizeof kAsyncConfigs[0]); }
 const char *async_config_name(int cfg) { return kAsyncConfigs[cfg].name; }
 bool async_forced_only(int cfg) { return kAsyncConfigs[cfg].forced_only; }
+bool async_mfma16(int cfg) { return kAsyncConfigs[cfg].mfma16 != 0; }
 int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
 int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
 
@@ -1156,8 +1206,8 @@ size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
 {
     SkPlan pl{0, 0, 0, 0, 0};
-    if (kAsyncConfigs[cfg].mfma16 != 4 || !async_eligible(a, cfg) || cus <= 0 ||
-        cus % kNumXcd != 0)
+    if (kAsyncConfigs[cfg].mfma16 != 4 || kAsyncConfigs[cfg].ti != 4 || !async_eligible(a, cfg) ||
+        cus <= 0 || cus % kNumXcd != 0)
         return pl;
     const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
     const int q = a.K / (AS_STAGES * AS_BK);
@@ -1168,6 +1218,12 @@ SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
     if (tiles % cus == 0 || 2 * tiles < cus || q < 2 || tiles >= (int64_t)1 << 24)
         return pl;
     const int64_t full = tiles / cus, rest = tiles % cus;
+    // Short of one wave the partly filled grid of whole tiles (or of 192 x
+    // 192 ones) does better unless any_size: measured, bf16 3584^3 (196
+    // tiles) 1141 TFLOP/s data-parallel against 890 split, 2049 x 4096 x
+    // 4096 (144) 748 against 692.
+    if (full == 0 && !any_size)
+        return pl;
     // After whole waves, a last wave of at least half the compute units stays
     // data-parallel: the kernel is power-bound, and such a wave runs at a
     // higher clock than a full one, which recovers most of what the idle
@@ -1201,9 +1257,10 @@ size_t stream_k_ws_floats(const SkPlan &sk) { return (size_t)2 * sk.grid * SK_SL
 hipError_t launch_async_sk(int cfg, int dt, int act, const GemmArgs &a, int group_m,
                            const SkPlan &sk, float *ws, int *counters, hipStream_t s)
 {
-    if (kAsyncConfigs[cfg].mfma16 != 4 || sk.sk_tiles <= 0 || sk.grid <= 0 || sk.q <= 0 ||
-        sk.per <= 0 || ws == nullptr || counters == nullptr || sk.grid % kNumXcd != 0 ||
-        (int64_t)sk.per * sk.grid < (int64_t)sk.sk_tiles * sk.q || sk.dp_tiles % sk.grid != 0)
+    if (kAsyncConfigs[cfg].mfma16 != 4 || kAsyncConfigs[cfg].ti != 4 || sk.sk_tiles <= 0 ||
+        sk.grid <= 0 || sk.q <= 0 || sk.per <= 0 || ws == nullptr || counters == nullptr ||
+        sk.grid % kNumXcd != 0 || (int64_t)sk.per * sk.grid < (int64_t)sk.sk_tiles * sk.q ||
+        sk.dp_tiles % sk.grid != 0)
         return hipErrorInvalidValue;
     const int tiles_m = async_tiles_m(a, cfg), tiles_n = async_tiles_n(a, cfg);
     dim3 grid(sk.grid), block(A16Geom<2, false>::NT);
@@ -1247,9 +1304,16 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                           A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
+        const bool t192 = kAsyncConfigs[cfg].ti == 3;
 #define TG_A16K(DT_, ACT_, KM_)                                                                  \
     do {                                                                                         \
-        if (wn == 4 && a.b_trans)                                                                \
+        if (t192 && a.b_trans)                                                                   \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 192>), grid,         \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (t192)                                                                           \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 192>), grid,        \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (wn == 4 && a.b_trans)                                                           \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, true, KM_>), grid, dim3(512), \
                                0, s, a, tiles_m, tiles_n, group_m);                              \
         else if (wn == 4)                                                                        \

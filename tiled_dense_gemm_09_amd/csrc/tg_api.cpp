@@ -242,8 +242,10 @@ int choose_config(int64_t M, int64_t N, int n_mat)
 }
 
 // Asynchronous-copy configuration for a problem, or -1: a forced name, else
-// the largest tile that still gives about one full wave of workgroups, else
-// the smallest eligible tile (most workgroups).
+// the 256 x 256 tiles on the 16x16x32 MFMA with about a full wave of
+// workgroups; with fewer, those or the 192 x 192 ones, whichever fills its
+// waves better, when it has at least half a wave of tiles; else the largest
+// 32x32x16 tile with about a full wave, else the smallest eligible tile.
 int choose_async(const tg::GemmArgs &a, const char *force)
 {
     const int n = tg::num_async_configs();
@@ -253,18 +255,48 @@ int choose_async(const tg::GemmArgs &a, const char *force)
                 return tg::async_eligible(a, i) ? i : -1;
         return -1;
     }
+    auto tiles = [&](int i) {
+        return (int64_t)tg::async_tiles_m(a, i) * tg::async_tiles_n(a, i) * a.n_mat;
+    };
+    // Short of a wave of 256 x 256 tiles (a whole one or more, with a short
+    // last one, is stream-K's, decided before): the kernel is power-bound,
+    // so a partly filled wave runs at a higher clock and costs less than its
+    // idle units suggest, but 192 x 192 tiles that fill their waves do
+    // better still, counted at 0.8 of the 256 x 256 tiles' rate (measured,
+    // bf16: 3584^3, 196 tiles of 256 against 361 of 192, 1141 against 922
+    // TFLOP/s; 3072^3, 144 against 256, 792 against 982; 4096^3 full waves of
+    // either, 1339 against 1073).
+    const int cus = device_cus();
+    auto fill = [&](int64_t t) {
+        const int64_t waves = (t + cus - 1) / cus;
+        return (double)t / (double)(waves * cus);
+    };
+    int best16 = -1;
+    double best_fill = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (tg::async_forced_only(i) || !tg::async_mfma16(i) || !tg::async_eligible(a, i))
+            continue;
+        const int64_t t = tiles(i);
+        if (tg::async_tile_m(i) == 256 && t >= 240)
+            return i;
+        const double f = (tg::async_tile_m(i) == 256 ? 1.0 : 0.8) * fill(t);
+        if (2 * t >= cus && f > best_fill) {
+            best16 = i;
+            best_fill = f;
+        }
+    }
+    if (best16 >= 0)
+        return best16;
     int best = -1;
     for (int i = 0; i < n; ++i) {
-        if (tg::async_forced_only(i) || !tg::async_eligible(a, i))
+        if (tg::async_forced_only(i) || tg::async_mfma16(i) || !tg::async_eligible(a, i))
             continue;
-        const int64_t tiles =
-            (int64_t)tg::async_tiles_m(a, i) * tg::async_tiles_n(a, i) * a.n_mat;
-        if (tiles >= 240)
+        if (tiles(i) >= 240)
             return i;
         best = i;
     }
-    // K off the 128 grid (masked on the 256 x 256 tiles only): without a
-    // full wave of those tiles, K padding or the tiled kernel does better
+    // K off the 128 grid (masked on the 16x16x32 tiles only): without half a
+    // wave of those tiles, K padding or the tiled kernel does better
     if (a.K % 128 != 0)
         return -1;
     return best;
@@ -1026,6 +1058,8 @@ int tg_lds_swizzle(int layout, int64_t row)
         return tg::swz_b<64>(r);
     case 3:
         return tg::swz_b16(r);
+    case 4:
+        return tg::swz_b192(r);
     default:
         return -1;
     }

@@ -55,6 +55,8 @@ int num_async_configs();
 const char *async_config_name(int cfg);
 // taken only when TG_FORCE_CONFIG names it
 bool async_forced_only(int cfg);
+// true for the configurations on the 16x16x32 MFMA (256 x 256 and 192 x 192 tiles)
+bool async_mfma16(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg);

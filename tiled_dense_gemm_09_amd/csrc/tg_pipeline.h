@@ -32,6 +32,15 @@ __host__ __device__ constexpr int swz_b(int r)
 // eight granule pairs, so the pass hits all 64 banks once.
 __host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * ((r >> 3) & 1)); }
 
+// B swizzle of the 192 x 192 16x16x32 kernel (384-byte rows, 24 granules;
+// rows of one parity start on the same bank, the other parity 128 bytes
+// over).  A transposing read pass covers two granules of rows a, a + 1, a +
+// 2, a + 3, a + 8, ..., a + 11 (a a multiple of 4): the four rows of each
+// parity must take four different granule pairs, which (r & 2) | ((r >> 1)
+// & 4) gives (bits 1 and 3 of the row); the XOR moves a granule only inside
+// its aligned group of eight, so it stays inside the 24-granule row.
+__host__ __device__ constexpr int swz_b192(int r) { return (r & 2) | ((r >> 1) & 4); }
+
 // Epilogue of one wave holding TI x TJ 32x32 FP32 accumulator blocks (the
 // bias already inside).  Lane l of block (i, j) holds row 32 i + l % 32 and
 // columns 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
