@@ -507,8 +507,9 @@ def run_sweep(torch, tg):
     captured graphs of 50 launches), bf16 products with M = 1..32
     (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB), and bf16
     shapes off the tile grid (X ~ N(0,1), W ~ N(0, 1/K)): token counts that
-    leave a partial last tile, pitches off the 8-element grid, and square
-    sizes whose K is not a multiple of 128."""
+    leave a partial last tile, grids short of a wave of 256 x 256 tiles,
+    pitches off the 8-element grid, and square sizes whose K is not a
+    multiple of 128."""
     def graph_ms(fn, per=50, reps=10):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -567,8 +568,10 @@ def run_sweep(torch, tg):
                               "library_GB/s": round(nb / ml / 1e6)}), flush=True)
         del Ws
     for (M, N, K) in ((2049, 4096, 4096), (3000, 11008, 4096), (5000, 4096, 4096),
-                      (4096, 4000, 4096), (4095, 4095, 4095), (4000, 4000, 4000),
-                      (8000, 8000, 8000)):
+                      (4096, 4000, 4096), (3584, 3584, 3584), (2304, 2304, 2304),
+                      (4608, 4608, 4608), (4095, 4095, 4095), (4097, 4097, 4097),
+                      (8191, 8191, 8191), (3000, 3000, 2999), (2000, 2000, 2000),
+                      (4000, 4000, 4000), (8000, 8000, 8000)):
         X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
         W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
         Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
