@@ -589,8 +589,9 @@ def run_sweep(torch, tg):
 
 def run_stream_k_sweep(torch, tg):
     """Shapes whose 256 x 256 tiles leave a partial last wave, timed with
-    stream-K on and off (TG_STREAMK) in the same process, beside the ROCm
-    library; bf16, X ~ N(0,1), W ~ N(0, 1/K), one JSON object per shape."""
+    stream-K as the library chooses it (TG_STREAMK=1), off (0) and on every
+    such grid (2) in the same process, beside the ROCm library; bf16, X ~
+    N(0,1), W ~ N(0, 1/K), one JSON object per shape."""
     torch.manual_seed(0)
     shapes = [(3072, 3072, 3072), (3584, 3584, 3584), (5120, 5120, 5120), (6144, 6144, 6144),
               (7168, 7168, 7168), (2049, 4096, 4096), (5000, 4096, 4096), (3000, 11008, 4096),
@@ -602,11 +603,10 @@ def run_stream_k_sweep(torch, tg):
         f = 2.0 * M * N * K
         steps = max(20, min(1000, int(4e13 / f)))
         rec = {"shape": "bf16 %dx%dx%d" % (M, N, K)}
-        for flag in ("1", "0"):
+        for flag, key in (("1", "default"), ("0", "off"), ("2", "any_size")):
             os.environ["TG_STREAMK"] = flag
             ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, steps // 5 + 2)
-            rec["on" if flag == "1" else "off"] = {"TFLOP/s": round(f / ms / 1e9, 1),
-                                                   "kernel": tg.last_kernel()}
+            rec[key] = {"TFLOP/s": round(f / ms / 1e9, 1), "kernel": tg.last_kernel()}
         os.environ.pop("TG_STREAMK")
         ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, steps // 5 + 2)
         rec["library_TFLOP/s"] = round(f / ml / 1e9, 1)
