@@ -96,6 +96,50 @@ def test_cold_k_padding_call_under_capture_takes_a_kernel_without_workspace(tg):
     assert tg.workspace_bytes() > w0
 
 
+def test_cold_staged_call_under_capture_takes_the_element_wise_kernel(tg):
+    # operands off the 16-byte grid on a large problem are normally staged
+    # through aligned copies in the workspace; when the workspace would have
+    # to grow during a capture, the call runs the tiled kernel with
+    # element-wise loads and stores (no workspace) and says so; the graph
+    # replays correctly, and the same call made eagerly afterwards is staged
+    import torch
+    w0 = tg.workspace_bytes()
+    n = 1025
+    while 16384 + 2 * (n * (n + 7) * 2 + n * (n + 7)) + 256 <= w0:
+        n = 2 * n + 1
+    if n > 8193:
+        pytest.skip("workspace already %d bytes" % w0)
+    M, N, K = n, n, n  # odd pitches: every operand off the grid
+    p = inputs.problem(BF16, M, N, K, seed=702, kind="int", bias=True, bias_kind="int")
+    A, B = util.to_dev(p["A"], BF16), util.to_dev(p["B"], BF16)
+    bias = util.to_dev(p["bias"], BF16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    say("case cold staged call under capture", M, N, K, "workspace", w0)
+    g, mark, raised = capture(lambda: tg.gemm(A, B, out=C, bias=bias))
+    assert raised is None, raised
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert "_unaligned" in kern and "not staged: stream capture" in kern, kern
+    assert tg.workspace_bytes() == w0
+    rows = [0, M // 2, M - 1]
+    refs = [oracle.gemm(BF16, p["A"], p["B"], p["bias"], rows=(r, r + 1))[1] for r in rows]
+    for i in range(2):
+        C.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "replay %d row %d" % (i, r))
+        tg.gemm(A, B, out=C, bias=bias)
+        torch.cuda.synchronize()
+        assert tg.last_kernel().endswith("_staged"), tg.last_kernel()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "eager %d row %d" % (i, r))
+    assert float(mark[0]) == 2.0
+    assert tg.workspace_bytes() > w0
+
+
 def test_cold_split_k_call_under_capture_launches_nothing(tg, monkeypatch):
     # a split-K call whose workspace would have to grow inside a capture
     # returns TG_ERROR_NOT_SUPPORTED, says why, and captures no launch: the
