@@ -159,7 +159,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", choices=["main", "plain", "ex", "mx", "attn", "qkv", "square8192",
-                                       "skinny", "small", "vendor", "copy", "sweep", "streamk"],
+                                       "skinny", "offgrid", "small", "vendor", "copy", "sweep",
+                                       "streamk"],
                     help="run one workload only (for profiling); no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true")
@@ -444,6 +445,28 @@ def run_secondary(args, torch, inputs, tg):
             "algorithmic_bytes": nbytes, "kernel": tg.last_kernel()}
         log("  ", out["bf16_skinny_32x8192x8192"])
         del X, Ws, Y, X32, Y32
+
+    if args.only in (None, "offgrid"):
+        # shapes off the configured tile grid, bf16, X ~ N(0,1), W ~ N(0,1/K):
+        # a grid short of one wave of 256 x 256 tiles (192 x 192 tiles), a
+        # ragged token count, and pitches off the 8-element grid (staged
+        # copies); the ROCm library GEMM on the same operands beside each
+        torch.manual_seed(3)
+        for (M, N, K) in ((3072, 3072, 3072), (2049, 4096, 4096), (4095, 4095, 4095)):
+            X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+            W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            f = 2.0 * M * N * K
+            log("off-grid: bf16 %dx%dx%d" % (M, N, K))
+            ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, warm)
+            kern = tg.last_kernel()
+            ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, warm)
+            key = "bf16_%dx%dx%d" % (M, N, K)
+            out[key] = {"ms": round(ms, 5), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 1),
+                        "frac_mfma_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                        "kernel": kern, "library_TFLOP/s": round(f / (ml * 1e-3) / 1e12, 1)}
+            log("  ", out[key])
+            del X, W, Y
 
     if args.only in (None, "vendor"):
         # context only: the ROCm BLAS library GEMM (torch.matmul) on the same
