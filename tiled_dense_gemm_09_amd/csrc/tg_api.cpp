@@ -42,6 +42,15 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// x rounded up to a multiple of m (m > 0, x >= 0), or -1 when the result
+// would not stay below 2^31 - 1024 (sizes padded for the kernels must fit
+// their 32-bit index arithmetic)
+int round_up_dim(int64_t x, int64_t m)
+{
+    const int64_t r = (x + m - 1) / m * m;
+    return r < kMaxDim - 1024 ? (int)r : -1;
+}
+
 // Byte span [lo, hi) of a rows x cols matrix with pitch ld (16-bit elements).
 struct Span {
     uintptr_t lo, hi;
@@ -309,14 +318,15 @@ int choose_async(const tg::GemmArgs &a, const char *force)
 // with a full wave of tiles.
 bool kpad_eligible(const tg::GemmArgs &a, const char *force)
 {
-    const int K2 = (a.K + 127) / 128 * 128;
-    if ((force && *force) || a.n_mat != 1 || a.K % 128 == 0 || a.K < 128 ||
+    const int K2 = round_up_dim(a.K, 128);
+    if ((force && *force) || a.n_mat != 1 || a.K % 128 == 0 || a.K < 128 || K2 < 0 ||
+        round_up_dim(a.N, 8) < 0 ||
         (double)a.M * a.N * a.K < (double)(1 << 30) || 8 * (K2 - a.K) > a.K)
         return false;
     tg::GemmArgs a2 = a;
     a2.K = K2;
     a2.lda = a2.K;
-    a2.ldb = a.b_trans ? a2.K : (a.N + 7) / 8 * 8;
+    a2.ldb = a.b_trans ? a2.K : round_up_dim(a.N, 8);
     const int cfg = choose_async(a2, nullptr);
     if (cfg < 0)
         return false;
@@ -351,7 +361,10 @@ StagePlan plan_staging(const tg::GemmArgs &a, const char *force, int cus, int sk
     if ((force && *force) || a.n_mat != 1 || a.M <= 32 || a.K < 8 ||
         (double)a.M * a.N * a.K < (double)(1 << 30))
         return sp;
-    const int N8 = (a.N + 7) / 8 * 8;
+    const int N8 = round_up_dim(a.N, 8), K8 = round_up_dim(a.K, 8);
+    const int K128 = round_up_dim(a.K, 128);
+    if (N8 < 0 || K8 < 0 || K128 < 0)
+        return sp;
     const bool c_ok = aligned16(a.C[0]) && a.ldc % 8 == 0 && N8 == a.N;
     const bool r_ok = a.R == nullptr || (aligned16(a.R) && a.ldr % 8 == 0 && c_ok);
     const bool bias_ok = a.bias == nullptr || (((uintptr_t)a.bias & 7u) == 0 && N8 == a.N);
@@ -382,7 +395,6 @@ StagePlan plan_staging(const tg::GemmArgs &a, const char *force, int cus, int sk
         sp.r_elems = sp.r ? round((int64_t)a.M * N8) : 0;
         sp.bias_elems = sp.bias ? round(N8) : 0;
     };
-    const int K128 = (a.K + 127) / 128 * 128;
     if (sk_mode != 0 && cus > 0 && 8 * (K128 - a.K) <= a.K) {
         const tg::GemmArgs a2 = staged(K128);
         for (int i = 0; i < tg::num_async_configs(); ++i) {
@@ -396,7 +408,7 @@ StagePlan plan_staging(const tg::GemmArgs &a, const char *force, int cus, int sk
             }
         }
     }
-    for (const int K2 : {(a.K + 7) / 8 * 8, K128}) {
+    for (const int K2 : {K8, K128}) {
         const int cfg = choose_async(staged(K2), nullptr);
         if (cfg >= 0) {
             take(cfg, K2);
@@ -533,7 +545,8 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     // K padding needs the workspace; when it cannot be had (a capture that
     // would grow it, no memory) the kernels that need none run instead
     bool kpad = !noalloc && fast && !force_generic && M > 32 && kpad_eligible(a, force);
-    const int kpad_k2 = (a.K + 127) / 128 * 128, kpad_n8 = (a.N + 7) / 8 * 8;
+    // (both sizes fit when kpad_eligible holds; -1 otherwise, then unused)
+    const int kpad_k2 = round_up_dim(a.K, 128), kpad_n8 = round_up_dim(a.N, 8);
     const int64_t kpad_a_elems = (int64_t)a.M * kpad_k2;
     const int64_t kpad_b_elems = b_trans ? (int64_t)a.N * kpad_k2 : (int64_t)kpad_k2 * kpad_n8;
     void *kpad_base = nullptr;
