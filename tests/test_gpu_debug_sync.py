@@ -16,7 +16,7 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 ENV_KEYS = ("TG_FORCE_CONFIG", "TG_SPLITK", "TG_STREAMK", "TG_SKINNY_COLS", "TG_SKINNY_BN",
-            "TG_SKINNY_SPLITS", "TG_ATTN_BM")
+            "TG_SKINNY_SPLITS", "TG_SKINNY_REGS", "TG_ATTN_BM")
 
 
 def say(*a):
@@ -134,8 +134,13 @@ CASES = [
     ("skinny_bn256", {"TG_SKINNY_BN": "256"}, gemm_case(16, 4096, 2048, "bf16"),
      "skinny_stream_bn256"),
     ("skinny_m32", {}, gemm_case(32, 2048, 2048), "skinny_stream_bn128"),
-    ("skinny_registers", {}, gemm_case(16, 1000, 1024), "skinny_bn"),
+    ("skinny_registers", {"TG_SKINNY_REGS": "1"}, gemm_case(16, 1000, 1024), "skinny_bn"),
     ("skinny_cols", {"TG_SKINNY_COLS": "1"}, gemm_case(16, 4096, 2048, "bf16"), "skinny_cols"),
+    ("skinny_realign", {}, gemm_case(16, 4099, 2048, "bf16", b_pad=3), "skinny_realign"),
+    ("skinny_nk", {}, gemm_case(16, 4096, 4096, "bf16", bt=True), "skinny_nk"),
+    ("skinny_nk_m32_tail", {}, gemm_case(24, 1000, 1000, bt=True, residual=True), "skinny_nk"),
+    ("skinny_realign_m32_xstaged", {}, gemm_case(24, 1500, 1000, a_pad=3, b_pad=1, residual=True),
+     "skinny_realign"),
     ("qkv", {}, qkv_case(1024, 1024, 1024), "async"),
     ("mx_e4m3", {}, mx_case(1024, 1024, 1024), "mx_256x256x64_s4"),
     ("attention_full", {}, attn_case(1, 2, 1024, 128, False), "attn"),

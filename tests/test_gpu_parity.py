@@ -593,6 +593,161 @@ def test_off_grid_operands_staged_on_stream_k_integer_exact(tg, monkeypatch):
     util.check_exact(util.to_bits(C), ref, "staged stream-K")
 
 
+REALIGN_CASES = [
+    # (dt, M, N, K, pitch pads of A, B, C, W offset, C offset (elements),
+    # split count forced or 0, random or integer inputs): small M with W,
+    # X or Y off the 16-byte grid, taken by the realigning streaming kernel.
+    # An odd vocabulary width at M = 1, 16 and 32 (unsplit, 419 tiles); an
+    # odd W pitch with W starting 3 elements into its buffer; every operand
+    # odd (X copied, K cut inside a slab); only Y off the grid; three tiles
+    # with K split 5 ways (320 deep: a short last chunk); forced split counts
+    (BF16, 1, 50257, 4096, (0, 0, 0), 0, 0, 0, "int"),
+    (F16, 16, 50257, 4096, (0, 0, 0), 0, 1, 0, "int"),
+    (BF16, 32, 50257, 2048, (0, 0, 0), 0, 0, 0, "normal"),
+    (BF16, 32, 4099, 1024, (0, 2, 1), 3, 0, 0, "int"),
+    (F16, 17, 1000, 1000, (3, 5, 0), 1, 0, 0, "int"),
+    (BF16, 16, 4095, 4095, (0, 0, 0), 0, 0, 0, "int"),
+    (F16, 5, 4096, 4096, (0, 0, 1), 0, 0, 0, "int"),
+    (BF16, 8, 300, 320, (0, 1, 0), 7, 0, 0, "int"),
+    (F16, 16, 2001, 2048, (0, 0, 0), 0, 0, 1, "int"),
+    (BF16, 24, 2001, 2048, (0, 0, 0), 0, 0, 3, "normal"),
+    (F16, 16, 2001, 2112, (0, 0, 0), 5, 0, 7, "int"),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,pads,woff,off,splits,kind", REALIGN_CASES)
+def test_small_m_off_grid_realigned(tg, monkeypatch, dt, M, N, K, pads, woff, off, splits, kind):
+    # NaN in every pitch padding, before W and around the output: the
+    # aligned pieces read past a row's last column feed only columns that
+    # are never stored, and rows past K read as zero.  Bias, GELU and a
+    # residual with its own odd pitch; bit-exact on integer inputs, within
+    # the tolerance on normal ones.
+    import torch
+    if splits:
+        monkeypatch.setenv("TG_SKINNY_SPLITS", str(splits))
+    else:
+        monkeypatch.delenv("TG_SKINNY_SPLITS", raising=False)
+    monkeypatch.delenv("TG_FORCE_CONFIG", raising=False)
+    act = oracle.ACT_GELU_TANH if kind == "normal" else oracle.ACT_NONE
+    p = inputs.problem(dt, M, N, K, seed=260 + M + N, kind=kind, bias=True,
+                       bias_kind="int" if kind == "int" else "bias")
+    R = inputs.draw(np.random.default_rng(261 + N), (M, N), "int", dt, 8.0)
+    lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
+    A = util.to_dev(padded(p["A"], lda, dt), dt)[:, :K]
+    wflat = np.concatenate([np.full(woff, NAN_BITS[dt], np.uint16),
+                            padded(p["B"], ldb, dt).reshape(-1)])
+    B = util.to_dev(wflat, dt)[woff:].view(K, ldb)[:, :N]
+    bias = util.to_dev(p["bias"], dt)
+    Rd = util.to_dev(padded(R, N + 3, dt), dt)[:, :N]
+    Cbuf = util.to_dev(np.full(M * ldc + 1, NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[off:off + M * ldc].view(M, ldc)[:, :N]
+    say("case realign", dt, M, N, K, "pitches", lda, ldb, ldc, "W offset", woff, "C offset", off,
+        "splits", splits or "planned", kind)
+    tg.gemm(A, B, out=C, bias=bias, act="gelu_tanh" if act else "none", residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("skinny_realign_bn120_split"), kern
+    if splits:  # the planner keeps a forced count within the K chunks
+        assert ("_split1x" in kern) == (splits == 1), kern
+    assert ("_m32" in kern) == (M > 16), kern
+    assert ("_xstaged" in kern) == (lda % 8 != 0 or K % 64 != 0), kern
+    f64, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], act=act, R=R)
+    got = util.to_bits(C)
+    if kind == "int":
+        util.check_exact(got, ref, "realign " + kern)
+    else:
+        util.check_tol(dt, got, f64, "realign " + kern, ref_bits=ref)
+    full = util.to_bits(Cbuf)
+    inside = np.zeros(full.shape, bool)
+    for i in range(M):
+        inside[off + i * ldc: off + i * ldc + N] = True
+    assert np.all(full[~inside] == NAN_BITS[dt]), "write outside the output"
+
+
+NK_CASES = [
+    # (dt, M, N, K, pitch pads of A, B (rows of the [N,K] store), C, split
+    # count forced or 0, random or integer inputs): small M with B stored
+    # [N,K], 16-byte aligned rows, taken by the register-streaming kernel.
+    # M = 1, 16, 32 at 8192 and an odd vocabulary width; K cut inside a
+    # 16-byte piece (1001, 777: the last piece masked) with X copied or read
+    # in place; Y with an odd pitch; forced split counts
+    (BF16, 1, 8192, 8192, (0, 0, 0), 0, "int"),
+    (F16, 16, 50257, 4096, (0, 0, 0), 0, "int"),
+    (BF16, 32, 4096, 4096, (0, 0, 3), 0, "normal"),
+    (F16, 17, 1000, 1001, (0, 7, 0), 0, "int"),
+    (BF16, 5, 300, 777, (7, 7, 1), 0, "int"),
+    (F16, 16, 2048, 2048, (0, 0, 0), 1, "int"),
+    (BF16, 24, 2000, 3000, (8, 8, 0), 3, "normal"),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,pads,splits,kind", NK_CASES)
+def test_small_m_b_stored_nk(tg, monkeypatch, dt, M, N, K, pads, splits, kind):
+    # NaN in every pitch padding and around the output; bias, GELU and a
+    # residual with an odd pitch; bit-exact on integer inputs, within the
+    # tolerance on normal ones
+    import torch
+    if splits:
+        monkeypatch.setenv("TG_SKINNY_SPLITS", str(splits))
+    else:
+        monkeypatch.delenv("TG_SKINNY_SPLITS", raising=False)
+    monkeypatch.delenv("TG_FORCE_CONFIG", raising=False)
+    act = oracle.ACT_GELU_TANH if kind == "normal" else oracle.ACT_NONE
+    p = inputs.problem(dt, M, N, K, seed=280 + M + N, kind=kind, bias=True,
+                       bias_kind="int" if kind == "int" else "bias",
+                       b_scale=1.0 if kind == "int" else K ** -0.5)
+    R = inputs.draw(np.random.default_rng(281 + N), (M, N), "int", dt, 8.0)
+    lda, ldb, ldc = K + pads[0], K + pads[1], N + pads[2]
+    A = util.to_dev(padded(p["A"], lda, dt), dt)[:, :K]
+    B = util.to_dev(padded(np.ascontiguousarray(p["B"].T), ldb, dt), dt)[:, :K].t()
+    bias = util.to_dev(p["bias"], dt)
+    Rd = util.to_dev(padded(R, N + 3, dt), dt)[:, :N]
+    Cbuf = util.to_dev(np.full((M, ldc), NAN_BITS[dt], np.uint16), dt)
+    C = Cbuf[:, :N]
+    say("case B[N,K] small M", dt, M, N, K, "pitches", lda, ldb, ldc, "splits",
+        splits or "planned", kind)
+    tg.gemm(A, B, out=C, bias=bias, act="gelu_tanh" if act else "none", residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("skinny_nk_bn64_split"), kern
+    if splits:
+        assert ("_split1x" in kern) == (splits == 1), kern
+    assert ("_m32" in kern) == (M > 16), kern
+    assert ("_xstaged" in kern) == (lda % 8 != 0), kern
+    f64, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], act=act, R=R)
+    got = util.to_bits(C)
+    if kind == "int":
+        util.check_exact(got, ref, "B[N,K] small M " + kern)
+    else:
+        util.check_tol(dt, got, f64, "B[N,K] small M " + kern, ref_bits=ref)
+    assert np.all(util.to_bits(Cbuf)[:, N:] == NAN_BITS[dt]), "wrote into the pitch padding"
+
+
+def test_realigned_kernel_forced_on_aligned_operands_matches_streaming(tg, monkeypatch):
+    # TG_FORCE_CONFIG=skinny_realign runs the realigning kernel on aligned
+    # operands too (every row offset 0); integer inputs: the same bits as
+    # the streaming kernel and the oracle
+    import torch
+    dt, M, N, K = BF16, 16, 4096, 2048
+    p = inputs.problem(dt, M, N, K, seed=270, kind="int", bias=True, bias_kind="int")
+    A, B, bias = util.to_dev(p["A"], dt), util.to_dev(p["B"], dt), util.to_dev(p["bias"], dt)
+    monkeypatch.delenv("TG_FORCE_CONFIG", raising=False)
+    C1 = tg.gemm(A, B, bias=bias)
+    torch.cuda.synchronize()
+    k1 = tg.last_kernel()
+    monkeypatch.setenv("TG_FORCE_CONFIG", "skinny_realign")
+    C2 = tg.gemm(A, B, bias=bias)
+    torch.cuda.synchronize()
+    k2 = tg.last_kernel()
+    say("  kernels", k1, "|", k2)
+    assert k1.startswith("skinny_stream") and k2.startswith("skinny_realign"), (k1, k2)
+    _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
+    util.check_exact(util.to_bits(C1), ref, "streaming")
+    util.check_exact(util.to_bits(C2), ref, "realign forced")
+
+
 def test_k_zero_gives_activated_bias(tg):
     import torch
     dt = BF16
@@ -1385,8 +1540,9 @@ def test_transposed_b_k_zero(tg):
 
 
 def test_small_m_dispatch_bounds(tg):
-    # M <= 32 streams W when the streaming kernel fits; larger M, or 16 < M
-    # <= 32 on shapes it does not fit, take the square-tile paths
+    # M <= 32 streams W: the split-K streaming kernel when it fits, the
+    # realigning one for other shapes with N and K of at least 256; larger M,
+    # or narrower shapes, take the square-tile paths
     import torch
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
     for M, expect in ((16, "skinny_stream"), (32, "skinny_stream"), (33, "tiled")):
@@ -1395,6 +1551,8 @@ def test_small_m_dispatch_bounds(tg):
         assert tg.last_kernel().startswith(expect), (M, tg.last_kernel())
     x = torch.zeros((20, 1000), dtype=torch.bfloat16, device="cuda")
     tg.gemm(x, torch.zeros((1000, 1000), dtype=torch.bfloat16, device="cuda"))
+    assert tg.last_kernel().startswith("skinny_realign"), tg.last_kernel()
+    tg.gemm(x, torch.zeros((1000, 200), dtype=torch.bfloat16, device="cuda"))
     assert not tg.last_kernel().startswith("skinny"), tg.last_kernel()
     torch.cuda.synchronize()
 

@@ -102,13 +102,19 @@ FAMILIES = [
     ("generic_bt", {"TG_FORCE_CONFIG": "generic"}, F16, 64, 96, 80, True, "generic_fma"),
     ("skinny_stream", {}, BF16, 16, 2048, 1024, False, "skinny_stream"),
     ("skinny_stream_m32", {}, F16, 32, 2048, 1024, False, "skinny_stream"),
-    ("skinny_registers", {}, F16, 16, 1000, 1024, False, "skinny_bn"),
+    ("skinny_registers", {"TG_SKINNY_REGS": "1"}, F16, 16, 1000, 1024, False, "skinny_bn"),
     ("skinny_cols", {"TG_SKINNY_COLS": "1"}, BF16, 16, 4096, 1024, False, "skinny_cols"),
+    ("skinny_realign", {"TG_FORCE_CONFIG": "skinny_realign"}, F16, 16, 1000, 1000, False,
+     "skinny_realign"),
+    ("skinny_realign_m32", {"TG_FORCE_CONFIG": "skinny_realign"}, BF16, 32, 1000, 1000, False,
+     "skinny_realign"),
+    ("skinny_nk", {}, F16, 16, 1000, 1000, True, "skinny_nk"),
+    ("skinny_nk_m32", {}, BF16, 32, 1000, 1000, True, "skinny_nk"),
 ]
 
 
 def set_env(monkeypatch, env):
-    for k in ("TG_FORCE_CONFIG", "TG_SPLITK", "TG_SKINNY_COLS"):
+    for k in ("TG_FORCE_CONFIG", "TG_SPLITK", "TG_SKINNY_COLS", "TG_SKINNY_REGS"):
         monkeypatch.delenv(k, raising=False)
     for k, v in env.items():
         monkeypatch.setenv(k, v)

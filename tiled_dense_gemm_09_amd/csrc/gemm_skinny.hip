@@ -811,6 +811,605 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Realigning variant: W off the 16-byte grid (a row pitch that is not a
+// multiple of 8 elements, or a base address that is only 2-byte aligned),
+// the shape of a decode step against an odd-sized vocabulary.  Row k of W
+// then starts at element offset (w0 + k ldb) mod 8 inside a 16-byte piece (w0:
+// the base's offset from the aligned address below it), different on each
+// of 8 consecutive rows, so neither the direct-to-LDS copies nor the
+// transposing LDS reads can take a row as it stands.
+//
+// Workgroup (tile, split) keeps 120 columns and one K-chunk.  For each row
+// of a 64-deep slab it copies the 16 aligned pieces (128 elements) that begin
+// with the piece holding the tile's first column: the 120 columns sit at the
+// row's offset o (0 <= o <= 7) inside them.  A slab advances the address by
+// 64 ldb elements, a multiple of 8, so the offset of slab row r is the same in
+// every slab and every tile, o(r) = (w0 + r ldb) mod 8, and since the 8 k
+// values of a fragment come from rows r = 0..7 mod 8, each fragment read has
+// one offset shared by every lane: the W fragments are read element by
+// element from LDS at that offset.  The MFMA covers 128 columns; the 8 past
+// the tile's 120 (and those past N) are computed from whatever the pieces
+// hold and never stored.  Pieces are clamped to the last one of the row that
+// holds a column below N, so every piece read holds an element of W.
+//
+// LDS stage (20 KiB, 4 stages, two workgroups per CU): W [64 rows][16
+// pieces], piece j of row r's run at position (j + 4 ((r >> 3) & 3)) mod 16,
+// which places the four rows a 64-lane element read touches (one per 16-lane
+// group, 8 rows apart) on disjoint banks; then X [16 rows][64 k] twice for
+// M <= 16 (once per 16 rows for M <= 32), granule c of row r at c ^ (r & 7).
+// X must be 16-byte aligned with a pitch of 8 elements and hold zeros (or
+// readable values) up to K rounded up to 64; rows of W at or past K read as
+// zero.  Split-K partials are combined as in the streaming kernel: in split
+// order by the last workgroup of each tile.
+namespace {
+
+constexpr int SR_BN = 120; // columns stored per workgroup
+constexpr int SR_BK = 64, SR_NT = 256, SR_STAGES = 4, SR_NJ = 2;
+constexpr int SR_ROW_BYTES = 256;                         // 16 pieces per slab row
+constexpr int SR_W_BYTES = SR_BK * SR_ROW_BYTES;          // 16 KiB
+constexpr int SR_STAGE_BYTES = SR_W_BYTES + 2 * SA_X_BYTES;
+constexpr int SR_COPIES = 5;                              // per wave per slab: 4 of W, 1 of X
+
+// Byte offset of element e (0 <= e < 136) of slab row r's run in a stage.
+__host__ __device__ constexpr int sr_off(int r, int e)
+{
+    return r * SR_ROW_BYTES + ((((e >> 3) + 4 * ((r >> 3) & 3)) & 15) << 4) + ((e & 7) << 1);
+}
+
+} // namespace
+
+template <int DT, int ACT, int MB>
+__global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs p, int n_tiles,
+                                                                       int k_chunk, int splits,
+                                                                       float *ws, int *counters)
+{
+    static_assert(MB == 1 || MB == 2, "up to 32 rows");
+    __shared__ __attribute__((aligned(1024))) unsigned char st[SR_STAGES][SR_STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // unit u = split n_tiles + tile, placed XCD-contiguously: neighbouring
+    // tiles share the 128-byte line at their boundary, fetched through one L2
+    const int units = n_tiles * splits;
+    const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+    const int uq = units / kNumXcd, ur = units % kNumXcd;
+    const int u = xcd * uq + (xcd < ur ? xcd : ur) + slot;
+    const int split = u / n_tiles;
+    const int tile_n = u - split * n_tiles;
+    const int n0 = tile_n * SR_BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int kbeg = split * k_chunk;
+    const int slabs = (min(K, kbeg + k_chunk) - kbeg + SR_BK - 1) / SR_BK;
+    const int64_t ldb = p.ldb;
+
+    // W in 16-byte pieces counted from the aligned address at or below its base
+    const uintptr_t wb = (uintptr_t)p.B[0];
+    const unsigned char *wal = (const unsigned char *)(wb & ~(uintptr_t)15);
+    const int64_t w0 = (int64_t)((wb & 15) >> 1);
+
+    // W copy c of this wave: slab row r = 4 (4 wave + c) + lane / 16, stage
+    // position lane % 16, which holds piece (lane % 16 - 4 ((r >> 3) & 3)) mod
+    // 16 of the row's run, clamped to the row's last piece with a column < N
+    const unsigned char *gw[4];
+    int wr[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int r = 4 * (wave * 4 + c) + (lane >> 4);
+        const int64_t e = w0 + (int64_t)(kbeg + r) * ldb; // row start, in elements
+        const int64_t first = (e + n0) >> 3, last = (e + N - 1) >> 3;
+        const int64_t j = ((lane & 15) - 4 * ((r >> 3) & 3)) & 15;
+        gw[c] = wal + 16 * (first + j < last ? first + j : last);
+        wr[c] = r;
+    }
+    const int64_t w_step = 2 * (int64_t)SR_BK * ldb; // bytes per slab
+    // X copy: rows 8 w + lane/8 for MB = 2, rows 8 (w & 1) + lane/8 for MB = 1
+    // (waves 2 and 3 write the duplicate), clamped to M-1, granule (lane%8) ^ (row & 7)
+    const int xr = 8 * (MB == 2 ? wave : (wave & 1)) + (lane >> 3);
+    const unsigned short *gx =
+        p.A + (int64_t)min(xr, M - 1) * p.lda + kbeg + (((lane & 7) ^ (xr & 7)) * 8);
+
+    auto copy = [&](int s, unsigned char *stage, int c) {
+        const unsigned lds = (unsigned)(uintptr_t)(lds_void *)stage;
+        if (c < 4) {
+            const unsigned char *src = gw[c] + s * w_step;
+            // a row k at or past K copies row k - 8d (d = ceil((k - K + 1) / 8)),
+            // whose run has the same offset; its values are masked at the read
+            if (kbeg + (s + 1) * SR_BK > K) {
+                const int k = kbeg + s * SR_BK + wr[c];
+                if (k >= K)
+                    src -= (int64_t)16 * ldb * ((k - K + 8) >> 3);
+            }
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src),
+                         "{m0}"(lds + (wave * 4 + c) * 1024)
+                         : "memory");
+        } else {
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gx + s * SR_BK),
+                         "{m0}"(lds + SR_W_BYTES + wave * 1024)
+                         : "memory");
+        }
+    };
+
+    // W fragment of block j, 32-deep half kk: lane l supplies column
+    // 32 wave + 16 j + l % 16 at k = 32 kk + 8 (l / 16) + t, t = 0..7; row
+    // 8 (l / 16) + t has offset o(t) = (w0 + t ldb) mod 8 (the same for every
+    // lane), and half kk = 1 lies 32 rows (8 KiB) further on.
+    int w_off[SR_NJ][8];
+    {
+        const int g = lane >> 4;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int o = (int)((w0 + t * (ldb & 7)) & 7);
+#pragma unroll
+            for (int j = 0; j < SR_NJ; ++j)
+                w_off[j][t] = sr_off(8 * g + t, o + 32 * wave + 16 * j + (lane & 15));
+        }
+    }
+    int x_off[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int r = 16 * mb + (lane & 15);
+            x_off[mb][kk] = SR_W_BYTES + r * 128 + (((4 * kk + (lane >> 4)) ^ (r & 7)) * 16);
+        }
+
+    f32x4 acc[MB][SR_NJ];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < SR_NJ; ++j)
+            acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // kmax: rows of the slab below K (64 except in a last slab that K cuts)
+    auto compute = [&](const unsigned char *stage, int kmax) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4 xf[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                xf[mb] = *reinterpret_cast<const u32x4 *>(stage + x_off[mb][kk]);
+#pragma unroll
+            for (int j = 0; j < SR_NJ; ++j) {
+                unsigned v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    v[t] = *reinterpret_cast<const unsigned short *>(stage + kk * 32 * SR_ROW_BYTES +
+                                                                     w_off[j][t]);
+                if (kmax < SR_BK) {
+                    const int r0 = 32 * kk + 8 * (lane >> 4);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        v[t] = r0 + t < kmax ? v[t] : 0u;
+                }
+                const u32x4 wf = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                                  v[6] | (v[7] << 16)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][j] = mfma16x16x32<DT>(wf, xf[mb], acc[mb][j]);
+            }
+        }
+    };
+
+    // slab s: wait for its copies (those of the next STAGES-2 slabs may stay
+    // in flight), barrier, copy slab s+STAGES-1 into the stage slab s-1 used
+    // (clamped past the end: repeats the last slab into a stage nobody
+    // reads), compute (steps past the last slab only keep the counts even)
+    auto step = [&](int s, auto sidx) {
+        constexpr int S = decltype(sidx)::value;
+        wait_vmcnt<(SR_STAGES - 2) * SR_COPIES>();
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        stage_barrier();
+        const int sc = min(s + SR_STAGES - 1, slabs - 1);
+#pragma unroll
+        for (int c = 0; c < SR_COPIES; ++c)
+            copy(sc, st[(S + SR_STAGES - 1) % SR_STAGES], c);
+        if (s < slabs)
+            compute(st[S], min(SR_BK, K - (kbeg + s * SR_BK)));
+    };
+    auto prologue = [&](auto sidx) {
+        constexpr int S = decltype(sidx)::value;
+#pragma unroll
+        for (int c = 0; c < SR_COPIES; ++c)
+            copy(min(S, slabs - 1), st[S], c);
+    };
+    static_for<0, SR_STAGES - 1>([&](auto i) { prologue(i); });
+    for (int s = 0; s < slabs; s += SR_STAGES)
+        static_for<0, SR_STAGES>([&](auto i) { step(s + decltype(i)::value, i); });
+    wait_vmcnt<0>();
+
+    // Lane l holds Y[m = 16 mb + l % 16][n = n0 + 32 w + 16 j + 4 (l / 16) + r]
+    // in acc[mb][j][r]; element-wise stores (Y, bias and R may sit anywhere).
+    auto store_rows = [&](const f32x4 (&val)[MB][SR_NJ]) {
+        const int nmax = min(N - n0, SR_BN);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + (lane & 15);
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < SR_NJ; ++j) {
+                const int nl = wave * 32 + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (nl + r >= nmax)
+                        continue;
+                    const int n = n0 + nl + r;
+                    float x = val[mb][j][r];
+                    if (p.bias != nullptr)
+                        x += from_bits<DT>(p.bias[n]);
+                    x = activate<ACT>(x);
+                    if (p.R != nullptr)
+                        x += from_bits<DT>(p.R[(int64_t)m * p.ldr + n]);
+                    p.C[0][(int64_t)m * p.ldc + n] = to_bits<DT>(x);
+                }
+            }
+        }
+    };
+    if (splits == 1) {
+        store_rows(acc);
+        return;
+    }
+
+    // Split-K: partials in accumulator order, device-coherent stores and
+    // loads, one arrival counter per tile, the last workgroup adds the
+    // splits in order 0..splits-1 (as in the streaming kernel above).
+    constexpr int PV = MB * SR_NJ;         // vectors per lane per split
+    constexpr int BLOCK = 16 * MB * 128;   // floats per workgroup partial
+    float *ws_tile = ws + (int64_t)tile_n * splits * BLOCK;
+    const int lane_off = (wave * PV) * 256 + lane * 4;
+    {
+        f32x4 v[PV];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < SR_NJ; ++j)
+                v[mb * SR_NJ + j] = acc[mb][j];
+        store_partial<PV>(ws_tile + split * BLOCK + lane_off, v); // stores and waits
+    }
+    int *s_last = reinterpret_cast<int *>(&st[0][0]);
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (old == splits - 1);
+    }
+    __syncthreads();
+    if (!*s_last)
+        return;
+
+    constexpr int RS = 4;       // splits read back per round
+    constexpr int L = RS * PV;  // loads per round: 8 or 16
+    f32x4 sum[MB][SR_NJ];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < SR_NJ; ++j)
+            sum[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
+        f32x4 v[L];
+#pragma unroll
+        for (int q = 0; q < RS; ++q) {
+            const float *src = ws_tile + min(sp0 + q, splits - 1) * BLOCK + lane_off;
+#pragma unroll
+            for (int t = 0; t < PV; ++t)
+                asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                             : "=v"(v[q * PV + t])
+                             : "v"(src + t * 256)
+                             : "memory");
+        }
+        // the loads above are invisible to the compiler's wait tracking: wait
+        // here and pass every value through, so nothing reads (or moves) one
+        // earlier
+        if constexpr (L == 16) {
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                           "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                           "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                         :
+                         : "memory");
+        } else {
+            static_assert(L == 8, "combine operand count");
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                           "+v"(v[6]), "+v"(v[7])
+                         :
+                         : "memory");
+        }
+#pragma unroll
+        for (int q = 0; q < RS; ++q)
+            if (sp0 + q < splits)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < SR_NJ; ++j)
+                        sum[mb][j] += v[q * PV + mb * SR_NJ + j];
+    }
+    store_rows(sum);
+    if (tid == 0)
+        __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Small M with B stored [N,K] (a linear layer's weight W[n][k]): each row of
+// W is K-contiguous, which is the MFMA operand layout itself (8 consecutive
+// k of one column per lane), so no LDS staging or transposition is needed:
+// every lane loads its W and X fragments straight into registers, SN_DEPTH
+// 32-deep steps ahead of use, and W is read exactly once.
+//
+// Workgroup (tile, split) owns 64 columns (4 blocks of 16) and one K-chunk
+// whose four quarters go to the four waves.  The waves' sums are added in LDS
+// in wave order; with K split over workgroups, wave 0 of each stores its
+// partial and the last workgroup of the tile adds them in split order (the
+// streaming kernel's device-coherent exchange).  Columns at or past N read
+// row N-1 and rows of X at or past M read row M-1 (never stored); fragments
+// at or past K are read from the last 16-byte piece that holds k = K-1 and
+// zeroed element by element.  W and X need 16-byte aligned bases and
+// pitches of 8 elements; Y, bias and R may sit anywhere.
+namespace {
+
+constexpr int SN_NT = 256, SN_BN = 64, SN_NJ = 4, SN_DEPTH = 6;
+constexpr int SN_ROUND = 4 * 128; // K-chunks are multiples of 4 waves x 128
+
+// Zero the elements at or past `valid` (0..8) of 8 packed 16-bit values.
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
+{
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = 2 * q + 1 < valid ? v[q] : (2 * q < valid ? (v[q] & 0xFFFFu) : 0u);
+    return o;
+}
+
+} // namespace
+
+template <int DT, int ACT, int MB>
+__global__ __launch_bounds__(SN_NT, 2) void gemm_skinny_nk_kernel(GemmArgs p, int n_tiles,
+                                                                  int k_chunk, int splits,
+                                                                  float *ws, int *counters)
+{
+    static_assert(MB == 1 || MB == 2, "up to 32 rows");
+    constexpr int PV = MB * SN_NJ; // accumulator vectors per lane
+    __shared__ f32x4 red[3][PV][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int split = blockIdx.x / n_tiles;
+    const int tile_n = blockIdx.x - split * n_tiles;
+    const int n0 = tile_n * SN_BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int kq = k_chunk / 4;
+    const int kw0 = split * k_chunk + wave * kq;
+    const int kw1 = min(K, kw0 + kq);
+    const int steps = kw1 > kw0 ? (kw1 - kw0 + 31) / 32 : 0;
+    const int g = lane >> 4;
+    const int klast = ((K - 1) >> 3) << 3; // first k of the last piece holding k = K-1
+
+    const unsigned short *wrow[SN_NJ];
+#pragma unroll
+    for (int j = 0; j < SN_NJ; ++j)
+        wrow[j] = p.B[0] + (int64_t)min(n0 + 16 * j + (lane & 15), N - 1) * p.ldb;
+    const unsigned short *xrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        xrow[mb] = p.A + (int64_t)min(16 * mb + (lane & 15), M - 1) * p.lda;
+
+    u32x4 wf[SN_DEPTH][SN_NJ], xf[SN_DEPTH][MB];
+    // step i: k = kw0 + 32 i + 8 (lane / 16); a step that K cuts reads the
+    // pieces at or past K from the last one (masked at use)
+    auto load = [&](int i, auto dslot) {
+        constexpr int D = decltype(dslot)::value;
+        int k = kw0 + 32 * i + 8 * g;
+        if (kw0 + 32 * (i + 1) > K)
+            k = min(k, klast);
+#pragma unroll
+        for (int j = 0; j < SN_NJ; ++j)
+            wf[D][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            xf[D][mb] = *reinterpret_cast<const u32x4 *>(xrow[mb] + k);
+    };
+
+    f32x4 acc[MB][SN_NJ];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < SN_NJ; ++j)
+            acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (steps > 0) {
+        static_for<0, SN_DEPTH>([&](auto d) { load(min((int)decltype(d)::value, steps - 1), d); });
+        for (int i0 = 0; i0 < steps; i0 += SN_DEPTH) {
+            static_for<0, SN_DEPTH>([&](auto d) {
+                constexpr int D = decltype(d)::value;
+                const int i = i0 + D;
+                if (i < steps) {
+                    u32x4 w[SN_NJ], x[MB];
+#pragma unroll
+                    for (int j = 0; j < SN_NJ; ++j)
+                        w[j] = wf[D][j];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        x[mb] = xf[D][mb];
+                    if (kw0 + 32 * (i + 1) > K) {
+                        const int valid = K - (kw0 + 32 * i + 8 * g);
+#pragma unroll
+                        for (int j = 0; j < SN_NJ; ++j)
+                            w[j] = keep_first(w[j], valid);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            x[mb] = keep_first(x[mb], valid);
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int j = 0; j < SN_NJ; ++j)
+                            acc[mb][j] = mfma16x16x32<DT>(w[j], x[mb], acc[mb][j]);
+                }
+                // refill the slot (clamped past the end: repeats the last step)
+                load(min(i + SN_DEPTH, steps - 1), d);
+            });
+        }
+    }
+
+    // waves 1..3 hand their sums to wave 0, which adds them in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < SN_NJ; ++j)
+                red[wave - 1][mb * SN_NJ + j][lane] = acc[mb][j];
+    }
+    __syncthreads();
+    if (wave > 0)
+        return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < SN_NJ; ++j)
+                acc[mb][j] += red[w][mb * SN_NJ + j][lane];
+
+    // Lane l holds Y[m = 16 mb + l % 16][n = n0 + 16 j + 4 (l / 16) + r] in
+    // acc[mb][j][r]; element-wise stores.
+    auto store_rows = [&](const f32x4 (&val)[MB][SN_NJ]) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + (lane & 15);
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < SN_NJ; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = n0 + 16 * j + 4 * g + r;
+                    if (n >= N)
+                        continue;
+                    float x = val[mb][j][r];
+                    if (p.bias != nullptr)
+                        x += from_bits<DT>(p.bias[n]);
+                    x = activate<ACT>(x);
+                    if (p.R != nullptr)
+                        x += from_bits<DT>(p.R[(int64_t)m * p.ldr + n]);
+                    p.C[0][(int64_t)m * p.ldc + n] = to_bits<DT>(x);
+                }
+            }
+        }
+    };
+    if (splits == 1) {
+        store_rows(acc);
+        return;
+    }
+
+    // K split over workgroups: this one's partial (PV KiB, 1 KiB per vector
+    // over the wave), then the arrival count; the last one adds every split
+    // in order 0..splits-1.
+    constexpr int BLOCK = PV * 256; // floats per workgroup partial
+    float *ws_tile = ws + (int64_t)tile_n * splits * BLOCK;
+    {
+        f32x4 v[PV];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < SN_NJ; ++j)
+                v[mb * SN_NJ + j] = acc[mb][j];
+        store_partial<PV>(ws_tile + split * BLOCK + lane * 4, v); // stores and waits
+    }
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != splits - 1)
+        return;
+
+    constexpr int RS = 16 / PV; // splits read back per round: 16 loads
+    f32x4 sum[MB][SN_NJ];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < SN_NJ; ++j)
+            sum[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
+        f32x4 v[16];
+#pragma unroll
+        for (int q = 0; q < RS; ++q) {
+            const float *src = ws_tile + min(sp0 + q, splits - 1) * BLOCK + lane * 4;
+#pragma unroll
+            for (int t = 0; t < PV; ++t)
+                asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                             : "=v"(v[q * PV + t])
+                             : "v"(src + t * 256)
+                             : "memory");
+        }
+        // the loads above are invisible to the compiler's wait tracking: wait
+        // here and pass every value through, so nothing reads one earlier
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                       "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                     :
+                     : "memory");
+#pragma unroll
+        for (int q = 0; q < RS; ++q)
+            if (sp0 + q < splits)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < SN_NJ; ++j)
+                        sum[mb][j] += v[q * PV + mb * SN_NJ + j];
+    }
+    store_rows(sum);
+    if (lane == 0)
+        __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+SkinnyPlan plan_skinny_nk(int M, int N, int K)
+{
+    SkinnyPlan pl;
+    pl.streaming = 4;
+    pl.mb = M > 16 ? 2 : 1;
+    pl.bn = SN_BN;
+    pl.n_tiles = (N + SN_BN - 1) / SN_BN;
+    // up to two workgroups per CU resident at once: K split so the units
+    // fill them, in chunks of whole 128-deep quarter rounds
+    const int quanta = (K + SN_ROUND - 1) / SN_ROUND;
+    int splits = 512 / pl.n_tiles;
+    const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
+    if (force && atoi(force) > 0)
+        splits = atoi(force);
+    splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
+    const int per = (quanta + splits - 1) / splits;
+    pl.k_chunk = per * SN_ROUND;
+    pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
+    return pl;
+}
+
+SkinnyPlan plan_skinny_realign(int M, int N, int K)
+{
+    SkinnyPlan pl;
+    pl.streaming = 3;
+    pl.mb = M > 16 ? 2 : 1;
+    pl.bn = SR_BN;
+    pl.n_tiles = (N + SR_BN - 1) / SR_BN;
+    // up to two workgroups per CU (512 on 256 CUs) resident at once: K split
+    // so the units fill them, in chunks of whole pipeline rounds
+    constexpr int round = SR_STAGES * SR_BK;
+    const int quanta = (K + round - 1) / round;
+    int splits = 512 / pl.n_tiles;
+    const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
+    if (force && atoi(force) > 0)
+        splits = atoi(force);
+    splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
+    const int per = (quanta + splits - 1) / splits;
+    pl.k_chunk = per * round;
+    pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
+    return pl;
+}
+
 SkinnyPlan plan_skinny(int M, int N, int K)
 {
     SkinnyPlan pl;
@@ -896,6 +1495,10 @@ size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N)
     (void)M;
     if (pl.splits <= 1)
         return 0;
+    if (pl.streaming == 3)
+        return (size_t)pl.splits * 16 * (size_t)pl.mb * 128 * (size_t)pl.n_tiles;
+    if (pl.streaming == 4)
+        return (size_t)pl.splits * 16 * (size_t)pl.mb * SN_BN * (size_t)pl.n_tiles;
     return pl.streaming ? (size_t)pl.splits * 16 * (size_t)pl.mb * (size_t)N
                         : (size_t)pl.splits * 16 * (size_t)pl.n_tiles * SK_BN;
 }
@@ -920,6 +1523,58 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
                 TG_SC(DT_BF16, ACT_NONE);
         }
 #undef TG_SC
+        return hipGetLastError();
+    }
+    if (pl.streaming == 4) {
+#define TG_SN(DT_, ACT_, MB_)                                                                    \
+    hipLaunchKernelGGL((gemm_skinny_nk_kernel<DT_, ACT_, MB_>), grid, dim3(SN_NT), 0, s, a,      \
+                       pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
+#define TG_SN_MB(DT_, ACT_)                                                                      \
+    do {                                                                                         \
+        if (pl.mb == 2)                                                                          \
+            TG_SN(DT_, ACT_, 2);                                                                 \
+        else                                                                                     \
+            TG_SN(DT_, ACT_, 1);                                                                 \
+    } while (0)
+        if (dt == DT_F16) {
+            if (act == ACT_GELU)
+                TG_SN_MB(DT_F16, ACT_GELU);
+            else
+                TG_SN_MB(DT_F16, ACT_NONE);
+        } else {
+            if (act == ACT_GELU)
+                TG_SN_MB(DT_BF16, ACT_GELU);
+            else
+                TG_SN_MB(DT_BF16, ACT_NONE);
+        }
+#undef TG_SN_MB
+#undef TG_SN
+        return hipGetLastError();
+    }
+    if (pl.streaming == 3) {
+#define TG_SR(DT_, ACT_, MB_)                                                                    \
+    hipLaunchKernelGGL((gemm_skinny_realign_kernel<DT_, ACT_, MB_>), grid, dim3(SR_NT), 0, s, a, \
+                       pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
+#define TG_SR_MB(DT_, ACT_)                                                                      \
+    do {                                                                                         \
+        if (pl.mb == 2)                                                                          \
+            TG_SR(DT_, ACT_, 2);                                                                 \
+        else                                                                                     \
+            TG_SR(DT_, ACT_, 1);                                                                 \
+    } while (0)
+        if (dt == DT_F16) {
+            if (act == ACT_GELU)
+                TG_SR_MB(DT_F16, ACT_GELU);
+            else
+                TG_SR_MB(DT_F16, ACT_NONE);
+        } else {
+            if (act == ACT_GELU)
+                TG_SR_MB(DT_BF16, ACT_GELU);
+            else
+                TG_SR_MB(DT_BF16, ACT_NONE);
+        }
+#undef TG_SR_MB
+#undef TG_SR
         return hipGetLastError();
     }
     if (pl.streaming == 1) {

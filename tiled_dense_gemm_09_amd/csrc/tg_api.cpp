@@ -614,7 +614,85 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             }
         }
     }
-    if (sk_cfg >= 0) {
+    // Small M (n_mat 1, M <= 32, N and K of at least 256; the bounds keep K
+    // and its roundings inside int):
+    //  - B [K,N] with W (or Y) off the 16-byte grid: the realigning streaming
+    //    kernel, which reads W through aligned 16-byte pieces.  Aligned shapes
+    //    that the split-K streaming kernel cannot take (N or K off its
+    //    multiples) run on it as well: it measured faster than the
+    //    register-staged kernel, which TG_SKINNY_REGS=1 selects (M <= 16).
+    //  - B stored [N,K], 16-byte aligned with a pitch of 8 elements: the
+    //    register-streaming kernel that loads MFMA fragments straight from W.
+    // X is copied into the workspace (zero-padded to the kernel's K
+    // granule) when it is off the grid or the realigning kernel's K is not a
+    // multiple of 64; the split-K partials need the workspace too, and
+    // without one the call runs unsplit (or, when X must be copied, on the
+    // kernels below).
+    const bool unforced = !(force && *force);
+    const bool small_m = n_mat == 1 && M <= 32 && K >= 256 && K < kMaxDim - 1024 && N >= 256 &&
+                         even;
+    const bool force_realign = force && strcmp(force, "skinny_realign") == 0;
+    const bool force_nk = force && strcmp(force, "skinny_nk") == 0;
+    const bool nk = small_m && b_trans && aligned16(B[0]) && ldb % 8 == 0 &&
+                    (force_nk || unforced);
+    const bool realign = small_m && !b_trans &&
+                         (force_realign || (unforced && !fast) ||
+                          (unforced && fast && env_int("TG_SKINNY_REGS", 0) != 1 &&
+                           tg::plan_skinny(a.M, a.N, a.K).streaming <= 0));
+    bool small_run = nk || realign;
+    tg::SkinnyPlan rpl{};
+    float *r_ws = nullptr;
+    int *r_counters = nullptr;
+    unsigned short *r_x = nullptr;
+    const int64_t r_kx = nk ? (K + 7) / 8 * 8 : (K + 63) / 64 * 64; // columns of a copied X
+    if (small_run) {
+        rpl = nk ? tg::plan_skinny_nk(a.M, a.N, a.K) : tg::plan_skinny_realign(a.M, a.N, a.K);
+        if (rpl.n_tiles > (int)(kCounterBytes / sizeof(int)))
+            rpl.splits = 1;
+        const bool x_ok = aligned16(A) && lda % 8 == 0 && (nk || K % 64 == 0);
+        // floats: the partials (a multiple of 4, so X stays 16-byte aligned), then X
+        const size_t p_floats =
+            rpl.splits > 1 ? (tg::skinny_ws_floats(rpl, a.M, a.N) + 3) / 4 * 4 : 0;
+        const size_t x_floats = x_ok ? 0 : (size_t)((M * r_kx + 1) / 2 + 4);
+        void *base = nullptr;
+        if (p_floats + x_floats > 0) {
+            tg_status st = TG_SUCCESS;
+            base = split_workspace(p_floats + x_floats, &st);
+            if (!base && x_ok && p_floats > 0) // unsplit: no workspace at all
+                rpl.splits = 1;
+        }
+        if (rpl.splits == 1) {
+            const int64_t round = nk ? 512 : 256; // the kernels' K-chunk granules
+            rpl.k_chunk = (int)((K + round - 1) / round * round);
+        }
+        if (!x_ok && !base) {
+            small_run = false;
+            if (!stg_note)
+                stg_note = " (X not copied: no workspace)";
+        } else if (base) {
+            r_counters = static_cast<int *>(base);
+            r_ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
+            if (!x_ok)
+                r_x = reinterpret_cast<unsigned short *>(r_ws + p_floats);
+            if (rpl.splits == 1)
+                r_ws = nullptr;
+        }
+    }
+    if (small_run) {
+        tg::GemmArgs a2 = a;
+        err = hipSuccess;
+        if (r_x) {
+            err = tg::launch_pad_copy(a.A, a.lda, a.M, a.K, r_x, a.M, (int)r_kx, s);
+            a2.A = r_x;
+            a2.lda = r_kx;
+        }
+        if (err == hipSuccess)
+            err = tg::launch_skinny(kdt, kact, a2, rpl, r_ws, r_counters, s);
+        char detail[64];
+        snprintf(detail, sizeof detail, "_%s_bn%d_split%dx%d%s%s", nk ? "nk" : "realign", rpl.bn,
+                 rpl.splits, rpl.k_chunk, rpl.mb == 2 ? "_m32" : "", r_x ? "_xstaged" : "");
+        set_last("skinny", detail);
+    } else if (sk_cfg >= 0) {
         const int group_m = env_int("TG_GROUP_M", 4);
         err = tg::launch_async_sk(sk_cfg, kdt, kact, a, group_m > 0 ? group_m : 4, sk,
                                   reinterpret_cast<float *>(static_cast<char *>(sk_base) +

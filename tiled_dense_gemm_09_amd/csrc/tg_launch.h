@@ -160,7 +160,7 @@ hipError_t launch_unpad_copy(const unsigned short *src, int src_pitch, unsigned 
 // zero.  M <= 16 has every kernel below; 16 < M <= 32 only the split-K
 // streaming kernel (streaming = -1 when the shape does not fit it).
 struct SkinnyPlan {
-    int streaming; // 2: column-tile kernel, 1: split-K streaming kernel, 0: register-staged kernel, -1: none
+    int streaming; // 4: B [N,K] kernel, 3: realigning kernel, 2: column-tile kernel, 1: split-K streaming kernel, 0: register-staged kernel, -1: none
     int mb;       // 16-row blocks (1: M <= 16, 2: M <= 32)
     int bn;       // columns per workgroup
     int splits;   // K splits
@@ -168,6 +168,13 @@ struct SkinnyPlan {
     int n_tiles;  // ceil(N / bn)
 };
 SkinnyPlan plan_skinny(int M, int N, int K);
+// The realigning small-M kernel (streaming = 3): W at any 2-byte alignment
+// and pitch, X 16-byte aligned with a pitch of 8 elements and readable (zero
+// past K) up to K rounded up to 64 columns; Y, bias and R anywhere.
+SkinnyPlan plan_skinny_realign(int M, int N, int K);
+// The small-M kernel for B stored [N,K] (streaming = 4): W and X with 16-byte
+// aligned bases and pitches of 8 elements; Y, bias and R anywhere.
+SkinnyPlan plan_skinny_nk(int M, int N, int K);
 size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N);
 hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &pl, float *ws,
                          int *counters, hipStream_t stream);
