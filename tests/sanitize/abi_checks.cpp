@@ -78,8 +78,8 @@ hipError_t launch_unpad_copy(const unsigned short *, int, unsigned short *, int6
     reached("launch_unpad_copy");
 }
 SkinnyPlan plan_skinny(int, int, int) { reached("plan_skinny"); }
-SkinnyPlan plan_skinny_realign(int, int, int) { reached("plan_skinny_realign"); }
-SkinnyPlan plan_skinny_nk(int, int, int) { reached("plan_skinny_nk"); }
+SkinnyPlan plan_skinny_realign(int, int, int, int) { reached("plan_skinny_realign"); }
+SkinnyPlan plan_skinny_nk(int, int, int, int) { reached("plan_skinny_nk"); }
 size_t skinny_ws_floats(const SkinnyPlan &, int, int) { reached("skinny_ws_floats"); }
 hipError_t launch_skinny(int, int, const GemmArgs &, const SkinnyPlan &, float *, int *, hipStream_t)
 {

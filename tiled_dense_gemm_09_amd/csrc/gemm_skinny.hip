@@ -842,6 +842,17 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
 // readable values) up to K rounded up to 64; rows of W at or past K read as
 // zero.  Split-K partials are combined as in the streaming kernel: in split
 // order by the last workgroup of each tile.
+//
+// BT: B stored [N,K] (a linear layer's weight W[n][k], 16-byte aligned with
+// a pitch of 8 elements).  Each row of W is then K-contiguous, the MFMA
+// operand layout itself, and the tile keeps 128 columns: a slab is W [128
+// rows n][64 k], copied 8 rows of 128 bytes (whole cache lines) per copy,
+// granule c of row r at c ^ (r & 7) as for X, and each fragment is one
+// 16-byte LDS read.  (Loading the fragments straight into registers reads
+// 64 bytes of 16 different rows per load, half of each line, and measured
+// 40 % slower.)  Rows at or past N read row N-1 (never stored); pieces at
+// or past K read the last piece holding k = K-1 and are zeroed element by
+// element.
 namespace {
 
 constexpr int SR_BN = 120; // columns stored per workgroup
@@ -851,6 +862,16 @@ constexpr int SR_W_BYTES = SR_BK * SR_ROW_BYTES;          // 16 KiB
 constexpr int SR_STAGE_BYTES = SR_W_BYTES + 2 * SA_X_BYTES;
 constexpr int SR_COPIES = 5;                              // per wave per slab: 4 of W, 1 of X
 
+// Zero the elements at or past `valid` of 8 packed 16-bit values.
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
+{
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = 2 * q + 1 < valid ? v[q] : (2 * q < valid ? (v[q] & 0xFFFFu) : 0u);
+    return o;
+}
+
 // Byte offset of element e (0 <= e < 136) of slab row r's run in a stage.
 __host__ __device__ constexpr int sr_off(int r, int e)
 {
@@ -859,12 +880,13 @@ __host__ __device__ constexpr int sr_off(int r, int e)
 
 } // namespace
 
-template <int DT, int ACT, int MB>
-__global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs p, int n_tiles,
-                                                                       int k_chunk, int splits,
-                                                                       float *ws, int *counters)
+template <int DT, int ACT, int MB, bool BT>
+__global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_pieces_kernel(GemmArgs p, int n_tiles,
+                                                                      int k_chunk, int splits,
+                                                                      float *ws, int *counters)
 {
     static_assert(MB == 1 || MB == 2, "up to 32 rows");
+    constexpr int TBN = BT ? 128 : SR_BN; // columns stored per workgroup
     __shared__ __attribute__((aligned(1024))) unsigned char st[SR_STAGES][SR_STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -878,32 +900,44 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
     const int u = xcd * uq + (xcd < ur ? xcd : ur) + slot;
     const int split = u / n_tiles;
     const int tile_n = u - split * n_tiles;
-    const int n0 = tile_n * SR_BN;
+    const int n0 = tile_n * TBN;
     const int M = p.M, N = p.N, K = p.K;
     const int kbeg = split * k_chunk;
     const int slabs = (min(K, kbeg + k_chunk) - kbeg + SR_BK - 1) / SR_BK;
     const int64_t ldb = p.ldb;
+    const int klast = ((K - 1) >> 3) << 3; // first k of the last piece holding k = K-1
 
     // W in 16-byte pieces counted from the aligned address at or below its base
     const uintptr_t wb = (uintptr_t)p.B[0];
     const unsigned char *wal = (const unsigned char *)(wb & ~(uintptr_t)15);
     const int64_t w0 = (int64_t)((wb & 15) >> 1);
 
-    // W copy c of this wave: slab row r = 4 (4 wave + c) + lane / 16, stage
-    // position lane % 16, which holds piece (lane % 16 - 4 ((r >> 3) & 3)) mod
-    // 16 of the row's run, clamped to the row's last piece with a column < N
+    // [K,N]: W copy c of this wave is slab row r = 4 (4 wave + c) + lane / 16,
+    // stage position lane % 16, which holds piece (lane % 16 - 4 ((r >> 3) &
+    // 3)) mod 16 of the row's run, clamped to the row's last piece with a
+    // column < N.  [N,K]: slab row (column n0 + r) r = 8 (4 wave + c) + lane /
+    // 8, stage position lane % 8, which holds granule (lane % 8) ^ (r & 7);
+    // wr[c] is then that granule's first k in slab 0.
     const unsigned char *gw[4];
     int wr[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int r = 4 * (wave * 4 + c) + (lane >> 4);
-        const int64_t e = w0 + (int64_t)(kbeg + r) * ldb; // row start, in elements
-        const int64_t first = (e + n0) >> 3, last = (e + N - 1) >> 3;
-        const int64_t j = ((lane & 15) - 4 * ((r >> 3) & 3)) & 15;
-        gw[c] = wal + 16 * (first + j < last ? first + j : last);
-        wr[c] = r;
+        if constexpr (BT) {
+            const int r = 8 * (wave * 4 + c) + (lane >> 3);
+            const int k = kbeg + 8 * ((lane & 7) ^ (r & 7));
+            gw[c] = reinterpret_cast<const unsigned char *>(p.B[0] +
+                                                            (int64_t)min(n0 + r, N - 1) * ldb + k);
+            wr[c] = k;
+        } else {
+            const int r = 4 * (wave * 4 + c) + (lane >> 4);
+            const int64_t e = w0 + (int64_t)(kbeg + r) * ldb; // row start, in elements
+            const int64_t first = (e + n0) >> 3, last = (e + N - 1) >> 3;
+            const int64_t j = ((lane & 15) - 4 * ((r >> 3) & 3)) & 15;
+            gw[c] = wal + 16 * (first + j < last ? first + j : last);
+            wr[c] = r;
+        }
     }
-    const int64_t w_step = 2 * (int64_t)SR_BK * ldb; // bytes per slab
+    const int64_t w_step = BT ? 2 * SR_BK : 2 * (int64_t)SR_BK * ldb; // bytes per slab
     // X copy: rows 8 w + lane/8 for MB = 2, rows 8 (w & 1) + lane/8 for MB = 1
     // (waves 2 and 3 write the duplicate), clamped to M-1, granule (lane%8) ^ (row & 7)
     const int xr = 8 * (MB == 2 ? wave : (wave & 1)) + (lane >> 3);
@@ -914,12 +948,19 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)stage;
         if (c < 4) {
             const unsigned char *src = gw[c] + s * w_step;
-            // a row k at or past K copies row k - 8d (d = ceil((k - K + 1) / 8)),
-            // whose run has the same offset; its values are masked at the read
             if (kbeg + (s + 1) * SR_BK > K) {
-                const int k = kbeg + s * SR_BK + wr[c];
-                if (k >= K)
-                    src -= (int64_t)16 * ldb * ((k - K + 8) >> 3);
+                if constexpr (BT) {
+                    // a granule at or past K reads the last one (masked at the read)
+                    const int k = wr[c] + s * SR_BK;
+                    if (k > klast)
+                        src -= 2 * (k - klast);
+                } else {
+                    // a row k at or past K copies row k - 8d (d = ceil((k - K + 1)
+                    // / 8)), whose run has the same offset; masked at the read
+                    const int k = kbeg + s * SR_BK + wr[c];
+                    if (k >= K)
+                        src -= (int64_t)16 * ldb * ((k - K + 8) >> 3);
+                }
             }
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src),
                          "{m0}"(lds + (wave * 4 + c) * 1024)
@@ -935,15 +976,27 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
     // 32 wave + 16 j + l % 16 at k = 32 kk + 8 (l / 16) + t, t = 0..7; row
     // 8 (l / 16) + t has offset o(t) = (w0 + t ldb) mod 8 (the same for every
     // lane), and half kk = 1 lies 32 rows (8 KiB) further on.
+    // [N,K]: the fragment of block j, half kk is the 16 bytes of slab row
+    // 32 wave + 16 j + l % 16 at granule 4 kk + l / 16 (w_off[j][kk]).
     int w_off[SR_NJ][8];
     {
         const int g = lane >> 4;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int o = (int)((w0 + t * (ldb & 7)) & 7);
+        if constexpr (BT) {
 #pragma unroll
             for (int j = 0; j < SR_NJ; ++j)
-                w_off[j][t] = sr_off(8 * g + t, o + 32 * wave + 16 * j + (lane & 15));
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int r = 32 * wave + 16 * j + (lane & 15);
+                    w_off[j][kk] = r * 128 + (((4 * kk + g) ^ (r & 7)) * 16);
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int o = (int)((w0 + t * (ldb & 7)) & 7);
+#pragma unroll
+                for (int j = 0; j < SR_NJ; ++j)
+                    w_off[j][t] = sr_off(8 * g + t, o + 32 * wave + 16 * j + (lane & 15));
+            }
         }
     }
     int x_off[MB][2];
@@ -972,19 +1025,26 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
                 xf[mb] = *reinterpret_cast<const u32x4 *>(stage + x_off[mb][kk]);
 #pragma unroll
             for (int j = 0; j < SR_NJ; ++j) {
-                unsigned v[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    v[t] = *reinterpret_cast<const unsigned short *>(stage + kk * 32 * SR_ROW_BYTES +
-                                                                     w_off[j][t]);
-                if (kmax < SR_BK) {
-                    const int r0 = 32 * kk + 8 * (lane >> 4);
+                u32x4 wf;
+                if constexpr (BT) {
+                    wf = *reinterpret_cast<const u32x4 *>(stage + w_off[j][kk]);
+                    if (kmax < SR_BK)
+                        wf = keep_first(wf, kmax - 32 * kk - 8 * (lane >> 4));
+                } else {
+                    unsigned v[8];
 #pragma unroll
                     for (int t = 0; t < 8; ++t)
-                        v[t] = r0 + t < kmax ? v[t] : 0u;
+                        v[t] = *reinterpret_cast<const unsigned short *>(
+                            stage + kk * 32 * SR_ROW_BYTES + w_off[j][t]);
+                    if (kmax < SR_BK) {
+                        const int r0 = 32 * kk + 8 * (lane >> 4);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            v[t] = r0 + t < kmax ? v[t] : 0u;
+                    }
+                    wf = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                               v[6] | (v[7] << 16)};
                 }
-                const u32x4 wf = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                                  v[6] | (v[7] << 16)};
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][j] = mfma16x16x32<DT>(wf, xf[mb], acc[mb][j]);
@@ -1022,7 +1082,7 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
     // Lane l holds Y[m = 16 mb + l % 16][n = n0 + 32 w + 16 j + 4 (l / 16) + r]
     // in acc[mb][j][r]; element-wise stores (Y, bias and R may sit anywhere).
     auto store_rows = [&](const f32x4 (&val)[MB][SR_NJ]) {
-        const int nmax = min(N - n0, SR_BN);
+        const int nmax = min(N - n0, TBN);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = 16 * mb + (lane & 15);
@@ -1131,283 +1191,44 @@ __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_realign_kernel(GemmArgs 
         __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// Small M with B stored [N,K] (a linear layer's weight W[n][k]): each row of
-// W is K-contiguous, which is the MFMA operand layout itself (8 consecutive
-// k of one column per lane), so no LDS staging or transposition is needed:
-// every lane loads its W and X fragments straight into registers, SN_DEPTH
-// 32-deep steps ahead of use, and W is read exactly once.
-//
-// Workgroup (tile, split) owns 64 columns (4 blocks of 16) and one K-chunk
-// whose four quarters go to the four waves.  The waves' sums are added in LDS
-// in wave order; with K split over workgroups, wave 0 of each stores its
-// partial and the last workgroup of the tile adds them in split order (the
-// streaming kernel's device-coherent exchange).  Columns at or past N read
-// row N-1 and rows of X at or past M read row M-1 (never stored); fragments
-// at or past K are read from the last 16-byte piece that holds k = K-1 and
-// zeroed element by element.  W and X need 16-byte aligned bases and
-// pitches of 8 elements; Y, bias and R may sit anywhere.
 namespace {
 
-constexpr int SN_NT = 256, SN_BN = 64, SN_NJ = 4, SN_DEPTH = 6;
-constexpr int SN_ROUND = 4 * 128; // K-chunks are multiples of 4 waves x 128
-
-// Zero the elements at or past `valid` (0..8) of 8 packed 16-bit values.
-__device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
-{
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        o[q] = 2 * q + 1 < valid ? v[q] : (2 * q < valid ? (v[q] & 0xFFFFu) : 0u);
-    return o;
-}
-
-} // namespace
-
-template <int DT, int ACT, int MB>
-__global__ __launch_bounds__(SN_NT, 2) void gemm_skinny_nk_kernel(GemmArgs p, int n_tiles,
-                                                                  int k_chunk, int splits,
-                                                                  float *ws, int *counters)
-{
-    static_assert(MB == 1 || MB == 2, "up to 32 rows");
-    constexpr int PV = MB * SN_NJ; // accumulator vectors per lane
-    __shared__ f32x4 red[3][PV][64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int split = blockIdx.x / n_tiles;
-    const int tile_n = blockIdx.x - split * n_tiles;
-    const int n0 = tile_n * SN_BN;
-    const int M = p.M, N = p.N, K = p.K;
-    const int kq = k_chunk / 4;
-    const int kw0 = split * k_chunk + wave * kq;
-    const int kw1 = min(K, kw0 + kq);
-    const int steps = kw1 > kw0 ? (kw1 - kw0 + 31) / 32 : 0;
-    const int g = lane >> 4;
-    const int klast = ((K - 1) >> 3) << 3; // first k of the last piece holding k = K-1
-
-    const unsigned short *wrow[SN_NJ];
-#pragma unroll
-    for (int j = 0; j < SN_NJ; ++j)
-        wrow[j] = p.B[0] + (int64_t)min(n0 + 16 * j + (lane & 15), N - 1) * p.ldb;
-    const unsigned short *xrow[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        xrow[mb] = p.A + (int64_t)min(16 * mb + (lane & 15), M - 1) * p.lda;
-
-    u32x4 wf[SN_DEPTH][SN_NJ], xf[SN_DEPTH][MB];
-    // step i: k = kw0 + 32 i + 8 (lane / 16); a step that K cuts reads the
-    // pieces at or past K from the last one (masked at use)
-    auto load = [&](int i, auto dslot) {
-        constexpr int D = decltype(dslot)::value;
-        int k = kw0 + 32 * i + 8 * g;
-        if (kw0 + 32 * (i + 1) > K)
-            k = min(k, klast);
-#pragma unroll
-        for (int j = 0; j < SN_NJ; ++j)
-            wf[D][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + k);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            xf[D][mb] = *reinterpret_cast<const u32x4 *>(xrow[mb] + k);
-    };
-
-    f32x4 acc[MB][SN_NJ];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < SN_NJ; ++j)
-            acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (steps > 0) {
-        static_for<0, SN_DEPTH>([&](auto d) { load(min((int)decltype(d)::value, steps - 1), d); });
-        for (int i0 = 0; i0 < steps; i0 += SN_DEPTH) {
-            static_for<0, SN_DEPTH>([&](auto d) {
-                constexpr int D = decltype(d)::value;
-                const int i = i0 + D;
-                if (i < steps) {
-                    u32x4 w[SN_NJ], x[MB];
-#pragma unroll
-                    for (int j = 0; j < SN_NJ; ++j)
-                        w[j] = wf[D][j];
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        x[mb] = xf[D][mb];
-                    if (kw0 + 32 * (i + 1) > K) {
-                        const int valid = K - (kw0 + 32 * i + 8 * g);
-#pragma unroll
-                        for (int j = 0; j < SN_NJ; ++j)
-                            w[j] = keep_first(w[j], valid);
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            x[mb] = keep_first(x[mb], valid);
-                    }
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                        for (int j = 0; j < SN_NJ; ++j)
-                            acc[mb][j] = mfma16x16x32<DT>(w[j], x[mb], acc[mb][j]);
-                }
-                // refill the slot (clamped past the end: repeats the last step)
-                load(min(i + SN_DEPTH, steps - 1), d);
-            });
-        }
-    }
-
-    // waves 1..3 hand their sums to wave 0, which adds them in wave order
-    if (wave > 0) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int j = 0; j < SN_NJ; ++j)
-                red[wave - 1][mb * SN_NJ + j][lane] = acc[mb][j];
-    }
-    __syncthreads();
-    if (wave > 0)
-        return;
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int j = 0; j < SN_NJ; ++j)
-                acc[mb][j] += red[w][mb * SN_NJ + j][lane];
-
-    // Lane l holds Y[m = 16 mb + l % 16][n = n0 + 16 j + 4 (l / 16) + r] in
-    // acc[mb][j][r]; element-wise stores.
-    auto store_rows = [&](const f32x4 (&val)[MB][SN_NJ]) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int m = 16 * mb + (lane & 15);
-            if (m >= M)
-                continue;
-#pragma unroll
-            for (int j = 0; j < SN_NJ; ++j) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = n0 + 16 * j + 4 * g + r;
-                    if (n >= N)
-                        continue;
-                    float x = val[mb][j][r];
-                    if (p.bias != nullptr)
-                        x += from_bits<DT>(p.bias[n]);
-                    x = activate<ACT>(x);
-                    if (p.R != nullptr)
-                        x += from_bits<DT>(p.R[(int64_t)m * p.ldr + n]);
-                    p.C[0][(int64_t)m * p.ldc + n] = to_bits<DT>(x);
-                }
-            }
-        }
-    };
-    if (splits == 1) {
-        store_rows(acc);
-        return;
-    }
-
-    // K split over workgroups: this one's partial (PV KiB, 1 KiB per vector
-    // over the wave), then the arrival count; the last one adds every split
-    // in order 0..splits-1.
-    constexpr int BLOCK = PV * 256; // floats per workgroup partial
-    float *ws_tile = ws + (int64_t)tile_n * splits * BLOCK;
-    {
-        f32x4 v[PV];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int j = 0; j < SN_NJ; ++j)
-                v[mb * SN_NJ + j] = acc[mb][j];
-        store_partial<PV>(ws_tile + split * BLOCK + lane * 4, v); // stores and waits
-    }
-    int old = 0;
-    if (lane == 0)
-        old = __hip_atomic_fetch_add(&counters[tile_n], 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != splits - 1)
-        return;
-
-    constexpr int RS = 16 / PV; // splits read back per round: 16 loads
-    f32x4 sum[MB][SN_NJ];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < SN_NJ; ++j)
-            sum[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
-        f32x4 v[16];
-#pragma unroll
-        for (int q = 0; q < RS; ++q) {
-            const float *src = ws_tile + min(sp0 + q, splits - 1) * BLOCK + lane * 4;
-#pragma unroll
-            for (int t = 0; t < PV; ++t)
-                asm volatile("global_load_dwordx4 %0, %1, off sc1"
-                             : "=v"(v[q * PV + t])
-                             : "v"(src + t * 256)
-                             : "memory");
-        }
-        // the loads above are invisible to the compiler's wait tracking: wait
-        // here and pass every value through, so nothing reads one earlier
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
-                       "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
-                       "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
-                     :
-                     : "memory");
-#pragma unroll
-        for (int q = 0; q < RS; ++q)
-            if (sp0 + q < splits)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int j = 0; j < SN_NJ; ++j)
-                        sum[mb][j] += v[q * PV + mb * SN_NJ + j];
-    }
-    store_rows(sum);
-    if (lane == 0)
-        __hip_atomic_store(&counters[tile_n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-SkinnyPlan plan_skinny_nk(int M, int N, int K)
+// Both layouts of the pieces kernel: up to two workgroups per CU (512 on 256
+// CUs) resident at once, K split so the units fill them, in chunks of whole
+// pipeline rounds; want_splits > 0 (or TG_SKINNY_SPLITS, for sweeps) asks for
+// a count, clamped to the chunks.
+SkinnyPlan plan_pieces(int M, int N, int K, int want_splits, bool bt)
 {
     SkinnyPlan pl;
-    pl.streaming = 4;
+    pl.streaming = bt ? 4 : 3;
     pl.mb = M > 16 ? 2 : 1;
-    pl.bn = SN_BN;
-    pl.n_tiles = (N + SN_BN - 1) / SN_BN;
-    // up to two workgroups per CU resident at once: K split so the units
-    // fill them, in chunks of whole 128-deep quarter rounds
-    const int quanta = (K + SN_ROUND - 1) / SN_ROUND;
-    int splits = 512 / pl.n_tiles;
-    const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
-    if (force && atoi(force) > 0)
-        splits = atoi(force);
-    splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
-    const int per = (quanta + splits - 1) / splits;
-    pl.k_chunk = per * SN_ROUND;
-    pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
-    return pl;
-}
-
-SkinnyPlan plan_skinny_realign(int M, int N, int K)
-{
-    SkinnyPlan pl;
-    pl.streaming = 3;
-    pl.mb = M > 16 ? 2 : 1;
-    pl.bn = SR_BN;
-    pl.n_tiles = (N + SR_BN - 1) / SR_BN;
-    // up to two workgroups per CU (512 on 256 CUs) resident at once: K split
-    // so the units fill them, in chunks of whole pipeline rounds
+    pl.bn = bt ? 128 : SR_BN;
+    pl.n_tiles = (N + pl.bn - 1) / pl.bn;
     constexpr int round = SR_STAGES * SR_BK;
     const int quanta = (K + round - 1) / round;
     int splits = 512 / pl.n_tiles;
-    const char *force = getenv("TG_SKINNY_SPLITS"); // for sweeps
+    const char *force = getenv("TG_SKINNY_SPLITS");
     if (force && atoi(force) > 0)
         splits = atoi(force);
+    if (want_splits > 0)
+        splits = want_splits;
     splits = splits < 1 ? 1 : (splits > quanta ? quanta : splits);
     const int per = (quanta + splits - 1) / splits;
     pl.k_chunk = per * round;
     pl.splits = (K + pl.k_chunk - 1) / pl.k_chunk;
     return pl;
+}
+
+} // namespace
+
+SkinnyPlan plan_skinny_realign(int M, int N, int K, int want_splits)
+{
+    return plan_pieces(M, N, K, want_splits, false);
+}
+
+SkinnyPlan plan_skinny_nk(int M, int N, int K, int want_splits)
+{
+    return plan_pieces(M, N, K, want_splits, true);
 }
 
 SkinnyPlan plan_skinny(int M, int N, int K)
@@ -1495,10 +1316,8 @@ size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N)
     (void)M;
     if (pl.splits <= 1)
         return 0;
-    if (pl.streaming == 3)
+    if (pl.streaming >= 3) // 128 columns computed per workgroup
         return (size_t)pl.splits * 16 * (size_t)pl.mb * 128 * (size_t)pl.n_tiles;
-    if (pl.streaming == 4)
-        return (size_t)pl.splits * 16 * (size_t)pl.mb * SN_BN * (size_t)pl.n_tiles;
     return pl.streaming ? (size_t)pl.splits * 16 * (size_t)pl.mb * (size_t)N
                         : (size_t)pl.splits * 16 * (size_t)pl.n_tiles * SK_BN;
 }
@@ -1525,42 +1344,20 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
 #undef TG_SC
         return hipGetLastError();
     }
-    if (pl.streaming == 4) {
-#define TG_SN(DT_, ACT_, MB_)                                                                    \
-    hipLaunchKernelGGL((gemm_skinny_nk_kernel<DT_, ACT_, MB_>), grid, dim3(SN_NT), 0, s, a,      \
-                       pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
-#define TG_SN_MB(DT_, ACT_)                                                                      \
-    do {                                                                                         \
-        if (pl.mb == 2)                                                                          \
-            TG_SN(DT_, ACT_, 2);                                                                 \
-        else                                                                                     \
-            TG_SN(DT_, ACT_, 1);                                                                 \
-    } while (0)
-        if (dt == DT_F16) {
-            if (act == ACT_GELU)
-                TG_SN_MB(DT_F16, ACT_GELU);
-            else
-                TG_SN_MB(DT_F16, ACT_NONE);
-        } else {
-            if (act == ACT_GELU)
-                TG_SN_MB(DT_BF16, ACT_GELU);
-            else
-                TG_SN_MB(DT_BF16, ACT_NONE);
-        }
-#undef TG_SN_MB
-#undef TG_SN
-        return hipGetLastError();
-    }
-    if (pl.streaming == 3) {
-#define TG_SR(DT_, ACT_, MB_)                                                                    \
-    hipLaunchKernelGGL((gemm_skinny_realign_kernel<DT_, ACT_, MB_>), grid, dim3(SR_NT), 0, s, a, \
-                       pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
+    if (pl.streaming >= 3) {
+#define TG_SR(DT_, ACT_, MB_, BT_)                                                               \
+    hipLaunchKernelGGL((gemm_skinny_pieces_kernel<DT_, ACT_, MB_, BT_>), grid, dim3(SR_NT), 0, s, \
+                       a, pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
 #define TG_SR_MB(DT_, ACT_)                                                                      \
     do {                                                                                         \
-        if (pl.mb == 2)                                                                          \
-            TG_SR(DT_, ACT_, 2);                                                                 \
+        if (pl.streaming == 4 && pl.mb == 2)                                                     \
+            TG_SR(DT_, ACT_, 2, true);                                                           \
+        else if (pl.streaming == 4)                                                              \
+            TG_SR(DT_, ACT_, 1, true);                                                           \
+        else if (pl.mb == 2)                                                                     \
+            TG_SR(DT_, ACT_, 2, false);                                                          \
         else                                                                                     \
-            TG_SR(DT_, ACT_, 1);                                                                 \
+            TG_SR(DT_, ACT_, 1, false);                                                          \
     } while (0)
         if (dt == DT_F16) {
             if (act == ACT_GELU)

@@ -622,10 +622,10 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     //    multiples) run on it as well: it measured faster than the
     //    register-staged kernel, which TG_SKINNY_REGS=1 selects (M <= 16).
     //  - B stored [N,K], 16-byte aligned with a pitch of 8 elements: the
-    //    register-streaming kernel that loads MFMA fragments straight from W.
-    // X is copied into the workspace (zero-padded to the kernel's K
-    // granule) when it is off the grid or the realigning kernel's K is not a
-    // multiple of 64; the split-K partials need the workspace too, and
+    //    same kernel with whole K-contiguous rows of W copied to LDS.
+    // X is copied into the workspace, zero-padded to a multiple of 64
+    // columns, when it is off the grid or K is not a multiple of 64; the
+    // split-K partials need the workspace too, and
     // without one the call runs unsplit (or, when X must be copied, on the
     // kernels below).
     const bool unforced = !(force && *force);
@@ -644,12 +644,12 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     float *r_ws = nullptr;
     int *r_counters = nullptr;
     unsigned short *r_x = nullptr;
-    const int64_t r_kx = nk ? (K + 7) / 8 * 8 : (K + 63) / 64 * 64; // columns of a copied X
+    const int64_t r_kx = (K + 63) / 64 * 64; // columns of a copied X
     if (small_run) {
         rpl = nk ? tg::plan_skinny_nk(a.M, a.N, a.K) : tg::plan_skinny_realign(a.M, a.N, a.K);
         if (rpl.n_tiles > (int)(kCounterBytes / sizeof(int)))
             rpl.splits = 1;
-        const bool x_ok = aligned16(A) && lda % 8 == 0 && (nk || K % 64 == 0);
+        const bool x_ok = aligned16(A) && lda % 8 == 0 && K % 64 == 0;
         // floats: the partials (a multiple of 4, so X stays 16-byte aligned), then X
         const size_t p_floats =
             rpl.splits > 1 ? (tg::skinny_ws_floats(rpl, a.M, a.N) + 3) / 4 * 4 : 0;
@@ -661,10 +661,9 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
             if (!base && x_ok && p_floats > 0) // unsplit: no workspace at all
                 rpl.splits = 1;
         }
-        if (rpl.splits == 1) {
-            const int64_t round = nk ? 512 : 256; // the kernels' K-chunk granules
-            rpl.k_chunk = (int)((K + round - 1) / round * round);
-        }
+        if (rpl.splits == 1) // one K chunk in the kernel's granule
+            rpl = nk ? tg::plan_skinny_nk(a.M, a.N, a.K, 1)
+                     : tg::plan_skinny_realign(a.M, a.N, a.K, 1);
         if (!x_ok && !base) {
             small_run = false;
             if (!stg_note)

@@ -171,10 +171,11 @@ SkinnyPlan plan_skinny(int M, int N, int K);
 // The realigning small-M kernel (streaming = 3): W at any 2-byte alignment
 // and pitch, X 16-byte aligned with a pitch of 8 elements and readable (zero
 // past K) up to K rounded up to 64 columns; Y, bias and R anywhere.
-SkinnyPlan plan_skinny_realign(int M, int N, int K);
-// The small-M kernel for B stored [N,K] (streaming = 4): W and X with 16-byte
-// aligned bases and pitches of 8 elements; Y, bias and R anywhere.
-SkinnyPlan plan_skinny_nk(int M, int N, int K);
+// want_splits > 0 asks for that many K splits (clamped to the K chunks).
+SkinnyPlan plan_skinny_realign(int M, int N, int K, int want_splits = 0);
+// The same kernel for B stored [N,K] (streaming = 4): W 16-byte aligned with
+// a pitch of 8 elements, X as above; Y, bias and R anywhere.
+SkinnyPlan plan_skinny_nk(int M, int N, int K, int want_splits = 0);
 size_t skinny_ws_floats(const SkinnyPlan &pl, int M, int N);
 hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &pl, float *ws,
                          int *counters, hipStream_t stream);
