@@ -748,6 +748,48 @@ def test_realigned_kernel_forced_on_aligned_operands_matches_streaming(tg, monke
     util.check_exact(util.to_bits(C2), ref, "realign forced")
 
 
+PARTIAL64_CASES = [
+    # (dt, M, N, K, B stored [N,K]): M (and N) off the 64 grid with more than
+    # an eighth of the last tile idle, taken by the 64-row tiles on either B
+    # layout: one row tile under 64 rows, 100 and 200 rows, N under one tile
+    (BF16, 48, 4096, 1024, False),
+    (F16, 48, 4096, 1024, True),
+    (F16, 100, 1000, 512, True),
+    (BF16, 200, 264, 384, False),
+    (F16, 33, 56, 256, True),
+    (BF16, 1000, 200, 256, True),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,trans_b", PARTIAL64_CASES)
+def test_partial_64_tiles_integer_exact(tg, monkeypatch, dt, M, N, K, trans_b):
+    # NaN in the pitch padding of every operand and around the output: the
+    # clamped copies of a partial tile read only inside the operands and the
+    # stores stop at M and N.  Integer inputs, bias and residual: bit-exact.
+    import torch
+    monkeypatch.delenv("TG_FORCE_CONFIG", raising=False)
+    p = inputs.problem(dt, M, N, K, seed=290 + M + N, kind="int", bias=True, bias_kind="int")
+    R = inputs.draw(np.random.default_rng(291 + M), (M, N), "int", dt, 8.0)
+    A = util.to_dev(padded(p["A"], K + 8, dt), dt)[:, :K]
+    if trans_b:
+        B = util.to_dev(padded(np.ascontiguousarray(p["B"].T), K + 8, dt), dt)[:, :K].t()
+    else:
+        B = util.to_dev(padded(p["B"], N + 8, dt), dt)[:, :N]
+    bias, Rd = util.to_dev(p["bias"], dt), util.to_dev(R, dt)
+    Cbuf = util.to_dev(np.full((M + 2, N + 8), NAN_BITS[dt], np.uint16), dt)
+    say("case partial 64 tiles", dt, M, N, K, "B[N,K]" if trans_b else "B[K,N]")
+    tg.gemm(A, B, out=Cbuf[:M, :N], bias=bias, residual=Rd)
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert kern.startswith("async_64x"), kern
+    _, ref = oracle.gemm_ex(dt, p["A"], p["B"], bias=p["bias"], R=R)
+    full = util.to_bits(Cbuf)
+    util.check_exact(full[:M, :N], ref, "partial 64 tiles " + kern)
+    assert np.all(full[:M, N:] == NAN_BITS[dt]) and np.all(full[M:] == NAN_BITS[dt]), \
+        "write outside the output"
+
+
 def test_k_zero_gives_activated_bias(tg):
     import torch
     dt = BF16
@@ -1267,8 +1309,8 @@ EX_SHAPES = [
     (F16, 192, 256, 512, "async_64x128x32_s4"),
     (BF16, 192, 320, 384, "async_64x64x32_s4"),   # N a multiple of 64, not of 128
     (BF16, 300, 170, 200, None),          # ragged: tiled kernel (B [K,N]) / generic (B [N,K])
-    (F16, 16, 1024, 2048, None),          # small M: streaming split-K kernel (B [K,N])
-    (BF16, 5, 520, 777, None),            # small M, ragged: register-staged kernel
+    (F16, 16, 1024, 2048, None),          # small M: streaming split-K kernel / B [N,K] kernel
+    (BF16, 5, 520, 777, None),            # small M, ragged: realigning kernel / generic
     (F16, 64, 128, 96, "generic"),
 ]
 
@@ -1286,7 +1328,10 @@ def test_residual_and_transposed_b_integer_exact(tg, monkeypatch, dt, M, N, K, f
     if force and force.startswith("async"):
         assert kern == force
     if trans_b and not (force or "").startswith("async"):
-        assert kern.startswith("generic")
+        # B stored [N,K] with pitch K: the small-M kernel when the rows are
+        # on the 16-byte grid, else the reported fallback
+        small = not force and M <= 32 and N >= 256 and K >= 256 and K % 8 == 0
+        assert kern.startswith("skinny_nk" if small else "generic"), kern
     _, ref = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T) if trans_b else p["B"],
                             trans_b=trans_b, bias=p["bias"], R=R)
     util.check_exact(bits, ref, "ex %s" % kern)
@@ -1541,11 +1586,12 @@ def test_transposed_b_k_zero(tg):
 
 def test_small_m_dispatch_bounds(tg):
     # M <= 32 streams W: the split-K streaming kernel when it fits, the
-    # realigning one for other shapes with N and K of at least 256; larger M,
-    # or narrower shapes, take the square-tile paths
+    # realigning one for other shapes with N and K of at least 256; larger M
+    # (one partial 64-row tile at M = 33), or narrower shapes, take the
+    # square-tile paths
     import torch
     w = torch.zeros((8192, 8192), dtype=torch.bfloat16, device="cuda")
-    for M, expect in ((16, "skinny_stream"), (32, "skinny_stream"), (33, "tiled")):
+    for M, expect in ((16, "skinny_stream"), (32, "skinny_stream"), (33, "async_64x64")):
         x = torch.zeros((M, 8192), dtype=torch.bfloat16, device="cuda")
         tg.gemm(x, w)
         assert tg.last_kernel().startswith(expect), (M, tg.last_kernel())

@@ -1168,12 +1168,18 @@ bool async_eligible(const GemmArgs &a, int cfg)
 {
     // An M (or an N that is a multiple of 8) that is not a multiple of the
     // tile is taken when the partial last row (column) tile wastes at most
-    // M / 8 rows (N / 8 columns).
-    const int pad = async_tiles_m(a, cfg) * async_tile_m(cfg) - a.M;
-    const bool m_ok = a.M % async_tile_m(cfg) == 0 || (a.M > async_tile_m(cfg) && 8 * pad <= a.M);
-    const int padn = async_tiles_n(a, cfg) * async_tile_n(cfg) - a.N;
-    const bool n_ok = a.N % async_tile_n(cfg) == 0 ||
-                      (a.N % 8 == 0 && a.N > async_tile_n(cfg) && 8 * padn <= a.N);
+    // M / 8 rows (N / 8 columns), and always by the 64-row (64-column)
+    // tiles: the copies of a partial tile read the last row (the last 8
+    // columns) again and the stores stop at M (N), so any partial tile is
+    // exact, and for such shapes the kernels left (element-wise loads, or
+    // none for B stored [N,K]) are several times slower than the idle rows
+    // of one tile cost.
+    const int tm = async_tile_m(cfg), tn = async_tile_n(cfg);
+    const int pad = async_tiles_m(a, cfg) * tm - a.M;
+    const bool m_ok = a.M % tm == 0 || tm == 64 || (a.M > tm && 8 * pad <= a.M);
+    const int padn = async_tiles_n(a, cfg) * tn - a.N;
+    const bool n_ok =
+        a.N % tn == 0 || (a.N % 8 == 0 && (tn == 64 || (a.N > tn && 8 * padn <= a.N)));
     return m_ok && n_ok &&
            async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0) && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
