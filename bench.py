@@ -444,7 +444,51 @@ def run_secondary(args, torch, inputs, tg):
             "TFLOP/s": round(2.0 * 32 * p["N"] * p["K"] / (ms * 1e-3) / 1e12, 1),
             "algorithmic_bytes": nbytes, "kernel": tg.last_kernel()}
         log("  ", out["bf16_skinny_32x8192x8192"])
-        del X, Ws, Y, X32, Y32
+        # the same product with W stored [N,K] (a linear layer's weight
+        # layout), rotated over four copies, and the library beside it on the
+        # same operands
+        Wts = [w.t().contiguous().t() for w in Ws]
+
+        def sknk():
+            tg.gemm(X, Wts[it[0] & 3], out=Y)
+            it[0] += 1
+
+        def sknk_lib():
+            torch.matmul(X, Wts[it[0] & 3], out=Y)
+            it[0] += 1
+
+        log("skinny: bf16 M=16 N=K=8192, W stored [N,K], rotated over 4 buffers")
+        ms = time_launches(sknk, steps, warm)
+        kern = tg.last_kernel()
+        ml = time_launches(sknk_lib, steps, warm)
+        nbytes = 2 * (p["N"] * p["K"] + p["M"] * p["K"] + p["M"] * p["N"])
+        out["bf16_skinny_16x8192x8192_w_nk"] = {
+            "ms": round(ms, 5), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "kernel": kern,
+            "library_GB/s": round(nbytes / (ml * 1e-3) / 1e9, 1)}
+        log("  ", out["bf16_skinny_16x8192x8192_w_nk"])
+        del X, Ws, Wts, Y, X32, Y32
+        # a decode step against an odd-sized vocabulary: W [4096, 50257]
+        # (412 MB, larger than the last-level cache), row pitch off the
+        # 16-byte grid, X ~ N(0,1), W ~ N(0,1/K)
+        torch.manual_seed(4)
+        M, N, K = 1, 50257, 4096
+        X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        log("skinny: bf16 1x50257x4096, W pitch 50257")
+        ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, warm)
+        kern = tg.last_kernel()
+        ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, warm)
+        nbytes = 2 * (N * K + M * K + M * N)
+        out["bf16_skinny_1x50257x4096_odd_pitch"] = {
+            "ms": round(ms, 5), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "kernel": kern,
+            "library_GB/s": round(nbytes / (ml * 1e-3) / 1e9, 1)}
+        log("  ", out["bf16_skinny_1x50257x4096_odd_pitch"])
+        del X, W, Y
 
     if args.only in (None, "offgrid"):
         # shapes off the configured tile grid, bf16, X ~ N(0,1), W ~ N(0,1/K):

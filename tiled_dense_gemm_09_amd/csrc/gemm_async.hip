@@ -784,6 +784,9 @@ __device__ __forceinline__ void a16_mainloop(
             const int i = q % MI, j = q / MI;
             acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
         }
+        // keep the wait below after these MFMAs (the compiler hoists it above
+        // them, which turns a late copy into an idle matrix core)
+        __builtin_amdgcn_sched_barrier(0);
         // copies of steps k+2 and k+3 may stay in flight; past the last step
         // the copies repeat the last tile into stages nobody reads, so the
         // count always holds
@@ -807,6 +810,12 @@ __device__ __forceinline__ void a16_mainloop(
                     read_piece(fn, nxt, q - q / PER);
             }
         }
+        // Without this fence the compiler moves the next step's first-half
+        // MFMAs up into this half, right behind the reads of their fragments,
+        // and reuses the fragment registers: every 8 MFMAs then wait on an
+        // LDS read issued a few instructions before (bf16 4096^3: 1.09-1.15
+        // PFLOP/s with the hoist, 1.24-1.29 without).
+        __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, st0);
     issue(min(1, KT - 1), st1);
