@@ -126,10 +126,12 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K,
  *    counters in a fixed scratch array of the library, 16 MiB + 16 KiB per
  *    device, held until the process ends (set up by the first call on each
  *    device, which also launches one small kernel that zeroes the
- *    counters; every split kernel leaves them at zero again);
- *  - a problem whose partials need more than 16 MiB (4 Mi floats) returns
- *    TG_ERROR_NOT_SUPPORTED and launches nothing (tg_last_kernel() gives
- *    the size it needed);
+ *    counters; every split kernel leaves them at zero again); the small-M
+ *    kernel for operands off the 16-byte grid also keeps its zero-padded
+ *    copy of A there when A is off the grid or K is not a multiple of 64;
+ *  - a problem whose partials (and copy) need more than 16 MiB (4 Mi
+ *    floats) returns TG_ERROR_NOT_SUPPORTED and launches nothing
+ *    (tg_last_kernel() gives the size it needed);
  *  - K off the 128 grid is never padded into a workspace (the kernels that
  *    need none run instead).
  * Every call on a device shares that device's scratch and finds it as the

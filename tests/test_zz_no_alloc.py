@@ -59,6 +59,10 @@ PATHS = [
      "async_128x128x32_s4_splitk"),
     ("K off the grid", {}, [(F16, 1024, 1024, 1032, "int"), (F16, 1024, 1024, 1000, "int")],
      "tiled_"),
+    # small M with W and Y on odd pitches: split-K partials in the scratch,
+    # and on the second call also the zero-padded copy of X (K = 1000)
+    ("small-M realigned", {}, [(BF16, 16, 4099, 4096, "normal"), (BF16, 8, 2001, 1000, "int")],
+     "skinny_realign"),
 ]
 
 
@@ -115,6 +119,37 @@ def test_oversized_scratch_request_launches_nothing(tg, monkeypatch):
     assert tg.last_kernel() == "async_128x128x32_s4_splitk4", tg.last_kernel()
     _, rbits = oracle.gemm(BF16, p["A"], p["B"], p["bias"])
     util.check_exact(util.to_bits(C), rbits, "16 MiB of partials")
+
+
+def test_small_m_copy_past_the_scratch_launches_nothing(tg):
+    # small M with W on an odd pitch and K = 300001 (not a multiple of 64):
+    # the zero-padded copy of A alone needs 19.2 MB, more than the scratch
+    # holds, so the allocation-free call refuses and launches nothing; the
+    # allocating entry point runs the same product
+    import torch
+    dt, M, N, K = BF16, 32, 257, 300001
+    rng = np.random.default_rng(955)
+    a = inputs.draw(rng, (M, K), "int", dt)
+    b = inputs.draw(rng, (K, N), "int", dt)
+    bias = np.zeros(N, np.uint16)
+    A, B, bd = util.to_dev(a, dt), util.to_dev(b, dt), util.to_dev(bias, dt)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    say("case small-M copy past the scratch", M, N, K)
+    with pytest.raises(tg.TgError) as e:
+        call(tg, True, dt, A, B, bd, 0, C)
+    assert e.value.status == NOT_SUPPORTED
+    kern = tg.last_kernel()
+    say("  ", kern)
+    assert kern.startswith("skinny_realign") and "fixed scratch" in kern, kern
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(C).all()), "the refused call launched something"
+    call(tg, False, dt, A, B, bd, 0, C)
+    torch.cuda.synchronize()
+    assert tg.last_kernel().startswith("skinny_realign"), tg.last_kernel()
+    got = util.to_bits(C)
+    for r in (0, M - 1):
+        _, ref = oracle.gemm(dt, a, b, bias, rows=(r, r + 1))
+        util.check_exact(got[r:r + 1], ref, "row %d" % r)
 
 
 def test_captured_call_replays_with_eager_calls_between(tg):

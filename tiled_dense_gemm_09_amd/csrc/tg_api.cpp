@@ -658,6 +658,12 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (p_floats + x_floats > 0) {
             tg_status st = TG_SUCCESS;
             base = split_workspace(p_floats + x_floats, &st);
+            if (!base && noalloc) {
+                // the allocation-free call runs the same kernels as the
+                // allocating one or nothing
+                set_last(nk ? "skinny_nk" : "skinny_realign", ws_note);
+                return st;
+            }
             if (!base && x_ok && p_floats > 0) // unsplit: no workspace at all
                 rpl.splits = 1;
         }
