@@ -513,13 +513,17 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 //    read rows 8 apart at the same columns, so the B swizzle gains a term in
 //    bit 3 of the row: granule c of row r at c ^ {0,6,10,12}[r & 3] ^
 //    2 ((r >> 3) & 1) (without it the bank-conflict counter doubles).
-//  - Step k (32 deep): the MFMAs of columns j < NJ / 2; wait for this wave's
-//    copies of step k+1 and barrier; the MFMAs of j >= NJ / 2 with the
-//    fragment reads of stage k+1 and the copies of step k+4 into stage k,
-//    which every wave finished reading before the barrier.  The order within
-//    a half is left to the compiler: pinning every MFMA with a scheduling
-//    barrier made it rotate the accumulator blocks through spare registers
-//    (about 500 register moves per four steps at WN = 2).
+//  - Step k (32 deep): the step's MFMAs, with the fragment reads of stage
+//    k+1 and the copies of step k+4 into stage k spread over the first three
+//    quarters of them (stage k was read into registers during step k-1,
+//    before the barrier that ended it); then wait for this wave's copies of
+//    step k+2 and its reads, and barrier.  The MFMA order inside a step is
+//    left to the compiler: pinning every MFMA with a scheduling barrier made
+//    it rotate the accumulator blocks through spare registers (about 500
+//    register moves per four steps at WN = 2).  A barrier in the middle of
+//    the step, with the reads and copies packed into its second half,
+//    measured 1.6 % slower at f16 4096^3 + GELU and 2.5 % at bf16 8192^3
+//    (sustained, alternating order in one process).
 namespace {
 
 // Tiles of the 16x16x32 kernels: TM x TM outputs (256, or 192 for sizes
@@ -771,61 +775,59 @@ __device__ __forceinline__ void a16_mainloop(
         }
     };
 
-    constexpr int MH = MI * NJ / 2; // MFMAs per half step
+    constexpr int MT = MI * NJ;       // MFMAs per step
     constexpr int OPS = Gm::READS + Gm::COPIES;
-    static_assert(OPS % Gm::COPIES == 0, "copies evenly spread over the second half");
+    constexpr int SPAN = MT * 3 / 4;  // MFMAs the reads and copies are spread over
     Frag f0, f1;
     auto step = [&](int kt, auto sidx, Frag &fc, Frag &fn) {
         constexpr int S = decltype(sidx)::value;
         unsigned char *cur = stage(sidx);
         unsigned char *nxt = stage(std::integral_constant<int, (S + 1) % 4>{});
+        // past the last step the copies repeat the last tile into stages
+        // nobody reads, so the wait counts below always hold
+        const int kc = min(kt + 4, KT - 1);
 #pragma unroll
-        for (int q = 0; q < MH; ++q) {
+        for (int q = 0; q < MT; ++q) {
             const int i = q % MI, j = q / MI;
             acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+            if (q < SPAN) {
+                // ops o0 .. o1-1 after this MFMA; op o is a copy where the
+                // running count of copies (evenly spread) steps up, else a read
+                const int o0 = q * OPS / SPAN, o1 = (q + 1) * OPS / SPAN;
+                for (int o = o0; o < o1; ++o) {
+                    const int upto = (o + 1) * Gm::COPIES / OPS, before = o * Gm::COPIES / OPS;
+                    if (upto > before)
+                        copy(kc, cur, upto - 1);
+                    else
+                        read_piece(fn, nxt, o - before);
+                }
+            }
         }
-        // keep the wait below after these MFMAs (the compiler hoists it above
-        // them, which turns a late copy into an idle matrix core)
+        // Keep the next step's MFMAs below the wait and barrier: the compiler
+        // otherwise moves them up behind the reads of their fragments and
+        // reuses the fragment registers, so every 8 MFMAs wait on an LDS read
+        // issued a few instructions before (bf16 4096^3: 1.09-1.15 PFLOP/s
+        // with the hoist, 1.24-1.29 without).
         __builtin_amdgcn_sched_barrier(0);
-        // copies of steps k+2 and k+3 may stay in flight; past the last step
-        // the copies repeat the last tile into stages nobody reads, so the
-        // count always holds
+        // copies of step k+2 landed (those of k+3 and k+4 may stay in
+        // flight) and this wave's reads of stage k+1 done; then everybody's
         wait_vmcnt<2 * Gm::COPIES>();
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         stage_barrier();
-        const int kc = min(kt + 4, KT - 1);
-        // second half: MFMAs, the next stage's reads and this step's copies
-        // (one copy after every READS / COPIES reads)
-#pragma unroll
-        for (int q = 0; q < (MH > OPS ? MH : OPS); ++q) {
-            if (q < MH) {
-                const int i = q % MI, j = NJ / 2 + q / MI;
-                acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
-            }
-            if (q < OPS) {
-                constexpr int PER = OPS / Gm::COPIES; // ops per copy slot
-                if (q % PER == PER - 1)
-                    copy(kc, cur, q / PER);
-                else
-                    read_piece(fn, nxt, q - q / PER);
-            }
-        }
-        // Without this fence the compiler moves the next step's first-half
-        // MFMAs up into this half, right behind the reads of their fragments,
-        // and reuses the fragment registers: every 8 MFMAs then wait on an
-        // LDS read issued a few instructions before (bf16 4096^3: 1.09-1.15
-        // PFLOP/s with the hoist, 1.24-1.29 without).
         __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, st0);
     issue(min(1, KT - 1), st1);
     issue(min(2, KT - 1), st2);
     issue(min(3, KT - 1), st3);
-    wait_vmcnt<3 * Gm::COPIES>();
+    wait_vmcnt<2 * Gm::COPIES>(); // steps 0 and 1 landed
     stage_barrier();
 #pragma unroll
     for (int q = 0; q < Gm::READS; ++q)
         read_piece(f0, st0, q);
+    // every wave's reads of stage 0 are done before step 0 copies into it
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
     for (int kt = 0; kt < KT; kt += 4) {
         step(kt, std::integral_constant<int, 0>{}, f0, f1);
         step(kt + 1, std::integral_constant<int, 1>{}, f1, f0);
