@@ -612,6 +612,9 @@ REALIGN_CASES = [
     (F16, 16, 2001, 2048, (0, 0, 0), 0, 0, 1, "int"),
     (BF16, 24, 2001, 2048, (0, 0, 0), 0, 0, 3, "normal"),
     (F16, 16, 2001, 2112, (0, 0, 0), 5, 0, 7, "int"),
+    # 257 to 511 tiles of 120 columns: 64-column tiles (501, the last one
+    # 3 columns wide), W 5 elements into its buffer, Y one element in
+    (F16, 16, 32003, 1024, (0, 3, 0), 5, 1, 0, "int"),
 ]
 
 
@@ -647,7 +650,9 @@ def test_small_m_off_grid_realigned(tg, monkeypatch, dt, M, N, K, pads, woff, of
     torch.cuda.synchronize()
     kern = tg.last_kernel()
     say("  kernel", kern)
-    assert kern.startswith("skinny_realign_bn120_split"), kern
+    assert kern.startswith("skinny_realign_bn"), kern
+    if N == 32003:
+        assert kern.startswith("skinny_realign_bn64_"), kern
     if splits:  # the planner keeps a forced count within the K chunks
         assert ("_split1x" in kern) == (splits == 1), kern
     assert ("_m32" in kern) == (M > 16), kern

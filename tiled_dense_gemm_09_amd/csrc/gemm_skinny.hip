@@ -820,7 +820,8 @@ __global__ __launch_bounds__(SC_NT, 1) void gemm_skinny_cols_kernel(GemmArgs p, 
 // of 8 consecutive rows, so neither the direct-to-LDS copies nor the
 // transposing LDS reads can take a row as it stands.
 //
-// Workgroup (tile, split) keeps 120 columns and one K-chunk.  For each row
+// Workgroup (tile, split) keeps 120 columns (fewer, down to 64, when that
+// brings a grid of 257 to 511 tiles near two per CU) and one K-chunk.  For each row
 // of a 64-deep slab it copies the 16 aligned pieces (128 elements) that begin
 // with the piece holding the tile's first column: the 120 columns sit at the
 // row's offset o (0 <= o <= 7) inside them.  A slab advances the address by
@@ -880,13 +881,16 @@ __host__ __device__ constexpr int sr_off(int r, int e)
 
 } // namespace
 
+// bn: columns stored per workgroup ([K,N]: a multiple of 8, at most 120;
+// [N,K]: 128)
 template <int DT, int ACT, int MB, bool BT>
 __global__ __launch_bounds__(SR_NT, 2) void gemm_skinny_pieces_kernel(GemmArgs p, int n_tiles,
-                                                                      int k_chunk, int splits,
-                                                                      float *ws, int *counters)
+                                                                      int bn, int k_chunk,
+                                                                      int splits, float *ws,
+                                                                      int *counters)
 {
     static_assert(MB == 1 || MB == 2, "up to 32 rows");
-    constexpr int TBN = BT ? 128 : SR_BN; // columns stored per workgroup
+    const int TBN = BT ? 128 : bn;
     __shared__ __attribute__((aligned(1024))) unsigned char st[SR_STAGES][SR_STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -1204,6 +1208,16 @@ SkinnyPlan plan_pieces(int M, int N, int K, int want_splits, bool bt)
     pl.mb = M > 16 ? 2 : 1;
     pl.bn = bt ? 128 : SR_BN;
     pl.n_tiles = (N + pl.bn - 1) / pl.bn;
+    if (!bt && pl.n_tiles > 256 && pl.n_tiles < 512) {
+        // Between one and two workgroups per CU most CUs would hold one, with
+        // half the copies in flight (16 x 32000 x 4096 with an odd pitch: 4.3
+        // TB/s on 267 tiles): narrower tiles (at least 64 columns; each still
+        // copies its 128-element runs) bring the count near 512.
+        int bn = ((N + 511) / 512 + 7) / 8 * 8;
+        bn = bn < 64 ? 64 : (bn > SR_BN ? SR_BN : bn);
+        pl.bn = bn;
+        pl.n_tiles = (N + bn - 1) / bn;
+    }
     constexpr int round = SR_STAGES * SR_BK;
     const int quanta = (K + round - 1) / round;
     int splits = 512 / pl.n_tiles;
@@ -1347,7 +1361,7 @@ hipError_t launch_skinny(int dt, int act, const GemmArgs &a, const SkinnyPlan &p
     if (pl.streaming >= 3) {
 #define TG_SR(DT_, ACT_, MB_, BT_)                                                               \
     hipLaunchKernelGGL((gemm_skinny_pieces_kernel<DT_, ACT_, MB_, BT_>), grid, dim3(SR_NT), 0, s, \
-                       a, pl.n_tiles, pl.k_chunk, pl.splits, ws, counters)
+                       a, pl.n_tiles, pl.bn, pl.k_chunk, pl.splits, ws, counters)
 #define TG_SR_MB(DT_, ACT_)                                                                      \
     do {                                                                                         \
         if (pl.streaming == 4 && pl.mb == 2)                                                     \
