@@ -572,8 +572,10 @@ def run_sweep(torch, tg):
     object per shape on stdout: square f16/bf16 GEMMs from 512^3 to 8192^3
     (A, B = U[-1,1]/8, no epilogue; up to 2048^3 both sides replayed from
     captured graphs of 50 launches), bf16 products with M = 1..32
-    (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB), and bf16
-    shapes off the tile grid (X ~ N(0,1), W ~ N(0, 1/K)): token counts that
+    (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB; also W stored
+    [N,K], and W on an odd pitch), token counts off the 64 grid and square
+    shapes with B in either layout, and bf16 shapes off the tile grid (X ~
+    N(0,1), W ~ N(0, 1/K)): token counts that
     leave a partial last tile, grids short of a wave of 256 x 256 tiles,
     pitches off the 8-element grid, and square sizes whose K is not a
     multiple of 128."""
@@ -634,6 +636,66 @@ def run_sweep(torch, tg):
                               "GB/s": round(nb / ms / 1e6), "kernel": kern,
                               "library_GB/s": round(nb / ml / 1e6)}), flush=True)
         del Ws
+    # small M with W stored [N,K] (rotated as above), and with W on an odd
+    # pitch (one copy: 412 MB at N = 50257 already exceeds the last-level cache)
+    for (N, K) in ((8192, 8192),):
+        rot = max(1, (1 << 30) // (N * K * 2))
+        Ws = [(torch.randn(N, K, dtype=torch.bfloat16, device="cuda") * K ** -0.5).t()
+              for _ in range(rot)]
+        for M in (1, 16, 32):
+            X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            it = [0]
+
+            def ours():
+                tg.gemm(X, Ws[it[0] % rot], out=Y)
+                it[0] += 1
+
+            def lib():
+                torch.matmul(X, Ws[it[0] % rot], out=Y)
+                it[0] += 1
+            ms = time_launches(ours, 500, 50)
+            kern = tg.last_kernel()
+            ml = time_launches(lib, 500, 50)
+            nb = 2 * (K * N + M * K + M * N)
+            print(json.dumps({"shape": "bf16 M=%d N=%d K=%d, W stored [N,K]" % (M, N, K),
+                              "ms": round(ms, 5), "GB/s": round(nb / ms / 1e6), "kernel": kern,
+                              "library_GB/s": round(nb / ml / 1e6)}), flush=True)
+        del Ws
+    for (M, N, K) in ((1, 50257, 4096), (16, 50257, 4096), (32, 50257, 4096),
+                      (16, 32000, 4096)):
+        X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        W = (torch.randn(K, N + 1, dtype=torch.bfloat16, device="cuda") * K ** -0.5)[:, :N]
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ms = time_launches(lambda: tg.gemm(X, W, out=Y), 200, 20)
+        kern = tg.last_kernel()
+        ml = time_launches(lambda: torch.matmul(X, W, out=Y), 200, 20)
+        nb = 2 * (K * N + M * K + M * N)
+        print(json.dumps({"shape": "bf16 M=%d N=%d K=%d, W pitch %d" % (M, N, K, N + 1),
+                          "ms": round(ms, 5), "GB/s": round(nb / ms / 1e6), "kernel": kern,
+                          "library_GB/s": round(nb / ml / 1e6)}), flush=True)
+        del X, W, Y
+    # token counts off the 64 grid and square shapes, both B layouts
+    for (M, N, K) in ((48, 4096, 4096), (100, 4096, 4096), (200, 4096, 4096),
+                      (4096, 4096, 4096), (8192, 8192, 8192)):
+        for trans in (False, True):
+            X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+            if trans:
+                W = (torch.randn(N, K, dtype=torch.bfloat16, device="cuda") * K ** -0.5).t()
+            else:
+                W = torch.randn(K, N, dtype=torch.bfloat16, device="cuda") * K ** -0.5
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            f = 2.0 * M * N * K
+            steps = max(20, min(500, int(2e13 / f)))
+            ms = time_launches(lambda: tg.gemm(X, W, out=Y), steps, steps // 10 + 2)
+            kern = tg.last_kernel()
+            ml = time_launches(lambda: torch.matmul(X, W, out=Y), steps, steps // 10 + 2)
+            print(json.dumps({"shape": "bf16 %dx%dx%d, B %s" % (M, N, K,
+                                                                "stored [N,K]" if trans else "[K,N]"),
+                              "ms": round(ms, 5), "TFLOP/s": round(f / ms / 1e9, 1),
+                              "kernel": kern, "library_TFLOP/s": round(f / ml / 1e9, 1)}),
+                  flush=True)
+            del X, W, Y
     for (M, N, K) in ((2049, 4096, 4096), (3000, 11008, 4096), (5000, 4096, 4096),
                       (4096, 4000, 4096), (3584, 3584, 3584), (2304, 2304, 2304),
                       (4608, 4608, 4608), (4095, 4095, 4095), (4097, 4097, 4097),
