@@ -90,6 +90,45 @@ def test_small_config_automatic_split_k(tg, monkeypatch, name, expect):
             util.check_tol(p["dt"], bits, f64, name + " split-K", ref_bits=rbits)
 
 
+MEDIUM_M_SPLIT_CASES = [
+    # (dt, M, N, K, trans_b, splits): grids of at most 128 tiles of 64 x 64
+    # with K >= 2048 split K by default, up to one wave of workgroups
+    (F16, 64, 4096, 4096, False, 4),
+    (BF16, 128, 2048, 2048, False, 4),
+    (F16, 96, 1000, 3072, False, 8),     # partial last row and column tiles
+    (BF16, 64, 2048, 4096, True, None),  # B stored [N,K]
+]
+
+
+@pytest.mark.parametrize("case", MEDIUM_M_SPLIT_CASES, ids=lambda c: "%dx%dx%d%s" % (
+    c[1], c[2], c[3], "_bt" if c[4] else ""))
+def test_medium_m_default_split_k(tg, case):
+    # integer inputs bit-exact; random inputs with bias and GELU within the
+    # tolerance, and the same bits on a second call (the partials are added
+    # in split order, not in arrival order)
+    dt, M, N, K, trans_b, splits = case
+    for integer in (True, False):
+        kind = "int" if integer else "normal"
+        p = inputs.problem(dt, M, N, K, seed=M + N + K + integer, kind=kind, bias=True,
+                           act=inputs.ACT_NONE if integer else inputs.ACT_GELU_TANH,
+                           bias_kind="int" if integer else "bias",
+                           b_scale=1.0 if integer else 1.0 / np.sqrt(K))
+        say("case medium-M split-K", dt, M, N, K, "B [N,K]" if trans_b else "B [K,N]", kind)
+        bits, kern = run_ex(tg, p, trans_b)
+        say("  kernel", kern)
+        if splits is None:
+            assert "_splitk" in kern, kern
+        else:
+            assert kern.endswith("_splitk%d" % splits), kern
+        f64, rbits = oracle.gemm(dt, p["A"], p["B"], p["bias"], p["act"])
+        if integer:
+            util.check_exact(bits, rbits, "medium-M split-K integer")
+        else:
+            util.check_tol(dt, bits, f64, "medium-M split-K", ref_bits=rbits)
+            again, _ = run_ex(tg, p, trans_b)
+            util.check_exact(again, bits, "medium-M split-K repeat")
+
+
 @pytest.mark.parametrize("name", ["f16_256", "f16_1024"])
 def test_small_config_integer_exact(tg, name):
     p = inputs.config_problem(name, integer=True)
@@ -1621,8 +1660,8 @@ def test_dispatch_choices(tg, monkeypatch):
     tg.gemm(c, c)
     assert tg.last_kernel() == "async_128x128x32_s4"
     # under-filled grids take the smaller asynchronous tiles (the largest
-    # with a full wave, else the smallest), unsplit unless TG_SPLITK asks
-    # (0: automatic, up to one wave of workgroups)
+    # with a full wave, else the smallest), split along K automatically only
+    # from K = 2048 on (TG_SPLITK=0: at any K, up to one wave of workgroups)
     b = torch.zeros((1024, 1024), dtype=torch.float16, device="cuda")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x64x32_s4"
@@ -1647,6 +1686,18 @@ def test_dispatch_choices(tg, monkeypatch):
     # whole waves (4096^3: 256 tiles) stay data-parallel
     tg.gemm(g, g)
     assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
+    # 64 x 4096 x 4096: 64 tiles of 64 x 64, four K splits fill the wave;
+    # 128 x 4096 x 14336: 128 tiles, two splits; TG_SPLITK=1 turns it off
+    h = torch.zeros((64, 4096), dtype=torch.float16, device="cuda")
+    tg.gemm(h, g)
+    assert tg.last_kernel() == "async_64x64x32_s4_splitk4", tg.last_kernel()
+    i = torch.zeros((128, 14336), dtype=torch.float16, device="cuda")
+    j = torch.zeros((14336, 4096), dtype=torch.float16, device="cuda")
+    tg.gemm(i, j)
+    assert tg.last_kernel().endswith("_splitk2"), tg.last_kernel()
+    monkeypatch.setenv("TG_SPLITK", "1")
+    tg.gemm(h, g)
+    assert tg.last_kernel() == "async_64x64x32_s4", tg.last_kernel()
     monkeypatch.setenv("TG_SPLITK", "0")
     tg.gemm(b, b)
     assert tg.last_kernel() == "async_64x64x32_s4"

@@ -63,6 +63,9 @@ PATHS = [
     # and on the second call also the zero-padded copy of X (K = 1000)
     ("small-M realigned", {}, [(BF16, 16, 4099, 4096, "normal"), (BF16, 8, 2001, 1000, "int")],
      "skinny_realign"),
+    # medium M with long K: the automatic split of the 64 x 64 tiles
+    ("medium-M split-K", {}, [(F16, 64, 4096, 4096, "normal"), (BF16, 128, 1024, 2048, "int")],
+     "async_64x64x32_s4_splitk"),
 ]
 
 

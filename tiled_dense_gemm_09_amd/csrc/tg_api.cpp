@@ -796,31 +796,48 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
     } else if ((!force_tiled || b_trans) && choose_async(a, force) >= 0) {
         const int cfg = choose_async(a, force);
         const int group_m = env_int("TG_GROUP_M", 4);
-        // Split-K is opt-in (TG_SPLITK=0: automatic, n: n splits): at 256^3
-        // and 1024^3 the three device-scope round trips of the exchange
-        // (partial stores, counter, read-back) cost more than the split saves
-        const int want = env_int("TG_SPLITK", 1);
-        const int splits = tg::plan_async_splits(a, cfg, want);
+        // Split-K over the 32x32x16-MFMA tiles: automatic for K >= 2048 (up
+        // to one wave of workgroups from grids of at most 128 tiles: 64 x
+        // 4096 x 4096 runs 13.7 us in four splits against 20.3 unsplit,
+        // 128 x 4096 x 14336 37.8 against 62.2 in two); below that the three
+        // device-scope round trips of the exchange (partial stores, counter,
+        // read-back) cost more than the split saves (256^3, 1024^3).
+        // TG_SPLITK=0: automatic at any K, n: n splits, 1: never.  An
+        // automatic split whose workspace cannot be had (a capture that would
+        // grow it, no memory) runs unsplit; a requested one, or one on the
+        // allocation-free entry point, launches nothing and says why.
+        const bool split_asked = getenv("TG_SPLITK") && *getenv("TG_SPLITK");
+        const int want = split_asked ? env_int("TG_SPLITK", 1) : (K >= 2048 ? 0 : 1);
+        int splits = tg::plan_async_splits(a, cfg, want);
         float *ws = nullptr;
         int *counters = nullptr;
+        const char *split_note = nullptr;
         if (splits > 1) {
             static_assert(tg::kMaxSplitTiles * sizeof(int) <= kCounterBytes, "counter room");
             tg_status st = TG_SUCCESS;
             void *base = split_workspace(tg::async_ws_floats(a, cfg, splits), &st);
-            if (!base) {
+            if (!base && (split_asked || noalloc)) {
                 char name[64];
                 snprintf(name, sizeof name, "%s_splitk%d", tg::async_config_name(cfg), splits);
                 set_last(name, ws_note);
                 return st;
             }
-            counters = static_cast<int *>(base);
-            ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
+            if (base) {
+                counters = static_cast<int *>(base);
+                ws = reinterpret_cast<float *>(static_cast<char *>(base) + kCounterBytes);
+            } else {
+                splits = 1;
+                split_note = st == TG_ERROR_NOT_SUPPORTED ? " (unsplit: stream capture)"
+                                                          : " (unsplit: no workspace)";
+            }
         }
         err = tg::launch_async(cfg, kdt, kact, a, group_m > 0 ? group_m : 4, splits, ws, counters,
                                s);
         char detail[64] = "";
         if (splits > 1)
             snprintf(detail, sizeof detail, "_splitk%d", splits);
+        else if (split_note)
+            snprintf(detail, sizeof detail, "%s", split_note);
         else if (sk_note)
             snprintf(detail, sizeof detail, "%s", sk_note);
         set_last(tg::async_config_name(cfg), detail);
