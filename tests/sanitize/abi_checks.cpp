@@ -250,7 +250,7 @@ int main()
     EXPECT(tg_schedule_tile(1 << 20, 1 << 20, 3, 4, 5, &mat, &tm, &tn) == -1);
     EXPECT(tg_schedule_tile(4, 4, 1, HUGE_, 3, &mat, &tm, &tn) == -1 ||
            (tm >= 0 && tm < 4 && tn >= 0 && tn < 4));
-    for (int layout = -1; layout < 6; ++layout)
+    for (int layout = -1; layout < 7; ++layout)
         for (int64_t r : {(int64_t)-1, (int64_t)0, (int64_t)5, (int64_t)1 << 40, HUGE_})
             EXPECT(tg_lds_swizzle(layout, r) >= -1);
     for (int64_t cols : {8, 64, 128, 256})

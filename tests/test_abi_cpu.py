@@ -303,7 +303,8 @@ def _b16_lanes(q0, h, col0):
     return rows, cols
 
 
-@pytest.mark.parametrize("layout,granules", [(0, 4), (1, 16), (1, 32), (2, 8), (3, 32), (4, 24)])
+@pytest.mark.parametrize("layout,granules", [(0, 4), (1, 16), (1, 32), (2, 8), (3, 32), (4, 24),
+                                             (5, 16)])
 def test_swizzles_permute_each_row(layout, granules):
     for r in range(64):
         s = _swz(layout, r)
@@ -352,6 +353,20 @@ def test_b_transposing_reads_192_tile_kernel_are_bank_conflict_free():
                 assert _max_bank_load(_b_pass(4, 384, rows, cols)) == 1
     rows, cols = _b16_lanes(0, 0, 0)
     assert _max_bank_load(_b_pass(4, 384, rows, cols, swizzle=False)) > 1  # control
+
+
+def test_b_transposing_reads_128_tile_kernel_are_bank_conflict_free():
+    # 256-byte rows (128 columns): every 16-column fragment of either wave
+    # column, both halves, both 32-lane passes
+    for q0 in (0, 2):
+        for h in range(2):
+            for col0 in range(0, 128, 16):
+                rows, cols = _b16_lanes(q0, h, col0)
+                assert _max_bank_load(_b_pass(5, 256, rows, cols)) == 1
+    rows, cols = _b16_lanes(0, 0, 0)
+    assert _max_bank_load(_b_pass(5, 256, rows, cols, swizzle=False)) > 1  # control
+    # the 192-tile swizzle does not cover these rows
+    assert _max_bank_load(_b_pass(4, 256, rows, cols)) > 1
 
 
 def test_bounds_rule_matches_printed_example():

@@ -38,7 +38,7 @@ def tg():
 
 
 # (dt, M, N, K, B stored [N,K]): every tile split (144 tiles, fewer than a
-# wave), two whole waves plus a partial one (576 tiles: 256 data-parallel,
+# wave but at least half of one), two whole waves plus a partial one (576 tiles: 256 data-parallel,
 # 320 split), a piece of one quad (K = 256), partial last row and column
 # tiles, and B stored [N,K]
 CASES = [
@@ -162,12 +162,14 @@ def test_stream_k_default_threshold(tg):
     # wave: 3000 x 11008 x 4096 (two waves + 4 tiles) takes stream-K; short
     # of a wave the grid stays whole: 3072^3 and 2049 x 4096 x 4096 (144
     # tiles of 256, 256 and 242 of 192) on 192 x 192 tiles, 3584^3 (196 of
-    # 256, 361 of 192) on a partly filled wave of 256 x 256 tiles
+    # 256, 361 of 192) on a partly filled wave of 256 x 256 tiles, where the
+    # 32x32x16 kernel measured faster than the 16x16x32 one (83 against 87
+    # us)
     import torch
     for (M, N, K), expect in (((3072, 3072, 3072), "async_192x192x32_s4_mfma16"),
                               ((3000, 11008, 4096), SK),
                               ((2049, 4096, 4096), "async_192x192x32_s4_mfma16"),
-                              ((3584, 3584, 3584), "async_256x256x32_s4_mfma16")):
+                              ((3584, 3584, 3584), "async_256x256x32_s4")):
         a = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
         b = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
         tg.gemm(a, b)

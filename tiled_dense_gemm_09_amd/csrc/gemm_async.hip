@@ -526,13 +526,13 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 //    (sustained, alternating order in one process).
 namespace {
 
-// Tiles of the 16x16x32 kernels: TM x TM outputs (256, or 192 for sizes
+// Tiles of the 16x16x32 kernels: TM x TM outputs (256; 192 or 128 for sizes
 // whose 256 x 256 tiles would leave most of a wave idle), K steps of 32.
 // A stage holds A [TM][32] K-contiguous, then B [32][TM] N-contiguous (or,
 // stored [N,K], [TM][32] like A).
 template <int TM>
 struct A16Tile {
-    static_assert(TM == 256 || TM == 192, "16x16x32 tile sizes");
+    static_assert(TM == 256 || TM == 192 || TM == 128, "16x16x32 tile sizes");
     static constexpr int A_BYTES = TM * AS_BK * 2;
     static constexpr int STAGE = 2 * A_BYTES;
 };
@@ -696,7 +696,7 @@ __device__ __forceinline__ void a16_mainloop(
             } else {
                 const unsigned byte = 1024u * q + 16u * lane;
                 const int rb = (int)(byte / (2 * TM));
-                const int gb0 = (int)(byte % (2 * TM) / 16) ^ swz_b192(rb);
+                const int gb0 = (int)(byte % (2 * TM) / 16) ^ (TM == 192 ? swz_b192(rb) : swz_b128(rb));
                 gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + gb0 * 8, p.N - 8) +
                         (int64_t)kt0 * b_step;
                 b_kl[c] = p.K - kt0 * AS_BK - rb;
@@ -749,7 +749,7 @@ __device__ __forceinline__ void a16_mainloop(
                 } else {
                     const int r = 8 * q16 + 4 * h + (jj >> 2);
                     const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
-                    const int sw = TM == 256 ? swz_b16(r) : swz_b192(r);
+                    const int sw = TM == 256 ? swz_b16(r) : TM == 192 ? swz_b192(r) : swz_b128(r);
                     b_off[j][h] = A_BYTES + r * (2 * TM) + (((col >> 3) ^ sw) * 16) + (col & 7) * 2;
                 }
             }
@@ -1142,6 +1142,9 @@ const AsyncConfig kAsyncConfigs[] = {
     // 192 x 192 tiles fill a wave where 256 x 256 ones leave much of it idle
     // (3072^2 outputs: 256 tiles against 144)
     {3, 3, 4, false, "async_192x192x32_s4_mfma16"},
+    // as fast as the 32x32x16 128 x 128 tiles (within 3 % over 264 shapes):
+    // at this size the K loop is bound by the latency of its steps
+    {2, 2, 4, true, "async_128x128x32_s4_mfma16"},
     {4, 4, 0, false, "async_256x256x32_s4"},
     {2, 2, 0, false, "async_128x128x32_s4"},
     {1, 2, 0, false, "async_64x128x32_s4"},
@@ -1231,7 +1234,10 @@ SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
     if (a.K % (AS_STAGES * AS_BK) != 0)
         return pl;
     // whole waves need no split; below half a wave each tile would be cut
-    // into more than two pieces (smaller tiles do better there)
+    // into more than two pieces, and the one workgroup that adds them reads
+    // every 256 KiB partial back on its own (measured with pieces of
+    // ceil(q / (CUs / tiles)) quads: 256 x 4096 x 4096, 16 tiles, 63.6 us
+    // against 21.1 on 64 x 64 tiles; 512 x 14336 x 4096 80.8 against 63.2)
     if (tiles % cus == 0 || 2 * tiles < cus || q < 2 || tiles >= (int64_t)1 << 24)
         return pl;
     const int64_t full = tiles / cus, rest = tiles % cus;
@@ -1321,10 +1327,16 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                           A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
-        const bool t192 = kAsyncConfigs[cfg].ti == 3;
+        const bool t192 = kAsyncConfigs[cfg].ti == 3, t128 = kAsyncConfigs[cfg].ti == 2;
 #define TG_A16K(DT_, ACT_, KM_)                                                                  \
     do {                                                                                         \
-        if (t192 && a.b_trans)                                                                   \
+        if (t128 && a.b_trans)                                                                   \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 128>), grid,         \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (t128)                                                                           \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 128>), grid,        \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (t192 && a.b_trans)                                                              \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 192>), grid,         \
                                dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
         else if (t192)                                                                           \

@@ -8,6 +8,7 @@
 // failure mode to avoid -- here the chosen kernel is always reported).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -250,64 +251,120 @@ int choose_config(int64_t M, int64_t N, int n_mat)
     return n - 1;
 }
 
+// Launch-time model of the asynchronous configurations, for grids short of a
+// full wave of 256 x 256 tiles.  A configuration with s K splits runs
+// n = ceil(tiles s / CUs) workgroups per CU; it costs
+//     a + b (K / s) (1 + r (n - 1))                      [us, K in thousands]
+// plus, split, e + h (partial bytes s M N 8, in MB: written once, read once),
+// and never less than the compulsory HBM traffic (A, B and C once) at bw.
+// Per workgroup the K loop is latency-bound: a 64 x 64 tile takes 3.9 us per
+// thousand k against 6.9 for 128 x 128, four times the work, so the larger
+// tile wins wherever it still fills the chip, and split-K buys back the
+// waves that a small grid leaves idle.  The coefficients are a least-squares
+// fit (relative error) of 3380 launches timed back to back on MI355X: bf16,
+// B in both layouts, M 64..2048 over 13 (N, K) pairs from 1024 to 14336, every
+// configuration with 1, 2, 4 and 8 splits; 11% rms error, and the choice it
+// makes lands within 1% of the fastest measured launch summed over the 260
+// shapes (largest single loss 19%).
+struct WaveCost {
+    int tm, tn;
+    bool m16;
+    double a, b, r, e;
+};
+constexpr WaveCost kWaveCost[] = {
+    {64, 64, false, 1.71, 3.86, 1.03, 2.92},    {64, 128, false, 1.93, 4.95, 1.26, 3.19},
+    {128, 128, false, 2.21, 6.86, 1.36, 4.21},  {192, 192, true, 6.72, 11.89, 1.42, 0.0},
+    {256, 256, false, 8.20, 16.49, 1.50, 0.0},  {256, 256, true, 8.24, 18.59, 1.50, 0.0},
+};
+constexpr double kSplitUsPerMB = 0.148; // partial traffic of a split
+constexpr double kModelHbmBytesPerUs = 4.49e6;
+
+// Modelled microseconds of configuration cfg with s splits; < 0 when the
+// configuration has no coefficients.
+double wave_cost_us(const tg::GemmArgs &a, int cfg, int s, int cus)
+{
+    const int tm = tg::async_tile_m(cfg), tn = tg::async_tile_n(cfg);
+    const bool m16 = tg::async_mfma16(cfg);
+    for (const WaveCost &w : kWaveCost) {
+        if (w.tm != tm || w.tn != tn || w.m16 != m16)
+            continue;
+        const double tiles = (double)tg::async_tiles_m(a, cfg) * tg::async_tiles_n(a, cfg) * a.n_mat;
+        const double n = std::ceil(tiles * s / cus);
+        double t = w.a + w.b * ((double)a.K / s / 1000.0) * (1.0 + w.r * (n - 1.0));
+        if (s > 1)
+            t += w.e + kSplitUsPerMB * s * (double)a.M * a.N * a.n_mat * 8.0 / 1e6;
+        const double bytes =
+            2.0 * ((double)a.M * a.K + (double)a.n_mat * ((double)a.K * a.N + (double)a.M * a.N));
+        return std::max(t, bytes / kModelHbmBytesPerUs);
+    }
+    return -1.0;
+}
+
+// Split count the model takes for configuration cfg (1 when no split is
+// possible or none pays).  Only splits whose partials fit the fixed scratch
+// are taken, so the allocation-free entry point makes the same choice.
+int model_splits(const tg::GemmArgs &a, int cfg, int cus)
+{
+    int best_s = 1;
+    double best_t = wave_cost_us(a, cfg, 1, cus);
+    for (int s = 2; s <= 8 && best_t >= 0.0; ++s) {
+        if (tg::plan_async_splits(a, cfg, s) != s || tg::async_ws_floats(a, cfg, s) > kScratchFloats)
+            continue;
+        const double t = wave_cost_us(a, cfg, s, cus);
+        if (t >= 0.0 && t < best_t) {
+            best_t = t;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
+
 // Asynchronous-copy configuration for a problem, or -1: a forced name, else
 // the 256 x 256 tiles on the 16x16x32 MFMA with about a full wave of
-// workgroups; with fewer, those or the 192 x 192 ones, whichever fills its
-// waves better, when it has at least half a wave of tiles; else the largest
-// 32x32x16 tile with about a full wave, else the smallest eligible tile.
-int choose_async(const tg::GemmArgs &a, const char *force)
+// workgroups (a whole one or more with a short last one is stream-K's,
+// decided before); with fewer, the configuration and split count of least
+// modelled time.  K off the 128 grid is masked on the 16x16x32 tiles only:
+// there they need half a wave of tiles, else K padding or the tiled kernel
+// does better.  splits (may be null: unsplit candidates only) receives the
+// model's split count for the returned configuration (1 for a forced one:
+// TG_SPLITK alone splits those).
+int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr)
 {
     const int n = tg::num_async_configs();
+    const int cus = device_cus();
+    if (splits)
+        *splits = 1;
     if (force && strncmp(force, "async", 5) == 0) {
         for (int i = 0; i < n; ++i)
-            if (strcmp(force, tg::async_config_name(i)) == 0)
+            if (strcmp(force, tg::async_config_name(i)) == 0) {
                 return tg::async_eligible(a, i) ? i : -1;
+            }
         return -1;
     }
     auto tiles = [&](int i) {
         return (int64_t)tg::async_tiles_m(a, i) * tg::async_tiles_n(a, i) * a.n_mat;
     };
-    // Short of a wave of 256 x 256 tiles (a whole one or more, with a short
-    // last one, is stream-K's, decided before): the kernel is power-bound,
-    // so a partly filled wave runs at a higher clock and costs less than its
-    // idle units suggest, but 192 x 192 tiles that fill their waves do
-    // better still, counted at 0.8 of the 256 x 256 tiles' rate (measured,
-    // bf16: 3584^3, 196 tiles of 256 against 361 of 192, 1141 against 922
-    // TFLOP/s; 3072^3, 144 against 256, 792 against 982; 4096^3 full waves of
-    // either, 1339 against 1073).
-    const int cus = device_cus();
-    auto fill = [&](int64_t t) {
-        const int64_t waves = (t + cus - 1) / cus;
-        return (double)t / (double)(waves * cus);
-    };
-    int best16 = -1;
-    double best_fill = 0.0;
-    for (int i = 0; i < n; ++i) {
-        if (tg::async_forced_only(i) || !tg::async_mfma16(i) || !tg::async_eligible(a, i))
-            continue;
-        const int64_t t = tiles(i);
-        if (tg::async_tile_m(i) == 256 && t >= 240)
+    for (int i = 0; i < n; ++i)
+        if (!tg::async_forced_only(i) && tg::async_mfma16(i) && tg::async_tile_m(i) == 256 &&
+            tg::async_eligible(a, i) && tiles(i) >= 240)
             return i;
-        const double f = (tg::async_tile_m(i) == 256 ? 1.0 : 0.8) * fill(t);
-        if (2 * t >= cus && f > best_fill) {
-            best16 = i;
-            best_fill = f;
+    int best = -1, best_s = 1;
+    double best_t = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (tg::async_forced_only(i) || !tg::async_eligible(a, i))
+            continue;
+        if (a.K % 128 != 0 && (!tg::async_mfma16(i) || 2 * tiles(i) < cus))
+            continue;
+        const int s = splits ? model_splits(a, i, cus) : 1;
+        const double t = wave_cost_us(a, i, s, cus);
+        if (t >= 0.0 && (best < 0 || t < best_t)) {
+            best = i;
+            best_s = s;
+            best_t = t;
         }
     }
-    if (best16 >= 0)
-        return best16;
-    int best = -1;
-    for (int i = 0; i < n; ++i) {
-        if (tg::async_forced_only(i) || tg::async_mfma16(i) || !tg::async_eligible(a, i))
-            continue;
-        if (tiles(i) >= 240)
-            return i;
-        best = i;
-    }
-    // K off the 128 grid (masked on the 16x16x32 tiles only): without half a
-    // wave of those tiles, K padding or the tiled kernel does better
-    if (a.K % 128 != 0)
-        return -1;
+    if (splits)
+        *splits = best_s;
     return best;
 }
 
@@ -327,11 +384,13 @@ bool kpad_eligible(const tg::GemmArgs &a, const char *force)
     a2.K = K2;
     a2.lda = a2.K;
     a2.ldb = a.b_trans ? a2.K : round_up_dim(a.N, 8);
-    const int cfg = choose_async(a2, nullptr);
-    if (cfg < 0)
+    if (choose_async(a2, nullptr) < 0)
         return false;
-    const int64_t tiles = (int64_t)tg::async_tiles_m(a2, cfg) * tg::async_tiles_n(a2, cfg);
-    return tiles >= 240;
+    for (int i = 0; i < tg::num_async_configs(); ++i)
+        if (!tg::async_forced_only(i) && tg::async_eligible(a2, i) &&
+            (int64_t)tg::async_tiles_m(a2, i) * tg::async_tiles_n(a2, i) >= 240)
+            return true;
+    return false;
 }
 
 // Operands off the 16-byte grid (a pitch that is not a multiple of 8
@@ -794,20 +853,18 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
                  pl.k_chunk, pl.mb == 2 ? "_m32" : "");
         set_last("skinny", detail);
     } else if ((!force_tiled || b_trans) && choose_async(a, force) >= 0) {
-        const int cfg = choose_async(a, force);
+        int auto_splits = 1;
+        const int cfg = choose_async(a, force, &auto_splits);
         const int group_m = env_int("TG_GROUP_M", 4);
-        // Split-K over the 32x32x16-MFMA tiles: automatic for K >= 2048 (up
-        // to one wave of workgroups from grids of at most 128 tiles: 64 x
-        // 4096 x 4096 runs 13.7 us in four splits against 20.3 unsplit,
-        // 128 x 4096 x 14336 37.8 against 62.2 in two); below that the three
-        // device-scope round trips of the exchange (partial stores, counter,
-        // read-back) cost more than the split saves (256^3, 1024^3).
-        // TG_SPLITK=0: automatic at any K, n: n splits, 1: never.  An
-        // automatic split whose workspace cannot be had (a capture that would
+        // Split-K over the 32x32x16-MFMA tiles: the count the launch-time
+        // model took with the configuration (64 x 4096 x 4096: four splits of
+        // 64 x 64 tiles, 12.2 us against 20.0 unsplit).  TG_SPLITK=n asks
+        // for n splits, 0 for enough to fill one wave, 1 for none.  A
+        // modelled split whose workspace cannot be had (a capture that would
         // grow it, no memory) runs unsplit; a requested one, or one on the
         // allocation-free entry point, launches nothing and says why.
         const bool split_asked = getenv("TG_SPLITK") && *getenv("TG_SPLITK");
-        const int want = split_asked ? env_int("TG_SPLITK", 1) : (K >= 2048 ? 0 : 1);
+        const int want = split_asked ? env_int("TG_SPLITK", 1) : auto_splits;
         int splits = tg::plan_async_splits(a, cfg, want);
         float *ws = nullptr;
         int *counters = nullptr;
@@ -1173,6 +1230,8 @@ int tg_lds_swizzle(int layout, int64_t row)
         return tg::swz_b16(r);
     case 4:
         return tg::swz_b192(r);
+    case 5:
+        return tg::swz_b128(r);
     default:
         return -1;
     }

@@ -41,6 +41,13 @@ __host__ __device__ constexpr int swz_b16(int r) { return swz_b<256>(r) ^ (2 * (
 // its aligned group of eight, so it stays inside the 24-granule row.
 __host__ __device__ constexpr int swz_b192(int r) { return (r & 2) | ((r >> 1) & 4); }
 
+// B swizzle of the 128 x 128 16x16x32 kernel (256-byte rows: every row spans
+// the whole bank window from bank 0).  A transposing read pass covers one
+// granule pair of rows a .. a + 3 and a + 8 .. a + 11; giving those eight
+// rows the eight distinct even XOR values 2 (r % 4) + 8 (bit 3 of r) puts
+// the eight pairs on disjoint banks, and an even XOR keeps each pair whole.
+__host__ __device__ constexpr int swz_b128(int r) { return ((r & 3) << 1) | (r & 8); }
+
 // Epilogue of one wave holding TI x TJ 32x32 FP32 accumulator blocks (the
 // bias already inside).  Lane l of block (i, j) holds row 32 i + l % 32 and
 // columns 32 j + 8 g + 4 (l / 32) + {0..3} in registers 4g..4g+3.  The
