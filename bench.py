@@ -573,8 +573,9 @@ def run_sweep(torch, tg):
     (A, B = U[-1,1]/8, no epilogue; up to 2048^3 both sides replayed from
     captured graphs of 50 launches), bf16 products with M = 1..32
     (W ~ N(0, 1/K) rotated over enough copies to exceed 1 GiB; also W stored
-    [N,K], and W on an odd pitch), token counts off the 64 grid and square
-    shapes with B in either layout, and bf16 shapes off the tile grid (X ~
+    [N,K], and W on an odd pitch), token counts off the 64 grid, medium
+    token counts and square shapes with B in either layout, and bf16 shapes
+    off the tile grid (X ~
     N(0,1), W ~ N(0, 1/K)): token counts that
     leave a partial last tile, grids short of a wave of 256 x 256 tiles,
     pitches off the 8-element grid, and square sizes whose K is not a
@@ -675,8 +676,12 @@ def run_sweep(torch, tg):
                           "ms": round(ms, 5), "GB/s": round(nb / ms / 1e6), "kernel": kern,
                           "library_GB/s": round(nb / ml / 1e6)}), flush=True)
         del X, W, Y
-    # token counts off the 64 grid and square shapes, both B layouts
+    # token counts off the 64 grid, medium token counts (grids short of a
+    # wave of 256 x 256 tiles: tile and split count from the launch-time
+    # model) and square shapes, both B layouts
     for (M, N, K) in ((48, 4096, 4096), (100, 4096, 4096), (200, 4096, 4096),
+                      (128, 4096, 14336), (384, 4096, 14336), (256, 14336, 4096),
+                      (640, 14336, 4096), (1024, 4096, 4096), (1024, 8192, 8192),
                       (4096, 4096, 4096), (8192, 8192, 8192)):
         for trans in (False, True):
             X = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")

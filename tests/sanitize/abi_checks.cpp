@@ -41,7 +41,7 @@ bool async_forced_only(int) { reached("async_forced_only"); }
 bool async_mfma16(int) { reached("async_mfma16"); }
 int async_tile_m(int) { reached("async_tile_m"); }
 int async_tile_n(int) { reached("async_tile_n"); }
-bool async_eligible(const GemmArgs &, int) { reached("async_eligible"); }
+bool async_eligible(const GemmArgs &, int, bool) { reached("async_eligible"); }
 int async_tiles_m(const GemmArgs &, int) { reached("async_tiles_m"); }
 int async_tiles_n(const GemmArgs &, int) { reached("async_tiles_n"); }
 int plan_async_splits(const GemmArgs &, int, int) { reached("plan_async_splits"); }

@@ -96,7 +96,7 @@ MEDIUM_M_SPLIT_CASES = [
     # launch-time model takes)
     (F16, 64, 4096, 4096, False, 4),
     (BF16, 128, 2048, 2048, False, 4),
-    (F16, 96, 1000, 3072, False, 8),     # partial last row and column tiles
+    (F16, 96, 1000, 3072, False, 6),     # partial last row and column tiles
     (BF16, 64, 2048, 4096, True, None),  # B stored [N,K]
 ]
 

@@ -1178,7 +1178,7 @@ static bool async_k_ok(int K, bool masked_ok)
     return K > 0 && (K % Q == 0 || (masked_ok && K % 8 == 0 && (K + Q - 1) / Q * Q - K <= K));
 }
 
-bool async_eligible(const GemmArgs &a, int cfg)
+bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
 {
     // An M (or an N that is a multiple of 8) that is not a multiple of the
     // tile is taken when the partial last row (column) tile wastes at most
@@ -1188,12 +1188,14 @@ bool async_eligible(const GemmArgs &a, int cfg)
     // exact, and for such shapes the kernels left (element-wise loads, or
     // none for B stored [N,K]) are several times slower than the idle rows
     // of one tile cost.
+    // any_pad drops the M / 8 bound (the tiles stay exact; the caller weighs
+    // the idle rows and columns itself).
     const int tm = async_tile_m(cfg), tn = async_tile_n(cfg);
     const int pad = async_tiles_m(a, cfg) * tm - a.M;
-    const bool m_ok = a.M % tm == 0 || tm == 64 || (a.M > tm && 8 * pad <= a.M);
+    const bool m_ok = any_pad || a.M % tm == 0 || tm == 64 || (a.M > tm && 8 * pad <= a.M);
     const int padn = async_tiles_n(a, cfg) * tn - a.N;
-    const bool n_ok =
-        a.N % tn == 0 || (a.N % 8 == 0 && (tn == 64 || (a.N > tn && 8 * padn <= a.N)));
+    const bool n_ok = a.N % tn == 0 ||
+                      (a.N % 8 == 0 && (any_pad || tn == 64 || (a.N > tn && 8 * padn <= a.N)));
     return m_ok && n_ok &&
            async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0) && ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;

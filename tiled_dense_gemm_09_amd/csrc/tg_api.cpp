@@ -255,32 +255,35 @@ int choose_config(int64_t M, int64_t N, int n_mat)
 // full wave of 256 x 256 tiles.  A configuration with s K splits runs
 // n = ceil(tiles s / CUs) workgroups per CU; it costs
 //     a + b (K / s) (1 + r (n - 1))                      [us, K in thousands]
-// plus, split, e + h (partial bytes s M N 8, in MB: written once, read once),
-// and never less than the compulsory HBM traffic (A, B and C once) at bw.
-// Per workgroup the K loop is latency-bound: a 64 x 64 tile takes 3.9 us per
-// thousand k against 6.9 for 128 x 128, four times the work, so the larger
-// tile wins wherever it still fills the chip, and split-K buys back the
-// waves that a small grid leaves idle.  The coefficients are a least-squares
-// fit (relative error) of 3380 launches timed back to back on MI355X: bf16,
-// B in both layouts, M 64..2048 over 13 (N, K) pairs from 1024 to 14336, every
-// configuration with 1, 2, 4 and 8 splits; 11% rms error, and the choice it
-// makes lands within 1% of the fastest measured launch summed over the 260
-// shapes (largest single loss 19%).
+// plus, split, e + h (partial bytes s M N 8, in MB: written once, read once)
+// + h2 (bytes s TM TN 4 of one tile's partials, in MB: the workgroup that
+// completes a tile reads them all on its own), and never less than the
+// compulsory HBM traffic (A, B and C once) at bw.  Per workgroup the K loop
+// is latency-bound: a 64 x 64 tile takes 3.9 us per thousand k against 7.1
+// for 128 x 128, four times the work, so the larger tile wins wherever it
+// still fills the chip, and split-K buys back the waves that a small grid
+// leaves idle.  The coefficients are a least-squares fit (relative error) of
+// 3380 launches timed back to back on MI355X: bf16, B in both layouts, M
+// 64..2048 over 13 (N, K) pairs from 1024 to 14336, every configuration
+// with 1, 2, 4 and 8 splits; 10% rms error.  Its choice lands within 0.7% of
+// the fastest measured launch summed over those 260 shapes, and within 0.6%
+// over 84 others it was not fitted on (M 96..3072, 7 more (N, K) pairs).
 struct WaveCost {
     int tm, tn;
     bool m16;
     double a, b, r, e;
 };
 constexpr WaveCost kWaveCost[] = {
-    {64, 64, false, 1.71, 3.86, 1.03, 2.92},    {64, 128, false, 1.93, 4.95, 1.26, 3.19},
-    {128, 128, false, 2.21, 6.86, 1.36, 4.21},  {192, 192, true, 6.72, 11.89, 1.42, 0.0},
-    {256, 256, false, 8.20, 16.49, 1.50, 0.0},  {256, 256, true, 8.24, 18.59, 1.50, 0.0},
+    {64, 64, false, 1.59, 3.87, 1.03, 2.27},    {64, 128, false, 1.67, 5.04, 1.24, 1.84},
+    {128, 128, false, 1.73, 7.08, 1.32, 1.56},  {192, 192, true, 6.65, 11.77, 1.42, 0.0},
+    {256, 256, false, 8.12, 16.32, 1.50, 0.0},  {256, 256, true, 8.16, 18.41, 1.50, 0.0},
 };
-constexpr double kSplitUsPerMB = 0.148; // partial traffic of a split
-constexpr double kModelHbmBytesPerUs = 4.49e6;
+constexpr double kSplitUsPerMB = 0.139;    // partial traffic of a split, all tiles
+constexpr double kCombineUsPerMB = 10.67;  // one tile's partials, read by one workgroup
+constexpr double kModelHbmBytesPerUs = 4.55e6;
 
-// Modelled microseconds of configuration cfg with s splits; < 0 when the
-// configuration has no coefficients.
+// Modelled microseconds of configuration cfg with s splits (plus a 1 %
+// tie-break); < 0 when the configuration has no coefficients.
 double wave_cost_us(const tg::GemmArgs &a, int cfg, int s, int cus)
 {
     const int tm = tg::async_tile_m(cfg), tn = tg::async_tile_n(cfg);
@@ -292,10 +295,15 @@ double wave_cost_us(const tg::GemmArgs &a, int cfg, int s, int cus)
         const double n = std::ceil(tiles * s / cus);
         double t = w.a + w.b * ((double)a.K / s / 1000.0) * (1.0 + w.r * (n - 1.0));
         if (s > 1)
-            t += w.e + kSplitUsPerMB * s * (double)a.M * a.N * a.n_mat * 8.0 / 1e6;
+            t += w.e + kSplitUsPerMB * s * (double)a.M * a.N * a.n_mat * 8.0 / 1e6 +
+                 kCombineUsPerMB * s * (double)tm * tn * 4.0 / 1e6;
         const double bytes =
             2.0 * ((double)a.M * a.K + (double)a.n_mat * ((double)a.K * a.N + (double)a.M * a.N));
-        return std::max(t, bytes / kModelHbmBytesPerUs);
+        // on the HBM floor the candidates tie: 1 % of the compute time
+        // breaks the tie towards the least work (64 x 4096 x 14336, 119 MB:
+        // four splits of 64 x 64 tiles, 25 us, not seven of half-empty
+        // 128 x 128 tiles, 33 us)
+        return std::max(t, bytes / kModelHbmBytesPerUs) + 0.01 * t;
     }
     return -1.0;
 }
@@ -348,10 +356,13 @@ int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr
         if (!tg::async_forced_only(i) && tg::async_mfma16(i) && tg::async_tile_m(i) == 256 &&
             tg::async_eligible(a, i) && tiles(i) >= 240)
             return i;
+    // Any padding of the last row or column tile is a candidate here: the
+    // model counts the padded tiles (640 x 14336: 168 tiles of 256 x 256,
+    // the last row half empty, against 560 of 128 x 128).
     int best = -1, best_s = 1;
     double best_t = 0.0;
     for (int i = 0; i < n; ++i) {
-        if (tg::async_forced_only(i) || !tg::async_eligible(a, i))
+        if (tg::async_forced_only(i) || !tg::async_eligible(a, i, true))
             continue;
         if (a.K % 128 != 0 && (!tg::async_mfma16(i) || 2 * tiles(i) < cus))
             continue;

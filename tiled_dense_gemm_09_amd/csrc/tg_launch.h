@@ -55,11 +55,11 @@ int num_async_configs();
 const char *async_config_name(int cfg);
 // taken only when TG_FORCE_CONFIG names it
 bool async_forced_only(int cfg);
-// true for the configurations on the 16x16x32 MFMA (256 x 256 and 192 x 192 tiles)
+// true for the configurations on the 16x16x32 MFMA (256 x 256, 192 x 192 and 128 x 128 tiles)
 bool async_mfma16(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
-bool async_eligible(const GemmArgs &a, int cfg);
+bool async_eligible(const GemmArgs &a, int cfg, bool any_pad = false);
 // Row and column tiles of a problem: the ceilings of M / tile height and
 // N / tile width (a partial last tile counts as a tile).
 int async_tiles_m(const GemmArgs &a, int cfg);
