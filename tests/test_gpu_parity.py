@@ -1253,14 +1253,16 @@ def test_k_dispatch_off_the_grids(tg):
     # masked loop (120 padded k, fewer than K); K = 36: 92 padded k would be
     # more than K, the tiled kernel; K = 1004 (off the 8-element grid, 20
     # padded k): K padding; K = 524 (116 padded k, more than K / 8): the tiled
-    # kernel.  1536 x 2048 outputs (48 tiles, under a wave): K = 1000 is
-    # padded instead of masked
+    # kernel.  1536 x 2048 outputs (48 tiles of 256 x 256, 192 of 128 x
+    # 128): K = 1000 masked on the 128 x 128 16x16x32 tiles; 768 x 2048 (96
+    # of them, under half a wave): K = 1000 padded instead
     import torch
     for (M, N), K, ld, expect in (((4096, 4096), 520, 520, "async_256x256x32_s4_mfma16"),
                                   ((4096, 4096), 36, 40, "tiled_"),
                                   ((4096, 4096), 1004, 1008, "_kpad"),
                                   ((4096, 4096), 524, 528, "tiled_"),
-                                  ((1536, 2048), 1000, 1000, "_kpad")):
+                                  ((1536, 2048), 1000, 1000, "async_128x128x32_s4_mfma16"),
+                                  ((768, 2048), 1000, 1000, "_kpad")):
         a = torch.zeros((M, ld), dtype=torch.float16, device="cuda")[:, :K]
         b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
         tg.gemm(a, b)

@@ -1142,9 +1142,10 @@ const AsyncConfig kAsyncConfigs[] = {
     // 192 x 192 tiles fill a wave where 256 x 256 ones leave much of it idle
     // (3072^2 outputs: 256 tiles against 144)
     {3, 3, 4, false, "async_192x192x32_s4_mfma16"},
-    // as fast as the 32x32x16 128 x 128 tiles (within 3 % over 264 shapes):
-    // at this size the K loop is bound by the latency of its steps
-    {2, 2, 4, true, "async_128x128x32_s4_mfma16"},
+    // as fast as the 32x32x16 128 x 128 tiles (within 3 % over 264 shapes:
+    // at this size the K loop is bound by the latency of its steps), and
+    // unlike them it masks K off the 128 grid in the kernel
+    {2, 2, 4, false, "async_128x128x32_s4_mfma16"},
     {4, 4, 0, false, "async_256x256x32_s4"},
     {2, 2, 0, false, "async_128x128x32_s4"},
     {1, 2, 0, false, "async_64x128x32_s4"},

@@ -277,6 +277,10 @@ constexpr WaveCost kWaveCost[] = {
     {64, 64, false, 1.59, 3.87, 1.03, 2.27},    {64, 128, false, 1.67, 5.04, 1.24, 1.84},
     {128, 128, false, 1.73, 7.08, 1.32, 1.56},  {192, 192, true, 6.65, 11.77, 1.42, 0.0},
     {256, 256, false, 8.12, 16.32, 1.50, 0.0},  {256, 256, true, 8.16, 18.41, 1.50, 0.0},
+    // the 16x16x32 128 x 128 tiles: timed like the 32x32x16 ones, 1 % dearer
+    // so that those (which can split K) keep the shapes both can take; for K
+    // off the 128 grid only the 16x16x32 tiles are candidates
+    {128, 128, true, 1.75, 7.15, 1.32, 0.0},
 };
 constexpr double kSplitUsPerMB = 0.139;    // partial traffic of a split, all tiles
 constexpr double kCombineUsPerMB = 10.67;  // one tile's partials, read by one workgroup
