@@ -288,7 +288,8 @@ int64_t tg_lds_offset(int64_t cols, int64_t row, int64_t col);
  * [K,N], 64-column (128-byte) rows; 3: B stored [K,N] in the 256 x 256
  * kernel on the 16x16x32 MFMA (512-byte rows); 4: B stored [K,N] in the
  * 192 x 192 kernel on the 16x16x32 MFMA (384-byte rows); 5: B stored [K,N]
- * in the 128 x 128 kernel on the 16x16x32 MFMA (256-byte rows).  Returns -1
+ * in the 128 x 128 kernel on the 16x16x32 MFMA (256-byte rows); 6: A (and
+ * B stored [N,K]) in 64-deep K steps, 128-byte rows of 64 k.  Returns -1
  * for an unknown layout or a negative row. */
 int tg_lds_swizzle(int layout, int64_t row);
 

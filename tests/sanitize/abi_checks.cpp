@@ -41,6 +41,7 @@ bool async_forced_only(int) { reached("async_forced_only"); }
 bool async_mfma16(int) { reached("async_mfma16"); }
 int async_tile_m(int) { reached("async_tile_m"); }
 int async_tile_n(int) { reached("async_tile_n"); }
+int async_k_step(int) { reached("async_k_step"); }
 bool async_eligible(const GemmArgs &, int, bool) { reached("async_eligible"); }
 int async_tiles_m(const GemmArgs &, int) { reached("async_tiles_m"); }
 int async_tiles_n(const GemmArgs &, int) { reached("async_tiles_n"); }
@@ -250,7 +251,7 @@ int main()
     EXPECT(tg_schedule_tile(1 << 20, 1 << 20, 3, 4, 5, &mat, &tm, &tn) == -1);
     EXPECT(tg_schedule_tile(4, 4, 1, HUGE_, 3, &mat, &tm, &tn) == -1 ||
            (tm >= 0 && tm < 4 && tn >= 0 && tn < 4));
-    for (int layout = -1; layout < 7; ++layout)
+    for (int layout = -1; layout < 8; ++layout)
         for (int64_t r : {(int64_t)-1, (int64_t)0, (int64_t)5, (int64_t)1 << 40, HUGE_})
             EXPECT(tg_lds_swizzle(layout, r) >= -1);
     for (int64_t cols : {8, 64, 128, 256})

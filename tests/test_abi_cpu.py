@@ -304,7 +304,7 @@ def _b16_lanes(q0, h, col0):
 
 
 @pytest.mark.parametrize("layout,granules", [(0, 4), (1, 16), (1, 32), (2, 8), (3, 32), (4, 24),
-                                             (5, 16)])
+                                             (5, 16), (6, 8)])
 def test_swizzles_permute_each_row(layout, granules):
     for r in range(64):
         s = _swz(layout, r)
@@ -355,10 +355,23 @@ def test_b_transposing_reads_192_tile_kernel_are_bank_conflict_free():
     assert _max_bank_load(_b_pass(4, 384, rows, cols, swizzle=False)) > 1  # control
 
 
+def test_a_fragment_reads_of_64_deep_steps_are_bank_conflict_free():
+    # 128-byte rows (64 k): 16 lanes read granule g of rows base .. base + 15
+    for base in range(0, 256, 16):
+        for gran in range(8):
+            pieces = [((base + i) * 128 + 16 * (gran ^ _swz(6, base + i)), 16) for i in range(16)]
+            assert _max_bank_load(pieces) == 1
+    control = [((i) * 128 + 16 * 0, 16) for i in range(16)]
+    assert _max_bank_load(control) == 8
+    # the 64-byte-row swizzle does not cover 128-byte rows
+    assert _max_bank_load([(i * 128 + 16 * (0 ^ _swz(0, i)), 16) for i in range(16)]) > 1
+
+
 def test_b_transposing_reads_128_tile_kernel_are_bank_conflict_free():
     # 256-byte rows (128 columns): every 16-column fragment of either wave
-    # column, both halves, both 32-lane passes
-    for q0 in (0, 2):
+    # column, both halves, both 32-lane passes, k rows 0..63 (the second
+    # 32-deep slice of a 64-deep step starts at row 32)
+    for q0 in (0, 2, 4, 6):
         for h in range(2):
             for col0 in range(0, 128, 16):
                 rows, cols = _b16_lanes(q0, h, col0)

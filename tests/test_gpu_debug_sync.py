@@ -110,6 +110,8 @@ CASES = [
      gemm_case(576, 768, 1000, bt=True, residual=True), "async_192x192x32_s4_mfma16"),
     ("async16_128_bt_kmask", {"TG_FORCE_CONFIG": "async_128x128x32_s4_mfma16"},
      gemm_case(384, 512, 1000, bt=True, residual=True), "async_128x128x32_s4_mfma16"),
+    ("async16_128k64_kmask", {"TG_FORCE_CONFIG": "async_128x128x64_s4_mfma16"},
+     gemm_case(384, 512, 1000, residual=True), "async_128x128x64_s4_mfma16"),
     ("async16_w8", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16_w8"},
      gemm_case(512, 512, 1024), "async_256x256x32_s4_mfma16_w8"),
     ("async32_256", {"TG_FORCE_CONFIG": "async_256x256x32_s4"},

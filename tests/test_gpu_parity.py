@@ -852,8 +852,9 @@ def test_k_zero_gives_activated_bias(tg):
 # ------------------------------------------------- async tile configurations
 
 ASYNC_CONFIGS = ["async_256x256x32_s4_mfma16_w8", "async_256x256x32_s4_mfma16",
-                 "async_128x128x32_s4_mfma16", "async_256x256x32_s4", "async_128x128x32_s4",
-                 "async_64x128x32_s4", "async_64x64x32_s4"]
+                 "async_128x128x32_s4_mfma16", "async_128x128x64_s4_mfma16",
+                 "async_256x256x32_s4", "async_128x128x32_s4", "async_64x128x32_s4",
+                 "async_64x64x32_s4"]
 
 
 @pytest.mark.parametrize("cfg", ASYNC_CONFIGS)
@@ -914,8 +915,8 @@ def test_192_tiles_chosen_for_3072_outputs(tg):
     # compared with the oracle
     import torch
     dt = BF16
-    p = inputs.problem(dt, 3072, 3072, 512, seed=74, kind="int", bias=True, bias_kind="int")
-    say("case 192 x 192 tiles chosen, 3072x3072x512")
+    p = inputs.problem(dt, 3072, 3072, 1024, seed=74, kind="int", bias=True, bias_kind="int")
+    say("case 192 x 192 tiles chosen, 3072x3072x1024")
     bits, kern = run(tg, p)
     assert kern == "async_192x192x32_s4_mfma16", kern
     _, ref = oracle.gemm(dt, p["A"], p["B"], p["bias"])
@@ -1090,6 +1091,7 @@ RAGGED_M_CASES = [
     # 128 x 128 tiles: a last row tile of 76 rows (the second wave row holds
     # 12)
     (BF16, 1100, 384, 256, "async_128x128x32_s4_mfma16"),
+    (F16, 1100, 384, 512, "async_128x128x64_s4_mfma16"),
     # the 32x32x16 kernel: last row tiles of 152, 104, 24 and 30 rows
     (BF16, 2200, 256, 256, "async_256x256x32_s4"),
     (F16, 1000, 384, 256, "async_128x128x32_s4"),
@@ -1130,6 +1132,7 @@ RAGGED_N_CASES = [
     (F16, 512, 2000, 256, "async_256x256x32_s4_mfma16"),
     (BF16, 384, 1096, 256, "async_192x192x32_s4_mfma16"),
     (F16, 256, 1000, 256, "async_128x128x32_s4_mfma16"),
+    (BF16, 384, 1000, 512, "async_128x128x64_s4_mfma16"),
     (BF16, 256, 2200, 384, "async_256x256x32_s4"),
     (F16, 256, 1000, 256, "async_128x128x32_s4"),
     (BF16, 192, 600, 512, "async_64x128x32_s4"),
@@ -1197,6 +1200,10 @@ KMASK_CASES = [
     (BF16, 768, 512, 4040, "async_256x256x32_s4_mfma16"),
     (F16, 576, 576, 200, "async_192x192x32_s4_mfma16"),
     (BF16, 384, 384, 200, "async_128x128x32_s4_mfma16"),
+    # 64-deep steps: K below one quad of 256 (the masked quad alone), and
+    # two whole quads plus a masked one
+    (F16, 384, 384, 200, "async_128x128x64_s4_mfma16"),
+    (BF16, 256, 512, 1000, "async_128x128x64_s4_mfma16"),
 ]
 
 
@@ -1358,6 +1365,7 @@ EX_SHAPES = [
     (F16, 512, 512, 512, "async_256x256x32_s4_mfma16_w8"),
     (F16, 384, 576, 256, "async_192x192x32_s4_mfma16"),
     (BF16, 384, 256, 384, "async_128x128x32_s4_mfma16"),
+    (F16, 256, 384, 768, "async_128x128x64_s4_mfma16"),
     (BF16, 256, 384, 256, "async_128x128x32_s4"),
     (F16, 192, 256, 512, "async_64x128x32_s4"),
     (BF16, 192, 320, 384, "async_64x64x32_s4"),   # N a multiple of 64, not of 128

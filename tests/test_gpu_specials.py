@@ -80,6 +80,10 @@ FAMILIES = [
      False, "async_128x128x32_s4_mfma16"),
     ("async16_128_bt", {"TG_FORCE_CONFIG": "async_128x128x32_s4_mfma16"}, BF16, 384, 256, 384,
      True, "async_128x128x32_s4_mfma16"),
+    ("async16_128k64", {"TG_FORCE_CONFIG": "async_128x128x64_s4_mfma16"}, F16, 256, 384, 512,
+     False, "async_128x128x64_s4_mfma16"),
+    ("async16_128k64_bt", {"TG_FORCE_CONFIG": "async_128x128x64_s4_mfma16"}, BF16, 384, 256, 768,
+     True, "async_128x128x64_s4_mfma16"),
     ("async32_256", {"TG_FORCE_CONFIG": "async_256x256x32_s4"}, BF16, 512, 512, 256, False,
      "async_256x256x32_s4"),
     ("async32_128", {"TG_FORCE_CONFIG": "async_128x128x32_s4"}, F16, 256, 256, 256, False,

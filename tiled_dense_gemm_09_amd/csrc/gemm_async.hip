@@ -527,13 +527,16 @@ __global__ __launch_bounds__(AS_NT, TI * TJ >= 16 ? 1 : 2) void gemm_async_kerne
 namespace {
 
 // Tiles of the 16x16x32 kernels: TM x TM outputs (256; 192 or 128 for sizes
-// whose 256 x 256 tiles would leave most of a wave idle), K steps of 32.
-// A stage holds A [TM][32] K-contiguous, then B [32][TM] N-contiguous (or,
-// stored [N,K], [TM][32] like A).
-template <int TM>
+// whose 256 x 256 tiles would leave most of a wave idle), K steps of KB = 32
+// (or 64 on the 128 x 128 tiles: twice the MFMAs per step and per barrier,
+// and every copy moves whole 128-byte row pieces).  A stage holds A [TM][KB]
+// K-contiguous, then B [KB][TM] N-contiguous (or, stored [N,K], [TM][KB]
+// like A).
+template <int TM, int KB = 32>
 struct A16Tile {
     static_assert(TM == 256 || TM == 192 || TM == 128, "16x16x32 tile sizes");
-    static constexpr int A_BYTES = TM * AS_BK * 2;
+    static_assert(KB == 32 || (KB == 64 && TM == 128), "K step");
+    static constexpr int A_BYTES = TM * KB * 2;
     static constexpr int STAGE = 2 * A_BYTES;
 };
 constexpr int A16_BM = 256, A16_BN = 256; // the stream-K kernel's tiles
@@ -541,18 +544,21 @@ constexpr int A16_STAGE = A16Tile<256>::STAGE;
 
 // WN x 2 waves; each wave owns (TM / 2) x (TM / WN) outputs: MI x NJ blocks
 // of 16 x 16.
-template <int WN, bool BT, int TM = 256>
+template <int WN, bool BT, int TM = 256, int KB = 32>
 struct A16Geom {
     static_assert(WN == 2 || (WN == 4 && TM == 256), "waves along N");
     static constexpr int NW = 2 * WN;               // waves
     static constexpr int NT = 64 * NW;              // lanes
+    static constexpr int KH = KB / 32;              // 32-deep MFMA k slices per step
     static constexpr int MI = TM / 32;              // 16-row blocks per wave
     static constexpr int NJ = TM / 16 / WN;         // 16-column blocks per wave
     static constexpr int WROWS = 16 * MI;           // rows per wave
     static constexpr int WCOLS = 16 * NJ;           // columns per wave
-    static constexpr int CA = TM / 16 / NW;         // A copies of 1 KiB per wave per step
+    static constexpr int CA = TM * KB / 512 / NW;   // A copies of 1 KiB per wave per step
     static constexpr int COPIES = 2 * CA;           // + as many B copies
-    static constexpr int READS = MI + (BT ? NJ : 2 * NJ); // A reads + B reads (2 transposing each)
+    // A reads + B reads (2 transposing each) per k slice
+    static constexpr int R1 = MI + (BT ? NJ : 2 * NJ);
+    static constexpr int READS = KH * R1;
     static constexpr int G = 2 * NJ;                // epilogue granules per wave-tile row
     static constexpr int EP_BYTES = WROWS * 16 * G; // wave tile restaged in LDS
 };
@@ -639,15 +645,21 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[MI][NJ], 
 // of the product with the weight Bm, accumulated into acc (which the caller
 // has initialised).  On return every copy has landed and every wave has
 // finished reading the stages, so the LDS is free.
-template <int DT, int WN, bool BT, bool KM, int TM = 256>
+template <int DT, int WN, bool BT, bool KM, int TM = 256, int KB = 32>
 __device__ __forceinline__ void a16_mainloop(
     const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int kt0, int KT, int wave,
     int lane, unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
-    f32x4 (&acc)[A16Geom<WN, BT, TM>::MI][A16Geom<WN, BT, TM>::NJ])
+    f32x4 (&acc)[A16Geom<WN, BT, TM, KB>::MI][A16Geom<WN, BT, TM, KB>::NJ])
 {
-    using Gm = A16Geom<WN, BT, TM>;
-    constexpr int MI = Gm::MI, NJ = Gm::NJ, CA = Gm::CA;
-    constexpr int A_BYTES = A16Tile<TM>::A_BYTES;
+    using Gm = A16Geom<WN, BT, TM, KB>;
+    constexpr int MI = Gm::MI, NJ = Gm::NJ, CA = Gm::CA, KH = Gm::KH;
+    constexpr int A_BYTES = A16Tile<TM, KB>::A_BYTES;
+    // A (and B stored [N,K]) rows of KB k: 64 bytes (4 granules, swizzle
+    // swz_a) or 128 bytes (8 granules, swz_a8); one 1 KiB copy fills 16 or
+    // 8 rows
+    constexpr int RG = KB / 8;                 // granules per row
+    constexpr int RPC = 64 / RG;               // rows per copy
+    auto swz_row = [](int r) { return KB == 32 ? swz_a(r) : swz_a8(r); };
     auto stage = [&](auto sidx) -> unsigned char * {
         constexpr int S = decltype(sidx)::value;
         if constexpr (S == 0)
@@ -662,14 +674,14 @@ __device__ __forceinline__ void a16_mainloop(
     const int wave_n = wave % WN;
     const int wave_m = wave / WN;
 
-    // copy c < CA: A copy q = CA w + c, rows 16 q .. 16 q + 15 (lane -> row
-    // 16 q + lane / 4, granule lane % 4); c >= CA: B copy q = CA w + c - CA,
-    // bytes 1024 q .. 1024 q + 1023 of [32][TM] (lane -> byte 1024 q + 16
-    // lane: row rb of 2 TM bytes, granule gb; at TM = 256 rows 2 q + lane /
-    // 32, granule lane % 32).  B stored [N,K] (BT) is staged like A:
-    // [TM n][32 k] K-contiguous, B copy q filling n-rows 16 q .. 16 q + 15
-    // with the A swizzle.
-    const int64_t b_step = BT ? (int64_t)AS_BK : (int64_t)AS_BK * p.ldb;
+    // copy c < CA: A copy q = CA w + c, rows RPC q .. RPC q + RPC - 1 (lane
+    // -> row RPC q + lane / RG, granule lane % RG); c >= CA: B copy q = CA w
+    // + c - CA, bytes 1024 q .. 1024 q + 1023 of [KB][TM] (lane -> byte 1024
+    // q + 16 lane: row rb of 2 TM bytes, granule gb; at TM = 256 rows 2 q +
+    // lane / 32, granule lane % 32).  B stored [N,K] (BT) is staged like A:
+    // [TM n][KB k] K-contiguous, B copy q filling n-rows RPC q .. RPC q +
+    // RPC - 1 with the A swizzle.
+    const int64_t b_step = BT ? (int64_t)KB : (int64_t)KB * p.ldb;
     // KM: copy c of step kt is inside K iff kt * 32 < a_kl[c] (b_kl[c])
     const unsigned short *ga[CA], *gb[CA];
     int a_kl[CA], b_kl[CA];
@@ -677,29 +689,29 @@ __device__ __forceinline__ void a16_mainloop(
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
         const int q = wave * CA + c;
-        const int ra = 16 * q + (lane >> 2);
-        const int ka = ((lane & 3) ^ swz_a(ra)) * 8;
+        const int ra = RPC * q + lane / RG;
+        const int ka = ((lane % RG) ^ swz_row(ra)) * 8;
         // rows past M (a last row tile that M does not fill) read row M-1:
         // every copy stays inside A, and those rows only reach outputs that
         // are never stored
-        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ka + (int64_t)kt0 * AS_BK;
-        a_kl[c] = p.K - kt0 * AS_BK - ka;
+        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ka + (int64_t)kt0 * KB;
+        a_kl[c] = p.K - kt0 * KB - ka;
         if constexpr (BT) {
-            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ka + (int64_t)kt0 * AS_BK;
+            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ka + (int64_t)kt0 * KB;
             b_kl[c] = a_kl[c];
         } else {
             if constexpr (TM == 256) {
                 const int rb = 2 * q + (lane >> 5);
                 gb[c] = Bm + (int64_t)rb * p.ldb +
                         min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) + (int64_t)kt0 * b_step;
-                b_kl[c] = p.K - kt0 * AS_BK - rb;
+                b_kl[c] = p.K - kt0 * KB - rb;
             } else {
                 const unsigned byte = 1024u * q + 16u * lane;
                 const int rb = (int)(byte / (2 * TM));
                 const int gb0 = (int)(byte % (2 * TM) / 16) ^ (TM == 192 ? swz_b192(rb) : swz_b128(rb));
                 gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + gb0 * 8, p.N - 8) +
                         (int64_t)kt0 * b_step;
-                b_kl[c] = p.K - kt0 * AS_BK - rb;
+                b_kl[c] = p.K - kt0 * KB - rb;
             }
         }
     }
@@ -707,15 +719,15 @@ __device__ __forceinline__ void a16_mainloop(
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
         if (c < CA) {
             const unsigned dst = lds + (wave * CA + c) * 1024;
-            const unsigned short *src = ga[c] + kt * AS_BK;
+            const unsigned short *src = ga[c] + kt * KB;
             if constexpr (KM)
-                src = kt * AS_BK < a_kl[c] ? src : zero;
+                src = kt * KB < a_kl[c] ? src : zero;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         } else {
             const unsigned dst = lds + A_BYTES + (wave * CA + c - CA) * 1024;
             const unsigned short *src = gb[c - CA] + kt * b_step;
             if constexpr (KM)
-                src = kt * AS_BK < b_kl[c - CA] ? src : zero;
+                src = kt * KB < b_kl[c - CA] ? src : zero;
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
         }
     };
@@ -725,57 +737,67 @@ __device__ __forceinline__ void a16_mainloop(
             copy(kt, st, c);
     };
 
-    // fragment offsets within a stage
+    // fragment offsets within a stage, per 32-deep k slice s: A row r, k
+    // granule 4 s + l / 16
     const int q16 = lane >> 4;
-    int a_off[MI];
+    int a_off[KH][MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int r = wave_m * Gm::WROWS + 16 * i + (lane & 15);
-        a_off[i] = r * 64 + ((q16 ^ swz_a(r)) * 16);
-    }
-    // B fragment j: transposing reads of [32 k][TM n] (two per fragment), or
-    // for BT one 128-bit read of n-row wave_n WCOLS + 16 j + l % 16, k
-    // granule l / 16 of [TM n][32 k] (b_off[j][0])
-    int b_off[NJ][2];
+    for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int r = wave_m * Gm::WROWS + 16 * i + (lane & 15);
+            a_off[s][i] = r * (2 * KB) + (((4 * s + q16) ^ swz_row(r)) * 16);
+        }
+    // B fragment j: transposing reads of [KB k][TM n] (two per fragment; k
+    // rows 32 s .. 32 s + 31 for slice s), or for BT one 128-bit read of
+    // n-row wave_n WCOLS + 16 j + l % 16, k granule 4 s + l / 16 of [TM n][KB
+    // k] (b_off[s][j][0])
+    int b_off[KH][NJ][2];
     {
         const int jj = lane & 15;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int s = 0; s < KH; ++s)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if constexpr (BT) {
-                    const int r = wave_n * Gm::WCOLS + 16 * j + jj;
-                    b_off[j][h] = A_BYTES + r * 64 + ((q16 ^ swz_a(r)) * 16);
-                } else {
-                    const int r = 8 * q16 + 4 * h + (jj >> 2);
-                    const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
-                    const int sw = TM == 256 ? swz_b16(r) : TM == 192 ? swz_b192(r) : swz_b128(r);
-                    b_off[j][h] = A_BYTES + r * (2 * TM) + (((col >> 3) ^ sw) * 16) + (col & 7) * 2;
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if constexpr (BT) {
+                        const int r = wave_n * Gm::WCOLS + 16 * j + jj;
+                        b_off[s][j][h] =
+                            A_BYTES + r * (2 * KB) + (((4 * s + q16) ^ swz_row(r)) * 16);
+                    } else {
+                        const int r = 32 * s + 8 * q16 + 4 * h + (jj >> 2);
+                        const int col = wave_n * Gm::WCOLS + 16 * j + 4 * (jj & 3);
+                        const int sw =
+                            TM == 256 ? swz_b16(r) : TM == 192 ? swz_b192(r) : swz_b128(r);
+                        b_off[s][j][h] =
+                            A_BYTES + r * (2 * TM) + (((col >> 3) ^ sw) * 16) + (col & 7) * 2;
+                    }
                 }
-            }
     }
 
     struct Frag {
-        u32x4 a[MI], b[NJ];
+        u32x4 a[KH][MI], b[KH][NJ];
     };
-    // read piece q: q < MI is A fragment q, then B fragment (q - MI) / 2,
-    // half (q - MI) % 2 (BT: B fragment q - MI)
+    // read piece q of slice s = q / R1, u = q % R1: u < MI is A fragment u,
+    // then B fragment (u - MI) / 2, half (u - MI) % 2 (BT: B fragment u - MI)
     auto read_piece = [&](Frag &f, const unsigned char *st, int q) {
-        if (q < MI) {
-            f.a[q] = *reinterpret_cast<const u32x4 *>(st + a_off[q]);
+        const int s = q / Gm::R1, u = q % Gm::R1;
+        if (u < MI) {
+            f.a[s][u] = *reinterpret_cast<const u32x4 *>(st + a_off[s][u]);
         } else if constexpr (BT) {
-            f.b[q - MI] = *reinterpret_cast<const u32x4 *>(st + b_off[q - MI][0]);
+            f.b[s][u - MI] = *reinterpret_cast<const u32x4 *>(st + b_off[s][u - MI][0]);
         } else {
-            const int j = (q - MI) >> 1, h = (q - MI) & 1;
+            const int j = (u - MI) >> 1, h = (u - MI) & 1;
             const s16x4 v =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[j][h]));
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st + b_off[s][j][h]));
             const u32x2 w = __builtin_bit_cast(u32x2, v);
-            f.b[j][2 * h] = w[0];
-            f.b[j][2 * h + 1] = w[1];
+            f.b[s][j][2 * h] = w[0];
+            f.b[s][j][2 * h + 1] = w[1];
         }
     };
 
-    constexpr int MT = MI * NJ;       // MFMAs per step
+    constexpr int MT = KH * MI * NJ;  // MFMAs per step
     constexpr int OPS = Gm::READS + Gm::COPIES;
     constexpr int SPAN = MT * 3 / 4;  // MFMAs the reads and copies are spread over
     Frag f0, f1;
@@ -788,8 +810,8 @@ __device__ __forceinline__ void a16_mainloop(
         const int kc = min(kt + 4, KT - 1);
 #pragma unroll
         for (int q = 0; q < MT; ++q) {
-            const int i = q % MI, j = q / MI;
-            acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+            const int s = q / (MI * NJ), i = q % MI, j = q / MI % NJ;
+            acc[i][j] = mfma16x16x32<DT>(fc.b[s][j], fc.a[s][i], acc[i][j]);
             if (q < SPAN) {
                 // ops o0 .. o1-1 after this MFMA; op o is a copy where the
                 // running count of copies (evenly spread) steps up, else a read
@@ -870,7 +892,7 @@ __device__ __forceinline__ void a16_init_acc(
 
 // Epilogue of a 16x16x32 wave tile: each wave restages its tile in its own
 // EP_BYTES of the (idle) stages and stores whole row segments.
-template <int DT, int ACT, int WN, bool BT, int TM = 256>
+template <int DT, int ACT, int WN, bool BT, int TM = 256, int KB = 32>
 __device__ __forceinline__ void a16_epilogue(
     const GemmArgs &p, unsigned short *Cm, int m0, int n0, int wave, int lane,
     unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
@@ -878,7 +900,7 @@ __device__ __forceinline__ void a16_epilogue(
 {
     using Gm = A16Geom<WN, BT, TM>;
     constexpr int MI = Gm::MI, NJ = Gm::NJ;
-    constexpr int PER_STAGE = A16Tile<TM>::STAGE / Gm::EP_BYTES; // wave tiles per stage
+    constexpr int PER_STAGE = A16Tile<TM, KB>::STAGE / Gm::EP_BYTES; // wave tiles per stage
     static_assert(PER_STAGE >= 1 && Gm::NW <= 4 * PER_STAGE, "epilogue fits the stages");
     const int es = wave / PER_STAGE;
     unsigned char *ep = (es == 0 ? st0 : es == 1 ? st1 : es == 2 ? st2 : st3) +
@@ -895,11 +917,11 @@ __device__ __forceinline__ void a16_epilogue(
                                                     cols);
 }
 
-template <int DT, int ACT, int WN, bool BT, bool KM, int TM = 256>
+template <int DT, int ACT, int WN, bool BT, bool KM, int TM = 256, int KB = 32>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
                                                                     int tiles_n, int group_m)
 {
-    constexpr int STAGE = A16Tile<TM>::STAGE;
+    constexpr int STAGE = A16Tile<TM, KB>::STAGE;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
@@ -917,14 +939,14 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     // pipeline fill, but the masking's registers stay out of the main loop,
     // where they made the compiler move the accumulators in and out of the
     // register file)
-    const int KT = (p.K / (AS_STAGES * AS_BK)) * AS_STAGES;
+    const int KT = (p.K / (AS_STAGES * KB)) * AS_STAGES;
     if (!KM || KT > 0)
-        a16_mainloop<DT, WN, BT, false, TM>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2, st3,
-                                            acc);
+        a16_mainloop<DT, WN, BT, false, TM, KB>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2,
+                                                st3, acc);
     if constexpr (KM)
-        a16_mainloop<DT, WN, BT, true, TM>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1,
-                                           st2, st3, acc);
-    a16_epilogue<DT, ACT, WN, BT, TM>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
+        a16_mainloop<DT, WN, BT, true, TM, KB>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1,
+                                               st2, st3, acc);
+    a16_epilogue<DT, ACT, WN, BT, TM, KB>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1133,6 +1155,7 @@ struct AsyncConfig {
     int mfma16; // tiles on the 16x16x32 MFMA with this many waves; 0: 32x32x16
     bool forced_only; // taken only when TG_FORCE_CONFIG names it
     const char *name;
+    int kb = 32;      // k per step of the K loop
 };
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
@@ -1146,6 +1169,10 @@ const AsyncConfig kAsyncConfigs[] = {
     // at this size the K loop is bound by the latency of its steps), and
     // unlike them it masks K off the 128 grid in the kernel
     {2, 2, 4, false, "async_128x128x32_s4_mfma16"},
+    // 64-deep steps: half the barriers and waits per k, whole 128-byte row
+    // pieces per copy (B [N,K] 1024 x 8192 x 8192: 117 against 156 us for the
+    // 32-deep tiles)
+    {2, 2, 4, false, "async_128x128x64_s4_mfma16", 64},
     {4, 4, 0, false, "async_256x256x32_s4"},
     {2, 2, 0, false, "async_128x128x32_s4"},
     {1, 2, 0, false, "async_64x128x32_s4"},
@@ -1159,6 +1186,7 @@ bool async_forced_only(int cfg) { return kAsyncConfigs[cfg].forced_only; }
 bool async_mfma16(int cfg) { return kAsyncConfigs[cfg].mfma16 != 0; }
 int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
 int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
+int async_k_step(int cfg) { return kAsyncConfigs[cfg].kb; }
 
 int async_tiles_m(const GemmArgs &a, int cfg)
 {
@@ -1170,12 +1198,12 @@ int async_tiles_n(const GemmArgs &a, int cfg)
     return (a.N + async_tile_n(cfg) - 1) / async_tile_n(cfg);
 }
 
-// K a multiple of the 128-deep loop; on the 16x16x32 configurations also a
-// multiple of 8 with at most as many padded k as real ones (the masked last
-// quad multiplies zeros for the rest)
-static bool async_k_ok(int K, bool masked_ok)
+// K a multiple of the loop's four steps (Q = 128 k, or 256 with 64-deep
+// steps); on the 16x16x32 configurations also a multiple of 8 with at most
+// as many padded k as real ones (the masked last quad multiplies zeros for
+// the rest)
+static bool async_k_ok(int K, bool masked_ok, int Q)
 {
-    constexpr int Q = AS_STAGES * AS_BK;
     return K > 0 && (K % Q == 0 || (masked_ok && K % 8 == 0 && (K + Q - 1) / Q * Q - K <= K));
 }
 
@@ -1198,7 +1226,8 @@ bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
     const bool n_ok = a.N % tn == 0 ||
                       (a.N % 8 == 0 && (any_pad || tn == 64 || (a.N > tn && 8 * padn <= a.N)));
     return m_ok && n_ok &&
-           async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0) && ((uintptr_t)a.bias & 7u) == 0 &&
+           async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0, AS_STAGES * kAsyncConfigs[cfg].kb) &&
+           ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
 
@@ -1322,7 +1351,7 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                                       ws == nullptr || counters == nullptr)))
         return hipErrorInvalidValue;
     dim3 grid(tiles_m * tiles_n * a.n_mat * splits), block(AS_NT);
-    const bool km = a.K % (AS_STAGES * AS_BK) != 0;
+    const bool km = a.K % (AS_STAGES * kAsyncConfigs[cfg].kb) != 0;
     if (km && splits != 1)
         return hipErrorInvalidValue;
     if (kAsyncConfigs[cfg].mfma16) {
@@ -1331,9 +1360,16 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
         const bool t192 = kAsyncConfigs[cfg].ti == 3, t128 = kAsyncConfigs[cfg].ti == 2;
+        const bool k64 = kAsyncConfigs[cfg].kb == 64;
 #define TG_A16K(DT_, ACT_, KM_)                                                                  \
     do {                                                                                         \
-        if (t128 && a.b_trans)                                                                   \
+        if (t128 && k64 && a.b_trans)                                                            \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 128, 64>), grid,     \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (t128 && k64)                                                                    \
+            hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 128, 64>), grid,    \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+        else if (t128 && a.b_trans)                                                              \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 128>), grid,         \
                                dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
         else if (t128)                                                                           \

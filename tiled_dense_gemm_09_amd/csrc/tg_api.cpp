@@ -253,38 +253,45 @@ int choose_config(int64_t M, int64_t N, int n_mat)
 
 // Launch-time model of the asynchronous configurations, for grids short of a
 // full wave of 256 x 256 tiles.  A configuration with s K splits runs
-// n = ceil(tiles s / CUs) workgroups per CU; it costs
-//     a + b (K / s) (1 + r (n - 1))                      [us, K in thousands]
-// plus, split, e + h (partial bytes s M N 8, in MB: written once, read once)
-// + h2 (bytes s TM TN 4 of one tile's partials, in MB: the workgroup that
-// completes a tile reads them all on its own), and never less than the
-// compulsory HBM traffic (A, B and C once) at bw.  Per workgroup the K loop
-// is latency-bound: a 64 x 64 tile takes 3.9 us per thousand k against 7.1
-// for 128 x 128, four times the work, so the larger tile wins wherever it
-// still fills the chip, and split-K buys back the waves that a small grid
-// leaves idle.  The coefficients are a least-squares fit (relative error) of
-// 3380 launches timed back to back on MI355X: bf16, B in both layouts, M
-// 64..2048 over 13 (N, K) pairs from 1024 to 14336, every configuration
-// with 1, 2, 4 and 8 splits; 10% rms error.  Its choice lands within 0.7% of
-// the fastest measured launch summed over those 260 shapes, and within 0.6%
-// over 84 others it was not fitted on (M 96..3072, 7 more (N, K) pairs).
+// n = ceil(tiles s / CUs) workgroups per CU, and keeps the fraction u =
+// tiles s / (n CUs) of the CUs busy; it costs
+//     a + b (K / s) (1 + r (n - 1)) (1 + g u)           [us, K in thousands]
+// with a and b per B layout, plus, split, e + h (partial bytes s M N 8, in
+// MB: written once, read once) + h2 (bytes s TM TN 4 of one tile's partials,
+// in MB: the workgroup that completes a tile reads them all on its own), and
+// never less than the compulsory HBM traffic (A, B and C once) at bw.  K
+// counts the k a masked last quad pads.  Per workgroup the K loop is
+// latency-bound: a 64 x 64 tile takes 3.0 us per thousand k against 5.5 for
+// 128 x 128 (four times the work) and 4.7 for 128 x 128 in 64-deep steps,
+// so the larger tile wins wherever it still fills the chip, and split-K buys
+// back the waves that a small grid leaves idle; g, the cost of a full wave
+// over an empty one, is the clock the board gives up under full load.  The
+// coefficients are a least-squares fit (relative error) of 6352 launches
+// timed back to back on MI355X: bf16, B in both layouts, 518 shapes (M
+// 64..3072, also off the tile grid, over 20 (N, K) pairs from 1024 to
+// 14336), every configuration with 1, 2, 4 and 8 splits; 7.2% rms error.
+// Fitted on four fifths of the shapes, its choice lands within 0.5% of the
+// fastest measured launch summed over those and over the fifth held out.
 struct WaveCost {
     int tm, tn;
     bool m16;
-    double a, b, r, e;
+    int kb;
+    double a_kn, b_kn, a_nk, b_nk, r, e;
 };
 constexpr WaveCost kWaveCost[] = {
-    {64, 64, false, 1.59, 3.87, 1.03, 2.27},    {64, 128, false, 1.67, 5.04, 1.24, 1.84},
-    {128, 128, false, 1.73, 7.08, 1.32, 1.56},  {192, 192, true, 6.65, 11.77, 1.42, 0.0},
-    {256, 256, false, 8.12, 16.32, 1.50, 0.0},  {256, 256, true, 8.16, 18.41, 1.50, 0.0},
-    // the 16x16x32 128 x 128 tiles: timed like the 32x32x16 ones, 1 % dearer
-    // so that those (which can split K) keep the shapes both can take; for K
-    // off the 128 grid only the 16x16x32 tiles are candidates
-    {128, 128, true, 1.75, 7.15, 1.32, 0.0},
+    {64, 64, false, 32, 1.97, 2.95, 1.40, 3.13, 0.85, 2.02},
+    {64, 128, false, 32, 2.21, 3.86, 1.23, 4.52, 0.97, 1.61},
+    {128, 128, false, 32, 2.31, 5.46, 1.74, 6.00, 1.06, 1.24},
+    {128, 128, true, 32, 3.92, 5.44, 3.34, 6.00, 1.02, 0.00},
+    {128, 128, true, 64, 5.18, 4.67, 4.94, 4.41, 1.15, 0.00},
+    {192, 192, true, 32, 6.99, 9.71, 6.64, 10.39, 1.07, 0.00},
+    {256, 256, false, 32, 8.26, 14.27, 7.82, 14.44, 1.20, 0.00},
+    {256, 256, true, 32, 8.72, 15.76, 7.82, 16.60, 0.99, 0.00},
 };
-constexpr double kSplitUsPerMB = 0.139;    // partial traffic of a split, all tiles
-constexpr double kCombineUsPerMB = 10.67;  // one tile's partials, read by one workgroup
-constexpr double kModelHbmBytesPerUs = 4.55e6;
+constexpr double kSplitUsPerMB = 0.142;    // partial traffic of a split, all tiles
+constexpr double kCombineUsPerMB = 10.82;  // one tile's partials, read by one workgroup
+constexpr double kModelHbmBytesPerUs = 4.552e6;
+constexpr double kFullWaveCost = 0.507;    // g: per-k cost of a full wave over an empty one
 
 // Modelled microseconds of configuration cfg with s splits (plus a 1 %
 // tie-break); < 0 when the configuration has no coefficients.
@@ -292,12 +299,17 @@ double wave_cost_us(const tg::GemmArgs &a, int cfg, int s, int cus)
 {
     const int tm = tg::async_tile_m(cfg), tn = tg::async_tile_n(cfg);
     const bool m16 = tg::async_mfma16(cfg);
+    const int kb = tg::async_k_step(cfg);
     for (const WaveCost &w : kWaveCost) {
-        if (w.tm != tm || w.tn != tn || w.m16 != m16)
+        if (w.tm != tm || w.tn != tn || w.m16 != m16 || w.kb != kb)
             continue;
         const double tiles = (double)tg::async_tiles_m(a, cfg) * tg::async_tiles_n(a, cfg) * a.n_mat;
         const double n = std::ceil(tiles * s / cus);
-        double t = w.a + w.b * ((double)a.K / s / 1000.0) * (1.0 + w.r * (n - 1.0));
+        const double u = tiles * s / (n * cus);
+        const int q = 4 * kb; // k of the loop's four steps: a masked last quad pads to it
+        const double k = m16 ? (double)((a.K + q - 1) / q * q) : (double)a.K;
+        const double wa = a.b_trans ? w.a_nk : w.a_kn, wb = a.b_trans ? w.b_nk : w.b_kn;
+        double t = wa + wb * (k / s / 1000.0) * (1.0 + w.r * (n - 1.0)) * (1.0 + kFullWaveCost * u);
         if (s > 1)
             t += w.e + kSplitUsPerMB * s * (double)a.M * a.N * a.n_mat * 8.0 / 1e6 +
                  kCombineUsPerMB * s * (double)tm * tn * 4.0 / 1e6;
@@ -347,9 +359,11 @@ int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr
     if (splits)
         *splits = 1;
     if (force && strncmp(force, "async", 5) == 0) {
+        // a forced configuration takes any padding of the last tiles (they
+        // stay exact; the cost is the caller's choice)
         for (int i = 0; i < n; ++i)
             if (strcmp(force, tg::async_config_name(i)) == 0) {
-                return tg::async_eligible(a, i) ? i : -1;
+                return tg::async_eligible(a, i, true) ? i : -1;
             }
         return -1;
     }
@@ -1247,6 +1261,8 @@ int tg_lds_swizzle(int layout, int64_t row)
         return tg::swz_b192(r);
     case 5:
         return tg::swz_b128(r);
+    case 6:
+        return tg::swz_a8(r);
     default:
         return -1;
     }

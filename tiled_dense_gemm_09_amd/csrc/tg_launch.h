@@ -59,6 +59,8 @@ bool async_forced_only(int cfg);
 bool async_mfma16(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
+// k per step of the configuration's K loop (32, or 64)
+int async_k_step(int cfg);
 bool async_eligible(const GemmArgs &a, int cfg, bool any_pad = false);
 // Row and column tiles of a problem: the ceilings of M / tile height and
 // N / tile width (a partial last tile counts as a tile).

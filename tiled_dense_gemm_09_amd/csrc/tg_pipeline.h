@@ -14,6 +14,12 @@ namespace tg {
 // 16-byte bank groups: row r covers groups 4 (r % 4) + (c ^ swz_a(r)).
 __host__ __device__ constexpr int swz_a(int r) { return (r >> 2) & 3; }
 
+// The same for 128-byte rows (64 k, 8 granules): rows r and r + 2 start on
+// the same bank, so the 16 rows of one read pass need 8 distinct XOR values
+// for each row parity: granule c of row r sits at c ^ ((r >> 1) & 7), and
+// the pass covers groups 8 (r % 2) + (c ^ ((r >> 1) & 7)), all 16 of them.
+__host__ __device__ constexpr int swz_a8(int r) { return (r >> 1) & 7; }
+
 // B swizzle for rows of 16 or more granules: {0, 6, 10, 12}[r & 3] as a
 // nibble table (a shift, not a branch chain).  For 8-granule (128-byte) rows
 // the rows r and r + 2 share banks; flipping granule bit 2 on rows with bit
