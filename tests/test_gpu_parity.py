@@ -947,6 +947,11 @@ SPLIT_CASES = [
     (F16, 128, 128, 384, "async_64x128x32_s4", 3),
     (BF16, 192, 320, 1024, "async_64x64x32_s4", 8),
     (F16, 1000, 384, 1024, "async_128x128x32_s4", 4),   # partial last row tile
+    # the 16x16x32 128 x 128 tiles: 64-deep steps in 4 splits of 512 k and
+    # (partial last row tile) 2 of 512; 32-deep steps in 3 splits of 512
+    (F16, 512, 768, 2048, "async_128x128x64_s4_mfma16", 4),
+    (BF16, 1000, 384, 1024, "async_128x128x64_s4_mfma16", 2),
+    (BF16, 384, 512, 1536, "async_128x128x32_s4_mfma16", 3),
 ]
 
 
@@ -973,7 +978,7 @@ def test_split_k_integer_exact(tg, monkeypatch, dt, M, N, K, cfg, splits, trans_
     util.check_exact(bits, ref, name)
 
 
-@pytest.mark.parametrize("dt,M,N,K,cfg,splits", SPLIT_CASES[:4])
+@pytest.mark.parametrize("dt,M,N,K,cfg,splits", SPLIT_CASES[:4] + SPLIT_CASES[-3:])
 def test_split_k_bias_gelu_random_and_repeatable(tg, monkeypatch, dt, M, N, K, cfg, splits):
     # random operands: within the tolerance, and the same bits on every call
     # (the splits are added in split order whatever order they finish in)

@@ -917,9 +917,100 @@ __device__ __forceinline__ void a16_epilogue(
                                                     cols);
 }
 
+// Split-K exchange of a 16x16x32 workgroup: the protocol of combine_splits
+// (device-coherent partial stores, one atomic count per workgroup, the last
+// workgroup reads every partial back and adds them in split order 0 ..
+// splits-1), with a split's partial stored as [NW waves][MI NJ vectors][64
+// lanes] of 16-byte vectors, vector NJ i + j holding accumulator block (i,
+// j).  Returns true in the workgroup that completed the count, with acc
+// replaced by the ordered sum of all the splits.
+template <int NW, int MI, int NJ>
+__device__ __forceinline__ bool combine_splits16(f32x4 (&acc)[MI][NJ], float *ws, int *counters,
+                                                 int tile, int split, int splits, int wave,
+                                                 int lane)
+{
+    constexpr int PV = MI * NJ;                      // vectors per lane per split
+    static_assert(PV == 16, "the 128 x 128 tiles' partials");
+    constexpr int BLOCK = NW * PV * 256;             // floats per split partial
+    constexpr int RS = 32 / PV;                      // splits read back per round
+    __shared__ int s_last16;
+    float *ws_tile = ws + (int64_t)tile * splits * BLOCK;
+    const int lane_off = wave * PV * 256 + lane * 4;
+    {
+        f32x4 v[PV];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                v[NJ * i + j] = acc[i][j];
+        store_partial<PV>(ws_tile + (int64_t)split * BLOCK + lane_off, v);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        s_last16 = (old == splits - 1);
+    }
+    __syncthreads();
+    if (!s_last16)
+        return false;
+    // rounds of RS splits, all 32 loads of a round in flight together, added
+    // in split order; indices past the last split repeat it and are not added
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += RS) {
+        f32x4 v[32];
+#pragma unroll
+        for (int u = 0; u < RS; ++u) {
+            const float *src = ws_tile + (int64_t)min(sp0 + u, splits - 1) * BLOCK + lane_off;
+#pragma unroll
+            for (int t = 0; t < PV; ++t)
+                asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                             : "=v"(v[u * PV + t])
+                             : "v"(src + t * 256)
+                             : "memory");
+        }
+        // the loads are invisible to the compiler's wait tracking: wait here
+        // with every value passed through, so nothing reads one earlier
+        asm volatile("s_waitcnt vmcnt(16)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                       "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                     :
+                     : "memory");
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]),
+                       "+v"(v[21]), "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]),
+                       "+v"(v[26]), "+v"(v[27]), "+v"(v[28]), "+v"(v[29]), "+v"(v[30]),
+                       "+v"(v[31])
+                     :
+                     : "memory");
+#pragma unroll
+        for (int u = 0; u < RS; ++u)
+            if (sp0 + u < splits)
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        acc[i][j] += v[u * PV + NJ * i + j];
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// splits > 1 (128 x 128 tiles only; grid = tiles x splits, block b = split
+// tiles + tile): split s runs steps [s KT / splits, (s + 1) KT / splits) of
+// the K loop (K a multiple of the four steps times splits), the bias enters
+// through split 0, and the partials meet in combine_splits16.
 template <int DT, int ACT, int WN, bool BT, bool KM, int TM = 256, int KB = 32>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, int tiles_m,
-                                                                    int tiles_n, int group_m)
+                                                                    int tiles_n, int group_m,
+                                                                    int splits, float *ws,
+                                                                    int *counters)
 {
     constexpr int STAGE = A16Tile<TM, KB>::STAGE;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
@@ -928,24 +1019,36 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_kernel(GemmArgs p, i
     __shared__ __attribute__((aligned(1024))) unsigned char st3[STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    constexpr bool SPLITS = TM == 128;
+    const int total = tiles_m * tiles_n * p.n_mat;
+    const int split = SPLITS ? (int)blockIdx.x / total : 0;
+    const int tile = SPLITS ? (int)blockIdx.x - split * total : (int)blockIdx.x;
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, tile);
     const int m0 = tc.tm * TM, n0 = tc.tn * TM;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
     f32x4 acc[A16Geom<WN, BT, TM>::MI][A16Geom<WN, BT, TM>::NJ];
-    a16_init_acc<DT, WN, TM>(p, n0, wave, lane, true, acc);
+    a16_init_acc<DT, WN, TM>(p, n0, wave, lane, split == 0, acc);
     // KM (K off the 128 grid): the whole quads on the unmasked loop, then
     // the last, partial quad on its own with the k past K masked (a second
     // pipeline fill, but the masking's registers stay out of the main loop,
     // where they made the compiler move the accumulators in and out of the
     // register file)
-    const int KT = (p.K / (AS_STAGES * KB)) * AS_STAGES;
+    // split s (K a multiple of four steps times splits, never KM) runs steps
+    // [s KT, (s + 1) KT) of KT = K / (KB splits)
+    const int KT = p.K / (AS_STAGES * KB * (SPLITS ? splits : 1)) * AS_STAGES;
     if (!KM || KT > 0)
-        a16_mainloop<DT, WN, BT, false, TM, KB>(p, m0, n0, Bm, 0, KT, wave, lane, st0, st1, st2,
-                                                st3, acc);
+        a16_mainloop<DT, WN, BT, false, TM, KB>(p, m0, n0, Bm, split * KT, KT, wave, lane, st0,
+                                                st1, st2, st3, acc);
     if constexpr (KM)
         a16_mainloop<DT, WN, BT, true, TM, KB>(p, m0, n0, Bm, KT, AS_STAGES, wave, lane, st0, st1,
                                                st2, st3, acc);
+    if constexpr (SPLITS && !KM) {
+        using Gm = A16Geom<WN, BT, TM>;
+        if (splits > 1 && !combine_splits16<Gm::NW, Gm::MI, Gm::NJ>(acc, ws, counters, tile, split,
+                                                                    splits, wave, lane))
+            return;
+    }
     a16_epilogue<DT, ACT, WN, BT, TM, KB>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
@@ -1234,7 +1337,8 @@ bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
 int plan_async_splits(const GemmArgs &a, int cfg, int want)
 {
     const AsyncConfig &c = kAsyncConfigs[cfg];
-    if (c.mfma16 || c.ti * c.tj > 4 || want == 1)
+    // the 32x32x16 tiles up to 128 x 128, and the 16x16x32 128 x 128 ones
+    if ((c.mfma16 && c.ti != 2) || c.ti * c.tj > 4 || want == 1)
         return 1;
     const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
     if (tiles > kMaxSplitTiles || (want <= 0 && tiles >= 240))
@@ -1244,7 +1348,7 @@ int plan_async_splits(const GemmArgs &a, int cfg, int want)
     int s = want > 0 ? want : (int)(256 / tiles);
     s = s > 8 ? 8 : s;
     for (; s >= 2; --s)
-        if (a.K % (s * AS_STAGES * AS_BK) == 0)
+        if (a.K % (s * AS_STAGES * c.kb) == 0)
             return s;
     return 1;
 }
@@ -1365,34 +1469,34 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
     do {                                                                                         \
         if (t128 && k64 && a.b_trans)                                                            \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 128, 64>), grid,     \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (t128 && k64)                                                                    \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 128, 64>), grid,    \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (t128 && a.b_trans)                                                              \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 128>), grid,         \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (t128)                                                                           \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 128>), grid,        \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (t192 && a.b_trans)                                                              \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_, 192>), grid,         \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (t192)                                                                           \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_, 192>), grid,        \
-                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m);                   \
+                               dim3(256), 0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                   \
         else if (wn == 4 && a.b_trans)                                                           \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, true, KM_>), grid, dim3(512), \
-                               0, s, a, tiles_m, tiles_n, group_m);                              \
+                               0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                              \
         else if (wn == 4)                                                                        \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 4, false, KM_>), grid, dim3(512), \
-                               0, s, a, tiles_m, tiles_n, group_m);                              \
+                               0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                              \
         else if (a.b_trans)                                                                      \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, true, KM_>), grid, dim3(256), \
-                               0, s, a, tiles_m, tiles_n, group_m);                              \
+                               0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                              \
         else                                                                                     \
             hipLaunchKernelGGL((gemm_async16_kernel<DT_, ACT_, 2, false, KM_>), grid, dim3(256), \
-                               0, s, a, tiles_m, tiles_n, group_m);                              \
+                               0, s, a, tiles_m, tiles_n, group_m, splits, ws, counters);                              \
     } while (0)
 #define TG_A16(DT_, ACT_)                                                                        \
     do {                                                                                         \

@@ -266,12 +266,12 @@ int choose_config(int64_t M, int64_t N, int n_mat)
 // so the larger tile wins wherever it still fills the chip, and split-K buys
 // back the waves that a small grid leaves idle; g, the cost of a full wave
 // over an empty one, is the clock the board gives up under full load.  The
-// coefficients are a least-squares fit (relative error) of 6352 launches
+// coefficients are a least-squares fit (relative error) of 7361 launches
 // timed back to back on MI355X: bf16, B in both layouts, 518 shapes (M
 // 64..3072, also off the tile grid, over 20 (N, K) pairs from 1024 to
-// 14336), every configuration with 1, 2, 4 and 8 splits; 7.2% rms error.
+// 14336), every configuration with 1, 2, 4 and 8 splits; 7.4% rms error.
 // Fitted on four fifths of the shapes, its choice lands within 0.5% of the
-// fastest measured launch summed over those and over the fifth held out.
+// fastest measured launch summed over those, 0.8% over the fifth held out.
 struct WaveCost {
     int tm, tn;
     bool m16;
@@ -279,19 +279,19 @@ struct WaveCost {
     double a_kn, b_kn, a_nk, b_nk, r, e;
 };
 constexpr WaveCost kWaveCost[] = {
-    {64, 64, false, 32, 1.97, 2.95, 1.40, 3.13, 0.85, 2.02},
-    {64, 128, false, 32, 2.21, 3.86, 1.23, 4.52, 0.97, 1.61},
-    {128, 128, false, 32, 2.31, 5.46, 1.74, 6.00, 1.06, 1.24},
-    {128, 128, true, 32, 3.92, 5.44, 3.34, 6.00, 1.02, 0.00},
-    {128, 128, true, 64, 5.18, 4.67, 4.94, 4.41, 1.15, 0.00},
-    {192, 192, true, 32, 6.99, 9.71, 6.64, 10.39, 1.07, 0.00},
-    {256, 256, false, 32, 8.26, 14.27, 7.82, 14.44, 1.20, 0.00},
-    {256, 256, true, 32, 8.72, 15.76, 7.82, 16.60, 0.99, 0.00},
+    {64, 64, false, 32, 1.93, 3.00, 1.36, 3.19, 0.84, 1.92},
+    {64, 128, false, 32, 2.16, 3.92, 1.18, 4.59, 0.96, 1.47},
+    {128, 128, false, 32, 2.23, 5.54, 1.68, 6.09, 1.04, 1.00},
+    {128, 128, true, 32, 3.86, 5.45, 3.50, 5.94, 1.11, 1.29},
+    {128, 128, true, 64, 5.12, 4.66, 4.92, 4.42, 1.24, 0.86},
+    {192, 192, true, 32, 6.96, 9.78, 6.62, 10.46, 1.08, 0.00},
+    {256, 256, false, 32, 8.24, 14.35, 7.79, 14.52, 1.21, 0.00},
+    {256, 256, true, 32, 8.69, 15.86, 7.78, 16.69, 1.00, 0.00},
 };
-constexpr double kSplitUsPerMB = 0.142;    // partial traffic of a split, all tiles
-constexpr double kCombineUsPerMB = 10.82;  // one tile's partials, read by one workgroup
-constexpr double kModelHbmBytesPerUs = 4.552e6;
-constexpr double kFullWaveCost = 0.507;    // g: per-k cost of a full wave over an empty one
+constexpr double kSplitUsPerMB = 0.148;    // partial traffic of a split, all tiles
+constexpr double kCombineUsPerMB = 11.29;  // one tile's partials, read by one workgroup
+constexpr double kModelHbmBytesPerUs = 4.574e6;
+constexpr double kFullWaveCost = 0.485;    // g: per-k cost of a full wave over an empty one
 
 // Modelled microseconds of configuration cfg with s splits (plus a 1 %
 // tie-break); < 0 when the configuration has no coefficients.
@@ -885,9 +885,10 @@ tg_status run(tg_dtype dt, int64_t M, int64_t N, int64_t K, const void *A, int64
         int auto_splits = 1;
         const int cfg = choose_async(a, force, &auto_splits);
         const int group_m = env_int("TG_GROUP_M", 4);
-        // Split-K over the 32x32x16-MFMA tiles: the count the launch-time
-        // model took with the configuration (64 x 4096 x 4096: four splits of
-        // 64 x 64 tiles, 12.2 us against 20.0 unsplit).  TG_SPLITK=n asks
+        // Split-K (the 32x32x16 tiles up to 128 x 128 and the 16x16x32 128 x
+        // 128 ones): the count the launch-time model took with the
+        // configuration (64 x 4096 x 4096: four splits of 64 x 64 tiles, 12.2
+        // us against 20.0 unsplit).  TG_SPLITK=n asks
         // for n splits, 0 for enough to fill one wave, 1 for none.  A
         // modelled split whose workspace cannot be had (a capture that would
         // grow it, no memory) runs unsplit; a requested one, or one on the
