@@ -210,3 +210,29 @@ def test_overlapping_views_and_host_bias_are_refused(tg):
         tg.gemm_mx(torch.zeros((1, 256), dtype=torch.uint8, device="cuda").expand(256, 256), s8,
                    a8, s8)
     torch.cuda.synchronize()
+
+
+def test_log_prints_each_choice_and_the_model_estimates():
+    # TG_LOG is read once per process: a child process with TG_LOG=2 prints
+    # the chosen kernel and the launch-time model's estimate of every
+    # candidate (a grid short of a wave of 256 x 256 tiles)
+    import os
+    import subprocess
+    import sys
+    code = ("import torch\n"
+            "from tiled_dense_gemm_09_amd import tg\n"
+            "x = torch.zeros((256, 4096), dtype=torch.bfloat16, device='cuda')\n"
+            "w = torch.zeros((4096, 4096), dtype=torch.bfloat16, device='cuda')\n"
+            "tg.gemm(x, w)\n"
+            "torch.cuda.synchronize()\n"
+            "print(tg.last_kernel())\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TG_LOG="2")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=100)
+    assert r.returncode == 0, r.stderr[-2000:]
+    chosen = r.stdout.strip().splitlines()[-1]
+    estimates = [l for l in r.stderr.splitlines() if l.startswith("[tg] model 256x4096x4096:")]
+    assert len(estimates) >= 4, r.stderr[-2000:]
+    assert "[tg] kernel: " + chosen in r.stderr, (chosen, r.stderr[-2000:])
+    assert any(chosen.split("_splitk")[0] + "," in l for l in estimates), (chosen, estimates)

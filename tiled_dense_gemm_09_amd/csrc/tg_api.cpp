@@ -33,7 +33,7 @@ void set_last(const char *name, const char *detail = nullptr)
         snprintf(g_last_kernel, sizeof g_last_kernel, "%s", name);
     static const bool log = [] {
         const char *e = getenv("TG_LOG");
-        return e && e[0] == '1';
+        return e && (e[0] == '1' || e[0] == '2');
     }();
     if (log)
         fprintf(stderr, "[tg] kernel: %s\n", g_last_kernel);
@@ -377,6 +377,11 @@ int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr
     // Any padding of the last row or column tile is a candidate here: the
     // model counts the padded tiles (640 x 14336: 168 tiles of 256 x 256,
     // the last row half empty, against 560 of 128 x 128).
+    // TG_LOG=2: every candidate's modelled time on stderr
+    static const bool log_model = [] {
+        const char *e = getenv("TG_LOG");
+        return e && e[0] == '2';
+    }();
     int best = -1, best_s = 1;
     double best_t = 0.0;
     for (int i = 0; i < n; ++i) {
@@ -386,6 +391,9 @@ int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr
             continue;
         const int s = splits ? model_splits(a, i, cus) : 1;
         const double t = wave_cost_us(a, i, s, cus);
+        if (log_model)
+            fprintf(stderr, "[tg] model %lldx%lldx%lld: %s, %d split(s): %.1f us\n",
+                    (long long)a.M, (long long)a.N, (long long)a.K, tg::async_config_name(i), s, t);
         if (t >= 0.0 && (best < 0 || t < best_t)) {
             best = i;
             best_s = s;
