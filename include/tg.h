@@ -39,7 +39,9 @@
  *    element; anything else runs a slower, correct scalar fallback.  The
  *    choice is never silent: tg_last_kernel()
  *    names the kernel and tile configuration the last call on this host
- *    thread launched (and TG_LOG=1 in the environment prints it).
+ *    thread launched (and TG_LOG=1 in the environment prints it; TG_LOG=2
+ *    also prints the launch-time model's estimate for each candidate
+ *    configuration of the asynchronous kernels).
  *  - Workspace: the split-K paths of tg_gemm, tg_gemm_bias_act, tg_gemm_ex
  *    and tg_gemm_qkv (small M, and square tiles that would leave most
  *    compute units idle; tg_last_kernel() then ends in "_split..." or
@@ -50,9 +52,13 @@
  *    synchronizes the device, frees the old buffer and clears the new one's
  *    counters on the caller's stream, so:
  *      - a call that would grow it while its stream is being captured into
- *        a HIP graph launches nothing: the split-K paths return
- *        TG_ERROR_NOT_SUPPORTED (tg_last_kernel() says why), the K-padding
- *        path runs a kernel that needs no workspace instead (reported);
+ *        a HIP graph does not grow it: a K split that the launch-time
+ *        model chose for the square tiles, and the small-M kernel for
+ *        operands off the grid or B stored [N,K], run unsplit instead; the
+ *        K-padding path runs a kernel that needs no workspace (all
+ *        reported by tg_last_kernel()); a split that TG_SPLITK asked for,
+ *        and the small-M streaming kernel's, launch nothing and return
+ *        TG_ERROR_NOT_SUPPORTED (tg_last_kernel() says why);
  *      - a graph that captured a call using the workspace must not be
  *        replayed after a later call grew it.
  *    Calls that use it are ordered by their streams; two such calls on
@@ -122,7 +128,9 @@ tg_status tg_gemm_bias_act(tg_dtype dt, int64_t M, int64_t N, int64_t K,
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, same kernels and bit-identical results; it
  * never allocates, frees or clears memory through the runtime:
- *  - the split-K paths (small M; TG_SPLITK) keep their partials and
+ *  - the split-K paths (small M, and the square tiles' K splits, chosen by
+ *    the launch-time model or by TG_SPLITK; the model takes only splits
+ *    whose partials fit this scratch) keep their partials and
  *    counters in a fixed scratch array of the library, 16 MiB + 16 KiB per
  *    device, held until the process ends (set up by the first call on each
  *    device, which also launches one small kernel that zeroes the

@@ -96,6 +96,59 @@ def test_cold_k_padding_call_under_capture_takes_a_kernel_without_workspace(tg):
     assert tg.workspace_bytes() > w0
 
 
+def test_cold_model_split_under_capture_runs_unsplit():
+    # 128 x 4096 x 14336: the launch-time model splits K.  In a fresh process
+    # (no workspace yet) a captured call would have to allocate it: it runs
+    # the same tiles unsplit instead and says so, and the graph replays the
+    # exact result; the same call made eagerly afterwards splits.  Integer
+    # operands: every sum is exact in FP32, so the unsplit replay, the split
+    # eager call and an FP32 reference round to the same bits.
+    import json
+    import os
+    import subprocess
+    import sys
+    code = r"""
+import json, torch
+from tiled_dense_gemm_09_amd import tg
+g0 = torch.Generator().manual_seed(702)
+A = torch.randint(-2, 3, (128, 14336), generator=g0).to(torch.bfloat16).cuda()
+B = torch.randint(-2, 3, (14336, 4096), generator=g0).to(torch.bfloat16).cuda()
+C = torch.full((128, 4096), float("nan"), dtype=torch.bfloat16, device="cuda")
+w0 = tg.workspace_bytes()
+g = torch.cuda.CUDAGraph()
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(side):
+    with torch.cuda.graph(g):
+        tg.gemm(A, B, out=C)
+torch.cuda.current_stream().wait_stream(side)
+torch.cuda.synchronize()
+k_cap = tg.last_kernel()
+w1 = tg.workspace_bytes()
+g.replay()
+torch.cuda.synchronize()
+rep = C.clone()
+C.fill_(float("nan"))
+tg.gemm(A, B, out=C)
+torch.cuda.synchronize()
+ref = (A.float() @ B.float()).to(torch.bfloat16)
+print(json.dumps({"w0": w0, "w1": w1, "w2": tg.workspace_bytes(), "captured": k_cap,
+                  "eager": tg.last_kernel(),
+                  "replay_eq_eager": bool(torch.equal(rep.view(torch.int16), C.view(torch.int16))),
+                  "eager_eq_ref": bool(torch.equal(C.view(torch.int16), ref.view(torch.int16)))}))
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=100)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    say("  ", d)
+    assert d["w0"] == 0 and d["w1"] == 0, d
+    assert d["captured"].endswith("(unsplit: stream capture)"), d
+    assert "_splitk" in d["eager"] and d["w2"] > 0, d
+    assert d["replay_eq_eager"] and d["eager_eq_ref"], d
+
+
 def test_cold_staged_call_under_capture_takes_the_element_wise_kernel(tg):
     # operands off the 16-byte grid on a large problem are normally staged
     # through aligned copies in the workspace; when the workspace would have
