@@ -1021,6 +1021,32 @@ def test_split_k_qkv_and_more_than_one_wave(tg, monkeypatch):
         util.check_exact(outs[t], ref, "split-K qkv again [%d]" % t)
 
 
+def test_split_k_qkv_on_16x16x32_tiles(tg, monkeypatch):
+    # three outputs of the 16x16x32 128 x 128 tiles in one split launch:
+    # forced (64-deep steps, 2 x 3 x 3 tiles x 4 splits), then the default
+    # dispatch of a small-M QKV with long K, which the launch-time model
+    # splits; integer operands, bit-exact
+    name = forced_split(monkeypatch, "async_128x128x64_s4_mfma16", 4)
+    q = inputs.qkv_problem(BF16, 256, 384, 1024, seed=163, kind="int")
+    say("case split-K qkv on 64-deep 128 x 128 tiles 256x384x1024 x3")
+    _, _, outs = run_qkv(tg, q)
+    assert tg.last_kernel() == name, tg.last_kernel()
+    for t in range(3):
+        _, ref = oracle.gemm(BF16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "16x16x32 split-K qkv [%d]" % t)
+    monkeypatch.delenv("TG_FORCE_CONFIG")
+    monkeypatch.delenv("TG_SPLITK")
+    q = inputs.qkv_problem(F16, 128, 1024, 4096, seed=164, kind="int")
+    say("case default qkv 128x1024x4096 x3")
+    _, _, outs = run_qkv(tg, q)
+    kern = tg.last_kernel()
+    say("  kernel", kern)
+    assert "_splitk" in kern, kern
+    for t in range(3):
+        _, ref = oracle.gemm(F16, q["X"], q["W"][t])
+        util.check_exact(outs[t], ref, "default split qkv [%d]" % t)
+
+
 def test_split_paths_replay_in_graphs(tg, monkeypatch):
     # both split-K paths keep per-tile counters that each launch leaves at
     # zero, so a captured call replays correctly with no reset; eager calls
