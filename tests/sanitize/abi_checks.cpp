@@ -39,6 +39,7 @@ int num_async_configs() { reached("num_async_configs"); }
 const char *async_config_name(int) { reached("async_config_name"); }
 bool async_forced_only(int) { reached("async_forced_only"); }
 bool async_mfma16(int) { reached("async_mfma16"); }
+bool async_pairs(int) { reached("async_pairs"); }
 int async_tile_m(int) { reached("async_tile_m"); }
 int async_tile_n(int) { reached("async_tile_n"); }
 int async_k_step(int) { reached("async_k_step"); }

@@ -1465,7 +1465,7 @@ def test_transposed_b_full_size(tg):
     R = inputs.draw(np.random.default_rng(99), (p["M"], p["N"]), "uniform", F16)
     say("case 4096 B[N,K] + residual")
     bits, kern = run_ex(tg, p, True, R)
-    assert kern == "async_256x256x32_s4_mfma16"
+    assert kern == "async_256x256x32p_s4_mfma16", kern
     f64, rbits = oracle.gemm_ex(F16, p["A"], np.ascontiguousarray(p["B"].T), trans_b=True,
                                 bias=p["bias"], act=oracle.ACT_GELU_TANH, R=R)
     util.check_tol(F16, bits, f64, "4096 B[N,K] + residual", ref_bits=rbits)
@@ -1762,3 +1762,51 @@ def test_invalid_arguments_raise(tg):
     a = torch.zeros((8, 8), dtype=torch.float16, device="cuda")
     with pytest.raises(tg.TgError):
         tg.gemm(a, a, out=a)  # output overlaps the inputs
+
+
+PAIR_CASES = [
+    # (dt, M, N, K, integer): the pair-staged 256 x 256 loop (B stored
+    # [N,K]): whole tiles, 4 and 2 pairs of 64 k; partial last row and
+    # column tiles (600 rows, 520 columns); a single four-step round
+    (F16, 512, 768, 1024, True),
+    (BF16, 512, 512, 512, True),
+    (BF16, 600, 520, 512, True),
+    (F16, 768, 512, 128, True),
+    (F16, 768, 512, 384, False),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,integer", PAIR_CASES)
+def test_pair_staged_loop(tg, monkeypatch, dt, M, N, K, integer):
+    monkeypatch.setenv("TG_FORCE_CONFIG", "async_256x256x32p_s4_mfma16")
+    kind = "int" if integer else "normal"
+    p = inputs.problem(dt, M, N, K, seed=1500 + M + K, kind=kind, bias=True,
+                       bias_kind="int" if integer else "bias",
+                       act=inputs.ACT_NONE if integer else inputs.ACT_GELU_TANH,
+                       b_scale=1.0 if integer else K ** -0.5)
+    R = inputs.draw(np.random.default_rng(1501 + N), (M, N), "int", dt, 4.0) if integer else None
+    say("case pair-staged loop", dt, M, N, K, kind)
+    bits, kern = run_ex(tg, p, True, R)
+    assert kern == "async_256x256x32p_s4_mfma16", kern
+    f64, rbits = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T), trans_b=True,
+                                bias=p["bias"], act=p["act"], R=R)
+    if integer:
+        util.check_exact(bits, rbits, "pair-staged loop")
+    else:
+        util.check_tol(dt, bits, f64, "pair-staged loop", ref_bits=rbits)
+
+
+def test_pair_staged_loop_dispatch(tg):
+    # taken unforced for B stored [N,K] with a full wave of 256 x 256 tiles
+    # and K a multiple of 128; K off that grid keeps the masked 32-deep loop,
+    # and B stored [K,N] never takes it
+    import torch
+    a = torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda")
+    tg.gemm(a, w.t())
+    assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
+    tg.gemm(a[:, :1000], w[:, :1000].t())
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
+    tg.gemm(a, w.t().contiguous())
+    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
+    torch.cuda.synchronize()

@@ -917,6 +917,172 @@ __device__ __forceinline__ void a16_epilogue(
                                                     cols);
 }
 
+// Pair-staged K loop of the 256 x 256 tiles, B stored [N,K]: two steps of
+// 32 k share one region per operand (A in st0 / st2, B in st1 / st3, each
+// [256 rows][64 k] in 128-byte rows), so each 1 KiB copy moves whole lines
+// (8 rows of 128 bytes), and one pair is copied while the other is read.
+// Steps 4t .. 4t+3 read pairs X = 2t (st0, st1) and Y = 2t + 1 (st2, st3):
+//  4t:   MFMAs; read step 4t+1 (X, second half); wait for Y, barrier
+//  4t+1: MFMAs; read step 4t+2 (Y, first half); copy pair 2t + 2 into X
+//  4t+2: MFMAs; read step 4t+3 (Y, second half); wait for X, barrier
+//  4t+3: MFMAs; read step 4t+4 (X, first half); copy pair 2t + 3 into Y
+// Two barriers per four steps; a copy has 1.5 steps to land.  KT is a
+// multiple of 4; past the last pair the copies repeat it into the region
+// nobody reads again.
+// (B stored [K,N] is left on the 32-deep loop: with its transposing reads
+// this schedule leaves the compiler moving accumulators between register
+// files, 380 to 500 moves per four steps.)
+template <int DT, int WN>
+__device__ __forceinline__ void a16_mainloop_pairs(
+    const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int KT, int wave, int lane,
+    unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
+    f32x4 (&acc)[A16Geom<WN, true, 256>::MI][A16Geom<WN, true, 256>::NJ])
+{
+    using Gm = A16Geom<WN, true, 256>;
+    constexpr int MI = Gm::MI, NJ = Gm::NJ;
+    constexpr int PC = 256 * 128 / 1024 / Gm::NW; // copies per operand per wave per pair
+    constexpr int COPIES = 2 * PC;
+    constexpr int READS = MI + NJ; // fragment reads per step
+    const int wave_n = wave % WN, wave_m = wave / WN;
+    const int NP = KT / 2; // pairs
+    // copy c: rows 8 q .. 8 q + 7 of a [256][64] region, q = PC wave + c
+    // (lane -> row 8 q + lane / 8, granule lane % 8 with the 128-byte-row
+    // swizzle); rows past M or N read the last one.  Each lane keeps a
+    // 32-bit byte offset from the tile's corner, the corner of pair pc being
+    // a uniform (scalar) address; the host keeps 256 rows of A and of B
+    // within 4 GiB.
+    unsigned oa[PC], ob[PC];
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+        const int r = 8 * (wave * PC + c) + (lane >> 3);
+        const int kg = ((lane & 7) ^ swz_a8(r)) * 8;
+        oa[c] = 2u * ((unsigned)(min(m0 + r, p.M - 1) - m0) * (unsigned)p.lda + kg);
+        ob[c] = 2u * ((unsigned)(min(n0 + r, p.N - 1) - n0) * (unsigned)p.ldb + kg);
+    }
+    const unsigned short *a_corner = p.A + (int64_t)m0 * p.lda;
+    const unsigned short *b_corner = Bm + (int64_t)n0 * p.ldb;
+    auto copy = [&](int pr, unsigned char *sa, unsigned char *sb, int c) {
+        const int64_t k0 = (int64_t)min(pr, NP - 1) * 64;
+        if (c < PC) {
+            const unsigned dst = (unsigned)(uintptr_t)(lds_void *)sa + (wave * PC + c) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(oa[c]), "s"(a_corner + k0),
+                         "{m0}"(dst)
+                         : "memory");
+        } else {
+            const unsigned dst =
+                (unsigned)(uintptr_t)(lds_void *)sb + (wave * PC + c - PC) * 1024;
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(ob[c - PC]), "s"(b_corner + k0),
+                         "{m0}"(dst)
+                         : "memory");
+        }
+    };
+    // fragment offsets of step half h: row r, k granule 4 h + l / 16 of a
+    // 128-byte row, so half 1 flips byte-offset bit 6
+    const int q16 = lane >> 4;
+    int a_off[MI], b_off[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int r = wave_m * Gm::WROWS + 16 * i + (lane & 15);
+        a_off[i] = r * 128 + ((q16 ^ swz_a8(r)) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = wave_n * Gm::WCOLS + 16 * j + (lane & 15);
+        b_off[j] = r * 128 + ((q16 ^ swz_a8(r)) * 16);
+    }
+    struct Frag {
+        u32x4 a[MI], b[NJ];
+    };
+    auto read_piece = [&](Frag &f, const unsigned char *sa, const unsigned char *sb, int h,
+                          int q) {
+        if (q < MI)
+            f.a[q] = *reinterpret_cast<const u32x4 *>(sa + (a_off[q] ^ (64 * h)));
+        else
+            f.b[q - MI] = *reinterpret_cast<const u32x4 *>(sb + (b_off[q - MI] ^ (64 * h)));
+    };
+    constexpr int MT = MI * NJ;
+    constexpr int SPAN = MT * 3 / 4;
+    // one step: the MFMAs of fc, with the reads of fn (half h of sa / sb)
+    // and, when pr >= 0, the copies of pair pr into ca / cb spread over the
+    // first three quarters; then the waits (and barrier) the schedule needs
+    auto step = [&](Frag &fc, Frag &fn, const unsigned char *sa, const unsigned char *sb, int h,
+                    int pr, unsigned char *ca, unsigned char *cb, bool bar) {
+        const int ops = READS + (pr >= 0 ? COPIES : 0);
+#pragma unroll
+        for (int q = 0; q < MT; ++q) {
+            const int i = q % MI, j = q / MI;
+            acc[i][j] = mfma16x16x32<DT>(fc.b[j], fc.a[i], acc[i][j]);
+            if (q < SPAN) {
+                const int o0 = q * ops / SPAN, o1 = (q + 1) * ops / SPAN;
+                for (int o = o0; o < o1; ++o) {
+                    if (pr >= 0) {
+                        const int upto = (o + 1) * COPIES / ops, before = o * COPIES / ops;
+                        if (upto > before)
+                            copy(pr, ca, cb, upto - 1);
+                        else
+                            read_piece(fn, sa, sb, h, o - before);
+                    } else {
+                        read_piece(fn, sa, sb, h, o);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+        if (bar) {
+            wait_vmcnt<0>();
+            stage_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    Frag f0, f1;
+    // prologue: pairs 0 and 1 in flight, pair 0 landed, fragments of step 0
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c)
+        copy(0, st0, st1, c);
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c)
+        copy(1, st2, st3, c);
+    wait_vmcnt<COPIES>();
+    stage_barrier();
+#pragma unroll
+    for (int q = 0; q < READS; ++q)
+        read_piece(f0, st0, st1, 0, q);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    for (int t = 0; 4 * t < KT; ++t) {
+        step(f0, f1, st0, st1, 1, -1, nullptr, nullptr, true);
+        step(f1, f0, st2, st3, 0, 2 * t + 2, st0, st1, false);
+        step(f0, f1, st2, st3, 1, -1, nullptr, nullptr, true);
+        step(f1, f0, st0, st1, 0, 2 * t + 3, st2, st3, false);
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
+}
+
+// Data-parallel kernel on the pair-staged loop (256 x 256 tiles, B stored
+// [N,K], K a multiple of 128).
+template <int DT, int ACT, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_async16p_kernel(GemmArgs p, int tiles_m,
+                                                                     int tiles_n, int group_m)
+{
+    constexpr int STAGE = A16Tile<256>::STAGE;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const TileCoord tc = schedule_tile(tiles_m, tiles_n, p.n_mat, group_m, blockIdx.x);
+    const int m0 = tc.tm * 256, n0 = tc.tn * 256;
+    const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
+    unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
+    f32x4 acc[A16Geom<WN, true, 256>::MI][A16Geom<WN, true, 256>::NJ];
+    a16_init_acc<DT, WN, 256>(p, n0, wave, lane, true, acc);
+    a16_mainloop_pairs<DT, WN>(p, m0, n0, Bm, p.K / AS_BK, wave, lane, st0, st1, st2, st3, acc);
+    a16_epilogue<DT, ACT, WN, true, 256, 32>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
+}
+
 // Split-K exchange of a 16x16x32 workgroup: the protocol of combine_splits
 // (device-coherent partial stores, one atomic count per workgroup, the last
 // workgroup reads every partial back and adds them in split order 0 ..
@@ -1259,10 +1425,21 @@ struct AsyncConfig {
     bool forced_only; // taken only when TG_FORCE_CONFIG names it
     const char *name;
     int kb = 32;      // k per step of the K loop
+    bool pairs = false; // the pair-staged K loop (B stored [N,K] only)
 };
+
+// The pair-staged loop's operands: B stored [N,K], and 256 rows of A and of
+// B within the 32-bit byte offsets of its copies
+bool pairs_ok(const GemmArgs &a)
+{
+    return a.b_trans && a.lda < (1 << 23) && a.ldb < (1 << 23);
+}
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
+    // B stored [N,K] with full waves of tiles: the pair-staged K loop (bf16
+    // 8192^3 and f16 4096^3 with GELU 6 to 10 % ahead of the 32-deep loop)
+    {4, 4, 4, false, "async_256x256x32p_s4_mfma16", 32, true},
     {4, 4, 4, false, "async_256x256x32_s4_mfma16"},
     {4, 4, 8, true, "async_256x256x32_s4_mfma16_w8"}, // never ahead of the 4-wave kernel
     // 192 x 192 tiles fill a wave where 256 x 256 ones leave much of it idle
@@ -1272,6 +1449,7 @@ const AsyncConfig kAsyncConfigs[] = {
     // at this size the K loop is bound by the latency of its steps), and
     // unlike them it masks K off the 128 grid in the kernel
     {2, 2, 4, false, "async_128x128x32_s4_mfma16"},
+
     // 64-deep steps: half the barriers and waits per k, whole 128-byte row
     // pieces per copy (B [N,K] 1024 x 8192 x 8192: 117 against 156 us for the
     // 32-deep tiles)
@@ -1287,6 +1465,7 @@ int num_async_configs() { return (int)(sizeof kAsyncConfigs / sizeof kAsyncConfi
 const char *async_config_name(int cfg) { return kAsyncConfigs[cfg].name; }
 bool async_forced_only(int cfg) { return kAsyncConfigs[cfg].forced_only; }
 bool async_mfma16(int cfg) { return kAsyncConfigs[cfg].mfma16 != 0; }
+bool async_pairs(int cfg) { return kAsyncConfigs[cfg].pairs; }
 int async_tile_m(int cfg) { return 64 * kAsyncConfigs[cfg].ti; }
 int async_tile_n(int cfg) { return 64 * kAsyncConfigs[cfg].tj; }
 int async_k_step(int cfg) { return kAsyncConfigs[cfg].kb; }
@@ -1328,8 +1507,9 @@ bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
     const int padn = async_tiles_n(a, cfg) * tn - a.N;
     const bool n_ok = a.N % tn == 0 ||
                       (a.N % 8 == 0 && (any_pad || tn == 64 || (a.N > tn && 8 * padn <= a.N)));
-    return m_ok && n_ok &&
-           async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0, AS_STAGES * kAsyncConfigs[cfg].kb) &&
+    return m_ok && n_ok && (!kAsyncConfigs[cfg].pairs || pairs_ok(a)) &&
+           async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0 && !kAsyncConfigs[cfg].pairs,
+                      AS_STAGES * kAsyncConfigs[cfg].kb) &&
            ((uintptr_t)a.bias & 7u) == 0 &&
            ((uintptr_t)a.R & 15u) == 0 && a.ldr % 8 == 0;
 }
@@ -1362,8 +1542,8 @@ size_t async_ws_floats(const GemmArgs &a, int cfg, int splits)
 SkPlan plan_stream_k(const GemmArgs &a, int cfg, int cus, bool any_size)
 {
     SkPlan pl{0, 0, 0, 0, 0};
-    if (kAsyncConfigs[cfg].mfma16 != 4 || kAsyncConfigs[cfg].ti != 4 || !async_eligible(a, cfg) ||
-        cus <= 0 || cus % kNumXcd != 0)
+    if (kAsyncConfigs[cfg].mfma16 != 4 || kAsyncConfigs[cfg].ti != 4 || kAsyncConfigs[cfg].pairs ||
+        !async_eligible(a, cfg) || cus <= 0 || cus % kNumXcd != 0)
         return pl;
     const int64_t tiles = (int64_t)async_tiles_m(a, cfg) * async_tiles_n(a, cfg) * a.n_mat;
     const int q = a.K / (AS_STAGES * AS_BK);
@@ -1463,6 +1643,26 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                           A16Geom<4, true>::NT == 512 && A16Geom<2, true>::NT == 256,
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
+        if (kAsyncConfigs[cfg].pairs) {
+            if (km || splits != 1 || kAsyncConfigs[cfg].ti != 4 || !pairs_ok(a))
+                return hipErrorInvalidValue;
+#define TG_A16P(DT_, ACT_)                                                                       \
+    hipLaunchKernelGGL((gemm_async16p_kernel<DT_, ACT_, 2>), grid, dim3(256), 0, s, a, tiles_m,   \
+                       tiles_n, group_m)
+            if (dt == DT_F16) {
+                if (act == ACT_GELU)
+                    TG_A16P(DT_F16, ACT_GELU);
+                else
+                    TG_A16P(DT_F16, ACT_NONE);
+            } else {
+                if (act == ACT_GELU)
+                    TG_A16P(DT_BF16, ACT_GELU);
+                else
+                    TG_A16P(DT_BF16, ACT_NONE);
+            }
+#undef TG_A16P
+            return hipGetLastError();
+        }
         const bool t192 = kAsyncConfigs[cfg].ti == 3, t128 = kAsyncConfigs[cfg].ti == 2;
         const bool k64 = kAsyncConfigs[cfg].kb == 64;
 #define TG_A16K(DT_, ACT_, KM_)                                                                  \

@@ -385,7 +385,7 @@ int choose_async(const tg::GemmArgs &a, const char *force, int *splits = nullptr
     int best = -1, best_s = 1;
     double best_t = 0.0;
     for (int i = 0; i < n; ++i) {
-        if (tg::async_forced_only(i) || !tg::async_eligible(a, i, true))
+        if (tg::async_forced_only(i) || tg::async_pairs(i) || !tg::async_eligible(a, i, true))
             continue;
         if (a.K % 128 != 0 && (!tg::async_mfma16(i) || 2 * tiles(i) < cus))
             continue;

@@ -57,6 +57,8 @@ const char *async_config_name(int cfg);
 bool async_forced_only(int cfg);
 // true for the configurations on the 16x16x32 MFMA (256 x 256, 192 x 192 and 128 x 128 tiles)
 bool async_mfma16(int cfg);
+// the pair-staged K loop: taken only for full waves of tiles, never modelled
+bool async_pairs(int cfg);
 int async_tile_m(int cfg);
 int async_tile_n(int cfg);
 // k per step of the configuration's K loop (32, or 64)
