@@ -640,17 +640,35 @@ __device__ __forceinline__ void restaged_epilogue16(const f32x4 (&acc)[MI][NJ], 
     }
 }
 
+// A pointer every lane holds the same value of, in scalar registers
+__device__ __forceinline__ const unsigned short *uniform_ptr(const unsigned short *ptr)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)ptr;
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+    return reinterpret_cast<const unsigned short *>(((uint64_t)hi << 32) | lo);
+}
+
 // The K loop of one TM x TM tile on the 16x16x32 MFMA: K-steps kt0 ..
 // kt0 + KT - 1 (KT a multiple of the four stages) of the tile at (m0, n0)
 // of the product with the weight Bm, accumulated into acc (which the caller
 // has initialised).  On return every copy has landed and every wave has
 // finished reading the stages, so the LDS is free.
-template <int DT, int WN, bool BT, bool KM, int TM = 256, int KB = 32>
+template <int DT, int WN, bool BT, bool KM, int TM = 256, int KB = 32, bool SC = true>
 __device__ __forceinline__ void a16_mainloop(
     const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int kt0, int KT, int wave,
     int lane, unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
     f32x4 (&acc)[A16Geom<WN, BT, TM, KB>::MI][A16Geom<WN, BT, TM, KB>::NJ])
 {
+    // SC: copies from scalar tile-corner addresses (below); the tile and its
+    // K range are the workgroup's, uniform
+    if constexpr (SC) {
+        m0 = __builtin_amdgcn_readfirstlane(m0);
+        n0 = __builtin_amdgcn_readfirstlane(n0);
+        kt0 = __builtin_amdgcn_readfirstlane(kt0);
+        KT = __builtin_amdgcn_readfirstlane(KT);
+        Bm = uniform_ptr(Bm);
+    }
     using Gm = A16Geom<WN, BT, TM, KB>;
     constexpr int MI = Gm::MI, NJ = Gm::NJ, CA = Gm::CA, KH = Gm::KH;
     constexpr int A_BYTES = A16Tile<TM, KB>::A_BYTES;
@@ -682,9 +700,17 @@ __device__ __forceinline__ void a16_mainloop(
     // [TM n][KB k] K-contiguous, B copy q filling n-rows RPC q .. RPC q +
     // RPC - 1 with the A swizzle.
     const int64_t b_step = BT ? (int64_t)KB : (int64_t)KB * p.ldb;
-    // KM: copy c of step kt is inside K iff kt * 32 < a_kl[c] (b_kl[c])
+    // KM: copy c of step kt is inside K iff kt * 32 < a_kl[c] (b_kl[c]).
+    // SC without KM: a copy is a uniform (scalar) tile-corner address plus
+    // the lane's 32-bit byte offset oa[c] (ob[c]); the host keeps TM rows of
+    // A (and of B stored [N,K]) within 4 GiB.  Otherwise each lane's 64-bit
+    // address ga[c] (gb[c]).
     const unsigned short *ga[CA], *gb[CA];
     int a_kl[CA], b_kl[CA];
+    unsigned oa[CA], ob[CA];
+    const unsigned short *a_corner = p.A + (int64_t)m0 * p.lda + (int64_t)kt0 * KB;
+    const unsigned short *b_corner =
+        (BT ? Bm + (int64_t)n0 * p.ldb : Bm + n0) + (int64_t)kt0 * b_step;
     const unsigned short *zero = reinterpret_cast<const unsigned short *>(kZeroGranule);
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
@@ -694,41 +720,57 @@ __device__ __forceinline__ void a16_mainloop(
         // rows past M (a last row tile that M does not fill) read row M-1:
         // every copy stays inside A, and those rows only reach outputs that
         // are never stored
-        ga[c] = p.A + (int64_t)min(m0 + ra, p.M - 1) * p.lda + ka + (int64_t)kt0 * KB;
+        const int ra_in = min(m0 + ra, p.M - 1) - m0;
+        ga[c] = a_corner + (int64_t)ra_in * p.lda + ka;
+        oa[c] = 2u * ((unsigned)ra_in * (unsigned)p.lda + (unsigned)ka);
         a_kl[c] = p.K - kt0 * KB - ka;
         if constexpr (BT) {
-            gb[c] = Bm + (int64_t)min(n0 + ra, p.N - 1) * p.ldb + ka + (int64_t)kt0 * KB;
+            const int rn = min(n0 + ra, p.N - 1) - n0;
+            gb[c] = b_corner + (int64_t)rn * p.ldb + ka;
+            ob[c] = 2u * ((unsigned)rn * (unsigned)p.ldb + (unsigned)ka);
             b_kl[c] = a_kl[c];
         } else {
+            int rb, cn;
             if constexpr (TM == 256) {
-                const int rb = 2 * q + (lane >> 5);
-                gb[c] = Bm + (int64_t)rb * p.ldb +
-                        min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) + (int64_t)kt0 * b_step;
-                b_kl[c] = p.K - kt0 * KB - rb;
+                rb = 2 * q + (lane >> 5);
+                cn = min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) - n0;
             } else {
                 const unsigned byte = 1024u * q + 16u * lane;
-                const int rb = (int)(byte / (2 * TM));
+                rb = (int)(byte / (2 * TM));
                 const int gb0 = (int)(byte % (2 * TM) / 16) ^ (TM == 192 ? swz_b192(rb) : swz_b128(rb));
-                gb[c] = Bm + (int64_t)rb * p.ldb + min(n0 + gb0 * 8, p.N - 8) +
-                        (int64_t)kt0 * b_step;
-                b_kl[c] = p.K - kt0 * KB - rb;
+                cn = min(n0 + gb0 * 8, p.N - 8) - n0;
             }
+            gb[c] = b_corner + (int64_t)rb * p.ldb + cn;
+            ob[c] = 2u * ((unsigned)rb * (unsigned)p.ldb + (unsigned)cn);
+            b_kl[c] = p.K - kt0 * KB - rb;
         }
     }
     auto copy = [&](int kt, unsigned char *st, int c) {
         const unsigned lds = (unsigned)(uintptr_t)(lds_void *)st;
         if (c < CA) {
             const unsigned dst = lds + (wave * CA + c) * 1024;
-            const unsigned short *src = ga[c] + kt * KB;
-            if constexpr (KM)
-                src = kt * KB < a_kl[c] ? src : zero;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+            if constexpr (KM || !SC) {
+                const unsigned short *src = ga[c] + kt * KB;
+                if constexpr (KM)
+                    src = kt * KB < a_kl[c] ? src : zero;
+                asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+            } else {
+                asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(oa[c]),
+                             "s"(a_corner + (int64_t)kt * KB), "{m0}"(dst)
+                             : "memory");
+            }
         } else {
             const unsigned dst = lds + A_BYTES + (wave * CA + c - CA) * 1024;
-            const unsigned short *src = gb[c - CA] + kt * b_step;
-            if constexpr (KM)
-                src = kt * KB < b_kl[c - CA] ? src : zero;
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+            if constexpr (KM || !SC) {
+                const unsigned short *src = gb[c - CA] + kt * b_step;
+                if constexpr (KM)
+                    src = kt * KB < b_kl[c - CA] ? src : zero;
+                asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+            } else {
+                asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(ob[c - CA]),
+                             "s"(b_corner + kt * b_step), "{m0}"(dst)
+                             : "memory");
+            }
         }
     };
     auto issue = [&](int kt, unsigned char *st) {
@@ -1323,8 +1365,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p
         int ln, wv;
         opaque(ln, wv);
         a16_init_acc<DT, WN>(p, n0, wv, ln, q0 == 0, acc);
-        a16_mainloop<DT, WN, BT, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv, ln, st0, st1,
-                                        st2, st3, acc);
+        // (64-bit lane addresses: the scalar-corner copies measured 5 to 9 %
+        // slower in this kernel, 4352 x 4096 x 4096)
+        a16_mainloop<DT, WN, BT, false, 256, 32, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv,
+                                                        ln, st0, st1, st2, st3, acc);
         bool finish = q0 == 0 && q1 == Q;
         if (!finish) {
             // pieces of tile ts: workgroups w_first .. w_last, piece s stored
@@ -1428,12 +1472,8 @@ struct AsyncConfig {
     bool pairs = false; // the pair-staged K loop (B stored [N,K] only)
 };
 
-// The pair-staged loop's operands: B stored [N,K], and 256 rows of A and of
-// B within the 32-bit byte offsets of its copies
-bool pairs_ok(const GemmArgs &a)
-{
-    return a.b_trans && a.lda < (1 << 23) && a.ldb < (1 << 23);
-}
+// The pair-staged loop's operand B: stored [N,K]
+bool pairs_ok(const GemmArgs &a) { return a.b_trans; }
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
@@ -1507,7 +1547,11 @@ bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
     const int padn = async_tiles_n(a, cfg) * tn - a.N;
     const bool n_ok = a.N % tn == 0 ||
                       (a.N % 8 == 0 && (any_pad || tn == 64 || (a.N > tn && 8 * padn <= a.N)));
+    // the 16x16x32 kernels' copies: 256 rows of A (and of B stored [N,K])
+    // within the 32-bit byte offsets of a lane
+    const bool ld32 = a.lda < (1 << 23) && (!a.b_trans || a.ldb < (1 << 23));
     return m_ok && n_ok && (!kAsyncConfigs[cfg].pairs || pairs_ok(a)) &&
+           (!kAsyncConfigs[cfg].mfma16 || ld32) &&
            async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0 && !kAsyncConfigs[cfg].pairs,
                       AS_STAGES * kAsyncConfigs[cfg].kb) &&
            ((uintptr_t)a.bias & 7u) == 0 &&
