@@ -42,11 +42,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_tokens(text):
+    """C++ source with comments removed and runs of whitespace collapsed
+    (string and character literals kept whole), so that the hash below
+    follows the code and not its comments."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
+    """Hash of the kernel sources' code (comments and layout ignored): the
+    HBM traffic record is reported only while it matches."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1796,6 +1796,26 @@ def test_pair_staged_loop(tg, monkeypatch, dt, M, N, K, integer):
         util.check_tol(dt, bits, f64, "pair-staged loop", ref_bits=rbits)
 
 
+def test_leading_dimension_past_32_bit_lane_offsets(tg):
+    # 256 rows of A at a pitch of 2^23 + 64 elements span more than 4 GiB,
+    # past the 32-bit lane offsets of the 16x16x32 kernels' copies: the
+    # 32x32x16 kernels take it, exact on integer operands
+    import torch
+    M, N, K, lda = 256, 512, 512, (1 << 23) + 64
+    Ab = inputs.draw(np.random.default_rng(1601), (M, K), "int", BF16, 4.0)
+    Bb = inputs.draw(np.random.default_rng(1602), (K, N), "int", BF16, 4.0)
+    say("case lda 2^23 + 64", M, N, K)
+    big = torch.zeros((M, lda), dtype=torch.bfloat16, device="cuda")
+    big[:, :K] = util.to_dev(Ab, BF16)
+    C = tg.gemm(big[:, :K], util.to_dev(Bb, BF16))
+    torch.cuda.synchronize()
+    kern = tg.last_kernel()
+    assert "mfma16" not in kern, kern
+    _, ref = oracle.gemm(BF16, Ab, Bb)
+    util.check_exact(util.to_bits(C), ref, "lda 2^23 + 64")
+    del big
+
+
 def test_pair_staged_loop_dispatch(tg):
     # taken unforced for B stored [N,K] with a full wave of 256 x 256 tiles
     # and K a multiple of 128; K off that grid keeps the masked 32-deep loop,

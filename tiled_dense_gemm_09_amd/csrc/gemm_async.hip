@@ -1365,8 +1365,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p
         int ln, wv;
         opaque(ln, wv);
         a16_init_acc<DT, WN>(p, n0, wv, ln, q0 == 0, acc);
-        // (64-bit lane addresses: the scalar-corner copies measured 5 to 9 %
-        // slower in this kernel, 4352 x 4096 x 4096)
+        // (64-bit lane addresses: the scalar-corner form measured level here,
+        // 4352 x 4096 x 4096 in alternating order, and moves this kernel's
+        // register spills around)
         a16_mainloop<DT, WN, BT, false, 256, 32, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv,
                                                         ln, st0, st1, st2, st3, acc);
         bool finish = q0 == 0 && q1 == Q;
