@@ -100,6 +100,8 @@ CASES = [
     ("async16_4096_gelu", {}, gemm_case(4096, 4096, 1024), "async_256x256x32_s4_mfma16"),
     ("async16_bt_bf16", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"},
      gemm_case(512, 512, 2048, "bf16", bt=True), "async_256x256x32_s4_mfma16"),
+    ("async16p_bt_residual", {"TG_FORCE_CONFIG": "async_256x256x32p_s4_mfma16"},
+     gemm_case(512, 768, 1024, "bf16", bt=True, residual=True), "async_256x256x32p_s4_mfma16"),
     ("async16_residual", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"},
      gemm_case(512, 768, 1024, residual=True), "async_256x256x32_s4_mfma16"),
     ("async16_kmask", {}, gemm_case(4096, 4096, 1000), "async_256x256x32_s4_mfma16"),

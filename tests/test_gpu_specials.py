@@ -70,6 +70,10 @@ FAMILIES = [
      False, "async_256x256x32_s4_mfma16"),
     ("async16_bf16_bt", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"}, BF16, 512, 512, 256,
      True, "async_256x256x32_s4_mfma16"),
+    ("async16p_bf16_bt", {"TG_FORCE_CONFIG": "async_256x256x32p_s4_mfma16"}, BF16, 512, 512,
+     256, True, "async_256x256x32p_s4_mfma16"),
+    ("async16p_f16_bt", {"TG_FORCE_CONFIG": "async_256x256x32p_s4_mfma16"}, F16, 512, 768,
+     384, True, "async_256x256x32p_s4_mfma16"),
     ("async16_w8", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16_w8"}, F16, 512, 512, 256,
      False, "async_256x256x32_s4_mfma16_w8"),
     ("async16_192", {"TG_FORCE_CONFIG": "async_192x192x32_s4_mfma16"}, F16, 384, 384, 256,
