@@ -97,7 +97,7 @@ def attn_case(B, H, S, D, causal):
 
 # (id, environment, inputs, expected kernel-name prefix)
 CASES = [
-    ("async16_4096_gelu", {}, gemm_case(4096, 4096, 1024), "async_256x256x32_s4_mfma16"),
+    ("async16p_4096_gelu", {}, gemm_case(4096, 4096, 1024), "async_256x256x32p_s4_mfma16"),
     ("async16_bt_bf16", {"TG_FORCE_CONFIG": "async_256x256x32_s4_mfma16"},
      gemm_case(512, 512, 2048, "bf16", bt=True), "async_256x256x32_s4_mfma16"),
     ("async16p_bt_residual", {"TG_FORCE_CONFIG": "async_256x256x32p_s4_mfma16"},

@@ -166,7 +166,7 @@ def test_gelu_config_full_output(tg):
     say("case f16_4096_gelu full", p["M"], p["N"], p["K"])
     bits, kern = run(tg, p)
     say("  kernel", kern)
-    assert kern.startswith("async_256x256x32_s4_mfma16"), kern
+    assert kern == "async_256x256x32p_s4_mfma16", kern
     f64, rbits = oracle.gemm(F16, p["A"], p["B"], p["bias"], oracle.ACT_GELU_TANH)
     util.check_tol(F16, bits, f64, "f16_4096_gelu", ref_bits=rbits)
 
@@ -176,7 +176,7 @@ def test_gelu_config_integer_bias_exact_full(tg):
     assert p["act"] == inputs.ACT_NONE and p["bias"] is not None
     say("case f16_4096 integer + bias, full")
     bits, kern = run(tg, p)
-    assert kern.startswith("async_256x256x32_s4_mfma16"), kern
+    assert kern == "async_256x256x32p_s4_mfma16", kern
     _, ref = oracle.gemm(F16, p["A"], p["B"], p["bias"])
     util.check_exact(bits, ref, "f16_4096 integer+bias")
 
@@ -210,7 +210,7 @@ def test_qkv_config_full_output(tg):
     q = inputs.config_problem("bf16_qkv")
     say("case bf16_qkv full", q["M"], q["N"], q["K"])
     _, _, outs = run_qkv(tg, q)
-    assert tg.last_kernel().startswith("async_256x256x32_s4_mfma16"), tg.last_kernel()
+    assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
     refs = oracle.gemm_qkv(BF16, q["X"], *q["W"])
     for t in range(3):
         util.check_tol(BF16, outs[t], refs[t][0], "qkv config [%d]" % t, ref_bits=refs[t][1])
@@ -370,7 +370,7 @@ def test_square_8192_full_output(tg):
     say("case bf16_8192 full", p["M"], p["N"], p["K"])
     bits, kern = run(tg, p)
     say("  kernel", kern)
-    assert kern.startswith("async_256x256x32_s4_mfma16"), kern
+    assert kern == "async_256x256x32p_s4_mfma16", kern
     f64, rbits = oracle.gemm(BF16, p["A"], p["B"])
     util.check_tol(BF16, bits, f64, "bf16_8192", ref_bits=rbits)
 
@@ -435,7 +435,7 @@ def test_square_8192_integer_exact_full(tg):
     p = inputs.config_problem("bf16_8192", integer=True)
     say("case bf16_8192 integer, full")
     bits, kern = run(tg, p)
-    assert kern.startswith("async_256x256x32_s4_mfma16"), kern
+    assert kern == "async_256x256x32p_s4_mfma16", kern
     _, ref = oracle.gemm(BF16, p["A"], p["B"])
     util.check_exact(bits, ref, "bf16_8192 integer")
 
@@ -1732,9 +1732,9 @@ def test_dispatch_choices(tg, monkeypatch):
     tg.gemm(f, g)
     assert tg.last_kernel() == "async_256x256x32_s4_mfma16_streamk", tg.last_kernel()
     monkeypatch.delenv("TG_STREAMK")
-    # whole waves (4096^3: 256 tiles) stay data-parallel
+    # whole waves (4096^3: 256 tiles) stay data-parallel, on the pair-staged loop
     tg.gemm(g, g)
-    assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
+    assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
     # below a full wave of 256 x 256 tiles the launch-time model picks the
     # tile and the split count: 64 x 4096 x 4096 in four splits of 64 x 64
     # tiles; 128 x 4096 x 14336 split as well; TG_SPLITK=1 turns it off
@@ -1765,19 +1765,24 @@ def test_invalid_arguments_raise(tg):
 
 
 PAIR_CASES = [
-    # (dt, M, N, K, integer): the pair-staged 256 x 256 loop (B stored
-    # [N,K]): whole tiles, 4 and 2 pairs of 64 k; partial last row and
-    # column tiles (600 rows, 520 columns); a single four-step round
-    (F16, 512, 768, 1024, True),
-    (BF16, 512, 512, 512, True),
-    (BF16, 600, 520, 512, True),
-    (F16, 768, 512, 128, True),
-    (F16, 768, 512, 384, False),
+    # (dt, M, N, K, integer, B stored [N,K]): the pair-staged 256 x 256 loop,
+    # both B layouts: whole tiles, 4 and 2 pairs of 64 k; partial last row
+    # and column tiles (600 rows, 520 columns); a single four-step round
+    (F16, 512, 768, 1024, True, True),
+    (BF16, 512, 512, 512, True, True),
+    (BF16, 600, 520, 512, True, True),
+    (F16, 768, 512, 128, True, True),
+    (F16, 768, 512, 384, False, True),
+    (F16, 512, 768, 1024, True, False),
+    (BF16, 512, 512, 512, True, False),
+    (BF16, 600, 520, 512, True, False),
+    (F16, 768, 512, 128, True, False),
+    (BF16, 768, 512, 384, False, False),
 ]
 
 
-@pytest.mark.parametrize("dt,M,N,K,integer", PAIR_CASES)
-def test_pair_staged_loop(tg, monkeypatch, dt, M, N, K, integer):
+@pytest.mark.parametrize("dt,M,N,K,integer,trans_b", PAIR_CASES)
+def test_pair_staged_loop(tg, monkeypatch, dt, M, N, K, integer, trans_b):
     monkeypatch.setenv("TG_FORCE_CONFIG", "async_256x256x32p_s4_mfma16")
     kind = "int" if integer else "normal"
     p = inputs.problem(dt, M, N, K, seed=1500 + M + K, kind=kind, bias=True,
@@ -1785,11 +1790,12 @@ def test_pair_staged_loop(tg, monkeypatch, dt, M, N, K, integer):
                        act=inputs.ACT_NONE if integer else inputs.ACT_GELU_TANH,
                        b_scale=1.0 if integer else K ** -0.5)
     R = inputs.draw(np.random.default_rng(1501 + N), (M, N), "int", dt, 4.0) if integer else None
-    say("case pair-staged loop", dt, M, N, K, kind)
-    bits, kern = run_ex(tg, p, True, R)
+    say("case pair-staged loop", dt, M, N, K, kind, "B[N,K]" if trans_b else "B[K,N]")
+    bits, kern = run_ex(tg, p, trans_b, R)
     assert kern == "async_256x256x32p_s4_mfma16", kern
-    f64, rbits = oracle.gemm_ex(dt, p["A"], np.ascontiguousarray(p["B"].T), trans_b=True,
-                                bias=p["bias"], act=p["act"], R=R)
+    B = np.ascontiguousarray(p["B"].T) if trans_b else p["B"]
+    f64, rbits = oracle.gemm_ex(dt, p["A"], B, trans_b=trans_b, bias=p["bias"], act=p["act"],
+                                R=R)
     if integer:
         util.check_exact(bits, rbits, "pair-staged loop")
     else:
@@ -1817,9 +1823,8 @@ def test_leading_dimension_past_32_bit_lane_offsets(tg):
 
 
 def test_pair_staged_loop_dispatch(tg):
-    # taken unforced for B stored [N,K] with a full wave of 256 x 256 tiles
-    # and K a multiple of 128; K off that grid keeps the masked 32-deep loop,
-    # and B stored [K,N] never takes it
+    # taken unforced with a full wave of 256 x 256 tiles and K a multiple of
+    # 128, B in either layout; K off that grid keeps the masked 32-deep loop
     import torch
     a = torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda")
@@ -1828,5 +1833,7 @@ def test_pair_staged_loop_dispatch(tg):
     tg.gemm(a[:, :1000], w[:, :1000].t())
     assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
     tg.gemm(a, w.t().contiguous())
+    assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
+    tg.gemm(a[:, :1000], w.t().contiguous()[:1000])
     assert tg.last_kernel() == "async_256x256x32_s4_mfma16", tg.last_kernel()
     torch.cuda.synchronize()

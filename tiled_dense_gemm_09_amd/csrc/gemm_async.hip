@@ -959,10 +959,11 @@ __device__ __forceinline__ void a16_epilogue(
                                                     cols);
 }
 
-// Pair-staged K loop of the 256 x 256 tiles, B stored [N,K]: two steps of
-// 32 k share one region per operand (A in st0 / st2, B in st1 / st3, each
-// [256 rows][64 k] in 128-byte rows), so each 1 KiB copy moves whole lines
-// (8 rows of 128 bytes), and one pair is copied while the other is read.
+// Pair-staged K loop of the 256 x 256 tiles: two steps of 32 k share one
+// region per operand (A in st0 / st2 as [256 rows][64 k] in 128-byte rows;
+// B in st1 / st3 likewise when stored [N,K], else as [64 k][256 n] in
+// 512-byte rows), so each 1 KiB copy moves whole lines (8 rows of 128
+// bytes, or 2 of 512), and one pair is copied while the other is read.
 // Steps 4t .. 4t+3 read pairs X = 2t (st0, st1) and Y = 2t + 1 (st2, st3):
 //  4t:   MFMAs; read step 4t+1 (X, second half); wait for Y, barrier
 //  4t+1: MFMAs; read step 4t+2 (Y, first half); copy pair 2t + 2 into X
@@ -971,16 +972,13 @@ __device__ __forceinline__ void a16_epilogue(
 // Two barriers per four steps; a copy has 1.5 steps to land.  KT is a
 // multiple of 4; past the last pair the copies repeat it into the region
 // nobody reads again.
-// (B stored [K,N] is left on the 32-deep loop: with its transposing reads
-// this schedule leaves the compiler moving accumulators between register
-// files, 380 to 500 moves per four steps.)
-template <int DT, int WN>
+template <int DT, int WN, bool BT>
 __device__ __forceinline__ void a16_mainloop_pairs(
     const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int KT, int wave, int lane,
     unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
-    f32x4 (&acc)[A16Geom<WN, true, 256>::MI][A16Geom<WN, true, 256>::NJ])
+    f32x4 (&acc)[A16Geom<WN, BT, 256>::MI][A16Geom<WN, BT, 256>::NJ])
 {
-    using Gm = A16Geom<WN, true, 256>;
+    using Gm = A16Geom<WN, BT, 256>;
     constexpr int MI = Gm::MI, NJ = Gm::NJ;
     constexpr int PC = 256 * 128 / 1024 / Gm::NW; // copies per operand per wave per pair
     constexpr int COPIES = 2 * PC;
@@ -989,22 +987,31 @@ __device__ __forceinline__ void a16_mainloop_pairs(
     const int NP = KT / 2; // pairs
     // copy c: rows 8 q .. 8 q + 7 of a [256][64] region, q = PC wave + c
     // (lane -> row 8 q + lane / 8, granule lane % 8 with the 128-byte-row
-    // swizzle); rows past M or N read the last one.  Each lane keeps a
-    // 32-bit byte offset from the tile's corner, the corner of pair pc being
-    // a uniform (scalar) address; the host keeps 256 rows of A and of B
-    // within 4 GiB.
+    // swizzle); rows past M or N read the last one.  B stored [K,N]: k rows
+    // 2 q, 2 q + 1 of the [64][256] region (lane -> row 2 q + lane / 32,
+    // granule lane % 32 with the 512-byte-row swizzle), columns past N read
+    // the last 8.  Each lane keeps a 32-bit byte offset from the tile's
+    // corner, the corner of pair pc being a uniform (scalar) address; the
+    // host keeps 256 rows of A (and of B stored [N,K]) within 4 GiB.
     unsigned oa[PC], ob[PC];
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
         const int r = 8 * (wave * PC + c) + (lane >> 3);
         const int kg = ((lane & 7) ^ swz_a8(r)) * 8;
         oa[c] = 2u * ((unsigned)(min(m0 + r, p.M - 1) - m0) * (unsigned)p.lda + kg);
-        ob[c] = 2u * ((unsigned)(min(n0 + r, p.N - 1) - n0) * (unsigned)p.ldb + kg);
+        if constexpr (BT) {
+            ob[c] = 2u * ((unsigned)(min(n0 + r, p.N - 1) - n0) * (unsigned)p.ldb + kg);
+        } else {
+            const int rb = 2 * (wave * PC + c) + (lane >> 5);
+            ob[c] = 2u * ((unsigned)rb * (unsigned)p.ldb +
+                          (unsigned)(min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) - n0));
+        }
     }
     const unsigned short *a_corner = p.A + (int64_t)m0 * p.lda;
-    const unsigned short *b_corner = Bm + (int64_t)n0 * p.ldb;
+    const unsigned short *b_corner = BT ? Bm + (int64_t)n0 * p.ldb : Bm + n0;
+    const int64_t b_pair = BT ? 64 : (int64_t)64 * p.ldb; // B elements per pair
     auto copy = [&](int pr, unsigned char *sa, unsigned char *sb, int c) {
-        const int64_t k0 = (int64_t)min(pr, NP - 1) * 64;
+        const int64_t pc = min(pr, NP - 1), k0 = pc * 64;
         if (c < PC) {
             const unsigned dst = (unsigned)(uintptr_t)(lds_void *)sa + (wave * PC + c) * 1024;
             asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(oa[c]), "s"(a_corner + k0),
@@ -1013,15 +1020,21 @@ __device__ __forceinline__ void a16_mainloop_pairs(
         } else {
             const unsigned dst =
                 (unsigned)(uintptr_t)(lds_void *)sb + (wave * PC + c - PC) * 1024;
-            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(ob[c - PC]), "s"(b_corner + k0),
-                         "{m0}"(dst)
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(ob[c - PC]),
+                         "s"(b_corner + pc * b_pair), "{m0}"(dst)
                          : "memory");
         }
     };
     // fragment offsets of step half h: row r, k granule 4 h + l / 16 of a
-    // 128-byte row, so half 1 flips byte-offset bit 6
-    const int q16 = lane >> 4;
-    int a_off[MI], b_off[NJ];
+    // 128-byte row, so half 1 flips byte-offset bit 6.  B stored [K,N]: two
+    // transposing reads per fragment from k rows 32 h + 8 (l / 16) + 4 hh +
+    // (l % 16) / 4 (half 1: 32 rows, 16 KiB, further; the swizzle ignores
+    // row bit 5); fragment column j sets granule bits 1..3 (2 j), which
+    // neither the wave's column base (a multiple of 16 granules) nor the row
+    // term touches, so fragment j's offset is fragment 0's XOR 32 j.
+    static_assert(BT || (NJ <= 8 && Gm::WCOLS % 128 == 0), "B [K,N] offsets by XOR");
+    const int q16 = lane >> 4, jj = lane & 15;
+    int a_off[MI], b_off[NJ], bk_off[2];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int r = wave_m * Gm::WROWS + 16 * i + (lane & 15);
@@ -1029,18 +1042,38 @@ __device__ __forceinline__ void a16_mainloop_pairs(
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int r = wave_n * Gm::WCOLS + 16 * j + (lane & 15);
+        const int r = wave_n * Gm::WCOLS + 16 * j + jj;
         b_off[j] = r * 128 + ((q16 ^ swz_a8(r)) * 16);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int r = 8 * q16 + 4 * hh + (jj >> 2);
+        const int col = wave_n * Gm::WCOLS + 4 * (jj & 3);
+        bk_off[hh] = r * 512 + (((col >> 3) ^ swz_b16(r)) * 16) + (col & 7) * 2;
     }
     struct Frag {
         u32x4 a[MI], b[NJ];
     };
+    // read piece q: B fragment q < NJ, then A fragment q - NJ.  (With the
+    // A fragments first, the B [K,N] loop compiled to 380-500 moves of
+    // accumulators between the register files per four steps; in this order
+    // both layouts have none.)  A B [K,N] fragment's two transposing reads
+    // are assigned as one vector.
     auto read_piece = [&](Frag &f, const unsigned char *sa, const unsigned char *sb, int h,
                           int q) {
-        if (q < MI)
-            f.a[q] = *reinterpret_cast<const u32x4 *>(sa + (a_off[q] ^ (64 * h)));
-        else
-            f.b[q - MI] = *reinterpret_cast<const u32x4 *>(sb + (b_off[q - MI] ^ (64 * h)));
+        if (q >= NJ) {
+            f.a[q - NJ] = *reinterpret_cast<const u32x4 *>(sa + (a_off[q - NJ] ^ (64 * h)));
+        } else if constexpr (BT) {
+            f.b[q] = *reinterpret_cast<const u32x4 *>(sb + (b_off[q] ^ (64 * h)));
+        } else {
+            const u32x2 w0 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (lds_s16x4 *)(sb + h * 16384 + (bk_off[0] ^ (32 * q)))));
+            const u32x2 w1 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (lds_s16x4 *)(sb + h * 16384 + (bk_off[1] ^ (32 * q)))));
+            f.b[q] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+        }
     };
     constexpr int MT = MI * NJ;
     constexpr int SPAN = MT * 3 / 4;
@@ -1102,9 +1135,9 @@ __device__ __forceinline__ void a16_mainloop_pairs(
     stage_barrier();
 }
 
-// Data-parallel kernel on the pair-staged loop (256 x 256 tiles, B stored
-// [N,K], K a multiple of 128).
-template <int DT, int ACT, int WN>
+// Data-parallel kernel on the pair-staged loop (256 x 256 tiles, K a
+// multiple of 128).
+template <int DT, int ACT, int WN, bool BT>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_async16p_kernel(GemmArgs p, int tiles_m,
                                                                      int tiles_n, int group_m)
 {
@@ -1119,10 +1152,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16p_kernel(GemmArgs p, 
     const int m0 = tc.tm * 256, n0 = tc.tn * 256;
     const unsigned short *Bm = tc.mat == 0 ? p.B[0] : (tc.mat == 1 ? p.B[1] : p.B[2]);
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
-    f32x4 acc[A16Geom<WN, true, 256>::MI][A16Geom<WN, true, 256>::NJ];
+    f32x4 acc[A16Geom<WN, BT, 256>::MI][A16Geom<WN, BT, 256>::NJ];
     a16_init_acc<DT, WN, 256>(p, n0, wave, lane, true, acc);
-    a16_mainloop_pairs<DT, WN>(p, m0, n0, Bm, p.K / AS_BK, wave, lane, st0, st1, st2, st3, acc);
-    a16_epilogue<DT, ACT, WN, true, 256, 32>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
+    a16_mainloop_pairs<DT, WN, BT>(p, m0, n0, Bm, p.K / AS_BK, wave, lane, st0, st1, st2, st3,
+                                   acc);
+    a16_epilogue<DT, ACT, WN, BT, 256, 32>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
 // Split-K exchange of a 16x16x32 workgroup: the protocol of combine_splits
@@ -1470,16 +1504,15 @@ struct AsyncConfig {
     bool forced_only; // taken only when TG_FORCE_CONFIG names it
     const char *name;
     int kb = 32;      // k per step of the K loop
-    bool pairs = false; // the pair-staged K loop (B stored [N,K] only)
+    bool pairs = false; // the pair-staged K loop (256 x 256, K a multiple of 128)
 };
 
-// The pair-staged loop's operand B: stored [N,K]
-bool pairs_ok(const GemmArgs &a) { return a.b_trans; }
 // in order of preference: the first eligible configuration with a full wave
 // of workgroups is taken
 const AsyncConfig kAsyncConfigs[] = {
-    // B stored [N,K] with full waves of tiles: the pair-staged K loop (bf16
-    // 8192^3 and f16 4096^3 with GELU 6 to 10 % ahead of the 32-deep loop)
+    // full waves of tiles: the pair-staged K loop (B stored [N,K]: bf16
+    // 4096^3 to 8192^3 7 to 10 % ahead of the 32-deep loop; B [K,N]: f16
+    // 4096^3 with GELU 3 % ahead, bf16 8192^3 and QKV level)
     {4, 4, 4, false, "async_256x256x32p_s4_mfma16", 32, true},
     {4, 4, 4, false, "async_256x256x32_s4_mfma16"},
     {4, 4, 8, true, "async_256x256x32_s4_mfma16_w8"}, // never ahead of the 4-wave kernel
@@ -1551,8 +1584,7 @@ bool async_eligible(const GemmArgs &a, int cfg, bool any_pad)
     // the 16x16x32 kernels' copies: 256 rows of A (and of B stored [N,K])
     // within the 32-bit byte offsets of a lane
     const bool ld32 = a.lda < (1 << 23) && (!a.b_trans || a.ldb < (1 << 23));
-    return m_ok && n_ok && (!kAsyncConfigs[cfg].pairs || pairs_ok(a)) &&
-           (!kAsyncConfigs[cfg].mfma16 || ld32) &&
+    return m_ok && n_ok && (!kAsyncConfigs[cfg].mfma16 || ld32) &&
            async_k_ok(a.K, kAsyncConfigs[cfg].mfma16 != 0 && !kAsyncConfigs[cfg].pairs,
                       AS_STAGES * kAsyncConfigs[cfg].kb) &&
            ((uintptr_t)a.bias & 7u) == 0 &&
@@ -1689,11 +1721,17 @@ hipError_t launch_async(int cfg, int dt, int act, const GemmArgs &a, int group_m
                       "block sizes below");
         const int wn = kAsyncConfigs[cfg].mfma16 / 2;
         if (kAsyncConfigs[cfg].pairs) {
-            if (km || splits != 1 || kAsyncConfigs[cfg].ti != 4 || !pairs_ok(a))
+            if (km || splits != 1 || kAsyncConfigs[cfg].ti != 4)
                 return hipErrorInvalidValue;
 #define TG_A16P(DT_, ACT_)                                                                       \
-    hipLaunchKernelGGL((gemm_async16p_kernel<DT_, ACT_, 2>), grid, dim3(256), 0, s, a, tiles_m,   \
-                       tiles_n, group_m)
+    do {                                                                                         \
+        if (a.b_trans)                                                                           \
+            hipLaunchKernelGGL((gemm_async16p_kernel<DT_, ACT_, 2, true>), grid, dim3(256), 0, s, \
+                               a, tiles_m, tiles_n, group_m);                                    \
+        else                                                                                     \
+            hipLaunchKernelGGL((gemm_async16p_kernel<DT_, ACT_, 2, false>), grid, dim3(256), 0,  \
+                               s, a, tiles_m, tiles_n, group_m);                                 \
+    } while (0)
             if (dt == DT_F16) {
                 if (act == ACT_GELU)
                     TG_A16P(DT_F16, ACT_GELU);
