@@ -969,16 +969,24 @@ __device__ __forceinline__ void a16_epilogue(
 //  4t+1: MFMAs; read step 4t+2 (Y, first half); copy pair 2t + 2 into X
 //  4t+2: MFMAs; read step 4t+3 (Y, second half); wait for X, barrier
 //  4t+3: MFMAs; read step 4t+4 (X, first half); copy pair 2t + 3 into Y
-// Two barriers per four steps; a copy has 1.5 steps to land.  KT is a
-// multiple of 4; past the last pair the copies repeat it into the region
-// nobody reads again.
+// Two barriers per four steps; a copy has 1.5 steps to land.  Steps kt0 ..
+// kt0 + KT - 1, KT and kt0 multiples of 4; past the last pair the copies
+// repeat it into the region nobody reads again.
 template <int DT, int WN, bool BT>
 __device__ __forceinline__ void a16_mainloop_pairs(
-    const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int KT, int wave, int lane,
-    unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
+    const GemmArgs &p, int m0, int n0, const unsigned short *Bm, int kt0, int KT, int wave,
+    int lane, unsigned char *st0, unsigned char *st1, unsigned char *st2, unsigned char *st3,
     f32x4 (&acc)[A16Geom<WN, BT, 256>::MI][A16Geom<WN, BT, 256>::NJ])
 {
     using Gm = A16Geom<WN, BT, 256>;
+    // the tile and its K range are the workgroup's: uniform, which the
+    // copies' scalar addresses need (the stream-K work loop hides it from
+    // the compiler)
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    kt0 = __builtin_amdgcn_readfirstlane(kt0);
+    KT = __builtin_amdgcn_readfirstlane(KT);
+    Bm = uniform_ptr(Bm);
     constexpr int MI = Gm::MI, NJ = Gm::NJ;
     constexpr int PC = 256 * 128 / 1024 / Gm::NW; // copies per operand per wave per pair
     constexpr int COPIES = 2 * PC;
@@ -1007,9 +1015,10 @@ __device__ __forceinline__ void a16_mainloop_pairs(
                           (unsigned)(min(n0 + ((lane & 31) ^ swz_b16(rb)) * 8, p.N - 8) - n0));
         }
     }
-    const unsigned short *a_corner = p.A + (int64_t)m0 * p.lda;
-    const unsigned short *b_corner = BT ? Bm + (int64_t)n0 * p.ldb : Bm + n0;
     const int64_t b_pair = BT ? 64 : (int64_t)64 * p.ldb; // B elements per pair
+    const unsigned short *a_corner = p.A + (int64_t)m0 * p.lda + (int64_t)kt0 * 32;
+    const unsigned short *b_corner =
+        (BT ? Bm + (int64_t)n0 * p.ldb : Bm + n0) + (int64_t)(kt0 / 2) * b_pair;
     auto copy = [&](int pr, unsigned char *sa, unsigned char *sb, int c) {
         const int64_t pc = min(pr, NP - 1), k0 = pc * 64;
         if (c < PC) {
@@ -1154,8 +1163,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16p_kernel(GemmArgs p, 
     unsigned short *Cm = tc.mat == 0 ? p.C[0] : (tc.mat == 1 ? p.C[1] : p.C[2]);
     f32x4 acc[A16Geom<WN, BT, 256>::MI][A16Geom<WN, BT, 256>::NJ];
     a16_init_acc<DT, WN, 256>(p, n0, wave, lane, true, acc);
-    a16_mainloop_pairs<DT, WN, BT>(p, m0, n0, Bm, p.K / AS_BK, wave, lane, st0, st1, st2, st3,
-                                   acc);
+    a16_mainloop_pairs<DT, WN, BT>(p, m0, n0, Bm, 0, p.K / AS_BK, wave, lane, st0, st1, st2,
+                                   st3, acc);
     a16_epilogue<DT, ACT, WN, BT, 256, 32>(p, Cm, m0, n0, wave, lane, st0, st1, st2, st3, acc);
 }
 
@@ -1399,11 +1408,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_async16_sk_kernel(GemmArgs p
         int ln, wv;
         opaque(ln, wv);
         a16_init_acc<DT, WN>(p, n0, wv, ln, q0 == 0, acc);
-        // (64-bit lane addresses: the scalar-corner form measured level here,
-        // 4352 x 4096 x 4096 in alternating order, and moves this kernel's
-        // register spills around)
-        a16_mainloop<DT, WN, BT, false, 256, 32, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv,
-                                                        ln, st0, st1, st2, st3, acc);
+        // B stored [N,K]: the pair-staged loop.  B [K,N]: the 32-deep loop
+        // with 64-bit lane addresses (in this kernel the pair-staged one
+        // compiles to accumulator moves between the register files, and
+        // the scalar-corner form measured level, 4352 x 4096 x 4096)
+        if constexpr (BT)
+            a16_mainloop_pairs<DT, WN, BT>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0), wv, ln, st0,
+                                           st1, st2, st3, acc);
+        else
+            a16_mainloop<DT, WN, BT, false, 256, 32, false>(p, m0, n0, Bm, 4 * q0, 4 * (q1 - q0),
+                                                            wv, ln, st0, st1, st2, st3, acc);
         bool finish = q0 == 0 && q1 == Q;
         if (!finish) {
             // pieces of tile ts: workgroups w_first .. w_last, piece s stored
