@@ -289,3 +289,40 @@ def test_log_prints_each_choice_and_the_model_estimates():
     assert len(estimates) >= 4, r.stderr[-2000:]
     assert "[tg] kernel: " + chosen in r.stderr, (chosen, r.stderr[-2000:])
     assert any(chosen.split("_splitk")[0] + "," in l for l in estimates), (chosen, estimates)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_pair_staged_kernel_replays_in_a_graph(tg, trans_b):
+    # a full wave of 256 x 256 tiles takes the pair-staged loop, which needs
+    # no workspace: captured, then replayed three times with the eager call
+    # between the replays, every result equal to the oracle's on sampled rows
+    import torch
+    M, N, K = 4096, 4096, 512
+    p = inputs.problem(BF16, M, N, K, seed=710 + int(trans_b), kind="int", bias=True,
+                       bias_kind="int")
+    A = util.to_dev(p["A"], BF16)
+    Bd = util.to_dev(np.ascontiguousarray(p["B"].T) if trans_b else p["B"], BF16)
+    B = Bd.t() if trans_b else Bd
+    bias = util.to_dev(p["bias"], BF16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    say("case pair-staged kernel in a graph", M, N, K, "B[N,K]" if trans_b else "B[K,N]")
+    g, mark, raised = capture(lambda: tg.gemm(A, B, out=C, bias=bias))
+    assert raised is None, raised
+    assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
+    rows = [0, 1, 255, 256, M // 2 + 3, M - 1]
+    refs = [oracle.gemm(BF16, p["A"], p["B"], p["bias"], rows=(r, r + 1))[1] for r in rows]
+    for i in range(3):
+        C.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "replay %d row %d" % (i, r))
+        C.fill_(float("nan"))
+        tg.gemm(A, B, out=C, bias=bias)
+        torch.cuda.synchronize()
+        assert tg.last_kernel() == "async_256x256x32p_s4_mfma16", tg.last_kernel()
+        got = util.to_bits(C)
+        for r, ref in zip(rows, refs):
+            util.check_exact(got[r:r + 1], ref, "eager %d row %d" % (i, r))
+    assert float(mark[0]) == 3.0
