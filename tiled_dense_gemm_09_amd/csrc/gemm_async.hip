@@ -1110,6 +1110,12 @@ __device__ __forceinline__ void a16_mainloop_pairs(
                     }
                 }
             }
+            // B stored [N,K]: each MFMA with its reads and copies kept in
+            // this order (bf16 8192^3 1479-1483 against 1417-1419 TFLOP/s
+            // left to the scheduler); with B [K,N] the fence costs half the
+            // rate (accumulator moves)
+            if constexpr (BT)
+                __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
