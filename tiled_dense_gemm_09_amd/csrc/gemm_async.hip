@@ -866,6 +866,11 @@ __device__ __forceinline__ void a16_mainloop(
                         read_piece(fn, nxt, o - before);
                 }
             }
+            // B stored [N,K]: each MFMA kept with its reads and copies in
+            // this order (bf16 1024 x 8192 x 8192 on 128 x 128 x 64 tiles
+            // 1227-1229 against 1159-1191 TFLOP/s left to the scheduler)
+            if constexpr (BT)
+                __builtin_amdgcn_sched_barrier(0);
         }
         // Keep the next step's MFMAs below the wait and barrier: the compiler
         // otherwise moves them up behind the reads of their fragments and
